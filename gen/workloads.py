@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for the paged MQA indexer.
+
+Input synthesis only: this module holds none of the method's arithmetic (no
+fp8 decode, no dot products, no binning, no selection).  FP8 E4M3FN encoding
+is done with PyTorch's own CPU cast.  Both the HIP path (tests, bench, smoke)
+and the CPU oracle consume what it produces.
+
+The workloads follow the five decode configurations the indexer is measured
+on (H=32, D=128, 64-token pages):
+
+  tiny_decode    B=1,  next_n=1, L=4096
+  long_decode    B=8,  next_n=1, L=131072
+  spec_verify    B=16, next_n=4, L=32768 (row j of a request sees L+j keys);
+                 variants fine / unit / mixed scale the head weights so the
+                 scores land below 16, mostly in 16..223, or across all three
+                 regimes, and "mixed" sets the K scale of 1% of the pool slots
+                 to +inf
+  varlen_decode  B=64, next_n=1, L log-uniform in [8192, 262144], stride 262144
+  very_long      B=4,  next_n=1, L=1048576; plus score rows [4, 1048576] drawn
+                 from 0.99 N(0, var 4) + 0.01 N(40, var 10)
+
+Value recipe: Q ~ N(0,1) cast to e4m3; K rows ~ N(0,1), per-token scale
+absmax/448, codes = e4m3(k / scale); head weights N(0,1)/sqrt(32) times the
+variant's factor.  Physical pages are a seeded permutation of one pool that
+has ~1% spare pages.  Slots of a request's last page past its longest row and
+the spare pages hold K = 448 with scale 1e6, so an unmasked read shows up as a
+huge score.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+HEADS = 32
+DIM = 128
+PAGE = 64
+
+SEEDS = {
+    "tiny_decode": 101,
+    "long_decode": 202,
+    "spec_verify/fine": 301,
+    "spec_verify/unit": 302,
+    "spec_verify/mixed": 303,
+    "varlen_decode": 404,
+    "very_long": 505,
+    "very_long/scores": 506,
+}
+
+# Head-weight factors for the three verify variants.
+VERIFY_WEIGHT_SCALE = {"fine": 0.25, "unit": 16.0, "mixed": 4.0}
+
+
+@dataclasses.dataclass
+class IndexerInputs:
+    """Host (numpy) arrays of one indexer call, in the library's layouts."""
+
+    name: str
+    q: np.ndarray            # uint8 [rows, 32, 128]   e4m3fn codes
+    kv_pages: np.ndarray     # uint8 [num_pages, 64, 128] e4m3fn codes
+    k_scales: np.ndarray     # f32   [num_pages, 64]
+    weights: np.ndarray      # f32   [rows, 32]
+    block_table: np.ndarray  # int32 [B, max_pages]
+    context_lens: np.ndarray  # int32 [rows]
+    next_n: int
+    logits_stride: int
+
+    @property
+    def B(self) -> int:
+        return self.block_table.shape[0]
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_pages(self) -> int:
+        return self.kv_pages.shape[0]
+
+    @property
+    def max_pages(self) -> int:
+        return self.block_table.shape[1]
+
+    def request_keys(self) -> np.ndarray:
+        """Longest row length of each request (the keys its K sweep reads)."""
+        return self.context_lens.reshape(self.B, self.next_n).max(axis=1)
+
+    def k_bytes(self) -> int:
+        """Bytes of K rows the indexer must read (128 B per key per request)."""
+        return int(self.request_keys().astype(np.int64).sum()) * DIM
+
+
+def to_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
+    """uint8 E4M3FN codes of float32 values (saturated to +-448 first)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def make_indexer_inputs(name, B, next_n, base_lens, seed, weight_scale=1.0,
+                        inf_frac=0.0, logits_stride=None, max_pages=None,
+                        spare_frac=0.01, pages_per_chunk=4096):
+    """Build one indexer call.
+
+    base_lens: int per request; row j of request b sees base_lens[b] + j keys.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    base_lens = np.asarray(base_lens, dtype=np.int64).reshape(B)
+    rows = B * next_n
+    lens = (base_lens[:, None] + np.arange(next_n)[None, :]).reshape(rows)
+    req_keys = base_lens + next_n - 1
+    req_pages = -(-req_keys // PAGE)
+    used = int(req_pages.sum())
+    num_pages = used + max(1, int(math.ceil(used * spare_frac)))
+    if max_pages is None:
+        max_pages = int(req_pages.max()) if B else 1
+    if logits_stride is None:
+        logits_stride = int(lens.max()) if rows else 1
+        logits_stride = -(-logits_stride // 4) * 4
+
+    # Q and head weights.
+    q = to_e4m3fn_codes(rng.standard_normal((rows, HEADS, DIM), dtype=np.float32))
+    weights = (rng.standard_normal((rows, HEADS), dtype=np.float32)
+               / np.float32(math.sqrt(HEADS)) * np.float32(weight_scale))
+
+    # K pool, generated in chunks of pages to bound host memory.
+    kv_pages = np.empty((num_pages, PAGE, DIM), dtype=np.uint8)
+    k_scales = np.empty((num_pages, PAGE), dtype=np.float32)
+    for p0 in range(0, num_pages, pages_per_chunk):
+        p1 = min(num_pages, p0 + pages_per_chunk)
+        k = rng.standard_normal(((p1 - p0) * PAGE, DIM), dtype=np.float32)
+        sc = np.abs(k).max(axis=1) / np.float32(448.0)
+        kv_pages[p0:p1] = to_e4m3fn_codes(k / sc[:, None]).reshape(p1 - p0, PAGE, DIM)
+        k_scales[p0:p1] = sc.reshape(p1 - p0, PAGE)
+
+    # Page table: a seeded permutation of the pool.
+    perm = rng.permutation(num_pages).astype(np.int32)
+    block_table = np.zeros((B, max_pages), dtype=np.int32)
+    offs = np.concatenate([[0], np.cumsum(req_pages)])
+    for b in range(B):
+        block_table[b, :req_pages[b]] = perm[offs[b]:offs[b + 1]]
+    spare = perm[used:]
+
+    # Poison: spare pages and slots past each request's longest row.
+    kv_pages[spare] = 0x7E
+    k_scales[spare] = 1e6
+    for b in range(B):
+        tail = int(req_keys[b] % PAGE)
+        if tail:
+            last = block_table[b, req_pages[b] - 1]
+            kv_pages[last, tail:] = 0x7E
+            k_scales[last, tail:] = 1e6
+
+    if inf_frac > 0.0:
+        mask = rng.random((num_pages, PAGE)) < inf_frac
+        k_scales[mask] = np.inf
+
+    return IndexerInputs(name=name, q=q, kv_pages=kv_pages, k_scales=k_scales,
+                         weights=weights, block_table=block_table,
+                         context_lens=lens.astype(np.int32), next_n=next_n,
+                         logits_stride=int(logits_stride))
+
+
+def config_inputs(name: str) -> IndexerInputs:
+    """The named decode workload at its full size."""
+    if name == "tiny_decode":
+        return make_indexer_inputs(name, 1, 1, [4096], SEEDS[name])
+    if name == "long_decode":
+        return make_indexer_inputs(name, 8, 1, [131072] * 8, SEEDS[name])
+    if name.startswith("spec_verify/"):
+        variant = name.split("/", 1)[1]
+        return make_indexer_inputs(
+            name, 16, 4, [32768] * 16, SEEDS[name],
+            weight_scale=VERIFY_WEIGHT_SCALE[variant],
+            inf_frac=0.01 if variant == "mixed" else 0.0)
+    if name == "varlen_decode":
+        rng = np.random.Generator(np.random.PCG64(SEEDS[name] + 1000))
+        lens = np.floor(np.exp(rng.uniform(math.log(8192), math.log(262144), 64)))
+        return make_indexer_inputs(name, 64, 1, lens.astype(np.int64), SEEDS[name],
+                                   logits_stride=262144, max_pages=262144 // PAGE)
+    if name == "very_long":
+        return make_indexer_inputs(name, 4, 1, [1048576] * 4, SEEDS[name])
+    raise KeyError(name)
+
+
+CONFIG_NAMES = ("tiny_decode", "long_decode", "spec_verify/fine",
+                "spec_verify/unit", "spec_verify/mixed", "varlen_decode",
+                "very_long")
+
+
+def very_long_scores(rows=4, n=1048576, seed=None) -> np.ndarray:
+    """float32 [rows, n]: 0.99 N(0, var 4) + 0.01 N(40, var 10), seeded."""
+    if seed is None:
+        seed = SEEDS["very_long/scores"]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    base = rng.standard_normal((rows, n), dtype=np.float32) * np.float32(2.0)
+    out = rng.standard_normal((rows, n), dtype=np.float32) * np.float32(math.sqrt(10.0))
+    out += np.float32(40.0)
+    mask = rng.random((rows, n)) < 0.01
+    return np.where(mask, out, base).astype(np.float32)

@@ -1,0 +1,12 @@
+"""CPU oracle of the paged MQA indexer (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package; the HIP library never does.
+"""
+from .indexer_oracle import *  # noqa: F401,F403
+from .indexer_oracle import (  # noqa: F401
+    E4M3FN, KEY_FP16, KEY_FP32, NUM_BINS, PAGE_SIZE, HEAD_DIM, NUM_HEADS,
+    check_logits, coarse_bin, coarse_histogram, decode_e4m3fn,
+    e4m3fn_decode_table, fp16_rne, head_sum_at, indexer_logits,
+    indexer_logits_at, logits_error_bound_at, score_keys, topk_row, topk_rows,
+)

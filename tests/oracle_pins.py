@@ -1,0 +1,481 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes the oracle module and returns a list of failure
+messages (empty when the oracle passes).  ``test_oracle_pins.py`` runs them on
+the real oracle; ``test_oracle_mutants.py`` runs them on copies of the oracle
+with a planted mistake and requires at least one to fail.
+
+What the pins lean on, none of which is the oracle's own code:
+  * the OCP E4M3FN bit definition and PyTorch's float8_e4m3fn cast;
+  * exact rational arithmetic (fractions.Fraction) for fp16 rounding, for the
+    dot products and for the whole logit formula on tiny inputs;
+  * hand-derived bins and keys in tests/golden/ (DeepGEMM PR #94 "What this
+    adds" bin definition; vLLM PR #52696 FP16 keys);
+  * closed-form bin populations over all 65,536 FP16 encodings;
+  * histogram invariants (total = live non-NaN count; additivity; padding);
+  * brute-force top-k with Python's sorted() and an explicit comparator.
+"""
+
+from __future__ import annotations
+
+import bisect
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- helpers --
+def load_golden_bins():
+    vals, bins = [], []
+    with open(os.path.join(GOLDEN, "coarse_bins_by_hand.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            v, b = line.split()
+            vals.append(float(v))
+            bins.append(int(b))
+    return np.array(vals, dtype=np.float32), np.array(bins, dtype=np.int64)
+
+
+def load_golden_keys():
+    out = []
+    with open(os.path.join(GOLDEN, "score_keys_by_hand.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            dt, v, k = line.split()
+            out.append((dt, np.float32(float(v)), int(k, 16)))
+    return out
+
+
+def torch_e4m3_decode(codes) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+
+
+_FP16_POS = None
+
+
+def _fp16_positive_values():
+    """Exact values of all finite non-negative fp16 encodings 0x0000..0x7BFF."""
+    global _FP16_POS
+    if _FP16_POS is None:
+        vals = []
+        for bits in range(0x7C00):
+            e, m = bits >> 10, bits & 0x3FF
+            if e == 0:
+                vals.append(Fraction(m, 1 << 24))
+            else:
+                vals.append(Fraction(1024 + m, 1024) * Fraction(2) ** (e - 15))
+        _FP16_POS = vals
+    return _FP16_POS
+
+
+def fraction_rne_fp16_bits(x: float) -> int:
+    """IEEE binary16 round-to-nearest-even of a finite double, by exact search."""
+    vals = _fp16_positive_values()
+    sign = 0x8000 if math.copysign(1.0, x) < 0 else 0
+    a = abs(Fraction(x))
+    if a >= Fraction(65520):
+        return sign | 0x7C00
+    i = bisect.bisect_left(vals, a)
+    if i < len(vals) and vals[i] == a:
+        return sign | i
+    lo, hi = i - 1, i
+    if hi >= len(vals):
+        return sign | lo
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    if dlo < dhi:
+        return sign | lo
+    if dhi < dlo:
+        return sign | hi
+    return sign | (lo if lo % 2 == 0 else hi)
+
+
+# ------------------------------------------------------------------- pins --
+def pin_e4m3(O):
+    fails = []
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.decode_e4m3fn(codes)
+    ref = torch_e4m3_decode(codes)
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    if not np.array_equal(nan_g, nan_r):
+        fails.append("e4m3 NaN codes differ from torch float8_e4m3fn")
+    ok = ~nan_r
+    if not np.array_equal(got[ok], ref[ok]):
+        fails.append("e4m3 values differ from torch float8_e4m3fn")
+    spot = {0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x38: 1.0,
+            0xFE: -448.0, 0x07: 7 * 2.0 ** -9}
+    for c, v in spot.items():
+        if got[c] != v:
+            fails.append(f"e4m3 code {c:#x} -> {got[c]}, spec says {v}")
+    if not (np.isnan(got[0x7F]) and np.isnan(got[0xFF])):
+        fails.append("e4m3 0x7F/0xFF must be NaN")
+    if not (got[0x80] == 0 and math.copysign(1, got[0x80]) < 0):
+        fails.append("e4m3 0x80 must be -0")
+    return fails
+
+
+def pin_fp16_rne(O, n_random=20000, seed=7):
+    fails = []
+    # every fp16 value round-trips
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = ~np.isnan(allh)
+    back = O.fp16_rne(allh[fin].astype(np.float32)).view(np.uint16)
+    if not np.array_equal(back, allh[fin].view(np.uint16)):
+        fails.append("fp16_rne does not round-trip fp16 values")
+    # midpoints between adjacent non-negative fp16 values, and +-1 fp32 ulp
+    vals = _fp16_positive_values()
+    mids = np.array([float((vals[i] + vals[i + 1]) / 2) for i in range(len(vals) - 1)]
+                    + [65520.0], dtype=np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, 0x7F800000, n_random, dtype=np.uint32).view(np.float32)
+    probe = np.concatenate([mids, up, dn, rnd, -mids[::97], -rnd[::7]])
+    got = O.fp16_rne(probe).view(np.uint16).astype(np.int64)
+    want = np.array([fraction_rne_fp16_bits(float(v)) for v in probe], dtype=np.int64)
+    bad = np.nonzero(got != want)[0]
+    if bad.size:
+        v = probe[bad[0]]
+        fails.append(f"fp16_rne({v!r}) = {got[bad[0]]:#06x}, exact RNE {want[bad[0]]:#06x}"
+                     f" ({bad.size} mismatches)")
+    return fails
+
+
+def pin_bins_golden(O):
+    vals, bins = load_golden_bins()
+    got = O.coarse_bin(vals)
+    bad = np.nonzero(got != bins)[0]
+    return [f"bin({vals[i]!r}) = {got[i]}, hand-derived {bins[i]}" for i in bad]
+
+
+def pin_bins_exhaustive(O):
+    """All 65,536 fp16 encodings: NaN excluded, order, closed-form populations."""
+    fails = []
+    enc = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = enc.view(np.float16).astype(np.float32)
+    b = O.coarse_bin(x)
+    nan = np.isnan(x)
+    if not np.all(b[nan] == -1):
+        fails.append("NaN encodings must get no bin")
+    if np.any((b[~nan] < 0) | (b[~nan] > 1023)):
+        fails.append("bins outside 0..1023")
+    # non-increasing in value; -0 sorts below +0
+    v = x[~nan].astype(np.float64)
+    neg = np.signbit(x[~nan])
+    order = np.lexsort((~neg, v))
+    bs = b[~nan][order]
+    if np.any(np.diff(bs) > 0):
+        fails.append("bin is not non-increasing in the score")
+    counts = np.bincount(b[~nan], minlength=1024)
+    expect = np.zeros(1024, dtype=np.int64)
+    for m in range(512):
+        if m < 304:
+            c = 64
+        elif m < 511:
+            k = m - 288
+            c = 2 ** (10 - int(math.floor(math.log2(k))))
+        else:
+            c = 0x7C00 - 0x5AF8 + 1  # encodings of 223.0 .. +inf
+        expect[511 - m] = c
+        expect[512 + m] = c
+    if not np.array_equal(counts, expect):
+        d = np.nonzero(counts != expect)[0]
+        fails.append(f"bin populations differ from closed form at bins {d[:8]}")
+    # fine regime equals the reversed 10-bit fp16 coarse key
+    mag = np.abs(x)
+    fine = (~nan) & (mag < 16)
+    k16 = np.where(enc >> 15 == 1, (~enc.astype(np.uint32)) & 0xFFFF,
+                   enc.astype(np.uint32) | 0x8000)
+    if not np.array_equal(b[fine], 1023 - (k16[fine] >> 6)):
+        fails.append("fine regime is not the reversed 10-bit fp16 coarse key")
+    return fails
+
+
+def pin_keys(O):
+    with np.errstate(over="ignore", invalid="ignore"):
+        return _pin_keys(O)
+
+
+def _pin_keys(O):
+    fails = []
+    for dt, v, k in load_golden_keys():
+        kd = O.KEY_FP32 if dt == "fp32" else O.KEY_FP16
+        got = int(O.score_keys(np.array([v], np.float32), kd)[0])
+        if got != k:
+            fails.append(f"{dt} key({v!r}) = {got:#x}, hand-derived {k:#x}")
+    # integer order of keys is the value order (-0 below +0), both dtypes
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(3000).astype(np.float32) * 50,
+                        np.array([0.0, -0.0, np.inf, -np.inf, 1e-30, -1e-30,
+                                  65519.0, 65521.0, -65521.0], np.float32)])
+    for kd, val in ((O.KEY_FP32, x.astype(np.float64)),
+                    (O.KEY_FP16, x.astype(np.float16).astype(np.float64))):
+        keys = O.score_keys(x, kd).astype(np.float64)
+        neg = np.signbit(x if kd == O.KEY_FP32 else x.astype(np.float16))
+        order = np.lexsort((~neg, val))
+        ks = keys[order]
+        if np.any(np.diff(ks) < 0):
+            fails.append(f"keys (dtype {kd}) do not follow the value order")
+        same = (np.diff(val[order]) == 0) & (np.diff(neg[order].astype(int)) == 0)
+        if np.any(np.diff(ks)[same] != 0):
+            fails.append(f"equal values get different keys (dtype {kd})")
+    return fails
+
+
+def pin_bins_coarsen_keys(O, seed=5):
+    """bin(x) < bin(y) implies key(x) > key(y), for FP32 and FP16 keys."""
+    rng = np.random.default_rng(seed)
+    vals, _ = load_golden_bins()
+    x = np.concatenate([vals[~np.isnan(vals)],
+                        (rng.standard_normal(4000) * 80).astype(np.float32),
+                        (rng.standard_normal(2000) * 4).astype(np.float32)])
+    b = O.coarse_bin(x)
+    fails = []
+    for kd in (O.KEY_FP32, O.KEY_FP16):
+        k = O.score_keys(x, kd).astype(np.float64)
+        # within increasing bins, max key of a later bin < min key of an earlier
+        ub = np.unique(b)
+        mins = np.array([k[b == u].min() for u in ub])
+        maxs = np.array([k[b == u].max() for u in ub])
+        if np.any(maxs[1:] >= mins[:-1]):
+            fails.append(f"bins do not coarsen the key order (dtype {kd})")
+    return fails
+
+
+def pin_histogram(O, seed=3):
+    fails = []
+    rng = np.random.default_rng(seed)
+    rows, n = 5, 3000
+    x = (rng.standard_normal((rows, n)) * rng.choice([0.5, 8, 90], (rows, 1))
+         ).astype(np.float32)
+    x[0, 10:20] = np.nan
+    x[1, :5] = [np.inf, -np.inf, 0.0, -0.0, np.nan]
+    lens = np.array([n, n - 7, 100, 0, 2999], dtype=np.int32)
+    pad_val = np.float32(1e30)  # would land in bin 0
+    for r in range(rows):
+        x[r, lens[r]:] = pad_val
+    h = O.coarse_histogram(x, lens)
+    live = np.array([np.sum(~np.isnan(x[r, :lens[r]])) for r in range(rows)])
+    if not np.array_equal(h.sum(axis=1), live):
+        fails.append("histogram total != live non-NaN count")
+    h2 = O.coarse_histogram(x, lens, hist_in=h)
+    if not np.array_equal(h2, 2 * h):
+        fails.append("histogram does not accumulate onto the incoming counts")
+    x2 = x.copy()
+    for r in range(rows):
+        x2[r, lens[r]:] = -pad_val
+    if not np.array_equal(O.coarse_histogram(x2, lens), h):
+        fails.append("padding columns change the histogram")
+    # brute force on one short row with the hand-checked bin values
+    vals, bins = load_golden_bins()
+    hv = O.coarse_histogram(vals[None, :], np.array([vals.size], np.int32))[0]
+    want = np.zeros(1024, np.int64)
+    for bb in bins:
+        if bb >= 0:
+            want[bb] += 1
+    if not np.array_equal(hv, want):
+        fails.append("histogram of the hand-derived values is wrong")
+    return fails
+
+
+def _brute_topk(x, length, k, key_dtype):
+    """Top-k by sorted() with an explicit comparator, no oracle code."""
+    items = []
+    for i in range(length):
+        v = float(x[i])
+        if math.isnan(v):
+            continue
+        if key_dtype == 1:
+            v = float(np.float16(np.float32(x[i])))
+        positive_zero_first = 0 if math.copysign(1.0, v) > 0 else 1
+        items.append((-v, positive_zero_first, i))
+    items.sort()
+    return sorted(i for _, _, i in items[:k])
+
+
+def pin_topk(O, seed=9):
+    fails = []
+    rng = np.random.default_rng(seed)
+    cases = []
+    for n, k in ((50, 7), (300, 64), (1000, 1000), (257, 300), (2048, 100)):
+        x = (rng.standard_normal(n) * 3).astype(np.float32)
+        x[rng.integers(0, n, n // 10)] = np.float32(1.5)  # fp32 ties
+        x[rng.integers(0, n, 3)] = np.nan
+        x[rng.integers(0, n, 2)] = np.inf
+        x[rng.integers(0, n, 2)] = -0.0
+        x[rng.integers(0, n, 2)] = 0.0
+        cases.append((x, n - 3, k))
+    # many fp32 values sharing one fp16 value
+    y = (np.float32(20.0) + rng.integers(0, 8, 600).astype(np.float32)
+         * np.float32(2.0 ** -10)).astype(np.float32)
+    cases.append((y, 600, 37))
+    for x, length, k in cases:
+        for kd in (O.KEY_FP32, O.KEY_FP16):
+            got = list(O.topk_row(x, length, k, kd))
+            want = _brute_topk(x, length, k, kd)
+            if got != want:
+                fails.append(f"top-{k} of a length-{length} row (dtype {kd}) "
+                             f"differs from brute force")
+    # special cases with known answers
+    n, k = 500, 64
+    const = np.full(n, 2.5, np.float32)
+    if list(O.topk_row(const, n, k, O.KEY_FP32)) != list(range(k)):
+        fails.append("constant row must select the lowest k indices")
+    inc = np.arange(n, dtype=np.float32)
+    if list(O.topk_row(inc, n, k, O.KEY_FP32)) != list(range(n - k, n)):
+        fails.append("increasing row must select the last k indices")
+    nan = np.full(n, np.nan, np.float32)
+    out = O.topk_rows(nan[None, :], np.array([n], np.int32), k, O.KEY_FP32)
+    if not np.all(out == -1):
+        fails.append("all-NaN row must give only -1")
+    short = O.topk_rows(inc[None, :], np.array([10], np.int32), k, O.KEY_FP32)[0]
+    if list(short[:10]) != list(range(10)) or not np.all(short[10:] == -1):
+        fails.append("a row with fewer live scores than k selects all, then -1")
+    return fails
+
+
+def pin_topk_invariants(O, seed=13):
+    fails = []
+    rng = np.random.default_rng(seed)
+    for _ in range(6):
+        n = int(rng.integers(3000, 9000))
+        k = int(rng.integers(1, 2500))
+        x = (rng.standard_normal(n) * rng.choice([1, 30, 300])).astype(np.float32)
+        x[rng.integers(0, n, 50)] = np.float32(x[0])
+        for kd in (O.KEY_FP32, O.KEY_FP16):
+            sel = O.topk_row(x, n, k, kd)
+            keys = O.score_keys(x, kd).astype(np.int64)
+            mask = np.zeros(n, bool)
+            mask[sel] = True
+            if sel.size != min(k, n) or np.unique(sel).size != sel.size:
+                fails.append("selected set has the wrong size")
+                continue
+            if mask.all():
+                continue
+            t = keys[mask].min()
+            if keys[~mask].max() > t:
+                fails.append("an unselected score outranks a selected one")
+            tie_out = np.nonzero((~mask) & (keys == t))[0]
+            tie_in = np.nonzero(mask & (keys == t))[0]
+            if tie_out.size and tie_in.size and tie_out.min() < tie_in.max():
+                fails.append("ties not broken by the lower index")
+    return fails
+
+
+def _tiny_logit_inputs(seed=21, B=2, next_n=2, base=70, weight_scale=1.0):
+    import gen
+    return gen.make_indexer_inputs("tiny", B, next_n, [base + 3 * b for b in range(B)],
+                                   seed, weight_scale=weight_scale)
+
+
+def pin_logits_exact(O, n_cols=6):
+    """The whole formula in exact rationals, rounded once to float32."""
+    fails = []
+    x = _tiny_logit_inputs()
+    got = O.indexer_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                           x.context_lens, x.next_n, x.logits_stride)
+    rng = np.random.default_rng(1)
+    for r in range(x.rows):
+        b = r // x.next_n
+        n = int(x.context_lens[r])
+        qd = torch_e4m3_decode(x.q[r])
+        cols = sorted(set(rng.integers(0, n, n_cols).tolist()) | {0, n - 1})
+        for s in cols:
+            page = int(x.block_table[b, s // 64])
+            slot = s % 64
+            kd = torch_e4m3_decode(x.kv_pages[page, slot])
+            sc = Fraction(float(x.k_scales[page, slot]))
+            total = Fraction(0)
+            for h in range(32):
+                dot = sum((Fraction(float(qd[h, d])) * Fraction(float(kd[d]))
+                           for d in range(128)), Fraction(0))
+                if dot > 0:
+                    total += Fraction(float(x.weights[r, h])) * dot
+            want = np.float32(float(sc * total))
+            g = got[r, s]
+            ulp = np.spacing(np.float32(abs(want))) if want != 0 else np.float32(1e-45)
+            if not abs(float(g) - float(want)) <= float(ulp):
+                fails.append(f"logit[{r},{s}] = {g}, exact {want}")
+        if not np.all(np.isnan(got[r, n:])):
+            fails.append(f"row {r}: columns past the length were written")
+    return fails
+
+
+def pin_logits_library(O):
+    """Unit weights and scales, one page: sum_h ReLU(Q K^T) by a numpy matmul."""
+    import gen
+    x = gen.make_indexer_inputs("lib", 1, 1, [64], 31)
+    x.weights[:] = 1.0
+    x.k_scales[:] = 1.0
+    got = O.indexer_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                           x.context_lens, 1, 64)
+    page = int(x.block_table[0, 0])
+    qd = torch_e4m3_decode(x.q[0])
+    kd = torch_e4m3_decode(x.kv_pages[page])
+    want = np.maximum(np.matmul(qd, kd.T), 0).sum(axis=0).astype(np.float32)
+    if not np.array_equal(got[0], want):
+        return ["unit-weight one-page logits differ from sum_h ReLU(Q K^T)"]
+    return []
+
+
+def pin_logits_paging(O):
+    """Permuting physical pages together with the block table changes nothing."""
+    x = _tiny_logit_inputs(seed=23, B=3, next_n=2, base=150)
+    a = O.indexer_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                         x.context_lens, x.next_n, x.logits_stride)
+    perm = np.random.default_rng(2).permutation(x.num_pages)
+    inv = np.argsort(perm)
+    kv2 = x.kv_pages[perm]
+    sc2 = x.k_scales[perm]
+    bt2 = inv[x.block_table].astype(np.int32)
+    bt2[x.block_table < 0] = 0
+    b = O.indexer_logits(x.q, kv2, sc2, x.weights, bt2, x.context_lens,
+                         x.next_n, x.logits_stride)
+    if not np.array_equal(a, b, equal_nan=True):
+        return ["logits change when pages are permuted with the block table"]
+    return []
+
+
+def pin_error_bound(O):
+    """An fp32 evaluation of the formula sits inside the bound; 3x bound fails."""
+    fails = []
+    x = _tiny_logit_inputs(seed=25, B=1, next_n=1, base=200, weight_scale=3.0)
+    want = O.indexer_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                            x.context_lens, 1, x.logits_stride)[0]
+    cols = np.arange(200)
+    bound = O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                    x.block_table, 1, 0, cols)
+    qd = torch_e4m3_decode(x.q[0]).astype(np.float32)
+    pages = x.block_table[0, cols // 64]
+    kd = torch_e4m3_decode(x.kv_pages[pages, cols % 64]).astype(np.float32)
+    sc = x.k_scales[pages, cols % 64]
+    # sequential float32 accumulation, vectorised over the 200 keys
+    acc = np.zeros(200, np.float32)
+    for h in range(32):
+        dot = np.zeros(200, np.float32)
+        for d in range(128):
+            dot = (dot + qd[h, d] * kd[:, d]).astype(np.float32)
+        acc = (acc + x.weights[0, h] * np.maximum(dot, np.float32(0))).astype(np.float32)
+    f32 = (acc * sc).astype(np.float32)
+    if not np.all(O.check_logits(f32, want, bound)):
+        fails.append("a plain fp32 evaluation falls outside the tolerance")
+    bad = want + 3 * bound.astype(np.float32)
+    moved = 3 * bound > np.spacing(np.abs(want))
+    if np.any(O.check_logits(bad, want, bound)[moved]):
+        fails.append("a 3x-bound error is accepted")
+    return fails
+
+
+ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_bins_golden, pin_bins_exhaustive,
+            pin_keys, pin_bins_coarsen_keys, pin_histogram, pin_topk,
+            pin_topk_invariants, pin_logits_exact, pin_logits_library,
+            pin_logits_paging, pin_error_bound)

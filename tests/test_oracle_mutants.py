@@ -1,0 +1,230 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU)
+and require the pins to catch it, so that passing pins mean something."""
+import importlib.util
+import math
+
+import numpy as np
+import pytest
+
+import oracle.indexer_oracle as base
+from tests import oracle_pins as P
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("oracle_mutant", base.__file__)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+# ---- mutations: each takes a fresh oracle module and breaks one thing ----
+def m_e4m3_bias(O):
+    t = O.E4M3FN.copy()
+    t[np.isfinite(t)] *= 0.5  # exponent bias 8 instead of 7
+    O.decode_e4m3fn = lambda c: t[np.asarray(c, dtype=np.uint8)]
+
+
+def m_e4m3_subnormal(O):
+    t = O.E4M3FN.copy()
+    for c in range(256):
+        if (c >> 3) & 0xF == 0 and c & 7:
+            s = -1 if c >> 7 else 1
+            t[c] = s * (1 + (c & 7) / 8) * 2.0 ** -7
+    O.decode_e4m3fn = lambda c: t[np.asarray(c, dtype=np.uint8)]
+
+
+def _wrap_bin(O, fn):
+    orig = O.coarse_bin
+    O.coarse_bin = lambda x: fn(np.asarray(x, np.float32), orig(x))
+
+
+def m_bin_sign_swapped(O):
+    _wrap_bin(O, lambda x, b: np.where(b >= 0, 1023 - b, b))
+
+
+def m_bin_unit_off_by_one(O):
+    def f(x, b):
+        a = np.abs(O.fp16_rne(x).astype(np.float64))
+        unit = (a >= 16) & (a < 223)
+        return np.where(unit, np.where(b < 512, b + 1, b - 1), b)
+    _wrap_bin(O, f)
+
+
+def m_bin_fine_shift7(O):
+    def f(x, b):
+        h = O.fp16_rne(x)
+        bits = h.view(np.uint16).astype(np.int64)
+        a = np.abs(h.astype(np.float64))
+        m = (bits & 0x7FFF) >> 7
+        alt = np.where(bits >> 15 == 1, 512 + m, 511 - m)
+        return np.where((a < 16) & (b >= 0), alt, b)
+    _wrap_bin(O, f)
+
+
+def m_bin_saturate_224(O):
+    def f(x, b):
+        a = np.abs(O.fp16_rne(x).astype(np.float64))
+        edge = (a >= 223) & (a < 224)
+        return np.where(edge, np.where(b < 512, 1, 1022), b)
+    _wrap_bin(O, f)
+
+
+def m_bin_regimes_on_fp32(O):
+    def f(x, b):
+        a = np.abs(x.astype(np.float64))
+        with np.errstate(invalid="ignore"):
+            lit = (a >= 16) & (a < 223)
+            m = 288 + np.floor(np.where(lit, a, 0)).astype(np.int64)
+        alt = np.where(np.signbit(x), 512 + m, 511 - m)
+        return np.where(lit & (b >= 0), alt, b)
+    _wrap_bin(O, f)
+
+
+def m_fp16_truncate(O):
+    def trunc(x):
+        x = np.asarray(x, dtype=np.float32)
+        h = x.astype(np.float16)
+        hv = h.astype(np.float32)
+        over = np.abs(hv) > np.abs(x)  # rounded away from zero
+        bits = h.view(np.uint16).astype(np.int32)
+        bits = np.where(over & np.isfinite(x), bits - 1, bits)  # one step back
+        return bits.astype(np.uint16).view(np.float16)
+    O.fp16_rne = trunc
+
+
+def m_logits_no_relu(O):
+    def row(q_row, w_row, keys, scales):
+        qd = O.decode_e4m3fn(q_row)
+        with np.errstate(invalid="ignore", over="ignore"):
+            return (scales * (w_row.astype(np.float64) @ (qd @ keys.T))).astype(np.float32)
+    O._row_logits = row
+
+
+def m_logits_no_scale(O):
+    orig = O._row_logits
+    O._row_logits = lambda q, w, k, s: orig(q, w, k, np.ones_like(s))
+
+
+def m_logits_heads_reversed(O):
+    orig = O._row_logits
+    O._row_logits = lambda q, w, k, s: orig(q, w[::-1].copy(), k, s)
+
+
+def m_gather_page_slot_swapped(O):
+    def keys_at(kv_pages, k_scales, bt_row, cols):
+        cols = np.asarray(cols, dtype=np.int64)
+        pages = np.asarray(bt_row, dtype=np.int64)[cols % 64]
+        slots = cols // 64
+        return O.decode_e4m3fn(kv_pages[pages, slots % 64]), \
+            k_scales[pages, slots % 64].astype(np.float64)
+    O._request_keys_at = keys_at
+
+
+def m_gather_logical_page(O):
+    def keys_at(kv_pages, k_scales, bt_row, cols):
+        cols = np.asarray(cols, dtype=np.int64)
+        pages = cols // 64  # ignores the block table
+        return O.decode_e4m3fn(kv_pages[pages, cols % 64]), \
+            k_scales[pages, cols % 64].astype(np.float64)
+    O._request_keys_at = keys_at
+
+
+def m_topk_ties_high(O):
+    def row(x, length, k, key_dtype):
+        x = np.asarray(x, dtype=np.float32)[:length]
+        cols = np.nonzero(~np.isnan(x))[0]
+        keys = O.score_keys(x[cols], key_dtype)
+        order = np.lexsort((-cols, -keys.astype(np.float64)))
+        return np.sort(cols[order[:min(k, cols.size)]])
+    O.topk_row = row
+
+
+def m_topk_keeps_nan(O):
+    def row(x, length, k, key_dtype):
+        x = np.asarray(x, dtype=np.float32)[:length]
+        cols = np.arange(x.size)
+        keys = O.score_keys(x, key_dtype)
+        order = np.lexsort((cols, -keys.astype(np.float64)))
+        return np.sort(cols[order[:min(k, cols.size)]])
+    O.topk_row = row
+
+
+def m_topk_ignores_length(O):
+    orig = O.topk_row
+    O.topk_row = lambda x, length, k, kd: orig(x, len(x), k, kd)
+
+
+def m_hist_counts_padding(O):
+    orig = O.coarse_histogram
+    O.coarse_histogram = lambda lg, lens, hist_in=None: orig(
+        lg, np.full(len(lens), np.asarray(lg).shape[1]), hist_in)
+
+
+def m_hist_drops_incoming(O):
+    orig = O.coarse_histogram
+    O.coarse_histogram = lambda lg, lens, hist_in=None: orig(lg, lens)
+
+
+def m_keys_negatives_not_inverted(O):
+    orig = O.score_keys
+
+    def keys(x, kd):
+        x = np.asarray(x, dtype=np.float32)
+        if kd == O.KEY_FP32:
+            return (x.view(np.uint32).astype(np.uint64) | 0x80000000)
+        return orig(x, kd)
+    O.score_keys = keys
+
+
+def m_keys_zero_signs_equal(O):
+    orig = O.score_keys
+
+    def keys(x, kd):
+        x = np.asarray(x, dtype=np.float32).copy()
+        x[x == 0] = 0.0
+        return orig(x, kd)
+    O.score_keys = keys
+
+
+MUTANTS = [
+    (m_e4m3_bias, [P.pin_e4m3]),
+    (m_e4m3_subnormal, [P.pin_e4m3]),
+    (m_bin_sign_swapped, [P.pin_bins_golden]),
+    (m_bin_unit_off_by_one, [P.pin_bins_golden, P.pin_bins_exhaustive]),
+    (m_bin_fine_shift7, [P.pin_bins_golden, P.pin_bins_exhaustive]),
+    (m_bin_saturate_224, [P.pin_bins_golden, P.pin_bins_exhaustive]),
+    (m_bin_regimes_on_fp32, [P.pin_bins_golden]),
+    (m_fp16_truncate, [P.pin_fp16_rne]),
+    (m_logits_no_relu, [P.pin_logits_exact, P.pin_logits_library]),
+    (m_logits_no_scale, [P.pin_logits_exact]),
+    (m_logits_heads_reversed, [P.pin_logits_exact]),
+    (m_gather_page_slot_swapped, [P.pin_logits_exact, P.pin_logits_paging]),
+    (m_gather_logical_page, [P.pin_logits_exact, P.pin_logits_paging]),
+    (m_topk_ties_high, [P.pin_topk, P.pin_topk_invariants]),
+    (m_topk_keeps_nan, [P.pin_topk]),
+    (m_topk_ignores_length, [P.pin_topk]),
+    (m_hist_counts_padding, [P.pin_histogram]),
+    (m_hist_drops_incoming, [P.pin_histogram]),
+    (m_keys_negatives_not_inverted, [P.pin_keys]),
+    (m_keys_zero_signs_equal, [P.pin_keys]),
+]
+
+
+@pytest.mark.parametrize("mutate,pins", MUTANTS, ids=[m.__name__ for m, _ in MUTANTS])
+def test_pins_catch_planted_mistake(mutate, pins):
+    O = fresh_oracle()
+    mutate(O)
+    fails = []
+    for pin in pins:
+        with np.errstate(all="ignore"):
+            try:
+                fails += pin(O)
+            except Exception as e:  # a crash is also a caught mistake
+                fails.append(f"{pin.__name__} raised {type(e).__name__}: {e}")
+    assert fails, f"no pin caught {mutate.__name__}"
+
+
+def test_fresh_copy_passes():
+    O = fresh_oracle()
+    assert not P.pin_bins_golden(O)
+    assert math.isnan(O.E4M3FN[0x7F])
