@@ -1,0 +1,188 @@
+/*
+ * paged_mqa_indexer.h -- C ABI of the MI355X (gfx950) paged MQA indexer.
+ *
+ * The decode-time sparse-attention indexer: for every query row it scores all
+ * live keys of its request through a paged FP8 K cache, emits a 1024-bin
+ * coarse histogram of those scores while they are still in registers, and a
+ * selector then picks the top-k columns of each row from that histogram's
+ * threshold bin plus a radix refine on the remaining key bits.
+ *
+ * Sources:
+ *   [P1] DeepGEMM PR #94, "[SM100] Paged MQA logits: fused coarse score
+ *        histogram for LiteTopK decode": "Motivation"; "What this adds"
+ *        (histogram argument and contract, bin regimes, per-token slots
+ *        flushed with packed 64-bit atomics, token Q tile); SGLang commit
+ *        "Replace the CuTe DSL selector with a JIT CUDA selector; add verify"
+ *        (exact top-2048 selector from the histogram, fallback, ties).
+ *   [P3] vLLM PR #52696, "[Performance][MLA] Use FP16 logits for sparse
+ *        indexer": "Summary" and commits (selection on FP16 score keys,
+ *        refining only the remaining key bits).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are device memory on the current HIP device;
+ *     the library never dereferences them on the host and never copies them.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call only enqueues kernels on it and returns; nothing is synchronised,
+ *     allocated or freed, and no pointer is kept after the call returns, so
+ *     the calls can be captured into a HIP graph.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     failed check returns its status and enqueues nothing.  Device-resident
+ *     values (lengths, page ids, histogram counts) cannot be checked on the
+ *     host; the kernels clamp them so that no access leaves its buffer, and
+ *     the results for out-of-contract values are unspecified.
+ *   - The buffers belong to the caller throughout.
+ */
+#ifndef PAGED_MQA_INDEXER_H
+#define PAGED_MQA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+typedef enum {
+  IDX_OK = 0,
+  IDX_EINVAL = 1,       /* null required pointer, non-positive size, k out of range   */
+  IDX_EUNSUPPORTED = 2, /* next_n outside 1..4, unknown key dtype, size above limits  */
+  IDX_EALIGN = 3,       /* a pointer or stride misses its required alignment          */
+  IDX_ELAUNCH = 4,      /* the HIP runtime rejected a launch or the device query      */
+  IDX_EWORKSPACE = 5    /* workspace smaller than topk_workspace_bytes()              */
+} idx_status;
+
+/* Score key used by topk_rows.  FP32: the float32 score itself.  FP16: the
+ * score rounded to IEEE binary16 (round to nearest even), so scores that round
+ * to the same FP16 value tie ([P3] Summary). */
+typedef enum { IDX_KEY_FP32 = 0, IDX_KEY_FP16 = 1 } idx_key_dtype;
+
+/* Fixed shape of the method ([P1] "What this adds": H = 32, D = 128). */
+#define IDX_NUM_HEADS 32
+#define IDX_HEAD_DIM 128
+#define IDX_PAGE_TOKENS 64
+#define IDX_NUM_BINS 1024
+#define IDX_CANDIDATE_CAPACITY 8192 /* [P1] SGLang commit: candidate_capacity */
+#define IDX_MAX_REQUESTS 4096
+#define IDX_MAX_ROWS 65535
+
+/*
+ * indexer_logits -- paged MQA logits with an optional fused coarse histogram.
+ * [P1] "Motivation", "What this adds".
+ *
+ * Rows: r = b * next_n + j for request b in [0, B) and token j in [0, next_n).
+ * Row r sees keys s in [0, len_r), len_r = context_lens[r] (speculative verify:
+ * token j of a request usually sees L + j keys).  Key s of request b lives in
+ * physical page block_table[b * max_pages + s / 64], slot s % 64.
+ *
+ *   logits[r * logits_stride + s] =
+ *       k_scales[page][slot] * sum_h weights[r*32 + h] * max(0, sum_d Q[r,h,d] * K[page,slot,d])
+ *
+ * with Q and K decoded from OCP FP8 E4M3FN, products summed in fp32.  Columns
+ * s >= len_r are not written (padding stays as the caller left it).  All
+ * next_n rows of a request are computed from one read of its K pages.
+ *
+ * q            (device) uint8 [B*next_n][32][128], E4M3FN codes, 16-B aligned
+ * kv_pages     (device) uint8 [num_pages][64][128], E4M3FN codes, 16-B aligned
+ * k_scales     (device) float [num_pages][64], one scale per token, 4-B aligned
+ * weights      (device) float [B*next_n][32], 16-B aligned
+ * block_table  (device) int32 [B][max_pages]; ids in [0, num_pages)
+ * context_lens (device) int32 [B*next_n]; 0 <= len_r <= min(max_pages*64, logits_stride)
+ * B            1 .. IDX_MAX_REQUESTS; next_n 1..4; B*next_n <= IDX_MAX_ROWS;
+ *              B*max_pages < 2^31
+ * logits       (device) float [B*next_n][logits_stride], 16-B aligned,
+ *              logits_stride > 0 and a multiple of 4
+ * hist         (device) int32 [B*next_n][1024] or NULL.  When given, every
+ *              live (s < len_r), non-NaN score adds 1 to bin(score) of its row;
+ *              counts accumulate across calls, so the caller zeroes the buffer
+ *              before the first call and resets it after consuming it.  Must
+ *              be 8-B aligned (pairs of bins are added with 64-bit atomics,
+ *              exact while every count stays below 2^31).  With hist == NULL
+ *              no histogram work runs, and the logits are bit-identical either way.
+ *
+ * bin(x), [P1] "What this adds" (descending, bin 0 = largest): h = fp16_RN(x),
+ *   a = |h|; m = (bits(h) & 0x7FFF) >> 6 if a < 16 (exponent + 4 mantissa bits),
+ *   m = 288 + floor(a) if 16 <= a < 223 (unit bins, same for both signs),
+ *   m = 511 if a >= 223 or inf (saturating); bin = 511 - m for a clear sign bit,
+ *   512 + m for a set one.
+ */
+idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
+                          const float* k_scales, const float* weights,
+                          const int32_t* block_table, const int32_t* context_lens,
+                          int32_t B, int32_t next_n, int32_t num_pages,
+                          int32_t max_pages, float* logits, int64_t logits_stride,
+                          int32_t* hist, void* stream);
+
+/*
+ * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
+ * `rows` rows (host-only query, no device work).  Returns 0 for rows <= 0.
+ */
+size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
+
+/*
+ * topk_rows -- exact per-row top-k of a score matrix.  [P1] SGLang commit
+ * (histogram-driven exact selector, fallback, lower index wins ties), [P1]
+ * "Motivation" (the selector's own first pass builds the histogram when the
+ * producer did not), [P3] Summary (FP16 keys, refining the remaining bits).
+ *
+ * For row r, the selectable columns are s < context_lens[r] whose score is not
+ * NaN.  The selected set is the first min(k, n_selectable) of them in the
+ * order (key descending, column ascending), where key is the score as FP32 or
+ * its fp16_RN value (key_dtype).  indices[r*k + 0 .. n-1] receive the set in
+ * unspecified order; indices[r*k + n .. k-1] receive -1.
+ *
+ * With hist != NULL (the producer's histogram of exactly these scores), the
+ * threshold bin is read from it: columns in higher bins are emitted directly,
+ * columns of the threshold bin become candidates (at most 8192 per row) that
+ * a radix select on the remaining key bits ranks.  The real counts found in
+ * the scores are checked against the threshold; a stale histogram, or a
+ * threshold bin with more than 8192 scores, makes that row fall back to an
+ * exact whole-row radix select -- the result is exact in every case.  With
+ * hist == NULL the histogram is first built from the scores.
+ *
+ * logits      (device) float [rows][logits_stride], 16-B aligned, stride % 4 == 0
+ * hist        (device) int32 [rows][1024] or NULL; read only
+ * context_lens(device) int32 [rows]; 0 <= len_r <= logits_stride
+ * rows        1 .. IDX_MAX_ROWS;  k in 1 .. IDX_CANDIDATE_CAPACITY
+ * key_dtype   IDX_KEY_FP32 or IDX_KEY_FP16
+ * indices     (device) int32 [rows][k]
+ * workspace   (device) scratch of at least topk_workspace_bytes(rows, ...) bytes,
+ *             256-B aligned; no initialisation needed; calls that share a
+ *             workspace must be ordered on one stream
+ */
+idx_status topk_rows(const float* logits, int64_t logits_stride,
+                     const int32_t* hist, const int32_t* context_lens,
+                     int32_t rows, int32_t k, int32_t key_dtype, int32_t* indices,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * score_histogram -- the selector's own first pass ([P1] "Motivation": the
+ * pass that builds the coarse histogram from the scores when the producer did
+ * not): adds bin(x) of every live (s < len_r), non-NaN score of each row to
+ * hist[r][*], with the same bin function as indexer_logits.
+ *
+ * scores       (device) float [rows][stride], 16-B aligned, stride % 4 == 0
+ * context_lens (device) int32 [rows]; 0 <= len_r <= stride
+ * rows         1 .. IDX_MAX_ROWS
+ * hist         (device) int32 [rows][1024], 8-B aligned; accumulated (+=)
+ */
+idx_status score_histogram(const float* scores, int64_t stride, const int32_t* context_lens,
+                           int32_t rows, int32_t* hist, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* indexer_status_str(int32_t status);
+
+/*
+ * hbm_read_probe -- measurement aid, not part of the method: streams `bytes`
+ * bytes (a multiple of 16) from `src` (device, 16-B aligned) with the same
+ * 16-B vector loads the logits kernel uses and writes one checksum word to
+ * *sink (device).  Its duration gives the practical HBM read ceiling that the
+ * logits kernel is compared with.
+ */
+idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_MQA_INDEXER_H */

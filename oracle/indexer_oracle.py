@@ -171,17 +171,20 @@ def indexer_logits_at(q, kv_pages, k_scales, weights, block_table, next_n, row,
 
 
 def logits_error_bound_at(q, kv_pages, k_scales, weights, block_table, next_n,
-                          row, cols, rel=1e-5):
+                          row, cols, rel=1e-5, unscaled=False):
     """Tolerance rel * sc_s * sum_h |w_h| * sum_d |q_hd * k_sd| (float64).
 
     The nested absolute sums bound every rounding a fp32 implementation of
-    the same formula makes, whatever its summation order.
+    the same formula makes, whatever its summation order.  ``unscaled`` leaves
+    out sc_s (the tolerance of the head sum itself).
     """
     b = row // next_n
     keys, sc = _request_keys_at(kv_pages, k_scales, block_table[b], cols)
     qd = np.abs(decode_e4m3fn(q[row]))
     abs_dots = qd @ np.abs(keys).T
     head = np.abs(weights[row].astype(np.float64)) @ abs_dots
+    if unscaled:
+        return rel * head
     with np.errstate(invalid="ignore", over="ignore"):
         return rel * np.abs(sc) * head
 

@@ -1,0 +1,235 @@
+"""Python binding of the MI355X paged MQA indexer C ABI (include/paged_mqa_indexer.h).
+
+Argument marshalling only: tensors are checked for dtype, device, shape and
+layout, their device pointers and the current HIP stream are handed to the C
+entry points of ``libpaged_mqa_indexer.so``, and a non-zero status raises
+``IndexerError``.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback path.  PyTorch only supplies device memory and
+streams.
+
+Entry points (same names as the C ABI):
+  indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens,
+                 next_n, logits, hist=None)
+  topk_workspace_bytes(rows, logits_stride, k)
+  topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None)
+  score_histogram(scores, context_lens, hist)
+  indexer_status_str(status)
+  hbm_read_probe(src, sink)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "IndexerError", "KEY_FP32", "KEY_FP16", "NUM_BINS", "CANDIDATE_CAPACITY",
+    "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits",
+    "topk_workspace_bytes", "topk_rows", "score_histogram", "indexer_status_str",
+    "hbm_read_probe",
+]
+
+KEY_FP32 = 0
+KEY_FP16 = 1
+NUM_BINS = 1024
+CANDIDATE_CAPACITY = 8192
+HEADS = 32
+HEAD_DIM = 128
+PAGE_TOKENS = 64
+
+EXPORTED_SYMBOLS = ("indexer_logits", "topk_workspace_bytes", "topk_rows",
+                    "score_histogram", "indexer_status_str", "hbm_read_probe")
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpaged_mqa_indexer.so"
+_lib = None
+
+
+class IndexerError(RuntimeError):
+    """A C entry point returned a non-zero idx_status."""
+
+    def __init__(self, func: str, status: int, msg: str):
+        super().__init__(f"{func} failed: {msg} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("PMQA_INDEXER_LIB", os.path.join(_PKG_DIR, _LIB_NAME))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is missing: build it with "
+            "`python -m paged_mqa_logits_indexer_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.indexer_logits.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp]
+    lib.indexer_logits.restype = ctypes.c_int
+    lib.topk_workspace_bytes.argtypes = [i32, i64, i32]
+    lib.topk_workspace_bytes.restype = sz
+    lib.topk_rows.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.topk_rows.restype = ctypes.c_int
+    lib.score_histogram.argtypes = [vp, i64, vp, i32, vp, vp]
+    lib.score_histogram.restype = ctypes.c_int
+    lib.indexer_status_str.argtypes = [i32]
+    lib.indexer_status_str.restype = ctypes.c_char_p
+    lib.hbm_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def indexer_status_str(status: int) -> str:
+    return load_library().indexer_status_str(int(status)).decode()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise IndexerError(func, status, indexer_status_str(status))
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens, next_n,
+                   logits, hist=None):
+    """Paged MQA logits (and histogram) on the current stream of q's device.
+
+    q [B*next_n, 32, 128] uint8 (e4m3fn codes); kv_pages [P, 64, 128] uint8;
+    k_scales [P, 64] float32; weights [B*next_n, 32] float32;
+    block_table [B, max_pages] int32; context_lens [B*next_n] int32;
+    logits [B*next_n, stride] float32 with unit column stride;
+    hist [B*next_n, 1024] int32 or None (accumulated into).
+    """
+    dev = q.device
+    _need(q, "q", torch.uint8, dev, 3)
+    _need(kv_pages, "kv_pages", torch.uint8, dev, 3)
+    _need(k_scales, "k_scales", torch.float32, dev, 2)
+    _need(weights, "weights", torch.float32, dev, 2)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    _need(logits, "logits", torch.float32, dev, 2)
+    B, max_pages = block_table.shape
+    rows = B * next_n
+    if tuple(q.shape) != (rows, HEADS, HEAD_DIM) or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous [{rows}, 32, 128]")
+    P = kv_pages.shape[0]
+    if tuple(kv_pages.shape) != (P, PAGE_TOKENS, HEAD_DIM) or not kv_pages.is_contiguous():
+        raise ValueError("kv_pages must be contiguous [P, 64, 128]")
+    if tuple(k_scales.shape) != (P, PAGE_TOKENS) or not k_scales.is_contiguous():
+        raise ValueError("k_scales must be contiguous [P, 64]")
+    if tuple(weights.shape) != (rows, HEADS) or not weights.is_contiguous():
+        raise ValueError(f"weights must be contiguous [{rows}, 32]")
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous")
+    if tuple(context_lens.shape) != (rows,) or not context_lens.is_contiguous():
+        raise ValueError(f"context_lens must be contiguous [{rows}]")
+    if logits.shape[0] != rows or logits.stride(1) != 1:
+        raise ValueError(f"logits must be [{rows}, stride] with unit column stride")
+    if hist is not None:
+        _need(hist, "hist", torch.int32, dev, 2)
+        if tuple(hist.shape) != (rows, NUM_BINS) or not hist.is_contiguous():
+            raise ValueError(f"hist must be contiguous [{rows}, 1024]")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.indexer_logits(
+            _ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(block_table),
+            _ptr(context_lens), int(B), int(next_n), int(P), int(max_pages), _ptr(logits),
+            int(logits.stride(0)), _ptr(hist), _stream_ptr(dev))
+    _check("indexer_logits", st)
+
+
+def topk_workspace_bytes(rows: int, logits_stride: int, k: int) -> int:
+    return int(load_library().topk_workspace_bytes(int(rows), int(logits_stride), int(k)))
+
+
+def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None):
+    """Exact per-row top-k indices into ``indices`` [rows, k] int32.
+
+    ``workspace`` is a uint8 GPU tensor of at least topk_workspace_bytes()
+    bytes; when None one is allocated with torch for this call.
+    """
+    dev = logits.device
+    _need(logits, "logits", torch.float32, dev, 2)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    _need(indices, "indices", torch.int32, dev, 2)
+    rows = logits.shape[0]
+    if logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    if tuple(context_lens.shape) != (rows,) or not context_lens.is_contiguous():
+        raise ValueError(f"context_lens must be contiguous [{rows}]")
+    if tuple(indices.shape) != (rows, k) or not indices.is_contiguous():
+        raise ValueError(f"indices must be contiguous [{rows}, {k}]")
+    if hist is not None:
+        _need(hist, "hist", torch.int32, dev, 2)
+        if tuple(hist.shape) != (rows, NUM_BINS) or not hist.is_contiguous():
+            raise ValueError(f"hist must be contiguous [{rows}, 1024]")
+    need = topk_workspace_bytes(rows, logits.stride(0), k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.topk_rows(_ptr(logits), int(logits.stride(0)), _ptr(hist), _ptr(context_lens),
+                           int(rows), int(k), int(key_dtype), _ptr(indices), _ptr(workspace),
+                           int(workspace.numel()), _stream_ptr(dev))
+    _check("topk_rows", st)
+
+
+def score_histogram(scores, context_lens, hist):
+    """Add the coarse bins of every live non-NaN score of each row to ``hist``."""
+    dev = scores.device
+    _need(scores, "scores", torch.float32, dev, 2)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    _need(hist, "hist", torch.int32, dev, 2)
+    rows = scores.shape[0]
+    if scores.stride(1) != 1:
+        raise ValueError("scores must have unit column stride")
+    if tuple(context_lens.shape) != (rows,) or not context_lens.is_contiguous():
+        raise ValueError(f"context_lens must be contiguous [{rows}]")
+    if tuple(hist.shape) != (rows, NUM_BINS) or not hist.is_contiguous():
+        raise ValueError(f"hist must be contiguous [{rows}, 1024]")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.score_histogram(_ptr(scores), int(scores.stride(0)), _ptr(context_lens),
+                                 int(rows), _ptr(hist), _stream_ptr(dev))
+    _check("score_histogram", st)
+
+
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream all bytes of ``src`` (contiguous GPU tensor) once; checksum to sink."""
+    if src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    _need(sink, "sink", torch.int32, src.device)
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    with torch.cuda.device(src.device):
+        st = lib.hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink),
+                                _stream_ptr(src.device))
+    _check("hbm_read_probe", st)

@@ -1,0 +1,107 @@
+// C ABI of the paged MQA indexer: host-side argument checks, then launches.
+// Every check runs before anything is enqueued; see paged_mqa_indexer.h.
+#include "indexer_common.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+idx_status from_hip(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* indexer_status_str(int32_t s) {
+  switch (s) {
+    case IDX_OK: return "IDX_OK";
+    case IDX_EINVAL: return "IDX_EINVAL: invalid argument";
+    case IDX_EUNSUPPORTED: return "IDX_EUNSUPPORTED: unsupported configuration";
+    case IDX_EALIGN: return "IDX_EALIGN: misaligned pointer or stride";
+    case IDX_ELAUNCH: return "IDX_ELAUNCH: HIP launch or device query failed";
+    case IDX_EWORKSPACE: return "IDX_EWORKSPACE: workspace too small";
+    default: return "unknown status";
+  }
+}
+
+idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                          const float* weights, const int32_t* block_table,
+                          const int32_t* context_lens, int32_t B, int32_t next_n,
+                          int32_t num_pages, int32_t max_pages, float* logits,
+                          int64_t logits_stride, int32_t* hist, void* stream) {
+  if (!q || !kv_pages || !k_scales || !weights || !block_table || !context_lens || !logits)
+    return IDX_EINVAL;
+  if (B <= 0 || num_pages <= 0 || max_pages <= 0 || logits_stride <= 0) return IDX_EINVAL;
+  if (next_n < 1 || next_n > 4) return IDX_EUNSUPPORTED;
+  if (B > IDX_MAX_REQUESTS || static_cast<int64_t>(B) * next_n > IDX_MAX_ROWS) return IDX_EUNSUPPORTED;
+  // The page list of all requests is indexed with 32-bit integers.
+  if (static_cast<int64_t>(B) * max_pages > INT32_MAX) return IDX_EUNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(weights, 16) || !aligned(k_scales, 4) ||
+      !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(logits, 16) ||
+      (logits_stride % 4) != 0 || (hist && !aligned(hist, 8)))
+    return IDX_EALIGN;
+  pmqa::LogitsArgs a;
+  a.q = q;
+  a.kv_pages = kv_pages;
+  a.k_scales = k_scales;
+  a.weights = weights;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.logits = logits;
+  a.hist = hist;
+  a.logits_stride = logits_stride;
+  a.B = B;
+  a.next_n = next_n;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  return from_hip(pmqa::launch_indexer_logits(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
+  (void)logits_stride;
+  (void)k;
+  return pmqa::topk_workspace_size(rows);
+}
+
+idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* hist,
+                     const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
+                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !context_lens || !indices || !workspace) return IDX_EINVAL;
+  if (rows <= 0 || logits_stride <= 0 || k < 1 || k > IDX_CANDIDATE_CAPACITY) return IDX_EINVAL;
+  if (key_dtype != IDX_KEY_FP32 && key_dtype != IDX_KEY_FP16) return IDX_EUNSUPPORTED;
+  if (rows > IDX_MAX_ROWS || logits_stride > (int64_t{1} << 31) - 4) return IDX_EUNSUPPORTED;
+  if (!aligned(logits, 16) || (logits_stride % 4) != 0 || !aligned(context_lens, 4) ||
+      !aligned(indices, 4) || !aligned(workspace, 256) || (hist && !aligned(hist, 8)))
+    return IDX_EALIGN;
+  if (workspace_bytes < pmqa::topk_workspace_size(rows)) return IDX_EWORKSPACE;
+  pmqa::TopkArgs a;
+  a.logits = logits;
+  a.hist = hist;
+  a.context_lens = context_lens;
+  a.indices = indices;
+  a.workspace = workspace;
+  a.logits_stride = logits_stride;
+  a.rows = rows;
+  a.k = k;
+  a.key_dtype = key_dtype;
+  return from_hip(pmqa::launch_topk_rows(a, static_cast<hipStream_t>(stream)));
+}
+
+idx_status score_histogram(const float* scores, int64_t stride, const int32_t* context_lens,
+                           int32_t rows, int32_t* hist, void* stream) {
+  if (!scores || !context_lens || !hist) return IDX_EINVAL;
+  if (rows <= 0 || stride <= 0) return IDX_EINVAL;
+  if (rows > IDX_MAX_ROWS || stride > (int64_t{1} << 31) - 4) return IDX_EUNSUPPORTED;
+  if (!aligned(scores, 16) || (stride % 4) != 0 || !aligned(context_lens, 4) || !aligned(hist, 8))
+    return IDX_EALIGN;
+  return from_hip(pmqa::launch_score_histogram(scores, stride, context_lens, rows, hist,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0) return IDX_EINVAL;
+  if (!aligned(src, 16) || (bytes % 16) != 0 || !aligned(sink, 4)) return IDX_EALIGN;
+  return from_hip(pmqa::launch_hbm_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Shared device definitions of the paged MQA indexer (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "paged_mqa_indexer.h"
+
+namespace pmqa {
+
+constexpr int kHeads = IDX_NUM_HEADS;          // 32
+constexpr int kDim = IDX_HEAD_DIM;             // 128
+constexpr int kPage = IDX_PAGE_TOKENS;         // 64 tokens per page
+constexpr int kPageBytes = kPage * kDim;       // 8 KiB of FP8 K per page
+constexpr int kBins = IDX_NUM_BINS;            // 1024
+constexpr int kCandCap = IDX_CANDIDATE_CAPACITY;  // 8192
+constexpr int kWave = 64;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Score -> FP16 (round to nearest even).  v_cvt_f16_f32 rounds with the mode
+// register's default (nearest even), keeps FP16 subnormals and turns
+// magnitudes >= 65520 into infinity, as IEEE binary16 requires.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f16_bits_rn(float x) {
+  _Float16 h = static_cast<_Float16>(x);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+}
+
+// Coarse histogram bin of an FP16 bit pattern (not NaN).  DeepGEMM PR #94,
+// "What this adds": 1024 descending bins; below 16 the bin is the exponent and
+// top 4 mantissa bits; from 16 to 223 unit-width bins (the magnitude's integer
+// part, the same for both signs); 223 and above, infinity included, one
+// saturating bin per end.  All three regimes are decided on the FP16 value.
+__device__ __forceinline__ int coarse_bin_f16(uint32_t hb) {
+  const uint32_t a = hb & 0x7FFFu;
+  uint32_t m;
+  if (a < 0x4C00u) {            // |h| < 16
+    m = a >> 6;                  // 0 .. 303
+  } else if (a < 0x5AF8u) {     // 16 <= |h| < 223 (0x5AF8 == 223.0)
+    const uint32_t e = (a >> 10) - 15u;             // 4 .. 7
+    const uint32_t sig = 0x400u | (a & 0x3FFu);     // 1.mantissa * 2^10
+    m = 288u + (sig >> (10u - e));                  // 288 + floor(|h|)
+  } else {
+    m = 511u;                    // saturating, includes infinity
+  }
+  return (hb & 0x8000u) ? static_cast<int>(512u + m) : static_cast<int>(511u - m);
+}
+
+__device__ __forceinline__ bool f16_is_nan(uint32_t hb) { return (hb & 0x7FFFu) > 0x7C00u; }
+
+// Order-preserving unsigned keys: larger score <=> larger key, -0 just below +0.
+__device__ __forceinline__ uint32_t key_f32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t key_f16(uint32_t hb) {
+  return (hb & 0x8000u) ? (~hb & 0xFFFFu) : (hb | 0x8000u);
+}
+
+// Wave-level helpers.
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+}  // namespace pmqa
+
+// Host-side launch entry points implemented by the kernel files.
+namespace pmqa {
+struct LogitsArgs {
+  const uint8_t* q;
+  const uint8_t* kv_pages;
+  const float* k_scales;
+  const float* weights;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* logits;
+  int32_t* hist;
+  int64_t logits_stride;
+  int32_t B;
+  int32_t next_n;
+  int32_t num_pages;
+  int32_t max_pages;
+};
+hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream);
+
+struct TopkArgs {
+  const float* logits;
+  const int32_t* hist;
+  const int32_t* context_lens;
+  int32_t* indices;
+  void* workspace;
+  int64_t logits_stride;
+  int32_t rows;
+  int32_t k;
+  int32_t key_dtype;
+};
+size_t topk_workspace_size(int32_t rows);
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream);
+
+hipError_t launch_score_histogram(const float* scores, int64_t stride, const int32_t* lens,
+                                  int32_t rows, int32_t* hist, hipStream_t stream);
+
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                                 hipStream_t stream);
+}  // namespace pmqa

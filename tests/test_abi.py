@@ -1,0 +1,164 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status before
+anything is launched (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_mqa_logits_indexer_amd as pmqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_mqa_indexer.h")
+
+IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_ELAUNCH, IDX_EWORKSPACE = range(6)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pmqa.library_path()):
+        pytest.fail("library not built: run python -m paged_mqa_logits_indexer_amd.build")
+    return pmqa.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(pmqa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {pmqa.library_path()}").read()
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert pmqa.indexer_status_str(code).startswith("IDX_")
+    assert "unknown" in pmqa.indexer_status_str(99)
+
+
+def test_workspace_query(lib):
+    assert pmqa.topk_workspace_bytes(0, 1024, 2048) == 0
+    one = pmqa.topk_workspace_bytes(1, 131072, 2048)
+    eight = pmqa.topk_workspace_bytes(8, 131072, 2048)
+    # per row: counters, a 1024-bin histogram, 8192 (key, column) candidates
+    assert one >= 16 + 4096 + 8192 * 8
+    assert eight >= 8 * (4096 + 8192 * 8)
+
+
+# Fake but aligned device addresses: every call below fails validation before
+# any of them could be dereferenced or anything launched.
+A = 0x10000
+
+
+def logits_call(lib, **kw):
+    args = dict(q=A, kv=A, sc=A, w=A, bt=A, lens=A, B=8, next_n=1, num_pages=16, max_pages=4,
+                logits=A, stride=256, hist=None, stream=None)
+    args.update(kw)
+    return lib.indexer_logits(args["q"], args["kv"], args["sc"], args["w"], args["bt"],
+                              args["lens"], args["B"], args["next_n"], args["num_pages"],
+                              args["max_pages"], args["logits"], args["stride"], args["hist"],
+                              args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), IDX_EINVAL),
+    (dict(kv=None), IDX_EINVAL),
+    (dict(lens=None), IDX_EINVAL),
+    (dict(logits=None), IDX_EINVAL),
+    (dict(B=0), IDX_EINVAL),
+    (dict(num_pages=0), IDX_EINVAL),
+    (dict(max_pages=-1), IDX_EINVAL),
+    (dict(stride=0), IDX_EINVAL),
+    (dict(next_n=0), IDX_EUNSUPPORTED),
+    (dict(next_n=5), IDX_EUNSUPPORTED),
+    (dict(B=4097), IDX_EUNSUPPORTED),
+    (dict(B=20000, next_n=4), IDX_EUNSUPPORTED),
+    (dict(B=4096, max_pages=1 << 20), IDX_EUNSUPPORTED),
+    (dict(q=A + 8), IDX_EALIGN),
+    (dict(kv=A + 4), IDX_EALIGN),
+    (dict(w=A + 4), IDX_EALIGN),
+    (dict(sc=A + 2), IDX_EALIGN),
+    (dict(logits=A + 4), IDX_EALIGN),
+    (dict(stride=258), IDX_EALIGN),
+    (dict(hist=A + 4), IDX_EALIGN),
+])
+def test_indexer_logits_rejects(lib, kw, status):
+    assert logits_call(lib, **kw) == status
+
+
+def topk_call(lib, **kw):
+    args = dict(logits=A, stride=256, hist=None, lens=A, rows=8, k=2048, key=0, idx=A, ws=A,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.topk_rows(args["logits"], args["stride"], args["hist"], args["lens"], args["rows"],
+                         args["k"], args["key"], args["idx"], args["ws"], args["ws_bytes"],
+                         args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), IDX_EINVAL),
+    (dict(lens=None), IDX_EINVAL),
+    (dict(idx=None), IDX_EINVAL),
+    (dict(ws=None), IDX_EINVAL),
+    (dict(rows=0), IDX_EINVAL),
+    (dict(k=0), IDX_EINVAL),
+    (dict(k=8193), IDX_EINVAL),
+    (dict(stride=-4), IDX_EINVAL),
+    (dict(key=2), IDX_EUNSUPPORTED),
+    (dict(rows=65536), IDX_EUNSUPPORTED),
+    (dict(logits=A + 4), IDX_EALIGN),
+    (dict(stride=6), IDX_EALIGN),
+    (dict(ws=A + 128), IDX_EALIGN),
+    (dict(hist=A + 4), IDX_EALIGN),
+    (dict(ws_bytes=1024), IDX_EWORKSPACE),
+])
+def test_topk_rows_rejects(lib, kw, status):
+    assert topk_call(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), IDX_EINVAL),
+    (dict(nbytes=0), IDX_EINVAL),
+    (dict(src=A + 8), IDX_EALIGN),
+    (dict(nbytes=100), IDX_EALIGN),
+])
+def test_probe_rejects(lib, kw, status):
+    args = dict(src=A, nbytes=1 << 20, sink=A)
+    args.update(kw)
+    assert lib.hbm_read_probe(args["src"], args["nbytes"], args["sink"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(scores=None), IDX_EINVAL),
+    (dict(hist=None), IDX_EINVAL),
+    (dict(rows=0), IDX_EINVAL),
+    (dict(stride=0), IDX_EINVAL),
+    (dict(rows=70000), IDX_EUNSUPPORTED),
+    (dict(scores=A + 4), IDX_EALIGN),
+    (dict(stride=10), IDX_EALIGN),
+    (dict(hist=A + 4), IDX_EALIGN),
+])
+def test_score_histogram_rejects(lib, kw, status):
+    args = dict(scores=A, stride=1024, lens=A, rows=4, hist=A)
+    args.update(kw)
+    assert lib.score_histogram(args["scores"], args["stride"], args["lens"], args["rows"],
+                               args["hist"], None) == status
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 32, 128, dtype=torch.uint8)
+    with pytest.raises((ValueError, TypeError)):
+        pmqa.indexer_logits(q, q, q, q, q, q, 1, q)

@@ -1,0 +1,262 @@
+"""HIP path vs the CPU oracle on small seeded inputs that still span several
+pages, ragged tails and every next_n, plus the edge cases of the method."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as O
+from tests import oracle_pins as P
+from tests.gpu_harness import (DEV, DevInputs, announce, check_hist, check_logits,
+                               check_padding, check_topk, topk)
+
+pytestmark = pytest.mark.gpu
+
+INF = float("inf")
+
+
+def _scores_dev(rows_list):
+    """Pack rows of different lengths into one [rows, stride] buffer (+inf pad)."""
+    n = max(len(r) for r in rows_list)
+    stride = max(4, -(-n // 4) * 4)
+    buf = np.full((len(rows_list), stride), np.inf, dtype=np.float32)
+    lens = np.zeros(len(rows_list), dtype=np.int32)
+    for i, r in enumerate(rows_list):
+        buf[i, :len(r)] = r
+        lens[i] = len(r)
+    return buf, lens
+
+
+def _edge_rows():
+    """Rows that hit every bin regime, rounding edge and special value."""
+    enc = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    vals = P._fp16_positive_values()
+    mids = np.array([float((vals[i] + vals[i + 1]) / 2) for i in range(len(vals) - 1)],
+                    dtype=np.float32)
+    mids = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)),
+                           np.nextafter(mids, np.float32(0))])
+    mids = np.concatenate([mids, -mids[::3]])
+    rng = np.random.default_rng(77)
+    bits = rng.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)
+    rnd = bits.view(np.float32)
+    golden, _ = P.load_golden_bins()
+    return [enc, mids, rnd, golden, np.zeros(0, np.float32), enc[:5]]
+
+
+def test_bins_of_every_fp16_encoding_and_rounding_edge(gpu):
+    rows = _edge_rows()
+    buf, lens = _scores_dev(rows)
+    s = torch.from_numpy(buf).to(DEV)
+    ln = torch.from_numpy(lens).to(DEV)
+    h = torch.zeros((len(rows), 1024), dtype=torch.int32, device=DEV)
+    announce(f"score_histogram edge rows {buf.shape}")
+    gpu.score_histogram(s, ln, h)
+    torch.cuda.synchronize()
+    check_hist(lens, buf, h.cpu().numpy())
+    # accumulates on a second call
+    gpu.score_histogram(s, ln, h)
+    torch.cuda.synchronize()
+    check_hist(lens, buf, h.cpu().numpy(), hist_in=O.coarse_histogram(buf, lens))
+
+
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+@pytest.mark.parametrize("k", [1, 100, 2048, 8192])
+def test_topk_edge_rows_without_histogram(gpu, key, k):
+    rows = _edge_rows()
+    buf, lens = _scores_dev(rows)
+    s = torch.from_numpy(buf).to(DEV)
+    ln = torch.from_numpy(lens).to(DEV)
+    announce(f"topk_rows hist=NULL edge rows k={k} key={key}")
+    idx = topk(s, None, ln, k, key)
+    check_topk(idx.cpu().numpy(), buf, lens, k, key)
+
+
+def _small_inputs(next_n, seed, base, weight_scale=1.0, inf_frac=0.0):
+    return gen.make_indexer_inputs(f"small{next_n}", len(base), next_n, base, seed,
+                                   weight_scale=weight_scale, inf_frac=inf_frac)
+
+
+SMALL = [
+    (1, 11, [1000, 130, 5000, 64, 4097]),
+    (2, 12, [777, 2049, 63]),
+    (3, 13, [3000, 65, 1]),
+    (4, 14, [4096, 1500, 129]),
+]
+
+
+@pytest.mark.parametrize("next_n,seed,base", SMALL, ids=[f"next_n{s[0]}" for s in SMALL])
+def test_small_logits_hist_topk(gpu, next_n, seed, base):
+    x = _small_inputs(next_n, seed, base)
+    d = DevInputs(x)
+    announce(f"indexer_logits small next_n={next_n} lens={x.context_lens.tolist()}")
+    lg, h = d.run(with_hist=True, fill=INF)
+    got = lg.cpu().numpy()
+    check_logits(x, got)
+    check_padding(x, got, INF)
+    check_hist(x.context_lens, got, h.cpu().numpy())
+    for key in (O.KEY_FP32, O.KEY_FP16):
+        for k in (64, 2048):
+            announce(f"topk_rows small next_n={next_n} k={k} key={key}")
+            idx = topk(lg, h, d.lens, k, key)
+            check_topk(idx.cpu().numpy(), got, x.context_lens, k, key)
+
+
+@pytest.mark.parametrize("variant,scale,inf_frac", [("unit", 16.0, 0.0), ("mixed", 4.0, 0.01)])
+def test_small_unit_and_mixed_regimes(gpu, variant, scale, inf_frac):
+    x = _small_inputs(4, 31, [2500, 700], weight_scale=scale, inf_frac=inf_frac)
+    d = DevInputs(x)
+    announce(f"indexer_logits {variant} regime")
+    lg, h = d.run(with_hist=True, fill=INF)
+    got = lg.cpu().numpy()
+    check_logits(x, got)
+    check_hist(x.context_lens, got, h.cpu().numpy())
+    for key in (O.KEY_FP32, O.KEY_FP16):
+        idx = topk(lg, h, d.lens, 512, key)
+        check_topk(idx.cpu().numpy(), got, x.context_lens, 512, key)
+
+
+def test_zero_length_and_tiny_rows(gpu):
+    x = gen.make_indexer_inputs("tiny_rows", 5, 1, [0, 1, 63, 64, 65], 41)
+    d = DevInputs(x)
+    announce("indexer_logits rows of length 0/1/63/64/65")
+    lg, h = d.run(with_hist=True, fill=INF)
+    got = lg.cpu().numpy()
+    check_logits(x, got)
+    check_padding(x, got, INF)
+    check_hist(x.context_lens, got, h.cpu().numpy())
+    assert int(h[0].sum()) == 0
+    for key in (O.KEY_FP32, O.KEY_FP16):
+        idx = topk(lg, h, d.lens, 2048, key).cpu().numpy()
+        check_topk(idx, got, x.context_lens, 2048, key)
+        assert np.all(idx[0] == -1)
+    # verify rows where the first token sees no key
+    y = gen.make_indexer_inputs("tiny_verify", 2, 3, [0, 5], 42)
+    e = DevInputs(y)
+    lg2, h2 = e.run(with_hist=True, fill=INF)
+    got2 = lg2.cpu().numpy()
+    check_logits(y, got2)
+    check_padding(y, got2, INF)
+    check_hist(y.context_lens, got2, h2.cpu().numpy())
+
+
+def test_histogram_off_is_bitwise_identical_and_counts_accumulate(gpu):
+    x = _small_inputs(2, 51, [3333, 999])
+    d = DevInputs(x)
+    announce("indexer_logits hist on/off and accumulate")
+    lg_on, h = d.run(with_hist=True, fill=0.0)
+    lg_off, _ = d.run(with_hist=False, fill=0.0)
+    assert torch.equal(lg_on.view(torch.int32), lg_off.view(torch.int32))
+    first = h.clone()
+    d.logits(lg_on, h)  # second call on the same histogram
+    torch.cuda.synchronize()
+    assert torch.equal(h, 2 * first)
+    # repeated runs are deterministic
+    lg3, h3 = d.run(with_hist=True, fill=0.0)
+    assert torch.equal(lg3.view(torch.int32), lg_off.view(torch.int32))
+    assert torch.equal(h3, first)
+
+
+def test_topk_stale_histograms_stay_exact(gpu):
+    x = _small_inputs(1, 61, [20000, 9000, 3000, 12000])
+    d = DevInputs(x)
+    announce("topk_rows stale histograms")
+    lg, h = d.run(with_hist=True, fill=INF)
+    got = lg.cpu().numpy()
+    lens = x.context_lens
+    stale = {
+        "zeros": torch.zeros_like(h),
+        "doubled": 2 * h,
+        "rolled": torch.roll(h, 1, dims=0),
+        "shifted": torch.roll(h, 37, dims=1),
+        "random": torch.randint(0, 50, h.shape, dtype=torch.int32, device=DEV),
+        "huge": torch.full_like(h, 3000),
+    }
+    for name, hs in stale.items():
+        for key in (O.KEY_FP32, O.KEY_FP16):
+            for k in (1, 2048, 5000):
+                announce(f"topk_rows stale={name} key={key} k={k}")
+                idx = topk(lg, hs, d.lens, k, key)
+                check_topk(idx.cpu().numpy(), got, lens, k, key)
+
+
+def test_topk_threshold_bin_overflow_falls_back_exactly(gpu):
+    rng = np.random.default_rng(71)
+    n = 30000
+    rows = [
+        np.full(n, 1.0, np.float32),                               # one value
+        (np.float32(5.0) + rng.integers(0, 64, n).astype(np.float32)
+         * np.float32(2.0 ** -8)).astype(np.float32),              # one fine bin, many values
+        np.concatenate([np.full(9000, 3.0, np.float32),
+                        rng.standard_normal(n - 9000).astype(np.float32)]),
+        np.where(rng.random(n) < 0.5, np.float32(np.nan), np.float32(2.0)).astype(np.float32),
+    ]
+    buf, lens = _scores_dev(rows)
+    s = torch.from_numpy(buf).to(DEV)
+    ln = torch.from_numpy(lens).to(DEV)
+    h = torch.zeros((len(rows), 1024), dtype=torch.int32, device=DEV)
+    gpu.score_histogram(s, ln, h)
+    for key in (O.KEY_FP32, O.KEY_FP16):
+        for k in (2048, 8192):
+            announce(f"topk_rows overflow rows key={key} k={k}")
+            idx = topk(s, h, ln, k, key)
+            check_topk(idx.cpu().numpy(), buf, lens, k, key)
+            idx = topk(s, None, ln, k, key)
+            check_topk(idx.cpu().numpy(), buf, lens, k, key)
+
+
+def test_topk_ties_across_chunks_go_to_lower_columns(gpu):
+    # equal keys spread over many collect workgroups and both refine paths
+    n = 50000
+    rng = np.random.default_rng(81)
+    a = rng.integers(0, 5, n).astype(np.float32)             # few distinct values
+    b = (np.float32(100.0) + rng.integers(0, 3, n).astype(np.float32)
+         * np.float32(2.0 ** -12)).astype(np.float32)        # fp16 ties, fp32 distinct
+    c = np.zeros(n, np.float32)
+    c[rng.integers(0, n, n // 2)] = -0.0                     # +0 / -0 mix
+    buf, lens = _scores_dev([a, b, c])
+    s = torch.from_numpy(buf).to(DEV)
+    ln = torch.from_numpy(lens).to(DEV)
+    h = torch.zeros((3, 1024), dtype=torch.int32, device=DEV)
+    gpu.score_histogram(s, ln, h)
+    for key in (O.KEY_FP32, O.KEY_FP16):
+        for k in (7, 2048, 6000):
+            announce(f"topk_rows ties key={key} k={k}")
+            idx = topk(s, h, ln, k, key)
+            check_topk(idx.cpu().numpy(), buf, lens, k, key)
+
+
+def test_calls_replay_in_a_hip_graph(gpu):
+    x = _small_inputs(2, 91, [5000, 3000])
+    d = DevInputs(x)
+    k = 2048
+    lg = d.new_logits(INF)
+    h = d.new_hist()
+    idx = torch.full((x.rows, k), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(gpu.topk_workspace_bytes(x.rows, x.logits_stride, k), dtype=torch.uint8,
+                     device=DEV)
+    announce("eager reference for graph replay")
+    d.logits(lg, h)
+    gpu.topk_rows(lg, h, d.lens, k, O.KEY_FP32, idx, ws)
+    torch.cuda.synchronize()
+    ref_lg, ref_h, ref_idx = lg.clone(), h.clone(), np.sort(idx.cpu().numpy(), axis=1)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            h.zero_()
+            d.logits(lg, h)
+            gpu.topk_rows(lg, h, d.lens, k, O.KEY_FP32, idx, ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        announce(f"graph replay {rep}")
+        lg.fill_(-1.0)
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref_h)
+        assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), ref_idx)
+        live = torch.from_numpy(np.arange(x.logits_stride)[None, :] < x.context_lens[:, None]).to(DEV)
+        assert torch.equal(torch.where(live, lg, 0.0), torch.where(live, ref_lg, 0.0))
+        _ = (lg * 2).sum().item()  # unrelated eager work between replays
