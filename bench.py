@@ -1,0 +1,257 @@
+"""Benchmark of the MI355X paged MQA indexer hot path.
+
+One step = indexer_logits (histogram on) + topk_rows (top-2048, FP32 keys)
+over the long-decode workload (B=8, next_n=1, L=131072, H=32, D=128, fp8
+e4m3 Q/K, 64-token pages with a shuffled block table), inputs resident in
+HBM.  Before every step a 1 GiB read sweep evicts the L2s and the 256 MiB
+Infinity Cache (so K comes from HBM, as with the cold-L2 protocol of the
+measurements this path is compared with) and the histogram is reset; both
+happen outside the kernels' timed interval.  The sweep reads rather than
+writes: a write sweep would leave the caches full of dirty lines whose
+write-back then competes with the timed kernel's reads.  Kernel times come
+from HIP events recorded on the stream the kernels run on.
+
+Prints one JSON line (rank 0, N=1):
+  value          mean us per step (logits + top-k kernels), lower is better
+  roofline       the logits kernel against the 8 TB/s HBM peak (algorithmic
+                 bytes per launch / mean launch time)
+  cpu_baseline   the CPU oracle on the same workload, timed on the host
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+FLUSH_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.json")
+KERNEL_SOURCES = ("paged_mqa_logits_indexer_amd/csrc/logits_kernel.hip",
+                  "paged_mqa_logits_indexer_amd/csrc/indexer_common.h")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(x) -> dict:
+    """Bytes one indexer_logits launch must move at minimum (read + write)."""
+    import numpy as np
+    req_keys = x.request_keys().astype(np.int64)
+    pages = (req_keys + 63) // 64
+    lens = x.context_lens.astype(np.int64)
+    k = int(req_keys.sum()) * 128            # fp8 K rows, once per request
+    scales = int(req_keys.sum()) * 4         # one fp32 scale per key
+    logits = int(lens.sum()) * 4             # fp32 logits written
+    table = int(pages.sum()) * 4             # block-table entries
+    qw = x.rows * (32 * 128 + 32 * 4 + 4)    # Q, weights, lengths
+    hist = x.rows * 1024 * 4 * 2             # histogram read-modify-write
+    return {"k": k, "total": k + scales + logits + table + qw + hist}
+
+
+def pct(a, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(a), q))
+
+
+def cpu_baseline(x, budget_s: float):
+    """The oracle (as it stands) on the whole workload, repeated ~budget_s."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        lg = O.indexer_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                              x.context_lens, x.next_n, x.logits_stride)
+        O.coarse_histogram(lg, x.context_lens)
+        O.topk_rows(lg, x.context_lens, 2048, O.KEY_FP32)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end:
+            break
+    mean_s = float(np.mean(times))
+    return {"value": mean_s * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole {x.name} step (logits over all {x.rows} rows, histogram, "
+                      f"top-2048 FP32) repeated {len(times)}x, {sum(times):.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long_decode")
+    ap.add_argument("--fp16-steps", type=int, default=100,
+                    help="steps of the second timing with FP16 score keys")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the cache eviction between steps (warm caches)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the indexer path has no multi-GPU part "
+              "(each request's rows are independent; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gen
+    import paged_mqa_logits_indexer_amd as pmqa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    x = gen.config_inputs(args.workload)
+    t = {k: torch.from_numpy(np.ascontiguousarray(getattr(x, k))).to(dev)
+         for k in ("q", "kv_pages", "k_scales", "weights", "block_table", "context_lens")}
+    logits = torch.full((x.rows, x.logits_stride), float("inf"), dtype=torch.float32, device=dev)
+    hist = torch.zeros((x.rows, 1024), dtype=torch.int32, device=dev)
+    K = 2048
+    idx = torch.empty((x.rows, K), dtype=torch.int32, device=dev)
+    ws = torch.empty(pmqa.topk_workspace_bytes(x.rows, x.logits_stride, K), dtype=torch.uint8,
+                     device=dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def evict():
+        if not args.no_flush:
+            pmqa.hbm_read_probe(flush, sink)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def logits_call():
+        pmqa.indexer_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"],
+                            t["block_table"], t["context_lens"], x.next_n, logits, hist)
+
+    def run(n_steps, key, record):
+        lt, tt = [], []
+        evs = []
+        for i in range(n_steps):
+            evict()
+            hist.zero_()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e2 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            logits_call()
+            e1.record(stream)
+            pmqa.topk_rows(logits, hist, t["context_lens"], K, key, idx, ws)
+            e2.record(stream)
+            evs.append((e0, e1, e2))
+        torch.cuda.synchronize()
+        if record:
+            for e0, e1, e2 in evs:
+                lt.append(e0.elapsed_time(e1) * 1e3)
+                tt.append(e1.elapsed_time(e2) * 1e3)
+        return lt, tt
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    run(args.warmup, pmqa.KEY_FP32, False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    lt, tt = run(args.steps, pmqa.KEY_FP32, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = [a + b for a, b in zip(lt, tt)]
+    print(f"[bench] FP16-key timing {args.fp16_steps} steps", file=sys.stderr, flush=True)
+    lt16, tt16 = run(args.fp16_steps, pmqa.KEY_FP16, True) if args.fp16_steps > 0 else ([], [])
+
+    # practical read ceiling over the same number of bytes as K
+    ab = algorithmic_bytes(x)
+    probe_src = torch.empty(ab["k"] // 4, dtype=torch.int32, device=dev)
+    probe_src.fill_(1)
+    pts = []
+    for i in range(30):
+        evict()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pmqa.hbm_read_probe(probe_src, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pts.append(e0.elapsed_time(e1) * 1e3)
+    probe_us = float(np.median(pts[5:]))
+
+    mean_logits = float(np.mean(lt))
+    achieved = ab["total"] / (mean_logits * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_src_sha") == kernel_source_digest() and tr.get("workload") == x.name:
+            traffic = tr.get("bytes_per_launch")
+    value = float(np.mean(step_us))
+    out = {
+        "metric": "indexer logits+hist+top-2048 us/step and HBM GB/s (% peak), B=8 L=128K",
+        "value": round(value, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(value / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-in/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": x.name, "B": x.B, "next_n": x.next_n,
+                   "context_len": int(x.context_lens.max()), "heads": 32, "head_dim": 128,
+                   "page_tokens": 64, "topk": K, "key": "fp32",
+                   "cache": "cold (1 GiB read sweep before each step)" if not args.no_flush else "warm"},
+        "breakdown_us": {
+            "indexer_logits_mean": round(mean_logits, 3),
+            "indexer_logits_p10": round(pct(lt, 10), 3),
+            "indexer_logits_median": round(pct(lt, 50), 3),
+            "indexer_logits_p90": round(pct(lt, 90), 3),
+            "topk_rows_fp32_mean": round(float(np.mean(tt)), 3),
+            "step_median": round(pct(step_us, 50), 3),
+            "step_p10": round(pct(step_us, 10), 3),
+            "step_p90": round(pct(step_us, 90), 3),
+        },
+        "fp16_keys": ({"step_us_mean": round(float(np.mean([a + b for a, b in zip(lt16, tt16)])), 3),
+                       "topk_rows_fp16_mean": round(float(np.mean(tt16)), 3)} if lt16 else None),
+        "hbm": {
+            "k_bytes": ab["k"],
+            "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),
+            "k_frac_of_peak": round(ab["k"] / (mean_logits * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "read_probe_us": round(probe_us, 3),
+            "read_probe_gbps": round(ab["k"] / (probe_us * 1e-6) / 1e9, 1),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "indexer_logits_kernel<1,true>",
+                     "bytes_per_launch": ab["total"]},
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_baseline_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -115,7 +115,9 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
 
 /*
  * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
- * `rows` rows (host-only query, no device work).  Returns 0 for rows <= 0.
+ * `rows` rows of `logits_stride` scores (host-only query, no device work):
+ * per row a 16-byte header, 8 bytes per 4096-score chunk, a 4 KiB histogram
+ * and 8192 8-byte candidates.  Returns 0 for rows <= 0 or logits_stride <= 0.
  */
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
 

@@ -58,9 +58,8 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages, const float
 }
 
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
-  (void)logits_stride;
   (void)k;
-  return pmqa::topk_workspace_size(rows);
+  return pmqa::topk_workspace_size(rows, logits_stride);
 }
 
 idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* hist,
@@ -73,7 +72,7 @@ idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* 
   if (!aligned(logits, 16) || (logits_stride % 4) != 0 || !aligned(context_lens, 4) ||
       !aligned(indices, 4) || !aligned(workspace, 256) || (hist && !aligned(hist, 8)))
     return IDX_EALIGN;
-  if (workspace_bytes < pmqa::topk_workspace_size(rows)) return IDX_EWORKSPACE;
+  if (workspace_bytes < pmqa::topk_workspace_size(rows, logits_stride)) return IDX_EWORKSPACE;
   pmqa::TopkArgs a;
   a.logits = logits;
   a.hist = hist;

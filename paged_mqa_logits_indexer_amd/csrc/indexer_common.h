@@ -118,7 +118,7 @@ struct TopkArgs {
   int32_t k;
   int32_t key_dtype;
 };
-size_t topk_workspace_size(int32_t rows);
+size_t topk_workspace_size(int32_t rows, int64_t logits_stride);
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream);
 
 hipError_t launch_score_histogram(const float* scores, int64_t stride, const int32_t* lens,

@@ -11,11 +11,12 @@
 // token Q tile of the same section).
 //
 // MI355X design:
-//   * Work split: the K pages of all requests form one list; the persistent
-//     grid (CUs x resident workgroups) takes equal contiguous shares of it, so
-//     every workgroup streams the same number of pages whatever the length
-//     mix.  A share that crosses into the next request flushes the histogram
-//     of the request it leaves.
+//   * Work split: a 2-D grid of (request, chunk of P pages); the workgroup of
+//     a chunk past its request's last page exits at once.  Every workgroup
+//     requests the rows' lengths, its page ids, Q and the head weights
+//     together on entry, so its first K load waits for a single round trip,
+//     and the grid holds a full round of resident workgroups or more, so the
+//     start-up of later workgroups overlaps the streaming of earlier ones.
 //   * K is read straight into registers in the operand layout of
 //     v_mfma_f32_16x16x128_f8f6f4: lane (n, g) = (lane % 16, lane / 16) takes
 //     key n of a 16-key block, bytes [16g, 16g+16) and [64+16g, 64+16g+16).
@@ -28,14 +29,30 @@
 //     leaves lane l with the logit of key l of the page (coalesced stores).
 //   * The next page of every wave is in flight while the current one is
 //     computed.
+//   * The histogram slots of the workgroup's rows live in LDS and are added
+//     to the global histogram (two bins per 64-bit atomic) when it finishes.
 #include "indexer_common.h"
 
 namespace pmqa {
 namespace {
 
+#ifndef PMQA_LOGITS_PREFETCH
+#define PMQA_LOGITS_PREFETCH 1
+#endif
+#ifndef PMQA_LOGITS_PAGES_PER_WG
+#define PMQA_LOGITS_PAGES_PER_WG 0  // 0: chosen from the grid shape
+#endif
 constexpr int kWaves = 4;
+constexpr int kPrefetch = PMQA_LOGITS_PREFETCH;  // pages in flight per wave
+constexpr int kRing = kPrefetch + 1;
+#ifndef PMQA_LOGITS_MAX_PPW
+#define PMQA_LOGITS_MAX_PPW 64
+#endif
+constexpr int kMaxPagesPerWg = PMQA_LOGITS_MAX_PPW;  // <= kWaves * kWave: one page-id fetch per wave
+static_assert(kMaxPagesPerWg <= kWaves * kWave, "page ids of a share must fit one fetch");
+// LDS staging of a share's scores: next_n * pages_per_wg * 64 floats at most.
+constexpr int kStageFloats = kMaxPagesPerWg * kPage;  // 16 KiB
 constexpr int kThreads = kWaves * kWave;
-constexpr int kReqPerThread = (IDX_MAX_REQUESTS + kThreads - 1) / kThreads;  // 16
 
 struct PageRegs {
   i32x4 v[8];   // [key block kb][half]: K bytes in MFMA operand layout
@@ -48,21 +65,41 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// The score exactly as it is stored.  Without the empty asm the compiler may
+// fold "float32 multiply, then round to FP16" into one mixed-precision FMA
+// that rounds the exact product straight to FP16, and the bin would then not
+// always be the bin of the float32 value written to memory.
+__device__ __forceinline__ float as_stored(float x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Buffer resource of one contiguous range (gfx9-family descriptor word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// One page of K in MFMA operand layout plus the scale of key `lane`.  Buffer
+// loads take the page's base from scalar registers and a loop-invariant
+// per-lane offset, so no address register is rewritten from one page to the
+// next (a rewritten address register whose previous value feeds an
+// outstanding load's destination would force a wait for all loads).
 __device__ __forceinline__ void load_page(const uint8_t* __restrict__ kv_pages,
                                           const float* __restrict__ k_scales,
-                                          int page, int lane, PageRegs& r) {
-  const int n = lane & 15, g = lane >> 4;
-  const uint8_t* base = kv_pages + static_cast<int64_t>(page) * kPageBytes + n * kDim + g * 16;
+                                          int page, int lane_off, int lane, PageRegs& r) {
+  const __amdgpu_buffer_rsrc_t kr = range_rsrc(kv_pages + static_cast<int64_t>(page) * kPageBytes, kPageBytes);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    r.v[2 * kb + 0] = *reinterpret_cast<const i32x4*>(base + kb * 16 * kDim);
-    r.v[2 * kb + 1] = *reinterpret_cast<const i32x4*>(base + kb * 16 * kDim + 64);
+    r.v[2 * kb + 0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + kb * 16 * kDim, 0, 0));
+    r.v[2 * kb + 1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + kb * 16 * kDim + 64, 0, 0));
   }
-  r.scale = k_scales[static_cast<int64_t>(page) * kPage + lane];
+  const __amdgpu_buffer_rsrc_t sr = range_rsrc(k_scales + static_cast<int64_t>(page) * kPage, kPage * 4);
+  r.scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, 0, 0));
 }
 
 // Sum over the four lane groups g of part[kb], leaving lane (n, g) with the
@@ -88,11 +125,16 @@ struct RequestRegs {
   int len[NN];
 };
 
+// Scores of page `lp` (the `lpi`-th page of the workgroup's share) for the
+// NN rows of the request.  Scores go to the workgroup's LDS staging area
+// s_out[j][lpi][lane]; they reach global memory after the share's last load
+// (see the kernel), because a global store issued between this page and the
+// next one's prefetch would have to complete before that page counts as
+// arrived: the vector-memory counter covers loads and stores in issue order.
 template <int NN, bool HIST>
-__device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lane,
-                                             const RequestRegs<NN>& rq,
-                                             float* __restrict__ logits,
-                                             int64_t stride, int row0, int* s_hist) {
+__device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi, int ppw,
+                                             int lane, const RequestRegs<NN>& rq,
+                                             float* s_out, int* s_hist) {
   const int g = lane >> 4;
   const int key = lp * kPage + lane;
 #pragma unroll
@@ -119,9 +161,9 @@ __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lan
       }
       part[kb] = s;
     }
-    const float logit = reduce_scatter4(part, g) * pr.scale;
+    const float logit = as_stored(reduce_scatter4(part, g) * pr.scale);
+    s_out[(j * ppw + lpi) * kPage + lane] = logit;
     if (key < rq.len[j]) {
-      logits[static_cast<int64_t>(row0 + j) * stride + key] = logit;
       if constexpr (HIST) {
         const uint32_t hb = f16_bits_rn(logit);
         if (!f16_is_nan(hb)) atomicAdd(&s_hist[j * kBins + coarse_bin_f16(hb)], 1);
@@ -130,152 +172,119 @@ __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lan
   }
 }
 
-__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& total) {
-  const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  const int inc = wave_inclusive_scan(v);
-  if (lane == kWave - 1) s_wave[wave] = inc;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int t = s_wave[w];
-    before += (w < wave) ? t : 0;
-    all += t;
-  }
-  total = all;
-  __syncthreads();
-  return before + inc - v;
-}
+// Resident waves per SIMD the register budget is held to: 4 for one row per
+// request (128 VGPRs), 3 for two rows, 2 for three or four.
+template <int NN>
+constexpr int kWavesPerSimd = NN == 1 ? (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 3 : 2))
+                                      : (NN == 2 && kPrefetch == 1 ? 3 : 2);
 
 template <int NN, bool HIST>
-__global__ __launch_bounds__(kThreads) void indexer_logits_kernel(LogitsArgs a) {
-  __shared__ int s_start[IDX_MAX_REQUESTS + 1];  // first global page of request b
-  __shared__ int s_wave[kWaves];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
+void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   __shared__ int s_hist[HIST ? NN * kBins : 1];
+  __shared__ __align__(16) float s_out[kStageFloats];  // [NN][pages_per_wg][64] scores
 
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int B = a.B;
+  const int b = blockIdx.y;
+  const int row0 = b * NN;
+  const int64_t p0_64 = static_cast<int64_t>(blockIdx.x) * pages_per_wg;  // first page
   // No row reads past its block-table row or writes past its logits row.
   const int64_t mk = min(static_cast<int64_t>(a.max_pages) * kPage, a.logits_stride);
   const int max_keys = static_cast<int>(min(mk, static_cast<int64_t>(INT32_MAX)));
 
-  // 1. Pages of each request (its longest row), exclusive prefix over requests.
-  // Loads are unconditional (index clamped) so that all of them are in flight
-  // together; requests past B count zero pages.
-  int pages_local[kReqPerThread];
-  int my_sum = 0;
+  // Everything the first K load depends on is requested at once: the rows'
+  // lengths, this wave's page ids (clamped into the block-table row, so the
+  // read is in bounds even past the request's last page), Q and the weights.
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int64_t last_id = a.max_pages - 1;
+  int ids = bt[min(p0_64 + wave + lane * kWaves, last_id)];
+  RequestRegs<NN> rq;
+  {
+    const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < kReqPerThread; ++i) {
-    const int b = tid * kReqPerThread + i;
-    const int bc = min(b, B - 1);
-    int mx = 0;
+    for (int j = 0; j < NN; ++j) {
+      rq.len[j] = min(max(a.context_lens[row0 + j], 0), max_keys);
 #pragma unroll
-    for (int j = 0; j < NN; ++j) mx = max(mx, a.context_lens[bc * NN + j]);
-    mx = min(max(mx, 0), max_keys);
-    const int pg = b < B ? (mx >> 6) + ((mx & (kPage - 1)) != 0) : 0;
-    pages_local[i] = pg;
-    my_sum += pg;
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint8_t* qp = a.q + (static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + m) * kDim + g * 16;
+        rq.q[j][mb][0] = *reinterpret_cast<const i32x4*>(qp);
+        rq.q[j][mb][1] = *reinterpret_cast<const i32x4*>(qp + 64);
+        rq.w[j][mb] = *reinterpret_cast<const f32x4*>(a.weights + static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + 4 * g);
+      }
+    }
   }
-  int total = 0;
-  int run = block_exclusive_scan(my_sum, s_wave, total);
+  int keys_b = 0;
 #pragma unroll
-  for (int i = 0; i < kReqPerThread; ++i) {
-    const int b = tid * kReqPerThread + i;
-    if (b < B) s_start[b] = run;
-    run += pages_local[i];
-  }
-  if (tid == 0) s_start[B] = total;
+  for (int j = 0; j < NN; ++j) keys_b = max(keys_b, rq.len[j]);
+  const int pages_b = (keys_b >> 6) + ((keys_b & (kPage - 1)) != 0);
+  if (p0_64 >= pages_b) return;  // past the request's last page (uniform)
+  const int p0 = static_cast<int>(p0_64);
+  const int p1 = static_cast<int>(min(p0_64 + pages_per_wg, static_cast<int64_t>(pages_b)));
+
   if constexpr (HIST) {
     for (int i = tid; i < NN * kBins; i += kThreads) s_hist[i] = 0;
+    __syncthreads();
   }
+  const int lpi0 = wave;  // share-local index of the wave's first page
+
+  // Pages p0 + wave, + kWaves, ... < p1; lane i of `ids` holds the wave's
+  // i-th page id.  A share has at most kMaxPagesPerWg pages, so one fetch
+  // covers it, and the loop below has no conditional load: a load inside a
+  // branch would make the compiler wait for every outstanding load (and, on
+  // this architecture, store) before the next page could be issued.
+  const int n_mine = p1 - p0 > wave ? (p1 - p0 - wave + kWaves - 1) / kWaves : 0;
+  auto page_id = [&](int it) {
+    const int id = __builtin_amdgcn_readlane(ids, it);
+    return min(max(id, 0), a.num_pages - 1);
+  };
+
+  if (n_mine > 0) {
+    // Ring of kRing page buffers: while page `it` is computed, pages
+    // it+1 .. it+kPrefetch are in flight.  Past the last page the last one
+    // is issued again (it is cached), which keeps every load unconditional.
+    const int lane_off = (lane & 15) * kDim + (lane >> 4) * 16;  // key n, group g
+    PageRegs buf[kRing];
+#pragma unroll
+    for (int s = 0; s < kPrefetch; ++s) {
+      load_page(a.kv_pages, a.k_scales, page_id(s < n_mine ? s : n_mine - 1), lane_off, lane, buf[s]);
+    }
+    for (int it0 = 0; it0 < n_mine; it0 += kRing) {
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        const int it = it0 + s;
+        if (it >= n_mine) break;
+        const int nx = it + kPrefetch < n_mine ? it + kPrefetch : n_mine - 1;
+        load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[(s + kPrefetch) % kRing]);
+        compute_page<NN, HIST>(buf[s], p0 + lpi0 + it * kWaves, lpi0 + it * kWaves,
+                               pages_per_wg, lane, rq, s_out, s_hist);
+      }
+    }
+  }
+
   __syncthreads();
-
-  // 2. This workgroup's equal share [p0, p1) of the global page list.
-  const int64_t G = gridDim.x;
-  int p0 = static_cast<int>(static_cast<int64_t>(total) * blockIdx.x / G);
-  const int p1 = static_cast<int>(static_cast<int64_t>(total) * (blockIdx.x + 1) / G);
-  if (p0 >= p1) return;
-
-  // Request holding page p0: the last b with s_start[b] <= p0.
-  int lo = 0, hi = B;  // s_start[lo] <= p0 < s_start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_start[mid] <= p0) lo = mid; else hi = mid;
+  // Live scores of the share, row by row, with 16-byte stores (the row offset
+  // p0 * 64 and the stride are multiples of 4 floats).
+#pragma unroll
+  for (int j = 0; j < NN; ++j) {
+    const int64_t k0 = static_cast<int64_t>(p0) * kPage;
+    const int n = static_cast<int>(min(static_cast<int64_t>(p1) * kPage, static_cast<int64_t>(rq.len[j])) - k0);
+    float* dst = a.logits + static_cast<int64_t>(row0 + j) * a.logits_stride + k0;
+    const float* src = s_out + j * pages_per_wg * kPage;
+    const int n4 = n >> 2;
+    for (int i = tid; i < n4; i += kThreads)
+      reinterpret_cast<f32x4*>(dst)[i] = reinterpret_cast<const f32x4*>(src)[i];
+    for (int i = (n4 << 2) + tid; i < n; i += kThreads) dst[i] = src[i];
   }
-  int b = lo;
-
-  while (p0 < p1) {
-    while (s_start[b + 1] <= p0) ++b;  // skip requests without pages
-    const int seg_begin = p0 - s_start[b];
-    const int seg_end = min(p1, s_start[b + 1]) - s_start[b];
-    const int row0 = b * NN;
-
-    RequestRegs<NN> rq;
-    {
-      const int m = lane & 15, g = lane >> 4;
-#pragma unroll
-      for (int j = 0; j < NN; ++j) {
-        rq.len[j] = min(max(a.context_lens[row0 + j], 0), max_keys);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const uint8_t* qp = a.q + (static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + m) * kDim + g * 16;
-          rq.q[j][mb][0] = *reinterpret_cast<const i32x4*>(qp);
-          rq.q[j][mb][1] = *reinterpret_cast<const i32x4*>(qp + 64);
-          rq.w[j][mb] = *reinterpret_cast<const f32x4*>(a.weights + static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + 4 * g);
-        }
-      }
+  if constexpr (HIST) {
+    // Flush this workgroup's slots: pairs of bins with one 64-bit atomic each.
+    unsigned long long* gh = reinterpret_cast<unsigned long long*>(a.hist + static_cast<int64_t>(row0) * kBins);
+    const uint2* sh = reinterpret_cast<const uint2*>(s_hist);
+    for (int i = tid; i < NN * kBins / 2; i += kThreads) {
+      const uint2 v = sh[i];
+      if (v.x | v.y) atomicAdd(gh + i, (static_cast<unsigned long long>(v.y) << 32) | v.x);
     }
-
-    // Pages seg_begin + wave, + kWaves, ... of request b; up to 64 page ids
-    // are fetched at once, lane i holding the id of the wave's i-th page.
-    const int n_mine = seg_end - seg_begin > wave ? (seg_end - seg_begin - wave + kWaves - 1) / kWaves : 0;
-    const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
-    auto fetch_ids = [&](int it0) {
-      const int it = it0 + lane;
-      int id = 0;
-      if (it < n_mine) id = bt[seg_begin + wave + it * kWaves];
-      return min(max(id, 0), a.num_pages - 1);
-    };
-    int ids = fetch_ids(0);
-    int ids_base = 0;
-
-    if (n_mine > 0) {
-      PageRegs cur, nxt;
-      load_page(a.kv_pages, a.k_scales, __builtin_amdgcn_readlane(ids, 0), lane, cur);
-      for (int it = 0; it < n_mine; it += 2) {
-        // Issue the next page (the current one again at the end: it is cached).
-        int it1 = it + 1 < n_mine ? it + 1 : it;
-        if (it1 - ids_base >= kWave) { ids = fetch_ids(it1); ids_base = it1; }
-        load_page(a.kv_pages, a.k_scales, __builtin_amdgcn_readlane(ids, it1 - ids_base), lane, nxt);
-        compute_page<NN, HIST>(cur, seg_begin + wave + it * kWaves, lane, rq, a.logits,
-                               a.logits_stride, row0, s_hist);
-        if (it + 1 >= n_mine) break;
-        int it2 = it + 2 < n_mine ? it + 2 : it + 1;
-        if (it2 - ids_base >= kWave) { ids = fetch_ids(it2); ids_base = it2; }
-        load_page(a.kv_pages, a.k_scales, __builtin_amdgcn_readlane(ids, it2 - ids_base), lane, cur);
-        compute_page<NN, HIST>(nxt, seg_begin + wave + (it + 1) * kWaves, lane, rq, a.logits,
-                               a.logits_stride, row0, s_hist);
-      }
-    }
-
-    if constexpr (HIST) {
-      // Flush the request's slots: pairs of bins with one 64-bit atomic each.
-      __syncthreads();
-      unsigned long long* gh = reinterpret_cast<unsigned long long*>(a.hist + static_cast<int64_t>(row0) * kBins);
-      uint2* sh = reinterpret_cast<uint2*>(s_hist);
-      for (int i = tid; i < NN * kBins / 2; i += kThreads) {
-        const uint2 v = sh[i];
-        if (v.x | v.y) {
-          atomicAdd(gh + i, (static_cast<unsigned long long>(v.y) << 32) | v.x);
-          sh[i] = uint2{0u, 0u};
-        }
-      }
-      __syncthreads();
-    }
-    p0 = s_start[b] + seg_end;
-    ++b;
   }
 }
 
@@ -311,8 +320,8 @@ DeviceInfo* device_info(int dev) {
 }
 
 template <int NN, bool HIST>
-hipError_t launch(const LogitsArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((indexer_logits_kernel<NN, HIST>), dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream) {
+  hipLaunchKernelGGL((indexer_logits_kernel<NN, HIST>), grid, dim3(kThreads), 0, stream, a, pages_per_wg);
   return hipGetLastError();
 }
 
@@ -325,20 +334,35 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream) {
   const DeviceInfo* info = device_info(dev);
   if (!info) return hipErrorInvalidDevice;
   const bool hist = a.hist != nullptr;
-  const int64_t upper = static_cast<int64_t>(a.B) * a.max_pages;  // pages at most
-  int64_t grid = static_cast<int64_t>(info->cus) * info->occ[a.next_n - 1][hist ? 1 : 0];
-  if (upper < grid) grid = upper;
-  if (grid < 1) grid = 1;
-  const int g = static_cast<int>(grid);
+  // Pages per workgroup.  Long streams per wave amortise a workgroup's start
+  // (one round trip for its page ids) and end (staged stores, histogram
+  // flush), so a share is as long as the grid allows while every CU still
+  // gets a workgroup: B * max_pages / CUs pages, 4..kMaxPagesPerWg.  The host
+  // cannot read the lengths, so B * max_pages is an upper bound; with many
+  // requests (B >= 32) the real lengths usually vary, and shorter shares
+  // (16 pages) give the static grid enough rounds to even out.
+  const int64_t pages_upper = static_cast<int64_t>(a.B) * a.max_pages;
+  int64_t ppw = (pages_upper + info->cus - 1) / info->cus;
+  if (a.B >= 32 && ppw > 16) ppw = 16;
+#if PMQA_LOGITS_PAGES_PER_WG
+  ppw = PMQA_LOGITS_PAGES_PER_WG;
+#endif
+  const int64_t ppw_max = kMaxPagesPerWg / a.next_n;  // the staging area holds next_n rows
+  ppw = ppw < 4 ? 4 : (ppw > ppw_max ? ppw_max : ppw);
+  ppw = ppw / kWaves * kWaves;
+  const int64_t chunks = (a.max_pages + ppw - 1) / ppw;
+  if (chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
+  const int p = static_cast<int>(ppw);
   switch (a.next_n * 2 + (hist ? 1 : 0)) {
-    case 2: return launch<1, false>(a, g, stream);
-    case 3: return launch<1, true>(a, g, stream);
-    case 4: return launch<2, false>(a, g, stream);
-    case 5: return launch<2, true>(a, g, stream);
-    case 6: return launch<3, false>(a, g, stream);
-    case 7: return launch<3, true>(a, g, stream);
-    case 8: return launch<4, false>(a, g, stream);
-    case 9: return launch<4, true>(a, g, stream);
+    case 2: return launch<1, false>(a, grid, p, stream);
+    case 3: return launch<1, true>(a, grid, p, stream);
+    case 4: return launch<2, false>(a, grid, p, stream);
+    case 5: return launch<2, true>(a, grid, p, stream);
+    case 6: return launch<3, false>(a, grid, p, stream);
+    case 7: return launch<3, true>(a, grid, p, stream);
+    case 8: return launch<4, false>(a, grid, p, stream);
+    case 9: return launch<4, true>(a, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -50,11 +50,14 @@ def test_status_strings(lib):
 
 def test_workspace_query(lib):
     assert pmqa.topk_workspace_bytes(0, 1024, 2048) == 0
+    assert pmqa.topk_workspace_bytes(4, 0, 2048) == 0
     one = pmqa.topk_workspace_bytes(1, 131072, 2048)
     eight = pmqa.topk_workspace_bytes(8, 131072, 2048)
-    # per row: counters, a 1024-bin histogram, 8192 (key, column) candidates
-    assert one >= 16 + 4096 + 8192 * 8
-    assert eight >= 8 * (4096 + 8192 * 8)
+    # per row: a header, one count pair per 4096-score chunk, a 1024-bin
+    # histogram and 8192 (key, column) candidates
+    assert one >= 16 + 32 * 8 + 4096 + 8192 * 8
+    assert eight >= 8 * (16 + 32 * 8 + 4096 + 8192 * 8)
+    assert pmqa.topk_workspace_bytes(8, 1 << 20, 2048) > eight
 
 
 # Fake but aligned device addresses: every call below fails validation before
