@@ -8,8 +8,16 @@ Infinity Cache (so K comes from HBM, as with the cold-L2 protocol of the
 measurements this path is compared with) and the histogram is reset; both
 happen outside the kernels' timed interval.  The sweep reads rather than
 writes: a write sweep would leave the caches full of dirty lines whose
-write-back then competes with the timed kernel's reads.  Kernel times come
-from HIP events recorded on the stream the kernels run on.
+write-back then competes with the timed kernel's reads.
+
+Kernel times come from HIP events that the library's own dispatches record
+(the *_timed entry points, hipExtLaunchKernel): a call's start event when its
+first kernel begins and its stop event when its last kernel ends, the same
+interval rocprofv3's kernel trace reports.  A step is timed from the start of
+the logits kernel to the end of the last top-k kernel, so the gap between
+the two calls counts.  Events recorded on the stream around the step are
+reported beside them; they also hold the dispatch latency of the first
+kernel.
 
 Prints one JSON line (rank 0, N=1):
   value          mean us per step (logits + top-k kernels), lower is better
@@ -139,43 +147,58 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
 
-    def logits_call():
-        pmqa.indexer_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"],
-                            t["block_table"], t["context_lens"], x.next_n, logits, hist)
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)  # creates the HIP event before a dispatch records it
+        return evs
 
-    def run(n_steps, key, record):
-        lt, tt = [], []
+    def run(n_steps, key, record, split=False):
+        """Steps of logits + top-k.  Without `split` only the step's start
+        (logits kernel begins) and end (last top-k kernel ends) are recorded,
+        so no event sits between the two calls; with it each call is timed
+        on its own."""
+        lt, tt, st, wt = [], [], [], []
         evs = []
         for i in range(n_steps):
+            ls, le, ts, te, ws0, ws1 = new_events(6)
             evict()
             hist.zero_()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e2 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            logits_call()
-            e1.record(stream)
-            pmqa.topk_rows(logits, hist, t["context_lens"], K, key, idx, ws)
-            e2.record(stream)
-            evs.append((e0, e1, e2))
+            ws0.record(stream)
+            pmqa.indexer_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"],
+                                t["block_table"], t["context_lens"], x.next_n, logits, hist,
+                                events=(ls, le if split else None))
+            pmqa.topk_rows(logits, hist, t["context_lens"], K, key, idx, ws,
+                           events=(ts if split else None, te))
+            ws1.record(stream)
+            evs.append((ls, le, ts, te, ws0, ws1))
         torch.cuda.synchronize()
         if record:
-            for e0, e1, e2 in evs:
-                lt.append(e0.elapsed_time(e1) * 1e3)
-                tt.append(e1.elapsed_time(e2) * 1e3)
-        return lt, tt
+            for ls, le, ts, te, ws0, ws1 in evs:
+                if split:
+                    lt.append(ls.elapsed_time(le) * 1e3)
+                    tt.append(ts.elapsed_time(te) * 1e3)
+                else:
+                    st.append(ls.elapsed_time(te) * 1e3)
+                    wt.append(ws0.elapsed_time(ws1) * 1e3)
+        return lt, tt, st, wt
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     run(args.warmup, pmqa.KEY_FP32, False)
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    lt, tt = run(args.steps, pmqa.KEY_FP32, True)
+    _, _, step_us, stream_us = run(args.steps, pmqa.KEY_FP32, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_us = [a + b for a, b in zip(lt, tt)]
+    print(f"[bench] per-call timing {args.steps} steps", file=sys.stderr, flush=True)
+    lt, tt, _, _ = run(args.steps, pmqa.KEY_FP32, True, split=True)
     print(f"[bench] FP16-key timing {args.fp16_steps} steps", file=sys.stderr, flush=True)
-    lt16, tt16 = run(args.fp16_steps, pmqa.KEY_FP16, True) if args.fp16_steps > 0 else ([], [])
+    if args.fp16_steps > 0:
+        _, _, st16, _ = run(args.fp16_steps, pmqa.KEY_FP16, True)
+        _, tt16, _, _ = run(args.fp16_steps, pmqa.KEY_FP16, True, split=True)
+    else:
+        st16, tt16 = [], []
 
     # practical read ceiling over the same number of bytes as K
     ab = algorithmic_bytes(x)
@@ -183,12 +206,9 @@ def main() -> int:
     probe_src.fill_(1)
     pts = []
     for i in range(30):
+        e0, e1 = new_events(2)
         evict()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        pmqa.hbm_read_probe(probe_src, sink)
-        e1.record(stream)
+        pmqa.hbm_read_probe(probe_src, sink, events=(e0, e1))
         torch.cuda.synchronize()
         pts.append(e0.elapsed_time(e1) * 1e3)
     probe_us = float(np.median(pts[5:]))
@@ -228,9 +248,11 @@ def main() -> int:
             "step_median": round(pct(step_us, 50), 3),
             "step_p10": round(pct(step_us, 10), 3),
             "step_p90": round(pct(step_us, 90), 3),
+            "step_stream_events_mean": round(float(np.mean(stream_us)), 3),
         },
-        "fp16_keys": ({"step_us_mean": round(float(np.mean([a + b for a, b in zip(lt16, tt16)])), 3),
-                       "topk_rows_fp16_mean": round(float(np.mean(tt16)), 3)} if lt16 else None),
+        "timing": "dispatch-recorded HIP events (hipExtLaunchKernel start/stop), mean over steps",
+        "fp16_keys": ({"step_us_mean": round(float(np.mean(st16)), 3),
+                       "topk_rows_fp16_mean": round(float(np.mean(tt16)), 3)} if st16 else None),
         "hbm": {
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),

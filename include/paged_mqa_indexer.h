@@ -115,9 +115,11 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
 
 /*
  * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
- * `rows` rows of `logits_stride` scores (host-only query, no device work):
- * per row a 16-byte header, 8 bytes per 4096-score chunk, a 4 KiB histogram
- * and 8192 8-byte candidates.  Returns 0 for rows <= 0 or logits_stride <= 0.
+ * `rows` rows of `logits_stride` scores and a given k (host-only query, no
+ * device work): per row a 16-byte header and a 4 KiB histogram, and per
+ * 4096-score chunk of a row 8 bytes of counts, 4 * min(k, 4096) bytes of
+ * columns and 32 KiB of candidates (about 12 bytes per score of the stride).
+ * Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
  */
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
 
@@ -170,6 +172,30 @@ idx_status topk_rows(const float* logits, int64_t logits_stride,
  */
 idx_status score_histogram(const float* scores, int64_t stride, const int32_t* context_lens,
                            int32_t rows, int32_t* hist, void* stream);
+
+/*
+ * Timing variants, for measurement: the same as indexer_logits, topk_rows
+ * and hbm_read_probe, plus two hipEvent_t handles (created by the caller, or
+ * NULL).  The call's own kernel dispatches record them (hipExtLaunchKernel):
+ * start_event when its first kernel begins and stop_event when its last
+ * kernel ends, so the elapsed time between them is the call's device time
+ * without the stream's dispatch gaps before and after it.  The results are
+ * those of the plain call.  Not meant for graph capture.
+ */
+idx_status indexer_logits_timed(const uint8_t* q, const uint8_t* kv_pages,
+                                const float* k_scales, const float* weights,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                int32_t B, int32_t next_n, int32_t num_pages,
+                                int32_t max_pages, float* logits, int64_t logits_stride,
+                                int32_t* hist, void* stream, void* start_event,
+                                void* stop_event);
+idx_status topk_rows_timed(const float* logits, int64_t logits_stride,
+                           const int32_t* hist, const int32_t* context_lens,
+                           int32_t rows, int32_t k, int32_t key_dtype, int32_t* indices,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* start_event, void* stop_event);
+idx_status hbm_read_probe_timed(const void* src, size_t bytes, uint32_t* sink, void* stream,
+                                void* start_event, void* stop_event);
 
 /* Human-readable name of a status code (static string). */
 const char* indexer_status_str(int32_t status);

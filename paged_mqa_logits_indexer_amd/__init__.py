@@ -9,12 +9,17 @@ streams.
 
 Entry points (same names as the C ABI):
   indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens,
-                 next_n, logits, hist=None)
+                 next_n, logits, hist=None, events=None)
   topk_workspace_bytes(rows, logits_stride, k)
-  topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None)
+  topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None,
+            events=None)
   score_histogram(scores, context_lens, hist)
   indexer_status_str(status)
-  hbm_read_probe(src, sink)
+  hbm_read_probe(src, sink, events=None)
+With ``events=(start, stop)`` (two torch.cuda.Event with timing enabled) the
+call goes to the ``*_timed`` C variant, whose kernel dispatches record the
+events themselves: start when the call's first kernel begins, stop when its
+last kernel ends.
 """
 
 from __future__ import annotations
@@ -40,7 +45,8 @@ HEAD_DIM = 128
 PAGE_TOKENS = 64
 
 EXPORTED_SYMBOLS = ("indexer_logits", "topk_workspace_bytes", "topk_rows",
-                    "score_histogram", "indexer_status_str", "hbm_read_probe")
+                    "score_histogram", "indexer_status_str", "hbm_read_probe",
+                    "indexer_logits_timed", "topk_rows_timed", "hbm_read_probe_timed")
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpaged_mqa_indexer.so"
@@ -83,6 +89,12 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_status_str.restype = ctypes.c_char_p
     lib.hbm_read_probe.argtypes = [vp, sz, vp, vp]
     lib.hbm_read_probe.restype = ctypes.c_int
+    lib.indexer_logits_timed.argtypes = lib.indexer_logits.argtypes + [vp, vp]
+    lib.indexer_logits_timed.restype = ctypes.c_int
+    lib.topk_rows_timed.argtypes = lib.topk_rows.argtypes + [vp, vp]
+    lib.topk_rows_timed.restype = ctypes.c_int
+    lib.hbm_read_probe_timed.argtypes = lib.hbm_read_probe.argtypes + [vp, vp]
+    lib.hbm_read_probe_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -117,8 +129,28 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _event_handles(events, device: torch.device):
+    """hipEvent_t handles of (start, stop), either of which may be None; a
+    torch event that was never recorded has no HIP event yet, so it is
+    recorded once to create it."""
+    if events is None:
+        return None
+    start, stop = events
+    handles = []
+    for ev in (start, stop):
+        if ev is None:
+            handles.append(None)
+            continue
+        if not isinstance(ev, torch.cuda.Event):
+            raise TypeError("events must be a pair of torch.cuda.Event (or None)")
+        if not ev.cuda_event:
+            ev.record(torch.cuda.current_stream(device))
+        handles.append(ev.cuda_event)
+    return handles
+
+
 def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens, next_n,
-                   logits, hist=None):
+                   logits, hist=None, events=None):
     """Paged MQA logits (and histogram) on the current stream of q's device.
 
     q [B*next_n, 32, 128] uint8 (e4m3fn codes); kv_pages [P, 64, 128] uint8;
@@ -158,10 +190,11 @@ def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens, ne
             raise ValueError(f"hist must be contiguous [{rows}, 1024]")
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.indexer_logits(
-            _ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(block_table),
-            _ptr(context_lens), int(B), int(next_n), int(P), int(max_pages), _ptr(logits),
-            int(logits.stride(0)), _ptr(hist), _stream_ptr(dev))
+        args = (_ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(block_table),
+                _ptr(context_lens), int(B), int(next_n), int(P), int(max_pages), _ptr(logits),
+                int(logits.stride(0)), _ptr(hist), _stream_ptr(dev))
+        ev = _event_handles(events, dev)
+        st = lib.indexer_logits(*args) if ev is None else lib.indexer_logits_timed(*args, *ev)
     _check("indexer_logits", st)
 
 
@@ -169,7 +202,7 @@ def topk_workspace_bytes(rows: int, logits_stride: int, k: int) -> int:
     return int(load_library().topk_workspace_bytes(int(rows), int(logits_stride), int(k)))
 
 
-def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None):
+def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None, events=None):
     """Exact per-row top-k indices into ``indices`` [rows, k] int32.
 
     ``workspace`` is a uint8 GPU tensor of at least topk_workspace_bytes()
@@ -196,9 +229,11 @@ def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None)
     _need(workspace, "workspace", torch.uint8, dev)
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.topk_rows(_ptr(logits), int(logits.stride(0)), _ptr(hist), _ptr(context_lens),
-                           int(rows), int(k), int(key_dtype), _ptr(indices), _ptr(workspace),
-                           int(workspace.numel()), _stream_ptr(dev))
+        args = (_ptr(logits), int(logits.stride(0)), _ptr(hist), _ptr(context_lens), int(rows),
+                int(k), int(key_dtype), _ptr(indices), _ptr(workspace), int(workspace.numel()),
+                _stream_ptr(dev))
+        ev = _event_handles(events, dev)
+        st = lib.topk_rows(*args) if ev is None else lib.topk_rows_timed(*args, *ev)
     _check("topk_rows", st)
 
 
@@ -222,7 +257,7 @@ def score_histogram(scores, context_lens, hist):
     _check("score_histogram", st)
 
 
-def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, events=None) -> None:
     """Stream all bytes of ``src`` (contiguous GPU tensor) once; checksum to sink."""
     if src.device.type != "cuda" or not src.is_contiguous():
         raise ValueError("src must be a contiguous GPU tensor")
@@ -230,6 +265,7 @@ def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
     lib = load_library()
     nbytes = src.numel() * src.element_size()
     with torch.cuda.device(src.device):
-        st = lib.hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink),
-                                _stream_ptr(src.device))
+        args = (_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream_ptr(src.device))
+        ev = _event_handles(events, src.device)
+        st = lib.hbm_read_probe(*args) if ev is None else lib.hbm_read_probe_timed(*args, *ev)
     _check("hbm_read_probe", st)

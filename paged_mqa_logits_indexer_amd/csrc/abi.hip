@@ -8,27 +8,17 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 idx_status from_hip(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_ELAUNCH; }
 
-}  // namespace
-
-extern "C" {
-
-const char* indexer_status_str(int32_t s) {
-  switch (s) {
-    case IDX_OK: return "IDX_OK";
-    case IDX_EINVAL: return "IDX_EINVAL: invalid argument";
-    case IDX_EUNSUPPORTED: return "IDX_EUNSUPPORTED: unsupported configuration";
-    case IDX_EALIGN: return "IDX_EALIGN: misaligned pointer or stride";
-    case IDX_ELAUNCH: return "IDX_ELAUNCH: HIP launch or device query failed";
-    case IDX_EWORKSPACE: return "IDX_EWORKSPACE: workspace too small";
-    default: return "unknown status";
-  }
+pmqa::LaunchEvents events(void* start, void* stop) {
+  pmqa::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start);
+  ev.stop = static_cast<hipEvent_t>(stop);
+  return ev;
 }
 
-idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
-                          const float* weights, const int32_t* block_table,
-                          const int32_t* context_lens, int32_t B, int32_t next_n,
-                          int32_t num_pages, int32_t max_pages, float* logits,
-                          int64_t logits_stride, int32_t* hist, void* stream) {
+idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                       const float* weights, const int32_t* block_table, const int32_t* context_lens,
+                       int32_t B, int32_t next_n, int32_t num_pages, int32_t max_pages, float* logits,
+                       int64_t logits_stride, int32_t* hist, void* stream, pmqa::LaunchEvents ev) {
   if (!q || !kv_pages || !k_scales || !weights || !block_table || !context_lens || !logits)
     return IDX_EINVAL;
   if (B <= 0 || num_pages <= 0 || max_pages <= 0 || logits_stride <= 0) return IDX_EINVAL;
@@ -54,17 +44,13 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages, const float
   a.next_n = next_n;
   a.num_pages = num_pages;
   a.max_pages = max_pages;
-  return from_hip(pmqa::launch_indexer_logits(a, static_cast<hipStream_t>(stream)));
+  return from_hip(pmqa::launch_indexer_logits(a, static_cast<hipStream_t>(stream), ev));
 }
 
-size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
-  (void)k;
-  return pmqa::topk_workspace_size(rows, logits_stride);
-}
-
-idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* hist,
+idx_status topk_call(const float* logits, int64_t logits_stride, const int32_t* hist,
                      const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
-                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
+                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream,
+                     pmqa::LaunchEvents ev) {
   if (!logits || !context_lens || !indices || !workspace) return IDX_EINVAL;
   if (rows <= 0 || logits_stride <= 0 || k < 1 || k > IDX_CANDIDATE_CAPACITY) return IDX_EINVAL;
   if (key_dtype != IDX_KEY_FP32 && key_dtype != IDX_KEY_FP16) return IDX_EUNSUPPORTED;
@@ -72,7 +58,7 @@ idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* 
   if (!aligned(logits, 16) || (logits_stride % 4) != 0 || !aligned(context_lens, 4) ||
       !aligned(indices, 4) || !aligned(workspace, 256) || (hist && !aligned(hist, 8)))
     return IDX_EALIGN;
-  if (workspace_bytes < pmqa::topk_workspace_size(rows, logits_stride)) return IDX_EWORKSPACE;
+  if (workspace_bytes < pmqa::topk_workspace_size(rows, logits_stride, k)) return IDX_EWORKSPACE;
   pmqa::TopkArgs a;
   a.logits = logits;
   a.hist = hist;
@@ -83,7 +69,67 @@ idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* 
   a.rows = rows;
   a.k = k;
   a.key_dtype = key_dtype;
-  return from_hip(pmqa::launch_topk_rows(a, static_cast<hipStream_t>(stream)));
+  return from_hip(pmqa::launch_topk_rows(a, static_cast<hipStream_t>(stream), ev));
+}
+
+idx_status probe_call(const void* src, size_t bytes, uint32_t* sink, void* stream, pmqa::LaunchEvents ev) {
+  if (!src || !sink || bytes == 0) return IDX_EINVAL;
+  if (!aligned(src, 16) || (bytes % 16) != 0 || !aligned(sink, 4)) return IDX_EALIGN;
+  return from_hip(pmqa::launch_hbm_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream), ev));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* indexer_status_str(int32_t s) {
+  switch (s) {
+    case IDX_OK: return "IDX_OK";
+    case IDX_EINVAL: return "IDX_EINVAL: invalid argument";
+    case IDX_EUNSUPPORTED: return "IDX_EUNSUPPORTED: unsupported configuration";
+    case IDX_EALIGN: return "IDX_EALIGN: misaligned pointer or stride";
+    case IDX_ELAUNCH: return "IDX_ELAUNCH: HIP launch or device query failed";
+    case IDX_EWORKSPACE: return "IDX_EWORKSPACE: workspace too small";
+    default: return "unknown status";
+  }
+}
+
+idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                          const float* weights, const int32_t* block_table,
+                          const int32_t* context_lens, int32_t B, int32_t next_n,
+                          int32_t num_pages, int32_t max_pages, float* logits,
+                          int64_t logits_stride, int32_t* hist, void* stream) {
+  return logits_call(q, kv_pages, k_scales, weights, block_table, context_lens, B, next_n, num_pages,
+                     max_pages, logits, logits_stride, hist, stream, pmqa::LaunchEvents{});
+}
+
+idx_status indexer_logits_timed(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                                const float* weights, const int32_t* block_table,
+                                const int32_t* context_lens, int32_t B, int32_t next_n,
+                                int32_t num_pages, int32_t max_pages, float* logits,
+                                int64_t logits_stride, int32_t* hist, void* stream,
+                                void* start_event, void* stop_event) {
+  return logits_call(q, kv_pages, k_scales, weights, block_table, context_lens, B, next_n, num_pages,
+                     max_pages, logits, logits_stride, hist, stream, events(start_event, stop_event));
+}
+
+size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
+  return pmqa::topk_workspace_size(rows, logits_stride, k);
+}
+
+idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* hist,
+                     const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
+                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_call(logits, logits_stride, hist, context_lens, rows, k, key_dtype, indices, workspace,
+                   workspace_bytes, stream, pmqa::LaunchEvents{});
+}
+
+idx_status topk_rows_timed(const float* logits, int64_t logits_stride, const int32_t* hist,
+                           const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
+                           int32_t* indices, void* workspace, size_t workspace_bytes, void* stream,
+                           void* start_event, void* stop_event) {
+  return topk_call(logits, logits_stride, hist, context_lens, rows, k, key_dtype, indices, workspace,
+                   workspace_bytes, stream, events(start_event, stop_event));
 }
 
 idx_status score_histogram(const float* scores, int64_t stride, const int32_t* context_lens,
@@ -98,9 +144,12 @@ idx_status score_histogram(const float* scores, int64_t stride, const int32_t* c
 }
 
 idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
-  if (!src || !sink || bytes == 0) return IDX_EINVAL;
-  if (!aligned(src, 16) || (bytes % 16) != 0 || !aligned(sink, 4)) return IDX_EALIGN;
-  return from_hip(pmqa::launch_hbm_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream)));
+  return probe_call(src, bytes, sink, stream, pmqa::LaunchEvents{});
+}
+
+idx_status hbm_read_probe_timed(const void* src, size_t bytes, uint32_t* sink, void* stream,
+                                void* start_event, void* stop_event) {
+  return probe_call(src, bytes, sink, stream, events(start_event, stop_event));
 }
 
 }  // extern "C"

@@ -1,8 +1,11 @@
 // Shared device definitions of the paged MQA indexer (gfx950 / CDNA4).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <climits>
 
 #include "paged_mqa_indexer.h"
 
@@ -64,20 +67,56 @@ __device__ __forceinline__ uint32_t key_f16(uint32_t hb) {
 // Wave-level helpers.
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
+// Wave-wide scans and reductions on DPP lane moves (gfx9 family): within
+// each row of 16 lanes, shifts by 1, 2, 4 and 8; then row_bcast:15 adds the
+// last lane of rows 0 and 2 into rows 1 and 3, and row_bcast:31 the last
+// lane of row 1 into rows 2 and 3.  A lane whose source lies outside the
+// row (or outside the masked rows) receives `identity`.  No LDS traffic,
+// unlike __shfl_up / __shfl_xor, which go through ds_bpermute.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_move(int v, int identity) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <typename Op>
+__device__ __forceinline__ int wave_inclusive_scan_op(int v, int identity, Op op) {
+  v = op(v, dpp_move<0x111>(v, identity));  // row_shr:1
+  v = op(v, dpp_move<0x112>(v, identity));  // row_shr:2
+  v = op(v, dpp_move<0x114>(v, identity));  // row_shr:4
+  v = op(v, dpp_move<0x118>(v, identity));  // row_shr:8
+  v = op(v, dpp_move<0x142, 0xA>(v, identity));  // row_bcast:15 into rows 1, 3
+  v = op(v, dpp_move<0x143, 0xC>(v, identity));  // row_bcast:31 into rows 2, 3
   return v;
 }
 
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  return wave_inclusive_scan_op(v, 0, [](int a, int b) { return a + b; });
+}
+
+// Reductions: the inclusive result of lane 63, the same in every lane.
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(v), kWave - 1);
+}
+__device__ __forceinline__ int wave_max(int v) {
+  return __builtin_amdgcn_readlane(
+      wave_inclusive_scan_op(v, INT_MIN, [](int a, int b) { return a > b ? a : b; }), kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(
+      wave_inclusive_scan_op(static_cast<int>(v), 0, [](int a, int b) { return a | b; }), kWave - 1));
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(
+      wave_inclusive_scan_op(static_cast<int>(v), -1, [](int a, int b) { return a & b; }), kWave - 1));
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits until every global load and store the wave has issued is complete
+// (vmcnt(0)), which costs a memory round trip right after global stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Number of set bits of `mask` below this lane.
@@ -90,6 +129,24 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 // Host-side launch entry points implemented by the kernel files.
 namespace pmqa {
+// Optional events recorded by a call's own dispatches (measurement only):
+// `start` when its first kernel begins, `stop` when its last kernel ends.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// One kernel launch; with events it goes through hipExtLaunchKernel, which
+// records them at the dispatch's own begin and end.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                          hipEvent_t start, hipEvent_t stop, Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, static_cast<KArgs>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<KArgs>(args)...);
+}
+
 struct LogitsArgs {
   const uint8_t* q;
   const uint8_t* kv_pages;
@@ -105,7 +162,7 @@ struct LogitsArgs {
   int32_t num_pages;
   int32_t max_pages;
 };
-hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream);
+hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, LaunchEvents ev = {});
 
 struct TopkArgs {
   const float* logits;
@@ -118,12 +175,12 @@ struct TopkArgs {
   int32_t k;
   int32_t key_dtype;
 };
-size_t topk_workspace_size(int32_t rows, int64_t logits_stride);
-hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream);
+size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k);
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev = {});
 
 hipError_t launch_score_histogram(const float* scores, int64_t stride, const int32_t* lens,
                                   int32_t rows, int32_t* hist, hipStream_t stream);
 
 hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
-                                 hipStream_t stream);
+                                 hipStream_t stream, LaunchEvents ev = {});
 }  // namespace pmqa

@@ -320,14 +320,15 @@ DeviceInfo* device_info(int dev) {
 }
 
 template <int NN, bool HIST>
-hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream) {
-  hipLaunchKernelGGL((indexer_logits_kernel<NN, HIST>), grid, dim3(kThreads), 0, stream, a, pages_per_wg);
+hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
+  launch_kernel(indexer_logits_kernel<NN, HIST>, grid, dim3(kThreads), stream, ev.start, ev.stop, a,
+                pages_per_wg);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream) {
+hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, LaunchEvents ev) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -355,14 +356,14 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
   const int p = static_cast<int>(ppw);
   switch (a.next_n * 2 + (hist ? 1 : 0)) {
-    case 2: return launch<1, false>(a, grid, p, stream);
-    case 3: return launch<1, true>(a, grid, p, stream);
-    case 4: return launch<2, false>(a, grid, p, stream);
-    case 5: return launch<2, true>(a, grid, p, stream);
-    case 6: return launch<3, false>(a, grid, p, stream);
-    case 7: return launch<3, true>(a, grid, p, stream);
-    case 8: return launch<4, false>(a, grid, p, stream);
-    case 9: return launch<4, true>(a, grid, p, stream);
+    case 2: return launch<1, false>(a, grid, p, stream, ev);
+    case 3: return launch<1, true>(a, grid, p, stream, ev);
+    case 4: return launch<2, false>(a, grid, p, stream, ev);
+    case 5: return launch<2, true>(a, grid, p, stream, ev);
+    case 6: return launch<3, false>(a, grid, p, stream, ev);
+    case 7: return launch<3, true>(a, grid, p, stream, ev);
+    case 8: return launch<4, false>(a, grid, p, stream, ev);
+    case 9: return launch<4, true>(a, grid, p, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }

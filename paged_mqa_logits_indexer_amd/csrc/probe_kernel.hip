@@ -30,12 +30,13 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32
 
 }  // namespace
 
-hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream,
+                                 LaunchEvents ev) {
   const int64_t n_vec = static_cast<int64_t>(bytes / 16);
   const int64_t grid = (n_vec + kProbeChunk - 1) / kProbeChunk;
   if (grid < 1 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(hbm_read_probe_kernel, dim3(static_cast<unsigned>(grid)), dim3(kProbeThreads), 0,
-                     stream, static_cast<const i32x4*>(src), n_vec, sink);
+  launch_kernel(hbm_read_probe_kernel, dim3(static_cast<unsigned>(grid)), dim3(kProbeThreads), stream,
+                ev.start, ev.stop, static_cast<const i32x4*>(src), n_vec, sink);
   return hipGetLastError();
 }
 

@@ -10,26 +10,29 @@
 // same selection on FP16 score keys, refining only the key bits the bin has
 // not fixed.
 //
+// Barriers here order LDS only (lds_barrier): no thread of a workgroup reads
+// global memory that another thread of it wrote.
+//
 // Launch sequence of one topk_rows call (one stream, no host sync):
 //   [hist == NULL only] topk_zero_hist + topk_hist: build the row histograms
 //                  in the workspace (the first pass the producer's fused
 //                  histogram normally replaces)
-//   topk_count     many workgroups per row, one 4096-score chunk each: the
-//                  threshold bin b* from the histogram; counts of the chunk's
-//                  scores above b* and in b* go to counts[row][chunk] (plain
-//                  stores, no atomics); chunk 0 publishes b*
-//   topk_write     the same chunks again: each workgroup adds up the counts of
-//                  the chunks before it, rescans its chunk and writes the
-//                  columns above b* to the output and the (key, column)
-//                  candidates of b* to the row's candidate list, at exact
-//                  positions (a block-wide scan keeps column order)
-//   topk_refine    one workgroup per row checks the real counts against b*:
-//                  if they confirm it, a radix select on the candidates'
-//                  remaining key bits finishes the row; otherwise an exact
-//                  radix select over the whole row does.  A kernel of its own:
-//                  a last-workgroup handoff inside topk_write would need a
-//                  device-scope fence per workgroup, which on this multi-die
-//                  part writes back and invalidates the L2 under the others.
+//   topk_scan      many workgroups per row, one 4096-score chunk each: the
+//                  threshold bin b* from the histogram (requested together
+//                  with the chunk's scores); the chunk's columns above b* and
+//                  its (key, column) candidates of b* go, in column order, to
+//                  the chunk's own slots in the workspace, and its two counts
+//                  to counts[row][chunk] (plain stores, no atomics)
+//   topk_refine    one workgroup per row adds up the chunk counts and checks
+//                  them against b*: if they confirm it, the columns above b*
+//                  are gathered into the output and the candidates into LDS,
+//                  where a radix select on the remaining key bits finishes the
+//                  row; otherwise an exact radix select over the whole row
+//                  does.  Chunk slots rather than exact output positions keep
+//                  the scan free of any cross-workgroup order: positions
+//                  would need either a second pass over the scores or a
+//                  device-scope handoff between workgroups, which on this
+//                  multi-die part means L2 write-backs under the other dies.
 //
 // Why the result is exact whatever the histogram holds: bin() is
 // non-increasing in the score and in its FP16 rounding, so every column of a
@@ -47,20 +50,27 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 4096;                // scores per workgroup
 constexpr int kPerIter = kThreads * 4;      // scores per block-wide step
+constexpr int kPerThread = kChunk / kThreads;  // consecutive scores per thread in the scan
 constexpr int kAllBins = kBins;             // threshold meaning "every live score"
 constexpr int kRefineThreads = 512;         // one workgroup per row finishes it
+static_assert(kBins == 4 * kThreads, "threshold_bin: four bins per thread");
 
 struct RowMeta {
-  int bstar;  // threshold bin the count pass used
+  int bstar;  // threshold bin the scan pass used
   int pad0, pad1, pad2;
 };
 
+// Scratch of one call.  Per (row, chunk) slot: up to gt_cap columns above b*
+// (gt_cap = min(k, 4096): a chunk with k of them already makes the row's
+// count contradict b*) and up to 4096 candidates of b*.
 struct Workspace {
   RowMeta* meta;   // [rows]
   int2* counts;    // [rows][max_chunks]: (above b*, in b*) per chunk
   int* hist;       // [rows][1024]: histograms built when the caller has none
-  uint2* cand;     // [rows][kCandCap]: (key, column) of the threshold bin
+  int* gt;         // [rows][max_chunks][gt_cap]: columns above b*
+  uint2* eq;       // [rows][max_chunks][kChunk]: (key, column) in b*
   int max_chunks;
+  int gt_cap;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -69,23 +79,30 @@ __host__ __device__ inline int chunks_for(int64_t stride) {
   return static_cast<int>((stride + kChunk - 1) / kChunk);
 }
 
-__host__ __device__ inline size_t workspace_size(int rows, int max_chunks) {
-  return align256(sizeof(RowMeta) * rows) + align256(sizeof(int2) * static_cast<size_t>(rows) * max_chunks) +
+__host__ __device__ inline int gt_cap_for(int k) { return k < kChunk ? k : kChunk; }
+
+__host__ __device__ inline size_t workspace_size(int rows, int max_chunks, int k) {
+  const size_t slots = static_cast<size_t>(rows) * max_chunks;
+  return align256(sizeof(RowMeta) * rows) + align256(sizeof(int2) * slots) +
          align256(sizeof(int) * kBins * static_cast<size_t>(rows)) +
-         sizeof(uint2) * kCandCap * static_cast<size_t>(rows);
+         align256(sizeof(int) * gt_cap_for(k) * slots) + sizeof(uint2) * kChunk * slots;
 }
 
-inline Workspace carve(void* base, int rows, int max_chunks) {
+inline Workspace carve(void* base, int rows, int max_chunks, int k) {
+  const size_t slots = static_cast<size_t>(rows) * max_chunks;
   char* p = static_cast<char*>(base);
   Workspace w;
   w.meta = reinterpret_cast<RowMeta*>(p);
   p += align256(sizeof(RowMeta) * rows);
   w.counts = reinterpret_cast<int2*>(p);
-  p += align256(sizeof(int2) * static_cast<size_t>(rows) * max_chunks);
+  p += align256(sizeof(int2) * slots);
   w.hist = reinterpret_cast<int*>(p);
   p += align256(sizeof(int) * kBins * static_cast<size_t>(rows));
-  w.cand = reinterpret_cast<uint2*>(p);
+  w.gt = reinterpret_cast<int*>(p);
+  p += align256(sizeof(int) * gt_cap_for(k) * slots);
+  w.eq = reinterpret_cast<uint2*>(p);
   w.max_chunks = max_chunks;
+  w.gt_cap = gt_cap_for(k);
   return w;
 }
 
@@ -111,11 +128,11 @@ __device__ __forceinline__ int block_sum(int v, int* s_red) {
   v = wave_sum(v);
   const int wave = threadIdx.x / kWave;
   if (__lane_id() == 0) s_red[wave] = v;
-  __syncthreads();
+  lds_barrier();
   int t = 0;
 #pragma unroll
   for (int w = 0; w < NT / kWave; ++w) t += s_red[w];
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -125,7 +142,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int* total) {
   const int inc = wave_inclusive_scan(v);
   const int wave = threadIdx.x / kWave;
   if (__lane_id() == kWave - 1) s_red[wave] = inc;
-  __syncthreads();
+  lds_barrier();
   int before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < NT / kWave; ++w) {
@@ -133,22 +150,16 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int* total) {
     before += (w < wave) ? t : 0;
     all += t;
   }
-  __syncthreads();
+  lds_barrier();
   *total = all;
   return before + inc - v;
 }
 
 // Threshold bin of a row: the first bin whose inclusive prefix count reaches
-// k, or kAllBins when the histogram holds at most k scores.
-__device__ int threshold_bin(const int* __restrict__ h, int k, int* s_red) {
-  constexpr int per = kBins / kThreads;  // 4 bins per thread
-  int c[per];
-  int sum = 0;
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    c[i] = h[threadIdx.x * per + i];
-    sum += c[i];
-  }
+// k, or kAllBins when the histogram holds at most k scores.  Thread t holds
+// the counts of bins 4t .. 4t+3.
+__device__ int threshold_bin(const int (&c)[4], int k, int* s_red) {
+  const int sum = c[0] + c[1] + c[2] + c[3];
   int total = 0;
   int run = block_excl_scan(sum, s_red, &total);
   if (total <= k) return kAllBins;
@@ -156,29 +167,16 @@ __device__ int threshold_bin(const int* __restrict__ h, int k, int* s_red) {
   // in any histogram this call produced; for a foreign one any bin is fine,
   // the counts checked later decide).
   if (threadIdx.x == 0) s_red[kWaves] = kAllBins;
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
-  for (int i = 0; i < per; ++i) {
-    if (run < k && run + c[i] >= k) s_red[kWaves] = threadIdx.x * per + i;
+  for (int i = 0; i < 4; ++i) {
+    if (run < k && run + c[i] >= k) s_red[kWaves] = threadIdx.x * 4 + i;
     run += c[i];
   }
-  __syncthreads();
+  lds_barrier();
   const int bstar = s_red[kWaves];
-  __syncthreads();
+  lds_barrier();
   return bstar;
-}
-
-// Classify four consecutive scores against b*.
-__device__ __forceinline__ void classify4(const f32x4& v, int s, int s1, int bstar, bool (&gt)[4],
-                                          bool (&eq)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t hb = f16_bits_rn(v[e]);
-    const bool live = (s + e < s1) && !f16_is_nan(hb);
-    const int bin = coarse_bin_f16(hb);
-    gt[e] = live && bin < bstar;
-    eq[e] = live && bin == bstar;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -200,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
   const int s0 = blockIdx.x * kChunk;
   if (s0 >= len) return;
   for (int i = threadIdx.x; i < kBins; i += kThreads) s_hist[i] = 0;
-  __syncthreads();
+  lds_barrier();
   const float* x = logits + static_cast<int64_t>(row) * stride;
   const int s1 = min(len, s0 + kChunk);
   for (int s = s0 + threadIdx.x * 4; s < s1; s += kPerIter) {
@@ -213,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   unsigned long long* gh = reinterpret_cast<unsigned long long*>(hist_out + static_cast<int64_t>(row) * kBins);
   const uint2* sh = reinterpret_cast<const uint2*>(s_hist);
   for (int i = threadIdx.x; i < kBins / 2; i += kThreads) {
@@ -223,46 +221,74 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void topk_count_kernel(const float* __restrict__ logits,
-                                                              int64_t stride,
-                                                              const int32_t* __restrict__ hist,
-                                                              const int32_t* __restrict__ lens, int k,
-                                                              Workspace ws) {
+// Thread t of a chunk's workgroup takes 16 consecutive columns; a block scan
+// of the per-thread counts gives every column its position in the chunk's
+// slot, so each slot list is in column order.
+template <int KEY>
+__global__ __launch_bounds__(kThreads) void topk_scan_kernel(const float* __restrict__ logits,
+                                                             int64_t stride,
+                                                             const int32_t* __restrict__ hist,
+                                                             const int32_t* __restrict__ lens, int k,
+                                                             Workspace ws) {
   __shared__ int s_red[kWaves + 1];
   const int row = blockIdx.y;
   const int c = blockIdx.x;
   const int len = clamp_len(lens, row, stride);
   if (c >= row_chunks(len)) return;
-  const int* h = (hist ? hist : ws.hist) + static_cast<int64_t>(row) * kBins;
-  const int bstar = threshold_bin(h, k, s_red);
-  if (c == 0 && threadIdx.x == 0) ws.meta[row] = RowMeta{bstar, 0, 0, 0};
 
+  // The histogram and the chunk's scores are requested together.
+  const int* h = (hist ? hist : ws.hist) + static_cast<int64_t>(row) * kBins + threadIdx.x * 4;
+  const int2 h01 = *reinterpret_cast<const int2*>(h);  // 8-B aligned
+  const int2 h23 = *reinterpret_cast<const int2*>(h + 2);
   const float* x = logits + static_cast<int64_t>(row) * stride;
-  const int s0 = c * kChunk;
-  const int s1 = min(len, s0 + kChunk);
-  int ng = 0, ne = 0;
-  for (int base = s0; base < s1; base += kPerIter) {
-    const int s = base + threadIdx.x * 4;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (s < s1) v = *reinterpret_cast<const f32x4*>(x + s);
-    bool gt[4], eq[4];
-    classify4(v, s, s1, bstar, gt, eq);
+  const int s0 = c * kChunk + threadIdx.x * kPerThread;
+  f32x4 v[kPerThread / 4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ng += gt[e];
-      ne += eq[e];
-    }
+  for (int i = 0; i < kPerThread / 4; ++i) {
+    // In bounds: s0 + 4i < len <= stride, and both are multiples of 4.
+    v[i] = s0 + 4 * i < len ? *reinterpret_cast<const f32x4*>(x + s0 + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Both counts at once: each is at most kChunk < 2^16.
-  const int both = block_sum(ng | (ne << 16), s_red);
-  if (threadIdx.x == 0)
-    ws.counts[static_cast<int64_t>(row) * ws.max_chunks + c] = int2{both & 0xFFFF, both >> 16};
+  const int hc[4] = {h01.x, h01.y, h23.x, h23.y};
+  const int bstar = threshold_bin(hc, k, s_red);
+
+  uint32_t gmask = 0u, emask = 0u;  // bit e: column s0 + e
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const uint32_t hb = f16_bits_rn(v[e / 4][e % 4]);
+    const bool live = s0 + e < len && !f16_is_nan(hb);
+    const int bin = coarse_bin_f16(hb);
+    gmask |= static_cast<uint32_t>(live && bin < bstar) << e;
+    emask |= static_cast<uint32_t>(live && bin == bstar) << e;
+  }
+  // Both counts in one scan: each is at most kChunk < 2^16.
+  int tot = 0;
+  const int pre = block_excl_scan(__popc(gmask) | (__popc(emask) << 16), s_red, &tot);
+  const int64_t slot = static_cast<int64_t>(row) * ws.max_chunks + c;
+  int* gt = ws.gt + slot * ws.gt_cap;
+  uint2* eq = ws.eq + slot * kChunk;
+  int og = pre & 0xFFFF, oe = pre >> 16;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    if ((gmask >> e) & 1u) {
+      if (og < ws.gt_cap) gt[og] = s0 + e;
+      ++og;
+    }
+    if ((emask >> e) & 1u) eq[oe++] = uint2{score_key<KEY>(v[e / 4][e % 4]), static_cast<uint32_t>(s0 + e)};
+  }
+  if (threadIdx.x == 0) {
+    ws.counts[slot] = int2{tot & 0xFFFF, tot >> 16};
+    if (c == 0) ws.meta[row] = RowMeta{bstar, 0, 0, 0};
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Shared memory of the refine pass.
 struct RefineShared {
   uint2 cand[kCandCap];   // 64 KiB
+  int pre_g[kRefineThreads];  // a block of chunks: offsets of their slot lists
+  int pre_e[kRefineThreads];
+  int cnt_g[kRefineThreads];  // and their lengths
+  int cnt_e[kRefineThreads];
   int digit_hist[256];
   int red[kRefineThreads / kWave + 4];
   int out_pos;
@@ -275,17 +301,14 @@ __device__ __forceinline__ void block_or_and(uint32_t o, uint32_t a, RefineShare
     sh.red_or = 0u;
     sh.red_and = 0xFFFFFFFFu;
   }
-  __syncthreads();
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    o |= __shfl_xor(o, off, kWave);
-    a &= __shfl_xor(a, off, kWave);
-  }
+  lds_barrier();
+  o = wave_or(o);
+  a = wave_and(a);
   if (__lane_id() == 0) {
     atomicOr(&sh.red_or, o);
     atomicAnd(&sh.red_and, a);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Given digit_hist (256 counts), the digit d at which the running count taken
@@ -313,10 +336,10 @@ __device__ int pick_digit(RefineShared& sh, int need, bool descending, int* befo
       run += c[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int d = sh.bcast[0];
   *before = sh.bcast[1];
-  __syncthreads();
+  lds_barrier();
   return d;
 }
 
@@ -340,12 +363,12 @@ __device__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above
     if (shift < 0) shift = 0;
     while (true) {
       for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
-      __syncthreads();
+      lds_barrier();
       for (int i = threadIdx.x; i < n; i += kRefineThreads) {
         const uint32_t key = sh.cand[i].x;
         if (((key ^ prefix) & fixed) == 0u) atomicAdd(&sh.digit_hist[(key >> shift) & 0xFFu], 1);
       }
-      __syncthreads();
+      lds_barrier();
       int before = 0;
       const int d = pick_digit(sh, need, true, &before);
       need -= before;
@@ -360,50 +383,13 @@ __device__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above
   return prefix;
 }
 
-// Among LDS candidates with key == T, the need-th smallest column.
-__device__ uint32_t select_col_lds(RefineShared& sh, int n, uint32_t T, int need) {
-  uint32_t o = 0u, a = 0xFFFFFFFFu;
-  for (int i = threadIdx.x; i < n; i += kRefineThreads) {
-    const uint2 c = sh.cand[i];
-    if (c.x == T) {
-      o |= c.y;
-      a &= c.y;
-    }
-  }
-  block_or_and(o, a, sh);
-  const uint32_t diff = sh.red_or ^ sh.red_and;
-  uint32_t prefix = sh.red_and & ~diff;
-  if (diff) {
-    uint32_t fixed = ~diff;
-    int shift = top_bit(diff) - 7;
-    if (shift < 0) shift = 0;
-    while (true) {
-      for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
-      __syncthreads();
-      for (int i = threadIdx.x; i < n; i += kRefineThreads) {
-        const uint2 c = sh.cand[i];
-        if (c.x == T && ((c.y ^ prefix) & fixed) == 0u) atomicAdd(&sh.digit_hist[(c.y >> shift) & 0xFFu], 1);
-      }
-      __syncthreads();
-      int before = 0;
-      const int d = pick_digit(sh, need, false, &before);
-      need -= before;
-      prefix |= static_cast<uint32_t>(d) << shift;
-      fixed |= 0xFFu << shift;
-      if (shift == 0) break;
-      shift = shift >= 8 ? shift - 8 : 0;
-    }
-  }
-  return prefix;
-}
-
 // Append this thread's column to the output through a block-wide LDS counter.
 __device__ __forceinline__ void emit(RefineShared& sh, int32_t* out, int k, bool take, int col) {
   const uint64_t m = __ballot(take);
   if (!m) return;
   int pos = 0;
   if (__lane_id() == 0) pos = atomicAdd(&sh.out_pos, __popcll(m));
-  pos = __shfl(pos, 0, kWave) + lanes_below(m);
+  pos = __builtin_amdgcn_readlane(pos, 0) + lanes_below(m);
   if (take && pos < k) out[pos] = col;
 }
 
@@ -416,13 +402,13 @@ __device__ void whole_row_select(RefineShared& sh, const float* __restrict__ x, 
   for (int s = threadIdx.x; s < len; s += kRefineThreads) cnt += (x[s] == x[s]) ? 1 : 0;
   const int n = block_sum<kRefineThreads>(cnt, sh.red);
   if (threadIdx.x == 0) sh.out_pos = 0;
-  __syncthreads();
+  lds_barrier();
   if (n <= k) {
     for (int s0 = 0; s0 < len; s0 += kRefineThreads) {
       const int s = s0 + threadIdx.x;
       emit(sh, out, k, s < len && x[s] == x[s], s);
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = n + threadIdx.x; i < k; i += kRefineThreads) out[i] = -1;
     return;
   }
@@ -431,14 +417,14 @@ __device__ void whole_row_select(RefineShared& sh, const float* __restrict__ x, 
   int need = k;
   for (int shift = kKeyBits - 8; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int s = threadIdx.x; s < len; s += kRefineThreads) {
       const float v = x[s];
       if (v != v) continue;
       const uint32_t key = score_key<KEY>(v);
       if (((key ^ prefix) & fixed) == 0u) atomicAdd(&sh.digit_hist[(key >> shift) & 0xFFu], 1);
     }
-    __syncthreads();
+    lds_barrier();
     int before = 0;
     const int d = pick_digit(sh, need, true, &before);
     need -= before;
@@ -466,70 +452,83 @@ __device__ void whole_row_select(RefineShared& sh, const float* __restrict__ x, 
   }
 }
 
-template <int KEY>
-__global__ __launch_bounds__(kThreads) void topk_write_kernel(const float* __restrict__ logits,
-                                                              int64_t stride,
-                                                              const int32_t* __restrict__ lens, int k,
-                                                              int32_t* __restrict__ indices,
-                                                              Workspace ws) {
-  __shared__ int s_red[kWaves];
-  const int row = blockIdx.y;
-  const int c = blockIdx.x;
-  const int len = clamp_len(lens, row, stride);
-  const int nch = row_chunks(len);
-  if (c >= nch) return;
-  const int bstar = ws.meta[row].bstar;
-  const int2* cnt = ws.counts + static_cast<int64_t>(row) * ws.max_chunks;
-  const float* x = logits + static_cast<int64_t>(row) * stride;
-  int32_t* out = indices + static_cast<int64_t>(row) * k;
-  uint2* cand = ws.cand + static_cast<int64_t>(row) * kCandCap;
-
-  // Positions of this chunk's columns: the counts of the chunks before it.
-  int pg = 0, pe = 0;
-  for (int i = threadIdx.x; i < c; i += kThreads) {
-    const int2 v = cnt[i];
-    pg += v.x;
-    pe += v.y;
-  }
-  int run_g = block_sum(pg, s_red);
-  int run_e = block_sum(pe, s_red);
-
-  const int s0 = c * kChunk;
-  const int s1 = min(len, s0 + kChunk);
-  for (int base = s0; base < s1; base += kPerIter) {
-    const int s = base + threadIdx.x * 4;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (s < s1) v = *reinterpret_cast<const f32x4*>(x + s);
-    bool gt[4], eq[4];
-    classify4(v, s, s1, bstar, gt, eq);
-    int tg = 0, te = 0;
+template <int NT>
+__device__ __forceinline__ int block_max(int v, int* s_red) {
+  v = wave_max(v);
+  if (__lane_id() == 0) s_red[threadIdx.x / kWave] = v;
+  lds_barrier();
+  int m = s_red[0];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tg += gt[e];
-      te += eq[e];
-    }
-    int tot = 0;
-    const int pre = block_excl_scan(tg | (te << 16), s_red, &tot);
-    int og = run_g + (pre & 0xFFFF), oe = run_e + (pre >> 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (gt[e]) {
-        if (og < k) out[og] = s + e;
-        ++og;
-      }
-      if (eq[e]) {
-        if (oe < kCandCap) cand[oe] = uint2{score_key<KEY>(v[e]), static_cast<uint32_t>(s + e)};
-        ++oe;
-      }
-    }
-    run_g += tot & 0xFFFF;
-    run_e += tot >> 16;
-  }
-
+  for (int w = 1; w < NT / kWave; ++w) m = max(m, s_red[w]);
+  lds_barrier();
+  return m;
 }
 
-// Finishes each row after the write pass: checks the real counts against b*
-// and either refines the candidates or selects over the whole row.
+// Concatenates a row's chunk slots in chunk order: the columns above b* to
+// out[0 .. n_gt), the candidates to sh.cand (or, when cand_out is given, only
+// their columns to cand_out[0 .. n_eq)), so both lists stay in column order.
+// Each chunk's counts must fit its slot, which the caller's count check
+// guarantees.  first = the counts of chunk threadIdx.x, already loaded.
+//
+// Chunks are taken kRefineThreads at a time; each gets tpc threads (a power
+// of two), and a thread copies kGatherPer consecutive entries of both of its
+// chunk's lists.  Every load of a round is issued before its first store, so
+// a round costs one memory round trip; loads are unconditional (clamped into
+// the slot), because a load under a branch would make the compiler wait for
+// every load issued before it.
+constexpr int kGatherPer = 8;
+__device__ void gather_slots(RefineShared& sh, const Workspace& ws, int64_t slot0, int nch, int2 first,
+                             int32_t* __restrict__ out, int32_t* __restrict__ cand_out) {
+  int base_g = 0, base_e = 0;
+  for (int cb = 0; cb < nch; cb += kRefineThreads) {
+    const int j = cb + threadIdx.x;
+    const int2 v = cb == 0 ? first : (j < nch ? ws.counts[slot0 + j] : int2{0, 0});
+    int tot_g = 0, tot_e = 0;
+    const int pg = block_excl_scan<kRefineThreads>(v.x, sh.red, &tot_g);
+    const int pe = block_excl_scan<kRefineThreads>(v.y, sh.red, &tot_e);
+    const int longest = block_max<kRefineThreads>(max(v.x, v.y), sh.red);
+    sh.pre_g[threadIdx.x] = pg;
+    sh.pre_e[threadIdx.x] = pe;
+    sh.cnt_g[threadIdx.x] = v.x;
+    sh.cnt_e[threadIdx.x] = v.y;
+    lds_barrier();
+    const int nb = min(kRefineThreads, nch - cb);
+    const int tpc = 1 << (31 - __clz(kRefineThreads / nb));  // threads per chunk
+    const int c = static_cast<int>(threadIdx.x) / tpc;
+    const bool active = c < nb;
+    const int cc = active ? c : nb - 1;
+    const int cg = sh.cnt_g[cc], ce = sh.cnt_e[cc], og = base_g + sh.pre_g[cc], oe = base_e + sh.pre_e[cc];
+    const int* gsrc = ws.gt + (slot0 + cb + cc) * ws.gt_cap;
+    const uint2* esrc = ws.eq + (slot0 + cb + cc) * kChunk;
+    const int glast = max(cg - 1, 0), elast = max(ce - 1, 0);
+    for (int r0 = 0; r0 < longest; r0 += tpc * kGatherPer) {
+      const int l0 = r0 + (static_cast<int>(threadIdx.x) % tpc) * kGatherPer;
+      int gv[kGatherPer];
+      uint2 ev[kGatherPer];
+#pragma unroll
+      for (int u = 0; u < kGatherPer; ++u) {
+        gv[u] = gsrc[min(l0 + u, glast)];
+        ev[u] = esrc[min(l0 + u, elast)];
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherPer; ++u) {
+        const int l = l0 + u;
+        if (active && l < cg) out[og + l] = gv[u];
+        if (active && l < ce) {
+          if (cand_out) cand_out[oe + l] = static_cast<int32_t>(ev[u].y);
+          else sh.cand[oe + l] = ev[u];
+        }
+      }
+    }
+    base_g += tot_g;
+    base_e += tot_e;
+    lds_barrier();
+  }
+}
+
+// Finishes each row after the scan pass: checks the real counts against b*,
+// then gathers the chunk slots and refines the candidates, or selects over
+// the whole row.
 template <int KEY>
 __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float* __restrict__ logits,
                                                                      int64_t stride,
@@ -541,14 +540,15 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float
   const int len = clamp_len(lens, row, stride);
   const int nch = row_chunks(len);
   const int bstar = ws.meta[row].bstar;
-  const int2* cnt = ws.counts + static_cast<int64_t>(row) * ws.max_chunks;
+  const int64_t slot0 = static_cast<int64_t>(row) * ws.max_chunks;
   const float* x = logits + static_cast<int64_t>(row) * stride;
   int32_t* out = indices + static_cast<int64_t>(row) * k;
-  const uint2* cand = ws.cand + static_cast<int64_t>(row) * kCandCap;
 
-  int tg = 0, te = 0;
-  for (int i = threadIdx.x; i < nch; i += kRefineThreads) {
-    const int2 v = cnt[i];
+  // Chunk counts: thread t keeps those of chunk t for the gather.
+  const int2 first = static_cast<int>(threadIdx.x) < nch ? ws.counts[slot0 + threadIdx.x] : int2{0, 0};
+  int tg = first.x, te = first.y;
+  for (int i = kRefineThreads + threadIdx.x; i < nch; i += kRefineThreads) {
+    const int2 v = ws.counts[slot0 + i];
     tg += v.x;
     te += v.y;
   }
@@ -561,33 +561,39 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float
     whole_row_select<KEY>(sh, x, len, k, out);
     return;
   }
-  if (bstar == kAllBins) {
-    for (int i = n_gt + threadIdx.x; i < k; i += kRefineThreads) out[i] = -1;
-    return;
-  }
   const int need = k - n_gt;
-  if (need == n_eq) {
-    for (int i = threadIdx.x; i < n_eq; i += kRefineThreads) out[n_gt + i] = static_cast<int>(cand[i].y);
+  if (bstar == kAllBins || need == n_eq) {
+    // Every candidate is taken (there are none below the all-bins threshold).
+    gather_slots(sh, ws, slot0, nch, first, out, out + n_gt);
+    for (int i = n_gt + n_eq + threadIdx.x; i < k; i += kRefineThreads) out[i] = -1;
     return;
   }
-  for (int i = threadIdx.x; i < n_eq; i += kRefineThreads) sh.cand[i] = cand[i];
+  gather_slots(sh, ws, slot0, nch, first, out, nullptr);
   if (threadIdx.x == 0) sh.out_pos = n_gt;
-  __syncthreads();
+  lds_barrier();
   int above = 0;
   const uint32_t T = select_key_lds(sh, n_eq, need, &above);
+  // Every key above T is taken, and of the keys equal to T the lowest
+  // columns: the candidate list is in column order, so those are the first
+  // need - above ties in list order.  Thread t ranks a run of consecutive
+  // candidates.
   const int ties_needed = need - above;
-  int tc = 0;
-  for (int i = threadIdx.x; i < n_eq; i += kRefineThreads) tc += sh.cand[i].x == T ? 1 : 0;
-  const int ties = block_sum<kRefineThreads>(tc, sh.red);
-  uint32_t col_cut = 0xFFFFFFFFu;
-  if (ties > ties_needed) col_cut = select_col_lds(sh, n_eq, T, ties_needed);
-  for (int i0 = 0; i0 < n_eq; i0 += kRefineThreads) {
-    const int i = i0 + threadIdx.x;
+  const int per = (n_eq + kRefineThreads - 1) / kRefineThreads;
+  const int i_begin = min(n_eq, static_cast<int>(threadIdx.x) * per);
+  const int i_end = min(n_eq, i_begin + per);
+  int my_ties = 0;
+  for (int i = i_begin; i < i_end; ++i) my_ties += sh.cand[i].x == T ? 1 : 0;
+  int all_ties = 0;
+  int rank = block_excl_scan<kRefineThreads>(my_ties, sh.red, &all_ties);
+  for (int u = 0; u < per; ++u) {
+    const int i = i_begin + u;
     bool take = false;
     int col = 0;
-    if (i < n_eq) {
+    if (i < i_end) {
       const uint2 cd = sh.cand[i];
-      take = cd.x > T || (cd.x == T && cd.y <= col_cut);
+      const bool tie = cd.x == T;
+      take = cd.x > T || (tie && rank < ties_needed);
+      rank += tie ? 1 : 0;
       col = static_cast<int>(cd.y);
     }
     emit(sh, out, k, take, col);
@@ -596,35 +602,34 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float
 
 }  // namespace
 
-size_t topk_workspace_size(int32_t rows, int64_t logits_stride) {
-  if (rows <= 0 || logits_stride <= 0) return 0;
-  return workspace_size(rows, chunks_for(logits_stride));
+size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k) {
+  if (rows <= 0 || logits_stride <= 0 || k <= 0) return 0;
+  return workspace_size(rows, chunks_for(logits_stride), k);
 }
 
-hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream) {
+template <int KEY>
+void launch_select(const TopkArgs& a, const Workspace& ws, dim3 grid, hipStream_t stream,
+                   hipEvent_t start, hipEvent_t stop) {
+  launch_kernel(topk_scan_kernel<KEY>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
+                a.logits_stride, a.hist, a.context_lens, a.k, ws);
+  launch_kernel(topk_refine_kernel<KEY>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop,
+                a.logits, a.logits_stride, a.context_lens, a.k, a.indices, ws);
+}
+
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
   const int max_chunks = chunks_for(a.logits_stride);
-  const Workspace ws = carve(a.workspace, a.rows, max_chunks);
+  const Workspace ws = carve(a.workspace, a.rows, max_chunks, a.k);
   const dim3 grid(static_cast<unsigned>(max_chunks), static_cast<unsigned>(a.rows));
-  const int32_t* hist = a.hist;
-  if (hist == nullptr) {
-    hipLaunchKernelGGL(topk_zero_hist_kernel, dim3(min(1024, (a.rows * kBins + 255) / 256)), dim3(256), 0,
-                       stream, ws.hist, a.rows);
-    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, a.logits, a.logits_stride,
-                       a.context_lens, ws.hist);
+  hipEvent_t start = ev.start;  // recorded by the first kernel of the call
+  if (a.hist == nullptr) {
+    launch_kernel(topk_zero_hist_kernel, dim3(min(1024, (a.rows * kBins + 255) / 256)), dim3(256), stream,
+                  start, nullptr, ws.hist, a.rows);
+    start = nullptr;
+    launch_kernel(topk_hist_kernel, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
+                  a.logits_stride, a.context_lens, ws.hist);
   }
-  hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, stream, a.logits, a.logits_stride, hist,
-                     a.context_lens, a.k, ws);
-  if (a.key_dtype == IDX_KEY_FP32) {
-    hipLaunchKernelGGL(topk_write_kernel<IDX_KEY_FP32>, grid, dim3(kThreads), 0, stream, a.logits,
-                       a.logits_stride, a.context_lens, a.k, a.indices, ws);
-    hipLaunchKernelGGL(topk_refine_kernel<IDX_KEY_FP32>, dim3(a.rows), dim3(kRefineThreads), 0, stream,
-                       a.logits, a.logits_stride, a.context_lens, a.k, a.indices, ws);
-  } else {
-    hipLaunchKernelGGL(topk_write_kernel<IDX_KEY_FP16>, grid, dim3(kThreads), 0, stream, a.logits,
-                       a.logits_stride, a.context_lens, a.k, a.indices, ws);
-    hipLaunchKernelGGL(topk_refine_kernel<IDX_KEY_FP16>, dim3(a.rows), dim3(kRefineThreads), 0, stream,
-                       a.logits, a.logits_stride, a.context_lens, a.k, a.indices, ws);
-  }
+  if (a.key_dtype == IDX_KEY_FP32) launch_select<IDX_KEY_FP32>(a, ws, grid, stream, start, ev.stop);
+  else launch_select<IDX_KEY_FP16>(a, ws, grid, stream, start, ev.stop);
   return hipGetLastError();
 }
 

@@ -48,16 +48,24 @@ def test_status_strings(lib):
     assert "unknown" in pmqa.indexer_status_str(99)
 
 
+def per_row_bytes(stride, k):
+    """The documented layout: a header and a histogram per row; per
+    4096-score chunk a count pair, min(k, 4096) columns and 4096 candidates."""
+    chunks = -(-stride // 4096)
+    return 16 + 4096 + chunks * (8 + 4 * min(k, 4096) + 8 * 4096)
+
+
 def test_workspace_query(lib):
     assert pmqa.topk_workspace_bytes(0, 1024, 2048) == 0
     assert pmqa.topk_workspace_bytes(4, 0, 2048) == 0
-    one = pmqa.topk_workspace_bytes(1, 131072, 2048)
-    eight = pmqa.topk_workspace_bytes(8, 131072, 2048)
-    # per row: a header, one count pair per 4096-score chunk, a 1024-bin
-    # histogram and 8192 (key, column) candidates
-    assert one >= 16 + 32 * 8 + 4096 + 8192 * 8
-    assert eight >= 8 * (16 + 32 * 8 + 4096 + 8192 * 8)
-    assert pmqa.topk_workspace_bytes(8, 1 << 20, 2048) > eight
+    assert pmqa.topk_workspace_bytes(4, 1024, 0) == 0
+    for rows, stride, k in ((1, 131072, 2048), (8, 131072, 2048), (3, 4100, 1), (64, 262144, 8192),
+                            (4, 1 << 20, 2048)):
+        got = pmqa.topk_workspace_bytes(rows, stride, k)
+        want = rows * per_row_bytes(stride, k)
+        assert want <= got <= want + 5 * 256, (rows, stride, k)
+    # columns above the threshold are kept per chunk only up to min(k, 4096)
+    assert pmqa.topk_workspace_bytes(8, 131072, 4096) == pmqa.topk_workspace_bytes(8, 131072, 8192)
 
 
 # Fake but aligned device addresses: every call below fails validation before
@@ -99,6 +107,19 @@ def logits_call(lib, **kw):
 ])
 def test_indexer_logits_rejects(lib, kw, status):
     assert logits_call(lib, **kw) == status
+
+
+def test_timed_variants_share_the_checks(lib):
+    """The timing variants run the same host checks (no event is touched)."""
+    assert lib.indexer_logits_timed(None, A, A, A, A, A, 8, 1, 16, 4, A, 256, None, None,
+                                    None, None) == IDX_EINVAL
+    assert lib.indexer_logits_timed(A, A, A, A, A, A, 8, 5, 16, 4, A, 256, None, None,
+                                    None, None) == IDX_EUNSUPPORTED
+    assert lib.topk_rows_timed(A, 256, None, A, 8, 0, 0, A, A, 1 << 30, None,
+                               None, None) == IDX_EINVAL
+    assert lib.topk_rows_timed(A, 256, None, A, 8, 2048, 0, A, A, 16, None,
+                               None, None) == IDX_EWORKSPACE
+    assert lib.hbm_read_probe_timed(A + 4, 64, A, None, None, None) == IDX_EALIGN
 
 
 def topk_call(lib, **kw):
