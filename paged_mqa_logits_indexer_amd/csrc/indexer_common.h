@@ -119,6 +119,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Lowest set lane of a ballot (lane 0 for an empty one).
+__device__ __forceinline__ int first_lane(uint64_t mask) {
+  return mask ? static_cast<int>(__builtin_ctzll(mask)) : 0;
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),

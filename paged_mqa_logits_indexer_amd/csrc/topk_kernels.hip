@@ -155,6 +155,32 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_red, int* total) {
   return before + inc - v;
 }
 
+// Exclusive prefixes of (a, b) in thread order from one pair of barriers;
+// *total = the block sums.
+template <int NT>
+__device__ __forceinline__ int2 block_excl_scan2(int a, int b, int* s_red, int2* total) {
+  const int ia = wave_inclusive_scan(a);
+  const int ib = wave_inclusive_scan(b);
+  const int wave = threadIdx.x / kWave;
+  if (__lane_id() == kWave - 1) {
+    s_red[2 * wave] = ia;
+    s_red[2 * wave + 1] = ib;
+  }
+  lds_barrier();
+  int ba = 0, bb = 0, ta = 0, tb = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    const int u = s_red[2 * w], v = s_red[2 * w + 1];
+    ba += w < wave ? u : 0;
+    bb += w < wave ? v : 0;
+    ta += u;
+    tb += v;
+  }
+  lds_barrier();
+  *total = int2{ta, tb};
+  return int2{ba + ia - a, bb + ib - b};
+}
+
 // Threshold bin of a row: the first bin whose inclusive prefix count reaches
 // k, or kAllBins when the histogram holds at most k scores.  Thread t holds
 // the counts of bins 4t .. 4t+3.
@@ -290,7 +316,9 @@ struct RefineShared {
   int cnt_g[kRefineThreads];  // and their lengths
   int cnt_e[kRefineThreads];
   int digit_hist[256];
-  int red[kRefineThreads / kWave + 4];
+  int red[2 * (kRefineThreads / kWave) + 4];
+  uint32_t small[kWave];  // the few keys left after a radix pass
+  int small_n;
   int out_pos;
   uint32_t red_or, red_and;
   int bcast[4];
@@ -311,17 +339,16 @@ __device__ __forceinline__ void block_or_and(uint32_t o, uint32_t a, RefineShare
   lds_barrier();
 }
 
-// Given digit_hist (256 counts), the digit d at which the running count taken
-// from the largest digit (descending) or the smallest first reaches `need`;
-// *before = the count strictly before d.
-__device__ int pick_digit(RefineShared& sh, int need, bool descending, int* before) {
+// Given digit_hist (256 counts), the digit d at which the running count
+// taken from the largest digit down first reaches `need`; *before = the count
+// strictly above d, *in_bin = the count of d.
+__device__ int pick_digit(RefineShared& sh, int need, int* before, int* in_bin) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     int c[4], sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pos = lane * 4 + i;
-      c[i] = sh.digit_hist[descending ? 255 - pos : pos];
+      c[i] = sh.digit_hist[255 - (lane * 4 + i)];
       sum += c[i];
     }
     const int inc = wave_inclusive_scan(sum);
@@ -329,9 +356,9 @@ __device__ int pick_digit(RefineShared& sh, int need, bool descending, int* befo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (run < need && run + c[i] >= need) {
-        const int pos = lane * 4 + i;
-        sh.bcast[0] = descending ? 255 - pos : pos;
+        sh.bcast[0] = 255 - (lane * 4 + i);
         sh.bcast[1] = run;
+        sh.bcast[2] = c[i];
       }
       run += c[i];
     }
@@ -339,14 +366,52 @@ __device__ int pick_digit(RefineShared& sh, int need, bool descending, int* befo
   lds_barrier();
   const int d = sh.bcast[0];
   *before = sh.bcast[1];
+  *in_bin = sh.bcast[2];
   lds_barrier();
   return d;
 }
 
 __device__ __forceinline__ int top_bit(uint32_t x) { return 31 - __clz(x); }
 
+// The need-th largest of the m <= 64 candidate keys that match (prefix,
+// fixed): the candidates are collected in LDS and wave 0 ranks each against
+// all the others.  *above = how many of them exceed the result.
+__device__ uint32_t rank_small(RefineShared& sh, int n, uint32_t prefix, uint32_t fixed, int need,
+                               int* above) {
+  for (int i = threadIdx.x; i < n; i += kRefineThreads) {
+    const uint32_t key = sh.cand[i].x;
+    if (((key ^ prefix) & fixed) == 0u) sh.small[atomicAdd(&sh.small_n, 1)] = key;
+  }
+  lds_barrier();
+  if (threadIdx.x < kWave) {
+    const int m = sh.small_n;
+    const int lane = threadIdx.x;
+    const uint32_t kj = lane < m ? sh.small[lane] : 0u;
+    int gtc = 0, gec = 0;
+    for (int i = 0; i < m; ++i) {
+      const uint32_t ki = sh.small[i];
+      gtc += ki > kj ? 1 : 0;
+      gec += ki >= kj ? 1 : 0;
+    }
+    // Lanes holding the answer: fewer than `need` keys above, at least
+    // `need` at or above (equal keys all qualify and agree).
+    const uint64_t ok = __ballot(lane < m && gtc < need && need <= gec);
+    const int src = first_lane(ok);
+    if (lane == 0) {
+      sh.bcast[0] = __builtin_amdgcn_readlane(static_cast<int>(kj), src);
+      sh.bcast[1] = __builtin_amdgcn_readlane(gtc, src);
+    }
+  }
+  lds_barrier();
+  const uint32_t T = static_cast<uint32_t>(sh.bcast[0]);
+  *above = sh.bcast[1];
+  lds_barrier();
+  return T;
+}
+
 // Radix select over the n LDS candidates: the key T of the need-th largest
-// key; *above = how many keys exceed T.  Bits every key shares are skipped.
+// key; *above = how many keys exceed T.  Bits every key shares are skipped,
+// and once a digit holds at most 64 keys they are ranked directly.
 __device__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above) {
   uint32_t o = 0u, a = 0xFFFFFFFFu;
   for (int i = threadIdx.x; i < n; i += kRefineThreads) {
@@ -363,19 +428,26 @@ __device__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above
     if (shift < 0) shift = 0;
     while (true) {
       for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
+      if (threadIdx.x == 0) sh.small_n = 0;
       lds_barrier();
       for (int i = threadIdx.x; i < n; i += kRefineThreads) {
         const uint32_t key = sh.cand[i].x;
         if (((key ^ prefix) & fixed) == 0u) atomicAdd(&sh.digit_hist[(key >> shift) & 0xFFu], 1);
       }
       lds_barrier();
-      int before = 0;
-      const int d = pick_digit(sh, need, true, &before);
+      int before = 0, in_bin = 0;
+      const int d = pick_digit(sh, need, &before, &in_bin);
       need -= before;
       gt += before;
       prefix |= static_cast<uint32_t>(d) << shift;
       fixed |= 0xFFu << shift;
       if (shift == 0) break;
+      if (in_bin <= kWave) {
+        int over = 0;
+        prefix = rank_small(sh, n, prefix, fixed, need, &over);
+        gt += over;
+        break;
+      }
       shift = shift >= 8 ? shift - 8 : 0;
     }
   }
@@ -426,7 +498,8 @@ __device__ void whole_row_select(RefineShared& sh, const float* __restrict__ x, 
     }
     lds_barrier();
     int before = 0;
-    const int d = pick_digit(sh, need, true, &before);
+    int in_bin = 0;
+    const int d = pick_digit(sh, need, &before, &in_bin);
     need -= before;
     prefix |= static_cast<uint32_t>(d) << shift;
     fixed |= 0xFFu << shift;
@@ -464,64 +537,95 @@ __device__ __forceinline__ int block_max(int v, int* s_red) {
   return m;
 }
 
-// Concatenates a row's chunk slots in chunk order: the columns above b* to
-// out[0 .. n_gt), the candidates to sh.cand (or, when cand_out is given, only
-// their columns to cand_out[0 .. n_eq)), so both lists stay in column order.
-// Each chunk's counts must fit its slot, which the caller's count check
-// guarantees.  first = the counts of chunk threadIdx.x, already loaded.
+// The gather of a row's chunk slots, in chunk order: the columns above b*
+// to out[0 .. n_gt), the candidates to sh.cand (or, when cand_out is given,
+// only their columns to cand_out[0 .. n_eq)), so both lists stay in column
+// order.  Each chunk's counts must fit its slot, which the caller's count
+// check guarantees.
 //
 // Chunks are taken kRefineThreads at a time; each gets tpc threads (a power
-// of two), and a thread copies kGatherPer consecutive entries of both of its
-// chunk's lists.  Every load of a round is issued before its first store, so
-// a round costs one memory round trip; loads are unconditional (clamped into
-// the slot), because a load under a branch would make the compiler wait for
-// every load issued before it.
+// of two), and a thread's share of a round is kGatherPer consecutive entries
+// of both of its chunk's lists.  Every load of a round is issued before its
+// first store, so a round costs one memory round trip; loads are
+// unconditional (clamped into the slot), because a load under a branch
+// would make the compiler wait for every load issued before it.
 constexpr int kGatherPer = 8;
-__device__ void gather_slots(RefineShared& sh, const Workspace& ws, int64_t slot0, int nch, int2 first,
-                             int32_t* __restrict__ out, int32_t* __restrict__ cand_out) {
-  int base_g = 0, base_e = 0;
-  for (int cb = 0; cb < nch; cb += kRefineThreads) {
+
+struct GatherLane {
+  int tpc;      // threads per chunk
+  int cc;       // this thread's chunk in the block (clamped to the last one)
+  bool active;  // the block has a chunk for this thread
+  int l0;       // first entry of this thread's share of a round
+};
+
+__device__ __forceinline__ GatherLane gather_lane(int nb) {
+  GatherLane g;
+  g.tpc = 1 << (31 - __clz(kRefineThreads / nb));
+  const int c = static_cast<int>(threadIdx.x) / g.tpc;
+  g.active = c < nb;
+  g.cc = g.active ? c : nb - 1;
+  g.l0 = (static_cast<int>(threadIdx.x) % g.tpc) * kGatherPer;
+  return g;
+}
+
+__device__ __forceinline__ void load_round(const int* gsrc, const uint2* esrc, int l, int glast, int elast,
+                                           int (&gv)[kGatherPer], uint2 (&ev)[kGatherPer]) {
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    gv[u] = gsrc[min(l + u, glast)];
+    ev[u] = esrc[min(l + u, elast)];
+  }
+}
+
+__device__ __forceinline__ void store_round(RefineShared& sh, bool active, int l, int cg, int ce, int og,
+                                            int oe, const int (&gv)[kGatherPer],
+                                            const uint2 (&ev)[kGatherPer], int32_t* __restrict__ out,
+                                            int32_t* __restrict__ cand_out) {
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    if (active && l + u < cg) out[og + l + u] = gv[u];
+    if (active && l + u < ce) {
+      if (cand_out) cand_out[oe + l + u] = static_cast<int32_t>(ev[u].y);
+      else sh.cand[oe + l + u] = ev[u];
+    }
+  }
+}
+
+// The rounds of one block of chunks after any already done: entries from
+// r_begin on.  cg/ce/og/oe: counts and list offsets of this thread's chunk.
+__device__ __forceinline__ void gather_rest(RefineShared& sh, const GatherLane& g, const int* gsrc,
+                                            const uint2* esrc, int r_begin, int cg, int ce, int og, int oe,
+                                            int32_t* __restrict__ out, int32_t* __restrict__ cand_out) {
+  const int step = g.tpc * kGatherPer;
+  for (int r0 = r_begin; r0 < max(cg, ce); r0 += step) {  // per chunk; no barrier inside
+    int gv[kGatherPer];
+    uint2 ev[kGatherPer];
+    load_round(gsrc, esrc, r0 + g.l0, max(cg - 1, 0), max(ce - 1, 0), gv, ev);
+    store_round(sh, g.active, r0 + g.l0, cg, ce, og, oe, gv, ev, out, cand_out);
+  }
+}
+
+// Blocks of chunks from cb0 on (rows of more than kRefineThreads chunks);
+// base_g / base_e = the list entries of the chunks before cb0.
+__device__ void gather_blocks(RefineShared& sh, const Workspace& ws, int64_t slot0, int nch, int cb0,
+                              int base_g, int base_e, int32_t* __restrict__ out,
+                              int32_t* __restrict__ cand_out) {
+  for (int cb = cb0; cb < nch; cb += kRefineThreads) {
     const int j = cb + threadIdx.x;
-    const int2 v = cb == 0 ? first : (j < nch ? ws.counts[slot0 + j] : int2{0, 0});
-    int tot_g = 0, tot_e = 0;
-    const int pg = block_excl_scan<kRefineThreads>(v.x, sh.red, &tot_g);
-    const int pe = block_excl_scan<kRefineThreads>(v.y, sh.red, &tot_e);
-    const int longest = block_max<kRefineThreads>(max(v.x, v.y), sh.red);
-    sh.pre_g[threadIdx.x] = pg;
-    sh.pre_e[threadIdx.x] = pe;
+    const int2 v = j < nch ? ws.counts[slot0 + j] : int2{0, 0};
+    int2 tot;
+    const int2 pre = block_excl_scan2<kRefineThreads>(v.x, v.y, sh.red, &tot);
+    sh.pre_g[threadIdx.x] = pre.x;
+    sh.pre_e[threadIdx.x] = pre.y;
     sh.cnt_g[threadIdx.x] = v.x;
     sh.cnt_e[threadIdx.x] = v.y;
     lds_barrier();
-    const int nb = min(kRefineThreads, nch - cb);
-    const int tpc = 1 << (31 - __clz(kRefineThreads / nb));  // threads per chunk
-    const int c = static_cast<int>(threadIdx.x) / tpc;
-    const bool active = c < nb;
-    const int cc = active ? c : nb - 1;
-    const int cg = sh.cnt_g[cc], ce = sh.cnt_e[cc], og = base_g + sh.pre_g[cc], oe = base_e + sh.pre_e[cc];
-    const int* gsrc = ws.gt + (slot0 + cb + cc) * ws.gt_cap;
-    const uint2* esrc = ws.eq + (slot0 + cb + cc) * kChunk;
-    const int glast = max(cg - 1, 0), elast = max(ce - 1, 0);
-    for (int r0 = 0; r0 < longest; r0 += tpc * kGatherPer) {
-      const int l0 = r0 + (static_cast<int>(threadIdx.x) % tpc) * kGatherPer;
-      int gv[kGatherPer];
-      uint2 ev[kGatherPer];
-#pragma unroll
-      for (int u = 0; u < kGatherPer; ++u) {
-        gv[u] = gsrc[min(l0 + u, glast)];
-        ev[u] = esrc[min(l0 + u, elast)];
-      }
-#pragma unroll
-      for (int u = 0; u < kGatherPer; ++u) {
-        const int l = l0 + u;
-        if (active && l < cg) out[og + l] = gv[u];
-        if (active && l < ce) {
-          if (cand_out) cand_out[oe + l] = static_cast<int32_t>(ev[u].y);
-          else sh.cand[oe + l] = ev[u];
-        }
-      }
-    }
-    base_g += tot_g;
-    base_e += tot_e;
+    const GatherLane g = gather_lane(min(kRefineThreads, nch - cb));
+    gather_rest(sh, g, ws.gt + (slot0 + cb + g.cc) * ws.gt_cap, ws.eq + (slot0 + cb + g.cc) * kChunk, 0,
+                sh.cnt_g[g.cc], sh.cnt_e[g.cc], base_g + sh.pre_g[g.cc], base_e + sh.pre_e[g.cc], out,
+                cand_out);
+    base_g += tot.x;
+    base_e += tot.y;
     lds_barrier();
   }
 }
@@ -544,16 +648,35 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float
   const float* x = logits + static_cast<int64_t>(row) * stride;
   int32_t* out = indices + static_cast<int64_t>(row) * k;
 
-  // Chunk counts: thread t keeps those of chunk t for the gather.
-  const int2 first = static_cast<int>(threadIdx.x) < nch ? ws.counts[slot0 + threadIdx.x] : int2{0, 0};
-  int tg = first.x, te = first.y;
-  for (int i = kRefineThreads + threadIdx.x; i < nch; i += kRefineThreads) {
-    const int2 v = ws.counts[slot0 + i];
-    tg += v.x;
-    te += v.y;
+  // Slots have fixed addresses, so the first round of the gather is
+  // requested together with the counts, before they are known (clamped into
+  // the slot; entries past a chunk's count are never used).
+  const GatherLane g = gather_lane(min(kRefineThreads, nch));
+  const int2 first_raw = ws.counts[slot0 + min(static_cast<int>(threadIdx.x), nch - 1)];  // unconditional load
+  const int2 first = static_cast<int>(threadIdx.x) < nch ? first_raw : int2{0, 0};
+  const int* gsrc = ws.gt + (slot0 + g.cc) * ws.gt_cap;
+  const uint2* esrc = ws.eq + (slot0 + g.cc) * kChunk;
+  int gv[kGatherPer];
+  uint2 ev[kGatherPer];
+  load_round(gsrc, esrc, g.l0, ws.gt_cap - 1, kChunk - 1, gv, ev);
+
+  // One block scan of both counts gives the first block's list offsets and
+  // its totals; longer rows add the sums of the other chunks.
+  int2 tot;
+  const int2 pre = block_excl_scan2<kRefineThreads>(first.x, first.y, sh.red, &tot);
+  int n_gt = tot.x, n_eq = tot.y;
+  if (nch > kRefineThreads) {
+    int tg = 0, te = 0;
+    for (int i = kRefineThreads + threadIdx.x; i < nch; i += kRefineThreads) {
+      const int2 v = ws.counts[slot0 + i];
+      tg += v.x;
+      te += v.y;
+    }
+    int2 rest;
+    block_excl_scan2<kRefineThreads>(tg, te, sh.red, &rest);
+    n_gt += rest.x;
+    n_eq += rest.y;
   }
-  const int n_gt = block_sum<kRefineThreads>(tg, sh.red);
-  const int n_eq = block_sum<kRefineThreads>(te, sh.red);
   bool valid;
   if (bstar == kAllBins) valid = n_gt <= k && n_eq == 0;
   else valid = n_gt < k && n_gt + n_eq >= k && n_eq <= kCandCap;
@@ -562,13 +685,26 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float
     return;
   }
   const int need = k - n_gt;
-  if (bstar == kAllBins || need == n_eq) {
-    // Every candidate is taken (there are none below the all-bins threshold).
-    gather_slots(sh, ws, slot0, nch, first, out, out + n_gt);
+  // When every candidate is taken (none exist below the all-bins threshold)
+  // their columns go straight to the output.
+  const bool direct = bstar == kAllBins || need == n_eq;
+  int32_t* cand_out = direct ? out + n_gt : nullptr;
+  sh.pre_g[threadIdx.x] = pre.x;
+  sh.pre_e[threadIdx.x] = pre.y;
+  sh.cnt_g[threadIdx.x] = first.x;
+  sh.cnt_e[threadIdx.x] = first.y;
+  lds_barrier();
+  {
+    const int cg = sh.cnt_g[g.cc], ce = sh.cnt_e[g.cc], og = sh.pre_g[g.cc], oe = sh.pre_e[g.cc];
+    store_round(sh, g.active, g.l0, cg, ce, og, oe, gv, ev, out, cand_out);
+    gather_rest(sh, g, gsrc, esrc, g.tpc * kGatherPer, cg, ce, og, oe, out, cand_out);
+  }
+  lds_barrier();
+  if (nch > kRefineThreads) gather_blocks(sh, ws, slot0, nch, kRefineThreads, tot.x, tot.y, out, cand_out);
+  if (direct) {
     for (int i = n_gt + n_eq + threadIdx.x; i < k; i += kRefineThreads) out[i] = -1;
     return;
   }
-  gather_slots(sh, ws, slot0, nch, first, out, nullptr);
   if (threadIdx.x == 0) sh.out_pos = n_gt;
   lds_barrier();
   int above = 0;
