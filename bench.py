@@ -19,6 +19,13 @@ the two calls counts.  Events recorded on the stream around the step are
 reported beside them; they also hold the dispatch latency of the first
 kernel.
 
+HBM traffic of the logits kernel comes from two rocprofv3 counter runs of
+this script (FETCH_SIZE, then WRITE_SIZE, with --copy-calibration so that a
+plain device copy of known size is counted too); --traffic-from turns their
+CSVs into bytes per launch, scaled by copy bytes / counted copy bytes, and
+stores them under profiles/ with a digest of the kernel source, so a later
+kernel change voids them.
+
 Prints one JSON line (rank 0, N=1):
   value          mean us per step (logits + top-k kernels), lower is better
   roofline       the logits kernel against the 8 TB/s HBM peak (algorithmic
@@ -42,6 +49,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.json")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.md")
+COPY_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
+LOGITS_KERNEL = "indexer_logits_kernel"
 KERNEL_SOURCES = ("paged_mqa_logits_indexer_amd/csrc/logits_kernel.hip",
                   "paged_mqa_logits_indexer_amd/csrc/indexer_common.h")
 
@@ -100,6 +110,47 @@ def cpu_baseline(x, budget_s: float):
                       f"top-2048 FP32) repeated {len(times)}x, {sum(times):.1f} s"}
 
 
+def read_counters(directory: str, counter: str):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc CSV run:
+    [(dispatch id, kernel name, value)] in dispatch order."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {directory}")
+    return rows
+
+
+def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """HBM bytes per logits launch from the FETCH_SIZE and WRITE_SIZE runs
+    (KiB per dispatch), each scaled by the same counter on the calibration
+    copies: the device-to-device copies after the last logits dispatch."""
+    import numpy as np
+    out = {"workload": workload, "kernel_src_sha": kernel_source_digest(),
+           "copy_bytes": COPY_BYTES}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read_counters(d, counter)
+        last_logits = max(i for i, (_, name, _) in enumerate(rows) if LOGITS_KERNEL in name)
+        logits = [v for _, name, v in rows if LOGITS_KERNEL in name]
+        copies = [v for _, name, v in rows[last_logits + 1:] if "copy" in name.lower()]
+        if not copies:
+            raise SystemExit(f"{counter}: no calibration copy after the last logits dispatch")
+        copy_kib = float(np.mean(copies))
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        out[counter] = {"logits_kib_per_dispatch": float(np.mean(logits)), "dispatches": len(logits),
+                        "copy_kib_per_dispatch": copy_kib, "copies": len(copies), "factor": factor,
+                        "bytes_per_launch": float(np.mean(logits)) * 1024.0 * factor}
+    out["bytes_per_launch"] = int(round(out["FETCH_SIZE"]["bytes_per_launch"]
+                                        + out["WRITE_SIZE"]["bytes_per_launch"]))
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,7 +163,18 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache eviction between steps (warm caches)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timing, run plain 256 MiB device copies (counter runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs into the traffic record (no GPU)")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        tr = traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(tr, f, indent=1)
+        print(json.dumps(tr))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the indexer path has no multi-GPU part "
@@ -212,6 +274,18 @@ def main() -> int:
         torch.cuda.synchronize()
         pts.append(e0.elapsed_time(e1) * 1e3)
     probe_us = float(np.median(pts[5:]))
+
+    if args.copy_calibration:
+        # int32 -> float32: an elementwise copy kernel (a same-dtype copy may
+        # go to a DMA engine, which the counters do not see); 4 B read and
+        # 4 B written per element.
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        for i in range(3):
+            evict()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     mean_logits = float(np.mean(lt))
     achieved = ab["total"] / (mean_logits * 1e-6) / 1e9
