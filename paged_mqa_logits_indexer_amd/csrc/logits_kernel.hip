@@ -42,17 +42,30 @@ namespace {
 #ifndef PMQA_LOGITS_PAGES_PER_WG
 #define PMQA_LOGITS_PAGES_PER_WG 0  // 0: chosen from the grid shape
 #endif
-constexpr int kWaves = 4;
+#ifndef PMQA_LOGITS_WAVES_MANY_ROWS
+#define PMQA_LOGITS_WAVES_MANY_ROWS 8
+#endif
+// Waves per workgroup: 4 for one or two rows per request; 8 for three or
+// four, whose waves hold two to a SIMD (register budget) -- one workgroup of
+// 8 per CU rather than two of 4, so that every wave's start-up loads are
+// issued before any of them streams K (a second workgroup's loads would queue
+// behind the first one's pages in the CU's memory pipeline).
+template <int NN>
+constexpr int kWavesOf = NN >= 3 ? PMQA_LOGITS_WAVES_MANY_ROWS : 4;
+constexpr int kWavesMax = 8;
 constexpr int kPrefetch = PMQA_LOGITS_PREFETCH;  // pages in flight per wave
 constexpr int kRing = kPrefetch + 1;
 #ifndef PMQA_LOGITS_MAX_PPW
 #define PMQA_LOGITS_MAX_PPW 64
 #endif
-constexpr int kMaxPagesPerWg = PMQA_LOGITS_MAX_PPW;  // <= kWaves * kWave: one page-id fetch per wave
-static_assert(kMaxPagesPerWg <= kWaves * kWave, "page ids of a share must fit one fetch");
-// LDS staging of a share's scores: next_n * pages_per_wg * 64 floats at most.
-constexpr int kStageFloats = kMaxPagesPerWg * kPage;  // 16 KiB
-constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxPagesPerWg = PMQA_LOGITS_MAX_PPW;  // <= waves * kWave: one page-id fetch per wave
+static_assert(kMaxPagesPerWg <= 4 * kWave, "page ids of a share must fit one fetch");
+// LDS staging of a share's scores: next_n * pages_per_wg * 64 floats
+// (16 KiB per row of the request).
+template <int NN>
+constexpr int kStageFloats = NN * kMaxPagesPerWg * kPage;
+template <int NN>
+constexpr int kThreadsOf = kWavesOf<NN> * kWave;
 
 struct PageRegs {
   i32x4 v[8];   // [key block kb][half]: K bytes in MFMA operand layout
@@ -103,19 +116,19 @@ __device__ __forceinline__ void load_page(const uint8_t* __restrict__ kv_pages,
 }
 
 // Sum over the four lane groups g of part[kb], leaving lane (n, g) with the
-// total of key block g.  Two exchanges instead of one per key block.
-__device__ __forceinline__ float reduce_scatter4(const float (&part)[4], int g) {
-  const bool hi = g >= 2;
-  const float s0 = hi ? part[0] : part[2];
-  const float s1 = hi ? part[1] : part[3];
-  const float r0 = __shfl_xor(s0, 32, kWave);
-  const float r1 = __shfl_xor(s1, 32, kWave);
-  const float k0 = (hi ? part[2] : part[0]) + r0;
-  const float k1 = (hi ? part[3] : part[1]) + r1;
-  const bool odd = g & 1;
-  const float s = odd ? k0 : k1;
-  const float r = __shfl_xor(s, 16, kWave);
-  return (odd ? k1 : k0) + r;
+// total of key block g.  Lane groups are rows of 16 lanes; gfx950's permlane
+// swaps exchange registers between rows in the VALU (no LDS round trip):
+// permlane32_swap(x, y) trades x of rows 2-3 for y of rows 0-1, so x + y is,
+// in rows 0-1, the pair sum (row r, row r+2) of part[kb] and, in rows 2-3,
+// that of part[kb+2]; permlane16_swap then trades the odd rows of k0 for the
+// even rows of k1, and the same add finishes the four-row sum.
+__device__ __forceinline__ float reduce_scatter4(const float (&part)[4]) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+  const float k0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);  // block 0 (rows 0-1) / 2 (rows 2-3)
+  const float k1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);  // block 1 / 3
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
 template <int NN>
@@ -135,7 +148,6 @@ template <int NN, bool HIST>
 __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi, int ppw,
                                              int lane, const RequestRegs<NN>& rq,
                                              float* s_out, int* s_hist) {
-  const int g = lane >> 4;
   const int key = lp * kPage + lane;
 #pragma unroll
   for (int j = 0; j < NN; ++j) {
@@ -161,7 +173,7 @@ __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi
       }
       part[kb] = s;
     }
-    const float logit = as_stored(reduce_scatter4(part, g) * pr.scale);
+    const float logit = as_stored(reduce_scatter4(part) * pr.scale);
     s_out[(j * ppw + lpi) * kPage + lane] = logit;
     if (key < rq.len[j]) {
       if constexpr (HIST) {
@@ -179,11 +191,13 @@ constexpr int kWavesPerSimd = NN == 1 ? (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 
                                       : (NN == 2 && kPrefetch == 1 ? 3 : 2);
 
 template <int NN, bool HIST>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
-void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
+__global__ __launch_bounds__(kThreadsOf<NN>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
+void indexer_logits_kernel(LogitsArgs a, int pages_per_wg, int lens_first) {
   __shared__ int s_hist[HIST ? NN * kBins : 1];
-  __shared__ __align__(16) float s_out[kStageFloats];  // [NN][pages_per_wg][64] scores
+  __shared__ __align__(16) float s_out[kStageFloats<NN>];  // [NN][pages_per_wg][64] scores
 
+  constexpr int kWaves = kWavesOf<NN>;
+  constexpr int kThreads = kThreadsOf<NN>;
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -193,6 +207,16 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   // No row reads past its block-table row or writes past its logits row.
   const int64_t mk = min(static_cast<int64_t>(a.max_pages) * kPage, a.logits_stride);
   const int max_keys = static_cast<int>(min(mk, static_cast<int64_t>(INT32_MAX)));
+
+  // With many requests of varied length most workgroups of the grid lie past
+  // their request's last page; then the lengths are read first, so those
+  // workgroups leave before requesting Q and page ids.
+  if (lens_first) {
+    int keys = 0;
+#pragma unroll
+    for (int j = 0; j < NN; ++j) keys = max(keys, min(max(a.context_lens[row0 + j], 0), max_keys));
+    if (p0_64 * kPage >= keys) return;  // uniform
+  }
 
   // Everything the first K load depends on is requested at once: the rows'
   // lengths, this wave's page ids (clamped into the block-table row, so the
@@ -300,19 +324,19 @@ DeviceInfo* device_info(int dev) {
   if (!ready[dev]) {
     DeviceInfo d;
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return nullptr;
-    auto occ = [](const void* f) {
+    auto occ = [](const void* f, int threads) {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kThreads, 0) != hipSuccess) n = 1;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, 0) != hipSuccess) n = 1;
       return n > 0 ? n : 1;
     };
-    d.occ[0][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<1, false>));
-    d.occ[0][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<1, true>));
-    d.occ[1][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<2, false>));
-    d.occ[1][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<2, true>));
-    d.occ[2][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<3, false>));
-    d.occ[2][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<3, true>));
-    d.occ[3][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<4, false>));
-    d.occ[3][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<4, true>));
+    d.occ[0][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<1, false>), kThreadsOf<1>);
+    d.occ[0][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<1, true>), kThreadsOf<1>);
+    d.occ[1][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<2, false>), kThreadsOf<2>);
+    d.occ[1][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<2, true>), kThreadsOf<2>);
+    d.occ[2][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<3, false>), kThreadsOf<3>);
+    d.occ[2][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<3, true>), kThreadsOf<3>);
+    d.occ[3][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<4, false>), kThreadsOf<4>);
+    d.occ[3][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<4, true>), kThreadsOf<4>);
     infos[dev] = d;
     ready[dev] = true;  // benign race: every thread computes the same values
   }
@@ -320,9 +344,10 @@ DeviceInfo* device_info(int dev) {
 }
 
 template <int NN, bool HIST>
-hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
-  launch_kernel(indexer_logits_kernel<NN, HIST>, grid, dim3(kThreads), stream, ev.start, ev.stop, a,
-                pages_per_wg);
+hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, int lens_first, hipStream_t stream,
+                  LaunchEvents ev) {
+  launch_kernel(indexer_logits_kernel<NN, HIST>, grid, dim3(kThreadsOf<NN>), stream, ev.start, ev.stop, a,
+                pages_per_wg, lens_first);
   return hipGetLastError();
 }
 
@@ -348,22 +373,22 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
 #if PMQA_LOGITS_PAGES_PER_WG
   ppw = PMQA_LOGITS_PAGES_PER_WG;
 #endif
-  const int64_t ppw_max = kMaxPagesPerWg / a.next_n;  // the staging area holds next_n rows
-  ppw = ppw < 4 ? 4 : (ppw > ppw_max ? ppw_max : ppw);
-  ppw = ppw / kWaves * kWaves;
+  ppw = (ppw + 3) / 4 * 4;  // rounded up: the grid then holds at most one workgroup per CU
+  ppw = ppw < 4 ? 4 : (ppw > kMaxPagesPerWg ? kMaxPagesPerWg : ppw);
   const int64_t chunks = (a.max_pages + ppw - 1) / ppw;
   if (chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
   const int p = static_cast<int>(ppw);
+  const int lens_first = a.B >= 32 ? 1 : 0;
   switch (a.next_n * 2 + (hist ? 1 : 0)) {
-    case 2: return launch<1, false>(a, grid, p, stream, ev);
-    case 3: return launch<1, true>(a, grid, p, stream, ev);
-    case 4: return launch<2, false>(a, grid, p, stream, ev);
-    case 5: return launch<2, true>(a, grid, p, stream, ev);
-    case 6: return launch<3, false>(a, grid, p, stream, ev);
-    case 7: return launch<3, true>(a, grid, p, stream, ev);
-    case 8: return launch<4, false>(a, grid, p, stream, ev);
-    case 9: return launch<4, true>(a, grid, p, stream, ev);
+    case 2: return launch<1, false>(a, grid, p, lens_first, stream, ev);
+    case 3: return launch<1, true>(a, grid, p, lens_first, stream, ev);
+    case 4: return launch<2, false>(a, grid, p, lens_first, stream, ev);
+    case 5: return launch<2, true>(a, grid, p, lens_first, stream, ev);
+    case 6: return launch<3, false>(a, grid, p, lens_first, stream, ev);
+    case 7: return launch<3, true>(a, grid, p, lens_first, stream, ev);
+    case 8: return launch<4, false>(a, grid, p, lens_first, stream, ev);
+    case 9: return launch<4, true>(a, grid, p, lens_first, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }
