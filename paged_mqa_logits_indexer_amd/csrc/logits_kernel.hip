@@ -192,9 +192,13 @@ constexpr int kWavesPerSimd = NN == 1 ? (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 
 
 template <int NN, bool HIST>
 __global__ __launch_bounds__(kThreadsOf<NN>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
-void indexer_logits_kernel(LogitsArgs a, int pages_per_wg, int lens_first) {
+void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   __shared__ int s_hist[HIST ? NN * kBins : 1];
   __shared__ __align__(16) float s_out[kStageFloats<NN>];  // [NN][pages_per_wg][64] scores
+  // Q in MFMA operand layout, [row][head block][half][lane], and the weights:
+  // fetched once per workgroup and read by every wave from here.
+  __shared__ __align__(16) i32x4 s_q[NN >= 2 ? NN * 4 * kWave : 1];
+  __shared__ __align__(16) float s_w[NN >= 2 ? NN * kHeads : 1];
 
   constexpr int kWaves = kWavesOf<NN>;
   constexpr int kThreads = kThreadsOf<NN>;
@@ -208,49 +212,59 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg, int lens_first) {
   const int64_t mk = min(static_cast<int64_t>(a.max_pages) * kPage, a.logits_stride);
   const int max_keys = static_cast<int>(min(mk, static_cast<int64_t>(INT32_MAX)));
 
-  // With many requests of varied length most workgroups of the grid lie past
-  // their request's last page; then the lengths are read first, so those
-  // workgroups leave before requesting Q and page ids.
-  if (lens_first) {
-    int keys = 0;
-#pragma unroll
-    for (int j = 0; j < NN; ++j) keys = max(keys, min(max(a.context_lens[row0 + j], 0), max_keys));
-    if (p0_64 * kPage >= keys) return;  // uniform
-  }
 
-  // Everything the first K load depends on is requested at once: the rows'
-  // lengths, this wave's page ids (clamped into the block-table row, so the
-  // read is in bounds even past the request's last page), Q and the weights.
+  // Start-up loads: this wave's page ids (clamped into the block-table row,
+  // so the read is in bounds even past the request's last page) and the
+  // rows' lengths, which the first K loads depend on; then Q and the
+  // weights.  With one row a wave loads its own Q operands (4 KiB, 3 % of
+  // its share's K).  With several rows Q is read from global memory once per
+  // workgroup, each wave fetching a slice into LDS: with four rows a wave's
+  // operands are 16 KiB, as much as two K pages, and eight waves fetching
+  // them each would hold up the CU's first K pages.
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
   const int64_t last_id = a.max_pages - 1;
   int ids = bt[min(p0_64 + wave + lane * kWaves, last_id)];
   RequestRegs<NN> rq;
-  {
-    const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < NN; ++j) {
-      rq.len[j] = min(max(a.context_lens[row0 + j], 0), max_keys);
+  for (int j = 0; j < NN; ++j) rq.len[j] = min(max(a.context_lens[row0 + j], 0), max_keys);
+  // Slice s = (row j, head block mb, half h) of Q: 64 lanes x 16 bytes.
+  constexpr bool kQViaLds = NN >= 2;
+  constexpr int kSlices = NN * 4;
+  constexpr int kSlicesPerWave = kQViaLds ? (kSlices + kWaves - 1) / kWaves : kSlices;
+  const int m = lane & 15, g = lane >> 4;
+  i32x4 q_slice[kSlicesPerWave];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const uint8_t* qp = a.q + (static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + m) * kDim + g * 16;
-        rq.q[j][mb][0] = *reinterpret_cast<const i32x4*>(qp);
-        rq.q[j][mb][1] = *reinterpret_cast<const i32x4*>(qp + 64);
-        rq.w[j][mb] = *reinterpret_cast<const f32x4*>(a.weights + static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + 4 * g);
-      }
+  for (int t = 0; t < kSlicesPerWave; ++t) {
+    if constexpr (!kQViaLds) {
+      const int j = t >> 2, mb = (t >> 1) & 1, h = t & 1;
+      q_slice[t] = *reinterpret_cast<const i32x4*>(
+          a.q + (static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + m) * kDim + g * 16 + h * 64);
+      continue;
     }
+    const int sl = min(wave + t * kWaves, kSlices - 1);  // clamped: loads stay unconditional
+    const int j = sl >> 2, mb = (sl >> 1) & 1, h = sl & 1;
+    q_slice[t] = *reinterpret_cast<const i32x4*>(
+        a.q + (static_cast<int64_t>(row0 + j) * kHeads + mb * 16 + m) * kDim + g * 16 + h * 64);
+  }
+  f32x4 w_direct[kQViaLds ? 1 : 2];
+  float w_val = 0.f;
+  if constexpr (kQViaLds) {
+    w_val = a.weights[static_cast<int64_t>(row0) * kHeads + min(tid, NN * kHeads - 1)];
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      w_direct[mb] = *reinterpret_cast<const f32x4*>(a.weights + static_cast<int64_t>(row0) * kHeads + mb * 16 + 4 * g);
   }
   int keys_b = 0;
 #pragma unroll
   for (int j = 0; j < NN; ++j) keys_b = max(keys_b, rq.len[j]);
   const int pages_b = (keys_b >> 6) + ((keys_b & (kPage - 1)) != 0);
-  if (p0_64 >= pages_b) return;  // past the request's last page (uniform)
+  // With many requests of varied length most workgroups of the grid lie past
+  // their request's last page; they leave here, before any K is requested.
+  if (p0_64 >= pages_b) return;  // uniform
   const int p0 = static_cast<int>(p0_64);
   const int p1 = static_cast<int>(min(p0_64 + pages_per_wg, static_cast<int64_t>(pages_b)));
 
-  if constexpr (HIST) {
-    for (int i = tid; i < NN * kBins; i += kThreads) s_hist[i] = 0;
-    __syncthreads();
-  }
   const int lpi0 = wave;  // share-local index of the wave's first page
 
   // Pages p0 + wave, + kWaves, ... < p1; lane i of `ids` holds the wave's
@@ -264,16 +278,61 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg, int lens_first) {
     return min(max(id, 0), a.num_pages - 1);
   };
 
-  if (n_mine > 0) {
-    // Ring of kRing page buffers: while page `it` is computed, pages
-    // it+1 .. it+kPrefetch are in flight.  Past the last page the last one
-    // is issued again (it is cached), which keeps every load unconditional.
-    const int lane_off = (lane & 15) * kDim + (lane >> 4) * 16;  // key n, group g
-    PageRegs buf[kRing];
+  // Ring of kRing page buffers: while page `it` is computed, pages
+  // it+1 .. it+kPrefetch are in flight.  Past the last page the last one is
+  // issued again (it is cached), which keeps every load unconditional; a wave
+  // without pages issues its first prefetch all the same.
+  const int lane_off = (lane & 15) * kDim + (lane >> 4) * 16;  // key n, group g
+  PageRegs buf[kRing];
+  const int n_last = max(n_mine, 1) - 1;
+  auto prefetch = [&]() {
 #pragma unroll
     for (int s = 0; s < kPrefetch; ++s) {
-      load_page(a.kv_pages, a.k_scales, page_id(s < n_mine ? s : n_mine - 1), lane_off, lane, buf[s]);
+      load_page(a.kv_pages, a.k_scales, page_id(s < n_last ? s : n_last), lane_off, lane, buf[s]);
     }
+  };
+
+  if constexpr (kQViaLds) {
+    // Several rows: the first K pages are requested before Q is staged, so
+    // they stream while Q arrives and goes through LDS.
+    prefetch();
+#pragma unroll
+    for (int t = 0; t < kSlicesPerWave; ++t) {
+      const int sl = wave + t * kWaves;
+      if (sl < kSlices) s_q[sl * kWave + lane] = q_slice[t];
+    }
+    if (tid < NN * kHeads) s_w[tid] = w_val;
+    if constexpr (HIST) {
+      for (int i = tid; i < NN * kBins; i += kThreads) s_hist[i] = 0;
+    }
+    lds_barrier();  // LDS only: the prefetched K pages stay in flight
+#pragma unroll
+    for (int j = 0; j < NN; ++j) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        rq.q[j][mb][0] = s_q[((j * 2 + mb) * 2 + 0) * kWave + lane];
+        rq.q[j][mb][1] = s_q[((j * 2 + mb) * 2 + 1) * kWave + lane];
+        rq.w[j][mb] = *reinterpret_cast<const f32x4*>(&s_w[j * kHeads + mb * 16 + 4 * g]);
+      }
+    }
+  } else {
+    // One row: the workgroup waits for its start-up loads (Q included), then
+    // all of its waves request K together; measured faster at this shape
+    // than streaming K behind each wave's own Q loads.
+    if constexpr (HIST) {
+      for (int i = tid; i < NN * kBins; i += kThreads) s_hist[i] = 0;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      rq.q[0][mb][0] = q_slice[mb * 2 + 0];
+      rq.q[0][mb][1] = q_slice[mb * 2 + 1];
+      rq.w[0][mb] = w_direct[mb];
+    }
+    prefetch();
+  }
+
+  if (n_mine > 0) {
     for (int it0 = 0; it0 < n_mine; it0 += kRing) {
 #pragma unroll
       for (int s = 0; s < kRing; ++s) {
@@ -293,7 +352,8 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg, int lens_first) {
 #pragma unroll
   for (int j = 0; j < NN; ++j) {
     const int64_t k0 = static_cast<int64_t>(p0) * kPage;
-    const int n = static_cast<int>(min(static_cast<int64_t>(p1) * kPage, static_cast<int64_t>(rq.len[j])) - k0);
+    // Live scores of this share (none for a workgroup past the request's end).
+    const int n = max(0, static_cast<int>(min(static_cast<int64_t>(p1) * kPage, static_cast<int64_t>(rq.len[j])) - k0));
     float* dst = a.logits + static_cast<int64_t>(row0 + j) * a.logits_stride + k0;
     const float* src = s_out + j * pages_per_wg * kPage;
     const int n4 = n >> 2;
@@ -344,10 +404,9 @@ DeviceInfo* device_info(int dev) {
 }
 
 template <int NN, bool HIST>
-hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, int lens_first, hipStream_t stream,
-                  LaunchEvents ev) {
+hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
   launch_kernel(indexer_logits_kernel<NN, HIST>, grid, dim3(kThreadsOf<NN>), stream, ev.start, ev.stop, a,
-                pages_per_wg, lens_first);
+                pages_per_wg);
   return hipGetLastError();
 }
 
@@ -379,16 +438,15 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   if (chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
   const int p = static_cast<int>(ppw);
-  const int lens_first = a.B >= 32 ? 1 : 0;
   switch (a.next_n * 2 + (hist ? 1 : 0)) {
-    case 2: return launch<1, false>(a, grid, p, lens_first, stream, ev);
-    case 3: return launch<1, true>(a, grid, p, lens_first, stream, ev);
-    case 4: return launch<2, false>(a, grid, p, lens_first, stream, ev);
-    case 5: return launch<2, true>(a, grid, p, lens_first, stream, ev);
-    case 6: return launch<3, false>(a, grid, p, lens_first, stream, ev);
-    case 7: return launch<3, true>(a, grid, p, lens_first, stream, ev);
-    case 8: return launch<4, false>(a, grid, p, lens_first, stream, ev);
-    case 9: return launch<4, true>(a, grid, p, lens_first, stream, ev);
+    case 2: return launch<1, false>(a, grid, p, stream, ev);
+    case 3: return launch<1, true>(a, grid, p, stream, ev);
+    case 4: return launch<2, false>(a, grid, p, stream, ev);
+    case 5: return launch<2, true>(a, grid, p, stream, ev);
+    case 6: return launch<3, false>(a, grid, p, stream, ev);
+    case 7: return launch<3, true>(a, grid, p, stream, ev);
+    case 8: return launch<4, false>(a, grid, p, stream, ev);
+    case 9: return launch<4, true>(a, grid, p, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }
