@@ -11,7 +11,7 @@ writes: a write sweep would leave the caches full of dirty lines whose
 write-back then competes with the timed kernel's reads.
 
 Kernel times come from HIP events that the library's own dispatches record
-(the *_timed entry points, hipExtLaunchKernel): a call's start event when its
+(indexer_time_next_call, hipExtLaunchKernel): a call's start event when its
 first kernel begins and its stop event when its last kernel ends, the same
 interval rocprofv3's kernel trace reports.  A step is timed from the start of
 the logits kernel to the end of the last top-k kernel, so the gap between
@@ -215,6 +215,29 @@ def main() -> int:
             e.record(stream)  # creates the HIP event before a dispatch records it
         return evs
 
+    stride16 = -(-x.logits_stride // 8) * 8  # 16-byte rows of halves
+    logits16 = torch.full((x.rows, stride16), float("inf"), dtype=torch.float16, device=dev)
+
+    def run16(n_steps, record, split=False):
+        """Steps with FP16 logits (indexer_logits_f16 + topk_rows_f16); as in
+        run(), only the step's ends are recorded unless `split`."""
+        out = []
+        evs = []
+        for i in range(n_steps):
+            ls, le, te = new_events(3)
+            evict()
+            hist.zero_()
+            pmqa.indexer_logits_f16(t["q"], t["kv_pages"], t["k_scales"], t["weights"],
+                                    t["block_table"], t["context_lens"], x.next_n, logits16, hist,
+                                    events=(ls, le if split else None))
+            pmqa.topk_rows_f16(logits16, hist, t["context_lens"], K, idx, ws,
+                               events=None if split else (None, te))
+            evs.append((ls, le if split else te))
+        torch.cuda.synchronize()
+        if record:
+            out = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        return out
+
     def run(n_steps, key, record, split=False):
         """Steps of logits + top-k.  Without `split` only the step's start
         (logits kernel begins) and end (last top-k kernel ends) are recorded,
@@ -259,8 +282,12 @@ def main() -> int:
     if args.fp16_steps > 0:
         _, _, st16, _ = run(args.fp16_steps, pmqa.KEY_FP16, True)
         _, tt16, _, _ = run(args.fp16_steps, pmqa.KEY_FP16, True, split=True)
+        print(f"[bench] FP16-logits timing {args.fp16_steps} steps", file=sys.stderr, flush=True)
+        run16(3, False)
+        st_h = run16(args.fp16_steps, True)
+        lt_h = run16(args.fp16_steps, True, split=True)
     else:
-        st16, tt16 = [], []
+        st16, tt16, lt_h, st_h = [], [], [], []
 
     # practical read ceiling over the same number of bytes as K
     ab = algorithmic_bytes(x)
@@ -327,6 +354,9 @@ def main() -> int:
         "timing": "dispatch-recorded HIP events (hipExtLaunchKernel start/stop), mean over steps",
         "fp16_keys": ({"step_us_mean": round(float(np.mean(st16)), 3),
                        "topk_rows_fp16_mean": round(float(np.mean(tt16)), 3)} if st16 else None),
+        # FP16 logits output: indexer_logits_f16 (halves) + topk_rows_f16 (FP16 keys)
+        "fp16_logits": ({"step_us_mean": round(float(np.mean(st_h)), 3),
+                         "indexer_logits_f16_mean": round(float(np.mean(lt_h)), 3)} if st_h else None),
         "hbm": {
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),

@@ -174,28 +174,50 @@ idx_status score_histogram(const float* scores, int64_t stride, const int32_t* c
                            int32_t rows, int32_t* hist, void* stream);
 
 /*
- * Timing variants, for measurement: the same as indexer_logits, topk_rows
- * and hbm_read_probe, plus two hipEvent_t handles (created by the caller, or
- * NULL).  The call's own kernel dispatches record them (hipExtLaunchKernel):
- * start_event when its first kernel begins and stop_event when its last
- * kernel ends, so the elapsed time between them is the call's device time
- * without the stream's dispatch gaps before and after it.  The results are
- * those of the plain call.  Not meant for graph capture.
+ * indexer_logits_f16 -- indexer_logits writing each score as the IEEE binary16
+ * value it rounds to (round to nearest even; magnitudes at or above 65520
+ * become infinities): [P3] "Summary" (FP16 logits for the sparse indexer).
+ * Everything else -- arguments, rows, lengths, histogram -- is as for
+ * indexer_logits; the histogram bins the same FP16 values (bin() already
+ * rounds to FP16), so it is identical to indexer_logits' histogram.
+ *
+ * logits        (device) uint16 [B*next_n][logits_stride], binary16 bits,
+ *               16-B aligned, logits_stride > 0 and a multiple of 8
  */
-idx_status indexer_logits_timed(const uint8_t* q, const uint8_t* kv_pages,
-                                const float* k_scales, const float* weights,
-                                const int32_t* block_table, const int32_t* context_lens,
-                                int32_t B, int32_t next_n, int32_t num_pages,
-                                int32_t max_pages, float* logits, int64_t logits_stride,
-                                int32_t* hist, void* stream, void* start_event,
-                                void* stop_event);
-idx_status topk_rows_timed(const float* logits, int64_t logits_stride,
-                           const int32_t* hist, const int32_t* context_lens,
-                           int32_t rows, int32_t k, int32_t key_dtype, int32_t* indices,
-                           void* workspace, size_t workspace_bytes, void* stream,
-                           void* start_event, void* stop_event);
-idx_status hbm_read_probe_timed(const void* src, size_t bytes, uint32_t* sink, void* stream,
-                                void* start_event, void* stop_event);
+idx_status indexer_logits_f16(const uint8_t* q, const uint8_t* kv_pages,
+                              const float* k_scales, const float* weights,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              int32_t B, int32_t next_n, int32_t num_pages,
+                              int32_t max_pages, uint16_t* logits, int64_t logits_stride,
+                              int32_t* hist, void* stream);
+
+/*
+ * topk_rows_f16 -- topk_rows over binary16 scores ([P3] "Summary": selection
+ * on FP16 logits).  The key is the FP16 value itself (scores that are the
+ * same half tie, and the lower column wins), the same order as topk_rows
+ * with IDX_KEY_FP16 on the float32 scores these halves round from.
+ *
+ * logits        (device) uint16 [rows][logits_stride], binary16 bits, 16-B
+ *               aligned, logits_stride a multiple of 8
+ * other arguments as for topk_rows; the workspace size is
+ * topk_workspace_bytes(rows, logits_stride, k)
+ */
+idx_status topk_rows_f16(const uint16_t* logits, int64_t logits_stride,
+                         const int32_t* hist, const int32_t* context_lens,
+                         int32_t rows, int32_t k, int32_t* indices,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * indexer_time_next_call -- measurement aid.  Arms the calling host thread:
+ * its next call of this library records start_event when that call's first
+ * kernel begins and stop_event when its last kernel ends (the dispatches
+ * record them themselves, hipExtLaunchKernel), so the elapsed time between
+ * them is the call's device time without the stream's dispatch gaps around
+ * it.  Either event may be NULL; events are hipEvent_t created by the
+ * caller.  The next call disarms it whatever its outcome (a call that fails
+ * a check records nothing).  Not meant for graph capture.
+ */
+idx_status indexer_time_next_call(void* start_event, void* stop_event);
 
 /* Human-readable name of a status code (static string). */
 const char* indexer_status_str(int32_t status);

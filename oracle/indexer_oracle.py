@@ -234,6 +234,45 @@ def fp16_rne(x) -> np.ndarray:
         return np.asarray(x, dtype=np.float32).astype(np.float16)
 
 
+def check_logits_f16(got, want, bound, head_sum=None, head_bound=None):
+    """Element-wise acceptance of FP16 logits (vLLM PR #52696 "Summary": the
+    indexer stores its logits as FP16).
+
+    A finite expected value accepts exactly the halves that are fp16_RN(y)
+    of some float32 y with |y - want| <= bound, i.e. the float32 values the
+    float32 check accepts, rounded: rounding is monotone, so these are the
+    halves between fp16_RN(ylo) and fp16_RN(yhi), ylo / yhi the least / the
+    greatest float32 in [want - bound, want + bound].  Non-finite expected
+    values are checked by class as in check_logits (an infinity rounds to
+    the same infinity, NaN stays NaN).  ``got`` is float16 (or its bits as
+    uint16).  Returns a boolean array, True where the element is accepted.
+    """
+    got = np.asarray(got)
+    if got.dtype == np.uint16:
+        got = got.view(np.float16)
+    g = got.astype(np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    bound = np.asarray(bound, dtype=np.float64)
+    ok = np.zeros(g.shape, dtype=bool)
+    fin = np.isfinite(want) & np.isfinite(bound)
+    if np.any(fin):
+        lo64, hi64 = want[fin] - bound[fin], want[fin] + bound[fin]
+        with np.errstate(over="ignore"):
+            lo32, hi32 = lo64.astype(np.float32), hi64.astype(np.float32)
+        lo32 = np.where(lo32.astype(np.float64) < lo64, np.nextafter(lo32, np.float32(np.inf)), lo32)
+        hi32 = np.where(hi32.astype(np.float64) > hi64, np.nextafter(hi32, np.float32(-np.inf)), hi32)
+        lo16 = fp16_rne(lo32).astype(np.float64)
+        hi16 = fp16_rne(hi32).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            ok[fin] = (lo16 <= g[fin]) & (g[fin] <= hi16)
+    nf = ~fin
+    if np.any(nf):
+        ok[nf] = check_logits(g[nf], want[nf], bound[nf],
+                              None if head_sum is None else np.asarray(head_sum)[nf],
+                              None if head_bound is None else np.asarray(head_bound)[nf])
+    return ok
+
+
 def coarse_bin(x) -> np.ndarray:
     """Bin 0..1023 of each float32 score; -1 for NaN (never counted).
 

@@ -9,17 +9,21 @@ streams.
 
 Entry points (same names as the C ABI):
   indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens,
-                 next_n, logits, hist=None, events=None)
+                 next_n, logits, hist=None, events=None)        float32 logits
+  indexer_logits_f16(... same ..., logits, hist=None, events=None) float16 logits
   topk_workspace_bytes(rows, logits_stride, k)
   topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None,
-            events=None)
+            events=None)                                          float32 scores
+  topk_rows_f16(logits, hist, context_lens, k, indices, workspace=None,
+                events=None)                                      float16 scores
   score_histogram(scores, context_lens, hist)
   indexer_status_str(status)
+  indexer_time_next_call(start, stop)
   hbm_read_probe(src, sink, events=None)
-With ``events=(start, stop)`` (two torch.cuda.Event with timing enabled) the
-call goes to the ``*_timed`` C variant, whose kernel dispatches record the
-events themselves: start when the call's first kernel begins, stop when its
-last kernel ends.
+With ``events=(start, stop)`` (torch.cuda.Event with timing enabled, either
+may be None) the call is preceded by indexer_time_next_call, so its own
+kernel dispatches record the events: start when its first kernel begins,
+stop when its last kernel ends.
 """
 
 from __future__ import annotations
@@ -31,9 +35,9 @@ import torch
 
 __all__ = [
     "IndexerError", "KEY_FP32", "KEY_FP16", "NUM_BINS", "CANDIDATE_CAPACITY",
-    "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits",
-    "topk_workspace_bytes", "topk_rows", "score_histogram", "indexer_status_str",
-    "hbm_read_probe",
+    "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits", "indexer_logits_f16",
+    "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram", "indexer_status_str",
+    "indexer_time_next_call", "hbm_read_probe",
 ]
 
 KEY_FP32 = 0
@@ -44,9 +48,9 @@ HEADS = 32
 HEAD_DIM = 128
 PAGE_TOKENS = 64
 
-EXPORTED_SYMBOLS = ("indexer_logits", "topk_workspace_bytes", "topk_rows",
-                    "score_histogram", "indexer_status_str", "hbm_read_probe",
-                    "indexer_logits_timed", "topk_rows_timed", "hbm_read_probe_timed")
+EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "topk_workspace_bytes", "topk_rows",
+                    "topk_rows_f16", "score_histogram", "indexer_status_str",
+                    "indexer_time_next_call", "hbm_read_probe")
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpaged_mqa_indexer.so"
@@ -89,12 +93,12 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_status_str.restype = ctypes.c_char_p
     lib.hbm_read_probe.argtypes = [vp, sz, vp, vp]
     lib.hbm_read_probe.restype = ctypes.c_int
-    lib.indexer_logits_timed.argtypes = lib.indexer_logits.argtypes + [vp, vp]
-    lib.indexer_logits_timed.restype = ctypes.c_int
-    lib.topk_rows_timed.argtypes = lib.topk_rows.argtypes + [vp, vp]
-    lib.topk_rows_timed.restype = ctypes.c_int
-    lib.hbm_read_probe_timed.argtypes = lib.hbm_read_probe.argtypes + [vp, vp]
-    lib.hbm_read_probe_timed.restype = ctypes.c_int
+    lib.indexer_logits_f16.argtypes = lib.indexer_logits.argtypes
+    lib.indexer_logits_f16.restype = ctypes.c_int
+    lib.topk_rows_f16.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
+    lib.topk_rows_f16.restype = ctypes.c_int
+    lib.indexer_time_next_call.argtypes = [vp, vp]
+    lib.indexer_time_next_call.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -133,8 +137,6 @@ def _event_handles(events, device: torch.device):
     """hipEvent_t handles of (start, stop), either of which may be None; a
     torch event that was never recorded has no HIP event yet, so it is
     recorded once to create it."""
-    if events is None:
-        return None
     start, stop = events
     handles = []
     for ev in (start, stop):
@@ -149,16 +151,21 @@ def _event_handles(events, device: torch.device):
     return handles
 
 
-def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens, next_n,
-                   logits, hist=None, events=None):
-    """Paged MQA logits (and histogram) on the current stream of q's device.
+def indexer_time_next_call(start, stop, device=None) -> None:
+    """Arm this host thread's next library call to record (start, stop)
+    from its own kernel dispatches (torch.cuda.Event, or None)."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    h = _event_handles((start, stop), dev)
+    _check("indexer_time_next_call", load_library().indexer_time_next_call(*h))
 
-    q [B*next_n, 32, 128] uint8 (e4m3fn codes); kv_pages [P, 64, 128] uint8;
-    k_scales [P, 64] float32; weights [B*next_n, 32] float32;
-    block_table [B, max_pages] int32; context_lens [B*next_n] int32;
-    logits [B*next_n, stride] float32 with unit column stride;
-    hist [B*next_n, 1024] int32 or None (accumulated into).
-    """
+
+def _arm(events, device) -> None:
+    if events is not None:
+        indexer_time_next_call(events[0], events[1], device)
+
+
+def _logits_call(name, dtype, q, kv_pages, k_scales, weights, block_table, context_lens, next_n,
+                 logits, hist, events):
     dev = q.device
     _need(q, "q", torch.uint8, dev, 3)
     _need(kv_pages, "kv_pages", torch.uint8, dev, 3)
@@ -166,7 +173,7 @@ def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens, ne
     _need(weights, "weights", torch.float32, dev, 2)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(context_lens, "context_lens", torch.int32, dev, 1)
-    _need(logits, "logits", torch.float32, dev, 2)
+    _need(logits, "logits", dtype, dev, 2)
     B, max_pages = block_table.shape
     rows = B * next_n
     if tuple(q.shape) != (rows, HEADS, HEAD_DIM) or not q.is_contiguous():
@@ -190,26 +197,42 @@ def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens, ne
             raise ValueError(f"hist must be contiguous [{rows}, 1024]")
     lib = load_library()
     with torch.cuda.device(dev):
-        args = (_ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(block_table),
-                _ptr(context_lens), int(B), int(next_n), int(P), int(max_pages), _ptr(logits),
-                int(logits.stride(0)), _ptr(hist), _stream_ptr(dev))
-        ev = _event_handles(events, dev)
-        st = lib.indexer_logits(*args) if ev is None else lib.indexer_logits_timed(*args, *ev)
-    _check("indexer_logits", st)
+        _arm(events, dev)
+        st = getattr(lib, name)(
+            _ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(block_table),
+            _ptr(context_lens), int(B), int(next_n), int(P), int(max_pages), _ptr(logits),
+            int(logits.stride(0)), _ptr(hist), _stream_ptr(dev))
+    _check(name, st)
+
+
+def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens, next_n,
+                   logits, hist=None, events=None):
+    """Paged MQA logits (and histogram) on the current stream of q's device.
+
+    q [B*next_n, 32, 128] uint8 (e4m3fn codes); kv_pages [P, 64, 128] uint8;
+    k_scales [P, 64] float32; weights [B*next_n, 32] float32;
+    block_table [B, max_pages] int32; context_lens [B*next_n] int32;
+    logits [B*next_n, stride] float32 with unit column stride;
+    hist [B*next_n, 1024] int32 or None (accumulated into).
+    """
+    _logits_call("indexer_logits", torch.float32, q, kv_pages, k_scales, weights, block_table,
+                 context_lens, next_n, logits, hist, events)
+
+
+def indexer_logits_f16(q, kv_pages, k_scales, weights, block_table, context_lens, next_n,
+                       logits, hist=None, events=None):
+    """indexer_logits writing float16 logits [B*next_n, stride] (stride % 8 == 0)."""
+    _logits_call("indexer_logits_f16", torch.float16, q, kv_pages, k_scales, weights, block_table,
+                 context_lens, next_n, logits, hist, events)
 
 
 def topk_workspace_bytes(rows: int, logits_stride: int, k: int) -> int:
     return int(load_library().topk_workspace_bytes(int(rows), int(logits_stride), int(k)))
 
 
-def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None, events=None):
-    """Exact per-row top-k indices into ``indices`` [rows, k] int32.
-
-    ``workspace`` is a uint8 GPU tensor of at least topk_workspace_bytes()
-    bytes; when None one is allocated with torch for this call.
-    """
+def _topk_call(name, dtype, logits, hist, context_lens, k, key_dtype, indices, workspace, events):
     dev = logits.device
-    _need(logits, "logits", torch.float32, dev, 2)
+    _need(logits, "logits", dtype, dev, 2)
     _need(context_lens, "context_lens", torch.int32, dev, 1)
     _need(indices, "indices", torch.int32, dev, 2)
     rows = logits.shape[0]
@@ -229,12 +252,30 @@ def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None,
     _need(workspace, "workspace", torch.uint8, dev)
     lib = load_library()
     with torch.cuda.device(dev):
-        args = (_ptr(logits), int(logits.stride(0)), _ptr(hist), _ptr(context_lens), int(rows),
-                int(k), int(key_dtype), _ptr(indices), _ptr(workspace), int(workspace.numel()),
-                _stream_ptr(dev))
-        ev = _event_handles(events, dev)
-        st = lib.topk_rows(*args) if ev is None else lib.topk_rows_timed(*args, *ev)
-    _check("topk_rows", st)
+        _arm(events, dev)
+        head = (_ptr(logits), int(logits.stride(0)), _ptr(hist), _ptr(context_lens), int(rows), int(k))
+        tail = (_ptr(indices), _ptr(workspace), int(workspace.numel()), _stream_ptr(dev))
+        if key_dtype is None:
+            st = getattr(lib, name)(*head, *tail)
+        else:
+            st = getattr(lib, name)(*head, int(key_dtype), *tail)
+    _check(name, st)
+
+
+def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None, events=None):
+    """Exact per-row top-k indices of float32 scores into ``indices`` [rows, k].
+
+    ``workspace`` is a uint8 GPU tensor of at least topk_workspace_bytes()
+    bytes; when None one is allocated with torch for this call.
+    """
+    _topk_call("topk_rows", torch.float32, logits, hist, context_lens, k, key_dtype, indices,
+               workspace, events)
+
+
+def topk_rows_f16(logits, hist, context_lens, k, indices, workspace=None, events=None):
+    """topk_rows over float16 scores [rows, stride] (stride % 8 == 0), FP16 keys."""
+    _topk_call("topk_rows_f16", torch.float16, logits, hist, context_lens, k, None, indices,
+               workspace, events)
 
 
 def score_histogram(scores, context_lens, hist):
@@ -265,7 +306,6 @@ def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, events=None) -> None:
     lib = load_library()
     nbytes = src.numel() * src.element_size()
     with torch.cuda.device(src.device):
-        args = (_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream_ptr(src.device))
-        ev = _event_handles(events, src.device)
-        st = lib.hbm_read_probe(*args) if ev is None else lib.hbm_read_probe_timed(*args, *ev)
+        _arm(events, src.device)
+        st = lib.hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream_ptr(src.device))
     _check("hbm_read_probe", st)

@@ -8,17 +8,22 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 idx_status from_hip(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_ELAUNCH; }
 
-pmqa::LaunchEvents events(void* start, void* stop) {
-  pmqa::LaunchEvents ev;
-  ev.start = static_cast<hipEvent_t>(start);
-  ev.stop = static_cast<hipEvent_t>(stop);
+// Events armed by indexer_time_next_call for this host thread's next call.
+thread_local pmqa::LaunchEvents t_next_events;
+
+// Every entry point takes (and so disarms) the armed events first, whether
+// or not its checks pass.
+pmqa::LaunchEvents take_events() {
+  const pmqa::LaunchEvents ev = t_next_events;
+  t_next_events = pmqa::LaunchEvents{};
   return ev;
 }
 
 idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
                        const float* weights, const int32_t* block_table, const int32_t* context_lens,
-                       int32_t B, int32_t next_n, int32_t num_pages, int32_t max_pages, float* logits,
-                       int64_t logits_stride, int32_t* hist, void* stream, pmqa::LaunchEvents ev) {
+                       int32_t B, int32_t next_n, int32_t num_pages, int32_t max_pages, void* logits,
+                       int64_t logits_stride, bool f16, int32_t* hist, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
   if (!q || !kv_pages || !k_scales || !weights || !block_table || !context_lens || !logits)
     return IDX_EINVAL;
   if (B <= 0 || num_pages <= 0 || max_pages <= 0 || logits_stride <= 0) return IDX_EINVAL;
@@ -26,9 +31,11 @@ idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k
   if (B > IDX_MAX_REQUESTS || static_cast<int64_t>(B) * next_n > IDX_MAX_ROWS) return IDX_EUNSUPPORTED;
   // The page list of all requests is indexed with 32-bit integers.
   if (static_cast<int64_t>(B) * max_pages > INT32_MAX) return IDX_EUNSUPPORTED;
+  // Rows are written with 16-byte stores: the stride is a multiple of 16 bytes.
+  const int64_t per16 = f16 ? 8 : 4;
   if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(weights, 16) || !aligned(k_scales, 4) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(logits, 16) ||
-      (logits_stride % 4) != 0 || (hist && !aligned(hist, 8)))
+      (logits_stride % per16) != 0 || (hist && !aligned(hist, 8)))
     return IDX_EALIGN;
   pmqa::LogitsArgs a;
   a.q = q;
@@ -40,6 +47,7 @@ idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k
   a.logits = logits;
   a.hist = hist;
   a.logits_stride = logits_stride;
+  a.logits_f16 = f16 ? 1 : 0;
   a.B = B;
   a.next_n = next_n;
   a.num_pages = num_pages;
@@ -47,15 +55,16 @@ idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k
   return from_hip(pmqa::launch_indexer_logits(a, static_cast<hipStream_t>(stream), ev));
 }
 
-idx_status topk_call(const float* logits, int64_t logits_stride, const int32_t* hist,
+idx_status topk_call(const void* logits, int64_t logits_stride, bool f16, const int32_t* hist,
                      const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
-                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream,
-                     pmqa::LaunchEvents ev) {
+                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
   if (!logits || !context_lens || !indices || !workspace) return IDX_EINVAL;
   if (rows <= 0 || logits_stride <= 0 || k < 1 || k > IDX_CANDIDATE_CAPACITY) return IDX_EINVAL;
   if (key_dtype != IDX_KEY_FP32 && key_dtype != IDX_KEY_FP16) return IDX_EUNSUPPORTED;
-  if (rows > IDX_MAX_ROWS || logits_stride > (int64_t{1} << 31) - 4) return IDX_EUNSUPPORTED;
-  if (!aligned(logits, 16) || (logits_stride % 4) != 0 || !aligned(context_lens, 4) ||
+  const int64_t per16 = f16 ? 8 : 4;  // rows are read with 16-byte loads
+  if (rows > IDX_MAX_ROWS || logits_stride > (int64_t{1} << 31) - per16) return IDX_EUNSUPPORTED;
+  if (!aligned(logits, 16) || (logits_stride % per16) != 0 || !aligned(context_lens, 4) ||
       !aligned(indices, 4) || !aligned(workspace, 256) || (hist && !aligned(hist, 8)))
     return IDX_EALIGN;
   if (workspace_bytes < pmqa::topk_workspace_size(rows, logits_stride, k)) return IDX_EWORKSPACE;
@@ -68,14 +77,9 @@ idx_status topk_call(const float* logits, int64_t logits_stride, const int32_t* 
   a.logits_stride = logits_stride;
   a.rows = rows;
   a.k = k;
-  a.key_dtype = key_dtype;
+  a.key_dtype = f16 ? IDX_KEY_FP16 : key_dtype;
+  a.logits_f16 = f16 ? 1 : 0;
   return from_hip(pmqa::launch_topk_rows(a, static_cast<hipStream_t>(stream), ev));
-}
-
-idx_status probe_call(const void* src, size_t bytes, uint32_t* sink, void* stream, pmqa::LaunchEvents ev) {
-  if (!src || !sink || bytes == 0) return IDX_EINVAL;
-  if (!aligned(src, 16) || (bytes % 16) != 0 || !aligned(sink, 4)) return IDX_EALIGN;
-  return from_hip(pmqa::launch_hbm_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream), ev));
 }
 
 }  // namespace
@@ -94,23 +98,28 @@ const char* indexer_status_str(int32_t s) {
   }
 }
 
+idx_status indexer_time_next_call(void* start_event, void* stop_event) {
+  t_next_events.start = static_cast<hipEvent_t>(start_event);
+  t_next_events.stop = static_cast<hipEvent_t>(stop_event);
+  return IDX_OK;
+}
+
 idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
                           const float* weights, const int32_t* block_table,
                           const int32_t* context_lens, int32_t B, int32_t next_n,
                           int32_t num_pages, int32_t max_pages, float* logits,
                           int64_t logits_stride, int32_t* hist, void* stream) {
   return logits_call(q, kv_pages, k_scales, weights, block_table, context_lens, B, next_n, num_pages,
-                     max_pages, logits, logits_stride, hist, stream, pmqa::LaunchEvents{});
+                     max_pages, logits, logits_stride, false, hist, stream);
 }
 
-idx_status indexer_logits_timed(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
-                                const float* weights, const int32_t* block_table,
-                                const int32_t* context_lens, int32_t B, int32_t next_n,
-                                int32_t num_pages, int32_t max_pages, float* logits,
-                                int64_t logits_stride, int32_t* hist, void* stream,
-                                void* start_event, void* stop_event) {
+idx_status indexer_logits_f16(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                              const float* weights, const int32_t* block_table,
+                              const int32_t* context_lens, int32_t B, int32_t next_n,
+                              int32_t num_pages, int32_t max_pages, uint16_t* logits,
+                              int64_t logits_stride, int32_t* hist, void* stream) {
   return logits_call(q, kv_pages, k_scales, weights, block_table, context_lens, B, next_n, num_pages,
-                     max_pages, logits, logits_stride, hist, stream, events(start_event, stop_event));
+                     max_pages, logits, logits_stride, true, hist, stream);
 }
 
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
@@ -120,20 +129,20 @@ size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
 idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* hist,
                      const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
                      int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
-  return topk_call(logits, logits_stride, hist, context_lens, rows, k, key_dtype, indices, workspace,
-                   workspace_bytes, stream, pmqa::LaunchEvents{});
+  return topk_call(logits, logits_stride, false, hist, context_lens, rows, k, key_dtype, indices,
+                   workspace, workspace_bytes, stream);
 }
 
-idx_status topk_rows_timed(const float* logits, int64_t logits_stride, const int32_t* hist,
-                           const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
-                           int32_t* indices, void* workspace, size_t workspace_bytes, void* stream,
-                           void* start_event, void* stop_event) {
-  return topk_call(logits, logits_stride, hist, context_lens, rows, k, key_dtype, indices, workspace,
-                   workspace_bytes, stream, events(start_event, stop_event));
+idx_status topk_rows_f16(const uint16_t* logits, int64_t logits_stride, const int32_t* hist,
+                         const int32_t* context_lens, int32_t rows, int32_t k, int32_t* indices,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_call(logits, logits_stride, true, hist, context_lens, rows, k, IDX_KEY_FP16, indices,
+                   workspace, workspace_bytes, stream);
 }
 
 idx_status score_histogram(const float* scores, int64_t stride, const int32_t* context_lens,
                            int32_t rows, int32_t* hist, void* stream) {
+  take_events();  // launches nothing timed; disarms like every call
   if (!scores || !context_lens || !hist) return IDX_EINVAL;
   if (rows <= 0 || stride <= 0) return IDX_EINVAL;
   if (rows > IDX_MAX_ROWS || stride > (int64_t{1} << 31) - 4) return IDX_EUNSUPPORTED;
@@ -144,12 +153,10 @@ idx_status score_histogram(const float* scores, int64_t stride, const int32_t* c
 }
 
 idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
-  return probe_call(src, bytes, sink, stream, pmqa::LaunchEvents{});
-}
-
-idx_status hbm_read_probe_timed(const void* src, size_t bytes, uint32_t* sink, void* stream,
-                                void* start_event, void* stop_event) {
-  return probe_call(src, bytes, sink, stream, events(start_event, stop_event));
+  const pmqa::LaunchEvents ev = take_events();
+  if (!src || !sink || bytes == 0) return IDX_EINVAL;
+  if (!aligned(src, 16) || (bytes % 16) != 0 || !aligned(sink, 4)) return IDX_EALIGN;
+  return from_hip(pmqa::launch_hbm_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream), ev));
 }
 
 }  // extern "C"

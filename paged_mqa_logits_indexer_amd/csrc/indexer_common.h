@@ -159,9 +159,10 @@ struct LogitsArgs {
   const float* weights;
   const int32_t* block_table;
   const int32_t* context_lens;
-  float* logits;
+  void* logits;      // float32, or IEEE binary16 bits with logits_f16
   int32_t* hist;
   int64_t logits_stride;
+  int32_t logits_f16;
   int32_t B;
   int32_t next_n;
   int32_t num_pages;
@@ -170,7 +171,7 @@ struct LogitsArgs {
 hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, LaunchEvents ev = {});
 
 struct TopkArgs {
-  const float* logits;
+  const void* logits;  // float32, or IEEE binary16 bits with logits_f16
   const int32_t* hist;
   const int32_t* context_lens;
   int32_t* indices;
@@ -179,6 +180,7 @@ struct TopkArgs {
   int32_t rows;
   int32_t k;
   int32_t key_dtype;
+  int32_t logits_f16;
 };
 size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k);
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev = {});

@@ -31,6 +31,8 @@
 //     computed.
 //   * The histogram slots of the workgroup's rows live in LDS and are added
 //     to the global histogram (two bins per 64-bit atomic) when it finishes.
+#include <type_traits>
+
 #include "indexer_common.h"
 
 namespace pmqa {
@@ -64,6 +66,9 @@ static_assert(kMaxPagesPerWg <= 4 * kWave, "page ids of a share must fit one fet
 // (16 KiB per row of the request).
 template <int NN>
 constexpr int kStageFloats = NN * kMaxPagesPerWg * kPage;
+// Staged score type: float32 logits, or the bits of their FP16 rounding.
+template <bool F16>
+using StageT = typename std::conditional<F16, uint16_t, float>::type;
 template <int NN>
 constexpr int kThreadsOf = kWavesOf<NN> * kWave;
 
@@ -140,14 +145,16 @@ struct RequestRegs {
 
 // Scores of page `lp` (the `lpi`-th page of the workgroup's share) for the
 // NN rows of the request.  Scores go to the workgroup's LDS staging area
-// s_out[j][lpi][lane]; they reach global memory after the share's last load
-// (see the kernel), because a global store issued between this page and the
-// next one's prefetch would have to complete before that page counts as
-// arrived: the vector-memory counter covers loads and stores in issue order.
-template <int NN, bool HIST>
+// s_out[j][lpi][lane] -- float32, or with F16 the IEEE half the score rounds
+// to (round to nearest even), the same half the histogram bins; they reach
+// global memory after the share's last load (see the kernel), because a
+// global store issued between this page and the next one's prefetch would
+// have to complete before that page counts as arrived: the vector-memory
+// counter covers loads and stores in issue order.
+template <int NN, bool HIST, bool F16>
 __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi, int ppw,
                                              int lane, const RequestRegs<NN>& rq,
-                                             float* s_out, int* s_hist) {
+                                             StageT<F16>* s_out, int* s_hist) {
   const int key = lp * kPage + lane;
 #pragma unroll
   for (int j = 0; j < NN; ++j) {
@@ -174,10 +181,12 @@ __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi
       part[kb] = s;
     }
     const float logit = as_stored(reduce_scatter4(part) * pr.scale);
-    s_out[(j * ppw + lpi) * kPage + lane] = logit;
+    uint32_t hb = 0u;
+    if constexpr (HIST || F16) hb = f16_bits_rn(logit);
+    if constexpr (F16) s_out[(j * ppw + lpi) * kPage + lane] = static_cast<uint16_t>(hb);
+    else s_out[(j * ppw + lpi) * kPage + lane] = logit;
     if (key < rq.len[j]) {
       if constexpr (HIST) {
-        const uint32_t hb = f16_bits_rn(logit);
         if (!f16_is_nan(hb)) atomicAdd(&s_hist[j * kBins + coarse_bin_f16(hb)], 1);
       }
     }
@@ -190,11 +199,11 @@ template <int NN>
 constexpr int kWavesPerSimd = NN == 1 ? (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 3 : 2))
                                       : (NN == 2 && kPrefetch == 1 ? 3 : 2);
 
-template <int NN, bool HIST>
+template <int NN, bool HIST, bool F16>
 __global__ __launch_bounds__(kThreadsOf<NN>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
 void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   __shared__ int s_hist[HIST ? NN * kBins : 1];
-  __shared__ __align__(16) float s_out[kStageFloats<NN>];  // [NN][pages_per_wg][64] scores
+  __shared__ __align__(16) StageT<F16> s_out[kStageFloats<NN>];  // [NN][pages_per_wg][64] scores
   // Q in MFMA operand layout, [row][head block][half][lane], and the weights:
   // fetched once per workgroup and read by every wave from here.
   __shared__ __align__(16) i32x4 s_q[NN >= 2 ? NN * 4 * kWave : 1];
@@ -340,26 +349,27 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
         if (it >= n_mine) break;
         const int nx = it + kPrefetch < n_mine ? it + kPrefetch : n_mine - 1;
         load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[(s + kPrefetch) % kRing]);
-        compute_page<NN, HIST>(buf[s], p0 + lpi0 + it * kWaves, lpi0 + it * kWaves,
-                               pages_per_wg, lane, rq, s_out, s_hist);
+        compute_page<NN, HIST, F16>(buf[s], p0 + lpi0 + it * kWaves, lpi0 + it * kWaves,
+                                    pages_per_wg, lane, rq, s_out, s_hist);
       }
     }
   }
 
   __syncthreads();
   // Live scores of the share, row by row, with 16-byte stores (the row offset
-  // p0 * 64 and the stride are multiples of 4 floats).
+  // p0 * 64 and the stride are multiples of 16 bytes: 4 floats, 8 halves).
+  constexpr int kPerVec = 16 / static_cast<int>(sizeof(StageT<F16>));
 #pragma unroll
   for (int j = 0; j < NN; ++j) {
     const int64_t k0 = static_cast<int64_t>(p0) * kPage;
     // Live scores of this share (none for a workgroup past the request's end).
     const int n = max(0, static_cast<int>(min(static_cast<int64_t>(p1) * kPage, static_cast<int64_t>(rq.len[j])) - k0));
-    float* dst = a.logits + static_cast<int64_t>(row0 + j) * a.logits_stride + k0;
-    const float* src = s_out + j * pages_per_wg * kPage;
-    const int n4 = n >> 2;
-    for (int i = tid; i < n4; i += kThreads)
-      reinterpret_cast<f32x4*>(dst)[i] = reinterpret_cast<const f32x4*>(src)[i];
-    for (int i = (n4 << 2) + tid; i < n; i += kThreads) dst[i] = src[i];
+    StageT<F16>* dst = static_cast<StageT<F16>*>(a.logits) + static_cast<int64_t>(row0 + j) * a.logits_stride + k0;
+    const StageT<F16>* src = s_out + j * pages_per_wg * kPage;
+    const int nv = n / kPerVec;
+    for (int i = tid; i < nv; i += kThreads)
+      reinterpret_cast<i32x4*>(dst)[i] = reinterpret_cast<const i32x4*>(src)[i];
+    for (int i = nv * kPerVec + tid; i < n; i += kThreads) dst[i] = src[i];
   }
   if constexpr (HIST) {
     // Flush this workgroup's slots: pairs of bins with one 64-bit atomic each.
@@ -374,7 +384,6 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
 
 struct DeviceInfo {
   int cus = 0;
-  int occ[4][2] = {};
 };
 
 DeviceInfo* device_info(int dev) {
@@ -384,28 +393,15 @@ DeviceInfo* device_info(int dev) {
   if (!ready[dev]) {
     DeviceInfo d;
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return nullptr;
-    auto occ = [](const void* f, int threads) {
-      int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, 0) != hipSuccess) n = 1;
-      return n > 0 ? n : 1;
-    };
-    d.occ[0][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<1, false>), kThreadsOf<1>);
-    d.occ[0][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<1, true>), kThreadsOf<1>);
-    d.occ[1][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<2, false>), kThreadsOf<2>);
-    d.occ[1][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<2, true>), kThreadsOf<2>);
-    d.occ[2][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<3, false>), kThreadsOf<3>);
-    d.occ[2][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<3, true>), kThreadsOf<3>);
-    d.occ[3][0] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<4, false>), kThreadsOf<4>);
-    d.occ[3][1] = occ(reinterpret_cast<const void*>(indexer_logits_kernel<4, true>), kThreadsOf<4>);
     infos[dev] = d;
     ready[dev] = true;  // benign race: every thread computes the same values
   }
   return &infos[dev];
 }
 
-template <int NN, bool HIST>
+template <int NN, bool HIST, bool F16>
 hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
-  launch_kernel(indexer_logits_kernel<NN, HIST>, grid, dim3(kThreadsOf<NN>), stream, ev.start, ev.stop, a,
+  launch_kernel(indexer_logits_kernel<NN, HIST, F16>, grid, dim3(kThreadsOf<NN>), stream, ev.start, ev.stop, a,
                 pages_per_wg);
   return hipGetLastError();
 }
@@ -438,15 +434,23 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   if (chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
   const int p = static_cast<int>(ppw);
-  switch (a.next_n * 2 + (hist ? 1 : 0)) {
-    case 2: return launch<1, false>(a, grid, p, stream, ev);
-    case 3: return launch<1, true>(a, grid, p, stream, ev);
-    case 4: return launch<2, false>(a, grid, p, stream, ev);
-    case 5: return launch<2, true>(a, grid, p, stream, ev);
-    case 6: return launch<3, false>(a, grid, p, stream, ev);
-    case 7: return launch<3, true>(a, grid, p, stream, ev);
-    case 8: return launch<4, false>(a, grid, p, stream, ev);
-    case 9: return launch<4, true>(a, grid, p, stream, ev);
+  switch ((a.next_n * 2 + (hist ? 1 : 0)) * 2 + (a.logits_f16 ? 1 : 0)) {
+    case 4: return launch<1, false, false>(a, grid, p, stream, ev);
+    case 5: return launch<1, false, true>(a, grid, p, stream, ev);
+    case 6: return launch<1, true, false>(a, grid, p, stream, ev);
+    case 7: return launch<1, true, true>(a, grid, p, stream, ev);
+    case 8: return launch<2, false, false>(a, grid, p, stream, ev);
+    case 9: return launch<2, false, true>(a, grid, p, stream, ev);
+    case 10: return launch<2, true, false>(a, grid, p, stream, ev);
+    case 11: return launch<2, true, true>(a, grid, p, stream, ev);
+    case 12: return launch<3, false, false>(a, grid, p, stream, ev);
+    case 13: return launch<3, false, true>(a, grid, p, stream, ev);
+    case 14: return launch<3, true, false>(a, grid, p, stream, ev);
+    case 15: return launch<3, true, true>(a, grid, p, stream, ev);
+    case 16: return launch<4, false, false>(a, grid, p, stream, ev);
+    case 17: return launch<4, false, true>(a, grid, p, stream, ev);
+    case 18: return launch<4, true, false>(a, grid, p, stream, ev);
+    case 19: return launch<4, true, true>(a, grid, p, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -49,7 +49,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 4096;                // scores per workgroup
-constexpr int kPerIter = kThreads * 4;      // scores per block-wide step
 constexpr int kPerThread = kChunk / kThreads;  // consecutive scores per thread in the scan
 constexpr int kAllBins = kBins;             // threshold meaning "every live score"
 constexpr int kRefineThreads = 512;         // one workgroup per row finishes it
@@ -110,6 +109,34 @@ template <int KEY>
 __device__ __forceinline__ uint32_t score_key(float x) {
   if constexpr (KEY == IDX_KEY_FP32) return key_f32(x);
   else return key_f16(f16_bits_rn(x));
+}
+
+// Scores are float32, or (F16) the bits of IEEE binary16 values, whose key
+// is always the FP16 key.
+template <bool F16>
+__device__ __forceinline__ const void* score_row(const void* scores, int row, int64_t stride) {
+  return static_cast<const char*>(scores) + static_cast<int64_t>(row) * stride * (F16 ? 2 : 4);
+}
+
+// Key of score s of a row, and whether the score is selectable (not NaN).
+template <int KEY, bool F16>
+__device__ __forceinline__ bool score_at(const void* row, int s, uint32_t* key) {
+  if constexpr (F16) {
+    const uint32_t hb = static_cast<const uint16_t*>(row)[s];
+    *key = key_f16(hb);
+    return !f16_is_nan(hb);
+  } else {
+    const float v = static_cast<const float*>(row)[s];
+    *key = score_key<KEY>(v);
+    return v == v;
+  }
+}
+
+// The FP16 bits of element e of a 16-byte vector of scores.
+template <bool F16>
+__device__ __forceinline__ uint32_t half_bits_of(const i32x4& v, int e) {
+  if constexpr (F16) return (static_cast<uint32_t>(v[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
+  else return f16_bits_rn(__int_as_float(v[e]));
 }
 
 __device__ __forceinline__ int clamp_len(const int32_t* lens, int row, int64_t stride) {
@@ -214,7 +241,8 @@ __global__ void topk_zero_hist_kernel(int* hist, int rows) {
 }
 
 // Histogram of each row's live non-NaN scores, added to hist_out.
-__global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ logits,
+template <bool F16>
+__global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restrict__ logits,
                                                              int64_t stride,
                                                              const int32_t* __restrict__ lens,
                                                              int* __restrict__ hist_out) {
@@ -225,14 +253,16 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
   if (s0 >= len) return;
   for (int i = threadIdx.x; i < kBins; i += kThreads) s_hist[i] = 0;
   lds_barrier();
-  const float* x = logits + static_cast<int64_t>(row) * stride;
+  const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
   const int s1 = min(len, s0 + kChunk);
-  for (int s = s0 + threadIdx.x * 4; s < s1; s += kPerIter) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(x + s);
+  constexpr int kPerVec = F16 ? 8 : 4;  // scores per 16-byte load
+  for (int s = s0 + threadIdx.x * kPerVec; s < s1; s += kThreads * kPerVec) {
+    // In bounds: s < len <= stride, s and the stride multiples of kPerVec.
+    const i32x4 v = *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s) * (F16 ? 2 : 4));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kPerVec; ++e) {
       if (s + e < s1) {
-        const uint32_t hb = f16_bits_rn(v[e]);
+        const uint32_t hb = half_bits_of<F16>(v, e);
         if (!f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
       }
     }
@@ -250,8 +280,8 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
 // Thread t of a chunk's workgroup takes 16 consecutive columns; a block scan
 // of the per-thread counts gives every column its position in the chunk's
 // slot, so each slot list is in column order.
-template <int KEY>
-__global__ __launch_bounds__(kThreads) void topk_scan_kernel(const float* __restrict__ logits,
+template <int KEY, bool F16>
+__global__ __launch_bounds__(kThreads) void topk_scan_kernel(const void* __restrict__ logits,
                                                              int64_t stride,
                                                              const int32_t* __restrict__ hist,
                                                              const int32_t* __restrict__ lens, int k,
@@ -266,13 +296,16 @@ __global__ __launch_bounds__(kThreads) void topk_scan_kernel(const float* __rest
   const int* h = (hist ? hist : ws.hist) + static_cast<int64_t>(row) * kBins + threadIdx.x * 4;
   const int2 h01 = *reinterpret_cast<const int2*>(h);  // 8-B aligned
   const int2 h23 = *reinterpret_cast<const int2*>(h + 2);
-  const float* x = logits + static_cast<int64_t>(row) * stride;
+  const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
   const int s0 = c * kChunk + threadIdx.x * kPerThread;
-  f32x4 v[kPerThread / 4];
+  constexpr int kPerVec = F16 ? 8 : 4;  // scores per 16-byte load
+  i32x4 v[kPerThread / kPerVec];
 #pragma unroll
-  for (int i = 0; i < kPerThread / 4; ++i) {
-    // In bounds: s0 + 4i < len <= stride, and both are multiples of 4.
-    v[i] = s0 + 4 * i < len ? *reinterpret_cast<const f32x4*>(x + s0 + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kPerThread / kPerVec; ++i) {
+    // In bounds: s0 + kPerVec*i < len <= stride, both multiples of kPerVec.
+    const int s = s0 + kPerVec * i;
+    v[i] = s < len ? *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s) * (F16 ? 2 : 4))
+                   : i32x4{0, 0, 0, 0};
   }
   const int hc[4] = {h01.x, h01.y, h23.x, h23.y};
   const int bstar = threshold_bin(hc, k, s_red);
@@ -280,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_kernel(const float* __rest
   uint32_t gmask = 0u, emask = 0u;  // bit e: column s0 + e
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const uint32_t hb = f16_bits_rn(v[e / 4][e % 4]);
+    const uint32_t hb = half_bits_of<F16>(v[e / kPerVec], e % kPerVec);
     const bool live = s0 + e < len && !f16_is_nan(hb);
     const int bin = coarse_bin_f16(hb);
     gmask |= static_cast<uint32_t>(live && bin < bstar) << e;
@@ -299,7 +332,12 @@ __global__ __launch_bounds__(kThreads) void topk_scan_kernel(const float* __rest
       if (og < ws.gt_cap) gt[og] = s0 + e;
       ++og;
     }
-    if ((emask >> e) & 1u) eq[oe++] = uint2{score_key<KEY>(v[e / 4][e % 4]), static_cast<uint32_t>(s0 + e)};
+    if ((emask >> e) & 1u) {
+      uint32_t key;
+      if constexpr (F16) key = key_f16(half_bits_of<F16>(v[e / kPerVec], e % kPerVec));
+      else key = score_key<KEY>(__int_as_float(v[e / kPerVec][e % kPerVec]));
+      eq[oe++] = uint2{key, static_cast<uint32_t>(s0 + e)};
+    }
   }
   if (threadIdx.x == 0) {
     ws.counts[slot] = int2{tot & 0xFFFF, tot >> 16};
@@ -467,33 +505,37 @@ __device__ __forceinline__ void emit(RefineShared& sh, int32_t* out, int k, bool
 
 // Exact selection over the whole row: a stale histogram, or a threshold bin
 // with more candidates than the capacity.
-template <int KEY>
-__device__ void whole_row_select(RefineShared& sh, const float* __restrict__ x, int len, int k,
+template <int KEY, bool F16>
+__device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, int len, int k,
                                  int32_t* __restrict__ out) {
+  constexpr int kKey = F16 ? IDX_KEY_FP16 : KEY;
   int cnt = 0;
-  for (int s = threadIdx.x; s < len; s += kRefineThreads) cnt += (x[s] == x[s]) ? 1 : 0;
+  for (int s = threadIdx.x; s < len; s += kRefineThreads) {
+    uint32_t key;
+    cnt += score_at<KEY, F16>(x, s, &key) ? 1 : 0;
+  }
   const int n = block_sum<kRefineThreads>(cnt, sh.red);
   if (threadIdx.x == 0) sh.out_pos = 0;
   lds_barrier();
   if (n <= k) {
     for (int s0 = 0; s0 < len; s0 += kRefineThreads) {
       const int s = s0 + threadIdx.x;
-      emit(sh, out, k, s < len && x[s] == x[s], s);
+      uint32_t key;
+      emit(sh, out, k, s < len && score_at<KEY, F16>(x, s, &key), s);
     }
     lds_barrier();
     for (int i = n + threadIdx.x; i < k; i += kRefineThreads) out[i] = -1;
     return;
   }
-  constexpr int kKeyBits = KEY == IDX_KEY_FP32 ? 32 : 16;
+  constexpr int kKeyBits = kKey == IDX_KEY_FP32 ? 32 : 16;
   uint32_t prefix = 0u, fixed = 0u;
   int need = k;
   for (int shift = kKeyBits - 8; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
     lds_barrier();
     for (int s = threadIdx.x; s < len; s += kRefineThreads) {
-      const float v = x[s];
-      if (v != v) continue;
-      const uint32_t key = score_key<KEY>(v);
+      uint32_t key;
+      if (!score_at<KEY, F16>(x, s, &key)) continue;
       if (((key ^ prefix) & fixed) == 0u) atomicAdd(&sh.digit_hist[(key >> shift) & 0xFFu], 1);
     }
     lds_barrier();
@@ -510,13 +552,10 @@ __device__ void whole_row_select(RefineShared& sh, const float* __restrict__ x, 
   for (int s0 = 0; s0 < len; s0 += kRefineThreads) {
     const int s = s0 + threadIdx.x;
     bool above = false, tie = false;
-    if (s < len) {
-      const float v = x[s];
-      if (v == v) {
-        const uint32_t key = score_key<KEY>(v);
-        above = key > T;
-        tie = key == T;
-      }
+    uint32_t key;
+    if (s < len && score_at<KEY, F16>(x, s, &key)) {
+      above = key > T;
+      tie = key == T;
     }
     int slice_ties = 0;
     const int rank = taken_ties + block_excl_scan<kRefineThreads>(tie ? 1 : 0, sh.red, &slice_ties);
@@ -633,8 +672,8 @@ __device__ void gather_blocks(RefineShared& sh, const Workspace& ws, int64_t slo
 // Finishes each row after the scan pass: checks the real counts against b*,
 // then gathers the chunk slots and refines the candidates, or selects over
 // the whole row.
-template <int KEY>
-__global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float* __restrict__ logits,
+template <int KEY, bool F16>
+__global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const void* __restrict__ logits,
                                                                      int64_t stride,
                                                                      const int32_t* __restrict__ lens,
                                                                      int k, int32_t* __restrict__ indices,
@@ -645,7 +684,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float
   const int nch = row_chunks(len);
   const int bstar = ws.meta[row].bstar;
   const int64_t slot0 = static_cast<int64_t>(row) * ws.max_chunks;
-  const float* x = logits + static_cast<int64_t>(row) * stride;
+  const void* x = score_row<F16>(logits, row, stride);
   int32_t* out = indices + static_cast<int64_t>(row) * k;
 
   // Slots have fixed addresses, so the first round of the gather is
@@ -681,7 +720,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const float
   if (bstar == kAllBins) valid = n_gt <= k && n_eq == 0;
   else valid = n_gt < k && n_gt + n_eq >= k && n_eq <= kCandCap;
   if (!valid) {
-    whole_row_select<KEY>(sh, x, len, k, out);
+    whole_row_select<KEY, F16>(sh, x, len, k, out);
     return;
   }
   const int need = k - n_gt;
@@ -743,12 +782,12 @@ size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k) {
   return workspace_size(rows, chunks_for(logits_stride), k);
 }
 
-template <int KEY>
+template <int KEY, bool F16>
 void launch_select(const TopkArgs& a, const Workspace& ws, dim3 grid, hipStream_t stream,
                    hipEvent_t start, hipEvent_t stop) {
-  launch_kernel(topk_scan_kernel<KEY>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
+  launch_kernel(topk_scan_kernel<KEY, F16>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
                 a.logits_stride, a.hist, a.context_lens, a.k, ws);
-  launch_kernel(topk_refine_kernel<KEY>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop,
+  launch_kernel(topk_refine_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop,
                 a.logits, a.logits_stride, a.context_lens, a.k, a.indices, ws);
 }
 
@@ -761,11 +800,17 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents 
     launch_kernel(topk_zero_hist_kernel, dim3(min(1024, (a.rows * kBins + 255) / 256)), dim3(256), stream,
                   start, nullptr, ws.hist, a.rows);
     start = nullptr;
-    launch_kernel(topk_hist_kernel, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
-                  a.logits_stride, a.context_lens, ws.hist);
+    if (a.logits_f16)
+      launch_kernel(topk_hist_kernel<true>, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
+                    a.logits_stride, a.context_lens, ws.hist);
+    else
+      launch_kernel(topk_hist_kernel<false>, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
+                    a.logits_stride, a.context_lens, ws.hist);
   }
-  if (a.key_dtype == IDX_KEY_FP32) launch_select<IDX_KEY_FP32>(a, ws, grid, stream, start, ev.stop);
-  else launch_select<IDX_KEY_FP16>(a, ws, grid, stream, start, ev.stop);
+  // FP16 scores are ranked by their FP16 keys.
+  if (a.logits_f16) launch_select<IDX_KEY_FP16, true>(a, ws, grid, stream, start, ev.stop);
+  else if (a.key_dtype == IDX_KEY_FP32) launch_select<IDX_KEY_FP32, false>(a, ws, grid, stream, start, ev.stop);
+  else launch_select<IDX_KEY_FP16, false>(a, ws, grid, stream, start, ev.stop);
   return hipGetLastError();
 }
 
@@ -773,7 +818,7 @@ hipError_t launch_score_histogram(const float* scores, int64_t stride, const int
                                   int32_t rows, int32_t* hist, hipStream_t stream) {
   const int64_t chunks64 = (stride + kChunk - 1) / kChunk;
   if (chunks64 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(static_cast<unsigned>(chunks64), static_cast<unsigned>(rows)),
+  hipLaunchKernelGGL(topk_hist_kernel<false>, dim3(static_cast<unsigned>(chunks64), static_cast<unsigned>(rows)),
                      dim3(kThreads), 0, stream, scores, stride, lens, hist);
   return hipGetLastError();
 }

@@ -44,12 +44,32 @@ class DevInputs:
         pmqa.indexer_logits(self.q, self.kv, self.sc, self.w, self.bt, self.lens,
                             self.x.next_n, logits, hist)
 
+    def f16_stride(self):
+        """The workload's stride rounded up to 8 halves (16-byte rows)."""
+        return -(-self.x.logits_stride // 8) * 8
+
+    def run_f16(self, with_hist=True, fill=float("inf")):
+        lg = torch.full((self.x.rows, self.f16_stride()), fill, dtype=torch.float16,
+                        device=self.device)
+        h = self.new_hist() if with_hist else None
+        pmqa.indexer_logits_f16(self.q, self.kv, self.sc, self.w, self.bt, self.lens,
+                                self.x.next_n, lg, h)
+        torch.cuda.synchronize()
+        return lg, h
+
     def run(self, with_hist=True, fill=float("inf")):
         lg = self.new_logits(fill)
         h = self.new_hist() if with_hist else None
         self.logits(lg, h)
         torch.cuda.synchronize()
         return lg, h
+
+
+def topk_f16(logits, hist, lens, k, workspace=None):
+    idx = torch.full((logits.shape[0], k), -7, dtype=torch.int32, device=logits.device)
+    pmqa.topk_rows_f16(logits, hist, lens, k, idx, workspace)
+    torch.cuda.synchronize()
+    return idx
 
 
 def topk(logits, hist, lens, k, key_dtype, workspace=None):
@@ -68,7 +88,9 @@ def sample_cols(n, sample, rng):
 
 
 def check_logits(x, got, sample=None, seed=0, rows=None):
-    """GPU logits within the tolerance of the oracle; returns max |err|/bound."""
+    """GPU logits within the tolerance of the oracle; returns max |err|/bound.
+    float16 logits are checked with the oracle's FP16 rule (the halves that
+    float32 values within the bound round to)."""
     rng = np.random.default_rng(seed)
     worst = 0.0
     rows = range(x.rows) if rows is None else rows
@@ -86,7 +108,8 @@ def check_logits(x, got, sample=None, seed=0, rows=None):
         hbound = O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
                                          x.block_table, x.next_n, r, cols, unscaled=True)
         g = got[r, cols]
-        ok = O.check_logits(g, want, bound, hsum, hbound)
+        check = O.check_logits_f16 if g.dtype == np.float16 else O.check_logits
+        ok = check(g, want, bound, hsum, hbound)
         if not ok.all():
             bad = np.nonzero(~ok)[0][:5]
             raise AssertionError(

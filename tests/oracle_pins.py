@@ -475,7 +475,66 @@ def pin_error_bound(O):
     return fails
 
 
-ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_bins_golden, pin_bins_exhaustive,
+
+def _f32_between(lo, hi):
+    """Every float32 in [lo, hi] (float64 bounds), by bit pattern."""
+    a = np.float32(lo)
+    if float(a) < lo:
+        a = np.nextafter(a, np.float32(np.inf))
+    b = np.float32(hi)
+    if float(b) > hi:
+        b = np.nextafter(b, np.float32(-np.inf))
+    if float(a) > float(b):
+        return np.zeros(0, np.float32)
+    ia, ib = int(np.array(a).view(np.int32)), int(np.array(b).view(np.int32))
+    if float(a) >= 0:  # both non-negative: bit order = value order
+        return np.arange(ia, ib + 1, dtype=np.int64).astype(np.int32).view(np.float32)
+    if float(b) < 0:   # both negative: bit order reversed
+        return np.arange(ib, ia + 1, dtype=np.int64).astype(np.int32).view(np.float32)
+    neg = np.arange(0x80000000, ia + (1 << 32) + 1, dtype=np.int64) & 0xFFFFFFFF
+    pos = np.arange(0, ib + 1, dtype=np.int64)
+    return np.concatenate([neg, pos]).astype(np.uint32).view(np.float32)
+
+
+def pin_logits_f16_check(O, seed=31):
+    """check_logits_f16 accepts exactly the halves that some float32 within the
+    bound rounds to: brute force over every such float32 (the definition),
+    against all halves near them; plus hand cases at a rounding tie."""
+    fails = []
+    rng = np.random.default_rng(seed)
+    cases = [(1.0, 2.0 ** -12), (1.0, 2.0 ** -11), (-3.0, 2.0 ** -9), (0.0, 1e-7), (65504.0, 16.0),
+             (65519.0, 1.0), (1e-6, 1e-8), (-2.0 ** -14, 2.0 ** -26)]
+    for _ in range(40):
+        mag = 10.0 ** rng.uniform(-6, 4.5)
+        want = float(np.float32(rng.choice([-1, 1]) * mag))
+        cases.append((want, abs(want) * 10.0 ** rng.uniform(-7, -3)))
+    halves = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    finite_halves = halves[np.isfinite(halves)]
+    for want, bound in cases:
+        ys = _f32_between(want - bound, want + bound)
+        if ys.size == 0 or ys.size > 3_000_000:
+            continue
+        reach = np.unique(O.fp16_rne(ys).view(np.uint16))
+        got = O.check_logits_f16(finite_halves, np.full(finite_halves.shape, want),
+                                 np.full(finite_halves.shape, bound))
+        accepted = np.unique(finite_halves[got].view(np.uint16))
+        reach_f = reach[np.isfinite(reach.view(np.float16))]
+        if not np.array_equal(np.sort(accepted), np.sort(reach_f)):
+            fails.append(f"want {want!r} bound {bound!r}: accepted "
+                         f"{finite_halves[got][:4].tolist()} vs reachable {reach.view(np.float16)[:4].tolist()}")
+    # 1 - 2^-12 is the tie between the halves 1 - 2^-11 and 1: even -> 1.0
+    one = O.check_logits_f16(np.array([1.0, 1 - 2 ** -11, 1 + 2 ** -10], np.float16),
+                             np.array([1.0] * 3), np.array([2.0 ** -12] * 3))
+    if one.tolist() != [True, False, False]:
+        fails.append(f"tie case: {one.tolist()}")
+    # infinities by class; an overflowing finite value rounds to infinity
+    cls = O.check_logits_f16(np.array([np.inf, -np.inf, np.inf], np.float16),
+                             np.array([np.inf, -np.inf, 70000.0]), np.array([1.0, 1.0, 1.0]))
+    if cls.tolist() != [True, True, True]:
+        fails.append(f"non-finite classes: {cls.tolist()}")
+    return fails
+
+ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_logits_f16_check, pin_bins_golden, pin_bins_exhaustive,
             pin_keys, pin_bins_coarsen_keys, pin_histogram, pin_topk,
             pin_topk_invariants, pin_logits_exact, pin_logits_library,
             pin_logits_paging, pin_error_bound)
