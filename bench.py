@@ -198,7 +198,7 @@ def main() -> int:
     hist = torch.zeros((x.rows, 1024), dtype=torch.int32, device=dev)
     K = 2048
     idx = torch.empty((x.rows, K), dtype=torch.int32, device=dev)
-    ws = torch.empty(pmqa.topk_workspace_bytes(x.rows, x.logits_stride, K), dtype=torch.uint8,
+    ws = torch.zeros(pmqa.topk_workspace_bytes(x.rows, x.logits_stride, K), dtype=torch.uint8,
                      device=dev)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)

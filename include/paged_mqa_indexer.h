@@ -115,11 +115,10 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
 
 /*
  * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
- * `rows` rows of `logits_stride` scores and a given k (host-only query, no
- * device work): per row a 16-byte header and a 4 KiB histogram, and per
- * 4096-score chunk of a row 8 bytes of counts, 4 * min(k, 4096) bytes of
- * columns and 32 KiB of candidates (about 12 bytes per score of the stride).
- * Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
+ * `rows` rows (host-only query, no device work): per row two 8-byte
+ * counter pairs, a 4 KiB histogram and 64 KiB of candidates, each array
+ * rounded up to 256 bytes.  Rows of at most 8192 scores (logits_stride <= 8192) leave the
+ * workspace untouched.  Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
  */
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
 
@@ -151,8 +150,13 @@ size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
  * key_dtype   IDX_KEY_FP32 or IDX_KEY_FP16
  * indices     (device) int32 [rows][k]
  * workspace   (device) scratch of at least topk_workspace_bytes(rows, ...) bytes,
- *             256-B aligned; no initialisation needed; calls that share a
- *             workspace must be ordered on one stream
+ *             256-B aligned, zero-filled before its first use; every call
+ *             leaves it ready for the next (also when a captured graph
+ *             replays the call), so it is zeroed once.  Should it not start
+ *             zeroed, rows whose histogram is exact are still exact (their
+ *             counts then disagree with the histogram and they are selected
+ *             from scratch).  Calls that share a workspace must be ordered on
+ *             one stream.
  */
 idx_status topk_rows(const float* logits, int64_t logits_stride,
                      const int32_t* hist, const int32_t* context_lens,

@@ -248,7 +248,7 @@ def _topk_call(name, dtype, logits, hist, context_lens, k, key_dtype, indices, w
             raise ValueError(f"hist must be contiguous [{rows}, 1024]")
     need = topk_workspace_bytes(rows, logits.stride(0), k)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev)
     lib = load_library()
     with torch.cuda.device(dev):
@@ -266,7 +266,8 @@ def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None,
     """Exact per-row top-k indices of float32 scores into ``indices`` [rows, k].
 
     ``workspace`` is a uint8 GPU tensor of at least topk_workspace_bytes()
-    bytes; when None one is allocated with torch for this call.
+    bytes, zero-filled before its first use (calls keep it reusable); when
+    None a zeroed one is allocated with torch for this call.
     """
     _topk_call("topk_rows", torch.float32, logits, hist, context_lens, k, key_dtype, indices,
                workspace, events)

@@ -14,25 +14,34 @@
 // global memory that another thread of it wrote.
 //
 // Launch sequence of one topk_rows call (one stream, no host sync):
-//   [hist == NULL only] topk_zero_hist + topk_hist: build the row histograms
-//                  in the workspace (the first pass the producer's fused
+//   rows of at most 8192 scores (stride <= 8192): topk_row, one 512-thread
+//                  workgroup per row, whole row in registers: the threshold
+//                  bin b* from the histogram (or from one it builds in LDS
+//                  when there is none), the columns above b* straight to the
+//                  output, the candidates of b* to LDS, where a radix select
+//                  on the remaining key bits finishes the row.
+//   longer rows:
+//   [hist == NULL] topk_zero_hist + topk_hist: build the row histograms in
+//                  the workspace (the first pass the producer's fused
 //                  histogram normally replaces)
-//   topk_scan      many workgroups per row, one 4096-score chunk each: the
-//                  threshold bin b* from the histogram (requested together
-//                  with the chunk's scores); the chunk's columns above b* and
-//                  its (key, column) candidates of b* go, in column order, to
-//                  the chunk's own slots in the workspace, and its two counts
-//                  to counts[row][chunk] (plain stores, no atomics)
-//   topk_refine    one workgroup per row adds up the chunk counts and checks
-//                  them against b*: if they confirm it, the columns above b*
-//                  are gathered into the output and the candidates into LDS,
-//                  where a radix select on the remaining key bits finishes the
-//                  row; otherwise an exact radix select over the whole row
-//                  does.  Chunk slots rather than exact output positions keep
-//                  the scan free of any cross-workgroup order: positions
-//                  would need either a second pass over the scores or a
-//                  device-scope handoff between workgroups, which on this
-//                  multi-die part means L2 write-backs under the other dies.
+//   topk_collect   one 256-thread workgroup per 4096-score chunk: b* from the
+//                  histogram (requested together with the chunk's scores),
+//                  then one 64-bit atomic add on the row's counter pair
+//                  (above b*, in b*) reserves the chunk's places: columns
+//                  above b* go straight to the output (places below k), the
+//                  (key, column) candidates of b* to the row's candidate
+//                  buffer (places below 8192)
+//   topk_finish    one 512-thread workgroup per row reads the counter pair
+//                  (with the row's bins and the first candidates) and checks
+//                  it against b*: if it confirms b*, the candidates are
+//                  ranked in LDS as above; otherwise an exact radix select
+//                  over the whole row rewrites the output.  It then clears
+//                  the counter pair for the next call.
+//
+// Scores are classified against the FP16-key range of b* (bin_key_range),
+// not by computing each score's bin.  Places taken by atomics put neither
+// list in column order: ties at the final key are cut by a radix select on
+// the column.
 //
 // Why the result is exact whatever the histogram holds: bin() is
 // non-increasing in the score and in its FP16 rounding, so every column of a
@@ -46,30 +55,27 @@
 namespace pmqa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;               // histogram and collect workgroups
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 4096;                // scores per workgroup
-constexpr int kPerThread = kChunk / kThreads;  // consecutive scores per thread in the scan
+constexpr int kPerThread = 16;              // consecutive scores per thread
+constexpr int kChunk = kThreads * kPerThread;  // 4096 scores per collect workgroup
+constexpr int kRefineThreads = 512;         // row and finish workgroups
+constexpr int kRowSpan = kRefineThreads * kPerThread;  // 8192: rows topk_row takes whole
 constexpr int kAllBins = kBins;             // threshold meaning "every live score"
-constexpr int kRefineThreads = 512;         // one workgroup per row finishes it
-static_assert(kBins == 4 * kThreads, "threshold_bin: four bins per thread");
+static_assert(kBins == 4 * kThreads, "collect: four bins per thread");
+static_assert(kBins == 2 * kRefineThreads, "row and finish: two bins per thread");
+static_assert(kRowSpan <= kCandCap, "a whole row's candidates fit the LDS buffer");
 
-struct RowMeta {
-  int bstar;  // threshold bin the scan pass used
-  int pad0, pad1, pad2;
-};
-
-// Scratch of one call.  Per (row, chunk) slot: up to gt_cap columns above b*
-// (gt_cap = min(k, 4096): a chunk with k of them already makes the row's
-// count contradict b*) and up to 4096 candidates of b*.
+// Scratch of one call of the chunked path.  The counter pairs must be zero
+// when a call starts; the finish pass leaves them zero.  Each row has two
+// pairs: even collect workgroups place their columns from the front of the
+// output row and of the candidate buffer, odd ones from the back, which
+// halves the atomics on each counter; the lists meet in the middle only when
+// the counts contradict b*.
 struct Workspace {
-  RowMeta* meta;   // [rows]
-  int2* counts;    // [rows][max_chunks]: (above b*, in b*) per chunk
-  int* hist;       // [rows][1024]: histograms built when the caller has none
-  int* gt;         // [rows][max_chunks][gt_cap]: columns above b*
-  uint2* eq;       // [rows][max_chunks][kChunk]: (key, column) in b*
-  int max_chunks;
-  int gt_cap;
+  unsigned long long* count;  // [rows][2]: (above b*) | (in b*) << 32, front and back
+  int* hist;                  // [rows][1024]: histograms built when the caller has none
+  uint2* cand;                // [rows][kCandCap]: (key, column) in b*
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -78,30 +84,19 @@ __host__ __device__ inline int chunks_for(int64_t stride) {
   return static_cast<int>((stride + kChunk - 1) / kChunk);
 }
 
-__host__ __device__ inline int gt_cap_for(int k) { return k < kChunk ? k : kChunk; }
-
-__host__ __device__ inline size_t workspace_size(int rows, int max_chunks, int k) {
-  const size_t slots = static_cast<size_t>(rows) * max_chunks;
-  return align256(sizeof(RowMeta) * rows) + align256(sizeof(int2) * slots) +
-         align256(sizeof(int) * kBins * static_cast<size_t>(rows)) +
-         align256(sizeof(int) * gt_cap_for(k) * slots) + sizeof(uint2) * kChunk * slots;
+__host__ __device__ inline size_t workspace_size(int rows) {
+  return align256(sizeof(unsigned long long) * 2 * rows) + align256(sizeof(int) * kBins * static_cast<size_t>(rows)) +
+         sizeof(uint2) * kCandCap * static_cast<size_t>(rows);
 }
 
-inline Workspace carve(void* base, int rows, int max_chunks, int k) {
-  const size_t slots = static_cast<size_t>(rows) * max_chunks;
+inline Workspace carve(void* base, int rows) {
   char* p = static_cast<char*>(base);
   Workspace w;
-  w.meta = reinterpret_cast<RowMeta*>(p);
-  p += align256(sizeof(RowMeta) * rows);
-  w.counts = reinterpret_cast<int2*>(p);
-  p += align256(sizeof(int2) * slots);
+  w.count = reinterpret_cast<unsigned long long*>(p);
+  p += align256(sizeof(unsigned long long) * 2 * rows);
   w.hist = reinterpret_cast<int*>(p);
   p += align256(sizeof(int) * kBins * static_cast<size_t>(rows));
-  w.gt = reinterpret_cast<int*>(p);
-  p += align256(sizeof(int) * gt_cap_for(k) * slots);
-  w.eq = reinterpret_cast<uint2*>(p);
-  w.max_chunks = max_chunks;
-  w.gt_cap = gt_cap_for(k);
+  w.cand = reinterpret_cast<uint2*>(p);
   return w;
 }
 
@@ -143,10 +138,6 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int row, int64_t s
   const int64_t l = lens[row];
   return static_cast<int>(l < 0 ? 0 : (l > stride ? stride : l));
 }
-
-// Workgroups a row uses: one per started chunk, at least one (an empty row
-// still needs its finishing workgroup).
-__device__ __forceinline__ int row_chunks(int len) { return len > 0 ? (len + kChunk - 1) / kChunk : 1; }
 
 // ---------------------------------------------------------------------------
 // Block-wide helpers for NT threads (s_red holds NT / 64 entries at least).
@@ -208,36 +199,117 @@ __device__ __forceinline__ int2 block_excl_scan2(int a, int b, int* s_red, int2*
   return int2{ba + ia - a, bb + ib - b};
 }
 
-// Threshold bin of a row: the first bin whose inclusive prefix count reaches
-// k, or kAllBins when the histogram holds at most k scores.  Thread t holds
-// the counts of bins 4t .. 4t+3.
-__device__ int threshold_bin(const int (&c)[4], int k, int* s_red) {
-  const int sum = c[0] + c[1] + c[2] + c[3];
-  int total = 0;
-  int run = block_excl_scan(sum, s_red, &total);
-  if (total <= k) return kAllBins;
-  // The crossing lies in exactly one thread's bins (counts are non-negative
-  // in any histogram this call produced; for a foreign one any bin is fine,
-  // the counts checked later decide).
-  if (threadIdx.x == 0) s_red[kWaves] = kAllBins;
-  lds_barrier();
+// Threshold bin of a row from NT threads holding B = 1024 / NT consecutive
+// bins each: the first bin whose running count reaches k, or kAllBins when
+// the histogram holds at most k scores; with it, the histogram's count before
+// that bin and in it.  The least such bin is taken, so all workgroups of a
+// row agree even on a foreign histogram with negative counts (whose crossing
+// need not be unique); the counts checked later decide.  s_red holds
+// NT / 64 + 3 entries.
+struct Threshold {
+  int bin, before, count;
+};
+
+template <int NT, int B>
+__device__ Threshold threshold_bin(const int (&c)[B], int k, int* s_red) {
+  int sum = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (run < k && run + c[i] >= k) s_red[kWaves] = threadIdx.x * 4 + i;
+  for (int i = 0; i < B; ++i) sum += c[i];
+  int total = 0;
+  const int run0 = block_excl_scan<NT>(sum, s_red, &total);
+  if (total <= k) return Threshold{kAllBins, total, 0};
+  constexpr int kSlot = NT / kWave;
+  if (threadIdx.x == 0) s_red[kSlot] = kAllBins;
+  lds_barrier();
+  int run = run0;
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    if (run < k && run + c[i] >= k) atomicMin(&s_red[kSlot], static_cast<int>(threadIdx.x) * B + i);
     run += c[i];
   }
   lds_barrier();
-  const int bstar = s_red[kWaves];
+  const int bstar = s_red[kSlot];
+  if (static_cast<int>(threadIdx.x) == bstar / B) {
+    run = run0;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if (i == bstar % B) {
+        s_red[kSlot + 1] = run;
+        s_red[kSlot + 2] = c[i];
+      }
+      run += c[i];
+    }
+  }
   lds_barrier();
-  return bstar;
+  const Threshold t{bstar, s_red[kSlot + 1], s_red[kSlot + 2]};
+  lds_barrier();
+  return t;
 }
 
+// The FP16 keys of the scores above b* lie in [hi, key(+inf)], those in b*
+// in [lo, hi); NaNs fall outside both.  Unsigned differences test each range
+// with one compare.
+struct Classifier {
+  uint32_t lo, eq_span, hi, gt_span;
+  __device__ explicit Classifier(int bstar) {
+    const KeyRange r = bin_key_range(bstar);
+    lo = r.lo;
+    hi = r.hi;
+    eq_span = r.hi - r.lo;
+    gt_span = r.hi <= 0xFC00u ? 0xFC01u - r.hi : 0u;
+  }
+  __device__ bool above(uint32_t key16) const { return key16 - hi < gt_span; }
+  __device__ bool in_bin(uint32_t key16) const { return key16 - lo < eq_span; }
+};
+
+// The 16 consecutive scores of a thread, from kPerThread / kPerVec 16-byte
+// loads.  Loads past the row's last live vector are clamped to it (in
+// bounds: the stride is a multiple of kPerVec) and their scores are masked
+// off by the caller.
+template <bool F16>
+struct ThreadScores {
+  static constexpr int kPerVec = F16 ? 8 : 4;
+  static constexpr int kVecs = kPerThread / kPerVec;
+  i32x4 v[kVecs];
+  __device__ void load(const char* x, int s0, int len) {
+    const int last_vec = len > 0 ? ((len - 1) / kPerVec) * kPerVec : 0;
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+      const int s = min(s0 + u * kPerVec, last_vec);
+      v[u] = *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s) * (F16 ? 2 : 4));
+    }
+  }
+  __device__ uint32_t half_bits(int i) const { return half_bits_of<F16>(v[i / kPerVec], i % kPerVec); }
+  // The selection key of score i (its FP16 key, or its FP32 key).
+  template <int KEY>
+  __device__ uint32_t key(int i) const {
+    if constexpr (!F16 && KEY == IDX_KEY_FP32) return key_f32(__int_as_float(v[i / kPerVec][i % kPerVec]));
+    else return key_f16(half_bits(i));
+  }
+  // Bit i of *gmask / *emask: score i is live and above b* / in b*.
+  __device__ void classify(const Classifier& cl, int s0, int len, uint32_t* gmask, uint32_t* emask) const {
+    uint32_t g = 0u, e = 0u;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const uint32_t k16 = key_f16(half_bits(i));
+      const bool live = s0 + i < len;
+      g |= static_cast<uint32_t>(live && cl.above(k16)) << i;
+      e |= static_cast<uint32_t>(live && cl.in_bin(k16)) << i;
+    }
+    *gmask = g;
+    *emask = e;
+  }
+};
+
 // ---------------------------------------------------------------------------
-__global__ void topk_zero_hist_kernel(int* hist, int rows) {
+// Clears the histograms (and counter pairs) of the rows.
+__global__ void topk_zero_hist_kernel(int* hist, unsigned long long* count, int rows) {
   const int64_t n = static_cast<int64_t>(rows) * kBins;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     hist[i] = 0;
+    if (i < 2 * rows) count[i] = 0ull;
+  }
 }
 
 // Histogram of each row's live non-NaN scores, added to hist_out.
@@ -277,82 +349,94 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Thread t of a chunk's workgroup takes 16 consecutive columns; a block scan
-// of the per-thread counts gives every column its position in the chunk's
-// slot, so each slot list is in column order.
-template <int KEY, bool F16>
-__global__ __launch_bounds__(kThreads) void topk_scan_kernel(const void* __restrict__ logits,
-                                                             int64_t stride,
-                                                             const int32_t* __restrict__ hist,
-                                                             const int32_t* __restrict__ lens, int k,
-                                                             Workspace ws) {
-  __shared__ int s_red[kWaves + 1];
+// One workgroup per M consecutive 4096-score chunks of a row; in chunk m
+// thread t takes columns 16t .. 16t+15.  The workgroup's two counts, found by
+// one block scan, are added to the row's counter pair in one atomic, whose old
+// value gives the workgroup's first places in both lists.  Several chunks per
+// workgroup keep the atomics on one row's counter to a few dozen, which the
+// memory side serves one after another.
+template <int KEY, bool F16, int M>
+__global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __restrict__ logits,
+                                                                int64_t stride,
+                                                                const int32_t* __restrict__ hist,
+                                                                const int32_t* __restrict__ lens, int k,
+                                                                int32_t* __restrict__ indices, Workspace ws) {
+  __shared__ int s_red[kWaves + 5];
   const int row = blockIdx.y;
-  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
   const int len = clamp_len(lens, row, stride);
-  if (c >= row_chunks(len)) return;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * M * kChunk;  // first column of the workgroup
+  if (first >= len) return;
 
-  // The histogram and the chunk's scores are requested together.
-  const int* h = (hist ? hist : ws.hist) + static_cast<int64_t>(row) * kBins + threadIdx.x * 4;
+  // The histogram and the chunks' scores are requested together.
+  const int* h = hist + static_cast<int64_t>(row) * kBins + tid * 4;
   const int2 h01 = *reinterpret_cast<const int2*>(h);  // 8-B aligned
   const int2 h23 = *reinterpret_cast<const int2*>(h + 2);
   const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
-  const int s0 = c * kChunk + threadIdx.x * kPerThread;
-  constexpr int kPerVec = F16 ? 8 : 4;  // scores per 16-byte load
-  i32x4 v[kPerThread / kPerVec];
+  int s0[M], live[M];  // live[m]: columns of chunk m below this length count
+  ThreadScores<F16> sc[M];
 #pragma unroll
-  for (int i = 0; i < kPerThread / kPerVec; ++i) {
-    // In bounds: s0 + kPerVec*i < len <= stride, both multiples of kPerVec.
-    const int s = s0 + kPerVec * i;
-    v[i] = s < len ? *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s) * (F16 ? 2 : 4))
-                   : i32x4{0, 0, 0, 0};
+  for (int m = 0; m < M; ++m) {
+    // A chunk that starts below len <= stride < 2^31 starts at most at
+    // 2^31 - 4096, so its columns fit an int; a chunk past the row end is
+    // read at column 0 and takes no column.
+    const int64_t c0 = first + m * kChunk;
+    s0[m] = c0 < len ? static_cast<int>(c0) + tid * kPerThread : 0;
+    live[m] = c0 < len ? len : 0;
+    sc[m].load(x, s0[m], len);
   }
   const int hc[4] = {h01.x, h01.y, h23.x, h23.y};
-  const int bstar = threshold_bin(hc, k, s_red);
+  const int bstar = threshold_bin<kThreads, 4>(hc, k, s_red).bin;
 
-  uint32_t gmask = 0u, emask = 0u;  // bit e: column s0 + e
+  const Classifier cl(bstar);
+  uint32_t gmask[M], emask[M];
+  int mine = 0;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const uint32_t hb = half_bits_of<F16>(v[e / kPerVec], e % kPerVec);
-    const bool live = s0 + e < len && !f16_is_nan(hb);
-    const int bin = coarse_bin_f16(hb);
-    gmask |= static_cast<uint32_t>(live && bin < bstar) << e;
-    emask |= static_cast<uint32_t>(live && bin == bstar) << e;
+  for (int m = 0; m < M; ++m) {
+    sc[m].classify(cl, s0[m], live[m], &gmask[m], &emask[m]);
+    mine += __popc(gmask[m]) | (__popc(emask[m]) << 16);
   }
-  // Both counts in one scan: each is at most kChunk < 2^16.
+  // Both counts in one scan: each is at most M * kChunk < 2^16.
   int tot = 0;
-  const int pre = block_excl_scan(__popc(gmask) | (__popc(emask) << 16), s_red, &tot);
-  const int64_t slot = static_cast<int64_t>(row) * ws.max_chunks + c;
-  int* gt = ws.gt + slot * ws.gt_cap;
-  uint2* eq = ws.eq + slot * kChunk;
-  int og = pre & 0xFFFF, oe = pre >> 16;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    if ((gmask >> e) & 1u) {
-      if (og < ws.gt_cap) gt[og] = s0 + e;
-      ++og;
-    }
-    if ((emask >> e) & 1u) {
-      uint32_t key;
-      if constexpr (F16) key = key_f16(half_bits_of<F16>(v[e / kPerVec], e % kPerVec));
-      else key = score_key<KEY>(__int_as_float(v[e / kPerVec][e % kPerVec]));
-      eq[oe++] = uint2{key, static_cast<uint32_t>(s0 + e)};
-    }
+  const int pre = block_excl_scan<kThreads>(mine, s_red, &tot);
+  if (tot == 0) return;  // uniform
+  if (tid == 0) {
+    const unsigned long long add =
+        static_cast<unsigned long long>(tot & 0xFFFF) | (static_cast<unsigned long long>(tot >> 16) << 32);
+    const unsigned long long base = atomicAdd(ws.count + 2 * row + (blockIdx.x & 1), add);
+    s_red[kWaves + 3] = static_cast<int>(static_cast<uint32_t>(base));
+    s_red[kWaves + 4] = static_cast<int>(static_cast<uint32_t>(base >> 32));
   }
-  if (threadIdx.x == 0) {
-    ws.counts[slot] = int2{tot & 0xFFFF, tot >> 16};
-    if (c == 0) ws.meta[row] = RowMeta{bstar, 0, 0, 0};
+  lds_barrier();
+  // Places as unsigned: a row holds fewer than 2^31 columns.
+  uint32_t og = static_cast<uint32_t>(s_red[kWaves + 3]) + static_cast<uint32_t>(pre & 0xFFFF);
+  uint32_t oe = static_cast<uint32_t>(s_red[kWaves + 4]) + static_cast<uint32_t>(pre >> 16);
+  // Place p counts from the front (even workgroups) or from the back (odd).
+  const bool back = (blockIdx.x & 1) != 0;
+  int32_t* out = indices + static_cast<int64_t>(row) * k;
+  uint2* cand = ws.cand + static_cast<int64_t>(row) * kCandCap;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      if ((gmask[m] >> i) & 1u) {
+        if (og < static_cast<uint32_t>(k)) out[back ? k - 1 - static_cast<int>(og) : static_cast<int>(og)] = s0[m] + i;
+        ++og;
+      }
+      if ((emask[m] >> i) & 1u) {
+        if (oe < static_cast<uint32_t>(kCandCap))
+          cand[back ? kCandCap - 1 - static_cast<int>(oe) : static_cast<int>(oe)] =
+              uint2{sc[m].template key<KEY>(i), static_cast<uint32_t>(s0[m] + i)};
+        ++oe;
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Shared memory of the refine pass.
+// Shared memory of the row and finish passes.
 struct RefineShared {
   uint2 cand[kCandCap];   // 64 KiB
-  int pre_g[kRefineThreads];  // a block of chunks: offsets of their slot lists
-  int pre_e[kRefineThreads];
-  int cnt_g[kRefineThreads];  // and their lengths
-  int cnt_e[kRefineThreads];
   int digit_hist[256];
   int red[2 * (kRefineThreads / kWave) + 4];
   uint32_t small[kWave];  // the few keys left after a radix pass
@@ -378,15 +462,17 @@ __device__ __forceinline__ void block_or_and(uint32_t o, uint32_t a, RefineShare
 }
 
 // Given digit_hist (256 counts), the digit d at which the running count
-// taken from the largest digit down first reaches `need`; *before = the count
-// strictly above d, *in_bin = the count of d.
-__device__ int pick_digit(RefineShared& sh, int need, int* before, int* in_bin) {
+// taken from the largest digit down (or, ascending, from the smallest up)
+// first reaches `need`; *before = the count strictly before d, *in_bin = the
+// count of d.
+__device__ int pick_digit(RefineShared& sh, int need, int* before, int* in_bin, bool descending = true) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     int c[4], sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      c[i] = sh.digit_hist[255 - (lane * 4 + i)];
+      const int pos = lane * 4 + i;
+      c[i] = sh.digit_hist[descending ? 255 - pos : pos];
       sum += c[i];
     }
     const int inc = wave_inclusive_scan(sum);
@@ -394,7 +480,8 @@ __device__ int pick_digit(RefineShared& sh, int need, int* before, int* in_bin) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (run < need && run + c[i] >= need) {
-        sh.bcast[0] = 255 - (lane * 4 + i);
+        const int pos = lane * 4 + i;
+        sh.bcast[0] = descending ? 255 - pos : pos;
         sh.bcast[1] = run;
         sh.bcast[2] = c[i];
       }
@@ -493,6 +580,45 @@ __device__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above
   return prefix;
 }
 
+// Among the LDS candidates with key == T, the need-th smallest column C:
+// taking the ties with column <= C takes exactly `need` of them (columns are
+// distinct).  For candidate lists not in column order.
+__device__ uint32_t select_col_lds(RefineShared& sh, int n, uint32_t T, int need) {
+  uint32_t o = 0u, a = 0xFFFFFFFFu;
+  for (int i = threadIdx.x; i < n; i += kRefineThreads) {
+    const uint2 c = sh.cand[i];
+    if (c.x == T) {
+      o |= c.y;
+      a &= c.y;
+    }
+  }
+  block_or_and(o, a, sh);
+  const uint32_t diff = sh.red_or ^ sh.red_and;
+  uint32_t prefix = sh.red_and & ~diff;
+  if (diff) {
+    uint32_t fixed = ~diff;
+    int shift = top_bit(diff) - 7;
+    if (shift < 0) shift = 0;
+    while (true) {
+      for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
+      lds_barrier();
+      for (int i = threadIdx.x; i < n; i += kRefineThreads) {
+        const uint2 c = sh.cand[i];
+        if (c.x == T && ((c.y ^ prefix) & fixed) == 0u) atomicAdd(&sh.digit_hist[(c.y >> shift) & 0xFFu], 1);
+      }
+      lds_barrier();
+      int before = 0, in_bin = 0;
+      const int d = pick_digit(sh, need, &before, &in_bin, false);
+      need -= before;
+      prefix |= static_cast<uint32_t>(d) << shift;
+      fixed |= 0xFFu << shift;
+      if (shift == 0) break;
+      shift = shift >= 8 ? shift - 8 : 0;
+    }
+  }
+  return prefix;
+}
+
 // Append this thread's column to the output through a block-wide LDS counter.
 __device__ __forceinline__ void emit(RefineShared& sh, int32_t* out, int k, bool take, int col) {
   const uint64_t m = __ballot(take);
@@ -564,241 +690,282 @@ __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, i
   }
 }
 
-template <int NT>
-__device__ __forceinline__ int block_max(int v, int* s_red) {
-  v = wave_max(v);
-  if (__lane_id() == 0) s_red[threadIdx.x / kWave] = v;
-  lds_barrier();
-  int m = s_red[0];
-#pragma unroll
-  for (int w = 1; w < NT / kWave; ++w) m = max(m, s_red[w]);
-  lds_barrier();
-  return m;
+// Counts confirm b* when the columns above it fall short of k and those in it
+// make up the difference (within the candidate capacity), or, for the
+// all-bins threshold, when every live score is above it and they are at most
+// k.
+__device__ __forceinline__ bool counts_confirm(int bstar, int n_gt, int n_eq, int k) {
+  if (bstar == kAllBins) return n_gt <= k && n_eq == 0;
+  return n_gt < k && n_gt + n_eq >= k && n_eq <= kCandCap;
 }
 
-// The gather of a row's chunk slots, in chunk order: the columns above b*
-// to out[0 .. n_gt), the candidates to sh.cand (or, when cand_out is given,
-// only their columns to cand_out[0 .. n_eq)), so both lists stay in column
-// order.  Each chunk's counts must fit its slot, which the caller's count
-// check guarantees.
-//
-// Chunks are taken kRefineThreads at a time; each gets tpc threads (a power
-// of two), and a thread's share of a round is kGatherPer consecutive entries
-// of both of its chunk's lists.  Every load of a round is issued before its
-// first store, so a round costs one memory round trip; loads are
-// unconditional (clamped into the slot), because a load under a branch
-// would make the compiler wait for every load issued before it.
-constexpr int kGatherPer = 8;
-
-struct GatherLane {
-  int tpc;      // threads per chunk
-  int cc;       // this thread's chunk in the block (clamped to the last one)
-  bool active;  // the block has a chunk for this thread
-  int l0;       // first entry of this thread's share of a round
-};
-
-__device__ __forceinline__ GatherLane gather_lane(int nb) {
-  GatherLane g;
-  g.tpc = 1 << (31 - __clz(kRefineThreads / nb));
-  const int c = static_cast<int>(threadIdx.x) / g.tpc;
-  g.active = c < nb;
-  g.cc = g.active ? c : nb - 1;
-  g.l0 = (static_cast<int>(threadIdx.x) % g.tpc) * kGatherPer;
-  return g;
-}
-
-__device__ __forceinline__ void load_round(const int* gsrc, const uint2* esrc, int l, int glast, int elast,
-                                           int (&gv)[kGatherPer], uint2 (&ev)[kGatherPer]) {
-#pragma unroll
-  for (int u = 0; u < kGatherPer; ++u) {
-    gv[u] = gsrc[min(l + u, glast)];
-    ev[u] = esrc[min(l + u, elast)];
-  }
-}
-
-__device__ __forceinline__ void store_round(RefineShared& sh, bool active, int l, int cg, int ce, int og,
-                                            int oe, const int (&gv)[kGatherPer],
-                                            const uint2 (&ev)[kGatherPer], int32_t* __restrict__ out,
-                                            int32_t* __restrict__ cand_out) {
-#pragma unroll
-  for (int u = 0; u < kGatherPer; ++u) {
-    if (active && l + u < cg) out[og + l + u] = gv[u];
-    if (active && l + u < ce) {
-      if (cand_out) cand_out[oe + l + u] = static_cast<int32_t>(ev[u].y);
-      else sh.cand[oe + l + u] = ev[u];
-    }
-  }
-}
-
-// The rounds of one block of chunks after any already done: entries from
-// r_begin on.  cg/ce/og/oe: counts and list offsets of this thread's chunk.
-__device__ __forceinline__ void gather_rest(RefineShared& sh, const GatherLane& g, const int* gsrc,
-                                            const uint2* esrc, int r_begin, int cg, int ce, int og, int oe,
-                                            int32_t* __restrict__ out, int32_t* __restrict__ cand_out) {
-  const int step = g.tpc * kGatherPer;
-  for (int r0 = r_begin; r0 < max(cg, ce); r0 += step) {  // per chunk; no barrier inside
-    int gv[kGatherPer];
-    uint2 ev[kGatherPer];
-    load_round(gsrc, esrc, r0 + g.l0, max(cg - 1, 0), max(ce - 1, 0), gv, ev);
-    store_round(sh, g.active, r0 + g.l0, cg, ce, og, oe, gv, ev, out, cand_out);
-  }
-}
-
-// Blocks of chunks from cb0 on (rows of more than kRefineThreads chunks);
-// base_g / base_e = the list entries of the chunks before cb0.
-__device__ void gather_blocks(RefineShared& sh, const Workspace& ws, int64_t slot0, int nch, int cb0,
-                              int base_g, int base_e, int32_t* __restrict__ out,
-                              int32_t* __restrict__ cand_out) {
-  for (int cb = cb0; cb < nch; cb += kRefineThreads) {
-    const int j = cb + threadIdx.x;
-    const int2 v = j < nch ? ws.counts[slot0 + j] : int2{0, 0};
-    int2 tot;
-    const int2 pre = block_excl_scan2<kRefineThreads>(v.x, v.y, sh.red, &tot);
-    sh.pre_g[threadIdx.x] = pre.x;
-    sh.pre_e[threadIdx.x] = pre.y;
-    sh.cnt_g[threadIdx.x] = v.x;
-    sh.cnt_e[threadIdx.x] = v.y;
-    lds_barrier();
-    const GatherLane g = gather_lane(min(kRefineThreads, nch - cb));
-    gather_rest(sh, g, ws.gt + (slot0 + cb + g.cc) * ws.gt_cap, ws.eq + (slot0 + cb + g.cc) * kChunk, 0,
-                sh.cnt_g[g.cc], sh.cnt_e[g.cc], base_g + sh.pre_g[g.cc], base_e + sh.pre_e[g.cc], out,
-                cand_out);
-    base_g += tot.x;
-    base_e += tot.y;
-    lds_barrier();
-  }
-}
-
-// Finishes each row after the scan pass: checks the real counts against b*,
-// then gathers the chunk slots and refines the candidates, or selects over
-// the whole row.
-template <int KEY, bool F16>
-__global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(const void* __restrict__ logits,
-                                                                     int64_t stride,
-                                                                     const int32_t* __restrict__ lens,
-                                                                     int k, int32_t* __restrict__ indices,
-                                                                     Workspace ws) {
-  __shared__ RefineShared sh;
-  const int row = blockIdx.x;
-  const int len = clamp_len(lens, row, stride);
-  const int nch = row_chunks(len);
-  const int bstar = ws.meta[row].bstar;
-  const int64_t slot0 = static_cast<int64_t>(row) * ws.max_chunks;
-  const void* x = score_row<F16>(logits, row, stride);
-  int32_t* out = indices + static_cast<int64_t>(row) * k;
-
-  // Slots have fixed addresses, so the first round of the gather is
-  // requested together with the counts, before they are known (clamped into
-  // the slot; entries past a chunk's count are never used).
-  const GatherLane g = gather_lane(min(kRefineThreads, nch));
-  const int2 first_raw = ws.counts[slot0 + min(static_cast<int>(threadIdx.x), nch - 1)];  // unconditional load
-  const int2 first = static_cast<int>(threadIdx.x) < nch ? first_raw : int2{0, 0};
-  const int* gsrc = ws.gt + (slot0 + g.cc) * ws.gt_cap;
-  const uint2* esrc = ws.eq + (slot0 + g.cc) * kChunk;
-  int gv[kGatherPer];
-  uint2 ev[kGatherPer];
-  load_round(gsrc, esrc, g.l0, ws.gt_cap - 1, kChunk - 1, gv, ev);
-
-  // One block scan of both counts gives the first block's list offsets and
-  // its totals; longer rows add the sums of the other chunks.
-  int2 tot;
-  const int2 pre = block_excl_scan2<kRefineThreads>(first.x, first.y, sh.red, &tot);
-  int n_gt = tot.x, n_eq = tot.y;
-  if (nch > kRefineThreads) {
-    int tg = 0, te = 0;
-    for (int i = kRefineThreads + threadIdx.x; i < nch; i += kRefineThreads) {
-      const int2 v = ws.counts[slot0 + i];
-      tg += v.x;
-      te += v.y;
-    }
-    int2 rest;
-    block_excl_scan2<kRefineThreads>(tg, te, sh.red, &rest);
-    n_gt += rest.x;
-    n_eq += rest.y;
-  }
-  bool valid;
-  if (bstar == kAllBins) valid = n_gt <= k && n_eq == 0;
-  else valid = n_gt < k && n_gt + n_eq >= k && n_eq <= kCandCap;
-  if (!valid) {
-    whole_row_select<KEY, F16>(sh, x, len, k, out);
-    return;
-  }
+// The n_eq candidates of b* are in sh.cand and the output row holds the n_gt
+// columns above b* outside [first_free, first_free + k - n_gt): the best
+// need = k - n_gt candidates fill that gap.  Every
+// key above the need-th largest key T is taken, and of the keys equal to T
+// the lowest columns: the first ones in list order when the list is in
+// column order (thread t ranks a run of consecutive candidates), else those
+// up to the column a radix select on the columns finds.
+__device__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt, int n_eq,
+                                  int first_free, bool column_order) {
   const int need = k - n_gt;
-  // When every candidate is taken (none exist below the all-bins threshold)
-  // their columns go straight to the output.
-  const bool direct = bstar == kAllBins || need == n_eq;
-  int32_t* cand_out = direct ? out + n_gt : nullptr;
-  sh.pre_g[threadIdx.x] = pre.x;
-  sh.pre_e[threadIdx.x] = pre.y;
-  sh.cnt_g[threadIdx.x] = first.x;
-  sh.cnt_e[threadIdx.x] = first.y;
-  lds_barrier();
-  {
-    const int cg = sh.cnt_g[g.cc], ce = sh.cnt_e[g.cc], og = sh.pre_g[g.cc], oe = sh.pre_e[g.cc];
-    store_round(sh, g.active, g.l0, cg, ce, og, oe, gv, ev, out, cand_out);
-    gather_rest(sh, g, gsrc, esrc, g.tpc * kGatherPer, cg, ce, og, oe, out, cand_out);
-  }
-  lds_barrier();
-  if (nch > kRefineThreads) gather_blocks(sh, ws, slot0, nch, kRefineThreads, tot.x, tot.y, out, cand_out);
-  if (direct) {
-    for (int i = n_gt + n_eq + threadIdx.x; i < k; i += kRefineThreads) out[i] = -1;
-    return;
-  }
-  if (threadIdx.x == 0) sh.out_pos = n_gt;
+  if (threadIdx.x == 0) sh.out_pos = first_free;
   lds_barrier();
   int above = 0;
   const uint32_t T = select_key_lds(sh, n_eq, need, &above);
-  // Every key above T is taken, and of the keys equal to T the lowest
-  // columns: the candidate list is in column order, so those are the first
-  // need - above ties in list order.  Thread t ranks a run of consecutive
-  // candidates.
   const int ties_needed = need - above;
-  const int per = (n_eq + kRefineThreads - 1) / kRefineThreads;
-  const int i_begin = min(n_eq, static_cast<int>(threadIdx.x) * per);
-  const int i_end = min(n_eq, i_begin + per);
-  int my_ties = 0;
-  for (int i = i_begin; i < i_end; ++i) my_ties += sh.cand[i].x == T ? 1 : 0;
-  int all_ties = 0;
-  int rank = block_excl_scan<kRefineThreads>(my_ties, sh.red, &all_ties);
-  for (int u = 0; u < per; ++u) {
-    const int i = i_begin + u;
+  if (column_order) {
+    const int per = (n_eq + kRefineThreads - 1) / kRefineThreads;
+    const int i_begin = min(n_eq, static_cast<int>(threadIdx.x) * per);
+    const int i_end = min(n_eq, i_begin + per);
+    int my_ties = 0;
+    for (int i = i_begin; i < i_end; ++i) my_ties += sh.cand[i].x == T ? 1 : 0;
+    int all_ties = 0;
+    int rank = block_excl_scan<kRefineThreads>(my_ties, sh.red, &all_ties);
+    for (int u = 0; u < per; ++u) {
+      const int i = i_begin + u;
+      bool take = false;
+      int col = 0;
+      if (i < i_end) {
+        const uint2 cd = sh.cand[i];
+        const bool tie = cd.x == T;
+        take = cd.x > T || (tie && rank < ties_needed);
+        rank += tie ? 1 : 0;
+        col = static_cast<int>(cd.y);
+      }
+      emit(sh, out, k, take, col);
+    }
+    return;
+  }
+  int tc = 0;
+  for (int i = threadIdx.x; i < n_eq; i += kRefineThreads) tc += sh.cand[i].x == T ? 1 : 0;
+  const int ties = block_sum<kRefineThreads>(tc, sh.red);
+  const uint32_t col_cut = ties > ties_needed ? select_col_lds(sh, n_eq, T, ties_needed) : 0xFFFFFFFFu;
+  for (int i0 = 0; i0 < n_eq; i0 += kRefineThreads) {
+    const int i = i0 + threadIdx.x;
     bool take = false;
     int col = 0;
-    if (i < i_end) {
+    if (i < n_eq) {
       const uint2 cd = sh.cand[i];
-      const bool tie = cd.x == T;
-      take = cd.x > T || (tie && rank < ties_needed);
-      rank += tie ? 1 : 0;
+      take = cd.x > T || (cd.x == T && cd.y <= col_cut);
       col = static_cast<int>(cd.y);
     }
     emit(sh, out, k, take, col);
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows of at most 8192 scores: one workgroup per row, thread t takes columns
+// 16t .. 16t+15, so the block scan of the per-thread counts keeps both lists
+// in column order.  OWN_HIST: no histogram was given; the workgroup bins its
+// row in LDS first.
+template <int KEY, bool F16, bool OWN_HIST>
+__global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __restrict__ logits,
+                                                                  int64_t stride,
+                                                                  const int32_t* __restrict__ hist,
+                                                                  const int32_t* __restrict__ lens, int k,
+                                                                  int32_t* __restrict__ indices) {
+  __shared__ RefineShared sh;
+  __shared__ int s_hist[OWN_HIST ? kBins : 1];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int len = clamp_len(lens, row, stride);
+  const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
+  int32_t* out = indices + static_cast<int64_t>(row) * k;
+
+  // The thread's two bins and its 16 scores are requested together.
+  int hv[2] = {0, 0};
+  if constexpr (!OWN_HIST) {
+    const int2 h = *reinterpret_cast<const int2*>(hist + static_cast<int64_t>(row) * kBins + 2 * tid);
+    hv[0] = h.x;
+    hv[1] = h.y;
+  }
+  const int s0 = tid * kPerThread;
+  ThreadScores<F16> sc;
+  sc.load(x, s0, len);
+  if constexpr (OWN_HIST) {
+    s_hist[2 * tid] = 0;
+    s_hist[2 * tid + 1] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const uint32_t hb = sc.half_bits(i);
+      if (s0 + i < len && !f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
+    }
+    lds_barrier();
+    hv[0] = s_hist[2 * tid];
+    hv[1] = s_hist[2 * tid + 1];
+  }
+  const int bstar = threshold_bin<kRefineThreads, 2>(hv, k, sh.red).bin;
+
+  const Classifier cl(bstar);
+  uint32_t gmask, emask;
+  sc.classify(cl, s0, len, &gmask, &emask);
+  int tot = 0;
+  const int pre = block_excl_scan<kRefineThreads>(__popc(gmask) | (__popc(emask) << 16), sh.red, &tot);
+  const int n_gt = tot & 0xFFFF, n_eq = tot >> 16;
+  if (!counts_confirm(bstar, n_gt, n_eq, k)) {
+    whole_row_select<KEY, F16>(sh, x, len, k, out);
+    return;
+  }
+  int og = pre & 0xFFFF, oe = pre >> 16;
+  // When every candidate is taken (none exist below the all-bins threshold)
+  // their columns go straight to the output.
+  const bool direct = bstar == kAllBins || k - n_gt == n_eq;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    if ((gmask >> i) & 1u) out[og++] = s0 + i;  // og < n_gt <= k
+    if ((emask >> i) & 1u) {
+      if (direct) out[n_gt + oe] = s0 + i;
+      else sh.cand[oe] = uint2{sc.template key<KEY>(i), static_cast<uint32_t>(s0 + i)};
+      ++oe;
+    }
+  }
+  if (direct) {
+    for (int i = n_gt + n_eq + tid; i < k; i += kRefineThreads) out[i] = -1;
+    return;
+  }
+  lds_barrier();
+  finish_candidates(sh, out, k, n_gt, n_eq, n_gt, true);
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per row after topk_collect: the two counter pairs, the
+// thread's two bins and the first 1024 candidates from each end are requested
+// together (the candidate buffer has a fixed address; entries past the
+// counts are unused).
+constexpr int kEarlyCand = 2;  // candidates per thread and end loaded with the counts
+
+__device__ __forceinline__ int saturate_int(uint32_t v) { return static_cast<int>(min(v, 0x3FFFFFFFu)); }
+
+template <int KEY, bool F16>
+__global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void* __restrict__ logits,
+                                                                     int64_t stride,
+                                                                     const int32_t* __restrict__ hist,
+                                                                     const int32_t* __restrict__ lens, int k,
+                                                                     int32_t* __restrict__ indices,
+                                                                     Workspace ws) {
+  __shared__ RefineShared sh;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int len = clamp_len(lens, row, stride);
+  const void* x = score_row<F16>(logits, row, stride);
+  int32_t* out = indices + static_cast<int64_t>(row) * k;
+  const uint2* cand = ws.cand + static_cast<int64_t>(row) * kCandCap;
+
+  const unsigned long long front = ws.count[2 * row], back = ws.count[2 * row + 1];
+  const int2 h = *reinterpret_cast<const int2*>(hist + static_cast<int64_t>(row) * kBins + 2 * tid);
+  uint2 early_f[kEarlyCand], early_b[kEarlyCand];
+#pragma unroll
+  for (int j = 0; j < kEarlyCand; ++j) {
+    early_f[j] = cand[j * kRefineThreads + tid];
+    early_b[j] = cand[kCandCap - 1 - (j * kRefineThreads + tid)];
+  }
+  const int hv[2] = {h.x, h.y};
+  const Threshold th = threshold_bin<kRefineThreads, 2>(hv, k, sh.red);
+  const int bstar = th.bin;
+  if (tid == 0) {  // the next call starts from zero
+    ws.count[2 * row] = 0ull;
+    ws.count[2 * row + 1] = 0ull;
+  }
+  // Saturated: beyond k (or the capacity) the counts fail the check anyway.
+  const int gf = saturate_int(static_cast<uint32_t>(front)), ef = saturate_int(static_cast<uint32_t>(front >> 32));
+  const int gb = saturate_int(static_cast<uint32_t>(back)), eb = saturate_int(static_cast<uint32_t>(back >> 32));
+  const int n_gt = gf + gb, n_eq = ef + eb;
+  // The counts must also equal the histogram's own: for an exact histogram
+  // they do, unless the counters did not start at zero (a workspace never
+  // used before), and then the row is selected from scratch rather than from
+  // places this call did not fill.
+  if (!counts_confirm(bstar, n_gt, n_eq, k) || n_gt != th.before || n_eq != th.count) {
+    whole_row_select<KEY, F16>(sh, x, len, k, out);
+    return;
+  }
+  // Columns above b* fill out[0 .. gf) and out[k - gb .. k); the selected
+  // candidates go in between.
+  if (bstar == kAllBins || k - n_gt == n_eq) {
+    // Every candidate is taken: their columns go straight to the output.
+#pragma unroll
+    for (int j = 0; j < kEarlyCand; ++j) {
+      const int i = j * kRefineThreads + tid;
+      if (i < ef) out[gf + i] = static_cast<int32_t>(early_f[j].y);
+      if (i < eb) out[gf + ef + i] = static_cast<int32_t>(early_b[j].y);
+    }
+    for (int i = kEarlyCand * kRefineThreads + tid; i < ef; i += kRefineThreads)
+      out[gf + i] = static_cast<int32_t>(cand[i].y);
+    for (int i = kEarlyCand * kRefineThreads + tid; i < eb; i += kRefineThreads)
+      out[gf + ef + i] = static_cast<int32_t>(cand[kCandCap - 1 - i].y);
+    for (int i = gf + n_eq + tid; i < k - gb; i += kRefineThreads) out[i] = -1;
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < kEarlyCand; ++j) {
+    const int i = j * kRefineThreads + tid;
+    if (i < ef) sh.cand[i] = early_f[j];
+    if (i < eb) sh.cand[ef + i] = early_b[j];
+  }
+  for (int i = kEarlyCand * kRefineThreads + tid; i < ef; i += kRefineThreads) sh.cand[i] = cand[i];
+  for (int i = kEarlyCand * kRefineThreads + tid; i < eb; i += kRefineThreads) sh.cand[ef + i] = cand[kCandCap - 1 - i];
+  lds_barrier();
+  finish_candidates(sh, out, k, n_gt, n_eq, gf, false);
+}
+
 }  // namespace
 
 size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k) {
   if (rows <= 0 || logits_stride <= 0 || k <= 0) return 0;
-  return workspace_size(rows, chunks_for(logits_stride), k);
+  return workspace_size(rows);
 }
 
 template <int KEY, bool F16>
-void launch_select(const TopkArgs& a, const Workspace& ws, dim3 grid, hipStream_t stream,
-                   hipEvent_t start, hipEvent_t stop) {
-  launch_kernel(topk_scan_kernel<KEY, F16>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
-                a.logits_stride, a.hist, a.context_lens, a.k, ws);
-  launch_kernel(topk_refine_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop,
-                a.logits, a.logits_stride, a.context_lens, a.k, a.indices, ws);
+void launch_rows_whole(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
+  if (a.hist)
+    launch_kernel(topk_row_kernel<KEY, F16, false>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
+                  a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+  else
+    launch_kernel(topk_row_kernel<KEY, F16, true>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
+                  a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+}
+
+// Chunks per collect workgroup: at most 64 workgroups per row up to rows of
+// 2^20 scores.
+inline int chunks_per_collect(int chunks) { return chunks > 128 ? 4 : chunks > 64 ? 2 : 1; }
+
+template <int KEY, bool F16, int M>
+void launch_collect(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int chunks, hipStream_t stream,
+                    hipEvent_t start) {
+  const dim3 grid(static_cast<unsigned>((chunks + M - 1) / M), static_cast<unsigned>(a.rows));
+  launch_kernel(topk_collect_kernel<KEY, F16, M>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
+                a.logits_stride, hist, a.context_lens, a.k, a.indices, ws);
+}
+
+template <int KEY, bool F16>
+void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int chunks, hipStream_t stream,
+                    hipEvent_t start, hipEvent_t stop) {
+  switch (chunks_per_collect(chunks)) {
+    case 4: launch_collect<KEY, F16, 4>(a, ws, hist, chunks, stream, start); break;
+    case 2: launch_collect<KEY, F16, 2>(a, ws, hist, chunks, stream, start); break;
+    default: launch_collect<KEY, F16, 1>(a, ws, hist, chunks, stream, start); break;
+  }
+  launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, a.logits,
+                a.logits_stride, hist, a.context_lens, a.k, a.indices, ws);
 }
 
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
-  const int max_chunks = chunks_for(a.logits_stride);
-  const Workspace ws = carve(a.workspace, a.rows, max_chunks, a.k);
-  const dim3 grid(static_cast<unsigned>(max_chunks), static_cast<unsigned>(a.rows));
+  // FP16 scores are ranked by their FP16 keys.
+  if (a.logits_stride <= kRowSpan) {
+    if (a.logits_f16) launch_rows_whole<IDX_KEY_FP16, true>(a, stream, ev);
+    else if (a.key_dtype == IDX_KEY_FP32) launch_rows_whole<IDX_KEY_FP32, false>(a, stream, ev);
+    else launch_rows_whole<IDX_KEY_FP16, false>(a, stream, ev);
+    return hipGetLastError();
+  }
+  const Workspace ws = carve(a.workspace, a.rows);
+  const int chunks = chunks_for(a.logits_stride);
+  const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.rows));
   hipEvent_t start = ev.start;  // recorded by the first kernel of the call
-  if (a.hist == nullptr) {
+  const int32_t* hist = a.hist;
+  if (hist == nullptr) {
     launch_kernel(topk_zero_hist_kernel, dim3(min(1024, (a.rows * kBins + 255) / 256)), dim3(256), stream,
-                  start, nullptr, ws.hist, a.rows);
+                  start, nullptr, ws.hist, ws.count, a.rows);
     start = nullptr;
     if (a.logits_f16)
       launch_kernel(topk_hist_kernel<true>, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
@@ -806,11 +973,11 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents 
     else
       launch_kernel(topk_hist_kernel<false>, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
                     a.logits_stride, a.context_lens, ws.hist);
+    hist = ws.hist;
   }
-  // FP16 scores are ranked by their FP16 keys.
-  if (a.logits_f16) launch_select<IDX_KEY_FP16, true>(a, ws, grid, stream, start, ev.stop);
-  else if (a.key_dtype == IDX_KEY_FP32) launch_select<IDX_KEY_FP32, false>(a, ws, grid, stream, start, ev.stop);
-  else launch_select<IDX_KEY_FP16, false>(a, ws, grid, stream, start, ev.stop);
+  if (a.logits_f16) launch_chunked<IDX_KEY_FP16, true>(a, ws, hist, chunks, stream, start, ev.stop);
+  else if (a.key_dtype == IDX_KEY_FP32) launch_chunked<IDX_KEY_FP32, false>(a, ws, hist, chunks, stream, start, ev.stop);
+  else launch_chunked<IDX_KEY_FP16, false>(a, ws, hist, chunks, stream, start, ev.stop);
   return hipGetLastError();
 }
 

@@ -65,6 +65,30 @@ class DevInputs:
         return lg, h
 
 
+# The selector gives each 8192-score chunk of a row its own workgroup; a row
+# of one chunk is finished by that workgroup alone, longer rows by the last
+# of their workgroups to arrive.  Edge-case tests run both: "one_chunk" keeps
+# the first 8192 columns of every row (stride 8192), "as_is" keeps the rows
+# (several chunks), and "wide" also pads the stride past 2^18 scores, so most
+# workgroups of the grid find no chunk.
+CHUNK = 8192
+WIDE_STRIDE = (1 << 18) + 8
+PATHS = ["one_chunk", "as_is", "wide"]
+
+
+def on_path(scores, lens, path):
+    """(scores, lens) as device tensors laid out for ``path``."""
+    if path == "as_is":
+        return scores, lens
+    if path == "one_chunk":
+        n = min(CHUNK, scores.shape[1])
+        return scores[:, :n].contiguous(), torch.clamp(lens, max=n)
+    w = torch.full((scores.shape[0], WIDE_STRIDE), float("inf"), dtype=scores.dtype,
+                   device=scores.device)
+    w[:, :scores.shape[1]] = scores
+    return w, lens
+
+
 def topk_f16(logits, hist, lens, k, workspace=None):
     idx = torch.full((logits.shape[0], k), -7, dtype=torch.int32, device=logits.device)
     pmqa.topk_rows_f16(logits, hist, lens, k, idx, workspace)

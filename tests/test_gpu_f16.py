@@ -12,8 +12,8 @@ import torch
 
 import gen
 import oracle as O
-from tests.gpu_harness import (DevInputs, announce, check_hist, check_logits, check_topk,
-                               topk_f16)
+from tests.gpu_harness import (PATHS, DevInputs, announce, check_hist, check_logits, check_topk,
+                               on_path, topk_f16)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +71,8 @@ def test_f16_workload_parity(gpu, name):
     torch.cuda.empty_cache()
 
 
-def test_f16_ties_and_stale_histogram(gpu):
+@pytest.mark.parametrize("path", PATHS)
+def test_f16_ties_and_stale_histogram(gpu, path):
     """Many equal halves (ties broken by the lower column) and a stale
     histogram (the selector must fall back and stay exact)."""
     rng = np.random.default_rng(41)
@@ -79,10 +80,11 @@ def test_f16_ties_and_stale_histogram(gpu):
     vals = rng.choice(np.array([1.0, 1.5, 2.0, -0.5, np.inf, np.nan], np.float32), size=(rows, stride),
                       p=[0.4, 0.2, 0.05, 0.3, 0.03, 0.02]).astype(np.float16)
     lens = np.array([stride, 12345, 4000], np.int32)
-    lg = torch.from_numpy(vals).to("cuda:0")
-    ln = torch.from_numpy(lens).to("cuda:0")
+    lg, ln = on_path(torch.from_numpy(vals).to("cuda:0"), torch.from_numpy(lens).to("cuda:0"), path)
+    vals, lens = lg.cpu().numpy(), ln.cpu().numpy()
     for hist in (None, torch.full((rows, 1024), 3, dtype=torch.int32, device="cuda:0")):
         for k in (1, 100, 2048, 8192):
-            announce(f"topk_rows_f16 ties k={k} hist={'stale' if hist is not None else 'NULL'}")
+            announce(f"topk_rows_f16 ties k={k} hist={'stale' if hist is not None else 'NULL'} "
+                     f"path={path}")
             idx = topk_f16(lg, hist, ln, k)
             check_topk(idx.cpu().numpy(), vals.astype(np.float32), lens, k, O.KEY_FP16)

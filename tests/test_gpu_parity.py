@@ -7,8 +7,8 @@ import torch
 import gen
 import oracle as O
 from tests import oracle_pins as P
-from tests.gpu_harness import (DEV, DevInputs, announce, check_hist, check_logits,
-                               check_padding, check_topk, topk)
+from tests.gpu_harness import (DEV, PATHS, DevInputs, announce, check_hist, check_logits,
+                               check_padding, check_topk, on_path, topk)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,16 +59,16 @@ def test_bins_of_every_fp16_encoding_and_rounding_edge(gpu):
     check_hist(lens, buf, h.cpu().numpy(), hist_in=O.coarse_histogram(buf, lens))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
 @pytest.mark.parametrize("k", [1, 100, 2048, 8192])
-def test_topk_edge_rows_without_histogram(gpu, key, k):
+def test_topk_edge_rows_without_histogram(gpu, key, k, path):
     rows = _edge_rows()
     buf, lens = _scores_dev(rows)
-    s = torch.from_numpy(buf).to(DEV)
-    ln = torch.from_numpy(lens).to(DEV)
-    announce(f"topk_rows hist=NULL edge rows k={k} key={key}")
+    s, ln = on_path(torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV), path)
+    announce(f"topk_rows hist=NULL edge rows k={k} key={key} path={path}")
     idx = topk(s, None, ln, k, key)
-    check_topk(idx.cpu().numpy(), buf, lens, k, key)
+    check_topk(idx.cpu().numpy(), s.cpu().numpy(), ln.cpu().numpy(), k, key)
 
 
 def _small_inputs(next_n, seed, base, weight_scale=1.0, inf_frac=0.0):
@@ -156,13 +156,15 @@ def test_histogram_off_is_bitwise_identical_and_counts_accumulate(gpu):
     assert torch.equal(h3, first)
 
 
-def test_topk_stale_histograms_stay_exact(gpu):
+@pytest.mark.parametrize("path", PATHS)
+def test_topk_stale_histograms_stay_exact(gpu, path):
     x = _small_inputs(1, 61, [20000, 9000, 3000, 12000])
     d = DevInputs(x)
-    announce("topk_rows stale histograms")
+    announce(f"topk_rows stale histograms path={path}")
     lg, h = d.run(with_hist=True, fill=INF)
+    lg, ln = on_path(lg, d.lens, path)
     got = lg.cpu().numpy()
-    lens = x.context_lens
+    lens = ln.cpu().numpy()
     stale = {
         "zeros": torch.zeros_like(h),
         "doubled": 2 * h,
@@ -175,11 +177,12 @@ def test_topk_stale_histograms_stay_exact(gpu):
         for key in (O.KEY_FP32, O.KEY_FP16):
             for k in (1, 2048, 5000):
                 announce(f"topk_rows stale={name} key={key} k={k}")
-                idx = topk(lg, hs, d.lens, k, key)
+                idx = topk(lg, hs, ln, k, key)
                 check_topk(idx.cpu().numpy(), got, lens, k, key)
 
 
-def test_topk_threshold_bin_overflow_falls_back_exactly(gpu):
+@pytest.mark.parametrize("path", PATHS)
+def test_topk_threshold_bin_overflow_falls_back_exactly(gpu, path):
     rng = np.random.default_rng(71)
     n = 30000
     rows = [
@@ -191,21 +194,22 @@ def test_topk_threshold_bin_overflow_falls_back_exactly(gpu):
         np.where(rng.random(n) < 0.5, np.float32(np.nan), np.float32(2.0)).astype(np.float32),
     ]
     buf, lens = _scores_dev(rows)
-    s = torch.from_numpy(buf).to(DEV)
-    ln = torch.from_numpy(lens).to(DEV)
+    s, ln = on_path(torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV), path)
+    buf, lens = s.cpu().numpy(), ln.cpu().numpy()
     h = torch.zeros((len(rows), 1024), dtype=torch.int32, device=DEV)
     gpu.score_histogram(s, ln, h)
     for key in (O.KEY_FP32, O.KEY_FP16):
         for k in (2048, 8192):
-            announce(f"topk_rows overflow rows key={key} k={k}")
+            announce(f"topk_rows overflow rows key={key} k={k} path={path}")
             idx = topk(s, h, ln, k, key)
             check_topk(idx.cpu().numpy(), buf, lens, k, key)
             idx = topk(s, None, ln, k, key)
             check_topk(idx.cpu().numpy(), buf, lens, k, key)
 
 
-def test_topk_ties_across_chunks_go_to_lower_columns(gpu):
-    # equal keys spread over many collect workgroups and both refine paths
+@pytest.mark.parametrize("path", PATHS)
+def test_topk_ties_go_to_lower_columns(gpu, path):
+    # equal keys spread over one or many chunks and both refine paths
     n = 50000
     rng = np.random.default_rng(81)
     a = rng.integers(0, 5, n).astype(np.float32)             # few distinct values
@@ -214,26 +218,46 @@ def test_topk_ties_across_chunks_go_to_lower_columns(gpu):
     c = np.zeros(n, np.float32)
     c[rng.integers(0, n, n // 2)] = -0.0                     # +0 / -0 mix
     buf, lens = _scores_dev([a, b, c])
-    s = torch.from_numpy(buf).to(DEV)
-    ln = torch.from_numpy(lens).to(DEV)
+    s, ln = on_path(torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV), path)
+    buf, lens = s.cpu().numpy(), ln.cpu().numpy()
     h = torch.zeros((3, 1024), dtype=torch.int32, device=DEV)
     gpu.score_histogram(s, ln, h)
     for key in (O.KEY_FP32, O.KEY_FP16):
         for k in (7, 2048, 6000):
-            announce(f"topk_rows ties key={key} k={k}")
+            announce(f"topk_rows ties key={key} k={k} path={path}")
             idx = topk(s, h, ln, k, key)
             check_topk(idx.cpu().numpy(), buf, lens, k, key)
 
 
+def test_topk_row_of_more_than_512_chunks(gpu):
+    # the last workgroup adds up and gathers the chunk slots 512 at a time
+    n = 512 * 8192 + 5000
+    rng = np.random.default_rng(95)
+    buf = (rng.standard_normal((1, n), dtype=np.float32) * np.float32(3.0)).astype(np.float32)
+    buf[0, rng.integers(0, n, 3000)] = np.float32(7.5)          # ties across many chunks
+    lens = np.array([n - 3], np.int32)
+    s = torch.from_numpy(buf).to(DEV)
+    ln = torch.from_numpy(lens).to(DEV)
+    h = torch.zeros((1, 1024), dtype=torch.int32, device=DEV)
+    gpu.score_histogram(s, ln, h)
+    for key in (O.KEY_FP32, O.KEY_FP16):
+        announce(f"topk_rows {n}-score row key={key}")
+        idx = topk(s, h, ln, 2048, key)
+        check_topk(idx.cpu().numpy(), buf, lens, 2048, key)
+
+
 def test_calls_replay_in_a_hip_graph(gpu):
-    x = _small_inputs(2, 91, [5000, 3000])
+    # one row of one selector chunk, one of several (the arrival counters of
+    # a replayed launch must start from zero again); the workspace starts
+    # out as garbage and eager calls on it run between the replays
+    x = _small_inputs(2, 91, [5000, 30000])
     d = DevInputs(x)
     k = 2048
     lg = d.new_logits(INF)
     h = d.new_hist()
     idx = torch.full((x.rows, k), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty(gpu.topk_workspace_bytes(x.rows, x.logits_stride, k), dtype=torch.uint8,
-                     device=DEV)
+    ws = torch.full((gpu.topk_workspace_bytes(x.rows, x.logits_stride, k),), 0xA5, dtype=torch.uint8,
+                    device=DEV)
     announce("eager reference for graph replay")
     d.logits(lg, h)
     gpu.topk_rows(lg, h, d.lens, k, O.KEY_FP32, idx, ws)
@@ -260,3 +284,7 @@ def test_calls_replay_in_a_hip_graph(gpu):
         live = torch.from_numpy(np.arange(x.logits_stride)[None, :] < x.context_lens[:, None]).to(DEV)
         assert torch.equal(torch.where(live, lg, 0.0), torch.where(live, ref_lg, 0.0))
         _ = (lg * 2).sum().item()  # unrelated eager work between replays
+        idx2 = torch.full((x.rows, k), -7, dtype=torch.int32, device=DEV)
+        gpu.topk_rows(lg, h, d.lens, k, O.KEY_FP32, idx2, ws)  # same workspace, eager
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(idx2.cpu().numpy(), axis=1), ref_idx)
