@@ -50,6 +50,7 @@
 // n_gt < k <= n_gt + n_eq, the top-k is those n_gt columns plus the best
 // k - n_gt of the candidates.  Any other count means the histogram was not the
 // histogram of these scores, and the row is selected from scratch.
+#include "bin_key_range.h"
 #include "indexer_common.h"
 
 namespace pmqa {
@@ -352,9 +353,9 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
 // One workgroup per M consecutive 4096-score chunks of a row; in chunk m
 // thread t takes columns 16t .. 16t+15.  The workgroup's two counts, found by
 // one block scan, are added to the row's counter pair in one atomic, whose old
-// value gives the workgroup's first places in both lists.  Several chunks per
-// workgroup keep the atomics on one row's counter to a few dozen, which the
-// memory side serves one after another.
+// value gives the workgroup's first places in both lists.  The memory side
+// serves the atomics on one counter one after another, so long rows give each
+// workgroup two chunks.
 template <int KEY, bool F16, int M>
 __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __restrict__ logits,
                                                                 int64_t stride,
@@ -926,9 +927,10 @@ void launch_rows_whole(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
                   a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
 }
 
-// Chunks per collect workgroup: at most 64 workgroups per row up to rows of
-// 2^20 scores.
-inline int chunks_per_collect(int chunks) { return chunks > 128 ? 4 : chunks > 64 ? 2 : 1; }
+// Chunks per collect workgroup: two for rows of more than 64 chunks, which
+// halves the atomics on their counters.  (Four measured no faster on rows of
+// 2^20 scores: the extra registers halve the waves per SIMD.)
+inline int chunks_per_collect(int chunks) { return chunks > 64 ? 2 : 1; }
 
 template <int KEY, bool F16, int M>
 void launch_collect(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int chunks, hipStream_t stream,
@@ -941,11 +943,8 @@ void launch_collect(const TopkArgs& a, const Workspace& ws, const int32_t* hist,
 template <int KEY, bool F16>
 void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int chunks, hipStream_t stream,
                     hipEvent_t start, hipEvent_t stop) {
-  switch (chunks_per_collect(chunks)) {
-    case 4: launch_collect<KEY, F16, 4>(a, ws, hist, chunks, stream, start); break;
-    case 2: launch_collect<KEY, F16, 2>(a, ws, hist, chunks, stream, start); break;
-    default: launch_collect<KEY, F16, 1>(a, ws, hist, chunks, stream, start); break;
-  }
+  if (chunks_per_collect(chunks) == 2) launch_collect<KEY, F16, 2>(a, ws, hist, chunks, stream, start);
+  else launch_collect<KEY, F16, 1>(a, ws, hist, chunks, stream, start);
   launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, a.logits,
                 a.logits_stride, hist, a.context_lens, a.k, a.indices, ws);
 }

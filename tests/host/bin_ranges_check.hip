@@ -5,6 +5,7 @@
 // number of mismatches and exits non-zero if there are any.
 #include <cstdio>
 
+#include "bin_key_range.h"
 #include "indexer_common.h"
 
 int main() {
