@@ -25,10 +25,16 @@
 //     same byte-to-k assignment, so the contraction over d is complete.
 //   * Heads are the MFMA rows (two 16-head blocks), keys the columns; a lane
 //     holds 8 heads of one key per row, so ReLU and the head weights are
-//     applied in-lane, and a two-step lane exchange finishes the head sum and
-//     leaves lane l with the logit of key l of the page (coalesced stores).
+//     applied in-lane, and two permlane swaps (register exchanges between
+//     16-lane rows, no LDS) finish the head sum and leave lane l with the
+//     logit of key l of the page (coalesced stores).
 //   * The next page of every wave is in flight while the current one is
-//     computed.
+//     computed.  Workgroups of requests with several rows fetch Q and the
+//     weights once and hand them to their waves through LDS; three or four
+//     rows get 8-wave workgroups.
+//   * Scores are staged in LDS and leave with 16-byte stores after the
+//     workgroup's last K load, as float32 or as their FP16 rounding (vLLM
+//     PR #52696, "Summary").
 //   * The histogram slots of the workgroup's rows live in LDS and are added
 //     to the global histogram (two bins per 64-bit atomic) when it finishes.
 #include <type_traits>
