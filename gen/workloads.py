@@ -21,7 +21,10 @@ on (H=32, D=128, 64-token pages):
 
 Value recipe: Q ~ N(0,1) cast to e4m3; K rows ~ N(0,1), per-token scale
 absmax/448, codes = e4m3(k / scale); head weights N(0,1)/sqrt(32) times the
-variant's factor.  Physical pages are a seeded permutation of one pool that
+variant's factor.  MXFP4 K (the "/mxfp4" workloads): the same K rows, each
+block of 32 dimensions scaled by 2^(floor(log2(absmax)) - 2) (E8M0 byte) and
+its elements rounded to the nearest E2M1 value (ties to the even code,
+saturated at +-6), packed 68 bytes per token.  Physical pages are a seeded permutation of one pool that
 has ~1% spare pages.  Slots of a request's last page past its longest row and
 the spare pages hold K = 448 with scale 1e6, so an unmasked read shows up as a
 huge score.
@@ -48,6 +51,8 @@ SEEDS = {
     "varlen_decode": 404,
     "very_long": 505,
     "very_long/scores": 506,
+    "long_decode/mxfp4": 212,
+    "spec_verify/mxfp4": 311,
 }
 
 # Head-weight factors for the three verify variants.
@@ -60,8 +65,9 @@ class IndexerInputs:
 
     name: str
     q: np.ndarray            # uint8 [rows, 32, 128]   e4m3fn codes
-    kv_pages: np.ndarray     # uint8 [num_pages, 64, 128] e4m3fn codes
-    k_scales: np.ndarray     # f32   [num_pages, 64]
+    kv_pages: np.ndarray     # uint8 [num_pages, 64, 128] e4m3fn codes, or
+                             #       [num_pages, 64, 68] packed MXFP4 tokens
+    k_scales: np.ndarray     # f32   [num_pages, 64] (None with MXFP4 pages)
     weights: np.ndarray      # f32   [rows, 32]
     block_table: np.ndarray  # int32 [B, max_pages]
     context_lens: np.ndarray  # int32 [rows]
@@ -88,9 +94,40 @@ class IndexerInputs:
         """Longest row length of each request (the keys its K sweep reads)."""
         return self.context_lens.reshape(self.B, self.next_n).max(axis=1)
 
+    @property
+    def mxfp4(self) -> bool:
+        return self.kv_pages.shape[-1] == MXFP4_TOKEN_BYTES
+
     def k_bytes(self) -> int:
-        """Bytes of K rows the indexer must read (128 B per key per request)."""
-        return int(self.request_keys().astype(np.int64).sum()) * DIM
+        """Bytes of K rows the indexer must read per request and key: 128
+        (FP8 codes; the scale is counted apart) or 68 (MXFP4 token)."""
+        return int(self.request_keys().astype(np.int64).sum()) * int(self.kv_pages.shape[-1])
+
+
+MXFP4_TOKEN_BYTES = 68
+_E2M1_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def to_mxfp4_tokens(k: np.ndarray) -> np.ndarray:
+    """float32 [n, 128] -> uint8 [n, 68] packed MXFP4 tokens (see module doc)."""
+    k = np.asarray(k, dtype=np.float64)
+    n = k.shape[0]
+    blocks = k.reshape(n, 4, 32)
+    amax = np.abs(blocks).max(axis=2)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    v = blocks / np.ldexp(1.0, e)[:, :, None]
+    a = np.minimum(np.abs(v), 6.0)
+    # nearest E2M1 magnitude, ties to the even code (codes 0..7 by magnitude)
+    hi = np.searchsorted(_E2M1_POS, a, side="left").clip(0, 7)
+    lo = (hi - 1).clip(0, 7)
+    dlo, dhi = a - _E2M1_POS[lo], _E2M1_POS[hi] - a
+    mag = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    codes = (mag | np.where((v < 0) & (mag > 0), 8, 0)).astype(np.uint8).reshape(n, 128)
+    out = np.empty((n, MXFP4_TOKEN_BYTES), dtype=np.uint8)
+    out[:, :64] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    out[:, 64:] = (e + 127).astype(np.uint8)
+    return out
 
 
 def to_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
@@ -102,11 +139,13 @@ def to_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
 
 def make_indexer_inputs(name, B, next_n, base_lens, seed, weight_scale=1.0,
                         inf_frac=0.0, logits_stride=None, max_pages=None,
-                        spare_frac=0.01, pages_per_chunk=4096):
+                        spare_frac=0.01, pages_per_chunk=4096, kfmt="fp8"):
     """Build one indexer call.
 
     base_lens: int per request; row j of request b sees base_lens[b] + j keys.
+    kfmt: "fp8" (E4M3 codes + per-token scales) or "mxfp4" (packed tokens).
     """
+    mx = kfmt == "mxfp4"
     rng = np.random.Generator(np.random.PCG64(seed))
     base_lens = np.asarray(base_lens, dtype=np.int64).reshape(B)
     rows = B * next_n
@@ -127,11 +166,14 @@ def make_indexer_inputs(name, B, next_n, base_lens, seed, weight_scale=1.0,
                / np.float32(math.sqrt(HEADS)) * np.float32(weight_scale))
 
     # K pool, generated in chunks of pages to bound host memory.
-    kv_pages = np.empty((num_pages, PAGE, DIM), dtype=np.uint8)
-    k_scales = np.empty((num_pages, PAGE), dtype=np.float32)
+    kv_pages = np.empty((num_pages, PAGE, MXFP4_TOKEN_BYTES if mx else DIM), dtype=np.uint8)
+    k_scales = None if mx else np.empty((num_pages, PAGE), dtype=np.float32)
     for p0 in range(0, num_pages, pages_per_chunk):
         p1 = min(num_pages, p0 + pages_per_chunk)
         k = rng.standard_normal(((p1 - p0) * PAGE, DIM), dtype=np.float32)
+        if mx:
+            kv_pages[p0:p1] = to_mxfp4_tokens(k).reshape(p1 - p0, PAGE, MXFP4_TOKEN_BYTES)
+            continue
         sc = np.abs(k).max(axis=1) / np.float32(448.0)
         kv_pages[p0:p1] = to_e4m3fn_codes(k / sc[:, None]).reshape(p1 - p0, PAGE, DIM)
         k_scales[p0:p1] = sc.reshape(p1 - p0, PAGE)
@@ -144,17 +186,23 @@ def make_indexer_inputs(name, B, next_n, base_lens, seed, weight_scale=1.0,
         block_table[b, :req_pages[b]] = perm[offs[b]:offs[b + 1]]
     spare = perm[used:]
 
-    # Poison: spare pages and slots past each request's longest row.
-    kv_pages[spare] = 0x7E
-    k_scales[spare] = 1e6
+    # Poison: spare pages and slots past each request's longest row (FP8:
+    # K = 448 with scale 1e6; MXFP4: every element +6 with scale 2^127).
+    def poison(page, tail=0):
+        if mx:
+            kv_pages[page, tail:, :64] = 0x77
+            kv_pages[page, tail:, 64:] = 254
+        else:
+            kv_pages[page, tail:] = 0x7E
+            k_scales[page, tail:] = 1e6
+
+    poison(spare)
     for b in range(B):
         tail = int(req_keys[b] % PAGE)
         if tail:
-            last = block_table[b, req_pages[b] - 1]
-            kv_pages[last, tail:] = 0x7E
-            k_scales[last, tail:] = 1e6
+            poison(block_table[b, req_pages[b] - 1], tail)
 
-    if inf_frac > 0.0:
+    if inf_frac > 0.0 and not mx:
         mask = rng.random((num_pages, PAGE)) < inf_frac
         k_scales[mask] = np.inf
 
@@ -183,12 +231,18 @@ def config_inputs(name: str) -> IndexerInputs:
                                    logits_stride=262144, max_pages=262144 // PAGE)
     if name == "very_long":
         return make_indexer_inputs(name, 4, 1, [1048576] * 4, SEEDS[name])
+    if name == "long_decode/mxfp4":
+        return make_indexer_inputs(name, 8, 1, [131072] * 8, SEEDS[name], kfmt="mxfp4")
+    if name == "spec_verify/mxfp4":
+        return make_indexer_inputs(name, 16, 4, [32768] * 16, SEEDS[name],
+                                   weight_scale=VERIFY_WEIGHT_SCALE["fine"], kfmt="mxfp4")
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("tiny_decode", "long_decode", "spec_verify/fine",
                 "spec_verify/unit", "spec_verify/mixed", "varlen_decode",
                 "very_long")
+MXFP4_CONFIG_NAMES = ("long_decode/mxfp4", "spec_verify/mxfp4")
 
 
 def very_long_scores(rows=4, n=1048576, seed=None) -> np.ndarray:

@@ -35,6 +35,12 @@ floating point is involved:
 * ``topk_rows``            -- exact top-k by a full sort, key descending, ties to
                               the lower column index (P1 SGLang commit: ties go
                               to the lower slot).
+* ``e2m1_decode_table``, ``decode_e8m0``, ``dequant_mxfp4_tokens`` -- block-scaled
+                              E2M1 (MXFP4) index keys in the packed 68-byte token
+                              layout (P2 "unpack_fp4_index_keys_to_fp8": block-scaled
+                              E2M1 index-K; P3 "the packed 68-byte cache layout",
+                              dequantized MXFP4 references).  The logits functions
+                              take such pages in place of FP8 pages + scales.
 
 Readings taken where the pages leave a step open (each is justified in the
 design notes of the repository):
@@ -49,6 +55,10 @@ design notes of the repository):
   selected; +-inf are counted in the saturating bins and are selectable.
 * FP16 keys order scores by fp16_RN(x); equal fp16 values are ties.
 * Fewer selectable scores than k: all of them, then -1 padding.
+* MXFP4 keys: a token is 64 bytes of E2M1 codes (dimension 2i in the low
+  nibble of byte i, 2i+1 in the high nibble) followed by four E8M0 scale
+  bytes, one per 32 consecutive dimensions; the key is code value times
+  2^(scale - 127), with no further per-token scale; Q stays E4M3.
 """
 
 from __future__ import annotations
@@ -97,13 +107,68 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# MXFP4 keys (OCP microscaling formats: E2M1 elements, E8M0 block scales)
+#     E2M1: sign bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent
+#     field 0 encodes subnormals m/2; no infinity or NaN.
+#     E8M0: an unsigned biased exponent, 2^(e - 127); 0xFF is NaN.
+# ---------------------------------------------------------------------------
+MXFP4_TOKEN_BYTES = 68  # 64 bytes of codes for 128 dimensions + 4 scale bytes
+MXFP4_BLOCK = 32        # dimensions per scale
+
+
+def e2m1_decode_table() -> np.ndarray:
+    """All 16 E2M1 codes decoded to float64 from the bit definition."""
+    table = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        sign = -1.0 if (code >> 3) & 1 else 1.0
+        exp_field = (code >> 1) & 0x3
+        mant = code & 0x1
+        if exp_field == 0:
+            value = sign * (mant / 2.0) * 2.0 ** (1 - 1)
+        else:
+            value = sign * (1.0 + mant / 2.0) * 2.0 ** (exp_field - 1)
+        table[code] = value
+    return table
+
+
+E2M1 = e2m1_decode_table()
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes to float64 powers of two (0xFF -> NaN)."""
+    e = np.asarray(codes, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+
+
+def dequant_mxfp4_tokens(tokens: np.ndarray) -> np.ndarray:
+    """uint8 [..., 68] packed MXFP4 tokens -> float64 [..., 128] keys."""
+    tokens = np.asarray(tokens, dtype=np.uint8)
+    data = tokens[..., :HEAD_DIM // 2]
+    codes = np.empty(data.shape[:-1] + (HEAD_DIM,), dtype=np.uint8)
+    codes[..., 0::2] = data & 0x0F
+    codes[..., 1::2] = data >> 4
+    scales = decode_e8m0(tokens[..., HEAD_DIM // 2:MXFP4_TOKEN_BYTES])  # [..., 4]
+    per_dim = np.repeat(scales, MXFP4_BLOCK, axis=-1)                  # [..., 128]
+    with np.errstate(invalid="ignore", over="ignore"):
+        return E2M1[codes] * per_dim
+
+
+def is_mxfp4_pages(kv_pages) -> bool:
+    """MXFP4 pages are [num_pages, 64, 68]; FP8 pages [num_pages, 64, 128]."""
+    return np.asarray(kv_pages).shape[-1] == MXFP4_TOKEN_BYTES
+
+
+# ---------------------------------------------------------------------------
 # O2-O4  logits
 # ---------------------------------------------------------------------------
 def _request_keys_at(kv_pages, k_scales, block_table_row, cols):
-    """Gather the keys at logical positions ``cols`` of one request."""
+    """Gather the keys at logical positions ``cols`` of one request: FP8
+    codes and their per-token scales, or MXFP4 tokens (scale 1)."""
     cols = np.asarray(cols, dtype=np.int64)
     pages = np.asarray(block_table_row, dtype=np.int64)[cols // PAGE_SIZE]
     slots = cols % PAGE_SIZE
+    if is_mxfp4_pages(kv_pages):
+        return dequant_mxfp4_tokens(kv_pages[pages, slots]), np.ones(len(cols))
     k8 = kv_pages[pages, slots]
     sc = k_scales[pages, slots]
     return decode_e4m3fn(k8), sc.astype(np.float64)
@@ -129,8 +194,9 @@ def indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens,
     """Dense logits of every live key of every row.
 
     q            uint8  [B*next_n, 32, 128]  (E4M3FN codes)
-    kv_pages     uint8  [num_pages, 64, 128] (E4M3FN codes)
-    k_scales     f32    [num_pages, 64]
+    kv_pages     uint8  [num_pages, 64, 128] (E4M3FN codes), or
+                 uint8  [num_pages, 64, 68]  (packed MXFP4 tokens)
+    k_scales     f32    [num_pages, 64] (None with MXFP4 pages)
     weights      f32    [B*next_n, 32]
     block_table  int32  [B, max_pages]       (shared by the next_n rows of b)
     context_lens int32  [B*next_n]           (row r sees keys [0, len_r))

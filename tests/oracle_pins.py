@@ -7,6 +7,9 @@ with a planted mistake and requires at least one to fail.
 
 What the pins lean on, none of which is the oracle's own code:
   * the OCP E4M3FN bit definition and PyTorch's float8_e4m3fn cast;
+  * the E2M1 value table of the OCP MX specification (tests/golden/) and
+    PyTorch's float8_e8m0fnu cast; hand-built MXFP4 tokens; the FP8 path on
+    MXFP4 keys with one scale per token;
   * exact rational arithmetic (fractions.Fraction) for fp16 rounding, for the
     dot products and for the whole logit formula on tiny inputs;
   * hand-derived bins and keys in tests/golden/ (DeepGEMM PR #94 "What this
@@ -534,7 +537,132 @@ def pin_logits_f16_check(O, seed=31):
         fails.append(f"non-finite classes: {cls.tolist()}")
     return fails
 
+# ---------------------------------------------------------- MXFP4 keys --
+def load_golden_e2m1():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e2m1_values_by_hand.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                c, v = line.split()
+                vals[int(c)] = float(v)
+    return vals
+
+
+def pin_e2m1(O):
+    """The 16 E2M1 values against the hand-written table from the MX spec,
+    signed zeros included."""
+    fails = []
+    want = load_golden_e2m1()
+    for c in range(16):
+        got = float(O.E2M1[c])
+        if got != want[c] or math.copysign(1.0, got) != math.copysign(1.0, want[c]):
+            fails.append(f"E2M1 code {c}: {got}, want {want[c]}")
+    return fails
+
+
+def pin_e8m0(O):
+    """All 256 E8M0 scale bytes against PyTorch's float8_e8m0fnu cast."""
+    codes = np.arange(256, dtype=np.uint8)
+    with np.errstate(invalid="ignore"):
+        want = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().numpy().astype(np.float64)
+    got = O.decode_e8m0(codes)
+    if not np.array_equal(got, want, equal_nan=True):
+        bad = np.nonzero(~((got == want) | (np.isnan(got) & np.isnan(want))))[0][:5]
+        return [f"E8M0 codes {bad.tolist()} differ from torch"]
+    return []
+
+
+def pin_mxfp4_layout(O):
+    """Hand-built tokens: dimension 2i in the low nibble of byte i, 2i+1 in the
+    high nibble; scale byte j covers dimensions 32j .. 32j+31."""
+    fails = []
+    tok = np.zeros((2, 68), dtype=np.uint8)
+    tok[0, 0] = 0x2B      # dim 0: code 0xB = -1.5, dim 1: code 2 = 1.0
+    tok[0, 20] = 0x70     # dim 40: 0, dim 41: code 7 = 6.0
+    tok[0, 63] = 0x0D     # dim 126: code 0xD = -3.0, dim 127: 0
+    tok[0, 64:68] = [127, 128, 125, 130]   # 1, 2, 1/4, 8
+    tok[1, :64] = 0x11    # every dimension 0.5
+    tok[1, 64:68] = [0, 254, 255, 127]     # 2^-127, 2^127, NaN, 1
+    want0 = np.zeros(128)
+    want0[0], want0[1], want0[41], want0[126] = -1.5, 1.0, 6.0 * 2, -3.0 * 8
+    got = O.dequant_mxfp4_tokens(tok)
+    if not np.array_equal(got[0], want0):
+        fails.append(f"token 0: nonzero dims {np.nonzero(got[0])[0].tolist()} "
+                     f"values {got[0][np.nonzero(got[0])[0]].tolist()}")
+    want1 = np.concatenate([np.full(32, 0.5 * 2.0 ** -127), np.full(32, 0.5 * 2.0 ** 127),
+                            np.full(32, np.nan), np.full(32, 0.5)])
+    if not np.array_equal(got[1], want1, equal_nan=True):
+        fails.append("token 1: block scales misapplied")
+    return fails
+
+
+def _mxfp4_as_fp8(x, scale_bytes):
+    """FP8 pages + per-token scales holding exactly the keys of MXFP4 pages
+    whose four block scales are all equal (every E2M1 value is an E4M3 value)."""
+    codes = np.empty(x.kv_pages.shape[:2] + (128,), dtype=np.uint8)
+    codes[..., 0::2] = x.kv_pages[..., :64] & 0x0F
+    codes[..., 1::2] = x.kv_pages[..., :64] >> 4
+    vals = load_golden_e2m1()
+    table = np.array([vals[c] for c in range(16)], dtype=np.float32)
+    kv8 = torch.from_numpy(table[codes]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sc = np.ldexp(np.float32(1.0), scale_bytes.astype(np.int64) - 127).astype(np.float32)
+    return kv8, sc
+
+
+def pin_mxfp4_matches_fp8_path(O):
+    """With one scale per token, MXFP4 logits equal the FP8-path logits of the
+    same keys written as E4M3 codes with that scale (bitwise)."""
+    import gen
+    x = gen.make_indexer_inputs("mx", 2, 2, [150, 131], 41, kfmt="mxfp4")
+    rng = np.random.default_rng(4)
+    per_tok = rng.integers(120, 134, size=x.kv_pages.shape[:2]).astype(np.uint8)
+    x.kv_pages[..., 64:68] = per_tok[..., None]
+    got = O.indexer_logits(x.q, x.kv_pages, None, x.weights, x.block_table,
+                           x.context_lens, x.next_n, x.logits_stride)
+    kv8, sc = _mxfp4_as_fp8(x, per_tok)
+    want = O.indexer_logits(x.q, kv8, sc, x.weights, x.block_table,
+                            x.context_lens, x.next_n, x.logits_stride)
+    if not np.array_equal(got, want, equal_nan=True):
+        return ["MXFP4 logits differ from the FP8 path on equal block scales"]
+    return []
+
+
+def pin_mxfp4_exact(O, n_cols=4):
+    """Different scales per block: the formula in exact rationals, rounded once."""
+    import gen
+    fails = []
+    x = gen.make_indexer_inputs("mx", 1, 2, [90], 43, kfmt="mxfp4")
+    rng = np.random.default_rng(6)
+    x.kv_pages[..., 64:68] = rng.integers(118, 138, size=x.kv_pages.shape[:2] + (4,)).astype(np.uint8)
+    got = O.indexer_logits(x.q, x.kv_pages, None, x.weights, x.block_table,
+                           x.context_lens, x.next_n, x.logits_stride)
+    vals = load_golden_e2m1()
+    for r in range(x.rows):
+        n = int(x.context_lens[r])
+        qd = torch_e4m3_decode(x.q[r])
+        for s in sorted(set(rng.integers(0, n, n_cols).tolist()) | {n - 1}):
+            tok = x.kv_pages[int(x.block_table[0, s // 64]), s % 64]
+            kd = []
+            for d in range(128):
+                byte = int(tok[d // 2])
+                code = (byte >> 4) if d % 2 else (byte & 0xF)
+                kd.append(Fraction(vals[code]) * Fraction(2) ** (int(tok[64 + d // 32]) - 127))
+            total = Fraction(0)
+            for h in range(32):
+                dot = sum((Fraction(float(qd[h, d])) * kd[d] for d in range(128)), Fraction(0))
+                if dot > 0:
+                    total += Fraction(float(x.weights[r, h])) * dot
+            want = np.float32(float(total))
+            g = got[r, s]
+            ulp = np.spacing(np.float32(abs(want))) if want != 0 else np.float32(1e-45)
+            if not abs(float(g) - float(want)) <= float(ulp):
+                fails.append(f"MXFP4 logit[{r},{s}] = {g}, exact {want}")
+    return fails
+
+
 ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_logits_f16_check, pin_bins_golden, pin_bins_exhaustive,
             pin_keys, pin_bins_coarsen_keys, pin_histogram, pin_topk,
             pin_topk_invariants, pin_logits_exact, pin_logits_library,
-            pin_logits_paging, pin_error_bound)
+            pin_logits_paging, pin_error_bound, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
+            pin_mxfp4_matches_fp8_path, pin_mxfp4_exact)

@@ -186,6 +186,52 @@ def m_keys_zero_signs_equal(O):
     O.score_keys = keys
 
 
+def m_e2m1_subnormal(O):
+    t = O.E2M1.copy()
+    t[1], t[9] = 1.0, -1.0  # subnormal read as 1.0 * 2^0
+    O.E2M1 = t
+
+
+def _wrap_dequant(O, fn):
+    O.dequant_mxfp4_tokens = lambda tok: fn(np.asarray(tok, dtype=np.uint8))
+
+
+def m_mxfp4_nibbles_swapped(O):
+    def deq(tok):
+        data = tok[..., :64]
+        codes = np.empty(data.shape[:-1] + (128,), dtype=np.uint8)
+        codes[..., 0::2] = data >> 4
+        codes[..., 1::2] = data & 0x0F
+        sc = np.repeat(O.decode_e8m0(tok[..., 64:68]), 32, axis=-1)
+        return O.E2M1[codes] * sc
+    _wrap_dequant(O, deq)
+
+
+def m_mxfp4_scale_blocks_reversed(O):
+    orig = O.dequant_mxfp4_tokens
+
+    def deq(tok):
+        t = tok.copy()
+        t[..., 64:68] = tok[..., 64:68][..., ::-1]
+        return orig(t)
+    _wrap_dequant(O, deq)
+
+
+def m_mxfp4_scale_ignored(O):
+    orig = O.dequant_mxfp4_tokens
+
+    def deq(tok):
+        t = tok.copy()
+        t[..., 64:68] = 127
+        return orig(t)
+    _wrap_dequant(O, deq)
+
+
+def m_e8m0_bias_128(O):
+    O.decode_e8m0 = lambda c: np.where(np.asarray(c, np.int64) == 255, np.nan,
+                                       np.ldexp(1.0, np.asarray(c, np.int64) - 128))
+
+
 MUTANTS = [
     (m_e4m3_bias, [P.pin_e4m3]),
     (m_e4m3_subnormal, [P.pin_e4m3]),
@@ -207,6 +253,11 @@ MUTANTS = [
     (m_hist_drops_incoming, [P.pin_histogram]),
     (m_keys_negatives_not_inverted, [P.pin_keys]),
     (m_keys_zero_signs_equal, [P.pin_keys]),
+    (m_e2m1_subnormal, [P.pin_e2m1, P.pin_mxfp4_matches_fp8_path]),
+    (m_mxfp4_nibbles_swapped, [P.pin_mxfp4_layout, P.pin_mxfp4_exact]),
+    (m_mxfp4_scale_blocks_reversed, [P.pin_mxfp4_layout, P.pin_mxfp4_exact]),
+    (m_mxfp4_scale_ignored, [P.pin_mxfp4_layout, P.pin_mxfp4_matches_fp8_path]),
+    (m_e8m0_bias_128, [P.pin_e8m0, P.pin_mxfp4_exact]),
 ]
 
 
