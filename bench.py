@@ -51,7 +51,9 @@ FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.json")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.md")
 COPY_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
-LOGITS_KERNEL = "indexer_logits_kernel"
+# The counted kernel: one row per request, histogram on, float32 logits, FP8 K
+# (the long-decode launch; other instantiations in the same run are ignored).
+LOGITS_KERNEL = "indexer_logits_kernel<1, true, false, 0>"
 KERNEL_SOURCES = ("paged_mqa_logits_indexer_amd/csrc/logits_kernel.hip",
                   "paged_mqa_logits_indexer_amd/csrc/indexer_common.h")
 
@@ -70,8 +72,12 @@ def algorithmic_bytes(x) -> dict:
     req_keys = x.request_keys().astype(np.int64)
     pages = (req_keys + 63) // 64
     lens = x.context_lens.astype(np.int64)
-    k = int(req_keys.sum()) * 128            # fp8 K rows, once per request
-    scales = int(req_keys.sum()) * 4         # one fp32 scale per key
+    if x.mxfp4:
+        k = int(req_keys.sum()) * 68         # packed MXFP4 tokens (codes + block scales)
+        scales = 0
+    else:
+        k = int(req_keys.sum()) * 128        # fp8 K rows, once per request
+        scales = int(req_keys.sum()) * 4     # one fp32 scale per key
     logits = int(lens.sum()) * 4             # fp32 logits written
     table = int(pages.sum()) * 4             # block-table entries
     qw = x.rows * (32 * 128 + 32 * 4 + 4)    # Q, weights, lengths
@@ -159,6 +165,8 @@ def main() -> int:
     ap.add_argument("--workload", default="long_decode")
     ap.add_argument("--fp16-steps", type=int, default=100,
                     help="steps of the second timing with FP16 score keys")
+    ap.add_argument("--mxfp4-steps", type=int, default=100,
+                    help="steps of the same shape with MXFP4 K (indexer_logits_mxfp4)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
@@ -192,8 +200,22 @@ def main() -> int:
     torch.cuda.set_device(dev)
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     x = gen.config_inputs(args.workload)
-    t = {k: torch.from_numpy(np.ascontiguousarray(getattr(x, k))).to(dev)
-         for k in ("q", "kv_pages", "k_scales", "weights", "block_table", "context_lens")}
+    def upload(x):
+        return {k: (None if getattr(x, k) is None
+                    else torch.from_numpy(np.ascontiguousarray(getattr(x, k))).to(dev))
+                for k in ("q", "kv_pages", "k_scales", "weights", "block_table", "context_lens")}
+
+    def call_logits(x, t, logits, hist, events):
+        """indexer_logits, or indexer_logits_mxfp4 for packed MXFP4 pages."""
+        if x.mxfp4:
+            pmqa.indexer_logits_mxfp4(t["q"], t["kv_pages"], t["weights"], t["block_table"],
+                                      t["context_lens"], x.next_n, logits, hist, events=events)
+        else:
+            pmqa.indexer_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"],
+                                t["block_table"], t["context_lens"], x.next_n, logits, hist,
+                                events=events)
+
+    t = upload(x)
     logits = torch.full((x.rows, x.logits_stride), float("inf"), dtype=torch.float32, device=dev)
     hist = torch.zeros((x.rows, 1024), dtype=torch.int32, device=dev)
     K = 2048
@@ -238,7 +260,7 @@ def main() -> int:
             out = [a.elapsed_time(b) * 1e3 for a, b in evs]
         return out
 
-    def run(n_steps, key, record, split=False):
+    def run(n_steps, key, record, split=False, x=x, t=t, logits=logits, hist=hist):
         """Steps of logits + top-k.  Without `split` only the step's start
         (logits kernel begins) and end (last top-k kernel ends) are recorded,
         so no event sits between the two calls; with it each call is timed
@@ -250,9 +272,7 @@ def main() -> int:
             evict()
             hist.zero_()
             ws0.record(stream)
-            pmqa.indexer_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"],
-                                t["block_table"], t["context_lens"], x.next_n, logits, hist,
-                                events=(ls, le if split else None))
+            call_logits(x, t, logits, hist, (ls, le if split else None))
             pmqa.topk_rows(logits, hist, t["context_lens"], K, key, idx, ws,
                            events=(ts if split else None, te))
             ws1.record(stream)
@@ -279,7 +299,7 @@ def main() -> int:
     print(f"[bench] per-call timing {args.steps} steps", file=sys.stderr, flush=True)
     lt, tt, _, _ = run(args.steps, pmqa.KEY_FP32, True, split=True)
     print(f"[bench] FP16-key timing {args.fp16_steps} steps", file=sys.stderr, flush=True)
-    if args.fp16_steps > 0:
+    if args.fp16_steps > 0 and not x.mxfp4:
         _, _, st16, _ = run(args.fp16_steps, pmqa.KEY_FP16, True)
         _, tt16, _, _ = run(args.fp16_steps, pmqa.KEY_FP16, True, split=True)
         print(f"[bench] FP16-logits timing {args.fp16_steps} steps", file=sys.stderr, flush=True)
@@ -288,6 +308,31 @@ def main() -> int:
         lt_h = run16(args.fp16_steps, True, split=True)
     else:
         st16, tt16, lt_h, st_h = [], [], [], []
+
+    # the same shape with MXFP4 K pages (half the K bytes)
+    mx_out = None
+    mx_name = {"long_decode": "long_decode/mxfp4"}.get(args.workload)
+    if mx_name is None and args.workload.startswith("spec_verify/") and not x.mxfp4:
+        mx_name = "spec_verify/mxfp4"
+    if args.mxfp4_steps > 0 and mx_name:
+        print(f"[bench] {mx_name}: {args.mxfp4_steps} steps", file=sys.stderr, flush=True)
+        xm = gen.config_inputs(mx_name)
+        tm = upload(xm)
+        lgm = torch.full((xm.rows, xm.logits_stride), float("inf"), dtype=torch.float32, device=dev)
+        hm = torch.zeros((xm.rows, 1024), dtype=torch.int32, device=dev)
+        mx_kw = dict(x=xm, t=tm, logits=lgm, hist=hm)
+        run(5, pmqa.KEY_FP32, False, **mx_kw)
+        _, _, st_m, _ = run(args.mxfp4_steps, pmqa.KEY_FP32, True, **mx_kw)
+        lt_m, tt_m, _, _ = run(args.mxfp4_steps, pmqa.KEY_FP32, True, split=True, **mx_kw)
+        abm = algorithmic_bytes(xm)
+        lm = float(np.mean(lt_m))
+        mx_out = {"workload": mx_name, "step_us_mean": round(float(np.mean(st_m)), 3),
+                  "indexer_logits_mxfp4_mean": round(lm, 3),
+                  "topk_rows_fp32_mean": round(float(np.mean(tt_m)), 3),
+                  "k_bytes": abm["k"], "bytes_per_launch": abm["total"],
+                  "achieved_gbps": round(abm["total"] / (lm * 1e-6) / 1e9, 1),
+                  "frac": round(abm["total"] / (lm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del tm, lgm, hm
 
     # practical read ceiling over the same number of bytes as K
     ab = algorithmic_bytes(x)
@@ -357,6 +402,9 @@ def main() -> int:
         # FP16 logits output: indexer_logits_f16 (halves) + topk_rows_f16 (FP16 keys)
         "fp16_logits": ({"step_us_mean": round(float(np.mean(st_h)), 3),
                          "indexer_logits_f16_mean": round(float(np.mean(lt_h)), 3)} if st_h else None),
+        # the same shape with MXFP4 K: indexer_logits_mxfp4 + topk_rows (FP32 keys);
+        # frac = algorithmic bytes / time against the HBM peak
+        "mxfp4_k": mx_out,
         "hbm": {
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),
@@ -366,7 +414,7 @@ def main() -> int:
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "indexer_logits_kernel<1,true>",
+                     "traffic": traffic, "kernel": "indexer_logits_kernel<1, true, false, 0>",
                      "bytes_per_launch": ab["total"]},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }

@@ -214,6 +214,11 @@ def make_indexer_inputs(name, B, next_n, base_lens, seed, weight_scale=1.0,
 
 def config_inputs(name: str) -> IndexerInputs:
     """The named decode workload at its full size."""
+    if name == "long_decode/mxfp4":
+        return make_indexer_inputs(name, 8, 1, [131072] * 8, SEEDS[name], kfmt="mxfp4")
+    if name == "spec_verify/mxfp4":
+        return make_indexer_inputs(name, 16, 4, [32768] * 16, SEEDS[name],
+                                   weight_scale=VERIFY_WEIGHT_SCALE["fine"], kfmt="mxfp4")
     if name == "tiny_decode":
         return make_indexer_inputs(name, 1, 1, [4096], SEEDS[name])
     if name == "long_decode":
@@ -231,11 +236,7 @@ def config_inputs(name: str) -> IndexerInputs:
                                    logits_stride=262144, max_pages=262144 // PAGE)
     if name == "very_long":
         return make_indexer_inputs(name, 4, 1, [1048576] * 4, SEEDS[name])
-    if name == "long_decode/mxfp4":
-        return make_indexer_inputs(name, 8, 1, [131072] * 8, SEEDS[name], kfmt="mxfp4")
-    if name == "spec_verify/mxfp4":
-        return make_indexer_inputs(name, 16, 4, [32768] * 16, SEEDS[name],
-                                   weight_scale=VERIFY_WEIGHT_SCALE["fine"], kfmt="mxfp4")
+
     raise KeyError(name)
 
 

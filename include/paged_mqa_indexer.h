@@ -14,9 +14,12 @@
  *        flushed with packed 64-bit atomics, token Q tile); SGLang commit
  *        "Replace the CuTe DSL selector with a JIT CUDA selector; add verify"
  *        (exact top-2048 selector from the histogram, fallback, ties).
+ *   [P2] SGLang PR #38944, "[DSV4.1] Enable the two-level candidate
+ *        indexer": the SM90 prefill commit (block-scaled E2M1 index-K).
  *   [P3] vLLM PR #52696, "[Performance][MLA] Use FP16 logits for sparse
  *        indexer": "Summary" and commits (selection on FP16 score keys,
- *        refining only the remaining key bits).
+ *        refining only the remaining key bits; FP16 logits; the MXFP4
+ *        indexer cache's packed 68-byte layout).
  *
  * Conventions for every entry point:
  *   - Pointers marked (device) are device memory on the current HIP device;
@@ -194,6 +197,28 @@ idx_status indexer_logits_f16(const uint8_t* q, const uint8_t* kv_pages,
                               int32_t B, int32_t next_n, int32_t num_pages,
                               int32_t max_pages, uint16_t* logits, int64_t logits_stride,
                               int32_t* hist, void* stream);
+
+/*
+ * indexer_logits_mxfp4 -- indexer_logits with MXFP4 keys: block-scaled E2M1
+ * index-K ([P2] SGLang PR #38944, the SM90 prefill commit) in the packed
+ * 68-byte token layout of the MXFP4 indexer cache ([P3] vLLM PR #52696),
+ * the fp8 x fp4 variant that [P1] "What this adds" names.  Per token: bytes 0..63 hold the 128 E2M1
+ * codes (dimension 2i in the low nibble of byte i, 2i+1 in the high nibble),
+ * bytes 64..67 the E8M0 scales of dimensions 0-31, 32-63, 64-95, 96-127.
+ * The key is code value * 2^(scale - 127); there is no per-token fp32 scale:
+ *   logit[r, s] = sum_h w[r, h] * ReLU(q[r, h, :] . k_s).
+ * Q stays E4M3.  The histogram (optional) is the same as for indexer_logits
+ * ([P1] supports it for FP8 only; here the same fused code serves both).
+ *
+ * kv_pages      (device) uint8 [num_pages][64][68], 16-B aligned
+ * logits        (device) float [B*next_n][logits_stride], stride % 4 == 0
+ * other arguments as for indexer_logits (no k_scales)
+ */
+idx_status indexer_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages,
+                                const float* weights, const int32_t* block_table,
+                                const int32_t* context_lens, int32_t B, int32_t next_n,
+                                int32_t num_pages, int32_t max_pages, float* logits,
+                                int64_t logits_stride, int32_t* hist, void* stream);
 
 /*
  * topk_rows_f16 -- topk_rows over binary16 scores ([P3] "Summary": selection

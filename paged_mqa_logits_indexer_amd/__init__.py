@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
   indexer_logits(q, kv_pages, k_scales, weights, block_table, context_lens,
                  next_n, logits, hist=None, events=None)        float32 logits
   indexer_logits_f16(... same ..., logits, hist=None, events=None) float16 logits
+  indexer_logits_mxfp4(q, kv_pages, weights, block_table, context_lens, next_n,
+                       logits, hist=None, events=None)  packed MXFP4 K, float32 logits
   topk_workspace_bytes(rows, logits_stride, k)
   topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None,
             events=None)                                          float32 scores
@@ -36,6 +38,7 @@ import torch
 __all__ = [
     "IndexerError", "KEY_FP32", "KEY_FP16", "NUM_BINS", "CANDIDATE_CAPACITY",
     "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits", "indexer_logits_f16",
+    "indexer_logits_mxfp4",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram", "indexer_status_str",
     "indexer_time_next_call", "hbm_read_probe",
 ]
@@ -47,8 +50,9 @@ CANDIDATE_CAPACITY = 8192
 HEADS = 32
 HEAD_DIM = 128
 PAGE_TOKENS = 64
+MXFP4_TOKEN_BYTES = 68
 
-EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "topk_workspace_bytes", "topk_rows",
+EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp4", "topk_workspace_bytes", "topk_rows",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
                     "indexer_time_next_call", "hbm_read_probe")
 
@@ -95,6 +99,8 @@ def load_library() -> ctypes.CDLL:
     lib.hbm_read_probe.restype = ctypes.c_int
     lib.indexer_logits_f16.argtypes = lib.indexer_logits.argtypes
     lib.indexer_logits_f16.restype = ctypes.c_int
+    lib.indexer_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp]
+    lib.indexer_logits_mxfp4.restype = ctypes.c_int
     lib.topk_rows_f16.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.topk_rows_f16.restype = ctypes.c_int
     lib.indexer_time_next_call.argtypes = [vp, vp]
@@ -166,10 +172,13 @@ def _arm(events, device) -> None:
 
 def _logits_call(name, dtype, q, kv_pages, k_scales, weights, block_table, context_lens, next_n,
                  logits, hist, events):
+    """k_scales None: MXFP4 pages [P, 64, 68] (indexer_logits_mxfp4)."""
     dev = q.device
+    mx = k_scales is None
     _need(q, "q", torch.uint8, dev, 3)
     _need(kv_pages, "kv_pages", torch.uint8, dev, 3)
-    _need(k_scales, "k_scales", torch.float32, dev, 2)
+    if not mx:
+        _need(k_scales, "k_scales", torch.float32, dev, 2)
     _need(weights, "weights", torch.float32, dev, 2)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(context_lens, "context_lens", torch.int32, dev, 1)
@@ -179,9 +188,10 @@ def _logits_call(name, dtype, q, kv_pages, k_scales, weights, block_table, conte
     if tuple(q.shape) != (rows, HEADS, HEAD_DIM) or not q.is_contiguous():
         raise ValueError(f"q must be contiguous [{rows}, 32, 128]")
     P = kv_pages.shape[0]
-    if tuple(kv_pages.shape) != (P, PAGE_TOKENS, HEAD_DIM) or not kv_pages.is_contiguous():
-        raise ValueError("kv_pages must be contiguous [P, 64, 128]")
-    if tuple(k_scales.shape) != (P, PAGE_TOKENS) or not k_scales.is_contiguous():
+    tok = MXFP4_TOKEN_BYTES if mx else HEAD_DIM
+    if tuple(kv_pages.shape) != (P, PAGE_TOKENS, tok) or not kv_pages.is_contiguous():
+        raise ValueError(f"kv_pages must be contiguous [P, 64, {tok}]")
+    if not mx and (tuple(k_scales.shape) != (P, PAGE_TOKENS) or not k_scales.is_contiguous()):
         raise ValueError("k_scales must be contiguous [P, 64]")
     if tuple(weights.shape) != (rows, HEADS) or not weights.is_contiguous():
         raise ValueError(f"weights must be contiguous [{rows}, 32]")
@@ -198,10 +208,12 @@ def _logits_call(name, dtype, q, kv_pages, k_scales, weights, block_table, conte
     lib = load_library()
     with torch.cuda.device(dev):
         _arm(events, dev)
-        st = getattr(lib, name)(
-            _ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(block_table),
-            _ptr(context_lens), int(B), int(next_n), int(P), int(max_pages), _ptr(logits),
-            int(logits.stride(0)), _ptr(hist), _stream_ptr(dev))
+        tail = (_ptr(weights), _ptr(block_table), _ptr(context_lens), int(B), int(next_n), int(P),
+                int(max_pages), _ptr(logits), int(logits.stride(0)), _ptr(hist), _stream_ptr(dev))
+        if mx:
+            st = getattr(lib, name)(_ptr(q), _ptr(kv_pages), *tail)
+        else:
+            st = getattr(lib, name)(_ptr(q), _ptr(kv_pages), _ptr(k_scales), *tail)
     _check(name, st)
 
 
@@ -223,6 +235,14 @@ def indexer_logits_f16(q, kv_pages, k_scales, weights, block_table, context_lens
                        logits, hist=None, events=None):
     """indexer_logits writing float16 logits [B*next_n, stride] (stride % 8 == 0)."""
     _logits_call("indexer_logits_f16", torch.float16, q, kv_pages, k_scales, weights, block_table,
+                 context_lens, next_n, logits, hist, events)
+
+
+def indexer_logits_mxfp4(q, kv_pages, weights, block_table, context_lens, next_n, logits,
+                         hist=None, events=None):
+    """indexer_logits with packed MXFP4 keys: kv_pages [P, 64, 68] uint8 (64 bytes
+    of E2M1 codes, then four E8M0 block scales per token); float32 logits."""
+    _logits_call("indexer_logits_mxfp4", torch.float32, q, kv_pages, None, weights, block_table,
                  context_lens, next_n, logits, hist, events)
 
 

@@ -22,9 +22,9 @@ pmqa::LaunchEvents take_events() {
 idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
                        const float* weights, const int32_t* block_table, const int32_t* context_lens,
                        int32_t B, int32_t next_n, int32_t num_pages, int32_t max_pages, void* logits,
-                       int64_t logits_stride, bool f16, int32_t* hist, void* stream) {
+                       int64_t logits_stride, bool f16, bool mxfp4, int32_t* hist, void* stream) {
   const pmqa::LaunchEvents ev = take_events();
-  if (!q || !kv_pages || !k_scales || !weights || !block_table || !context_lens || !logits)
+  if (!q || !kv_pages || (!mxfp4 && !k_scales) || !weights || !block_table || !context_lens || !logits)
     return IDX_EINVAL;
   if (B <= 0 || num_pages <= 0 || max_pages <= 0 || logits_stride <= 0) return IDX_EINVAL;
   if (next_n < 1 || next_n > 4) return IDX_EUNSUPPORTED;
@@ -33,7 +33,7 @@ idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k
   if (static_cast<int64_t>(B) * max_pages > INT32_MAX) return IDX_EUNSUPPORTED;
   // Rows are written with 16-byte stores: the stride is a multiple of 16 bytes.
   const int64_t per16 = f16 ? 8 : 4;
-  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(weights, 16) || !aligned(k_scales, 4) ||
+  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(weights, 16) || (!mxfp4 && !aligned(k_scales, 4)) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(logits, 16) ||
       (logits_stride % per16) != 0 || (hist && !aligned(hist, 8)))
     return IDX_EALIGN;
@@ -48,6 +48,7 @@ idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k
   a.hist = hist;
   a.logits_stride = logits_stride;
   a.logits_f16 = f16 ? 1 : 0;
+  a.k_mxfp4 = mxfp4 ? 1 : 0;
   a.B = B;
   a.next_n = next_n;
   a.num_pages = num_pages;
@@ -110,7 +111,7 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages, const float
                           int32_t num_pages, int32_t max_pages, float* logits,
                           int64_t logits_stride, int32_t* hist, void* stream) {
   return logits_call(q, kv_pages, k_scales, weights, block_table, context_lens, B, next_n, num_pages,
-                     max_pages, logits, logits_stride, false, hist, stream);
+                     max_pages, logits, logits_stride, false, false, hist, stream);
 }
 
 idx_status indexer_logits_f16(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
@@ -119,7 +120,15 @@ idx_status indexer_logits_f16(const uint8_t* q, const uint8_t* kv_pages, const f
                               int32_t num_pages, int32_t max_pages, uint16_t* logits,
                               int64_t logits_stride, int32_t* hist, void* stream) {
   return logits_call(q, kv_pages, k_scales, weights, block_table, context_lens, B, next_n, num_pages,
-                     max_pages, logits, logits_stride, true, hist, stream);
+                     max_pages, logits, logits_stride, true, false, hist, stream);
+}
+
+idx_status indexer_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages, const float* weights,
+                                const int32_t* block_table, const int32_t* context_lens, int32_t B,
+                                int32_t next_n, int32_t num_pages, int32_t max_pages, float* logits,
+                                int64_t logits_stride, int32_t* hist, void* stream) {
+  return logits_call(q, kv_pages, nullptr, weights, block_table, context_lens, B, next_n, num_pages,
+                     max_pages, logits, logits_stride, false, true, hist, stream);
 }
 
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {

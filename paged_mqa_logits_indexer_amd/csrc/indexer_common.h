@@ -154,8 +154,8 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipSt
 
 struct LogitsArgs {
   const uint8_t* q;
-  const uint8_t* kv_pages;
-  const float* k_scales;
+  const uint8_t* kv_pages;  // FP8 codes [pages][64][128], or packed MXFP4 tokens [pages][64][68]
+  const float* k_scales;    // FP8 only
   const float* weights;
   const int32_t* block_table;
   const int32_t* context_lens;
@@ -163,6 +163,7 @@ struct LogitsArgs {
   int32_t* hist;
   int64_t logits_stride;
   int32_t logits_f16;
+  int32_t k_mxfp4;   // K pages are packed MXFP4 tokens (float32 logits only)
   int32_t B;
   int32_t next_n;
   int32_t num_pages;

@@ -78,9 +78,27 @@ using StageT = typename std::conditional<F16, uint16_t, float>::type;
 template <int NN>
 constexpr int kThreadsOf = kWavesOf<NN> * kWave;
 
-struct PageRegs {
+// K page formats: FP8 E4M3 codes with a per-token fp32 scale (two arrays),
+// or MXFP4 tokens -- 64 bytes of E2M1 codes (dimension 2i in the low nibble
+// of byte i) and four E8M0 scale bytes, one per 32 dimensions, packed into 68
+// bytes (SGLang PR #38944, block-scaled E2M1 index-K; vLLM PR #52696, the
+// packed 68-byte cache layout).
+constexpr int kKFp8 = 0;
+constexpr int kKMxfp4 = 1;
+constexpr int kMxTokenBytes = 68;
+constexpr int kMxPageBytes = kPage * kMxTokenBytes;  // 4352
+
+template <int KF>
+struct PageRegs;
+template <>
+struct PageRegs<kKFp8> {
   i32x4 v[8];   // [key block kb][half]: K bytes in MFMA operand layout
   float scale;  // k_scales of key `lane` of the page
+};
+template <>
+struct PageRegs<kKMxfp4> {
+  i32x4 v[4];   // [key block kb]: 32 E2M1 codes of key n, dimensions 32g .. 32g+31
+  int sc[4];    // [key block kb]: the key's four E8M0 scale bytes
 };
 
 // ReLU as one integer max on the bit pattern: a set sign bit makes the int32
@@ -115,7 +133,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, u
 // outstanding load's destination would force a wait for all loads).
 __device__ __forceinline__ void load_page(const uint8_t* __restrict__ kv_pages,
                                           const float* __restrict__ k_scales,
-                                          int page, int lane_off, int lane, PageRegs& r) {
+                                          int page, int lane_off, int lane, PageRegs<kKFp8>& r) {
   const __amdgpu_buffer_rsrc_t kr = range_rsrc(kv_pages + static_cast<int64_t>(page) * kPageBytes, kPageBytes);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -124,6 +142,25 @@ __device__ __forceinline__ void load_page(const uint8_t* __restrict__ kv_pages,
   }
   const __amdgpu_buffer_rsrc_t sr = range_rsrc(k_scales + static_cast<int64_t>(page) * kPage, kPage * 4);
   r.scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, 0, 0));
+}
+
+// One page of MXFP4 K.  For the fp8 x fp4 MFMA (16x16x128) lane (n, g) of
+// the fp4 operand holds dimensions 32g .. 32g+31 of key n, element i in
+// nibble i, and the E8M0 scale that lane passes covers those 32 dimensions
+// (checked on the device with single-element operands); the fp8 Q operand
+// keeps its layout.  So lane (n, g) reads bytes [16g, 16g+16) of token
+// 16 kb + n -- one 16-byte load at a 4-byte-aligned offset -- and the token's
+// scale word.  lane_off = 68 n + 16 g.
+__device__ __forceinline__ void load_page(const uint8_t* __restrict__ kv_pages,
+                                          const float* __restrict__ /*k_scales*/,
+                                          int page, int lane_off, int lane, PageRegs<kKMxfp4>& r) {
+  const __amdgpu_buffer_rsrc_t kr = range_rsrc(kv_pages + static_cast<int64_t>(page) * kMxPageBytes, kMxPageBytes);
+  const int scale_off = (lane & 15) * kMxTokenBytes + 64;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    r.v[kb] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + kb * 16 * kMxTokenBytes, 0, 0));
+    r.sc[kb] = __builtin_amdgcn_raw_buffer_load_b32(kr, scale_off + kb * 16 * kMxTokenBytes, 0, 0);
+  }
 }
 
 // Sum over the four lane groups g of part[kb], leaving lane (n, g) with the
@@ -157,8 +194,8 @@ struct RequestRegs {
 // global store issued between this page and the next one's prefetch would
 // have to complete before that page counts as arrived: the vector-memory
 // counter covers loads and stores in issue order.
-template <int NN, bool HIST, bool F16>
-__device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi, int ppw,
+template <int NN, bool HIST, bool F16, int KF>
+__device__ __forceinline__ void compute_page(const PageRegs<KF>& pr, int lp, int lpi, int ppw,
                                              int lane, const RequestRegs<NN>& rq,
                                              StageT<F16>* s_out, int* s_hist) {
   const int key = lp * kPage + lane;
@@ -167,12 +204,20 @@ __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi
     f32x4 acc[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const i32x8 b = cat8(pr.v[2 * kb], pr.v[2 * kb + 1]);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const i32x8 a = cat8(rq.q[j][mb][0], rq.q[j][mb][1]);
-        acc[kb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        if constexpr (KF == kKFp8) {
+          const i32x8 b = cat8(pr.v[2 * kb], pr.v[2 * kb + 1]);
+          acc[kb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        } else {
+          // B in E2M1 (format 4): only its first four registers are read.
+          const i32x8 b = cat8(pr.v[kb], i32x4{0, 0, 0, 0});
+          const int scale = (pr.sc[kb] >> (8 * (lane >> 4))) & 0xFF;
+          acc[kb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, scale);
+        }
       }
     }
     float part[4];
@@ -186,7 +231,9 @@ __device__ __forceinline__ void compute_page(const PageRegs& pr, int lp, int lpi
       }
       part[kb] = s;
     }
-    const float logit = as_stored(reduce_scatter4(part) * pr.scale);
+    float head_sum = reduce_scatter4(part);
+    if constexpr (KF == kKFp8) head_sum *= pr.scale;  // MXFP4 scales are in the products
+    const float logit = as_stored(head_sum);
     uint32_t hb = 0u;
     if constexpr (HIST || F16) hb = f16_bits_rn(logit);
     if constexpr (F16) s_out[(j * ppw + lpi) * kPage + lane] = static_cast<uint16_t>(hb);
@@ -205,7 +252,7 @@ template <int NN>
 constexpr int kWavesPerSimd = NN == 1 ? (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 3 : 2))
                                       : (NN == 2 && kPrefetch == 1 ? 3 : 2);
 
-template <int NN, bool HIST, bool F16>
+template <int NN, bool HIST, bool F16, int KF>
 __global__ __launch_bounds__(kThreadsOf<NN>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
 void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   __shared__ int s_hist[HIST ? NN * kBins : 1];
@@ -297,8 +344,8 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   // it+1 .. it+kPrefetch are in flight.  Past the last page the last one is
   // issued again (it is cached), which keeps every load unconditional; a wave
   // without pages issues its first prefetch all the same.
-  const int lane_off = (lane & 15) * kDim + (lane >> 4) * 16;  // key n, group g
-  PageRegs buf[kRing];
+  const int lane_off = (lane & 15) * (KF == kKFp8 ? kDim : kMxTokenBytes) + (lane >> 4) * 16;  // key n, group g
+  PageRegs<KF> buf[kRing];
   const int n_last = max(n_mine, 1) - 1;
   auto prefetch = [&]() {
 #pragma unroll
@@ -355,7 +402,7 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
         if (it >= n_mine) break;
         const int nx = it + kPrefetch < n_mine ? it + kPrefetch : n_mine - 1;
         load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[(s + kPrefetch) % kRing]);
-        compute_page<NN, HIST, F16>(buf[s], p0 + lpi0 + it * kWaves, lpi0 + it * kWaves,
+        compute_page<NN, HIST, F16, KF>(buf[s], p0 + lpi0 + it * kWaves, lpi0 + it * kWaves,
                                     pages_per_wg, lane, rq, s_out, s_hist);
       }
     }
@@ -405,11 +452,19 @@ DeviceInfo* device_info(int dev) {
   return &infos[dev];
 }
 
-template <int NN, bool HIST, bool F16>
+template <int NN, bool HIST, bool F16, int KF>
 hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
-  launch_kernel(indexer_logits_kernel<NN, HIST, F16>, grid, dim3(kThreadsOf<NN>), stream, ev.start, ev.stop, a,
+  launch_kernel(indexer_logits_kernel<NN, HIST, F16, KF>, grid, dim3(kThreadsOf<NN>), stream, ev.start, ev.stop, a,
                 pages_per_wg);
   return hipGetLastError();
+}
+
+// MXFP4 K is served with float32 logits only.
+template <int NN, bool HIST>
+hipError_t launch_fmt(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
+  if (a.k_mxfp4) return launch<NN, HIST, false, kKMxfp4>(a, grid, pages_per_wg, stream, ev);
+  if (a.logits_f16) return launch<NN, HIST, true, kKFp8>(a, grid, pages_per_wg, stream, ev);
+  return launch<NN, HIST, false, kKFp8>(a, grid, pages_per_wg, stream, ev);
 }
 
 }  // namespace
@@ -440,23 +495,16 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   if (chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
   const int p = static_cast<int>(ppw);
-  switch ((a.next_n * 2 + (hist ? 1 : 0)) * 2 + (a.logits_f16 ? 1 : 0)) {
-    case 4: return launch<1, false, false>(a, grid, p, stream, ev);
-    case 5: return launch<1, false, true>(a, grid, p, stream, ev);
-    case 6: return launch<1, true, false>(a, grid, p, stream, ev);
-    case 7: return launch<1, true, true>(a, grid, p, stream, ev);
-    case 8: return launch<2, false, false>(a, grid, p, stream, ev);
-    case 9: return launch<2, false, true>(a, grid, p, stream, ev);
-    case 10: return launch<2, true, false>(a, grid, p, stream, ev);
-    case 11: return launch<2, true, true>(a, grid, p, stream, ev);
-    case 12: return launch<3, false, false>(a, grid, p, stream, ev);
-    case 13: return launch<3, false, true>(a, grid, p, stream, ev);
-    case 14: return launch<3, true, false>(a, grid, p, stream, ev);
-    case 15: return launch<3, true, true>(a, grid, p, stream, ev);
-    case 16: return launch<4, false, false>(a, grid, p, stream, ev);
-    case 17: return launch<4, false, true>(a, grid, p, stream, ev);
-    case 18: return launch<4, true, false>(a, grid, p, stream, ev);
-    case 19: return launch<4, true, true>(a, grid, p, stream, ev);
+  if (a.k_mxfp4 && a.logits_f16) return hipErrorInvalidValue;
+  switch (a.next_n * 2 + (hist ? 1 : 0)) {
+    case 2: return launch_fmt<1, false>(a, grid, p, stream, ev);
+    case 3: return launch_fmt<1, true>(a, grid, p, stream, ev);
+    case 4: return launch_fmt<2, false>(a, grid, p, stream, ev);
+    case 5: return launch_fmt<2, true>(a, grid, p, stream, ev);
+    case 6: return launch_fmt<3, false>(a, grid, p, stream, ev);
+    case 7: return launch_fmt<3, true>(a, grid, p, stream, ev);
+    case 8: return launch_fmt<4, false>(a, grid, p, stream, ev);
+    case 9: return launch_fmt<4, true>(a, grid, p, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }

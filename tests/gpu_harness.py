@@ -28,7 +28,8 @@ class DevInputs:
         self.device = device
         self.q = torch.from_numpy(np.ascontiguousarray(x.q)).to(device)
         self.kv = torch.from_numpy(np.ascontiguousarray(x.kv_pages)).to(device)
-        self.sc = torch.from_numpy(np.ascontiguousarray(x.k_scales)).to(device)
+        # MXFP4 pages ([P, 64, 68] packed tokens) carry their scales inside
+        self.sc = None if x.k_scales is None else torch.from_numpy(np.ascontiguousarray(x.k_scales)).to(device)
         self.w = torch.from_numpy(np.ascontiguousarray(x.weights)).to(device)
         self.bt = torch.from_numpy(np.ascontiguousarray(x.block_table)).to(device)
         self.lens = torch.from_numpy(np.ascontiguousarray(x.context_lens)).to(device)
@@ -41,6 +42,10 @@ class DevInputs:
         return torch.zeros((self.x.rows, 1024), dtype=torch.int32, device=self.device)
 
     def logits(self, logits, hist=None):
+        if self.sc is None:
+            pmqa.indexer_logits_mxfp4(self.q, self.kv, self.w, self.bt, self.lens,
+                                      self.x.next_n, logits, hist)
+            return
         pmqa.indexer_logits(self.q, self.kv, self.sc, self.w, self.bt, self.lens,
                             self.x.next_n, logits, hist)
 

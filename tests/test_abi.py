@@ -201,3 +201,28 @@ def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 32, 128, dtype=torch.uint8)
     with pytest.raises((ValueError, TypeError)):
         pmqa.indexer_logits(q, q, q, q, q, q, 1, q)
+
+
+def mxfp4_call(lib, **kw):
+    args = dict(q=A, kv=A, w=A, bt=A, lens=A, B=8, next_n=1, num_pages=16, max_pages=4,
+                logits=A, stride=256, hist=None, stream=None)
+    args.update(kw)
+    return lib.indexer_logits_mxfp4(args["q"], args["kv"], args["w"], args["bt"], args["lens"],
+                                    args["B"], args["next_n"], args["num_pages"],
+                                    args["max_pages"], args["logits"], args["stride"],
+                                    args["hist"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), IDX_EINVAL),
+    (dict(kv=None), IDX_EINVAL),
+    (dict(logits=None), IDX_EINVAL),
+    (dict(next_n=5), IDX_EUNSUPPORTED),
+    (dict(B=0), IDX_EINVAL),
+    (dict(kv=A + 4), IDX_EALIGN),
+    (dict(stride=254), IDX_EALIGN),
+    (dict(hist=A + 4), IDX_EALIGN),
+])
+def test_mxfp4_logits_rejects_before_launch(lib, kw, status):
+    # no k_scales argument: the scales travel inside the 68-byte tokens
+    assert mxfp4_call(lib, **kw) == status
