@@ -11,3 +11,4 @@ from .indexer_oracle import (  # noqa: F401
     e4m3fn_decode_table, fp16_rne, head_sum_at, indexer_logits,
     indexer_logits_at, logits_error_bound_at, score_keys, topk_row, topk_rows,
 )
+from . import candidates  # noqa: F401,E402

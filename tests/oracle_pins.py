@@ -16,7 +16,10 @@ What the pins lean on, none of which is the oracle's own code:
     adds" bin definition; vLLM PR #52696 FP16 keys);
   * closed-form bin populations over all 65,536 FP16 encodings;
   * histogram invariants (total = live non-NaN count; additivity; padding);
-  * brute-force top-k with Python's sorted() and an explicit comparator.
+  * brute-force top-k with Python's sorted() and an explicit comparator;
+  * for the candidate indexer: explicit loops for the block maxima, sorted()
+    and the page transform per block, and the dense logits at the listed
+    positions.
 """
 
 from __future__ import annotations
@@ -661,8 +664,123 @@ def pin_mxfp4_exact(O, n_cols=4):
     return fails
 
 
+# ------------------------------------------------- candidate indexer --
+def pin_block_amax8(O, seed=61):
+    """Brute force with explicit comparisons: live scores only, NaN skipped,
+    the newest block +inf, nothing past ceil(len / 8)."""
+    fails = []
+    rng = np.random.default_rng(seed)
+    rows, width = 6, 70
+    sc = rng.standard_normal((rows, width)).astype(np.float32)
+    sc[rng.random((rows, width)) < 0.1] = np.nan
+    sc[0, 3] = np.inf
+    sc[1, 8:16] = np.nan          # a block of NaNs only
+    sc[2, 10] = -np.inf
+    lens = np.array([70, 23, 8, 1, 0, 57])
+    got = O.candidates.block_amax8(sc, lens)
+    for r in range(rows):
+        n = int(lens[r])
+        nb = -(-n // 8)
+        for j in range(got.shape[1]):
+            if j >= nb:
+                if not np.isnan(got[r, j]):
+                    fails.append(f"amax8[{r},{j}] written past the count")
+                continue
+            if j == nb - 1:
+                want = np.float32(np.inf)
+            else:
+                best = None
+                for i in range(8 * j, min(n, 8 * j + 8)):
+                    v = float(sc[r, i])
+                    if v != v:
+                        continue
+                    if best is None or v > best:
+                        best = v
+                want = np.float32(np.nan if best is None else best)
+            g = got[r, j]
+            if not ((np.isnan(want) and np.isnan(g)) or g == want):
+                fails.append(f"amax8[{r},{j}] = {g}, want {want}")
+    return fails
+
+
+def pin_sort_candidate_blocks(O, seed=63):
+    """Python sorted() and the page transform written out per block."""
+    import gen
+    fails = []
+    rng = np.random.default_rng(seed)
+    # rows of the last request have at most kb blocks: the identity table,
+    # whatever subset the input lists
+    x = gen.make_indexer_inputs("blk", 3, 2, [700, 900, 60], 7)
+    rows, kb = x.rows, 12
+    n_blocks = -(-x.context_lens.astype(np.int64) // 8)
+    blocks = np.full((rows, kb), -1, dtype=np.int32)
+    for r in range(rows):
+        pick = rng.choice(int(n_blocks[r]), size=min(kb - r % 3, int(n_blocks[r]) - 2), replace=False)
+        blocks[r, :len(pick)] = pick
+    table, slots = O.candidates.sort_candidate_blocks(blocks, n_blocks, x.block_table, x.next_n)
+    big = 2 ** 31 - 1
+    for r in range(rows):
+        if n_blocks[r] <= kb:
+            ids = list(range(int(n_blocks[r])))
+        else:
+            ids = sorted(int(b) for b in blocks[r] if b >= 0)
+        want_t = ids + [big] * (kb - len(ids))
+        want_s = []
+        for b in ids:
+            page = int(x.block_table[r // x.next_n, (b * 8) // 64])
+            want_s.append(page * 8 + b % 8)
+        want_s += [big] * (kb - len(ids))
+        if table[r].tolist() != want_t:
+            fails.append(f"row {r}: table {table[r].tolist()} want {want_t}")
+        if slots[r].tolist() != want_s:
+            fails.append(f"row {r}: slots {slots[r].tolist()} want {want_s}")
+    return fails
+
+
+def pin_sparse_logits(O, seed=65):
+    """Sparse logits are the dense logits at the listed blocks' live keys, in
+    table order; sparse_to_logical and sparse_row_lens agree."""
+    import gen
+    fails = []
+    rng = np.random.default_rng(seed)
+    x = gen.make_indexer_inputs("sp", 2, 2, [300, 451], 9)
+    dense = O.indexer_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                             x.context_lens, x.next_n, x.logits_stride)
+    kb = 9
+    big = 2 ** 31 - 1
+    table = np.full((x.rows, kb), big, dtype=np.int32)
+    for r in range(x.rows):
+        nb = -(-int(x.context_lens[r]) // 8)
+        ids = np.sort(rng.choice(nb - 1, size=kb - 1 - r % 2, replace=False))
+        ids = np.concatenate([ids, [nb - 1]])  # the newest block, partly live
+        table[r, :len(ids)] = ids
+    got = O.candidates.sparse_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                                     table, x.context_lens, x.next_n)
+    lens = O.candidates.sparse_row_lens(table, x.context_lens)
+    for r in range(x.rows):
+        col = 0
+        for i in range(kb):
+            b = int(table[r, i])
+            for t in range(8):
+                c = 8 * i + t
+                key = 8 * b + t
+                live = b != big and key < int(x.context_lens[r])
+                if live:
+                    if got[r, c] != dense[r, key]:
+                        fails.append(f"sparse[{r},{c}] != dense[{r},{key}]")
+                    if int(O.candidates.sparse_to_logical(table[r:r + 1], np.array([[c]]))[0, 0]) != key:
+                        fails.append(f"sparse column {c} of row {r} maps elsewhere")
+                    col += 1
+                elif not np.isnan(got[r, c]):
+                    fails.append(f"sparse[{r},{c}] written though not live")
+        if int(lens[r]) != col:
+            fails.append(f"row {r}: sparse length {int(lens[r])}, live {col}")
+    return fails
+
+
 ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_logits_f16_check, pin_bins_golden, pin_bins_exhaustive,
             pin_keys, pin_bins_coarsen_keys, pin_histogram, pin_topk,
             pin_topk_invariants, pin_logits_exact, pin_logits_library,
             pin_logits_paging, pin_error_bound, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
-            pin_mxfp4_matches_fp8_path, pin_mxfp4_exact)
+            pin_mxfp4_matches_fp8_path, pin_mxfp4_exact, pin_block_amax8,
+            pin_sort_candidate_blocks, pin_sparse_logits)

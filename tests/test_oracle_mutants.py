@@ -2,6 +2,7 @@
 and require the pins to catch it, so that passing pins mean something."""
 import importlib.util
 import math
+import os
 
 import numpy as np
 import pytest
@@ -14,6 +15,13 @@ def fresh_oracle():
     spec = importlib.util.spec_from_file_location("oracle_mutant", base.__file__)
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
+    # a fresh copy of the candidate-indexer oracle too (inside the package, so
+    # its relative import of the logits oracle resolves)
+    cspec = importlib.util.spec_from_file_location(
+        "oracle.candidates_mutant", os.path.join(os.path.dirname(base.__file__), "candidates.py"))
+    cmod = importlib.util.module_from_spec(cspec)
+    cspec.loader.exec_module(cmod)
+    mod.candidates = cmod
     return mod
 
 
@@ -232,6 +240,59 @@ def m_e8m0_bias_128(O):
                                        np.ldexp(1.0, np.asarray(c, np.int64) - 128))
 
 
+def m_amax8_block_count(O):
+    # floor(len / 8) + 1 blocks: one too many when len is a multiple of 8
+    orig = O.candidates.block_amax8
+
+    def amax(sc, lens, fill=np.nan):
+        lens = np.asarray(lens, np.int64)
+        sc = np.asarray(sc, np.float32)
+        wide = np.full((sc.shape[0], sc.shape[1] + 8), np.nan, np.float32)
+        wide[:, :sc.shape[1]] = sc
+        out = orig(wide, np.where(lens % 8 == 0, lens + 1, lens), fill)
+        return out[:, :max(out.shape[1], 1)]
+    O.candidates.block_amax8 = amax
+
+
+def m_amax8_newest_not_inf(O):
+    def amax(sc, lens, fill=np.nan):
+        sc = np.asarray(sc, np.float32)
+        lens = np.asarray(lens, np.int64)
+        nb = -(-lens // 8)
+        out = np.full((sc.shape[0], max(int(nb.max()), 1)), fill, np.float32)
+        for r in range(sc.shape[0]):
+            for j in range(int(nb[r])):
+                with np.errstate(invalid="ignore"):
+                    out[r, j] = np.fmax.reduce(sc[r, 8 * j:min(int(lens[r]), 8 * j + 8)])
+        return out
+    O.candidates.block_amax8 = amax
+
+
+def m_sort_no_identity(O):
+    orig = O.candidates.sort_candidate_blocks
+    O.candidates.sort_candidate_blocks = lambda b, n, bt, nn: orig(
+        b, np.full(len(n), 1 << 30), bt, nn)
+
+
+def m_sort_slot_transform(O):
+    orig = O.candidates.sort_candidate_blocks
+
+    def sort(b, n, bt, nn):
+        t, s = orig(b, n, bt, nn)
+        s = np.where(t != 2 ** 31 - 1, s - (t % 8) + (t // 8) % 8, s).astype(np.int32)
+        return t, s
+    O.candidates.sort_candidate_blocks = sort
+
+
+def m_sparse_block_offset(O):
+    def sp(q, kv, ks, w, bt, table, lens, nn, fill=np.nan):
+        t = np.asarray(table, np.int64)
+        t = np.where(t != 2 ** 31 - 1, t + 1, t)
+        return orig(q, kv, ks, w, bt, t, lens, nn, fill)
+    orig = O.candidates.sparse_logits
+    O.candidates.sparse_logits = sp
+
+
 MUTANTS = [
     (m_e4m3_bias, [P.pin_e4m3]),
     (m_e4m3_subnormal, [P.pin_e4m3]),
@@ -258,6 +319,11 @@ MUTANTS = [
     (m_mxfp4_scale_blocks_reversed, [P.pin_mxfp4_layout, P.pin_mxfp4_exact]),
     (m_mxfp4_scale_ignored, [P.pin_mxfp4_layout, P.pin_mxfp4_matches_fp8_path]),
     (m_e8m0_bias_128, [P.pin_e8m0, P.pin_mxfp4_exact]),
+    (m_amax8_block_count, [P.pin_block_amax8]),
+    (m_amax8_newest_not_inf, [P.pin_block_amax8]),
+    (m_sort_no_identity, [P.pin_sort_candidate_blocks]),
+    (m_sort_slot_transform, [P.pin_sort_candidate_blocks]),
+    (m_sparse_block_offset, [P.pin_sparse_logits]),
 ]
 
 
