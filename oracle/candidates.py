@@ -29,7 +29,9 @@ and the consumer side is
 * ``sparse_to_logical``      -- sparse column -> logical key position.
 
 Readings taken where the page is silent: scores that are NaN are ignored by
-the block maximum (NaN only when every live score of the block is NaN);
+the block maximum (NaN only when every live score of the block is NaN); the
+sort drops ids outside [0, ceil(len / 8)) and repeats (a block is listed
+once);
 block b covers keys 8b .. 8b+7, only keys below the row length are live; the
 pool slot of logical key s is page * 64 + s % 64 with page the row's block
 table entry s // 64, so block b's slot / 8 is page * 8 + b % 8; the sparse
@@ -82,7 +84,8 @@ def sort_candidate_blocks(blocks, n_blocks, block_table, next_n):
         if n <= kb:
             ids = np.arange(n)
         else:
-            ids = np.unique(blocks[r][blocks[r] >= 0])
+            b = blocks[r]
+            ids = np.unique(b[(b >= 0) & (b < n)])
         table[r, :len(ids)] = ids
         pages = np.asarray(block_table[r // next_n], dtype=np.int64)[(ids * BLOCK) // PAGE_SIZE]
         slots[r, :len(ids)] = (pages * PAGE_SIZE + (ids * BLOCK) % PAGE_SIZE) // BLOCK

@@ -717,13 +717,16 @@ def pin_sort_candidate_blocks(O, seed=63):
     for r in range(rows):
         pick = rng.choice(int(n_blocks[r]), size=min(kb - r % 3, int(n_blocks[r]) - 2), replace=False)
         blocks[r, :len(pick)] = pick
+        if r % 2 and len(pick) > 3:  # a repeat and an id past the row: both dropped
+            blocks[r, 1] = blocks[r, 0]
+            blocks[r, 2] = int(n_blocks[r]) + 3
     table, slots = O.candidates.sort_candidate_blocks(blocks, n_blocks, x.block_table, x.next_n)
     big = 2 ** 31 - 1
     for r in range(rows):
         if n_blocks[r] <= kb:
             ids = list(range(int(n_blocks[r])))
         else:
-            ids = sorted(int(b) for b in blocks[r] if b >= 0)
+            ids = sorted(set(int(b) for b in blocks[r] if 0 <= b < int(n_blocks[r])))
         want_t = ids + [big] * (kb - len(ids))
         want_s = []
         for b in ids:
