@@ -15,7 +15,9 @@
  *        "Replace the CuTe DSL selector with a JIT CUDA selector; add verify"
  *        (exact top-2048 selector from the histogram, fallback, ties).
  *   [P2] SGLang PR #38944, "[DSV4.1] Enable the two-level candidate
- *        indexer": the SM90 prefill commit (block-scaled E2M1 index-K).
+ *        indexer": the sparse paged logits path, amax8_varlen and
+ *        sort_candidate_blocks; the SM90 prefill commit (block-scaled E2M1
+ *        index-K).
  *   [P3] vLLM PR #52696, "[Performance][MLA] Use FP16 logits for sparse
  *        indexer": "Summary" and commits (selection on FP16 score keys,
  *        refining only the remaining key bits; FP16 logits; the MXFP4
@@ -219,6 +221,76 @@ idx_status indexer_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages,
                                 const int32_t* context_lens, int32_t B, int32_t next_n,
                                 int32_t num_pages, int32_t max_pages, float* logits,
                                 int64_t logits_stride, int32_t* hist, void* stream);
+
+/*
+ * Two-level candidate indexer ([P2] SGLang PR #38944: the candidate-source
+ * layer publishes an ascending table of 8-token logical blocks per query
+ * row; the layers after it score those blocks only -- paged sparse MQA
+ * logits -- and select inside that sparse row).  Block b holds keys
+ * 8b .. 8b+7 of the row; only keys below the row's length are live.
+ *
+ * block_amax8 -- [P2] amax8_varlen: out[r][j] = maximum of the live scores
+ * 8j .. 8j+7 of row r (NaN ignored; NaN if all are NaN) for j < ceil(len_r/8),
+ * except the newest block, written as +inf so it is always selected; nothing
+ * is written at or past ceil(len_r / 8).  The block top-k is topk_rows over
+ * these rows with lengths ceil(len_r / 8).
+ *
+ * scores       (device) float [rows][stride], 16-B aligned, stride % 4 == 0
+ * context_lens (device) int32 [rows]; clamped to [0, stride]
+ * out          (device) float [rows][out_stride], out_stride >= ceil(stride/8)
+ */
+idx_status block_amax8(const float* scores, int64_t stride, const int32_t* context_lens,
+                       int32_t rows, float* out, int64_t out_stride, void* stream);
+
+/*
+ * sort_candidate_blocks -- [P2] sort_candidate_blocks: the selected block ids
+ * of each row (any order, -1 padded; ids outside [0, ceil(len/8)) and
+ * repeats are ignored) become the ascending table padded with INT32_MAX,
+ * and the same blocks as pool slots / 8 through the row's page table:
+ * (page * 64 + (8b) % 64) / 8 with page = block_table[row / next_n][8b / 64].
+ * Rows with at most kb blocks get the identity table 0 .. ceil(len/8)-1.
+ * sparse_lens[r] receives the live keys of the listed blocks (the sparse row
+ * length).  A counting sort over a 16 KiB bitmap: rows hold at most 2^17
+ * blocks, so max_len (an upper bound of every length) is at most 2^20.
+ * `table` may be `blocks` itself (every read precedes the first write).
+ *
+ * blocks       (device) int32 [rows][kb]
+ * block_table  (device) int32 [rows / next_n][max_pages]
+ * table, slots (device) int32 [rows][kb];  sparse_lens (device) int32 [rows]
+ */
+idx_status sort_candidate_blocks(const int32_t* blocks, int32_t kb, const int32_t* context_lens,
+                                 int32_t rows, int64_t max_len, const int32_t* block_table,
+                                 int32_t max_pages, int32_t next_n, int32_t* table, int32_t* slots,
+                                 int32_t* sparse_lens, void* stream);
+
+/*
+ * indexer_sparse_logits -- [P2] paged sparse MQA logits: for row r and table
+ * entry i (block b = table[r][i] != INT32_MAX) and t in 0..7 with key
+ * 8b + t < len_r, logits[r][8i + t] = the indexer logit of that key
+ * (indexer_logits' formula, FP8 K), its K row read at pool slot
+ * 8 * slots[r][i] + t of kv_pages / k_scales.  Other columns are not
+ * written.  Each row has its own table, Q and weights (next_n rows of a
+ * request are independent rows here).
+ *
+ * q, kv_pages, k_scales, weights as for indexer_logits (per row)
+ * table, slots  (device) int32 [rows][kb] from sort_candidate_blocks
+ * logits        (device) float [rows][logits_stride], logits_stride >= 8 kb
+ */
+idx_status indexer_sparse_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                                 const float* weights, const int32_t* table, const int32_t* slots,
+                                 int32_t kb, const int32_t* context_lens, int32_t rows,
+                                 int32_t num_pages, float* logits, int64_t logits_stride,
+                                 void* stream);
+
+/*
+ * sparse_to_logical -- the selection inside a sparse row as logical key
+ * positions: out[r][j] = 8 * table[r][c / 8] + c % 8 for c = indices[r][j];
+ * -1 (and columns past the table or on padding) give -1.
+ *
+ * indices, out  (device) int32 [rows][k];  table (device) int32 [rows][kb]
+ */
+idx_status sparse_to_logical(const int32_t* indices, int32_t k, const int32_t* table,
+                             int32_t kb, int32_t rows, int32_t* out, void* stream);
 
 /*
  * topk_rows_f16 -- topk_rows over binary16 scores ([P3] "Summary": selection

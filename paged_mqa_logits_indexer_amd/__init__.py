@@ -19,6 +19,12 @@ Entry points (same names as the C ABI):
   topk_rows_f16(logits, hist, context_lens, k, indices, workspace=None,
                 events=None)                                      float16 scores
   score_histogram(scores, context_lens, hist)
+  block_amax8(scores, context_lens, out)                       two-level candidate indexer:
+  sort_candidate_blocks(blocks, context_lens, max_len, block_table, next_n,
+                        table, slots, sparse_lens)
+  indexer_sparse_logits(q, kv_pages, k_scales, weights, table, slots,
+                        context_lens, logits)
+  sparse_to_logical(indices, table, out)
   indexer_status_str(status)
   indexer_time_next_call(start, stop)
   hbm_read_probe(src, sink, events=None)
@@ -38,7 +44,8 @@ import torch
 __all__ = [
     "IndexerError", "KEY_FP32", "KEY_FP16", "NUM_BINS", "CANDIDATE_CAPACITY",
     "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits", "indexer_logits_f16",
-    "indexer_logits_mxfp4",
+    "indexer_logits_mxfp4", "block_amax8", "sort_candidate_blocks", "indexer_sparse_logits",
+    "sparse_to_logical",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram", "indexer_status_str",
     "indexer_time_next_call", "hbm_read_probe",
 ]
@@ -52,7 +59,9 @@ HEAD_DIM = 128
 PAGE_TOKENS = 64
 MXFP4_TOKEN_BYTES = 68
 
-EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp4", "topk_workspace_bytes", "topk_rows",
+EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp4", "block_amax8",
+                    "sort_candidate_blocks", "indexer_sparse_logits", "sparse_to_logical",
+                    "topk_workspace_bytes", "topk_rows",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
                     "indexer_time_next_call", "hbm_read_probe")
 
@@ -101,6 +110,14 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_logits_f16.restype = ctypes.c_int
     lib.indexer_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp]
     lib.indexer_logits_mxfp4.restype = ctypes.c_int
+    lib.block_amax8.argtypes = [vp, i64, vp, i32, vp, i64, vp]
+    lib.block_amax8.restype = ctypes.c_int
+    lib.sort_candidate_blocks.argtypes = [vp, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp, vp]
+    lib.sort_candidate_blocks.restype = ctypes.c_int
+    lib.indexer_sparse_logits.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i64, vp]
+    lib.indexer_sparse_logits.restype = ctypes.c_int
+    lib.sparse_to_logical.argtypes = [vp, i32, vp, i32, i32, vp, vp]
+    lib.sparse_to_logical.restype = ctypes.c_int
     lib.topk_rows_f16.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.topk_rows_f16.restype = ctypes.c_int
     lib.indexer_time_next_call.argtypes = [vp, vp]
@@ -244,6 +261,93 @@ def indexer_logits_mxfp4(q, kv_pages, weights, block_table, context_lens, next_n
     of E2M1 codes, then four E8M0 block scales per token); float32 logits."""
     _logits_call("indexer_logits_mxfp4", torch.float32, q, kv_pages, None, weights, block_table,
                  context_lens, next_n, logits, hist, events)
+
+
+def _rows2(t, name, dtype, dev, rows=None):
+    _need(t, name, dtype, dev, 2)
+    if not t.is_contiguous() or (rows is not None and t.shape[0] != rows):
+        raise ValueError(f"{name} must be contiguous [{rows if rows is not None else 'rows'}, n]")
+
+
+def block_amax8(scores, context_lens, out, events=None):
+    """Block maxima of 8 scores per row (newest block +inf) into out [rows, >= ceil(stride/8)]."""
+    dev = scores.device
+    _need(scores, "scores", torch.float32, dev, 2)
+    rows = scores.shape[0]
+    _rows2(out, "out", torch.float32, dev, rows)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    if scores.stride(1) != 1 or tuple(context_lens.shape) != (rows,):
+        raise ValueError("scores must have unit column stride; context_lens [rows]")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        st = lib.block_amax8(_ptr(scores), int(scores.stride(0)), _ptr(context_lens), int(rows), _ptr(out),
+                             int(out.stride(0)), _stream_ptr(dev))
+    _check("block_amax8", st)
+
+
+def sort_candidate_blocks(blocks, context_lens, max_len, block_table, next_n, table, slots, sparse_lens,
+                          events=None):
+    """Ascending INT32_MAX-padded block tables, pool slots / 8 and sparse row lengths."""
+    dev = blocks.device
+    _rows2(blocks, "blocks", torch.int32, dev)
+    rows, kb = blocks.shape
+    _rows2(table, "table", torch.int32, dev, rows)
+    _rows2(slots, "slots", torch.int32, dev, rows)
+    _rows2(block_table, "block_table", torch.int32, dev)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    _need(sparse_lens, "sparse_lens", torch.int32, dev, 1)
+    if table.shape[1] != kb or slots.shape[1] != kb:
+        raise ValueError("table and slots must be [rows, kb] like blocks")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        st = lib.sort_candidate_blocks(_ptr(blocks), int(kb), _ptr(context_lens), int(rows), int(max_len),
+                                       _ptr(block_table), int(block_table.shape[1]), int(next_n),
+                                       _ptr(table), _ptr(slots), _ptr(sparse_lens), _stream_ptr(dev))
+    _check("sort_candidate_blocks", st)
+
+
+def indexer_sparse_logits(q, kv_pages, k_scales, weights, table, slots, context_lens, logits,
+                          events=None):
+    """Logits of the listed 8-token blocks only: logits [rows, >= 8 kb]."""
+    dev = q.device
+    _need(q, "q", torch.uint8, dev, 3)
+    _need(kv_pages, "kv_pages", torch.uint8, dev, 3)
+    _need(k_scales, "k_scales", torch.float32, dev, 2)
+    _need(weights, "weights", torch.float32, dev, 2)
+    _rows2(table, "table", torch.int32, dev)
+    rows, kb = table.shape
+    _rows2(slots, "slots", torch.int32, dev, rows)
+    _need(context_lens, "context_lens", torch.int32, dev, 1)
+    _need(logits, "logits", torch.float32, dev, 2)
+    if tuple(q.shape) != (rows, HEADS, HEAD_DIM) or tuple(weights.shape) != (rows, HEADS):
+        raise ValueError(f"q [{rows}, 32, 128] and weights [{rows}, 32] (one per row)")
+    if logits.shape[0] != rows or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, stride] with unit column stride")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        st = lib.indexer_sparse_logits(_ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(table),
+                                       _ptr(slots), int(kb), _ptr(context_lens), int(rows),
+                                       int(kv_pages.shape[0]), _ptr(logits), int(logits.stride(0)),
+                                       _stream_ptr(dev))
+    _check("indexer_sparse_logits", st)
+
+
+def sparse_to_logical(indices, table, out, events=None):
+    """Sparse-row columns -> logical key positions (-1 stays -1)."""
+    dev = indices.device
+    _rows2(indices, "indices", torch.int32, dev)
+    rows, k = indices.shape
+    _rows2(table, "table", torch.int32, dev, rows)
+    _rows2(out, "out", torch.int32, dev, rows)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        st = lib.sparse_to_logical(_ptr(indices), int(k), _ptr(table), int(table.shape[1]), int(rows),
+                                   _ptr(out), _stream_ptr(dev))
+    _check("sparse_to_logical", st)
 
 
 def topk_workspace_bytes(rows: int, logits_stride: int, k: int) -> int:

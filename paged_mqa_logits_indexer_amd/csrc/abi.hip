@@ -161,6 +161,76 @@ idx_status score_histogram(const float* scores, int64_t stride, const int32_t* c
                                                static_cast<hipStream_t>(stream)));
 }
 
+idx_status block_amax8(const float* scores, int64_t stride, const int32_t* context_lens, int32_t rows,
+                       float* out, int64_t out_stride, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!scores || !context_lens || !out) return IDX_EINVAL;
+  if (rows <= 0 || stride <= 0 || out_stride < (stride + 7) / 8) return IDX_EINVAL;
+  if (rows > IDX_MAX_ROWS || stride > (int64_t{1} << 31) - 4) return IDX_EUNSUPPORTED;
+  if (!aligned(scores, 16) || (stride % 4) != 0 || !aligned(context_lens, 4) || !aligned(out, 4))
+    return IDX_EALIGN;
+  return from_hip(pmqa::launch_block_amax8(scores, stride, context_lens, rows, out, out_stride,
+                                           static_cast<hipStream_t>(stream), ev));
+}
+
+idx_status sort_candidate_blocks(const int32_t* blocks, int32_t kb, const int32_t* context_lens,
+                                 int32_t rows, int64_t max_len, const int32_t* block_table,
+                                 int32_t max_pages, int32_t next_n, int32_t* table, int32_t* slots,
+                                 int32_t* sparse_lens, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!blocks || !context_lens || !block_table || !table || !slots || !sparse_lens) return IDX_EINVAL;
+  if (rows <= 0 || kb <= 0 || max_len <= 0 || max_pages <= 0 || next_n < 1) return IDX_EINVAL;
+  if (rows % next_n != 0) return IDX_EINVAL;
+  if (rows > IDX_MAX_ROWS || kb > pmqa::kMaxCandidateBlocks ||
+      max_len > static_cast<int64_t>(pmqa::kMaxCandidateBlocks) * 8)
+    return IDX_EUNSUPPORTED;
+  if (!aligned(blocks, 4) || !aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(table, 4) ||
+      !aligned(slots, 4) || !aligned(sparse_lens, 4))
+    return IDX_EALIGN;
+  return from_hip(pmqa::launch_sort_candidate_blocks(blocks, kb, context_lens, rows, max_len, block_table,
+                                                     max_pages, next_n, table, slots, sparse_lens,
+                                                     static_cast<hipStream_t>(stream), ev));
+}
+
+idx_status indexer_sparse_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                                 const float* weights, const int32_t* table, const int32_t* slots,
+                                 int32_t kb, const int32_t* context_lens, int32_t rows, int32_t num_pages,
+                                 float* logits, int64_t logits_stride, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!q || !kv_pages || !k_scales || !weights || !table || !slots || !context_lens || !logits)
+    return IDX_EINVAL;
+  if (rows <= 0 || kb <= 0 || num_pages <= 0 || logits_stride < static_cast<int64_t>(kb) * 8) return IDX_EINVAL;
+  if (rows > IDX_MAX_ROWS || kb > pmqa::kMaxCandidateBlocks) return IDX_EUNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(k_scales, 4) || !aligned(weights, 16) ||
+      !aligned(table, 4) || !aligned(slots, 4) || !aligned(context_lens, 4) || !aligned(logits, 4))
+    return IDX_EALIGN;
+  pmqa::SparseLogitsArgs a;
+  a.q = q;
+  a.kv_pages = kv_pages;
+  a.k_scales = k_scales;
+  a.weights = weights;
+  a.table = table;
+  a.slots = slots;
+  a.context_lens = context_lens;
+  a.logits = logits;
+  a.logits_stride = logits_stride;
+  a.rows = rows;
+  a.kb = kb;
+  a.num_pages = num_pages;
+  return from_hip(pmqa::launch_indexer_sparse_logits(a, static_cast<hipStream_t>(stream), ev));
+}
+
+idx_status sparse_to_logical(const int32_t* indices, int32_t k, const int32_t* table, int32_t kb, int32_t rows,
+                             int32_t* out, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!indices || !table || !out) return IDX_EINVAL;
+  if (rows <= 0 || k <= 0 || kb <= 0) return IDX_EINVAL;
+  if (rows > IDX_MAX_ROWS || kb > pmqa::kMaxCandidateBlocks) return IDX_EUNSUPPORTED;
+  if (!aligned(indices, 4) || !aligned(table, 4) || !aligned(out, 4)) return IDX_EALIGN;
+  return from_hip(pmqa::launch_sparse_to_logical(indices, k, table, kb, rows, out,
+                                                 static_cast<hipStream_t>(stream), ev));
+}
+
 idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   const pmqa::LaunchEvents ev = take_events();
   if (!src || !sink || bytes == 0) return IDX_EINVAL;

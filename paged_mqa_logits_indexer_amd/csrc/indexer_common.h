@@ -171,6 +171,34 @@ struct LogitsArgs {
 };
 hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, LaunchEvents ev = {});
 
+// Two-level candidate indexer.  Candidate blocks are 8 tokens; a row's bitmap
+// of them is 16 KiB, so rows hold at most 2^17 blocks (2^20 keys).
+constexpr int kMaxCandidateBlocks = 1 << 17;
+
+struct SparseLogitsArgs {
+  const uint8_t* q;          // E4M3 [rows][32][128]
+  const uint8_t* kv_pages;   // E4M3 [num_pages][64][128]
+  const float* k_scales;     // [num_pages][64]
+  const float* weights;      // [rows][32]
+  const int32_t* table;      // [rows][kb] ascending block ids, INT32_MAX padded
+  const int32_t* slots;      // [rows][kb] the same blocks as pool slot / 8
+  const int32_t* context_lens;  // [rows]
+  float* logits;             // [rows][logits_stride], column 8 i + t = key 8 table[i] + t
+  int64_t logits_stride;
+  int32_t rows;
+  int32_t kb;
+  int32_t num_pages;
+};
+hipError_t launch_indexer_sparse_logits(const SparseLogitsArgs& a, hipStream_t stream, LaunchEvents ev = {});
+hipError_t launch_block_amax8(const float* scores, int64_t stride, const int32_t* lens, int32_t rows, float* out,
+                              int64_t out_stride, hipStream_t stream, LaunchEvents ev = {});
+hipError_t launch_sort_candidate_blocks(const int32_t* blocks, int32_t kb, const int32_t* lens, int32_t rows,
+                                        int64_t max_len, const int32_t* block_table, int32_t max_pages,
+                                        int32_t next_n, int32_t* table, int32_t* slots, int32_t* sparse_lens,
+                                        hipStream_t stream, LaunchEvents ev = {});
+hipError_t launch_sparse_to_logical(const int32_t* idx, int32_t k, const int32_t* table, int32_t kb, int32_t rows,
+                                    int32_t* out, hipStream_t stream, LaunchEvents ev = {});
+
 struct TopkArgs {
   const void* logits;  // float32, or IEEE binary16 bits with logits_f16
   const int32_t* hist;

@@ -90,6 +90,8 @@ constexpr int kThreadsOf = kWavesOf<NN> * kWave;
 constexpr int kKFp8 = 0;
 constexpr int kKMxfp4 = 1;
 constexpr int kMxTokenBytes = 68;
+constexpr int kBlk8 = 8;                              // tokens per candidate block
+constexpr int kBlocksPerChunk = kPage / kBlk8;        // 8 blocks = 64 sparse columns
 constexpr int kMxPageBytes = kPage * kMxTokenBytes;  // 4352
 
 template <int KF>
@@ -441,6 +443,88 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Paged sparse MQA logits: the consumer layers of the two-level candidate
+// indexer (SGLang PR #38944) score only the 8-token blocks a source layer
+// published.  Sparse column 8 i + t of a row is key 8 table[i] + t; the K row
+// sits at pool slot 8 slots[i] + t (the published table carries the blocks as
+// pool slots / 8, so no block-table lookup is needed here).  Each wave takes
+// 64 columns (8 table entries) at a time: lane (n, g) of key block kb reads
+// the K row of column 16 kb + n -- the dense kernel's operand layout with a
+// gathered address per lane -- and the same MFMA + epilogue computes the 64
+// logits.  Columns whose entry is padding, or whose key is at or past the
+// row length, are not written.
+constexpr int kSparseWaves = 4;
+constexpr int kSparseChunksPerWg = 16;  // 64-column chunks per workgroup
+
+__global__ __launch_bounds__(kSparseWaves * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
+  __shared__ __align__(16) float s_out[kSparseChunksPerWg * kPage];
+  __shared__ uint8_t s_live[kSparseChunksPerWg * kPage];
+  const int tid = threadIdx.x;
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int row = blockIdx.y;
+  const int chunks = (a.kb + kBlocksPerChunk - 1) / kBlocksPerChunk;
+  const int c0 = blockIdx.x * kSparseChunksPerWg;
+  if (c0 >= chunks) return;
+  const int c1 = min(c0 + kSparseChunksPerWg, chunks);
+  const int len = max(a.context_lens[row], 0);
+  const int m = lane & 15, g = lane >> 4;
+
+  RequestRegs<1> rq;
+  rq.len[0] = len;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      rq.q[0][mb][h] = *reinterpret_cast<const i32x4*>(
+          a.q + (static_cast<int64_t>(row) * kHeads + mb * 16 + m) * kDim + g * 16 + h * 64);
+    rq.w[0][mb] = *reinterpret_cast<const f32x4*>(a.weights + static_cast<int64_t>(row) * kHeads + mb * 16 + 4 * g);
+  }
+  const int32_t* tab = a.table + static_cast<int64_t>(row) * a.kb;
+  const int32_t* slt = a.slots + static_cast<int64_t>(row) * a.kb;
+  const int64_t pool_keys = static_cast<int64_t>(a.num_pages) * kPage;
+  const int t = m & (kBlk8 - 1);  // token of the lane's key within its block
+
+  for (int c = c0 + wave; c < c1; c += kSparseWaves) {
+    // Table entries of this lane's four keys (clamped loads, masked below).
+    int key_slot[4];
+    bool live[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int i = c * kBlocksPerChunk + kb * 2 + (m >> 3);
+      const int ic = min(i, a.kb - 1);
+      const int blk = tab[ic];
+      const int s8 = slt[ic];
+      const int64_t ps = static_cast<int64_t>(s8) * kBlk8 + t;
+      live[kb] = i < a.kb && blk != INT_MAX && static_cast<int64_t>(blk) * kBlk8 + t < len && s8 >= 0 &&
+                 ps < pool_keys;
+      key_slot[kb] = live[kb] ? static_cast<int>(ps) : 0;
+    }
+    PageRegs<kKFp8> pr;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const i32x4* src = reinterpret_cast<const i32x4*>(a.kv_pages + static_cast<int64_t>(key_slot[kb]) * kDim + g * 16);
+      pr.v[2 * kb + 0] = src[0];
+      pr.v[2 * kb + 1] = src[4];  // + 64 bytes
+    }
+    // lane l's own column 64 c + l is key n = l % 16 of key block l / 16
+    const int own = lane >> 4;
+    const int own_slot = own == 0 ? key_slot[0] : own == 1 ? key_slot[1] : own == 2 ? key_slot[2] : key_slot[3];
+    const bool own_live = own == 0 ? live[0] : own == 1 ? live[1] : own == 2 ? live[2] : live[3];
+    pr.scale = a.k_scales[own_slot];
+    const int lpi = c - c0;
+    compute_page<1, false, false, kKFp8>(pr, 0, lpi, kSparseChunksPerWg, lane, rq, s_out, nullptr);
+    s_live[lpi * kPage + lane] = own_live ? 1 : 0;
+  }
+  __syncthreads();
+  float* dst = a.logits + static_cast<int64_t>(row) * a.logits_stride + static_cast<int64_t>(c0) * kPage;
+  const int ncols = (c1 - c0) * kPage;
+  for (int i = tid; i < ncols; i += kSparseWaves * kWave)
+    if (s_live[i]) dst[i] = s_out[i];
+}
+
 struct DeviceInfo {
   int cus = 0;
 };
@@ -513,6 +597,15 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
     case 9: return launch_fmt<4, true>(a, grid, p, stream, ev);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_indexer_sparse_logits(const SparseLogitsArgs& a, hipStream_t stream, LaunchEvents ev) {
+  const int64_t chunks = (static_cast<int64_t>(a.kb) + kBlocksPerChunk - 1) / kBlocksPerChunk;
+  const int64_t gx = (chunks + kSparseChunksPerWg - 1) / kSparseChunksPerWg;
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  launch_kernel(indexer_sparse_logits_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(a.rows)),
+                dim3(kSparseWaves * kWave), stream, ev.start, ev.stop, a);
+  return hipGetLastError();
 }
 
 }  // namespace pmqa
