@@ -167,6 +167,10 @@ def main() -> int:
                     help="steps of the second timing with FP16 score keys")
     ap.add_argument("--mxfp4-steps", type=int, default=100,
                     help="steps of the same shape with MXFP4 K (indexer_logits_mxfp4)")
+    ap.add_argument("--candidate-steps", type=int, default=50,
+                    help="steps of the two-level candidate chain on the dense logits")
+    ap.add_argument("--candidate-blocks", type=int, default=512,
+                    help="8-token blocks the source layer publishes per row")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
@@ -334,6 +338,72 @@ def main() -> int:
                   "frac": round(abm["total"] / (lm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
         del tm, lgm, hm
 
+    # two-level candidate chain on this workload's dense logits (FP8 K):
+    # publish = block maxima + block top-k + sorted table; select = sparse
+    # logits over the published blocks + top-k inside the sparse row + map
+    cand_out = None
+    if args.candidate_steps > 0 and not x.mxfp4:
+        kbk = args.candidate_blocks
+        print(f"[bench] candidate chain ({kbk} blocks): {args.candidate_steps} steps",
+              file=sys.stderr, flush=True)
+        hist.zero_()
+        call_logits(x, t, logits, None, None)
+        width = -(-(-(-x.logits_stride // 8)) // 4) * 4
+        am = torch.empty((x.rows, width), dtype=torch.float32, device=dev)
+        ah = torch.zeros((x.rows, 1024), dtype=torch.int32, device=dev)
+        blens = (t["context_lens"] + 7) // 8
+        bsel = torch.empty((x.rows, kbk), dtype=torch.int32, device=dev)
+        table = torch.empty_like(bsel)
+        slots = torch.empty_like(bsel)
+        slens = torch.empty(x.rows, dtype=torch.int32, device=dev)
+        sparse = torch.empty((x.rows, kbk * 8), dtype=torch.float32, device=dev)
+        ssel = torch.empty((x.rows, K), dtype=torch.int32, device=dev)
+        pos = torch.empty_like(ssel)
+        ws_b = torch.zeros(pmqa.topk_workspace_bytes(x.rows, width, kbk), dtype=torch.uint8, device=dev)
+        ws_s = torch.zeros(pmqa.topk_workspace_bytes(x.rows, kbk * 8, K), dtype=torch.uint8, device=dev)
+        names = ("block_amax8", "block_topk", "sort_candidate_blocks", "indexer_sparse_logits",
+                 "sparse_topk", "sparse_to_logical")
+
+        def chain(n_steps, record):
+            per = {nm: [] for nm in names}
+            pub, sel = [], []
+            for i in range(n_steps):
+                ev = new_events(12)
+                evict()
+                ah.zero_()
+                pmqa.block_amax8(logits, t["context_lens"], am, ah, events=(ev[0], ev[1]))
+                pmqa.topk_rows(am, ah, blens, kbk, pmqa.KEY_FP32, bsel, ws_b, events=(ev[2], ev[3]))
+                pmqa.sort_candidate_blocks(bsel, t["context_lens"], x.logits_stride, t["block_table"],
+                                           x.next_n, table, slots, slens, events=(ev[4], ev[5]))
+                pmqa.indexer_sparse_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"], table,
+                                           slots, t["context_lens"], sparse, events=(ev[6], ev[7]))
+                pmqa.topk_rows(sparse, None, slens, K, pmqa.KEY_FP32, ssel, ws_s, events=(ev[8], ev[9]))
+                pmqa.sparse_to_logical(ssel, table, pos, events=(ev[10], ev[11]))
+                if record:
+                    per["_ev"] = per.get("_ev", []) + [ev]
+            torch.cuda.synchronize()
+            if record:
+                for ev in per.pop("_ev"):
+                    for j, nm in enumerate(names):
+                        per[nm].append(ev[2 * j].elapsed_time(ev[2 * j + 1]) * 1e3)
+                    pub.append(ev[0].elapsed_time(ev[5]) * 1e3)
+                    sel.append(ev[6].elapsed_time(ev[11]) * 1e3)
+            return per, pub, sel
+
+        chain(3, False)
+        per, pub, sel = chain(args.candidate_steps, True)
+        keys_listed = int(slens.sum().item())
+        sp_bytes = keys_listed * (128 + 4 + 4) + x.rows * kbk * 8 + x.rows * (32 * 128 + 32 * 4 + 4)
+        sp_us = float(np.mean(per["indexer_sparse_logits"]))
+        cand_out = {"blocks_per_row": kbk, "k": K,
+                    "publish_us_mean": round(float(np.mean(pub)), 3),
+                    "select_us_mean": round(float(np.mean(sel)), 3),
+                    "per_call_us_mean": {nm: round(float(np.mean(per[nm])), 3) for nm in names},
+                    "sparse_logits_bytes": sp_bytes,
+                    "sparse_logits_gbps": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
+                    "note": "publish/select spans include the dispatch gaps between their calls"}
+        del am, ah, bsel, table, slots, slens, sparse, ssel, pos, ws_b, ws_s
+
     # practical read ceiling over the same number of bytes as K
     ab = algorithmic_bytes(x)
     probe_src = torch.empty(ab["k"] // 4, dtype=torch.int32, device=dev)
@@ -405,6 +475,8 @@ def main() -> int:
         # the same shape with MXFP4 K: indexer_logits_mxfp4 + topk_rows (FP32 keys);
         # frac = algorithmic bytes / time against the HBM peak
         "mxfp4_k": mx_out,
+        # two-level candidate indexer on this workload (SGLang PR #38944)
+        "candidate_chain": cand_out,
         "hbm": {
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),

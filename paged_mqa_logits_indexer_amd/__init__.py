@@ -110,7 +110,7 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_logits_f16.restype = ctypes.c_int
     lib.indexer_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp]
     lib.indexer_logits_mxfp4.restype = ctypes.c_int
-    lib.block_amax8.argtypes = [vp, i64, vp, i32, vp, i64, vp]
+    lib.block_amax8.argtypes = [vp, i64, vp, i32, vp, i64, vp, vp]
     lib.block_amax8.restype = ctypes.c_int
     lib.sort_candidate_blocks.argtypes = [vp, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp, vp]
     lib.sort_candidate_blocks.restype = ctypes.c_int
@@ -269,8 +269,9 @@ def _rows2(t, name, dtype, dev, rows=None):
         raise ValueError(f"{name} must be contiguous [{rows if rows is not None else 'rows'}, n]")
 
 
-def block_amax8(scores, context_lens, out, events=None):
-    """Block maxima of 8 scores per row (newest block +inf) into out [rows, >= ceil(stride/8)]."""
+def block_amax8(scores, context_lens, out, hist=None, events=None):
+    """Block maxima of 8 scores per row (newest block +inf) into out [rows, >= ceil(stride/8)];
+    with ``hist`` [rows, 1024] int32 their coarse histogram is accumulated too."""
     dev = scores.device
     _need(scores, "scores", torch.float32, dev, 2)
     rows = scores.shape[0]
@@ -281,8 +282,10 @@ def block_amax8(scores, context_lens, out, events=None):
     lib = load_library()
     with torch.cuda.device(dev):
         _arm(events, dev)
+        if hist is not None:
+            _rows2(hist, "hist", torch.int32, dev, rows)
         st = lib.block_amax8(_ptr(scores), int(scores.stride(0)), _ptr(context_lens), int(rows), _ptr(out),
-                             int(out.stride(0)), _stream_ptr(dev))
+                             int(out.stride(0)), _ptr(hist), _stream_ptr(dev))
     _check("block_amax8", st)
 
 

@@ -26,23 +26,47 @@ constexpr int kWordsPerThread = kBitmapWords / kSortThreads;
 // scores (v_max_f32 returns the other operand when one is NaN), +inf for the
 // row's newest block; nothing is written at or past ceil(len / 8).  Every
 // block before the newest lies wholly below len, so its two 16-byte loads
-// read live scores only.
+// read live scores only.  HIST: the maxima also go into the row's coarse
+// histogram (per-workgroup LDS slots added with 64-bit atomics, as in the
+// logits kernel), so the block top-k can skip its own first pass.
+template <bool HIST>
 __global__ __launch_bounds__(256) void block_amax8_kernel(const float* __restrict__ scores, int64_t stride,
                                                           const int32_t* __restrict__ lens,
-                                                          float* __restrict__ out, int64_t out_stride) {
+                                                          float* __restrict__ out, int64_t out_stride,
+                                                          int32_t* __restrict__ hist) {
+  __shared__ int s_hist[HIST ? kBins : 1];
   const int row = blockIdx.y;
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t l = lens[row];
   const int64_t len = l < 0 ? 0 : (l > stride ? stride : l);
   const int64_t nb = (len + kBlk - 1) / kBlk;
-  if (j >= nb) return;
-  float m = __int_as_float(0x7F800000);  // +inf: the newest block
-  if (j < nb - 1) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(scores + static_cast<int64_t>(row) * stride + kBlk * j);
-    const f32x4 a = p[0], b = p[1];
-    m = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+  if (static_cast<int64_t>(blockIdx.x) * 256 >= nb) return;  // uniform: no block of this row here
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < kBins; i += 256) s_hist[i] = 0;
+    __syncthreads();
   }
-  out[static_cast<int64_t>(row) * out_stride + j] = m;
+  if (j < nb) {
+    float m = __int_as_float(0x7F800000);  // +inf: the newest block
+    if (j < nb - 1) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(scores + static_cast<int64_t>(row) * stride + kBlk * j);
+      const f32x4 a = p[0], b = p[1];
+      m = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+    }
+    out[static_cast<int64_t>(row) * out_stride + j] = m;
+    if constexpr (HIST) {
+      const uint32_t hb = f16_bits_rn(m);
+      if (!f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
+    }
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    unsigned long long* gh = reinterpret_cast<unsigned long long*>(hist + static_cast<int64_t>(row) * kBins);
+    const uint2* sh = reinterpret_cast<const uint2*>(s_hist);
+    for (int i = threadIdx.x; i < kBins / 2; i += 256) {
+      const uint2 v = sh[i];
+      if (v.x | v.y) atomicAdd(gh + i, (static_cast<unsigned long long>(v.y) << 32) | v.x);
+    }
+  }
 }
 
 // One workgroup per row.  Rows with at most kb blocks get the identity table;
@@ -107,16 +131,18 @@ __global__ __launch_bounds__(kSortThreads) void sort_candidate_blocks_kernel(
     while (m) {
       const int bit = __ffs(m) - 1;
       m &= m - 1u;
-      const int b = (w0 + u) * 32 + bit;
-      tout[base] = b;  // base < total <= kb: at most kb bits were set
-      sout[base] = slot8(b);
-      ++base;
+      tout[base++] = (w0 + u) * 32 + bit;  // base < total <= kb: at most kb bits were set
     }
   }
   for (int i = total + tid; i < kb; i += kSortThreads) {
     tout[i] = INT_MAX;
     sout[i] = INT_MAX;
   }
+  // The page transform in a second pass over the written table (visible to
+  // the whole workgroup after the barrier), so a thread's block-table loads
+  // are independent of each other rather than one per emitted id in turn.
+  __syncthreads();
+  for (int i = tid; i < total; i += kSortThreads) sout[i] = slot8(tout[i]);
   if (tid == 0) {
     // every listed block is whole except the newest, which holds len - 8 (nb - 1) keys
     const bool newest = (s_bits[(nb - 1) >> 5] >> ((nb - 1) & 31)) & 1u;
@@ -146,12 +172,17 @@ __global__ void sparse_to_logical_kernel(const int32_t* __restrict__ idx, int k,
 }  // namespace
 
 hipError_t launch_block_amax8(const float* scores, int64_t stride, const int32_t* lens, int32_t rows, float* out,
-                              int64_t out_stride, hipStream_t stream, LaunchEvents ev) {
+                              int64_t out_stride, int32_t* hist, hipStream_t stream, LaunchEvents ev) {
   const int64_t nbmax = (stride + kBlk - 1) / kBlk;
   const int64_t gx = (nbmax + 255) / 256;
   if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
-  launch_kernel(block_amax8_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(rows)), dim3(256), stream,
-                ev.start, ev.stop, scores, stride, lens, out, out_stride);
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(rows));
+  if (hist)
+    launch_kernel(block_amax8_kernel<true>, grid, dim3(256), stream, ev.start, ev.stop, scores, stride, lens, out,
+                  out_stride, hist);
+  else
+    launch_kernel(block_amax8_kernel<false>, grid, dim3(256), stream, ev.start, ev.stop, scores, stride, lens, out,
+                  out_stride, hist);
   return hipGetLastError();
 }
 

@@ -455,7 +455,7 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
 // logits.  Columns whose entry is padding, or whose key is at or past the
 // row length, are not written.
 constexpr int kSparseWaves = 4;
-constexpr int kSparseChunksPerWg = 16;  // 64-column chunks per workgroup
+constexpr int kSparseChunksPerWg = kSparseWaves;  // one 64-column chunk per wave: tables are short
 
 __global__ __launch_bounds__(kSparseWaves * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 void indexer_sparse_logits_kernel(SparseLogitsArgs a) {

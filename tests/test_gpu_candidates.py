@@ -31,11 +31,18 @@ def test_block_amax8(gpu):
     ln = torch.from_numpy(lens).to(DEV)
     width = -(-stride // 8)
     out = torch.full((rows, width + 3), SENT, dtype=torch.float32, device=DEV)
+    out2 = torch.full((rows, width + 3), SENT, dtype=torch.float32, device=DEV)
+    h = torch.zeros((rows, 1024), dtype=torch.int32, device=DEV)
     announce("block_amax8")
     gpu.block_amax8(s, ln, out)
+    gpu.block_amax8(s, ln, out2, h)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
+    assert np.array_equal(got, out2.cpu().numpy(), equal_nan=True), "the histogram changes the maxima"
     want = C.block_amax8(sc, lens)
+    blk_lens = -(-lens.astype(np.int64) // 8)
+    assert np.array_equal(h.cpu().numpy(), O.coarse_histogram(got[:, :width], blk_lens)), \
+        "histogram of the block maxima differs"
     for r in range(rows):
         nb = -(-int(lens[r]) // 8)
         g, w = got[r, :nb], want[r, :nb]
@@ -129,11 +136,12 @@ def test_candidate_chain(gpu, name, kb_blocks):
     dense = lg.cpu().numpy()
     width = -(-(-(-x.logits_stride // 8)) // 4) * 4  # ceil(stride / 8), 16-byte rows for the top-k
     am = torch.full((x.rows, width), SENT, dtype=torch.float32, device=DEV)
+    ah = torch.zeros((x.rows, 1024), dtype=torch.int32, device=DEV)
     announce(f"{name}: block_amax8")
-    gpu.block_amax8(lg, d.lens, am)
+    gpu.block_amax8(lg, d.lens, am, ah)
     blens = torch.from_numpy(-(-lens.astype(np.int64) // 8).astype(np.int32)).to(DEV)
     announce(f"{name}: block top-{kb_blocks}")
-    bsel = topk(am, None, blens, kb_blocks, O.KEY_FP32)
+    bsel = topk(am, ah, blens, kb_blocks, O.KEY_FP32)
     am_h = am.cpu().numpy()
     want_am = C.block_amax8(dense, lens)
     for r in range(x.rows):
