@@ -287,6 +287,19 @@ idx_status indexer_sparse_logits(const uint8_t* q, const uint8_t* kv_pages, cons
                                  void* stream);
 
 /*
+ * indexer_sparse_logits_mxfp4 -- indexer_sparse_logits over packed MXFP4
+ * pages (the fp8 x fp4 sparse logits [P2] routes the paged fp4 decode path
+ * through; the keys as in indexer_logits_mxfp4).  kv_pages uint8
+ * [num_pages][64][68], no k_scales; other arguments as above.
+ */
+idx_status indexer_sparse_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages,
+                                       const float* weights, const int32_t* table,
+                                       const int32_t* slots, int32_t kb,
+                                       const int32_t* context_lens, int32_t rows,
+                                       int32_t num_pages, float* logits,
+                                       int64_t logits_stride, void* stream);
+
+/*
  * sparse_to_logical -- the selection inside a sparse row as logical key
  * positions: out[r][j] = 8 * table[r][c / 8] + c % 8 for c = indices[r][j];
  * -1 (and columns past the table or on padding) give -1.

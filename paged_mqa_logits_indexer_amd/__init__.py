@@ -45,6 +45,7 @@ __all__ = [
     "IndexerError", "KEY_FP32", "KEY_FP16", "NUM_BINS", "CANDIDATE_CAPACITY",
     "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits", "indexer_logits_f16",
     "indexer_logits_mxfp4", "block_amax8", "sort_candidate_blocks", "indexer_sparse_logits",
+    "indexer_sparse_logits_mxfp4",
     "sparse_to_logical",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram", "indexer_status_str",
     "indexer_time_next_call", "hbm_read_probe",
@@ -60,7 +61,8 @@ PAGE_TOKENS = 64
 MXFP4_TOKEN_BYTES = 68
 
 EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp4", "block_amax8",
-                    "sort_candidate_blocks", "indexer_sparse_logits", "sparse_to_logical",
+                    "sort_candidate_blocks", "indexer_sparse_logits", "indexer_sparse_logits_mxfp4",
+                    "sparse_to_logical",
                     "topk_workspace_bytes", "topk_rows",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
                     "indexer_time_next_call", "hbm_read_probe")
@@ -116,6 +118,8 @@ def load_library() -> ctypes.CDLL:
     lib.sort_candidate_blocks.restype = ctypes.c_int
     lib.indexer_sparse_logits.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i64, vp]
     lib.indexer_sparse_logits.restype = ctypes.c_int
+    lib.indexer_sparse_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i64, vp]
+    lib.indexer_sparse_logits_mxfp4.restype = ctypes.c_int
     lib.sparse_to_logical.argtypes = [vp, i32, vp, i32, i32, vp, vp]
     lib.sparse_to_logical.restype = ctypes.c_int
     lib.topk_rows_f16.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
@@ -313,11 +317,17 @@ def sort_candidate_blocks(blocks, context_lens, max_len, block_table, next_n, ta
 
 def indexer_sparse_logits(q, kv_pages, k_scales, weights, table, slots, context_lens, logits,
                           events=None):
-    """Logits of the listed 8-token blocks only: logits [rows, >= 8 kb]."""
+    """Logits of the listed 8-token blocks only: logits [rows, >= 8 kb].  With
+    k_scales None, kv_pages are packed MXFP4 tokens [P, 64, 68]
+    (indexer_sparse_logits_mxfp4)."""
     dev = q.device
+    mx = k_scales is None
     _need(q, "q", torch.uint8, dev, 3)
     _need(kv_pages, "kv_pages", torch.uint8, dev, 3)
-    _need(k_scales, "k_scales", torch.float32, dev, 2)
+    if kv_pages.shape[1:] != ((PAGE_TOKENS, MXFP4_TOKEN_BYTES) if mx else (PAGE_TOKENS, HEAD_DIM)):
+        raise ValueError("kv_pages must be [P, 64, 68] (MXFP4) or [P, 64, 128] with k_scales")
+    if not mx:
+        _need(k_scales, "k_scales", torch.float32, dev, 2)
     _need(weights, "weights", torch.float32, dev, 2)
     _rows2(table, "table", torch.int32, dev)
     rows, kb = table.shape
@@ -331,11 +341,13 @@ def indexer_sparse_logits(q, kv_pages, k_scales, weights, table, slots, context_
     lib = load_library()
     with torch.cuda.device(dev):
         _arm(events, dev)
-        st = lib.indexer_sparse_logits(_ptr(q), _ptr(kv_pages), _ptr(k_scales), _ptr(weights), _ptr(table),
-                                       _ptr(slots), int(kb), _ptr(context_lens), int(rows),
-                                       int(kv_pages.shape[0]), _ptr(logits), int(logits.stride(0)),
-                                       _stream_ptr(dev))
-    _check("indexer_sparse_logits", st)
+        tail = (_ptr(weights), _ptr(table), _ptr(slots), int(kb), _ptr(context_lens), int(rows),
+                int(kv_pages.shape[0]), _ptr(logits), int(logits.stride(0)), _stream_ptr(dev))
+        if mx:
+            st = lib.indexer_sparse_logits_mxfp4(_ptr(q), _ptr(kv_pages), *tail)
+        else:
+            st = lib.indexer_sparse_logits(_ptr(q), _ptr(kv_pages), _ptr(k_scales), *tail)
+    _check("indexer_sparse_logits_mxfp4" if mx else "indexer_sparse_logits", st)
 
 
 def sparse_to_logical(indices, table, out, events=None):

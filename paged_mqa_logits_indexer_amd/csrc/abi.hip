@@ -193,19 +193,20 @@ idx_status sort_candidate_blocks(const int32_t* blocks, int32_t kb, const int32_
                                                      static_cast<hipStream_t>(stream), ev));
 }
 
-idx_status indexer_sparse_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
-                                 const float* weights, const int32_t* table, const int32_t* slots,
-                                 int32_t kb, const int32_t* context_lens, int32_t rows, int32_t num_pages,
-                                 float* logits, int64_t logits_stride, void* stream) {
+static idx_status sparse_logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                              const float* weights, const int32_t* table, const int32_t* slots, int32_t kb,
+                              const int32_t* context_lens, int32_t rows, int32_t num_pages, float* logits,
+                              int64_t logits_stride, bool mxfp4, void* stream) {
   const pmqa::LaunchEvents ev = take_events();
-  if (!q || !kv_pages || !k_scales || !weights || !table || !slots || !context_lens || !logits)
+  if (!q || !kv_pages || (!mxfp4 && !k_scales) || !weights || !table || !slots || !context_lens || !logits)
     return IDX_EINVAL;
   if (rows <= 0 || kb <= 0 || num_pages <= 0 || logits_stride < static_cast<int64_t>(kb) * 8) return IDX_EINVAL;
   if (rows > IDX_MAX_ROWS || kb > pmqa::kMaxCandidateBlocks) return IDX_EUNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(kv_pages, 16) || !aligned(k_scales, 4) || !aligned(weights, 16) ||
+  if (!aligned(q, 16) || !aligned(kv_pages, 16) || (!mxfp4 && !aligned(k_scales, 4)) || !aligned(weights, 16) ||
       !aligned(table, 4) || !aligned(slots, 4) || !aligned(context_lens, 4) || !aligned(logits, 4))
     return IDX_EALIGN;
   pmqa::SparseLogitsArgs a;
+  a.k_mxfp4 = mxfp4 ? 1 : 0;
   a.q = q;
   a.kv_pages = kv_pages;
   a.k_scales = k_scales;
@@ -219,6 +220,22 @@ idx_status indexer_sparse_logits(const uint8_t* q, const uint8_t* kv_pages, cons
   a.kb = kb;
   a.num_pages = num_pages;
   return from_hip(pmqa::launch_indexer_sparse_logits(a, static_cast<hipStream_t>(stream), ev));
+}
+
+idx_status indexer_sparse_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                                 const float* weights, const int32_t* table, const int32_t* slots,
+                                 int32_t kb, const int32_t* context_lens, int32_t rows, int32_t num_pages,
+                                 float* logits, int64_t logits_stride, void* stream) {
+  return sparse_logits_call(q, kv_pages, k_scales, weights, table, slots, kb, context_lens, rows, num_pages,
+                            logits, logits_stride, false, stream);
+}
+
+idx_status indexer_sparse_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages, const float* weights,
+                                       const int32_t* table, const int32_t* slots, int32_t kb,
+                                       const int32_t* context_lens, int32_t rows, int32_t num_pages,
+                                       float* logits, int64_t logits_stride, void* stream) {
+  return sparse_logits_call(q, kv_pages, nullptr, weights, table, slots, kb, context_lens, rows, num_pages,
+                            logits, logits_stride, true, stream);
 }
 
 idx_status sparse_to_logical(const int32_t* indices, int32_t k, const int32_t* table, int32_t kb, int32_t rows,

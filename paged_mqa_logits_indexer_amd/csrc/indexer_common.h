@@ -177,8 +177,8 @@ constexpr int kMaxCandidateBlocks = 1 << 17;
 
 struct SparseLogitsArgs {
   const uint8_t* q;          // E4M3 [rows][32][128]
-  const uint8_t* kv_pages;   // E4M3 [num_pages][64][128]
-  const float* k_scales;     // [num_pages][64]
+  const uint8_t* kv_pages;   // E4M3 [num_pages][64][128], or packed MXFP4 tokens [num_pages][64][68]
+  const float* k_scales;     // [num_pages][64] (FP8 only)
   const float* weights;      // [rows][32]
   const int32_t* table;      // [rows][kb] ascending block ids, INT32_MAX padded
   const int32_t* slots;      // [rows][kb] the same blocks as pool slot / 8
@@ -188,6 +188,7 @@ struct SparseLogitsArgs {
   int32_t rows;
   int32_t kb;
   int32_t num_pages;
+  int32_t k_mxfp4;
 };
 hipError_t launch_indexer_sparse_logits(const SparseLogitsArgs& a, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_block_amax8(const float* scores, int64_t stride, const int32_t* lens, int32_t rows, float* out,

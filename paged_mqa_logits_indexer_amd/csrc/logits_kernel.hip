@@ -457,6 +457,7 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
 constexpr int kSparseWaves = 4;
 constexpr int kSparseChunksPerWg = kSparseWaves;  // one 64-column chunk per wave: tables are short
 
+template <int KF>
 __global__ __launch_bounds__(kSparseWaves * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
   __shared__ __align__(16) float s_out[kSparseChunksPerWg * kPage];
@@ -502,20 +503,30 @@ void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
                  ps < pool_keys;
       key_slot[kb] = live[kb] ? static_cast<int>(ps) : 0;
     }
-    PageRegs<kKFp8> pr;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const i32x4* src = reinterpret_cast<const i32x4*>(a.kv_pages + static_cast<int64_t>(key_slot[kb]) * kDim + g * 16);
-      pr.v[2 * kb + 0] = src[0];
-      pr.v[2 * kb + 1] = src[4];  // + 64 bytes
-    }
+    PageRegs<KF> pr;
     // lane l's own column 64 c + l is key n = l % 16 of key block l / 16
     const int own = lane >> 4;
-    const int own_slot = own == 0 ? key_slot[0] : own == 1 ? key_slot[1] : own == 2 ? key_slot[2] : key_slot[3];
     const bool own_live = own == 0 ? live[0] : own == 1 ? live[1] : own == 2 ? live[2] : live[3];
-    pr.scale = a.k_scales[own_slot];
+    if constexpr (KF == kKFp8) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const i32x4* src = reinterpret_cast<const i32x4*>(a.kv_pages + static_cast<int64_t>(key_slot[kb]) * kDim + g * 16);
+        pr.v[2 * kb + 0] = src[0];
+        pr.v[2 * kb + 1] = src[4];  // + 64 bytes
+      }
+      const int own_slot = own == 0 ? key_slot[0] : own == 1 ? key_slot[1] : own == 2 ? key_slot[2] : key_slot[3];
+      pr.scale = a.k_scales[own_slot];
+    } else {
+      // MXFP4 token: bytes [16g, 16g+16) of its 64 code bytes and its scale word
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint8_t* tok = a.kv_pages + static_cast<int64_t>(key_slot[kb]) * kMxTokenBytes;
+        pr.v[kb] = *reinterpret_cast<const i32x4*>(tok + g * 16);  // 4-byte aligned
+        pr.sc[kb] = *reinterpret_cast<const int*>(tok + 64);
+      }
+    }
     const int lpi = c - c0;
-    compute_page<1, false, false, kKFp8>(pr, 0, lpi, kSparseChunksPerWg, lane, rq, s_out, nullptr);
+    compute_page<1, false, false, KF>(pr, 0, lpi, kSparseChunksPerWg, lane, rq, s_out, nullptr);
     s_live[lpi * kPage + lane] = own_live ? 1 : 0;
   }
   __syncthreads();
@@ -603,8 +614,13 @@ hipError_t launch_indexer_sparse_logits(const SparseLogitsArgs& a, hipStream_t s
   const int64_t chunks = (static_cast<int64_t>(a.kb) + kBlocksPerChunk - 1) / kBlocksPerChunk;
   const int64_t gx = (chunks + kSparseChunksPerWg - 1) / kSparseChunksPerWg;
   if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
-  launch_kernel(indexer_sparse_logits_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(a.rows)),
-                dim3(kSparseWaves * kWave), stream, ev.start, ev.stop, a);
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(a.rows));
+  if (a.k_mxfp4)
+    launch_kernel(indexer_sparse_logits_kernel<kKMxfp4>, grid, dim3(kSparseWaves * kWave), stream, ev.start,
+                  ev.stop, a);
+  else
+    launch_kernel(indexer_sparse_logits_kernel<kKFp8>, grid, dim3(kSparseWaves * kWave), stream, ev.start,
+                  ev.stop, a);
   return hipGetLastError();
 }
 

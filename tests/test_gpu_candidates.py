@@ -89,9 +89,10 @@ def test_sort_candidate_blocks(gpu, in_place):
     assert np.array_equal(slens.cpu().numpy(), C.sparse_row_lens(want_t, lens))
 
 
-def test_sparse_logits(gpu):
+@pytest.mark.parametrize("kfmt", ["fp8", "mxfp4"])
+def test_sparse_logits(gpu, kfmt):
     rng = np.random.default_rng(75)
-    x = gen.make_indexer_inputs("sparse", 3, 2, [20000, 3000, 700], 19)
+    x = gen.make_indexer_inputs("sparse", 3, 2, [20000, 3000, 700], 19, kfmt=kfmt)
     d = DevInputs(x)
     kb = 200
     lens = x.context_lens
@@ -104,7 +105,7 @@ def test_sparse_logits(gpu):
     table, slots = C.sort_candidate_blocks(blocks, n_blocks, x.block_table, x.next_n)
     stride = kb * 8 + 12
     lg = torch.full((x.rows, stride), float("inf"), dtype=torch.float32, device=DEV)
-    announce("indexer_sparse_logits")
+    announce(f"indexer_sparse_logits {kfmt}")
     gpu.indexer_sparse_logits(d.q, d.kv, d.sc, d.w, torch.from_numpy(table).to(DEV),
                               torch.from_numpy(slots).to(DEV), d.lens, lg)
     torch.cuda.synchronize()
@@ -124,7 +125,8 @@ def test_sparse_logits(gpu):
         assert ok.all(), f"row {r}: {int((~ok).sum())} sparse logits outside tolerance"
 
 
-@pytest.mark.parametrize("name,kb_blocks", [("long_decode", 512), ("spec_verify/fine", 256)])
+@pytest.mark.parametrize("name,kb_blocks", [("long_decode", 512), ("spec_verify/fine", 256),
+                                            ("long_decode/mxfp4", 512)])
 def test_candidate_chain(gpu, name, kb_blocks):
     """Dense logits -> block maxima -> block top-k -> sorted table -> sparse
     logits -> top-2048 inside the sparse row -> logical positions."""
