@@ -19,6 +19,13 @@ on (H=32, D=128, 64-token pages):
   very_long      B=4,  next_n=1, L=1048576; plus score rows [4, 1048576] drawn
                  from 0.99 N(0, var 4) + 0.01 N(40, var 10)
 
+and one ragged prefill (extend) batch, the second workload of the pages'
+prefill path:
+
+  prefill/extend 4 requests x 2048 new tokens over cached prefixes of 0, 6K,
+                 14K and 30K keys (contexts 2K, 8K, 16K, 32K); row i of a
+                 request sees prefix + 1 + i keys (causal); 8192 rows
+
 Value recipe: Q ~ N(0,1) cast to e4m3; K rows ~ N(0,1), per-token scale
 absmax/448, codes = e4m3(k / scale); head weights N(0,1)/sqrt(32) times the
 variant's factor.  MXFP4 K (the "/mxfp4" workloads): the same K rows, each
@@ -53,7 +60,14 @@ SEEDS = {
     "very_long/scores": 506,
     "long_decode/mxfp4": 212,
     "spec_verify/mxfp4": 311,
+    "prefill/extend": 601,
+    "prefill/extend_mxfp4": 611,
 }
+
+# Ragged prefill (extend) batch: four requests append 2048 tokens each to
+# cached prefixes, so their contexts hold 2K, 8K, 16K and 32K keys.
+PREFILL_Q_LENS = (2048, 2048, 2048, 2048)
+PREFILL_PREFIX_LENS = (0, 6144, 14336, 30720)
 
 # Head-weight factors for the three verify variants.
 VERIFY_WEIGHT_SCALE = {"fine": 0.25, "unit": 16.0, "mixed": 4.0}
@@ -71,8 +85,9 @@ class IndexerInputs:
     weights: np.ndarray      # f32   [rows, 32]
     block_table: np.ndarray  # int32 [B, max_pages]
     context_lens: np.ndarray  # int32 [rows]
-    next_n: int
+    next_n: int               # rows per request (0 for a ragged prefill batch)
     logits_stride: int
+    cu_q: np.ndarray = None   # int32 [B + 1] row offsets of a ragged prefill batch
 
     @property
     def B(self) -> int:
@@ -92,6 +107,9 @@ class IndexerInputs:
 
     def request_keys(self) -> np.ndarray:
         """Longest row length of each request (the keys its K sweep reads)."""
+        if self.cu_q is not None:
+            return np.array([int(self.context_lens[a:b].max()) if b > a else 0
+                             for a, b in zip(self.cu_q[:-1], self.cu_q[1:])], dtype=np.int64)
         return self.context_lens.reshape(self.B, self.next_n).max(axis=1)
 
     @property
@@ -145,12 +163,40 @@ def make_indexer_inputs(name, B, next_n, base_lens, seed, weight_scale=1.0,
     base_lens: int per request; row j of request b sees base_lens[b] + j keys.
     kfmt: "fp8" (E4M3 codes + per-token scales) or "mxfp4" (packed tokens).
     """
+    return _make_inputs(name, np.full(B, next_n, dtype=np.int64), base_lens, seed, weight_scale,
+                        inf_frac, logits_stride, max_pages, spare_frac, pages_per_chunk, kfmt)
+
+
+def make_prefill_inputs(name, q_lens, prefix_lens, seed, weight_scale=1.0, logits_stride=None,
+                        max_pages=None, kfmt="fp8"):
+    """A ragged prefill (extend) batch: request b appends q_lens[b] tokens to a
+    cached prefix of prefix_lens[b] keys, so its context holds
+    prefix_lens[b] + q_lens[b] keys and its row i (causal) sees
+    prefix_lens[b] + 1 + i of them.  Rows are packed request after request;
+    cu_q holds the row offsets.  A request may have no rows."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int64).reshape(q_lens.shape)
+    x = _make_inputs(name, q_lens, prefix_lens + 1, seed, weight_scale, 0.0, logits_stride,
+                     max_pages, 0.01, 4096, kfmt)
+    x.cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    x.next_n = 0
+    return x
+
+
+def _make_inputs(name, n_rows, base_lens, seed, weight_scale, inf_frac, logits_stride,
+                 max_pages, spare_frac, pages_per_chunk, kfmt):
+    """Requests of n_rows[b] rows each; row j of request b sees base_lens[b] + j
+    keys (the K slots of its context up to base_lens[b] + n_rows[b] - 1)."""
     mx = kfmt == "mxfp4"
     rng = np.random.Generator(np.random.PCG64(seed))
+    n_rows = np.asarray(n_rows, dtype=np.int64)
+    B = n_rows.shape[0]
     base_lens = np.asarray(base_lens, dtype=np.int64).reshape(B)
-    rows = B * next_n
-    lens = (base_lens[:, None] + np.arange(next_n)[None, :]).reshape(rows)
-    req_keys = base_lens + next_n - 1
+    rows = int(n_rows.sum())
+    lens = np.concatenate([base_lens[b] + np.arange(n_rows[b]) for b in range(B)] or
+                          [np.zeros(0, np.int64)]).astype(np.int64)
+    next_n = int(n_rows[0]) if B else 0
+    req_keys = np.maximum(base_lens + n_rows - 1, 0)
     req_pages = -(-req_keys // PAGE)
     used = int(req_pages.sum())
     num_pages = used + max(1, int(math.ceil(used * spare_frac)))
@@ -219,6 +265,9 @@ def config_inputs(name: str) -> IndexerInputs:
     if name == "spec_verify/mxfp4":
         return make_indexer_inputs(name, 16, 4, [32768] * 16, SEEDS[name],
                                    weight_scale=VERIFY_WEIGHT_SCALE["fine"], kfmt="mxfp4")
+    if name in ("prefill/extend", "prefill/extend_mxfp4"):
+        return make_prefill_inputs(name, PREFILL_Q_LENS, PREFILL_PREFIX_LENS, SEEDS[name],
+                                   kfmt="mxfp4" if name.endswith("mxfp4") else "fp8")
     if name == "tiny_decode":
         return make_indexer_inputs(name, 1, 1, [4096], SEEDS[name])
     if name == "long_decode":
@@ -244,6 +293,7 @@ CONFIG_NAMES = ("tiny_decode", "long_decode", "spec_verify/fine",
                 "spec_verify/unit", "spec_verify/mixed", "varlen_decode",
                 "very_long")
 MXFP4_CONFIG_NAMES = ("long_decode/mxfp4", "spec_verify/mxfp4")
+PREFILL_CONFIG_NAMES = ("prefill/extend", "prefill/extend_mxfp4")
 
 
 def very_long_scores(rows=4, n=1048576, seed=None) -> np.ndarray:

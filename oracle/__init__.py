@@ -12,3 +12,4 @@ from .indexer_oracle import (  # noqa: F401
     indexer_logits_at, logits_error_bound_at, score_keys, topk_row, topk_rows,
 )
 from . import candidates  # noqa: F401,E402
+from . import prefill  # noqa: F401,E402

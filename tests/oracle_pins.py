@@ -781,9 +781,61 @@ def pin_sparse_logits(O, seed=65):
     return fails
 
 
+def pin_prefill_decode_case(O):
+    """A ragged batch whose requests all have next_n rows is a decode call:
+    the prefill oracle equals the decode oracle bit for bit (fill included)."""
+    import gen
+    x = gen.make_indexer_inputs("pd", 3, 2, [300, 451, 17], 9)
+    cu = np.arange(x.B + 1, dtype=np.int32) * x.next_n
+    want = O.indexer_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                            x.context_lens, x.next_n, x.logits_stride)
+    got = O.prefill.prefill_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table, cu,
+                                   x.context_lens, x.logits_stride)
+    if not np.array_equal(got, want, equal_nan=True):
+        return ["prefill logits of a decode-shaped batch differ from the decode logits"]
+    return []
+
+
+def pin_prefill_exact(O, n_cols=3):
+    """Ragged rows (an empty request included) in exact rationals: row t of
+    request r (found by walking cu_q) scores keys [0, len_t) of r's pages."""
+    import gen
+    fails = []
+    x = gen.make_prefill_inputs("pe", [3, 0, 2, 1], [70, 5, 0, 130], 41)
+    got = O.prefill.prefill_logits(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                                   x.cu_q, x.context_lens, x.logits_stride)
+    rng = np.random.default_rng(3)
+    for t in range(x.rows):
+        r = next(i for i in range(x.B) if x.cu_q[i] <= t < x.cu_q[i + 1])
+        n = int(x.context_lens[t])
+        qd = torch_e4m3_decode(x.q[t])
+        cols = sorted(set(rng.integers(0, n, n_cols).tolist()) | {n - 1})
+        for s in cols:
+            page = int(x.block_table[r, s // 64])
+            kd = torch_e4m3_decode(x.kv_pages[page, s % 64])
+            total = Fraction(0)
+            for h in range(32):
+                dot = sum((Fraction(float(qd[h, d])) * Fraction(float(kd[d])) for d in range(128)),
+                          Fraction(0))
+                if dot > 0:
+                    total += Fraction(float(x.weights[t, h])) * dot
+            want = np.float32(float(Fraction(float(x.k_scales[page, s % 64])) * total))
+            ulp = np.spacing(np.float32(abs(want))) if want != 0 else np.float32(1e-45)
+            if not abs(float(got[t, s]) - float(want)) <= float(ulp):
+                fails.append(f"prefill logit[{t},{s}] = {got[t, s]}, exact {want}")
+        if not np.all(np.isnan(got[t, n:])):
+            fails.append(f"prefill row {t}: columns past its length were written")
+        at = O.prefill.prefill_logits_at(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                                         x.cu_q, t, np.array(cols))
+        if not np.array_equal(at, got[t, cols]):
+            fails.append(f"prefill_logits_at row {t} differs from prefill_logits")
+    return fails
+
+
 ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_logits_f16_check, pin_bins_golden, pin_bins_exhaustive,
             pin_keys, pin_bins_coarsen_keys, pin_histogram, pin_topk,
             pin_topk_invariants, pin_logits_exact, pin_logits_library,
             pin_logits_paging, pin_error_bound, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
             pin_mxfp4_matches_fp8_path, pin_mxfp4_exact, pin_block_amax8,
-            pin_sort_candidate_blocks, pin_sparse_logits)
+            pin_sort_candidate_blocks, pin_sparse_logits, pin_prefill_decode_case,
+            pin_prefill_exact)

@@ -22,6 +22,11 @@ def fresh_oracle():
     cmod = importlib.util.module_from_spec(cspec)
     cspec.loader.exec_module(cmod)
     mod.candidates = cmod
+    pspec = importlib.util.spec_from_file_location(
+        "oracle.prefill_mutant", os.path.join(os.path.dirname(base.__file__), "prefill.py"))
+    pmod = importlib.util.module_from_spec(pspec)
+    pspec.loader.exec_module(pmod)
+    mod.prefill = pmod
     return mod
 
 
@@ -293,6 +298,39 @@ def m_sparse_block_offset(O):
     O.candidates.sparse_logits = sp
 
 
+def _wrap_prefill(O, fn):
+    orig = O.prefill.prefill_logits
+    O.prefill.prefill_logits = lambda q, kv, ks, w, bt, cu, lens, *a, **k: fn(orig, q, kv, ks, w, bt,
+                                                                               np.asarray(cu), np.asarray(lens),
+                                                                               *a, **k)
+
+
+def m_prefill_tables_reversed(O):
+    # every row reads the pages of the mirror-image request
+    _wrap_prefill(O, lambda f, q, kv, ks, w, bt, cu, lens, *a, **k: f(q, kv, ks, w, bt[::-1], cu, lens,
+                                                                       *a, **k))
+
+
+def m_prefill_request_max_len(O):
+    # every row of a request scores the request's longest visible range
+    def f(orig, q, kv, ks, w, bt, cu, lens, *a, **k):
+        l2 = lens.copy()
+        for r in range(cu.size - 1):
+            if cu[r + 1] > cu[r]:
+                l2[cu[r]:cu[r + 1]] = lens[cu[r]:cu[r + 1]].max()
+        return orig(q, kv, ks, w, bt, cu, l2, *a, **k)
+    _wrap_prefill(O, f)
+
+
+def m_prefill_boundary_row(O):
+    # the first row of every request after the first goes to the request before
+    def f(orig, q, kv, ks, w, bt, cu, lens, *a, **k):
+        c2 = cu.copy()
+        c2[1:-1] += 1
+        return orig(q, kv, ks, w, bt, np.minimum(c2, cu[-1]), lens, *a, **k)
+    _wrap_prefill(O, f)
+
+
 MUTANTS = [
     (m_e4m3_bias, [P.pin_e4m3]),
     (m_e4m3_subnormal, [P.pin_e4m3]),
@@ -324,6 +362,9 @@ MUTANTS = [
     (m_sort_no_identity, [P.pin_sort_candidate_blocks]),
     (m_sort_slot_transform, [P.pin_sort_candidate_blocks]),
     (m_sparse_block_offset, [P.pin_sparse_logits]),
+    (m_prefill_tables_reversed, [P.pin_prefill_decode_case, P.pin_prefill_exact]),
+    (m_prefill_request_max_len, [P.pin_prefill_decode_case, P.pin_prefill_exact]),
+    (m_prefill_boundary_row, [P.pin_prefill_decode_case, P.pin_prefill_exact]),
 ]
 
 
