@@ -16,8 +16,8 @@
  *        (exact top-2048 selector from the histogram, fallback, ties).
  *   [P2] SGLang PR #38944, "[DSV4.1] Enable the two-level candidate
  *        indexer": the sparse paged logits path, amax8_varlen and
- *        sort_candidate_blocks; the SM90 prefill commit (block-scaled E2M1
- *        index-K).
+ *        sort_candidate_blocks; the SM90 prefill commit (ragged extend
+ *        batches scored per request; block-scaled E2M1 index-K).
  *   [P3] vLLM PR #52696, "[Performance][MLA] Use FP16 logits for sparse
  *        indexer": "Summary" and commits (selection on FP16 score keys,
  *        refining only the remaining key bits; FP16 logits; the MXFP4
@@ -298,6 +298,54 @@ idx_status indexer_sparse_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages
                                        const int32_t* context_lens, int32_t rows,
                                        int32_t num_pages, float* logits,
                                        int64_t logits_stride, void* stream);
+
+/*
+ * indexer_prefill_logits -- [P2] the SM90 FP8 prefill commit: indexer
+ * logits of a ragged prefill (extend) batch.  Request r owns rows
+ * cu_q[r] .. cu_q[r+1]-1 (cu_q ascending, cu_q[0] = 0, cu_q[requests] =
+ * tokens; a request may own none).  Row t of request r scores the keys
+ * s < row_lens[t] of r through block_table[r]:
+ *   logits[t][s] = k_scales[page][slot] * sum_h w[t][h] * ReLU(q[t][h] . k_s)
+ * with indexer_logits' formula, FP32 accumulation and output.  For an extend
+ * chunk of n rows appended to a context of L keys (prefix included), causal
+ * visibility is row_lens = L - n + 1 + i for its row i (the decode path's
+ * next_n convention, so a batch of next_n-row requests is a decode call).
+ * Columns >= row_lens[t] are not written; rows feed topk_rows with
+ * context_lens = row_lens.
+ *
+ * q            (device) uint8 [tokens][32][128] E4M3FN, 16-byte aligned
+ * kv_pages     (device) uint8 [num_pages][64][128] E4M3FN, 16-byte aligned
+ * k_scales     (device) float [num_pages][64]
+ * weights      (device) float [tokens][32], 16-byte aligned
+ * block_table  (device) int32 [requests][max_pages]
+ * cu_q         (device) int32 [requests + 1]
+ * row_lens     (device) int32 [tokens], clamped to [0, min(64 max_pages,
+ *              logits_stride)]
+ * logits       (device) float [tokens][logits_stride], 16-byte aligned,
+ *              logits_stride a multiple of 4
+ * requests     1 .. IDX_MAX_REQUESTS;  tokens 1 .. IDX_MAX_ROWS
+ * Errors: IDX_EINVAL (NULL pointer, non-positive size), IDX_EUNSUPPORTED
+ * (limits above), IDX_EALIGN (alignment, stride), IDX_ELAUNCH.
+ */
+idx_status indexer_prefill_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                                  const float* weights, const int32_t* block_table,
+                                  int32_t max_pages, const int32_t* cu_q, int32_t requests,
+                                  int32_t tokens, const int32_t* row_lens, int32_t num_pages,
+                                  float* logits, int64_t logits_stride, void* stream);
+
+/*
+ * indexer_prefill_logits_mxfp4 -- indexer_prefill_logits over packed MXFP4
+ * pages (the block-scaled E2M1 index-K of [P2]'s prefill commit, consumed
+ * by the fp8 x fp4 MFMA directly instead of being unpacked to E4M3 first;
+ * the keys as in indexer_logits_mxfp4).  kv_pages uint8 [num_pages][64][68],
+ * no k_scales; other arguments as above.
+ */
+idx_status indexer_prefill_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages,
+                                        const float* weights, const int32_t* block_table,
+                                        int32_t max_pages, const int32_t* cu_q,
+                                        int32_t requests, int32_t tokens,
+                                        const int32_t* row_lens, int32_t num_pages,
+                                        float* logits, int64_t logits_stride, void* stream);
 
 /*
  * sparse_to_logical -- the selection inside a sparse row as logical key

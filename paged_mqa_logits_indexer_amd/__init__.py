@@ -45,7 +45,7 @@ __all__ = [
     "IndexerError", "KEY_FP32", "KEY_FP16", "NUM_BINS", "CANDIDATE_CAPACITY",
     "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits", "indexer_logits_f16",
     "indexer_logits_mxfp4", "block_amax8", "sort_candidate_blocks", "indexer_sparse_logits",
-    "indexer_sparse_logits_mxfp4",
+    "indexer_sparse_logits_mxfp4", "indexer_prefill_logits", "indexer_prefill_logits_mxfp4",
     "sparse_to_logical",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram", "indexer_status_str",
     "indexer_time_next_call", "hbm_read_probe",
@@ -62,7 +62,7 @@ MXFP4_TOKEN_BYTES = 68
 
 EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp4", "block_amax8",
                     "sort_candidate_blocks", "indexer_sparse_logits", "indexer_sparse_logits_mxfp4",
-                    "sparse_to_logical",
+                    "indexer_prefill_logits", "indexer_prefill_logits_mxfp4", "sparse_to_logical",
                     "topk_workspace_bytes", "topk_rows",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
                     "indexer_time_next_call", "hbm_read_probe")
@@ -120,6 +120,10 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_sparse_logits.restype = ctypes.c_int
     lib.indexer_sparse_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i64, vp]
     lib.indexer_sparse_logits_mxfp4.restype = ctypes.c_int
+    lib.indexer_prefill_logits.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, i64, vp]
+    lib.indexer_prefill_logits.restype = ctypes.c_int
+    lib.indexer_prefill_logits_mxfp4.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, i64, vp]
+    lib.indexer_prefill_logits_mxfp4.restype = ctypes.c_int
     lib.sparse_to_logical.argtypes = [vp, i32, vp, i32, i32, vp, vp]
     lib.sparse_to_logical.restype = ctypes.c_int
     lib.topk_rows_f16.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
@@ -348,6 +352,46 @@ def indexer_sparse_logits(q, kv_pages, k_scales, weights, table, slots, context_
         else:
             st = lib.indexer_sparse_logits(_ptr(q), _ptr(kv_pages), _ptr(k_scales), *tail)
     _check("indexer_sparse_logits_mxfp4" if mx else "indexer_sparse_logits", st)
+
+
+def indexer_prefill_logits(q, kv_pages, k_scales, weights, block_table, cu_q, row_lens, logits,
+                           events=None):
+    """Ragged prefill logits: request r owns rows cu_q[r] .. cu_q[r+1]-1; row t
+    scores keys [0, row_lens[t]) of its request into logits [tokens, stride].
+    With k_scales None, kv_pages are packed MXFP4 tokens
+    (indexer_prefill_logits_mxfp4)."""
+    dev = q.device
+    mx = k_scales is None
+    _need(q, "q", torch.uint8, dev, 3)
+    _need(kv_pages, "kv_pages", torch.uint8, dev, 3)
+    if kv_pages.shape[1:] != ((PAGE_TOKENS, MXFP4_TOKEN_BYTES) if mx else (PAGE_TOKENS, HEAD_DIM)):
+        raise ValueError("kv_pages must be [P, 64, 68] (MXFP4) or [P, 64, 128] with k_scales")
+    if not mx:
+        _need(k_scales, "k_scales", torch.float32, dev, 2)
+    _need(weights, "weights", torch.float32, dev, 2)
+    _rows2(block_table, "block_table", torch.int32, dev)
+    _need(cu_q, "cu_q", torch.int32, dev, 1)
+    _need(row_lens, "row_lens", torch.int32, dev, 1)
+    _need(logits, "logits", torch.float32, dev, 2)
+    tokens = q.shape[0]
+    requests = block_table.shape[0]
+    if tuple(q.shape) != (tokens, HEADS, HEAD_DIM) or tuple(weights.shape) != (tokens, HEADS):
+        raise ValueError(f"q [{tokens}, 32, 128] and weights [{tokens}, 32] (one per row)")
+    if cu_q.shape[0] != requests + 1 or row_lens.shape[0] != tokens:
+        raise ValueError("cu_q must be [requests + 1] and row_lens [tokens]")
+    if logits.shape[0] != tokens or logits.stride(1) != 1:
+        raise ValueError("logits must be [tokens, stride] with unit column stride")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        tail = (_ptr(weights), _ptr(block_table), int(block_table.shape[1]), _ptr(cu_q), int(requests),
+                int(tokens), _ptr(row_lens), int(kv_pages.shape[0]), _ptr(logits), int(logits.stride(0)),
+                _stream_ptr(dev))
+        if mx:
+            st = lib.indexer_prefill_logits_mxfp4(_ptr(q), _ptr(kv_pages), *tail)
+        else:
+            st = lib.indexer_prefill_logits(_ptr(q), _ptr(kv_pages), _ptr(k_scales), *tail)
+    _check("indexer_prefill_logits_mxfp4" if mx else "indexer_prefill_logits", st)
 
 
 def sparse_to_logical(indices, table, out, events=None):

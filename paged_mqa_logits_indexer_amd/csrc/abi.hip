@@ -238,6 +238,54 @@ idx_status indexer_sparse_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages
                             logits, logits_stride, true, stream);
 }
 
+static idx_status prefill_call(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                               const float* weights, const int32_t* block_table, int32_t max_pages,
+                               const int32_t* cu_q, int32_t requests, int32_t tokens, const int32_t* row_lens,
+                               int32_t num_pages, float* logits, int64_t logits_stride, bool mxfp4, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!q || !kv_pages || (!mxfp4 && !k_scales) || !weights || !block_table || !cu_q || !row_lens || !logits)
+    return IDX_EINVAL;
+  if (requests <= 0 || tokens <= 0 || num_pages <= 0 || max_pages <= 0 || logits_stride <= 0) return IDX_EINVAL;
+  if (requests > IDX_MAX_REQUESTS || tokens > IDX_MAX_ROWS) return IDX_EUNSUPPORTED;
+  if (static_cast<int64_t>(requests) * max_pages > INT32_MAX) return IDX_EUNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(kv_pages, 16) || (!mxfp4 && !aligned(k_scales, 4)) || !aligned(weights, 16) ||
+      !aligned(block_table, 4) || !aligned(cu_q, 4) || !aligned(row_lens, 4) || !aligned(logits, 16) ||
+      (logits_stride % 4) != 0)
+    return IDX_EALIGN;
+  pmqa::PrefillArgs a;
+  a.q = q;
+  a.kv_pages = kv_pages;
+  a.k_scales = k_scales;
+  a.weights = weights;
+  a.block_table = block_table;
+  a.cu_q = cu_q;
+  a.row_lens = row_lens;
+  a.logits = logits;
+  a.logits_stride = logits_stride;
+  a.requests = requests;
+  a.tokens = tokens;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  a.k_mxfp4 = mxfp4 ? 1 : 0;
+  return from_hip(pmqa::launch_indexer_prefill_logits(a, static_cast<hipStream_t>(stream), ev));
+}
+
+idx_status indexer_prefill_logits(const uint8_t* q, const uint8_t* kv_pages, const float* k_scales,
+                                  const float* weights, const int32_t* block_table, int32_t max_pages,
+                                  const int32_t* cu_q, int32_t requests, int32_t tokens, const int32_t* row_lens,
+                                  int32_t num_pages, float* logits, int64_t logits_stride, void* stream) {
+  return prefill_call(q, kv_pages, k_scales, weights, block_table, max_pages, cu_q, requests, tokens, row_lens,
+                      num_pages, logits, logits_stride, false, stream);
+}
+
+idx_status indexer_prefill_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages, const float* weights,
+                                        const int32_t* block_table, int32_t max_pages, const int32_t* cu_q,
+                                        int32_t requests, int32_t tokens, const int32_t* row_lens,
+                                        int32_t num_pages, float* logits, int64_t logits_stride, void* stream) {
+  return prefill_call(q, kv_pages, nullptr, weights, block_table, max_pages, cu_q, requests, tokens, row_lens,
+                      num_pages, logits, logits_stride, true, stream);
+}
+
 idx_status sparse_to_logical(const int32_t* indices, int32_t k, const int32_t* table, int32_t kb, int32_t rows,
                              int32_t* out, void* stream) {
   const pmqa::LaunchEvents ev = take_events();

@@ -191,6 +191,26 @@ struct SparseLogitsArgs {
   int32_t k_mxfp4;
 };
 hipError_t launch_indexer_sparse_logits(const SparseLogitsArgs& a, hipStream_t stream, LaunchEvents ev = {});
+
+// Ragged prefill (extend) logits: request r owns rows cu_q[r] .. cu_q[r+1]-1,
+// row t scores keys [0, row_lens[t]) of its request.
+struct PrefillArgs {
+  const uint8_t* q;            // E4M3 [tokens][32][128]
+  const uint8_t* kv_pages;     // E4M3 [num_pages][64][128], or packed MXFP4 tokens [num_pages][64][68]
+  const float* k_scales;       // [num_pages][64] (FP8 only)
+  const float* weights;        // [tokens][32]
+  const int32_t* block_table;  // [requests][max_pages]
+  const int32_t* cu_q;         // [requests + 1]
+  const int32_t* row_lens;     // [tokens]
+  float* logits;               // [tokens][logits_stride]
+  int64_t logits_stride;
+  int32_t requests;
+  int32_t tokens;
+  int32_t num_pages;
+  int32_t max_pages;
+  int32_t k_mxfp4;
+};
+hipError_t launch_indexer_prefill_logits(const PrefillArgs& a, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_block_amax8(const float* scores, int64_t stride, const int32_t* lens, int32_t rows, float* out,
                               int64_t out_stride, int32_t* hist, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_sort_candidate_blocks(const int32_t* blocks, int32_t kb, const int32_t* lens, int32_t rows,

@@ -536,6 +536,163 @@ void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
     if (s_live[i]) dst[i] = s_out[i];
 }
 
+// ---------------------------------------------------------------------------
+// Ragged prefill (extend) logits (SGLang PR #38944, the commit adding an SM90
+// FP8 prefill path): every query row of an extend batch against its own
+// request's keys, scored request by request so one read of a K page serves
+// many rows.  A workgroup takes a tile of kPfTile consecutive rows of one
+// request and a chunk of kPfPages pages; each wave keeps kPfRowsPerWave rows'
+// Q operands and weights in registers and walks every page of the chunk, so
+// the page the first wave brings in reaches the others from the CU's cache.
+// The contraction and epilogue are the decode kernel's (compute_page): a
+// prefill logit is bitwise the decode logit of the same row and key.
+//
+// Tiles are numbered request by request, ceil(rows_r / kPfTile) each; the
+// grid's y extent bounds their count (tokens / kPfTile + requests) and each
+// workgroup finds its request with a wave scan over cu_q.  The x extent (key
+// chunks) is a multiple of 8, so -- workgroups going to the 8 XCDs in turn by
+// linear id -- chunk x of every tile runs on XCD x % 8, and the rows of one
+// request read that chunk's pages from a single L2.
+#ifndef PMQA_PREFILL_WAVES
+#define PMQA_PREFILL_WAVES 4
+#endif
+#ifndef PMQA_PREFILL_PAGES
+#define PMQA_PREFILL_PAGES 8
+#endif
+constexpr int kPfWaves = PMQA_PREFILL_WAVES;
+constexpr int kPfRowsPerWave = 4;
+constexpr int kPfTile = kPfWaves * kPfRowsPerWave;
+constexpr int kPfPages = PMQA_PREFILL_PAGES;
+constexpr int kXcds = 8;
+static_assert(kPfTile <= kWave && (kPfTile & (kPfTile - 1)) == 0, "a tile's rows fit one wave");
+static_assert(kPfPages <= kWave, "page ids of a chunk fit one wave");
+
+struct PrefillTile {
+  int req;      // request of the tile; -1 past the last tile
+  int row0;     // first row of the tile
+  int row_end;  // one past the request's last row (at most tokens)
+};
+
+// Tile y -> request: an inclusive wave scan of ceil(rows_r / kPfTile) over
+// the requests, 64 at a time.  Malformed offsets (decreasing) count as empty
+// requests.  Uniform across the wave.
+__device__ __forceinline__ PrefillTile find_prefill_tile(const int32_t* __restrict__ cu_q, int R, int tokens,
+                                                         int y, int lane) {
+  int base = 0;
+  for (int c = 0; c < R; c += kWave) {
+    const int r = c + lane;
+    const int lo = cu_q[min(r, R)];
+    const int hi = cu_q[min(r + 1, R)];
+    const int t = r < R ? (max(hi - lo, 0) + kPfTile - 1) / kPfTile : 0;
+    int incl = t;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int tot = __shfl(incl, kWave - 1);
+    if (y < base + tot) {
+      const unsigned long long hit = __ballot(base + incl > y);
+      const int l = static_cast<int>(__builtin_ctzll(hit));
+      PrefillTile pt;
+      pt.req = c + l;
+      pt.row0 = __shfl(lo, l) + (y - base - __shfl(incl - t, l)) * kPfTile;
+      pt.row_end = min(__shfl(hi, l), tokens);
+      return pt;
+    }
+    base += tot;
+  }
+  return PrefillTile{-1, 0, 0};
+}
+
+template <int KF>
+__global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void indexer_prefill_logits_kernel(PrefillArgs a) {
+  __shared__ __align__(16) float s_out[kPfTile * kPfPages * kPage];  // [row of tile][page][64]
+  const int tid = threadIdx.x;
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const PrefillTile pt = find_prefill_tile(a.cu_q, a.requests, a.tokens, blockIdx.y, lane);
+  if (pt.req < 0) return;
+  // No row reads past its block-table row or writes past its logits row.
+  const int64_t mk = min(static_cast<int64_t>(a.max_pages) * kPage, a.logits_stride);
+  const int max_keys = static_cast<int>(min(mk, static_cast<int64_t>(INT32_MAX)));
+  // Lane i of every 16-lane group holds the visible length of tile row i
+  // (0 past the request's last row); the tile's key extent is their maximum.
+  const int ri = pt.row0 + (lane & (kPfTile - 1));
+  const bool ri_live = ri >= 0 && ri < pt.row_end;
+  const int ri_len = a.row_lens[min(max(ri, 0), a.tokens - 1)];
+  const int li = ri_live ? min(max(ri_len, 0), max_keys) : 0;
+  int keys_t = li;
+#pragma unroll
+  for (int d = 1; d < kPfTile; d <<= 1) keys_t = max(keys_t, __shfl_xor(keys_t, d));
+  keys_t = __builtin_amdgcn_readfirstlane(keys_t);
+  const int pages_t = (keys_t + kPage - 1) / kPage;
+  const int p0 = static_cast<int>(blockIdx.x) * kPfPages;
+  if (p0 >= pages_t) return;  // uniform over the workgroup
+  const int n_pg = min(kPfPages, pages_t - p0);
+  const int32_t* bt = a.block_table + static_cast<int64_t>(pt.req) * a.max_pages;
+  const int ids = bt[min(p0 + lane, a.max_pages - 1)];
+
+  // This wave's rows: Q operands and head weights (clamped loads; rows past
+  // the request have length 0 and are never written).
+  const int m = lane & 15, g = lane >> 4;
+  RequestRegs<kPfRowsPerWave> rq;
+#pragma unroll
+  for (int j = 0; j < kPfRowsPerWave; ++j) {
+    const int row = pt.row0 + wave * kPfRowsPerWave + j;
+    const bool live = row >= 0 && row < pt.row_end;
+    const int lj = __shfl(li, wave * kPfRowsPerWave + j);
+    rq.len[j] = live ? lj : 0;
+    const int64_t qr = min(max(row, 0), a.tokens - 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        rq.q[j][mb][h] = *reinterpret_cast<const i32x4*>(a.q + (qr * kHeads + mb * 16 + m) * kDim + g * 16 + h * 64);
+      rq.w[j][mb] = *reinterpret_cast<const f32x4*>(a.weights + qr * kHeads + mb * 16 + 4 * g);
+    }
+  }
+
+  auto page_id = [&](int it) {
+    const int id = __builtin_amdgcn_readlane(ids, it);
+    return min(max(id, 0), a.num_pages - 1);
+  };
+  const int lane_off = (lane & 15) * (KF == kKFp8 ? kDim : kMxTokenBytes) + (lane >> 4) * 16;
+  float* s_w = s_out + wave * kPfRowsPerWave * kPfPages * kPage;
+  // Two page buffers: page it + 1 is in flight while page it is computed
+  // (past the last page the last one is issued again, from cache).
+  PageRegs<KF> buf[2];
+  load_page(a.kv_pages, a.k_scales, page_id(0), lane_off, lane, buf[0]);
+  for (int it0 = 0; it0 < n_pg; it0 += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int it = it0 + s;
+      if (it >= n_pg) break;
+      const int nx = it + 1 < n_pg ? it + 1 : n_pg - 1;
+      load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[s ^ 1]);
+      compute_page<kPfRowsPerWave, false, false, KF>(buf[s], p0 + it, it, kPfPages, lane, rq, s_w, nullptr);
+    }
+  }
+
+  // The wave's staged scores leave with 16-byte stores (row offset p0 * 64
+  // and the stride are multiples of 4 floats).  Only this wave wrote them.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < kPfRowsPerWave; ++j) {
+    const int n = max(0, min(rq.len[j] - p0 * kPage, n_pg * kPage));
+    if (n == 0) continue;
+    const int row = pt.row0 + wave * kPfRowsPerWave + j;
+    float* dst = a.logits + static_cast<int64_t>(row) * a.logits_stride + static_cast<int64_t>(p0) * kPage;
+    const float* src = s_w + j * kPfPages * kPage;
+    const int nv = n / 4;
+    for (int i = lane; i < nv; i += kWave)
+      reinterpret_cast<f32x4*>(dst)[i] = reinterpret_cast<const f32x4*>(src)[i];
+    for (int i = nv * 4 + lane; i < n; i += kWave) dst[i] = src[i];
+  }
+}
+
 struct DeviceInfo {
   int cus = 0;
 };
@@ -608,6 +765,20 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
     case 9: return launch_fmt<4, true>(a, grid, p, stream, ev);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_indexer_prefill_logits(const PrefillArgs& a, hipStream_t stream, LaunchEvents ev) {
+  const int64_t chunks = (static_cast<int64_t>(a.max_pages) + kPfPages - 1) / kPfPages;
+  const int64_t gx = (chunks + kXcds - 1) / kXcds * kXcds;
+  const int64_t gy = (static_cast<int64_t>(a.tokens) + kPfTile - 1) / kPfTile + a.requests;
+  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+  if (a.k_mxfp4)
+    launch_kernel(indexer_prefill_logits_kernel<kKMxfp4>, grid, dim3(kPfWaves * kWave), stream, ev.start, ev.stop,
+                  a);
+  else
+    launch_kernel(indexer_prefill_logits_kernel<kKFp8>, grid, dim3(kPfWaves * kWave), stream, ev.start, ev.stop, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_indexer_sparse_logits(const SparseLogitsArgs& a, hipStream_t stream, LaunchEvents ev) {

@@ -226,3 +226,43 @@ def mxfp4_call(lib, **kw):
 def test_mxfp4_logits_rejects_before_launch(lib, kw, status):
     # no k_scales argument: the scales travel inside the 68-byte tokens
     assert mxfp4_call(lib, **kw) == status
+
+
+def prefill_call(lib, mx=False, **kw):
+    args = dict(q=A, kv=A, sc=A, w=A, bt=A, max_pages=4, cu=A, requests=2, tokens=40, lens=A,
+                num_pages=16, logits=A, stride=256, stream=None)
+    args.update(kw)
+    tail = (args["w"], args["bt"], args["max_pages"], args["cu"], args["requests"], args["tokens"],
+            args["lens"], args["num_pages"], args["logits"], args["stride"], args["stream"])
+    if mx:
+        return lib.indexer_prefill_logits_mxfp4(args["q"], args["kv"], *tail)
+    return lib.indexer_prefill_logits(args["q"], args["kv"], args["sc"], *tail)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), IDX_EINVAL),
+    (dict(kv=None), IDX_EINVAL),
+    (dict(cu=None), IDX_EINVAL),
+    (dict(lens=None), IDX_EINVAL),
+    (dict(bt=None), IDX_EINVAL),
+    (dict(logits=None), IDX_EINVAL),
+    (dict(requests=0), IDX_EINVAL),
+    (dict(tokens=0), IDX_EINVAL),
+    (dict(max_pages=0), IDX_EINVAL),
+    (dict(num_pages=-1), IDX_EINVAL),
+    (dict(requests=4097), IDX_EUNSUPPORTED),
+    (dict(tokens=65536), IDX_EUNSUPPORTED),
+    (dict(requests=4096, max_pages=1 << 20), IDX_EUNSUPPORTED),
+    (dict(q=A + 8), IDX_EALIGN),
+    (dict(w=A + 4), IDX_EALIGN),
+    (dict(cu=A + 2), IDX_EALIGN),
+    (dict(logits=A + 4), IDX_EALIGN),
+    (dict(stride=258), IDX_EALIGN),
+])
+def test_prefill_rejects_before_launch(lib, mx, kw, status):
+    assert prefill_call(lib, mx=mx, **kw) == status
+
+
+def test_prefill_needs_scales_for_fp8(lib):
+    assert prefill_call(lib, sc=None) == IDX_EINVAL
