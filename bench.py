@@ -47,6 +47,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA, MI355X
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.json")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.md")
@@ -169,6 +170,8 @@ def main() -> int:
                     help="steps of the same shape with MXFP4 K (indexer_logits_mxfp4)")
     ap.add_argument("--candidate-steps", type=int, default=50,
                     help="steps of the two-level candidate chain on the dense logits")
+    ap.add_argument("--prefill-steps", type=int, default=30,
+                    help="steps of the ragged prefill (extend) logits on prefill/extend")
     ap.add_argument("--candidate-blocks", type=int, default=512,
                     help="8-token blocks the source layer publishes per row")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
@@ -404,6 +407,40 @@ def main() -> int:
                     "note": "publish/select spans include the dispatch gaps between their calls"}
         del am, ah, bsel, table, slots, slens, sparse, ssel, pos, ws_b, ws_s
 
+    # ragged prefill (extend) logits (SGLang PR #38944, SM90 FP8 prefill):
+    # compute-bound, priced against the fp8 MFMA peak
+    pf_out = None
+    if args.prefill_steps > 0:
+        pf_out = {}
+        for pname in ("prefill/extend", "prefill/extend_mxfp4"):
+            print(f"[bench] {pname}: {args.prefill_steps} steps", file=sys.stderr, flush=True)
+            xp = gen.config_inputs(pname)
+            tp = upload(xp)
+            cu = torch.from_numpy(np.ascontiguousarray(xp.cu_q)).to(dev)
+            lgp = torch.empty((xp.rows, xp.logits_stride), dtype=torch.float32, device=dev)
+            pts_pf = []
+            for i in range(args.prefill_steps + 3):
+                e0, e1 = new_events(2)
+                evict()
+                pmqa.indexer_prefill_logits(tp["q"], tp["kv_pages"], tp["k_scales"], tp["weights"],
+                                            tp["block_table"], cu, tp["context_lens"], lgp,
+                                            events=(e0, e1))
+                pts_pf.append((e0, e1))
+            torch.cuda.synchronize()
+            us = [a.elapsed_time(b) * 1e3 for a, b in pts_pf[3:]]
+            pairs = int(xp.context_lens.astype(np.int64).sum())
+            flop = pairs * 2 * 32 * 128
+            pu = float(np.mean(us))
+            pf_out[pname] = {
+                "rows": xp.rows, "row_key_pairs": pairs, "us_mean": round(pu, 3),
+                "us_median": round(pct(us, 50), 3), "mfma_flop": flop,
+                "tflops": round(flop / (pu * 1e-6) / 1e12, 1),
+                "mfma_peak_tflops": FP8_MFMA_PEAK_TFLOPS,
+                "mfma_frac": round(flop / (pu * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
+                "logits_write_bytes": pairs * 4,
+                "logits_write_gbps": round(pairs * 4 / (pu * 1e-6) / 1e9, 1)}
+            del tp, cu, lgp
+
     # practical read ceiling over the same number of bytes as K
     ab = algorithmic_bytes(x)
     probe_src = torch.empty(ab["k"] // 4, dtype=torch.int32, device=dev)
@@ -477,6 +514,8 @@ def main() -> int:
         "mxfp4_k": mx_out,
         # two-level candidate indexer on this workload (SGLang PR #38944)
         "candidate_chain": cand_out,
+        # ragged prefill (extend) logits: 4 requests x 2048 rows, contexts 2K..32K
+        "prefill": pf_out,
         "hbm": {
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),
