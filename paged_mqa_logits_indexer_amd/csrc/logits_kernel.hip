@@ -541,18 +541,25 @@ void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
 // FP8 prefill path): every query row of an extend batch against its own
 // request's keys, scored request by request so one read of a K page serves
 // many rows.  A workgroup takes a tile of kPfTile consecutive rows of one
-// request and a chunk of kPfPages pages; each wave keeps kPfRowsPerWave rows'
-// Q operands and weights in registers and walks every page of the chunk, so
-// the page the first wave brings in reaches the others from the CU's cache.
-// The contraction and epilogue are the decode kernel's (compute_page): a
-// prefill logit is bitwise the decode logit of the same row and key.
+// request; each wave keeps kPfRowsPerWave rows' Q operands and weights in
+// registers and walks the workgroup's pages, so the page the first wave
+// brings in reaches the others from the CU's cache.  The contraction and
+// epilogue are the decode kernel's (compute_page): a prefill logit is
+// bitwise the decode logit of the same row and key.
 //
-// Tiles are numbered request by request, ceil(rows_r / kPfTile) each; the
-// grid's y extent bounds their count (tokens / kPfTile + requests) and each
-// workgroup finds its request with a wave scan over cu_q.  The x extent (key
-// chunks) is a multiple of 8, so -- workgroups going to the 8 XCDs in turn by
-// linear id -- chunk x of every tile runs on XCD x % 8, and the rows of one
-// request read that chunk's pages from a single L2.
+// Grid (splits, tiles).  Tiles are numbered request by request,
+// ceil(rows_r / kPfTile) each; the y extent bounds their count (tokens /
+// kPfTile + requests) and each workgroup finds its request with a wave scan
+// over cu_q.  The `splits` workgroups of a tile divide the tile's pages into
+// contiguous ranges of equal length, so a workgroup's Q is fetched once for a
+// long stream of pages and no workgroup of a short tile sits idle: a grid
+// over (page chunk, tile) would hold mostly workgroups past their tile's last
+// page, and the dispatcher, not the arithmetic, would set the pace.  Tiles are
+// dispatched last to first (in a causal extend batch the longest rows come
+// last), so the short tiles fill in at the end.  `splits` is a multiple of 8:
+// workgroups go to the 8 XCDs in turn by linear id, so split s of every tile
+// runs on XCD s % 8, and neighbouring tiles (whose ranges nearly coincide)
+// read their pages from one L2.
 #ifndef PMQA_PREFILL_WAVES
 #define PMQA_PREFILL_WAVES 4
 #endif
@@ -562,10 +569,10 @@ void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
 constexpr int kPfWaves = PMQA_PREFILL_WAVES;
 constexpr int kPfRowsPerWave = 4;
 constexpr int kPfTile = kPfWaves * kPfRowsPerWave;
-constexpr int kPfPages = PMQA_PREFILL_PAGES;
+constexpr int kPfPages = PMQA_PREFILL_PAGES;  // pages staged in LDS between stores
 constexpr int kXcds = 8;
 static_assert(kPfTile <= kWave && (kPfTile & (kPfTile - 1)) == 0, "a tile's rows fit one wave");
-static_assert(kPfPages <= kWave, "page ids of a chunk fit one wave");
+static_assert(kPfPages <= kWave && (kWave % kPfPages) == 0, "staging groups tile a 64-page window");
 
 struct PrefillTile {
   int req;      // request of the tile; -1 past the last tile
@@ -608,17 +615,18 @@ __device__ __forceinline__ PrefillTile find_prefill_tile(const int32_t* __restri
 template <int KF>
 __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_prefill_logits_kernel(PrefillArgs a) {
-  __shared__ __align__(16) float s_out[kPfTile * kPfPages * kPage];  // [row of tile][page][64]
+  __shared__ __align__(16) float s_out[kPfTile * kPfPages * kPage];  // [row of tile][page of group][64]
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const PrefillTile pt = find_prefill_tile(a.cu_q, a.requests, a.tokens, blockIdx.y, lane);
+  const int y = static_cast<int>(gridDim.y - 1 - blockIdx.y);  // last tile first
+  const PrefillTile pt = find_prefill_tile(a.cu_q, a.requests, a.tokens, y, lane);
   if (pt.req < 0) return;
   // No row reads past its block-table row or writes past its logits row.
   const int64_t mk = min(static_cast<int64_t>(a.max_pages) * kPage, a.logits_stride);
   const int max_keys = static_cast<int>(min(mk, static_cast<int64_t>(INT32_MAX)));
-  // Lane i of every 16-lane group holds the visible length of tile row i
-  // (0 past the request's last row); the tile's key extent is their maximum.
+  // Lane i of every kPfTile-lane group holds the visible length of tile row
+  // i (0 past the request's last row); the tile's key extent is their maximum.
   const int ri = pt.row0 + (lane & (kPfTile - 1));
   const bool ri_live = ri >= 0 && ri < pt.row_end;
   const int ri_len = a.row_lens[min(max(ri, 0), a.tokens - 1)];
@@ -628,11 +636,12 @@ void indexer_prefill_logits_kernel(PrefillArgs a) {
   for (int d = 1; d < kPfTile; d <<= 1) keys_t = max(keys_t, __shfl_xor(keys_t, d));
   keys_t = __builtin_amdgcn_readfirstlane(keys_t);
   const int pages_t = (keys_t + kPage - 1) / kPage;
-  const int p0 = static_cast<int>(blockIdx.x) * kPfPages;
-  if (p0 >= pages_t) return;  // uniform over the workgroup
-  const int n_pg = min(kPfPages, pages_t - p0);
+  // This workgroup's contiguous share [pb, pe) of the tile's pages.
+  const int64_t sp = static_cast<int64_t>(blockIdx.x);
+  const int pb = static_cast<int>(sp * pages_t / gridDim.x);
+  const int pe = static_cast<int>((sp + 1) * pages_t / gridDim.x);
+  if (pb >= pe) return;  // uniform over the workgroup
   const int32_t* bt = a.block_table + static_cast<int64_t>(pt.req) * a.max_pages;
-  const int ids = bt[min(p0 + lane, a.max_pages - 1)];
 
   // This wave's rows: Q operands and head weights (clamped loads; rows past
   // the request have length 0 and are never written).
@@ -654,42 +663,55 @@ void indexer_prefill_logits_kernel(PrefillArgs a) {
     }
   }
 
-  auto page_id = [&](int it) {
-    const int id = __builtin_amdgcn_readlane(ids, it);
-    return min(max(id, 0), a.num_pages - 1);
-  };
   const int lane_off = (lane & 15) * (KF == kKFp8 ? kDim : kMxTokenBytes) + (lane >> 4) * 16;
   float* s_w = s_out + wave * kPfRowsPerWave * kPfPages * kPage;
-  // Two page buffers: page it + 1 is in flight while page it is computed
-  // (past the last page the last one is issued again, from cache).
-  PageRegs<KF> buf[2];
-  load_page(a.kv_pages, a.k_scales, page_id(0), lane_off, lane, buf[0]);
-  for (int it0 = 0; it0 < n_pg; it0 += 2) {
+  // Staged scores of pages [g0, g0 + np) leave with 16-byte stores (the
+  // column offset g0 * 64 and the stride are multiples of 4 floats).  Only
+  // this wave wrote them; its next writes to the staging area come after
+  // these reads in the wave's own LDS order.
+  auto flush = [&](int g0, int np) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int it = it0 + s;
-      if (it >= n_pg) break;
-      const int nx = it + 1 < n_pg ? it + 1 : n_pg - 1;
-      load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[s ^ 1]);
-      compute_page<kPfRowsPerWave, false, false, KF>(buf[s], p0 + it, it, kPfPages, lane, rq, s_w, nullptr);
+    for (int j = 0; j < kPfRowsPerWave; ++j) {
+      const int n = max(0, min(rq.len[j] - g0 * kPage, np * kPage));
+      if (n == 0) continue;
+      const int row = pt.row0 + wave * kPfRowsPerWave + j;
+      float* dst = a.logits + static_cast<int64_t>(row) * a.logits_stride + static_cast<int64_t>(g0) * kPage;
+      const float* src = s_w + j * kPfPages * kPage;
+      const int nv = n / 4;
+      for (int i = lane; i < nv; i += kWave)
+        reinterpret_cast<f32x4*>(dst)[i] = reinterpret_cast<const f32x4*>(src)[i];
+      for (int i = nv * 4 + lane; i < n; i += kWave) dst[i] = src[i];
     }
-  }
+  };
 
-  // The wave's staged scores leave with 16-byte stores (row offset p0 * 64
-  // and the stride are multiples of 4 floats).  Only this wave wrote them.
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+  // Windows of up to 64 pages: lane i of `ids` holds the id of the window's
+  // i-th page.  Two page buffers: page it + 1 is in flight while page it is
+  // computed (past the window's last page the last one is issued again, from
+  // cache).  Every kPfPages pages (and at the window's end) the staged scores
+  // are stored.
+  for (int w0 = pb; w0 < pe; w0 += kWave) {
+    const int nw = min(kWave, pe - w0);
+    const int ids = bt[min(w0 + lane, a.max_pages - 1)];
+    auto page_id = [&](int it) {
+      const int id = __builtin_amdgcn_readlane(ids, it);
+      return min(max(id, 0), a.num_pages - 1);
+    };
+    PageRegs<KF> buf[2];
+    load_page(a.kv_pages, a.k_scales, page_id(0), lane_off, lane, buf[0]);
+    for (int it0 = 0; it0 < nw; it0 += 2) {
 #pragma unroll
-  for (int j = 0; j < kPfRowsPerWave; ++j) {
-    const int n = max(0, min(rq.len[j] - p0 * kPage, n_pg * kPage));
-    if (n == 0) continue;
-    const int row = pt.row0 + wave * kPfRowsPerWave + j;
-    float* dst = a.logits + static_cast<int64_t>(row) * a.logits_stride + static_cast<int64_t>(p0) * kPage;
-    const float* src = s_w + j * kPfPages * kPage;
-    const int nv = n / 4;
-    for (int i = lane; i < nv; i += kWave)
-      reinterpret_cast<f32x4*>(dst)[i] = reinterpret_cast<const f32x4*>(src)[i];
-    for (int i = nv * 4 + lane; i < n; i += kWave) dst[i] = src[i];
+      for (int s = 0; s < 2; ++s) {
+        const int it = it0 + s;
+        if (it >= nw) break;
+        const int nx = it + 1 < nw ? it + 1 : nw - 1;
+        load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[s ^ 1]);
+        const int slot = it % kPfPages;
+        compute_page<kPfRowsPerWave, false, false, KF>(buf[s], w0 + it, slot, kPfPages, lane, rq, s_w, nullptr);
+        if (slot == kPfPages - 1 || it == nw - 1) flush(w0 + it - slot, slot + 1);
+      }
+    }
   }
 }
 
@@ -768,11 +790,18 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
 }
 
 hipError_t launch_indexer_prefill_logits(const PrefillArgs& a, hipStream_t stream, LaunchEvents ev) {
-  const int64_t chunks = (static_cast<int64_t>(a.max_pages) + kPfPages - 1) / kPfPages;
-  const int64_t gx = (chunks + kXcds - 1) / kXcds * kXcds;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const DeviceInfo* info = device_info(dev);
+  if (!info) return hipErrorInvalidDevice;
   const int64_t gy = (static_cast<int64_t>(a.tokens) + kPfTile - 1) / kPfTile + a.requests;
-  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+  if (gy > 65535) return hipErrorInvalidValue;
+  // Workgroups per tile: 8 (one per XCD), more when there are too few tiles
+  // to give every CU two workgroups; never more than a tile can have pages.
+  int64_t splits = kXcds;
+  while (splits * gy < 2 * info->cus && splits < kWave * kXcds) splits *= 2;
+  const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(gy));
   if (a.k_mxfp4)
     launch_kernel(indexer_prefill_logits_kernel<kKMxfp4>, grid, dim3(kPfWaves * kWave), stream, ev.start, ev.stop,
                   a);
