@@ -573,6 +573,8 @@ constexpr int kPfPages = PMQA_PREFILL_PAGES;  // pages staged in LDS between sto
 constexpr int kXcds = 8;
 static_assert(kPfTile <= kWave && (kPfTile & (kPfTile - 1)) == 0, "a tile's rows fit one wave");
 static_assert(kPfPages <= kWave && (kWave % kPfPages) == 0, "staging groups tile a 64-page window");
+constexpr int kRingSlot = kPageBytes / 16;  // 16-byte pieces of one FP8 page
+static_assert(kPfWaves * kWave * 2 == kRingSlot, "two pieces per thread fill a page");
 
 struct PrefillTile {
   int req;      // request of the tile; -1 past the last tile
@@ -616,6 +618,7 @@ template <int KF>
 __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_prefill_logits_kernel(PrefillArgs a) {
   __shared__ __align__(16) float s_out[kPfTile * kPfPages * kPage];  // [row of tile][page of group][64]
+  __shared__ __align__(16) i32x4 s_ring[KF == kKFp8 ? 2 * kRingSlot : 1];  // two FP8 pages, swizzled
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -687,10 +690,8 @@ void indexer_prefill_logits_kernel(PrefillArgs a) {
   };
 
   // Windows of up to 64 pages: lane i of `ids` holds the id of the window's
-  // i-th page.  Two page buffers: page it + 1 is in flight while page it is
-  // computed (past the window's last page the last one is issued again, from
-  // cache).  Every kPfPages pages (and at the window's end) the staged scores
-  // are stored.
+  // i-th page.  Every kPfPages pages (and at the window's end) the staged
+  // scores are stored.
   for (int w0 = pb; w0 < pe; w0 += kWave) {
     const int nw = min(kWave, pe - w0);
     const int ids = bt[min(w0 + lane, a.max_pages - 1)];
@@ -698,18 +699,77 @@ void indexer_prefill_logits_kernel(PrefillArgs a) {
       const int id = __builtin_amdgcn_readlane(ids, it);
       return min(max(id, 0), a.num_pages - 1);
     };
-    PageRegs<KF> buf[2];
-    load_page(a.kv_pages, a.k_scales, page_id(0), lane_off, lane, buf[0]);
-    for (int it0 = 0; it0 < nw; it0 += 2) {
+    if constexpr (KF == kKFp8) {
+      // FP8 pages go through a two-slot LDS ring: the workgroup loads each
+      // page once (two 16-byte pieces per thread, held in registers while
+      // the previous page is computed) and every wave reads its MFMA
+      // operands from LDS -- a quarter of the vector-memory traffic of four
+      // waves loading the page each, and two pages in flight.  Piece q of a
+      // page (key q / 8, 16-byte column q % 8) sits at column
+      // (q % 8) ^ ((key / 2) % 8) of the key's 128-byte LDS row, so the 16
+      // keys an operand read touches spread over all banks.
+      i32x4 gk[2][2];
+      float gs[2];
+      auto gload = [&](int it, int set) {
+        const int pid = page_id(it);
+        const __amdgpu_buffer_rsrc_t kr = range_rsrc(a.kv_pages + static_cast<int64_t>(pid) * kPageBytes, kPageBytes);
+        gk[set][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, tid * 16, 0, 0));
+        gk[set][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, kPageBytes / 2 + tid * 16, 0, 0));
+        const __amdgpu_buffer_rsrc_t sr = range_rsrc(a.k_scales + static_cast<int64_t>(pid) * kPage, kPage * 4);
+        gs[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, 0, 0));
+      };
+      auto lwrite = [&](int set, int slot) {
+        i32x4* ring = s_ring + slot * kRingSlot;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int it = it0 + s;
-        if (it >= nw) break;
-        const int nx = it + 1 < nw ? it + 1 : nw - 1;
-        load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[s ^ 1]);
-        const int slot = it % kPfPages;
-        compute_page<kPfRowsPerWave, false, false, KF>(buf[s], w0 + it, slot, kPfPages, lane, rq, s_w, nullptr);
-        if (slot == kPfPages - 1 || it == nw - 1) flush(w0 + it - slot, slot + 1);
+        for (int ch = 0; ch < 2; ++ch) {
+          const int q = tid + ch * kPfWaves * kWave;
+          const int n = q >> 3;
+          ring[n * 8 + ((q & 7) ^ ((n >> 1) & 7))] = gk[set][ch];
+        }
+      };
+      gload(0, 0);
+      gload(min(1, nw - 1), 1);
+      lwrite(0, 0);
+      lds_barrier();
+      for (int it0 = 0; it0 < nw; it0 += 2) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int it = it0 + s;
+          if (it >= nw) break;
+          PageRegs<kKFp8> pr;
+          const i32x4* ring = s_ring + s * kRingSlot;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int n = kb * 16 + m;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) pr.v[2 * kb + h] = ring[n * 8 + ((g + 4 * h) ^ ((n >> 1) & 7))];
+          }
+          pr.scale = gs[s];
+          gload(min(it + 2, nw - 1), s);
+          const int slot = it % kPfPages;
+          compute_page<kPfRowsPerWave, false, false, KF>(pr, w0 + it, slot, kPfPages, lane, rq, s_w, nullptr);
+          if (slot == kPfPages - 1 || it == nw - 1) flush(w0 + it - slot, slot + 1);
+          lwrite(s ^ 1, s ^ 1);
+          lds_barrier();
+        }
+      }
+    } else {
+      // MXFP4 pages stay in registers: two page buffers, page it + 1 in
+      // flight while page it is computed (past the window's last page the
+      // last one is issued again, from cache).
+      PageRegs<KF> buf[2];
+      load_page(a.kv_pages, a.k_scales, page_id(0), lane_off, lane, buf[0]);
+      for (int it0 = 0; it0 < nw; it0 += 2) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int it = it0 + s;
+          if (it >= nw) break;
+          const int nx = it + 1 < nw ? it + 1 : nw - 1;
+          load_page(a.kv_pages, a.k_scales, page_id(nx), lane_off, lane, buf[s ^ 1]);
+          const int slot = it % kPfPages;
+          compute_page<kPfRowsPerWave, false, false, KF>(buf[s], w0 + it, slot, kPfPages, lane, rq, s_w, nullptr);
+          if (slot == kPfPages - 1 || it == nw - 1) flush(w0 + it - slot, slot + 1);
+        }
       }
     }
   }
