@@ -564,7 +564,7 @@ void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
 #define PMQA_PREFILL_WAVES 4
 #endif
 #ifndef PMQA_PREFILL_PAGES
-#define PMQA_PREFILL_PAGES 8
+#define PMQA_PREFILL_PAGES 16
 #endif
 constexpr int kPfWaves = PMQA_PREFILL_WAVES;
 constexpr int kPfRowsPerWave = 4;
