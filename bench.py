@@ -52,9 +52,10 @@ FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.json")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.md")
 COPY_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
-# The counted kernel: one row per request, histogram on, float32 logits, FP8 K
+# The counted kernel: one row per request, histogram on, float32 logits, FP8 K,
+# the (chunks, B) grid
 # (the long-decode launch; other instantiations in the same run are ignored).
-LOGITS_KERNEL = "indexer_logits_kernel<1, true, false, 0>"
+LOGITS_KERNEL = "indexer_logits_kernel<1, true, false, 0, false>"
 KERNEL_SOURCES = ("paged_mqa_logits_indexer_amd/csrc/logits_kernel.hip",
                   "paged_mqa_logits_indexer_amd/csrc/indexer_common.h")
 
@@ -525,7 +526,7 @@ def main() -> int:
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "indexer_logits_kernel<1, true, false, 0>",
+                     "traffic": traffic, "kernel": "indexer_logits_kernel<1, true, false, 0, false>",
                      "bytes_per_launch": ab["total"]},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }

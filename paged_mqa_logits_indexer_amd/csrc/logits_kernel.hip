@@ -50,6 +50,15 @@ namespace {
 #ifndef PMQA_LOGITS_PAGES_PER_WG
 #define PMQA_LOGITS_PAGES_PER_WG 0  // 0: chosen from the grid shape
 #endif
+#ifndef PMQA_LOGITS_PERSIST
+#define PMQA_LOGITS_PERSIST 1
+#endif
+#ifndef PMQA_LOGITS_PERSIST_PPW
+#define PMQA_LOGITS_PERSIST_PPW 64
+#endif
+#ifndef PMQA_LOGITS_PERSIST_WGS_PER_CU
+#define PMQA_LOGITS_PERSIST_WGS_PER_CU 2
+#endif
 #ifndef PMQA_LOGITS_WAVES_MANY_ROWS
 #define PMQA_LOGITS_WAVES_MANY_ROWS 8
 #endif
@@ -258,24 +267,17 @@ template <int NN>
 constexpr int kWavesPerSimd = NN == 1 ? (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 3 : 2))
                                       : (NN == 2 && kPrefetch == 1 ? 3 : 2);
 
+// One share of the grid: pages [p0_64, p0_64 + pages_per_wg) of request b
+// (the workgroup returns at once if that is past the request's last page).
 template <int NN, bool HIST, bool F16, int KF>
-__global__ __launch_bounds__(kThreadsOf<NN>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
-void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
-  __shared__ int s_hist[HIST ? NN * kBins : 1];
-  __shared__ __align__(16) StageT<F16> s_out[kStageFloats<NN>];  // [NN][pages_per_wg][64] scores
-  // Q in MFMA operand layout, [row][head block][half][lane], and the weights:
-  // fetched once per workgroup and read by every wave from here.
-  __shared__ __align__(16) i32x4 s_q[NN >= 2 ? NN * 4 * kWave : 1];
-  __shared__ __align__(16) float s_w[NN >= 2 ? NN * kHeads : 1];
-
+__device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_wg, int b, int64_t p0_64,
+                                             int* s_hist, StageT<F16>* s_out, i32x4* s_q, float* s_w) {
   constexpr int kWaves = kWavesOf<NN>;
   constexpr int kThreads = kThreadsOf<NN>;
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int b = blockIdx.y;
   const int row0 = b * NN;
-  const int64_t p0_64 = static_cast<int64_t>(blockIdx.x) * pages_per_wg;  // first page
   // No row reads past its block-table row or writes past its logits row.
   const int64_t mk = min(static_cast<int64_t>(a.max_pages) * kPage, a.logits_stride);
   const int max_keys = static_cast<int>(min(mk, static_cast<int64_t>(INT32_MAX)));
@@ -440,6 +442,78 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
       const uint2 v = sh[i];
       if (v.x | v.y) atomicAdd(gh + i, (static_cast<unsigned long long>(v.y) << 32) | v.x);
     }
+  }
+}
+
+// Requests the persistent grid serves (their share counts are prefix-summed
+// in LDS).
+constexpr int kPersistMaxB = 256;
+
+// Grid (chunks, B): workgroup (c, b) computes share c of request b.  With
+// PERSIST the grid is a fixed number of workgroups instead, and the
+// shares that exist -- ceil(pages_b / pages_per_wg) per request, from the
+// rows' lengths -- are numbered request by request and dealt out round
+// robin: with many requests of varied length a (chunks, B) grid is mostly
+// workgroups past their request's end, which the dispatcher has to launch
+// all the same.
+template <int NN, bool HIST, bool F16, int KF, bool PERSIST>
+__global__ __launch_bounds__(kThreadsOf<NN>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
+void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
+  __shared__ int s_hist[HIST ? NN * kBins : 1];
+  __shared__ __align__(16) StageT<F16> s_out[kStageFloats<NN>];  // [NN][pages_per_wg][64] scores
+  // Q in MFMA operand layout, [row][head block][half][lane], and the weights:
+  // fetched once per workgroup and read by every wave from here.
+  __shared__ __align__(16) i32x4 s_q[NN >= 2 ? NN * 4 * kWave : 1];
+  __shared__ __align__(16) float s_w[NN >= 2 ? NN * kHeads : 1];
+  __shared__ int s_pref[PERSIST ? kPersistMaxB + 1 : 1];  // shares of requests < b (persistent grid)
+
+  if constexpr (!PERSIST) {
+    logits_share<NN, HIST, F16, KF>(a, pages_per_wg, blockIdx.y, static_cast<int64_t>(blockIdx.x) * pages_per_wg,
+                                    s_hist, s_out, s_q, s_w);
+    return;
+  }
+  constexpr int kThreads = kThreadsOf<NN>;
+  const int tid = threadIdx.x;
+  const int lane = __lane_id();
+  const int64_t mk = min(static_cast<int64_t>(a.max_pages) * kPage, a.logits_stride);
+  const int max_keys = static_cast<int>(min(mk, static_cast<int64_t>(INT32_MAX)));
+  const int nb = min(a.B, kPersistMaxB);  // the host launches this mode only for B <= kPersistMaxB
+  for (int r = tid; r < nb; r += kThreads) {
+    int keys = 0;
+#pragma unroll
+    for (int j = 0; j < NN; ++j) keys = max(keys, min(max(a.context_lens[r * NN + j], 0), max_keys));
+    const int pages = (keys + kPage - 1) / kPage;
+    s_pref[r + 1] = (pages + pages_per_wg - 1) / pages_per_wg;
+  }
+  if (tid == 0) s_pref[0] = 0;
+  __syncthreads();
+  if (tid < kWave) {
+    int base = 0;
+    for (int c = 0; c < nb; c += kWave) {
+      const int r = c + lane;
+      int incl = r < nb ? s_pref[r + 1] : 0;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+      }
+      if (r < nb) s_pref[r + 1] = base + incl;
+      base += __shfl(incl, kWave - 1);
+    }
+  }
+  __syncthreads();
+  const int total = s_pref[nb];
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // the request whose shares hold `item`: s_pref[b] <= item < s_pref[b + 1]
+    int lo = 0, hi = nb;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= item) lo = mid;
+      else hi = mid;
+    }
+    logits_share<NN, HIST, F16, KF>(a, pages_per_wg, lo, static_cast<int64_t>(item - s_pref[lo]) * pages_per_wg,
+                                    s_hist, s_out, s_q, s_w);
+    __syncthreads();  // LDS of this share is read to the end before the next one writes it
   }
 }
 
@@ -792,19 +866,30 @@ DeviceInfo* device_info(int dev) {
   return &infos[dev];
 }
 
+// The persistent grid is built for one row per request (the decode shape
+// with many requests) and FP8 K; other shapes take the (chunks, B) grid.
 template <int NN, bool HIST, bool F16, int KF>
-hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
-  launch_kernel(indexer_logits_kernel<NN, HIST, F16, KF>, grid, dim3(kThreadsOf<NN>), stream, ev.start, ev.stop, a,
-                pages_per_wg);
+hipError_t launch(const LogitsArgs& a, dim3 grid, int pages_per_wg, int persistent, hipStream_t stream,
+                  LaunchEvents ev) {
+  if constexpr (NN == 1 && KF == kKFp8) {
+    if (persistent) {
+      launch_kernel(indexer_logits_kernel<NN, HIST, F16, KF, true>, grid, dim3(kThreadsOf<NN>), stream, ev.start,
+                    ev.stop, a, pages_per_wg);
+      return hipGetLastError();
+    }
+  }
+  launch_kernel(indexer_logits_kernel<NN, HIST, F16, KF, false>, grid, dim3(kThreadsOf<NN>), stream, ev.start,
+                ev.stop, a, pages_per_wg);
   return hipGetLastError();
 }
 
 // MXFP4 K is served with float32 logits only.
 template <int NN, bool HIST>
-hipError_t launch_fmt(const LogitsArgs& a, dim3 grid, int pages_per_wg, hipStream_t stream, LaunchEvents ev) {
-  if (a.k_mxfp4) return launch<NN, HIST, false, kKMxfp4>(a, grid, pages_per_wg, stream, ev);
-  if (a.logits_f16) return launch<NN, HIST, true, kKFp8>(a, grid, pages_per_wg, stream, ev);
-  return launch<NN, HIST, false, kKFp8>(a, grid, pages_per_wg, stream, ev);
+hipError_t launch_fmt(const LogitsArgs& a, dim3 grid, int pages_per_wg, int persistent, hipStream_t stream,
+                      LaunchEvents ev) {
+  if (a.k_mxfp4) return launch<NN, HIST, false, kKMxfp4>(a, grid, pages_per_wg, persistent, stream, ev);
+  if (a.logits_f16) return launch<NN, HIST, true, kKFp8>(a, grid, pages_per_wg, persistent, stream, ev);
+  return launch<NN, HIST, false, kKFp8>(a, grid, pages_per_wg, persistent, stream, ev);
 }
 
 }  // namespace
@@ -833,18 +918,30 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   ppw = ppw < 4 ? 4 : (ppw > kMaxPagesPerWg ? kMaxPagesPerWg : ppw);
   const int64_t chunks = (a.max_pages + ppw - 1) / ppw;
   if (chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
+  dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
+  // Many requests (lengths usually varied): a persistent grid of a few
+  // workgroups per CU deals out the shares that exist.
+  int persistent = 0;
+#if PMQA_LOGITS_PERSIST
+  if (a.next_n == 1 && !a.k_mxfp4 && a.B >= 32 && a.B <= kPersistMaxB) {
+    ppw = PMQA_LOGITS_PERSIST_PPW;  // equal shares dealt round robin: longer ones cost no balance
+    const int64_t upper = (a.max_pages + ppw - 1) / ppw * a.B;
+    const int64_t wgs = static_cast<int64_t>(PMQA_LOGITS_PERSIST_WGS_PER_CU) * info->cus;
+    grid = dim3(static_cast<unsigned>(upper < wgs ? upper : wgs), 1);
+    persistent = 1;
+  }
+#endif
   const int p = static_cast<int>(ppw);
   if (a.k_mxfp4 && a.logits_f16) return hipErrorInvalidValue;
   switch (a.next_n * 2 + (hist ? 1 : 0)) {
-    case 2: return launch_fmt<1, false>(a, grid, p, stream, ev);
-    case 3: return launch_fmt<1, true>(a, grid, p, stream, ev);
-    case 4: return launch_fmt<2, false>(a, grid, p, stream, ev);
-    case 5: return launch_fmt<2, true>(a, grid, p, stream, ev);
-    case 6: return launch_fmt<3, false>(a, grid, p, stream, ev);
-    case 7: return launch_fmt<3, true>(a, grid, p, stream, ev);
-    case 8: return launch_fmt<4, false>(a, grid, p, stream, ev);
-    case 9: return launch_fmt<4, true>(a, grid, p, stream, ev);
+    case 2: return launch_fmt<1, false>(a, grid, p, persistent, stream, ev);
+    case 3: return launch_fmt<1, true>(a, grid, p, persistent, stream, ev);
+    case 4: return launch_fmt<2, false>(a, grid, p, persistent, stream, ev);
+    case 5: return launch_fmt<2, true>(a, grid, p, persistent, stream, ev);
+    case 6: return launch_fmt<3, false>(a, grid, p, persistent, stream, ev);
+    case 7: return launch_fmt<3, true>(a, grid, p, persistent, stream, ev);
+    case 8: return launch_fmt<4, false>(a, grid, p, persistent, stream, ev);
+    case 9: return launch_fmt<4, true>(a, grid, p, persistent, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }
