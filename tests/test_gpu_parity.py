@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import gen
+import paged_mqa_logits_indexer_amd as pmqa
 import oracle as O
 from tests import oracle_pins as P
 from tests.gpu_harness import (DEV, PATHS, DevInputs, announce, check_hist, check_logits,
@@ -137,6 +138,41 @@ def test_zero_length_and_tiny_rows(gpu):
     check_logits(y, got2)
     check_padding(y, got2, INF)
     check_hist(y.context_lens, got2, h2.cpu().numpy())
+
+
+def test_many_requests_persistent_grid(gpu):
+    """B >= 32 one-row requests take the persistent grid (64-page shares
+    dealt round robin from the lengths): element by element against the
+    oracle with empty, tiny and multi-share rows, and bitwise against the
+    same requests scored by two calls of 20 (the (chunks, B) grid)."""
+    rng = np.random.default_rng(4040)
+    lens = rng.integers(0, 9000, 40)
+    lens[:6] = [0, 1, 63, 64, 4096, 8193]  # empty, one key, page edges, share edges
+    x = gen.make_indexer_inputs("persist40", 40, 1, lens.tolist(), 43, logits_stride=9216)
+    d = DevInputs(x)
+    announce(f"indexer_logits persistent grid B=40 lens={x.context_lens.tolist()}")
+    lg, h = d.run(with_hist=True, fill=INF)
+    got = lg.cpu().numpy()
+    check_logits(x, got)
+    check_padding(x, got, INF)
+    check_hist(x.context_lens, got, h.cpu().numpy())
+    for key in (O.KEY_FP32, O.KEY_FP16):
+        idx = topk(lg, h, d.lens, 2048, key)
+        check_topk(idx.cpu().numpy(), got, x.context_lens, 2048, key)
+    # the same requests in two halves of 20: the (chunks, B) grid
+    halves = []
+    for r0 in (0, 20):
+        lg2 = d.new_logits(INF)
+        h2 = d.new_hist()
+        sl = slice(r0, r0 + 20)
+        pmqa.indexer_logits(d.q[sl].contiguous(), d.kv, d.sc, d.w[sl].contiguous(), d.bt[sl].contiguous(),
+                            d.lens[sl].contiguous(), 1, lg2[sl], h2[sl])
+        halves.append((lg2[sl], h2[sl]))
+    torch.cuda.synchronize()
+    got2 = torch.cat([a for a, _ in halves]).cpu().numpy()
+    h_2 = torch.cat([b for _, b in halves]).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), got2.view(np.uint32)), "persistent grid differs from the static grid"
+    assert np.array_equal(h.cpu().numpy(), h_2)
 
 
 def test_histogram_off_is_bitwise_identical_and_counts_accumulate(gpu):
