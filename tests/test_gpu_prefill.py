@@ -152,3 +152,31 @@ def test_prefill_extend_workload(gpu, name):
         assert np.array_equal(got[i, :n].view(np.uint32), dec[i, :n].view(np.uint32)), \
             f"row {t}: prefill logits differ from the decode logits of the same row"
     check_rows(x, got, rows, sample=256, seed=3)
+
+
+@pytest.mark.parametrize("kfmt", ["fp8", "mxfp4"])
+def test_prefill_long_ranges_cross_page_windows(gpu, kfmt):
+    """A request of 1040 rows over a 48000-key prefix next to a small one:
+    each of a tile's 8 workgroups walks about 96 pages, more than one
+    64-page window of page ids, with the staging flushed every 16 pages.
+    Sampled rows bitwise against the decode kernel, and within tolerance of
+    the oracle at sampled keys; columns past each row stay untouched."""
+    x = gen.make_prefill_inputs(f"pf_long_{kfmt}", [1040, 7], [48000, 300], 91, kfmt=kfmt)
+    pd = PrefillDev(x)
+    announce(f"indexer_prefill_logits long ranges {kfmt} rows={x.rows}")
+    lg = pd.run(gpu)
+    rows = np.array([0, 1, 15, 16, 517, 1023, 1038, 1039, 1040, 1046])
+    got = lg.index_select(0, torch.from_numpy(rows).to(DEV)).cpu().numpy()
+    q, w, bt, lens = _decode_of_rows(x, pd.d, rows)
+    dec = torch.full((rows.size, x.logits_stride), SENT, dtype=torch.float32, device=DEV)
+    if pd.d.sc is None:
+        gpu.indexer_logits_mxfp4(q, pd.d.kv, w, bt, lens, 1, dec, None)
+    else:
+        gpu.indexer_logits(q, pd.d.kv, pd.d.sc, w, bt, lens, 1, dec, None)
+    torch.cuda.synchronize()
+    dec = dec.cpu().numpy()
+    for i, t in enumerate(rows):
+        n = int(x.context_lens[t])
+        assert np.array_equal(got[i, :n].view(np.uint32), dec[i, :n].view(np.uint32)), \
+            f"row {t}: prefill logits differ from the decode logits of the same row"
+    check_rows(x, got, rows, sample=200, seed=7)
