@@ -21,9 +21,10 @@
 //                  output, the candidates of b* to LDS, where a radix select
 //                  on the remaining key bits finishes the row.
 //   longer rows:
-//   [hist == NULL] topk_zero_hist + topk_hist: build the row histograms in
-//                  the workspace (the first pass the producer's fused
-//                  histogram normally replaces)
+//   [hist == NULL] topk_hist: build the row histograms in the workspace
+//                  (the first pass the producer's fused histogram normally
+//                  replaces); every call leaves them zero for the next one,
+//                  as the finish pass clears the bins it reads
 //   topk_collect   one 256-thread workgroup per 4096-score chunk: b* from the
 //                  histogram (requested together with the chunk's scores),
 //                  then one 64-bit atomic add on the row's counter pair
@@ -303,16 +304,6 @@ struct ThreadScores {
 };
 
 // ---------------------------------------------------------------------------
-// Clears the histograms (and counter pairs) of the rows.
-__global__ void topk_zero_hist_kernel(int* hist, unsigned long long* count, int rows) {
-  const int64_t n = static_cast<int64_t>(rows) * kBins;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    hist[i] = 0;
-    if (i < 2 * rows) count[i] = 0ull;
-  }
-}
-
 // Histogram of each row's live non-NaN scores, added to hist_out.
 template <bool F16>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restrict__ logits,
@@ -329,13 +320,24 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
   const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
   const int s1 = min(len, s0 + kChunk);
   constexpr int kPerVec = F16 ? 8 : 4;  // scores per 16-byte load
-  for (int s = s0 + threadIdx.x * kPerVec; s < s1; s += kThreads * kPerVec) {
-    // In bounds: s < len <= stride, s and the stride multiples of kPerVec.
-    const i32x4 v = *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s) * (F16 ? 2 : 4));
+  constexpr int kVecs = kChunk / (kThreads * kPerVec);
+  // All of a thread's loads are requested before any is binned.  In bounds:
+  // a vector starting at s < len <= stride ends inside the row (s and the
+  // stride are multiples of kPerVec); past the chunk's end the chunk's first
+  // vector is read again and not binned.
+  i32x4 v[kVecs];
+#pragma unroll
+  for (int u = 0; u < kVecs; ++u) {
+    const int s = s0 + (u * kThreads + static_cast<int>(threadIdx.x)) * kPerVec;
+    v[u] = *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s < s1 ? s : s0) * (F16 ? 2 : 4));
+  }
+#pragma unroll
+  for (int u = 0; u < kVecs; ++u) {
+    const int s = s0 + (u * kThreads + static_cast<int>(threadIdx.x)) * kPerVec;
 #pragma unroll
     for (int e = 0; e < kPerVec; ++e) {
       if (s + e < s1) {
-        const uint32_t hb = half_bits_of<F16>(v, e);
+        const uint32_t hb = half_bits_of<F16>(v[u], e);
         if (!f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
       }
     }
@@ -865,6 +867,9 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
   const int hv[2] = {h.x, h.y};
   const Threshold th = threshold_bin<kRefineThreads, 2>(hv, k, sh.red);
   const int bstar = th.bin;
+  if (hist == ws.hist) {  // built by this call (no histogram given): the next call starts from zero
+    *reinterpret_cast<int2*>(ws.hist + static_cast<int64_t>(row) * kBins + 2 * tid) = make_int2(0, 0);
+  }
   if (tid == 0) {  // the next call starts from zero
     ws.count[2 * row] = 0ull;
     ws.count[2 * row + 1] = 0ull;
@@ -963,15 +968,16 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents 
   hipEvent_t start = ev.start;  // recorded by the first kernel of the call
   const int32_t* hist = a.hist;
   if (hist == nullptr) {
-    launch_kernel(topk_zero_hist_kernel, dim3(min(1024, (a.rows * kBins + 255) / 256)), dim3(256), stream,
-                  start, nullptr, ws.hist, ws.count, a.rows);
-    start = nullptr;
+    // The workspace histograms are zero (at allocation, then left so by the
+    // finish pass); ones that are not make the counts contradict b*, and
+    // the row is selected from scratch.
     if (a.logits_f16)
-      launch_kernel(topk_hist_kernel<true>, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
+      launch_kernel(topk_hist_kernel<true>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
                     a.logits_stride, a.context_lens, ws.hist);
     else
-      launch_kernel(topk_hist_kernel<false>, grid, dim3(kThreads), stream, nullptr, nullptr, a.logits,
+      launch_kernel(topk_hist_kernel<false>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
                     a.logits_stride, a.context_lens, ws.hist);
+    start = nullptr;
     hist = ws.hist;
   }
   if (a.logits_f16) launch_chunked<IDX_KEY_FP16, true>(a, ws, hist, chunks, stream, start, ev.stop);

@@ -282,6 +282,26 @@ def test_topk_row_of_more_than_512_chunks(gpu):
         check_topk(idx.cpu().numpy(), buf, lens, 2048, key)
 
 
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+def test_topk_without_histogram_reuses_its_workspace(gpu, key):
+    """hist=NULL on rows longer than 8192: the selector builds its histograms
+    in the workspace, and every call leaves them zero for the next.  A
+    workspace that starts as garbage, then calls on different rows through
+    the same workspace: each result exact."""
+    rng = np.random.default_rng(606)
+    n = 40000
+    ws = torch.full((gpu.topk_workspace_bytes(3, n, 2048),), 0xA5, dtype=torch.uint8, device=DEV)
+    for call in range(4):
+        rows = [rng.standard_normal(n).astype(np.float32) * np.float32(2.0 ** call),
+                np.round(rng.standard_normal(n - 1001) * 3).astype(np.float32),  # many ties
+                np.where(rng.random(n - 7) < 0.01, np.float32(40.0), rng.standard_normal(n - 7)).astype(np.float32)]
+        buf, lens = _scores_dev(rows)
+        s_, ln = torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV)
+        announce(f"topk_rows hist=NULL workspace reuse call={call} key={key}")
+        idx = topk(s_, None, ln, 2048, key, workspace=ws)
+        check_topk(idx.cpu().numpy(), buf, lens, 2048, key)
+
+
 def test_calls_replay_in_a_hip_graph(gpu):
     # one row of one selector chunk, one of several (the arrival counters of
     # a replayed launch must start from zero again); the workspace starts
