@@ -158,9 +158,10 @@ size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
  *             256-B aligned, zero-filled before its first use; every call
  *             leaves it ready for the next (also when a captured graph
  *             replays the call), so it is zeroed once.  Should it not start
- *             zeroed, rows whose histogram is exact are still exact (their
- *             counts then disagree with the histogram and they are selected
- *             from scratch).  Calls that share a workspace must be ordered on
+ *             zeroed, results stay exact: the counts found in the scores then
+ *             disagree with the counter pairs or with the histogram built on
+ *             top of the garbage (hist == NULL), and those rows are selected
+ *             from scratch.  Calls that share a workspace must be ordered on
  *             one stream.
  */
 idx_status topk_rows(const float* logits, int64_t logits_stride,
