@@ -344,3 +344,40 @@ def test_calls_replay_in_a_hip_graph(gpu):
         gpu.topk_rows(lg, h, d.lens, k, O.KEY_FP32, idx2, ws)  # same workspace, eager
         torch.cuda.synchronize()
         assert np.array_equal(np.sort(idx2.cpu().numpy(), axis=1), ref_idx)
+
+
+def test_topk_without_histogram_replays_in_a_hip_graph(gpu):
+    """hist=NULL on long rows in a captured graph: the selector's own
+    histogram lives in the workspace, which each call leaves zero, so every
+    replay (with eager calls on the same workspace between them) is exact."""
+    rng = np.random.default_rng(707)
+    rows = [rng.standard_normal(30000).astype(np.float32),
+            np.round(rng.standard_normal(20001) * 4).astype(np.float32)]
+    buf, lens = _scores_dev(rows)
+    s_, ln = torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV)
+    k = 2048
+    ws = torch.full((gpu.topk_workspace_bytes(2, buf.shape[1], k),), 0xA5, dtype=torch.uint8, device=DEV)
+    idx = torch.full((2, k), -7, dtype=torch.int32, device=DEV)
+    announce("topk_rows hist=NULL eager before capture")
+    gpu.topk_rows(s_, None, ln, k, O.KEY_FP16, idx, ws)
+    torch.cuda.synchronize()
+    check_topk(idx.cpu().numpy(), buf, lens, k, O.KEY_FP16)
+    ref = np.sort(idx.cpu().numpy(), axis=1)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            gpu.topk_rows(s_, None, ln, k, O.KEY_FP16, idx, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        announce(f"hist=NULL graph replay {rep}")
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), ref)
+        idx2 = torch.full((2, k), -7, dtype=torch.int32, device=DEV)
+        gpu.topk_rows(s_, None, ln, k, O.KEY_FP16, idx2, ws)  # same workspace, eager
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(idx2.cpu().numpy(), axis=1), ref)
