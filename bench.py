@@ -495,6 +495,7 @@ def main() -> int:
         del src, dst
 
     mean_logits = float(np.mean(lt))
+    mfma_flop = int(x.context_lens.astype(np.int64).sum()) * 2 * 32 * 128
     achieved = ab["total"] / (mean_logits * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -553,6 +554,10 @@ def main() -> int:
             "read_probe_us": round(probe_us, 3),
             "read_probe_gbps": round(ab["k"] / (probe_us * 1e-6) / 1e9, 1),
         },
+        # MFMA work of the same launch: 2*32*128 flop per (row, live key)
+        "mfma": {"flop_per_launch": mfma_flop,
+                 "tflops": round(mfma_flop / (mean_logits * 1e-6) / 1e12, 1),
+                 "frac_of_fp8_peak": round(mfma_flop / (mean_logits * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "indexer_logits_kernel<1, true, false, 0, false>",
