@@ -623,51 +623,127 @@ __device__ uint32_t select_col_lds(RefineShared& sh, int n, uint32_t T, int need
 }
 
 // Append this thread's column to the output through a block-wide LDS counter.
+// Lanes of the wave that are not active (a per-thread loop that ended) take
+// no part: the first active lane reserves the places.
 __device__ __forceinline__ void emit(RefineShared& sh, int32_t* out, int k, bool take, int col) {
   const uint64_t m = __ballot(take);
   if (!m) return;
+  const int leader = __builtin_amdgcn_readfirstlane(static_cast<int>(__lane_id()));
   int pos = 0;
-  if (__lane_id() == 0) pos = atomicAdd(&sh.out_pos, __popcll(m));
-  pos = __builtin_amdgcn_readlane(pos, 0) + lanes_below(m);
+  if (static_cast<int>(__lane_id()) == leader) pos = atomicAdd(&sh.out_pos, __popcll(m));
+  pos = __builtin_amdgcn_readfirstlane(pos) + lanes_below(m);
   if (take && pos < k) out[pos] = col;
 }
 
 // Exact selection over the whole row: a stale histogram, or a threshold bin
-// with more candidates than the capacity.
+// with more candidates than the capacity.  Thread t owns the contiguous
+// columns [t * seg, (t + 1) * seg) (seg a multiple of 8, so its 16-byte
+// vectors are aligned for float and half rows alike) and reads them with
+// 16-byte loads, four in flight; after the digit passes one block scan of the
+// threads' tie counts ranks the ties at the final key in column order.
+template <bool F16>
+struct SegmentReader {
+  static constexpr int kPerVec = F16 ? 8 : 4;
+  static constexpr int kBatch = 4;  // vectors in flight per thread
+  const char* x;
+  int begin, end;  // this thread's columns
+  __device__ SegmentReader(const void* row, int len) : x(static_cast<const char*>(row)) {
+    const int seg = ((len + kRefineThreads - 1) / kRefineThreads + 7) / 8 * 8;
+    begin = min(len, static_cast<int>(threadIdx.x) * seg);
+    end = min(len, begin + seg);
+  }
+  // f(column, key, live) for every column of the segment, in column order.
+  // A vector that starts below end starts below len <= stride and ends
+  // inside the row (the stride is a multiple of kPerVec); vectors of a batch
+  // past the segment read its first vector again and are not visited.
+  template <int KEY, typename F>
+  __device__ void for_each(F&& f) const {
+    for (int s0 = begin; s0 < end; s0 += kBatch * kPerVec) {
+      i32x4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int s = s0 + u * kPerVec;
+        v[u] = *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s < end ? s : begin) * (F16 ? 2 : 4));
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+        for (int e = 0; e < kPerVec; ++e) {
+          const int s = s0 + u * kPerVec + e;
+          if (s < end) {
+            uint32_t key;
+            bool live;
+            if constexpr (F16) {
+              const uint32_t hb = half_bits_of<true>(v[u], e);
+              key = key_f16(hb);
+              live = !f16_is_nan(hb);
+            } else {
+              const float val = __int_as_float(v[u][e]);
+              key = score_key<KEY>(val);
+              live = val == val;
+            }
+            f(s, key, live);
+          }
+        }
+      }
+    }
+  }
+};
+
+// hist[d] += 1 for every active lane with `act`.  With AGGREGATE the lanes
+// that share the first such lane's digit add their count with one atomic:
+// the top bytes of FP32 keys are sign and exponent, so a row of scores in one
+// exponent range would otherwise queue 64 increments of one LDS word per
+// instruction (unit-regime verify rows: 73 -> 64 us); FP16 keys measured
+// faster without it.
+template <bool AGGREGATE>
+__device__ __forceinline__ void digit_add(int* hist, bool act, uint32_t d) {
+  if constexpr (!AGGREGATE) {
+    if (act) atomicAdd(&hist[d], 1);
+    return;
+  }
+  const uint64_t m = __ballot(act);
+  if (!m) return;
+  const int l = static_cast<int>(__builtin_ctzll(m));
+  const uint32_t dl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(d), l));
+  const uint64_t same = __ballot(act && d == dl);
+  if (static_cast<int>(__lane_id()) == l) atomicAdd(&hist[dl], static_cast<int>(__popcll(same)));
+  if (act && d != dl) atomicAdd(&hist[d], 1);
+}
+
 template <int KEY, bool F16>
 __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, int len, int k,
                                  int32_t* __restrict__ out) {
   constexpr int kKey = F16 ? IDX_KEY_FP16 : KEY;
-  int cnt = 0;
-  for (int s = threadIdx.x; s < len; s += kRefineThreads) {
-    uint32_t key;
-    cnt += score_at<KEY, F16>(x, s, &key) ? 1 : 0;
-  }
-  const int n = block_sum<kRefineThreads>(cnt, sh.red);
+  constexpr int kKeyBits = kKey == IDX_KEY_FP32 ? 32 : 16;
+  const SegmentReader<F16> rd(x, len);
+  // Pass 1: the live count and the histogram of the top key digit.
+  for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
   if (threadIdx.x == 0) sh.out_pos = 0;
   lds_barrier();
+  int cnt = 0;
+  rd.template for_each<KEY>([&](int, uint32_t key, bool live) {
+    cnt += live ? 1 : 0;
+    digit_add<kKey == IDX_KEY_FP32>(sh.digit_hist, live, key >> (kKeyBits - 8));
+  });
+  const int n = block_sum<kRefineThreads>(cnt, sh.red);  // its barriers also publish digit_hist
   if (n <= k) {
-    for (int s0 = 0; s0 < len; s0 += kRefineThreads) {
-      const int s = s0 + threadIdx.x;
-      uint32_t key;
-      emit(sh, out, k, s < len && score_at<KEY, F16>(x, s, &key), s);
-    }
+    rd.template for_each<KEY>([&](int s, uint32_t, bool live) { emit(sh, out, k, live, s); });
     lds_barrier();
     for (int i = n + threadIdx.x; i < k; i += kRefineThreads) out[i] = -1;
     return;
   }
-  constexpr int kKeyBits = kKey == IDX_KEY_FP32 ? 32 : 16;
   uint32_t prefix = 0u, fixed = 0u;
   int need = k;
   for (int shift = kKeyBits - 8; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
-    lds_barrier();
-    for (int s = threadIdx.x; s < len; s += kRefineThreads) {
-      uint32_t key;
-      if (!score_at<KEY, F16>(x, s, &key)) continue;
-      if (((key ^ prefix) & fixed) == 0u) atomicAdd(&sh.digit_hist[(key >> shift) & 0xFFu], 1);
+    if (shift != kKeyBits - 8) {
+      for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
+      lds_barrier();
+      rd.template for_each<KEY>([&](int, uint32_t key, bool live) {
+        digit_add<kKey == IDX_KEY_FP32>(sh.digit_hist, live && ((key ^ prefix) & fixed) == 0u, (key >> shift) & 0xFFu);
+      });
+      lds_barrier();
     }
-    lds_barrier();
     int before = 0;
     int in_bin = 0;
     const int d = pick_digit(sh, need, &before, &in_bin);
@@ -676,21 +752,17 @@ __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, i
     fixed |= 0xFFu << shift;
   }
   const uint32_t T = prefix;
-  // Keys above T, then the `need` lowest columns with key == T, in column order.
-  int taken_ties = 0;
-  for (int s0 = 0; s0 < len; s0 += kRefineThreads) {
-    const int s = s0 + threadIdx.x;
-    bool above = false, tie = false;
-    uint32_t key;
-    if (s < len && score_at<KEY, F16>(x, s, &key)) {
-      above = key > T;
-      tie = key == T;
-    }
-    int slice_ties = 0;
-    const int rank = taken_ties + block_excl_scan<kRefineThreads>(tie ? 1 : 0, sh.red, &slice_ties);
-    emit(sh, out, k, above || (tie && rank < need), s);
-    taken_ties += slice_ties;
-  }
+  // Keys above T, then the `need` lowest columns with key == T: a thread's
+  // ties come after those of every lower thread.
+  int my_ties = 0;
+  rd.template for_each<KEY>([&](int, uint32_t key, bool live) { my_ties += (live && key == T) ? 1 : 0; });
+  int all_ties = 0;
+  int rank = block_excl_scan<kRefineThreads>(my_ties, sh.red, &all_ties);
+  rd.template for_each<KEY>([&](int s, uint32_t key, bool live) {
+    const bool tie = live && key == T;
+    emit(sh, out, k, (live && key > T) || (tie && rank < need), s);
+    rank += tie ? 1 : 0;
+  });
 }
 
 // Counts confirm b* when the columns above it fall short of k and those in it
