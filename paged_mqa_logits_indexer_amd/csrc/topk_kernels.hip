@@ -711,6 +711,9 @@ __device__ __forceinline__ void digit_add(int* hist, bool act, uint32_t d) {
   if (act && d != dl) atomicAdd(&hist[d], 1);
 }
 
+__device__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt, int n_eq,
+                                  int first_free, bool column_order);
+
 template <int KEY, bool F16>
 __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, int len, int k,
                                  int32_t* __restrict__ out) {
@@ -750,6 +753,29 @@ __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, i
     need -= before;
     prefix |= static_cast<uint32_t>(d) << shift;
     fixed |= 0xFFu << shift;
+    if (shift > 0 && in_bin <= kCandCap) {
+      // The keys that share the prefix fit the LDS buffer: one pass emits the
+      // keys above the prefix and gathers these candidates, and the row is
+      // finished in LDS as for a confirmed threshold bin.
+      if (threadIdx.x == 0) sh.small_n = 0;
+      lds_barrier();
+      rd.template for_each<KEY>([&](int s, uint32_t key, bool live) {
+        emit(sh, out, k, live && (key & fixed) > prefix, s);
+        const bool cand = live && (key & fixed) == prefix;
+        const uint64_t m = __ballot(cand);
+        if (m) {
+          const int leader = __builtin_amdgcn_readfirstlane(static_cast<int>(__lane_id()));
+          int pos = 0;
+          if (static_cast<int>(__lane_id()) == leader) pos = atomicAdd(&sh.small_n, __popcll(m));
+          pos = __builtin_amdgcn_readfirstlane(pos) + lanes_below(m);
+          if (cand) sh.cand[pos] = uint2{key, static_cast<uint32_t>(s)};
+        }
+      });
+      lds_barrier();
+      const int n_above = k - need;
+      finish_candidates(sh, out, k, n_above, in_bin, n_above, false);
+      return;
+    }
   }
   const uint32_t T = prefix;
   // Keys above T, then the `need` lowest columns with key == T: a thread's

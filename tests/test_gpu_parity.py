@@ -381,3 +381,25 @@ def test_topk_without_histogram_replays_in_a_hip_graph(gpu):
         gpu.topk_rows(s_, None, ln, k, O.KEY_FP16, idx2, ws)  # same workspace, eager
         torch.cuda.synchronize()
         assert np.array_equal(np.sort(idx2.cpu().numpy(), axis=1), ref)
+
+
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+def test_topk_fallback_overflow_shapes(gpu, key):
+    """Threshold bins over the 8192-candidate capacity send rows to the
+    whole-row select: scores spread over the saturating bin (the keys under
+    the chosen digit prefix soon fit the LDS buffer and the row is finished
+    there), 20,000 copies of one saturating value (no prefix narrows them:
+    ties cut by column at the last digit), and a row of 8192 + 1 equal scores
+    in a unit bin next to larger ones."""
+    rng = np.random.default_rng(808)
+    rows = [np.concatenate([rng.uniform(223, 4000, 16000), rng.standard_normal(24000) * 50]).astype(np.float32),
+            np.concatenate([np.full(20000, 300.0), rng.standard_normal(20000)]).astype(np.float32),
+            np.concatenate([np.full(8193, 100.0), rng.uniform(101, 150, 1000), rng.standard_normal(9000)]).astype(np.float32)]
+    for r in rows:
+        rng.shuffle(r)
+    buf, lens = _scores_dev(rows)
+    s_, ln = torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV)
+    for k in (2048, 8192):
+        announce(f"topk_rows overflow fallback shapes k={k} key={key}")
+        idx = topk(s_, None, ln, k, key)
+        check_topk(idx.cpu().numpy(), buf, lens, k, key)
