@@ -626,10 +626,11 @@ void indexer_sparse_logits_kernel(SparseLogitsArgs a) {
 // request's keys, scored request by request so one read of a K page serves
 // many rows.  A workgroup takes a tile of kPfTile consecutive rows of one
 // request; each wave keeps kPfRowsPerWave rows' Q operands and weights in
-// registers and walks the workgroup's pages, so the page the first wave
-// brings in reaches the others from the CU's cache.  The contraction and
-// epilogue are the decode kernel's (compute_page): a prefill logit is
-// bitwise the decode logit of the same row and key.
+// registers and walks all of the workgroup's pages (FP8 pages reach the
+// waves through an LDS ring the workgroup fills once per page; MXFP4 pages
+// each wave loads itself, from the CU's cache after the first wave).  The
+// contraction and epilogue are the decode kernel's (compute_page): a prefill
+// logit is bitwise the decode logit of the same row and key.
 //
 // Grid (splits, tiles).  Tiles are numbered request by request,
 // ceil(rows_r / kPfTile) each; the y extent bounds their count (tokens /
