@@ -304,8 +304,12 @@ struct ThreadScores {
 };
 
 // ---------------------------------------------------------------------------
-// Histogram of each row's live non-NaN scores, added to hist_out.
-template <bool F16>
+// Histogram of each row's live non-NaN scores, added to hist_out.  One
+// workgroup per M consecutive 4096-score chunks: the workgroup's bins are
+// added to the row's with global atomics, and the memory side serves the
+// atomics on one bin one after another, so long rows give each workgroup
+// several chunks (fewer contributions per bin).
+template <bool F16, int M>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restrict__ logits,
                                                              int64_t stride,
                                                              const int32_t* __restrict__ lens,
@@ -313,32 +317,38 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
   __shared__ int s_hist[kBins];
   const int row = blockIdx.y;
   const int len = clamp_len(lens, row, stride);
-  const int s0 = blockIdx.x * kChunk;
-  if (s0 >= len) return;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * M * kChunk;
+  if (first >= len) return;
   for (int i = threadIdx.x; i < kBins; i += kThreads) s_hist[i] = 0;
-  lds_barrier();
   const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
-  const int s1 = min(len, s0 + kChunk);
   constexpr int kPerVec = F16 ? 8 : 4;  // scores per 16-byte load
   constexpr int kVecs = kChunk / (kThreads * kPerVec);
   // All of a thread's loads are requested before any is binned.  In bounds:
   // a vector starting at s < len <= stride ends inside the row (s and the
-  // stride are multiples of kPerVec); past the chunk's end the chunk's first
-  // vector is read again and not binned.
-  i32x4 v[kVecs];
+  // stride are multiples of kPerVec); vectors past the row's end read the
+  // workgroup's first vector again and are not binned.
+  const int f = static_cast<int>(first);  // first < len < 2^31
+  i32x4 v[M][kVecs];
 #pragma unroll
-  for (int u = 0; u < kVecs; ++u) {
-    const int s = s0 + (u * kThreads + static_cast<int>(threadIdx.x)) * kPerVec;
-    v[u] = *reinterpret_cast<const i32x4*>(x + static_cast<int64_t>(s < s1 ? s : s0) * (F16 ? 2 : 4));
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+      const int64_t s = first + m * kChunk + (u * kThreads + static_cast<int>(threadIdx.x)) * kPerVec;
+      v[m][u] = *reinterpret_cast<const i32x4*>(x + (s < len ? s : f) * (F16 ? 2 : 4));
+    }
   }
+  lds_barrier();  // the bins are zero
 #pragma unroll
-  for (int u = 0; u < kVecs; ++u) {
-    const int s = s0 + (u * kThreads + static_cast<int>(threadIdx.x)) * kPerVec;
+  for (int m = 0; m < M; ++m) {
 #pragma unroll
-    for (int e = 0; e < kPerVec; ++e) {
-      if (s + e < s1) {
-        const uint32_t hb = half_bits_of<F16>(v[u], e);
-        if (!f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
+    for (int u = 0; u < kVecs; ++u) {
+      const int64_t s = first + m * kChunk + (u * kThreads + static_cast<int>(threadIdx.x)) * kPerVec;
+#pragma unroll
+      for (int e = 0; e < kPerVec; ++e) {
+        if (s + e < len) {
+          const uint32_t hb = half_bits_of<F16>(v[m][u], e);
+          if (!f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
+        }
       }
     }
   }
@@ -346,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
   unsigned long long* gh = reinterpret_cast<unsigned long long*>(hist_out + static_cast<int64_t>(row) * kBins);
   const uint2* sh = reinterpret_cast<const uint2*>(s_hist);
   for (int i = threadIdx.x; i < kBins / 2; i += kThreads) {
-    const uint2 v = sh[i];
-    if (v.x | v.y) atomicAdd(gh + i, (static_cast<unsigned long long>(v.y) << 32) | v.x);
+    const uint2 w = sh[i];
+    if (w.x | w.y) atomicAdd(gh + i, (static_cast<unsigned long long>(w.y) << 32) | w.x);
   }
 }
 
@@ -1035,6 +1045,12 @@ void launch_rows_whole(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
 // 2^20 scores: the extra registers halve the waves per SIMD.)
 inline int chunks_per_collect(int chunks) { return chunks > 64 ? 2 : 1; }
 
+// Chunks per histogram workgroup for rows of more than 64 chunks.
+#ifndef PMQA_TOPK_HIST_CHUNKS
+#define PMQA_TOPK_HIST_CHUNKS 2
+#endif
+constexpr int kHistChunks = PMQA_TOPK_HIST_CHUNKS;
+
 template <int KEY, bool F16, int M>
 void launch_collect(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int chunks, hipStream_t stream,
                     hipEvent_t start) {
@@ -1069,12 +1085,21 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents 
     // The workspace histograms are zero (at allocation, then left so by the
     // finish pass); ones that are not make the counts contradict b*, and
     // the row is selected from scratch.
-    if (a.logits_f16)
-      launch_kernel(topk_hist_kernel<true>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
+    if (chunks > 64) {
+      const dim3 hgrid(static_cast<unsigned>((chunks + kHistChunks - 1) / kHistChunks), static_cast<unsigned>(a.rows));
+      if (a.logits_f16)
+        launch_kernel(topk_hist_kernel<true, kHistChunks>, hgrid, dim3(kThreads), stream, start, nullptr, a.logits,
+                      a.logits_stride, a.context_lens, ws.hist);
+      else
+        launch_kernel(topk_hist_kernel<false, kHistChunks>, hgrid, dim3(kThreads), stream, start, nullptr, a.logits,
+                      a.logits_stride, a.context_lens, ws.hist);
+    } else if (a.logits_f16) {
+      launch_kernel(topk_hist_kernel<true, 1>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
                     a.logits_stride, a.context_lens, ws.hist);
-    else
-      launch_kernel(topk_hist_kernel<false>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
+    } else {
+      launch_kernel(topk_hist_kernel<false, 1>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
                     a.logits_stride, a.context_lens, ws.hist);
+    }
     start = nullptr;
     hist = ws.hist;
   }
@@ -1088,7 +1113,7 @@ hipError_t launch_score_histogram(const float* scores, int64_t stride, const int
                                   int32_t rows, int32_t* hist, hipStream_t stream) {
   const int64_t chunks64 = (stride + kChunk - 1) / kChunk;
   if (chunks64 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_hist_kernel<false>, dim3(static_cast<unsigned>(chunks64), static_cast<unsigned>(rows)),
+  hipLaunchKernelGGL((topk_hist_kernel<false, 1>), dim3(static_cast<unsigned>(chunks64), static_cast<unsigned>(rows)),
                      dim3(kThreads), 0, stream, scores, stride, lens, hist);
   return hipGetLastError();
 }
