@@ -122,7 +122,7 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
  * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
  * `rows` rows (host-only query, no device work): per row two 8-byte
  * counter pairs, a 4 KiB histogram and 64 KiB of candidates, each array
- * rounded up to 256 bytes.  Rows of at most 8192 scores (logits_stride <= 8192) leave the
+ * rounded up to 256 bytes.  Rows of at most 16384 scores (logits_stride <= 16384) leave the
  * workspace untouched.  Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
  */
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);

@@ -14,7 +14,7 @@
 // global memory that another thread of it wrote.
 //
 // Launch sequence of one topk_rows call (one stream, no host sync):
-//   rows of at most 8192 scores (stride <= 8192): topk_row, one 512-thread
+//   rows of at most 16384 scores (stride <= 16384): topk_row, one 512-thread
 //                  workgroup per row, whole row in registers: the threshold
 //                  bin b* from the histogram (or from one it builds in LDS
 //                  when there is none), the columns above b* straight to the
@@ -67,6 +67,7 @@ constexpr int kAllBins = kBins;             // threshold meaning "every live sco
 static_assert(kBins == 4 * kThreads, "collect: four bins per thread");
 static_assert(kBins == 2 * kRefineThreads, "row and finish: two bins per thread");
 static_assert(kRowSpan <= kCandCap, "a whole row's candidates fit the LDS buffer");
+constexpr int kRowSpanMax = 2 * kRowSpan;  // 16384: rows topk_row takes in two parts per thread
 
 // Scratch of one call of the chunked path.  The counter pairs must be zero
 // when a call starts; the finish pass leaves them zero.  Each row has two
@@ -866,11 +867,12 @@ __device__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, i
 }
 
 // ---------------------------------------------------------------------------
-// Rows of at most 8192 scores: one workgroup per row, thread t takes columns
-// 16t .. 16t+15, so the block scan of the per-thread counts keeps both lists
-// in column order.  OWN_HIST: no histogram was given; the workgroup bins its
-// row in LDS first.
-template <int KEY, bool F16, bool OWN_HIST>
+// Rows of at most M * 8192 scores: one workgroup per row, thread t takes
+// columns 8192m + 16t .. 8192m + 16t+15 of each part m, so block scans of the
+// per-thread counts (part 0's places before part 1's) keep both lists in
+// column order.  OWN_HIST: no histogram was given; the workgroup bins its row
+// in LDS first.
+template <int KEY, bool F16, bool OWN_HIST, int M>
 __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __restrict__ logits,
                                                                   int64_t stride,
                                                                   const int32_t* __restrict__ hist,
@@ -884,24 +886,32 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
   const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
   int32_t* out = indices + static_cast<int64_t>(row) * k;
 
-  // The thread's two bins and its 16 scores are requested together.
+  // The thread's two bins and its 16 scores of each 8192-column part are
+  // requested together.
   int hv[2] = {0, 0};
   if constexpr (!OWN_HIST) {
     const int2 h = *reinterpret_cast<const int2*>(hist + static_cast<int64_t>(row) * kBins + 2 * tid);
     hv[0] = h.x;
     hv[1] = h.y;
   }
-  const int s0 = tid * kPerThread;
-  ThreadScores<F16> sc;
-  sc.load(x, s0, len);
+  int s0[M];
+  ThreadScores<F16> sc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    s0[m] = m * kRowSpan + tid * kPerThread;
+    sc[m].load(x, s0[m], len);
+  }
   if constexpr (OWN_HIST) {
     s_hist[2 * tid] = 0;
     s_hist[2 * tid + 1] = 0;
     lds_barrier();
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const uint32_t hb = sc.half_bits(i);
-      if (s0 + i < len && !f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        const uint32_t hb = sc[m].half_bits(i);
+        if (s0[m] + i < len && !f16_is_nan(hb)) atomicAdd(&s_hist[coarse_bin_f16(hb)], 1);
+      }
     }
     lds_barrier();
     hv[0] = s_hist[2 * tid];
@@ -910,26 +920,47 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
   const int bstar = threshold_bin<kRefineThreads, 2>(hv, k, sh.red).bin;
 
   const Classifier cl(bstar);
-  uint32_t gmask, emask;
-  sc.classify(cl, s0, len, &gmask, &emask);
-  int tot = 0;
-  const int pre = block_excl_scan<kRefineThreads>(__popc(gmask) | (__popc(emask) << 16), sh.red, &tot);
-  const int n_gt = tot & 0xFFFF, n_eq = tot >> 16;
+  uint32_t gmask[M], emask[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) sc[m].classify(cl, s0[m], len, &gmask[m], &emask[m]);
+  // Places in column order: every column of part 0 before any of part 1.
+  int og[M], oe[M];
+  int n_gt, n_eq;
+  if constexpr (M == 1) {
+    int tot = 0;
+    const int pre = block_excl_scan<kRefineThreads>(__popc(gmask[0]) | (__popc(emask[0]) << 16), sh.red, &tot);
+    n_gt = tot & 0xFFFF;
+    n_eq = tot >> 16;
+    og[0] = pre & 0xFFFF;
+    oe[0] = pre >> 16;
+  } else {
+    int2 tot;
+    const int2 pre = block_excl_scan2<kRefineThreads>(__popc(gmask[0]) | (__popc(emask[0]) << 16),
+                                                      __popc(gmask[1]) | (__popc(emask[1]) << 16), sh.red, &tot);
+    n_gt = (tot.x & 0xFFFF) + (tot.y & 0xFFFF);  // each at most 16384
+    n_eq = (tot.x >> 16) + (tot.y >> 16);
+    og[0] = pre.x & 0xFFFF;
+    oe[0] = pre.x >> 16;
+    og[1] = (tot.x & 0xFFFF) + (pre.y & 0xFFFF);
+    oe[1] = (tot.x >> 16) + (pre.y >> 16);
+  }
   if (!counts_confirm(bstar, n_gt, n_eq, k)) {
     whole_row_select<KEY, F16>(sh, x, len, k, out);
     return;
   }
-  int og = pre & 0xFFFF, oe = pre >> 16;
   // When every candidate is taken (none exist below the all-bins threshold)
   // their columns go straight to the output.
   const bool direct = bstar == kAllBins || k - n_gt == n_eq;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    if ((gmask >> i) & 1u) out[og++] = s0 + i;  // og < n_gt <= k
-    if ((emask >> i) & 1u) {
-      if (direct) out[n_gt + oe] = s0 + i;
-      else sh.cand[oe] = uint2{sc.template key<KEY>(i), static_cast<uint32_t>(s0 + i)};
-      ++oe;
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      if ((gmask[m] >> i) & 1u) out[og[m]++] = s0[m] + i;  // og < n_gt <= k
+      if ((emask[m] >> i) & 1u) {
+        if (direct) out[n_gt + oe[m]] = s0[m] + i;
+        else sh.cand[oe[m]] = uint2{sc[m].template key<KEY>(i), static_cast<uint32_t>(s0[m] + i)};
+        ++oe[m];
+      }
     }
   }
   if (direct) {
@@ -1032,11 +1063,20 @@ size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k) {
 
 template <int KEY, bool F16>
 void launch_rows_whole(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
+  if (a.logits_stride > kRowSpan) {  // rows of up to 2 * kRowSpan: two parts per thread
+    if (a.hist)
+      launch_kernel(topk_row_kernel<KEY, F16, false, 2>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start,
+                    ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+    else
+      launch_kernel(topk_row_kernel<KEY, F16, true, 2>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start,
+                    ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+    return;
+  }
   if (a.hist)
-    launch_kernel(topk_row_kernel<KEY, F16, false>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
+    launch_kernel(topk_row_kernel<KEY, F16, false, 1>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
                   a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
   else
-    launch_kernel(topk_row_kernel<KEY, F16, true>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
+    launch_kernel(topk_row_kernel<KEY, F16, true, 1>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
                   a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
 }
 
@@ -1070,7 +1110,7 @@ void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist,
 
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
   // FP16 scores are ranked by their FP16 keys.
-  if (a.logits_stride <= kRowSpan) {
+  if (a.logits_stride <= kRowSpanMax) {
     if (a.logits_f16) launch_rows_whole<IDX_KEY_FP16, true>(a, stream, ev);
     else if (a.key_dtype == IDX_KEY_FP32) launch_rows_whole<IDX_KEY_FP32, false>(a, stream, ev);
     else launch_rows_whole<IDX_KEY_FP16, false>(a, stream, ev);

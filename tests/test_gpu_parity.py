@@ -403,3 +403,27 @@ def test_topk_fallback_overflow_shapes(gpu, key):
         announce(f"topk_rows overflow fallback shapes k={k} key={key}")
         idx = topk(s_, None, ln, k, key)
         check_topk(idx.cpu().numpy(), buf, lens, k, key)
+
+
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+@pytest.mark.parametrize("k", [1, 2048, 8192])
+def test_topk_rows_up_to_16384_in_one_workgroup(gpu, key, k):
+    """Rows of 8193 .. 16384 scores take the one-workgroup kernel with two
+    8192-column parts per thread (candidates in column order across the part
+    boundary): lengths 0, 1, 8191 .. 8193, 12000 and 16384, ties spanning both
+    parts, with the producer's histogram (score_histogram) and without."""
+    rng = np.random.default_rng(909 + k)
+    rows = [np.zeros(0, np.float32), np.array([3.0], np.float32),
+            rng.standard_normal(8191).astype(np.float32), rng.standard_normal(8192).astype(np.float32),
+            rng.standard_normal(8193).astype(np.float32),
+            np.round(rng.standard_normal(12000) * 2).astype(np.float32),   # ties in both parts
+            rng.standard_normal(16384).astype(np.float32) * np.float32(30.0)]
+    buf, lens = _scores_dev(rows)
+    buf = np.concatenate([buf, np.full((buf.shape[0], 16384 - buf.shape[1]), np.inf, np.float32)], axis=1)
+    s_, ln = torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV)
+    h = torch.zeros((len(rows), 1024), dtype=torch.int32, device=DEV)
+    gpu.score_histogram(s_, ln, h)
+    for hist in (h, None):
+        announce(f"topk_rows stride 16384 k={k} key={key} hist={'given' if hist is not None else 'NULL'}")
+        idx = topk(s_, hist, ln, k, key)
+        check_topk(idx.cpu().numpy(), buf, lens, k, key)
