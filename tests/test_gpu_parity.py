@@ -173,6 +173,16 @@ def test_many_requests_persistent_grid(gpu):
     h_2 = torch.cat([b for _, b in halves]).cpu().numpy()
     assert np.array_equal(got.view(np.uint32), got2.view(np.uint32)), "persistent grid differs from the static grid"
     assert np.array_equal(h.cpu().numpy(), h_2)
+    # FP16 output through the persistent grid: the halves the float32 logits
+    # round to (round to nearest even), the same histogram
+    announce("indexer_logits_f16 persistent grid B=40")
+    lg16, h16 = d.run_f16(with_hist=True, fill=INF)
+    got16 = lg16.cpu().numpy()[:, :x.logits_stride]
+    live = np.arange(x.logits_stride)[None, :] < x.context_lens[:, None]
+    want16 = got.astype(np.float16)
+    assert np.array_equal(np.where(live, got16, 0).view(np.uint16), np.where(live, want16, 0).view(np.uint16))
+    assert np.all(np.isinf(got16[~live]))
+    assert np.array_equal(h16.cpu().numpy(), h.cpu().numpy())
 
 
 def test_histogram_off_is_bitwise_identical_and_counts_accumulate(gpu):
