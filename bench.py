@@ -173,6 +173,8 @@ def main() -> int:
                     help="steps of the two-level candidate chain on the dense logits")
     ap.add_argument("--prefill-steps", type=int, default=30,
                     help="steps of the ragged prefill (extend) logits on prefill/extend")
+    ap.add_argument("--hist-steps", type=int, default=50,
+                    help="steps of the logits kernel with and without the histogram (interleaved)")
     ap.add_argument("--scores-steps", type=int, default=30,
                     help="steps of top-2048 over the very-long synthetic score rows (no histogram)")
     ap.add_argument("--candidate-blocks", type=int, default=512,
@@ -410,6 +412,26 @@ def main() -> int:
                     "note": "publish/select spans include the dispatch gaps between their calls"}
         del am, ah, bsel, table, slots, slens, sparse, ssel, pos, ws_b, ws_s
 
+    # cost of the fused histogram: the logits kernel with and without it,
+    # interleaved (the pages' producer-cost measure: histogram extra)
+    hx_out = None
+    if args.hist_steps > 0:
+        print(f"[bench] histogram on/off: {args.hist_steps} steps each", file=sys.stderr, flush=True)
+        on_us, off_us = [], []
+        for i in range(args.hist_steps + 2):
+            for with_hist in (True, False):
+                e0, e1 = new_events(2)
+                evict()
+                hist.zero_()
+                call_logits(x, t, logits, hist if with_hist else None, (e0, e1))
+                torch.cuda.synchronize()
+                if i >= 2:
+                    (on_us if with_hist else off_us).append(e0.elapsed_time(e1) * 1e3)
+        hx_out = {"with_hist_us_mean": round(float(np.mean(on_us)), 3),
+                  "without_hist_us_mean": round(float(np.mean(off_us)), 3),
+                  "extra_us_mean": round(float(np.mean(on_us) - np.mean(off_us)), 3),
+                  "extra_us_median": round(pct(on_us, 50) - pct(off_us, 50), 3)}
+
     # ragged prefill (extend) logits (SGLang PR #38944, SM90 FP8 prefill):
     # compute-bound, priced against the fp8 MFMA peak
     pf_out = None
@@ -543,6 +565,8 @@ def main() -> int:
         "mxfp4_k": mx_out,
         # two-level candidate indexer on this workload (SGLang PR #38944)
         "candidate_chain": cand_out,
+        # logits kernel with the fused histogram minus without it
+        "histogram_extra": hx_out,
         # ragged prefill (extend) logits: 4 requests x 2048 rows, contexts 2K..32K
         "prefill": pf_out,
         # top-2048 over synthetic score rows [4, 1048576], FP16 keys, hist=NULL
