@@ -55,6 +55,19 @@ __host__ __device__ __forceinline__ int coarse_bin_f16(uint32_t hb) {
 
 __host__ __device__ __forceinline__ bool f16_is_nan(uint32_t hb) { return (hb & 0x7FFFu) > 0x7C00u; }
 
+// The same bin without branches (a NaN gets the saturating bin; callers
+// exclude NaNs): the fine regime from the bits, the unit regime from the
+// exact float value of |h| -- truncated, it is floor(|h|), and clamping it at
+// 223 first folds the saturating bin (infinity included) into the formula.
+// Checked against coarse_bin_f16 for every non-NaN encoding on the host.
+__host__ __device__ __forceinline__ int coarse_bin_f16_flat(uint32_t hb) {
+  const uint32_t a = hb & 0x7FFFu;
+  const float mag = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(a)));
+  const uint32_t unit = 288u + static_cast<uint32_t>(fminf(mag, 223.0f));
+  const uint32_t m = a < 0x4C00u ? (a >> 6) : unit;
+  return (hb & 0x8000u) ? static_cast<int>(512u + m) : static_cast<int>(511u - m);
+}
+
 // Order-preserving unsigned keys: larger score <=> larger key, -0 just below +0.
 __device__ __forceinline__ uint32_t key_f32(float x) {
   const uint32_t u = __float_as_uint(x);

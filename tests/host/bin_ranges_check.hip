@@ -2,7 +2,9 @@
 // every FP16 encoding and every threshold bin (plus "all bins"): a half is in
 // the key range [lo, hi) exactly when its bin is b, and in [hi, key(+inf)]
 // exactly when its bin comes before b; NaNs are in neither.  Prints the
-// number of mismatches and exits non-zero if there are any.
+// number of mismatches and exits non-zero if there are any.  Also checks the
+// branch-free bin (coarse_bin_f16_flat) against coarse_bin_f16 for every
+// non-NaN half.
 #include <cstdio>
 
 #include "bin_key_range.h"
@@ -29,6 +31,15 @@ int main() {
       }
       ++checked;
     }
+  }
+  // the branch-free bin the logits kernel uses, against the reference form
+  for (uint32_t hb = 0; hb < 0x10000u; ++hb) {
+    if (f16_is_nan(hb)) continue;
+    if (coarse_bin_f16_flat(hb) != coarse_bin_f16(hb)) {
+      if (bad < 10) std::printf("flat bin of half 0x%04x: %d, want %d\n", hb, coarse_bin_f16_flat(hb), coarse_bin_f16(hb));
+      ++bad;
+    }
+    ++checked;
   }
   std::printf("checked %ld, mismatches %ld\n", checked, bad);
   return bad == 0 ? 0 : 1;
