@@ -54,7 +54,7 @@ namespace {
 #define PMQA_LOGITS_PERSIST 1
 #endif
 #ifndef PMQA_LOGITS_PERSIST_PPW
-#define PMQA_LOGITS_PERSIST_PPW 64
+#define PMQA_LOGITS_PERSIST_PPW 64  // <= PMQA_LOGITS_MAX_PPW
 #endif
 #ifndef PMQA_LOGITS_PERSIST_WGS_PER_CU
 #define PMQA_LOGITS_PERSIST_WGS_PER_CU 2
@@ -79,12 +79,17 @@ constexpr int kPrefetchOf = (KF == 1 && NN == 1) ? 2 : kPrefetch;
 #ifndef PMQA_LOGITS_MAX_PPW
 #define PMQA_LOGITS_MAX_PPW 64
 #endif
-constexpr int kMaxPagesPerWg = PMQA_LOGITS_MAX_PPW;  // <= waves * kWave: one page-id fetch per wave
-static_assert(kMaxPagesPerWg <= 4 * kWave, "page ids of a share must fit one fetch");
+// Pages per share at most: 128 with one row per request (its staging is then
+// 32 KiB; a long row's bins receive the flush atomics of half as many
+// workgroups: very_long 104.1 -> 103.3 us, histogram extra 2.1 -> 0.3 us),
+// 64 with several (their staging is NN times larger).
+constexpr int kMaxPagesPerWg = PMQA_LOGITS_MAX_PPW;
+constexpr int kMaxPagesPerWgOneRow = 2 * kMaxPagesPerWg;
+static_assert(kMaxPagesPerWgOneRow <= 4 * kWave, "page ids of a share must fit one fetch");
 // LDS staging of a share's scores: next_n * pages_per_wg * 64 floats
-// (16 KiB per row of the request).
+// (32 KiB for one row, 16 KiB per row with several).
 template <int NN>
-constexpr int kStageFloats = NN * kMaxPagesPerWg * kPage;
+constexpr int kStageFloats = NN * (NN == 1 ? kMaxPagesPerWgOneRow : kMaxPagesPerWg) * kPage;
 // Staged score type: float32 logits, or the bits of their FP16 rounding.
 template <bool F16>
 using StageT = typename std::conditional<F16, uint16_t, float>::type;
@@ -356,7 +361,7 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
   const int lpi0 = wave;  // share-local index of the wave's first page
 
   // Pages p0 + wave, + kWaves, ... < p1; lane i of `ids` holds the wave's
-  // i-th page id.  A share has at most kMaxPagesPerWg pages, so one fetch
+  // i-th page id.  A share has at most 4 * 64 pages, so one fetch
   // covers it, and the loop below has no conditional load: a load inside a
   // branch would make the compiler wait for every outstanding load (and, on
   // this architecture, store) before the next page could be issued.
@@ -478,7 +483,10 @@ template <int NN, bool HIST, bool F16, int KF, bool PERSIST>
 __global__ __launch_bounds__(kThreadsOf<NN>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<NN>)))
 void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   __shared__ int s_hist[HIST ? NN * kBins + 1 : 1];  // the rows' bins and a spare slot
-  __shared__ __align__(16) StageT<F16> s_out[kStageFloats<NN>];  // [NN][pages_per_wg][64] scores
+  // [NN][pages_per_wg][64] scores.  The persistent grid's shares are 64
+  // pages: its staging stays at 16 KiB (the 32 KiB one-row staging measured
+  // varlen 130.0 -> 135.3 us with the histogram on).
+  __shared__ __align__(16) StageT<F16> s_out[PERSIST ? NN * kMaxPagesPerWg * kPage : kStageFloats<NN>];
   // Q in MFMA operand layout, [row][head block][half][lane], and the weights:
   // fetched once per workgroup and read by every wave from here.
   __shared__ __align__(16) i32x4 s_q[NN >= 2 ? NN * 4 * kWave : 1];
@@ -923,7 +931,7 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   // Pages per workgroup.  Long streams per wave amortise a workgroup's start
   // (one round trip for its page ids) and end (staged stores, histogram
   // flush), so a share is as long as the grid allows while every CU still
-  // gets a workgroup: B * max_pages / CUs pages, 4..kMaxPagesPerWg.  The host
+  // gets a workgroup: B * max_pages / CUs pages, 4..max_ppw.  The host
   // cannot read the lengths, so B * max_pages is an upper bound; with many
   // requests (B >= 32) the real lengths usually vary, and shorter shares
   // (16 pages) give the static grid enough rounds to even out.
@@ -934,7 +942,8 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   ppw = PMQA_LOGITS_PAGES_PER_WG;
 #endif
   ppw = (ppw + 3) / 4 * 4;  // rounded up: the grid then holds at most one workgroup per CU
-  ppw = ppw < 4 ? 4 : (ppw > kMaxPagesPerWg ? kMaxPagesPerWg : ppw);
+  const int64_t max_ppw = a.next_n == 1 ? kMaxPagesPerWgOneRow : kMaxPagesPerWg;
+  ppw = ppw < 4 ? 4 : (ppw > max_ppw ? max_ppw : ppw);
   const int64_t chunks = (a.max_pages + ppw - 1) / ppw;
   if (chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
@@ -943,7 +952,7 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   int persistent = 0;
 #if PMQA_LOGITS_PERSIST
   if (a.next_n == 1 && !a.k_mxfp4 && a.B >= 32 && a.B <= kPersistMaxB) {
-    ppw = PMQA_LOGITS_PERSIST_PPW;  // equal shares dealt round robin: longer ones cost no balance
+    ppw = PMQA_LOGITS_PERSIST_PPW;  // equal shares dealt round robin (at most kMaxPagesPerWg)
     const int64_t upper = (a.max_pages + ppw - 1) / ppw * a.B;
     const int64_t wgs = static_cast<int64_t>(PMQA_LOGITS_PERSIST_WGS_PER_CU) * info->cus;
     grid = dim3(static_cast<unsigned>(upper < wgs ? upper : wgs), 1);
