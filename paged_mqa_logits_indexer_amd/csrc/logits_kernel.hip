@@ -69,7 +69,6 @@ namespace {
 // behind the first one's pages in the CU's memory pipeline).
 template <int NN>
 constexpr int kWavesOf = NN >= 3 ? PMQA_LOGITS_WAVES_MANY_ROWS : 4;
-constexpr int kWavesMax = 8;
 constexpr int kPrefetch = PMQA_LOGITS_PREFETCH;  // pages in flight per wave
 // MXFP4 pages are half the bytes: with one row per request a wave keeps two
 // of them in flight (measured 18.6 -> 16.8 us at long decode; with more rows
