@@ -1,0 +1,116 @@
+"""The benchmark's host-side logic, without a GPU: the refusal of more than
+one GPU, the algorithmic bytes the roofline is priced on, and the traffic
+record made from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) scaled
+by a plain copy of known size."""
+import csv
+import json
+import os
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
+
+
+def _decode_shape(lens, next_n=1, mxfp4=False):
+    lens = np.asarray(lens, np.int32)
+    return SimpleNamespace(
+        context_lens=lens, rows=lens.size, mxfp4=mxfp4,
+        request_keys=lambda: lens.reshape(-1, next_n).max(axis=1))
+
+
+def test_long_decode_algorithmic_bytes():
+    # B=8 requests of 131072 keys: K 128 B and one fp32 scale per key, one fp32
+    # logit per key, 2048 block-table entries per request, Q (32x128 fp8),
+    # 32 fp32 weights and the length per row, and the 1024-bin histogram
+    # read and written once per row.
+    ab = bench.algorithmic_bytes(_decode_shape([131072] * 8))
+    assert ab["k"] == 8 * 131072 * 128 == 134_217_728
+    assert ab["total"] == 142_771_232
+
+
+def test_algorithmic_bytes_ragged_and_verify_rows():
+    # Two requests with next_n=2: the K sweep reads each request once, up to
+    # its longest row; logits are per row; a partial page still costs a
+    # whole block-table entry.
+    ab = bench.algorithmic_bytes(_decode_shape([100, 65, 0, 3], next_n=2))
+    keys = 100 + 3
+    assert ab["k"] == keys * 128
+    want = keys * 132 + (100 + 65 + 3) * 4 + (2 + 1) * 4 + 4 * (4096 + 128 + 4) + 4 * 8192
+    assert ab["total"] == want
+
+
+def test_algorithmic_bytes_mxfp4_tokens():
+    # A packed MXFP4 token is 64 B of codes and 4 E8M0 block scales; no
+    # separate fp32 scale.
+    ab = bench.algorithmic_bytes(_decode_shape([64] * 2, mxfp4=True))
+    assert ab["k"] == 128 * 68
+    assert ab["total"] == 128 * 68 + 128 * 4 + 2 * 4 + 2 * (4096 + 128 + 4) + 2 * 8192
+
+
+def _write_counters(path, counter, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": value})
+
+
+LOGITS = bench.LOGITS_KERNEL + "(LogitsArgs, int)"
+COPY = "void at::native::elementwise_kernel_copy"
+
+
+def test_traffic_record_scales_by_the_copy(tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    # FETCH_SIZE reads the copy's bytes at half (factor 2); a logits launch
+    # before the copies is averaged, other kernels and copies before the last
+    # logits dispatch are ignored.
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [
+        (COPY, 1.0), (LOGITS, 1000.0), ("topk_row_kernel", 9e9), (LOGITS, 1200.0),
+        (COPY, copy_kib / 2), (COPY, copy_kib / 2)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [
+        (LOGITS, 300.0), (LOGITS, 300.0), (COPY, copy_kib)])
+    tr = bench.traffic_from(str(tmp_path / "f"), str(tmp_path / "w"), "long_decode")
+    assert tr["workload"] == "long_decode"
+    assert tr["kernel_src_sha"] == bench.kernel_source_digest()
+    assert tr["FETCH_SIZE"]["dispatches"] == 2 and tr["FETCH_SIZE"]["copies"] == 2
+    assert tr["FETCH_SIZE"]["factor"] == pytest.approx(2.0)
+    assert tr["FETCH_SIZE"]["bytes_per_launch"] == pytest.approx(1100.0 * 1024 * 2)
+    assert tr["WRITE_SIZE"]["factor"] == pytest.approx(1.0)
+    assert tr["bytes_per_launch"] == round(1100.0 * 1024 * 2 + 300.0 * 1024)
+
+
+def test_traffic_record_needs_a_copy_after_the_logits(tmp_path):
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [(COPY, 5.0), (LOGITS, 10.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [(LOGITS, 1.0), (COPY, 2.0)])
+    with pytest.raises(SystemExit, match="calibration copy"):
+        bench.traffic_from(str(tmp_path / "f"), str(tmp_path / "w"), "long_decode")
+
+
+def test_committed_traffic_record_is_close_to_the_algorithmic_bytes():
+    # The committed counter record of the long-decode launch: HBM bytes within
+    # a few percent of the algorithmic minimum (no re-reads), and its kernel
+    # digest names a source state (the bench drops the figure when the digest
+    # differs from the current source).
+    with open(bench.TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    assert tr["workload"] == "long_decode"
+    assert len(tr["kernel_src_sha"]) == 16
+    total = bench.algorithmic_bytes(_decode_shape([131072] * 8))["total"]
+    assert total <= tr["bytes_per_launch"] <= 1.05 * total
