@@ -701,25 +701,52 @@ struct SegmentReader {
   }
 };
 
-// hist[d] += 1 for every active lane with `act`.  With AGGREGATE the lanes
-// that share the first such lane's digit add their count with one atomic:
-// the top bytes of FP32 keys are sign and exponent, so a row of scores in one
-// exponent range would otherwise queue 64 increments of one LDS word per
-// instruction (unit-regime verify rows: 73 -> 64 us); FP16 keys measured
-// faster without it.
-template <bool AGGREGATE>
-__device__ __forceinline__ void digit_add(int* hist, bool act, uint32_t d) {
-  if constexpr (!AGGREGATE) {
-    if (act) atomicAdd(&hist[d], 1);
-    return;
+// Digit counts of the whole-row passes.  FP32 keys: one copy of the 256
+// bins per lane position, kept in the candidate buffer (unused until the
+// gather) with bin d of lane l at word 64 d + l, so the 64 adds of one
+// instruction fall on 64 different words and banks.  The top bytes of FP32
+// keys are sign and exponent: with a single copy a wave whose scores share a
+// few of them queues up to 64 increments of one word per instruction (a
+// unit-regime verify row of 32K scores: fallback 45.7 -> 41.9 us; aggregating
+// the first lane's digit with ballots, the design before, gave 73 -> 64 us
+// over plain adds).  FP16 keys add to digit_hist directly (measured faster).
+static_assert(sizeof(uint2) * kCandCap >= sizeof(int) * 256 * kWave, "lane bins fit the candidate buffer");
+
+template <bool LANE_BINS>
+__device__ __forceinline__ void digit_clear(RefineShared& sh) {
+  if constexpr (LANE_BINS) {
+    i32x4* p = reinterpret_cast<i32x4*>(sh.cand);
+    for (int i = threadIdx.x; i < 256 * kWave / 4; i += kRefineThreads) p[i] = i32x4{0, 0, 0, 0};
+  } else {
+    for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
   }
-  const uint64_t m = __ballot(act);
-  if (!m) return;
-  const int l = static_cast<int>(__builtin_ctzll(m));
-  const uint32_t dl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(d), l));
-  const uint64_t same = __ballot(act && d == dl);
-  if (static_cast<int>(__lane_id()) == l) atomicAdd(&hist[dl], static_cast<int>(__popcll(same)));
-  if (act && d != dl) atomicAdd(&hist[d], 1);
+}
+
+template <bool LANE_BINS>
+__device__ __forceinline__ void digit_add(RefineShared& sh, bool act, uint32_t d) {
+  if constexpr (LANE_BINS) {
+    if (act) atomicAdd(&reinterpret_cast<int*>(sh.cand)[d * kWave + __lane_id()], 1);
+  } else {
+    if (act) atomicAdd(&sh.digit_hist[d], 1);
+  }
+}
+
+// After a barrier that makes the adds visible: digit_hist[d] = the sum of
+// bin d's copies (lane l reads copy (l + j) mod 64 at step j, 64 banks per
+// instruction), published by a barrier.
+template <bool LANE_BINS>
+__device__ __forceinline__ void digit_publish(RefineShared& sh) {
+  if constexpr (LANE_BINS) {
+    const int* b = reinterpret_cast<const int*>(sh.cand);
+    const int l = __lane_id();
+    for (int d = threadIdx.x; d < 256; d += kRefineThreads) {
+      int sum = 0;
+#pragma unroll 8
+      for (int j = 0; j < kWave; ++j) sum += b[d * kWave + ((l + j) & (kWave - 1))];
+      sh.digit_hist[d] = sum;
+    }
+    lds_barrier();
+  }
 }
 
 __device__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt, int n_eq,
@@ -731,16 +758,17 @@ __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, i
   constexpr int kKey = F16 ? IDX_KEY_FP16 : KEY;
   constexpr int kKeyBits = kKey == IDX_KEY_FP32 ? 32 : 16;
   const SegmentReader<F16> rd(x, len);
+  constexpr bool kLaneBins = kKey == IDX_KEY_FP32;
   // Pass 1: the live count and the histogram of the top key digit.
-  for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
+  digit_clear<kLaneBins>(sh);
   if (threadIdx.x == 0) sh.out_pos = 0;
   lds_barrier();
   int cnt = 0;
   rd.template for_each<KEY>([&](int, uint32_t key, bool live) {
     cnt += live ? 1 : 0;
-    digit_add<kKey == IDX_KEY_FP32>(sh.digit_hist, live, key >> (kKeyBits - 8));
+    digit_add<kLaneBins>(sh, live, key >> (kKeyBits - 8));
   });
-  const int n = block_sum<kRefineThreads>(cnt, sh.red);  // its barriers also publish digit_hist
+  const int n = block_sum<kRefineThreads>(cnt, sh.red);  // its barriers also make the adds visible
   if (n <= k) {
     rd.template for_each<KEY>([&](int s, uint32_t, bool live) { emit(sh, out, k, live, s); });
     lds_barrier();
@@ -751,13 +779,14 @@ __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, i
   int need = k;
   for (int shift = kKeyBits - 8; shift >= 0; shift -= 8) {
     if (shift != kKeyBits - 8) {
-      for (int i = threadIdx.x; i < 256; i += kRefineThreads) sh.digit_hist[i] = 0;
+      digit_clear<kLaneBins>(sh);  // the last pass's reads ended before pick_digit's barriers
       lds_barrier();
       rd.template for_each<KEY>([&](int, uint32_t key, bool live) {
-        digit_add<kKey == IDX_KEY_FP32>(sh.digit_hist, live && ((key ^ prefix) & fixed) == 0u, (key >> shift) & 0xFFu);
+        digit_add<kLaneBins>(sh, live && ((key ^ prefix) & fixed) == 0u, (key >> shift) & 0xFFu);
       });
       lds_barrier();
     }
+    digit_publish<kLaneBins>(sh);
     int before = 0;
     int in_bin = 0;
     const int d = pick_digit(sh, need, &before, &in_bin);
