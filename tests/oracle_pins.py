@@ -482,6 +482,165 @@ def pin_error_bound(O):
 
 
 
+# ------------------------------------------------- acceptance helpers --
+def _exact_dots(qd, kd):
+    """Exact rational q_h . k for the 32 heads (qd [32,128], kd [128])."""
+    return [sum((Fraction(float(qd[h, d])) * Fraction(float(kd[d])) for d in range(128)),
+                Fraction(0)) for h in range(32)]
+
+
+def _exact_abs_dots(qd, kd):
+    return [sum((abs(Fraction(float(qd[h, d])) * Fraction(float(kd[d]))) for d in range(128)),
+                Fraction(0)) for h in range(32)]
+
+
+def _acceptance_inputs():
+    """Tiny inputs with an infinite K scale on some slots, so that the head
+    sum and the scaled logit part ways (the mixed verify workload's case)."""
+    import gen
+    x = gen.make_indexer_inputs("acc", 1, 2, [130], 41, weight_scale=2.0)
+    # scales spread over several binades so that scaled and unscaled differ
+    rng = np.random.default_rng(3)
+    x.k_scales[:] = (2.0 ** rng.integers(-12, 6, size=x.k_scales.shape)).astype(np.float32)
+    x.k_scales[x.block_table[0, 0], [3, 17]] = np.inf
+    x.k_scales[x.block_table[0, 1], 5] = np.inf
+    return x
+
+
+def pin_head_sum_exact(O):
+    """head_sum_at = sum_h w_h * ReLU(q_h . k_s) in exact rationals, before
+    any K scale (also where the scale is infinite), within the float64
+    rounding of a 32-term sum (gamma_32 of the absolute terms)."""
+    fails = []
+    x = _acceptance_inputs()
+    cols = np.array([0, 3, 17, 40, 64 + 5, 64 + 30, 129])
+    for r in range(x.rows):
+        got = O.head_sum_at(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                            x.next_n, r, cols)
+        qd = torch_e4m3_decode(x.q[r])
+        for i, s in enumerate(cols.tolist()):
+            page = int(x.block_table[r // x.next_n, s // 64])
+            kd = torch_e4m3_decode(x.kv_pages[page, s % 64])
+            terms = [Fraction(float(x.weights[r, h])) * d
+                     for h, d in enumerate(_exact_dots(qd, kd)) if d > 0]
+            exact = sum(terms, Fraction(0))
+            tol = 32 * 2.0 ** -53 * float(sum((abs(t) for t in terms), Fraction(0)))
+            if not (math.isfinite(float(got[i])) and abs(Fraction(float(got[i])) - exact) <= Fraction(tol)):
+                fails.append(f"head_sum row {r} col {s}: {got[i]!r}, exact {float(exact)!r}")
+    return fails
+
+
+def pin_error_bound_exact(O):
+    """logits_error_bound_at = rel * |sc_s| * sum_h |w_h| * sum_d |q_hd k_sd|
+    (and without |sc_s| when unscaled) in exact rationals, to float64
+    rounding; scales spread over 2^-12 .. 2^5 so the two modes differ."""
+    fails = []
+    x = _acceptance_inputs()
+    cols = np.array([1, 3, 20, 64 + 5, 64 + 63, 128])
+    rel = 1e-5
+    for r in range(x.rows):
+        scaled = O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                         x.block_table, x.next_n, r, cols, rel=rel)
+        unscaled = O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                           x.block_table, x.next_n, r, cols, rel=rel,
+                                           unscaled=True)
+        qd = torch_e4m3_decode(x.q[r])
+        for i, s in enumerate(cols.tolist()):
+            page = int(x.block_table[r // x.next_n, s // 64])
+            kd = torch_e4m3_decode(x.kv_pages[page, s % 64])
+            head = sum((abs(Fraction(float(x.weights[r, h]))) * a
+                        for h, a in enumerate(_exact_abs_dots(qd, kd))), Fraction(0))
+            want_u = Fraction(rel) * head
+            if abs(Fraction(float(unscaled[i])) - want_u) > want_u * Fraction(1, 2 ** 40):
+                fails.append(f"unscaled bound row {r} col {s}: {unscaled[i]!r} vs {float(want_u)!r}")
+            sc = float(x.k_scales[page, s % 64])
+            if math.isinf(sc):
+                if not np.isinf(scaled[i]):
+                    fails.append(f"scaled bound at an infinite scale is {scaled[i]!r}")
+                continue
+            want_s = want_u * abs(Fraction(sc))
+            if abs(Fraction(float(scaled[i])) - want_s) > want_s * Fraction(1, 2 ** 40):
+                fails.append(f"scaled bound row {r} col {s}: {scaled[i]!r} vs {float(want_s)!r}")
+    return fails
+
+
+def pin_check_logits_classes(O):
+    """check_logits on hand-built cases.  A finite expected value is judged by
+    |got - want| <= bound alone (the near-zero waiver never widens it).  A
+    non-finite expected value (an infinite K scale) is judged by class: NaN
+    matches NaN, an infinity the same infinity; the waiver -- the unscaled
+    head sum within its own tolerance of zero, so its sign is rounding --
+    accepts any infinity or NaN, never a finite value, and a wrong-signed
+    infinity with a large head sum is refused."""
+    inf, nan = np.inf, np.nan
+    # got, want, bound, head_sum, head_bound, accepted
+    cases = [
+        (1.0, 1.0, 0.0, 0.0, 1.0, True),
+        (1.5, 1.0, 0.5, 0.0, 1.0, True),
+        (1.5, 1.0, 0.25, 0.0, 1.0, False),      # waiver not for finite values
+        (5.0, 1.0, 1.0, 1e-9, 1.0, False),
+        (-1.0, 1.0, 1.0, 0.0, 1.0, False),
+        (inf, 1.0, 1.0, 0.0, 1.0, False),
+        (nan, 1.0, 1.0, 0.0, 1.0, False),
+        (nan, nan, inf, 0.0, 1e-5, True),        # NaN <-> NaN
+        (nan, nan, inf, 3.0, 1e-5, True),
+        (inf, nan, inf, 0.0, 1e-5, True),        # head sum zero: either class
+        (-inf, nan, inf, 0.0, 1e-5, True),
+        (inf, nan, inf, 3.0, 1e-5, False),
+        (inf, inf, inf, 5.0, 1e-4, True),
+        (-inf, -inf, inf, -5.0, 1e-4, True),
+        (-inf, inf, inf, 5.0, 1e-4, False),      # wrong sign, large head sum
+        (inf, -inf, inf, -5.0, 1e-4, False),
+        (nan, inf, inf, 5.0, 1e-4, False),
+        (-inf, inf, inf, 5e-5, 1e-4, True),      # head sum within rounding of 0
+        (nan, -inf, inf, -1e-4, 1e-4, True),
+        (-inf, inf, inf, 1.0001e-4, 1e-4, False),
+        (1e30, inf, inf, 1e-6, 1e-4, False),     # a finite value is never an inf
+        (0.0, nan, inf, 0.0, 1e-5, False),
+    ]
+    fails = []
+    g, w, b, hs, hb, acc = (np.array(c, dtype=np.float64) for c in zip(*cases))
+    got = O.check_logits(g, w, b, hs, hb)
+    for i, case in enumerate(cases):
+        if bool(got[i]) != case[-1]:
+            fails.append(f"check_logits{case[:-1]} = {bool(got[i])}, expected {case[-1]}")
+    # without head sums, no waiver at all
+    got = O.check_logits(np.array([inf, -inf, nan]), np.array([nan, inf, -inf]),
+                         np.array([inf, inf, inf]))
+    if got.any():
+        fails.append(f"class mismatches accepted without a waiver: {got.tolist()}")
+    # from the formula: at an infinite scale the logit is the head sum's sign
+    # times infinity (NaN for a zero sum); flipping that sign is refused
+    # wherever the head sum is clear of its tolerance
+    x = _acceptance_inputs()
+    cols = np.arange(130)
+    for r in range(x.rows):
+        want = O.indexer_logits_at(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                                   x.next_n, r, cols)
+        bound = O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                        x.block_table, x.next_n, r, cols)
+        hs = O.head_sum_at(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                           x.next_n, r, cols)
+        hb = O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                     x.block_table, x.next_n, r, cols, unscaled=True)
+        nf = ~np.isfinite(want)
+        if nf.sum() != 3:
+            fails.append(f"row {r}: expected 3 infinite-scale logits, got {int(nf.sum())}")
+        for c in np.nonzero(nf)[0]:
+            sign = np.sign(hs[c])
+            expect = np.nan if sign == 0 else sign * np.inf
+            if not (np.isnan(want[c]) if sign == 0 else want[c] == expect):
+                fails.append(f"row {r} col {c}: logit {want[c]} vs head sum {hs[c]}")
+            if abs(hs[c]) > hb[c] and sign != 0:
+                if O.check_logits(np.array([-expect]), want[c:c + 1], bound[c:c + 1],
+                                  hs[c:c + 1], hb[c:c + 1])[0]:
+                    fails.append(f"row {r} col {c}: the wrong-signed infinity is accepted")
+            if not O.check_logits(want[c:c + 1], want[c:c + 1], bound[c:c + 1],
+                                  hs[c:c + 1], hb[c:c + 1])[0]:
+                fails.append(f"row {r} col {c}: the oracle's own value is refused")
+    return fails
+
+
 def _f32_between(lo, hi):
     """Every float32 in [lo, hi] (float64 bounds), by bit pattern."""
     a = np.float32(lo)
@@ -835,7 +994,8 @@ def pin_prefill_exact(O, n_cols=3):
 ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_logits_f16_check, pin_bins_golden, pin_bins_exhaustive,
             pin_keys, pin_bins_coarsen_keys, pin_histogram, pin_topk,
             pin_topk_invariants, pin_logits_exact, pin_logits_library,
-            pin_logits_paging, pin_error_bound, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
+            pin_logits_paging, pin_error_bound, pin_head_sum_exact,
+            pin_error_bound_exact, pin_check_logits_classes, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
             pin_mxfp4_matches_fp8_path, pin_mxfp4_exact, pin_block_amax8,
             pin_sort_candidate_blocks, pin_sparse_logits, pin_prefill_decode_case,
             pin_prefill_exact)

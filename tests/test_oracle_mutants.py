@@ -331,6 +331,81 @@ def m_prefill_boundary_row(O):
     _wrap_prefill(O, f)
 
 
+# ---- the acceptance helpers (head sum, error bound, class check) ----
+def m_head_sum_no_relu(O):
+    def hs(q, kv_pages, k_scales, weights, block_table, next_n, row, cols):
+        keys, _ = O._request_keys_at(kv_pages, k_scales, block_table[row // next_n], cols)
+        return weights[row].astype(np.float64) @ (O.decode_e4m3fn(q[row]) @ keys.T)
+    O.head_sum_at = hs
+
+
+def m_head_sum_scaled(O):
+    orig = O.head_sum_at
+
+    def hs(q, kv_pages, k_scales, weights, block_table, next_n, row, cols):
+        _, sc = O._request_keys_at(kv_pages, k_scales, block_table[row // next_n], cols)
+        with np.errstate(invalid="ignore", over="ignore"):
+            return sc * orig(q, kv_pages, k_scales, weights, block_table, next_n, row, cols)
+    O.head_sum_at = hs
+
+
+def m_bound_unscaled_keeps_scale(O):
+    orig = O.logits_error_bound_at
+    O.logits_error_bound_at = lambda *a, rel=1e-5, unscaled=False: orig(*a, rel=rel)
+
+
+def m_bound_signed_dots(O):
+    def bound(q, kv_pages, k_scales, weights, block_table, next_n, row, cols, rel=1e-5,
+              unscaled=False):
+        keys, sc = O._request_keys_at(kv_pages, k_scales, block_table[row // next_n], cols)
+        head = np.abs(weights[row].astype(np.float64)) @ np.abs(O.decode_e4m3fn(q[row]) @ keys.T)
+        with np.errstate(invalid="ignore", over="ignore"):
+            return rel * head if unscaled else rel * np.abs(sc) * head
+    O.logits_error_bound_at = bound
+
+
+def m_waiver_on_finite(O):
+    orig = O.check_logits
+
+    def check(got, want, bound, head_sum=None, head_bound=None):
+        ok = orig(got, want, bound, head_sum, head_bound)
+        if head_sum is not None and head_bound is not None:
+            ok |= np.abs(np.asarray(head_sum)) <= np.asarray(head_bound)
+        return ok
+    O.check_logits = check
+
+
+def m_inf_sign_ignored(O):
+    orig = O.check_logits
+
+    def check(got, want, bound, head_sum=None, head_bound=None):
+        ok = orig(got, want, bound, head_sum, head_bound)
+        return ok | (np.isinf(np.asarray(got, np.float64)) & np.isinf(np.asarray(want, np.float64)))
+    O.check_logits = check
+
+
+def m_nan_matches_any_nonfinite(O):
+    orig = O.check_logits
+
+    def check(got, want, bound, head_sum=None, head_bound=None):
+        g, w = np.asarray(got, np.float64), np.asarray(want, np.float64)
+        ok = orig(got, want, bound, head_sum, head_bound)
+        return ok | (np.isnan(w) & ~np.isfinite(g)) | (np.isnan(g) & ~np.isfinite(w))
+    O.check_logits = check
+
+
+def m_waiver_accepts_finite(O):
+    orig = O.check_logits
+
+    def check(got, want, bound, head_sum=None, head_bound=None):
+        ok = orig(got, want, bound, head_sum, head_bound)
+        if head_sum is not None and head_bound is not None:
+            nf = ~np.isfinite(np.asarray(want, np.float64))
+            ok |= nf & (np.abs(np.asarray(head_sum)) <= np.asarray(head_bound))
+        return ok
+    O.check_logits = check
+
+
 MUTANTS = [
     (m_e4m3_bias, [P.pin_e4m3]),
     (m_e4m3_subnormal, [P.pin_e4m3]),
@@ -365,6 +440,14 @@ MUTANTS = [
     (m_prefill_tables_reversed, [P.pin_prefill_decode_case, P.pin_prefill_exact]),
     (m_prefill_request_max_len, [P.pin_prefill_decode_case, P.pin_prefill_exact]),
     (m_prefill_boundary_row, [P.pin_prefill_decode_case, P.pin_prefill_exact]),
+    (m_head_sum_no_relu, [P.pin_head_sum_exact]),
+    (m_head_sum_scaled, [P.pin_head_sum_exact]),
+    (m_bound_unscaled_keeps_scale, [P.pin_error_bound_exact]),
+    (m_bound_signed_dots, [P.pin_error_bound_exact]),
+    (m_waiver_on_finite, [P.pin_check_logits_classes]),
+    (m_inf_sign_ignored, [P.pin_check_logits_classes]),
+    (m_nan_matches_any_nonfinite, [P.pin_check_logits_classes]),
+    (m_waiver_accepts_finite, [P.pin_check_logits_classes]),
 ]
 
 
