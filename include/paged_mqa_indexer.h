@@ -70,6 +70,9 @@ typedef enum { IDX_KEY_FP32 = 0, IDX_KEY_FP16 = 1 } idx_key_dtype;
 #define IDX_CANDIDATE_CAPACITY 8192 /* [P1] SGLang commit: candidate_capacity */
 #define IDX_MAX_REQUESTS 4096
 #define IDX_MAX_ROWS 65535
+/* topk_rows: rows of more than 16384 scores go through the chunked path,
+ * whose strides are limited to 2^23 (8x the longest context on the pages). */
+#define IDX_TOPK_MAX_STRIDE (1 << 23)
 
 /*
  * indexer_logits -- paged MQA logits with an optional fused coarse histogram.
@@ -120,10 +123,12 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
 
 /*
  * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
- * `rows` rows (host-only query, no device work): per row two 8-byte
- * counter pairs, a 4 KiB histogram and 64 KiB of candidates, each array
- * rounded up to 256 bytes.  Rows of at most 16384 scores (logits_stride <= 16384) leave the
- * workspace untouched.  Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
+ * `rows` rows (host-only query, no device work): one 73,984-byte record per
+ * row -- two 8-byte counter pairs (padded to 256 bytes), a 4 KiB histogram,
+ * 64 KiB of candidates and 4 KiB of per-workgroup counts -- whatever the
+ * stride and k, so a row's record sits at the same place for every call.
+ * Rows of at most 16384 scores (logits_stride <= 16384) leave the workspace
+ * untouched.  Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
  */
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
 
@@ -148,21 +153,23 @@ size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
  * exact whole-row radix select -- the result is exact in every case.  With
  * hist == NULL the histogram is first built from the scores.
  *
- * logits      (device) float [rows][logits_stride], 16-B aligned, stride % 4 == 0
+ * logits      (device) float [rows][logits_stride], 16-B aligned, stride % 4 == 0,
+ *             logits_stride <= IDX_TOPK_MAX_STRIDE
  * hist        (device) int32 [rows][1024] or NULL; read only
  * context_lens(device) int32 [rows]; 0 <= len_r <= logits_stride
  * rows        1 .. IDX_MAX_ROWS;  k in 1 .. IDX_CANDIDATE_CAPACITY
  * key_dtype   IDX_KEY_FP32 or IDX_KEY_FP16
  * indices     (device) int32 [rows][k]
  * workspace   (device) scratch of at least topk_workspace_bytes(rows, ...) bytes,
- *             256-B aligned, zero-filled before its first use; every call
- *             leaves it ready for the next (also when a captured graph
- *             replays the call), so it is zeroed once.  Should it not start
- *             zeroed, results stay exact: the counts found in the scores then
- *             disagree with the counter pairs or with the histogram built on
- *             top of the garbage (hist == NULL), and those rows are selected
- *             from scratch.  Calls that share a workspace must be ordered on
- *             one stream.
+ *             256-B aligned, owned by the caller; it needs no initialisation.
+ *             Results are exact whatever it holds: the collect workgroups
+ *             store their counts beside the atomic counters they add to, and
+ *             a row whose counters did not start at zero (or whose workspace
+ *             histogram, hist == NULL, did not) is selected from scratch.
+ *             Every call leaves its rows' counters and built histograms zero
+ *             (also when a captured graph replays it), so only the first call
+ *             on a fresh or overwritten workspace takes that slower path.
+ *             Calls that share a workspace must be ordered on one stream.
  */
 idx_status topk_rows(const float* logits, int64_t logits_stride,
                      const int32_t* hist, const int32_t* context_lens,

@@ -47,8 +47,8 @@ __all__ = [
     "indexer_logits_mxfp4", "block_amax8", "sort_candidate_blocks", "indexer_sparse_logits",
     "indexer_sparse_logits_mxfp4", "indexer_prefill_logits", "indexer_prefill_logits_mxfp4",
     "sparse_to_logical",
-    "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram", "indexer_status_str",
-    "indexer_time_next_call", "hbm_read_probe",
+    "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram",
+    "indexer_status_str", "indexer_time_next_call", "hbm_read_probe",
 ]
 
 KEY_FP32 = 0
@@ -429,10 +429,10 @@ def _topk_call(name, dtype, logits, hist, context_lens, k, key_dtype, indices, w
         _need(hist, "hist", torch.int32, dev, 2)
         if tuple(hist.shape) != (rows, NUM_BINS) or not hist.is_contiguous():
             raise ValueError(f"hist must be contiguous [{rows}, 1024]")
-    need = topk_workspace_bytes(rows, logits.stride(0), k)
     if workspace is None:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, dev)
+        workspace = _device_workspace(dev, topk_workspace_bytes(rows, logits.stride(0), k))
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
     lib = load_library()
     with torch.cuda.device(dev):
         _arm(events, dev)
@@ -445,12 +445,28 @@ def _topk_call(name, dtype, logits, hist, context_lens, k, key_dtype, indices, w
     _check(name, st)
 
 
+# One workspace per device for calls that pass none, allocated the first time
+# a call needs more than the current one holds and reused after that.
+_workspaces: dict = {}
+
+
+def _device_workspace(dev: torch.device, need: int) -> torch.Tensor:
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
 def topk_rows(logits, hist, context_lens, k, key_dtype, indices, workspace=None, events=None):
     """Exact per-row top-k indices of float32 scores into ``indices`` [rows, k].
 
     ``workspace`` is a uint8 GPU tensor of at least topk_workspace_bytes()
-    bytes, zero-filled before its first use (calls keep it reusable); when
-    None a zeroed one is allocated with torch for this call.
+    bytes (no initialisation needed).  When None, the device's shared
+    workspace of this module is used (allocated, or grown, only when a call
+    needs more than it holds); calls that use it must be ordered on one
+    stream.
     """
     _topk_call("topk_rows", torch.float32, logits, hist, context_lens, k, key_dtype, indices,
                workspace, events)

@@ -64,7 +64,7 @@ idx_status topk_call(const void* logits, int64_t logits_stride, bool f16, const 
   if (rows <= 0 || logits_stride <= 0 || k < 1 || k > IDX_CANDIDATE_CAPACITY) return IDX_EINVAL;
   if (key_dtype != IDX_KEY_FP32 && key_dtype != IDX_KEY_FP16) return IDX_EUNSUPPORTED;
   const int64_t per16 = f16 ? 8 : 4;  // rows are read with 16-byte loads
-  if (rows > IDX_MAX_ROWS || logits_stride > (int64_t{1} << 31) - per16) return IDX_EUNSUPPORTED;
+  if (rows > IDX_MAX_ROWS || logits_stride > IDX_TOPK_MAX_STRIDE) return IDX_EUNSUPPORTED;
   if (!aligned(logits, 16) || (logits_stride % per16) != 0 || !aligned(context_lens, 4) ||
       !aligned(indices, 4) || !aligned(workspace, 256) || (hist && !aligned(hist, 8)))
     return IDX_EALIGN;

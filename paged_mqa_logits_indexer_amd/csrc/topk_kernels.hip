@@ -69,39 +69,54 @@ static_assert(kBins == 2 * kRefineThreads, "row and finish: two bins per thread"
 static_assert(kRowSpan <= kCandCap, "a whole row's candidates fit the LDS buffer");
 constexpr int kRowSpanMax = 2 * kRowSpan;  // 16384: rows topk_row takes in two parts per thread
 
-// Scratch of one call of the chunked path.  The counter pairs must be zero
-// when a call starts; the finish pass leaves them zero.  Each row has two
-// pairs: even collect workgroups place their columns from the front of the
-// output row and of the candidate buffer, odd ones from the back, which
-// halves the atomics on each counter; the lists meet in the middle only when
-// the counts contradict b*.
-struct Workspace {
-  unsigned long long* count;  // [rows][2]: (above b*) | (in b*) << 32, front and back
-  int* hist;                  // [rows][1024]: histograms built when the caller has none
-  uint2* cand;                // [rows][kCandCap]: (key, column) in b*
-};
+// Scratch of the chunked path, one fixed-size record per row, so a row's
+// counters sit at the same place whatever the call's row count or stride:
+//   counters  two (above b*) | (in b*) << 32 pairs.  Even collect workgroups
+//             place their columns from the front of the output row and of
+//             the candidate buffer, odd ones from the back, which halves the
+//             atomics on each counter; the lists meet in the middle only when
+//             the counts contradict b*.  The finish pass leaves them zero.
+//   hist      1024 bins, built here when the caller has no histogram (left
+//             zero by the finish pass as well)
+//   cand      8192 (key, column) candidates of b*
+//   slots     the two counts of each collect workgroup, stored (not added),
+//             so their sums are this call's true counts whatever the
+//             counters held before it: a counter pair that did not start at
+//             zero (a workspace never used before, or overwritten since) is
+//             detected exactly, and its row is selected from scratch.
+constexpr int kMaxCollectWgs = 1024;                 // per row: rows of up to 2^23 scores
+constexpr size_t kRecCount = 0;
+constexpr size_t kRecHist = 256;
+constexpr size_t kRecCand = kRecHist + sizeof(int) * kBins;
+constexpr size_t kRecSlots = kRecCand + sizeof(uint2) * kCandCap;
+constexpr size_t kRowScratchBytes = kRecSlots + sizeof(int) * kMaxCollectWgs;  // 73,984
+static_assert(kRowScratchBytes % 256 == 0, "records keep 256-byte alignment");
+constexpr int64_t kRecHistStride = static_cast<int64_t>(kRowScratchBytes / sizeof(int));  // ints per record
+constexpr int64_t kMaxChunkedStride = int64_t{2} * kMaxCollectWgs * kThreads * kPerThread;  // 2^23
 
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+struct Workspace {
+  char* base;
+  __device__ unsigned long long* count(int row) const {
+    return reinterpret_cast<unsigned long long*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecCount);
+  }
+  __host__ __device__ int* hist(int row) const {
+    return reinterpret_cast<int*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecHist);
+  }
+  __device__ uint2* cand(int row) const {
+    return reinterpret_cast<uint2*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecCand);
+  }
+  __device__ int* slots(int row) const {
+    return reinterpret_cast<int*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecSlots);
+  }
+};
 
 __host__ __device__ inline int chunks_for(int64_t stride) {
   return static_cast<int>((stride + kChunk - 1) / kChunk);
 }
 
-__host__ __device__ inline size_t workspace_size(int rows) {
-  return align256(sizeof(unsigned long long) * 2 * rows) + align256(sizeof(int) * kBins * static_cast<size_t>(rows)) +
-         sizeof(uint2) * kCandCap * static_cast<size_t>(rows);
-}
+__host__ __device__ inline size_t workspace_size(int rows) { return kRowScratchBytes * static_cast<size_t>(rows); }
 
-inline Workspace carve(void* base, int rows) {
-  char* p = static_cast<char*>(base);
-  Workspace w;
-  w.count = reinterpret_cast<unsigned long long*>(p);
-  p += align256(sizeof(unsigned long long) * 2 * rows);
-  w.hist = reinterpret_cast<int*>(p);
-  p += align256(sizeof(int) * kBins * static_cast<size_t>(rows));
-  w.cand = reinterpret_cast<uint2*>(p);
-  return w;
-}
+inline Workspace carve(void* base) { return Workspace{static_cast<char*>(base)}; }
 
 template <int KEY>
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -314,7 +329,8 @@ template <bool F16, int M>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restrict__ logits,
                                                              int64_t stride,
                                                              const int32_t* __restrict__ lens,
-                                                             int* __restrict__ hist_out) {
+                                                             int* __restrict__ hist_out,
+                                                             int64_t hist_stride) {
   __shared__ int s_hist[kBins];
   const int row = blockIdx.y;
   const int len = clamp_len(lens, row, stride);
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
     }
   }
   lds_barrier();
-  unsigned long long* gh = reinterpret_cast<unsigned long long*>(hist_out + static_cast<int64_t>(row) * kBins);
+  unsigned long long* gh = reinterpret_cast<unsigned long long*>(hist_out + row * hist_stride);
   const uint2* sh = reinterpret_cast<const uint2*>(s_hist);
   for (int i = threadIdx.x; i < kBins / 2; i += kThreads) {
     const uint2 w = sh[i];
@@ -373,6 +389,7 @@ template <int KEY, bool F16, int M>
 __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __restrict__ logits,
                                                                 int64_t stride,
                                                                 const int32_t* __restrict__ hist,
+                                                                int64_t hist_stride,
                                                                 const int32_t* __restrict__ lens, int k,
                                                                 int32_t* __restrict__ indices, Workspace ws) {
   __shared__ int s_red[kWaves + 5];
@@ -383,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
   if (first >= len) return;
 
   // The histogram and the chunks' scores are requested together.
-  const int* h = hist + static_cast<int64_t>(row) * kBins + tid * 4;
+  const int* h = hist + row * hist_stride + tid * 4;
   const int2 h01 = *reinterpret_cast<const int2*>(h);  // 8-B aligned
   const int2 h23 = *reinterpret_cast<const int2*>(h + 2);
   const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
@@ -413,11 +430,14 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
   // Both counts in one scan: each is at most M * kChunk < 2^16.
   int tot = 0;
   const int pre = block_excl_scan<kThreads>(mine, s_red, &tot);
+  // The workgroup's true counts, stored for the finish pass's check of the
+  // counters (blockIdx.x < kMaxCollectWgs: the host limits the stride).
+  if (tid == 0) ws.slots(row)[blockIdx.x] = tot;
   if (tot == 0) return;  // uniform
   if (tid == 0) {
     const unsigned long long add =
         static_cast<unsigned long long>(tot & 0xFFFF) | (static_cast<unsigned long long>(tot >> 16) << 32);
-    const unsigned long long base = atomicAdd(ws.count + 2 * row + (blockIdx.x & 1), add);
+    const unsigned long long base = atomicAdd(ws.count(row) + (blockIdx.x & 1), add);
     s_red[kWaves + 3] = static_cast<int>(static_cast<uint32_t>(base));
     s_red[kWaves + 4] = static_cast<int>(static_cast<uint32_t>(base >> 32));
   }
@@ -428,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
   // Place p counts from the front (even workgroups) or from the back (odd).
   const bool back = (blockIdx.x & 1) != 0;
   int32_t* out = indices + static_cast<int64_t>(row) * k;
-  uint2* cand = ws.cand + static_cast<int64_t>(row) * kCandCap;
+  uint2* cand = ws.cand(row);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
 #pragma unroll
@@ -1003,30 +1023,57 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
 
 // ---------------------------------------------------------------------------
 // One workgroup per row after topk_collect: the two counter pairs, the
-// thread's two bins and the first 1024 candidates from each end are requested
-// together (the candidate buffer has a fixed address; entries past the
-// counts are unused).
+// collect workgroups' stored counts, the thread's two bins and the first 1024
+// candidates from each end are requested together (the candidate buffer has a
+// fixed address; entries past the counts are unused).
 constexpr int kEarlyCand = 2;  // candidates per thread and end loaded with the counts
+constexpr int kSlotsPerThread = kMaxCollectWgs / kRefineThreads;
+static_assert(kSlotsPerThread * kRefineThreads == kMaxCollectWgs && kRefineThreads % 2 == 0,
+              "a thread's slots are all front or all back");
 
-__device__ __forceinline__ int saturate_int(uint32_t v) { return static_cast<int>(min(v, 0x3FFFFFFFu)); }
+// Block sums of four counts (one pair of LDS barriers).
+__device__ __forceinline__ i32x4 block_sum4(i32x4 v, int* s_red4) {
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v[c] = wave_sum(v[c]);
+    if (__lane_id() == 0) s_red4[4 * wave + c] = v[c];
+  }
+  lds_barrier();
+  i32x4 t{0, 0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < kRefineThreads / kWave; ++w)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] += s_red4[4 * w + c];
+  lds_barrier();
+  return t;
+}
 
 template <int KEY, bool F16>
 __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void* __restrict__ logits,
                                                                      int64_t stride,
                                                                      const int32_t* __restrict__ hist,
+                                                                     int64_t hist_stride, int own_hist,
                                                                      const int32_t* __restrict__ lens, int k,
                                                                      int32_t* __restrict__ indices,
-                                                                     Workspace ws) {
+                                                                     Workspace ws, int collect_span) {
   __shared__ RefineShared sh;
+  __shared__ int s_red4[4 * (kRefineThreads / kWave)];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int len = clamp_len(lens, row, stride);
   const void* x = score_row<F16>(logits, row, stride);
   int32_t* out = indices + static_cast<int64_t>(row) * k;
-  const uint2* cand = ws.cand + static_cast<int64_t>(row) * kCandCap;
+  const uint2* cand = ws.cand(row);
+  unsigned long long* count = ws.count(row);
+  // Collect workgroups that took part: those whose first column is below len.
+  const int n_wg = static_cast<int>((static_cast<int64_t>(len) + collect_span - 1) / collect_span);
 
-  const unsigned long long front = ws.count[2 * row], back = ws.count[2 * row + 1];
-  const int2 h = *reinterpret_cast<const int2*>(hist + static_cast<int64_t>(row) * kBins + 2 * tid);
+  const unsigned long long front = count[0], back = count[1];
+  const int2 h = *reinterpret_cast<const int2*>(hist + row * hist_stride + 2 * tid);
+  int slot[kSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) slot[j] = ws.slots(row)[j * kRefineThreads + tid];
   uint2 early_f[kEarlyCand], early_b[kEarlyCand];
 #pragma unroll
   for (int j = 0; j < kEarlyCand; ++j) {
@@ -1034,24 +1081,34 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
     early_b[j] = cand[kCandCap - 1 - (j * kRefineThreads + tid)];
   }
   const int hv[2] = {h.x, h.y};
-  const Threshold th = threshold_bin<kRefineThreads, 2>(hv, k, sh.red);
-  const int bstar = th.bin;
-  if (hist == ws.hist) {  // built by this call (no histogram given): the next call starts from zero
-    *reinterpret_cast<int2*>(ws.hist + static_cast<int64_t>(row) * kBins + 2 * tid) = make_int2(0, 0);
+  const int bstar = threshold_bin<kRefineThreads, 2>(hv, k, sh.red).bin;
+  // This call's true counts: the sums of the slots of the workgroups that
+  // ran, even ones (front pair) and odd ones (back pair) apart.
+  i32x4 mine{0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int v = j * kRefineThreads + tid < n_wg ? slot[j] : 0;
+    mine[(tid & 1) * 2 + 0] += v & 0xFFFF;
+    mine[(tid & 1) * 2 + 1] += v >> 16;
+  }
+  const i32x4 t = block_sum4(mine, s_red4);
+  if (own_hist) {  // built by this call (no histogram given): the next call starts from zero
+    *reinterpret_cast<int2*>(ws.hist(row) + 2 * tid) = make_int2(0, 0);
   }
   if (tid == 0) {  // the next call starts from zero
-    ws.count[2 * row] = 0ull;
-    ws.count[2 * row + 1] = 0ull;
+    count[0] = 0ull;
+    count[1] = 0ull;
   }
-  // Saturated: beyond k (or the capacity) the counts fail the check anyway.
-  const int gf = saturate_int(static_cast<uint32_t>(front)), ef = saturate_int(static_cast<uint32_t>(front >> 32));
-  const int gb = saturate_int(static_cast<uint32_t>(back)), eb = saturate_int(static_cast<uint32_t>(back >> 32));
+  // The counters must hold exactly this call's counts: a pair that did not
+  // start at zero shifted every place its workgroups took, so the row is
+  // selected from scratch rather than from places this call did not fill.
+  const bool counters_ok = static_cast<uint32_t>(front) == static_cast<uint32_t>(t[0]) &&
+                           static_cast<uint32_t>(front >> 32) == static_cast<uint32_t>(t[1]) &&
+                           static_cast<uint32_t>(back) == static_cast<uint32_t>(t[2]) &&
+                           static_cast<uint32_t>(back >> 32) == static_cast<uint32_t>(t[3]);
+  const int gf = t[0], ef = t[1], gb = t[2], eb = t[3];
   const int n_gt = gf + gb, n_eq = ef + eb;
-  // The counts must also equal the histogram's own: for an exact histogram
-  // they do, unless the counters did not start at zero (a workspace never
-  // used before), and then the row is selected from scratch rather than from
-  // places this call did not fill.
-  if (!counts_confirm(bstar, n_gt, n_eq, k) || n_gt != th.before || n_eq != th.count) {
+  if (!counters_ok || !counts_confirm(bstar, n_gt, n_eq, k)) {
     whole_row_select<KEY, F16>(sh, x, len, k, out);
     return;
   }
@@ -1122,20 +1179,22 @@ inline int chunks_per_collect(int chunks) { return chunks > 64 ? 2 : 1; }
 constexpr int kHistChunks = PMQA_TOPK_HIST_CHUNKS;
 
 template <int KEY, bool F16, int M>
-void launch_collect(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int chunks, hipStream_t stream,
-                    hipEvent_t start) {
+void launch_collect(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int64_t hist_stride, int chunks,
+                    hipStream_t stream, hipEvent_t start) {
   const dim3 grid(static_cast<unsigned>((chunks + M - 1) / M), static_cast<unsigned>(a.rows));
   launch_kernel(topk_collect_kernel<KEY, F16, M>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
-                a.logits_stride, hist, a.context_lens, a.k, a.indices, ws);
+                a.logits_stride, hist, hist_stride, a.context_lens, a.k, a.indices, ws);
 }
 
 template <int KEY, bool F16>
-void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int chunks, hipStream_t stream,
-                    hipEvent_t start, hipEvent_t stop) {
-  if (chunks_per_collect(chunks) == 2) launch_collect<KEY, F16, 2>(a, ws, hist, chunks, stream, start);
-  else launch_collect<KEY, F16, 1>(a, ws, hist, chunks, stream, start);
+void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist, int64_t hist_stride, bool own_hist,
+                    int chunks, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  const int m = chunks_per_collect(chunks);
+  if (m == 2) launch_collect<KEY, F16, 2>(a, ws, hist, hist_stride, chunks, stream, start);
+  else launch_collect<KEY, F16, 1>(a, ws, hist, hist_stride, chunks, stream, start);
   launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, a.logits,
-                a.logits_stride, hist, a.context_lens, a.k, a.indices, ws);
+                a.logits_stride, hist, hist_stride, own_hist ? 1 : 0, a.context_lens, a.k, a.indices, ws,
+                m * kChunk);
 }
 
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
@@ -1146,36 +1205,42 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents 
     else launch_rows_whole<IDX_KEY_FP16, false>(a, stream, ev);
     return hipGetLastError();
   }
-  const Workspace ws = carve(a.workspace, a.rows);
+  if (a.logits_stride > kMaxChunkedStride) return hipErrorInvalidValue;  // checked by the ABI first
+  const Workspace ws = carve(a.workspace);
   const int chunks = chunks_for(a.logits_stride);
   const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.rows));
   hipEvent_t start = ev.start;  // recorded by the first kernel of the call
   const int32_t* hist = a.hist;
+  int64_t hist_stride = kBins;
   if (hist == nullptr) {
-    // The workspace histograms are zero (at allocation, then left so by the
-    // finish pass); ones that are not make the counts contradict b*, and
-    // the row is selected from scratch.
+    // The workspace histograms are zero (left so by the finish pass); ones
+    // that are not are a stale histogram, which the counts in the scores
+    // overrule (the row is then selected from scratch).
+    int* wh = ws.hist(0);
     if (chunks > 64) {
       const dim3 hgrid(static_cast<unsigned>((chunks + kHistChunks - 1) / kHistChunks), static_cast<unsigned>(a.rows));
       if (a.logits_f16)
         launch_kernel(topk_hist_kernel<true, kHistChunks>, hgrid, dim3(kThreads), stream, start, nullptr, a.logits,
-                      a.logits_stride, a.context_lens, ws.hist);
+                      a.logits_stride, a.context_lens, wh, kRecHistStride);
       else
         launch_kernel(topk_hist_kernel<false, kHistChunks>, hgrid, dim3(kThreads), stream, start, nullptr, a.logits,
-                      a.logits_stride, a.context_lens, ws.hist);
+                      a.logits_stride, a.context_lens, wh, kRecHistStride);
     } else if (a.logits_f16) {
       launch_kernel(topk_hist_kernel<true, 1>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
-                    a.logits_stride, a.context_lens, ws.hist);
+                    a.logits_stride, a.context_lens, wh, kRecHistStride);
     } else {
       launch_kernel(topk_hist_kernel<false, 1>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
-                    a.logits_stride, a.context_lens, ws.hist);
+                    a.logits_stride, a.context_lens, wh, kRecHistStride);
     }
     start = nullptr;
-    hist = ws.hist;
+    hist = wh;
+    hist_stride = kRecHistStride;
   }
-  if (a.logits_f16) launch_chunked<IDX_KEY_FP16, true>(a, ws, hist, chunks, stream, start, ev.stop);
-  else if (a.key_dtype == IDX_KEY_FP32) launch_chunked<IDX_KEY_FP32, false>(a, ws, hist, chunks, stream, start, ev.stop);
-  else launch_chunked<IDX_KEY_FP16, false>(a, ws, hist, chunks, stream, start, ev.stop);
+  const bool own = a.hist == nullptr;
+  if (a.logits_f16) launch_chunked<IDX_KEY_FP16, true>(a, ws, hist, hist_stride, own, chunks, stream, start, ev.stop);
+  else if (a.key_dtype == IDX_KEY_FP32)
+    launch_chunked<IDX_KEY_FP32, false>(a, ws, hist, hist_stride, own, chunks, stream, start, ev.stop);
+  else launch_chunked<IDX_KEY_FP16, false>(a, ws, hist, hist_stride, own, chunks, stream, start, ev.stop);
   return hipGetLastError();
 }
 
@@ -1184,7 +1249,7 @@ hipError_t launch_score_histogram(const float* scores, int64_t stride, const int
   const int64_t chunks64 = (stride + kChunk - 1) / kChunk;
   if (chunks64 > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((topk_hist_kernel<false, 1>), dim3(static_cast<unsigned>(chunks64), static_cast<unsigned>(rows)),
-                     dim3(kThreads), 0, stream, scores, stride, lens, hist);
+                     dim3(kThreads), 0, stream, scores, stride, lens, hist, static_cast<int64_t>(kBins));
   return hipGetLastError();
 }
 

@@ -49,9 +49,10 @@ def test_status_strings(lib):
 
 
 def per_row_bytes(stride, k):
-    """The documented layout: per row two counter pairs, a histogram and 8192
-    candidates (whatever the stride and k)."""
-    return 16 + 4096 + 8 * 8192
+    """The documented layout: one record per row -- two counter pairs padded
+    to 256 bytes, a histogram, 8192 candidates and 1024 per-workgroup counts
+    (whatever the stride and k)."""
+    return 256 + 4096 + 8 * 8192 + 4 * 1024
 
 
 def test_workspace_query(lib):
@@ -61,8 +62,7 @@ def test_workspace_query(lib):
     for rows, stride, k in ((1, 131072, 2048), (8, 131072, 2048), (3, 4100, 1), (64, 262144, 8192),
                             (4, 1 << 20, 2048)):
         got = pmqa.topk_workspace_bytes(rows, stride, k)
-        want = rows * per_row_bytes(stride, k)
-        assert want <= got <= want + 2 * 256, (rows, stride, k)
+        assert got == rows * per_row_bytes(stride, k), (rows, stride, k)
 
 
 # Fake but aligned device addresses: every call below fails validation before
@@ -162,6 +162,7 @@ def topk_call(lib, **kw):
     (dict(ws=A + 128), IDX_EALIGN),
     (dict(hist=A + 4), IDX_EALIGN),
     (dict(ws_bytes=1024), IDX_EWORKSPACE),
+    (dict(stride=(1 << 23) + 4), IDX_EUNSUPPORTED),
 ])
 def test_topk_rows_rejects(lib, kw, status):
     assert topk_call(lib, **kw) == status

@@ -292,6 +292,69 @@ def test_topk_row_of_more_than_512_chunks(gpu):
         check_topk(idx.cpu().numpy(), buf, lens, 2048, key)
 
 
+def _threshold(hist_row, k):
+    """The selector's threshold bin of one histogram row: the least bin whose
+    running count reaches k (1024 when the row holds at most k), with the
+    histogram's count before it and in it."""
+    c = np.cumsum(hist_row.astype(np.int64))
+    if c[-1] <= k:
+        return 1024, int(c[-1]), 0
+    b = int(np.argmax(c >= k))
+    return b, int(c[b] - hist_row[b]), int(hist_row[b])
+
+
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+def test_topk_garbage_workspace_with_stale_histogram(gpu, key):
+    """A workspace nobody initialised, together with a stale histogram: random
+    bytes, 0xA5 everywhere, and counters crafted so that, added to this
+    call's true counts, they equal the stale histogram's own counts -- the
+    case a check of the counters against the histogram alone would pass
+    with shifted places.  Every call exact, and the next call on the same
+    workspace (now left clean) too."""
+    x = _small_inputs(1, 61, [20000, 9000, 3000, 12000])
+    d = DevInputs(x)
+    announce(f"topk_rows garbage workspace + stale histogram key={key}")
+    lg, h = d.run(with_hist=True, fill=INF)
+    got = lg.cpu().numpy()
+    lens = x.context_lens
+    rows = x.rows
+    rec = gpu.topk_workspace_bytes(1, lg.shape[1], 1)
+    assert rec % 8 == 0
+    stale = {
+        "exact": h.clone(),
+        "zeros": torch.zeros_like(h),
+        "doubled": 2 * h,
+        "rolled": torch.roll(h, 1, dims=0),
+        "shifted": torch.roll(h, 37, dims=1),
+    }
+    rng = np.random.default_rng(5)
+    for k in (100, 2048):
+        for name, hs in stale.items():
+            hs_np = hs.cpu().numpy()
+            for fill in ("random", "a5", "crafted"):
+                if fill == "random":
+                    ws = torch.from_numpy(rng.integers(0, 256, rows * rec, dtype=np.uint8)).to(DEV)
+                else:
+                    ws = torch.full((rows * rec,), 0xA5, dtype=torch.uint8, device=DEV)
+                if fill == "crafted":
+                    counters = np.zeros((rows, 2), np.uint64)
+                    for r in range(rows):
+                        b, before, count = _threshold(hs_np[r], k)
+                        bins = O.coarse_bin(got[r, :int(lens[r])])
+                        live = bins >= 0
+                        gt = int(np.sum(live & (bins < b)))
+                        eq = int(np.sum(bins == b))
+                        g_gt = (before - gt) % (1 << 32)
+                        g_eq = (count - eq) % (1 << 32)
+                        counters[r, 0] = np.uint64(g_gt | (g_eq << 32))
+                    w64 = ws.view(torch.int64).view(rows, rec // 8)
+                    w64[:, 0:2] = torch.from_numpy(counters.view(np.int64)).to(DEV)
+                for call in range(2):
+                    announce(f"topk_rows ws={fill} stale={name} k={k} key={key} call={call}")
+                    idx = topk(lg, hs, d.lens, k, key, workspace=ws)
+                    check_topk(idx.cpu().numpy(), got, lens, k, key)
+
+
 @pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
 def test_topk_without_histogram_reuses_its_workspace(gpu, key):
     """hist=NULL on rows longer than 8192: the selector builds its histograms
