@@ -54,7 +54,8 @@ typedef enum {
   IDX_EUNSUPPORTED = 2, /* next_n outside 1..4, unknown key dtype, size above limits  */
   IDX_EALIGN = 3,       /* a pointer or stride misses its required alignment          */
   IDX_ELAUNCH = 4,      /* the HIP runtime rejected a launch or the device query      */
-  IDX_EWORKSPACE = 5    /* workspace smaller than topk_workspace_bytes()              */
+  IDX_EWORKSPACE = 5,   /* workspace smaller than topk_workspace_bytes()              */
+  IDX_ESCRATCH = 6      /* topk_rows_noalloc: more rows than its fixed scratch holds  */
 } idx_status;
 
 /* Score key used by topk_rows.  FP32: the float32 score itself.  FP16: the
@@ -73,6 +74,8 @@ typedef enum { IDX_KEY_FP32 = 0, IDX_KEY_FP16 = 1 } idx_key_dtype;
 /* topk_rows: rows of more than 16384 scores go through the chunked path,
  * whose strides are limited to 2^23 (8x the longest context on the pages). */
 #define IDX_TOPK_MAX_STRIDE (1 << 23)
+/* topk_rows_noalloc: rows its fixed scratch holds (chunked path only). */
+#define IDX_NOALLOC_MAX_ROWS 256
 
 /*
  * indexer_logits -- paged MQA logits with an optional fused coarse histogram.
@@ -175,6 +178,26 @@ idx_status topk_rows(const float* logits, int64_t logits_stride,
                      const int32_t* hist, const int32_t* context_lens,
                      int32_t rows, int32_t k, int32_t key_dtype, int32_t* indices,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * topk_rows_noalloc -- topk_rows without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc).  The chunked path's per-row records
+ * (rows of more than 16384 scores) live in a fixed array of the library,
+ * IDX_NOALLOC_MAX_ROWS records = 18,939,904 bytes per GPU, held from the
+ * time the library is loaded until the process ends; its device address is
+ * looked up once per GPU, on the first call there.  The call allocates and
+ * frees nothing.  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must not
+ * be issued; calls ordered on one stream are fine.  Nothing in the array has
+ * to start at zero (see topk_rows' workspace).  Arguments as for topk_rows;
+ * rows > IDX_NOALLOC_MAX_ROWS with logits_stride > 16384 returns
+ * IDX_ESCRATCH before anything is launched.
+ */
+idx_status topk_rows_noalloc(const float* logits, int64_t logits_stride,
+                             const int32_t* hist, const int32_t* context_lens,
+                             int32_t rows, int32_t k, int32_t key_dtype, int32_t* indices,
+                             void* stream);
 
 /*
  * score_histogram -- the selector's own first pass ([P1] "Motivation": the

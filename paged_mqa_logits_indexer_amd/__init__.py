@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
             events=None)                                          float32 scores
   topk_rows_f16(logits, hist, context_lens, k, indices, workspace=None,
                 events=None)                                      float16 scores
+  topk_rows_noalloc(logits, hist, context_lens, k, key_dtype, indices,
+                    events=None)          float32 scores, the library's fixed scratch
   score_histogram(scores, context_lens, hist)
   block_amax8(scores, context_lens, out)                       two-level candidate indexer:
   sort_candidate_blocks(blocks, context_lens, max_len, block_table, next_n,
@@ -47,7 +49,7 @@ __all__ = [
     "indexer_logits_mxfp4", "block_amax8", "sort_candidate_blocks", "indexer_sparse_logits",
     "indexer_sparse_logits_mxfp4", "indexer_prefill_logits", "indexer_prefill_logits_mxfp4",
     "sparse_to_logical",
-    "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "score_histogram",
+    "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "topk_rows_noalloc", "score_histogram",
     "indexer_status_str", "indexer_time_next_call", "hbm_read_probe",
 ]
 
@@ -63,7 +65,7 @@ MXFP4_TOKEN_BYTES = 68
 EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp4", "block_amax8",
                     "sort_candidate_blocks", "indexer_sparse_logits", "indexer_sparse_logits_mxfp4",
                     "indexer_prefill_logits", "indexer_prefill_logits_mxfp4", "sparse_to_logical",
-                    "topk_workspace_bytes", "topk_rows",
+                    "topk_workspace_bytes", "topk_rows", "topk_rows_noalloc",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
                     "indexer_time_next_call", "hbm_read_probe")
 
@@ -128,6 +130,8 @@ def load_library() -> ctypes.CDLL:
     lib.sparse_to_logical.restype = ctypes.c_int
     lib.topk_rows_f16.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.topk_rows_f16.restype = ctypes.c_int
+    lib.topk_rows_noalloc.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
+    lib.topk_rows_noalloc.restype = ctypes.c_int
     lib.indexer_time_next_call.argtypes = [vp, vp]
     lib.indexer_time_next_call.restype = ctypes.c_int
     _lib = lib
@@ -429,7 +433,9 @@ def _topk_call(name, dtype, logits, hist, context_lens, k, key_dtype, indices, w
         _need(hist, "hist", torch.int32, dev, 2)
         if tuple(hist.shape) != (rows, NUM_BINS) or not hist.is_contiguous():
             raise ValueError(f"hist must be contiguous [{rows}, 1024]")
-    if workspace is None:
+    if name == "topk_rows_noalloc":
+        workspace = None
+    elif workspace is None:
         workspace = _device_workspace(dev, topk_workspace_bytes(rows, logits.stride(0), k))
     else:
         _need(workspace, "workspace", torch.uint8, dev)
@@ -437,7 +443,10 @@ def _topk_call(name, dtype, logits, hist, context_lens, k, key_dtype, indices, w
     with torch.cuda.device(dev):
         _arm(events, dev)
         head = (_ptr(logits), int(logits.stride(0)), _ptr(hist), _ptr(context_lens), int(rows), int(k))
-        tail = (_ptr(indices), _ptr(workspace), int(workspace.numel()), _stream_ptr(dev))
+        if workspace is None:
+            tail = (_ptr(indices), _stream_ptr(dev))
+        else:
+            tail = (_ptr(indices), _ptr(workspace), int(workspace.numel()), _stream_ptr(dev))
         if key_dtype is None:
             st = getattr(lib, name)(*head, *tail)
         else:
@@ -476,6 +485,14 @@ def topk_rows_f16(logits, hist, context_lens, k, indices, workspace=None, events
     """topk_rows over float16 scores [rows, stride] (stride % 8 == 0), FP16 keys."""
     _topk_call("topk_rows_f16", torch.float16, logits, hist, context_lens, k, None, indices,
                workspace, events)
+
+
+def topk_rows_noalloc(logits, hist, context_lens, k, key_dtype, indices, events=None):
+    """topk_rows with the library's fixed per-GPU scratch instead of a workspace
+    (at most 256 rows when rows hold more than 16384 scores); allocates
+    nothing.  Calls that overlap on one GPU race on that scratch."""
+    _topk_call("topk_rows_noalloc", torch.float32, logits, hist, context_lens, k, key_dtype, indices,
+               None, events)
 
 
 def score_histogram(scores, context_lens, hist):

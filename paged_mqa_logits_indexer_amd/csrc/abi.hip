@@ -56,19 +56,25 @@ idx_status logits_call(const uint8_t* q, const uint8_t* kv_pages, const float* k
   return from_hip(pmqa::launch_indexer_logits(a, static_cast<hipStream_t>(stream), ev));
 }
 
+// noalloc: topk_rows_noalloc, whose scratch is the library's fixed array.
 idx_status topk_call(const void* logits, int64_t logits_stride, bool f16, const int32_t* hist,
                      const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
-                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
+                     int32_t* indices, void* workspace, size_t workspace_bytes, void* stream,
+                     bool noalloc = false) {
   const pmqa::LaunchEvents ev = take_events();
-  if (!logits || !context_lens || !indices || !workspace) return IDX_EINVAL;
+  if (!logits || !context_lens || !indices || (!noalloc && !workspace)) return IDX_EINVAL;
   if (rows <= 0 || logits_stride <= 0 || k < 1 || k > IDX_CANDIDATE_CAPACITY) return IDX_EINVAL;
   if (key_dtype != IDX_KEY_FP32 && key_dtype != IDX_KEY_FP16) return IDX_EUNSUPPORTED;
   const int64_t per16 = f16 ? 8 : 4;  // rows are read with 16-byte loads
   if (rows > IDX_MAX_ROWS || logits_stride > IDX_TOPK_MAX_STRIDE) return IDX_EUNSUPPORTED;
   if (!aligned(logits, 16) || (logits_stride % per16) != 0 || !aligned(context_lens, 4) ||
-      !aligned(indices, 4) || !aligned(workspace, 256) || (hist && !aligned(hist, 8)))
+      !aligned(indices, 4) || (!noalloc && !aligned(workspace, 256)) || (hist && !aligned(hist, 8)))
     return IDX_EALIGN;
-  if (workspace_bytes < pmqa::topk_workspace_size(rows, logits_stride, k)) return IDX_EWORKSPACE;
+  if (noalloc) {
+    if (logits_stride > 16384 && rows > IDX_NOALLOC_MAX_ROWS) return IDX_ESCRATCH;
+  } else if (workspace_bytes < pmqa::topk_workspace_size(rows, logits_stride, k)) {
+    return IDX_EWORKSPACE;
+  }
   pmqa::TopkArgs a;
   a.logits = logits;
   a.hist = hist;
@@ -80,6 +86,7 @@ idx_status topk_call(const void* logits, int64_t logits_stride, bool f16, const 
   a.k = k;
   a.key_dtype = f16 ? IDX_KEY_FP16 : key_dtype;
   a.logits_f16 = f16 ? 1 : 0;
+  if (noalloc) return from_hip(pmqa::launch_topk_rows_noalloc(a, static_cast<hipStream_t>(stream), ev));
   return from_hip(pmqa::launch_topk_rows(a, static_cast<hipStream_t>(stream), ev));
 }
 
@@ -95,6 +102,8 @@ const char* indexer_status_str(int32_t s) {
     case IDX_EALIGN: return "IDX_EALIGN: misaligned pointer or stride";
     case IDX_ELAUNCH: return "IDX_ELAUNCH: HIP launch or device query failed";
     case IDX_EWORKSPACE: return "IDX_EWORKSPACE: workspace too small";
+    case IDX_ESCRATCH:
+      return "IDX_ESCRATCH: more rows than the fixed scratch of topk_rows_noalloc holds (IDX_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
   }
 }
@@ -140,6 +149,13 @@ idx_status topk_rows(const float* logits, int64_t logits_stride, const int32_t* 
                      int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
   return topk_call(logits, logits_stride, false, hist, context_lens, rows, k, key_dtype, indices,
                    workspace, workspace_bytes, stream);
+}
+
+idx_status topk_rows_noalloc(const float* logits, int64_t logits_stride, const int32_t* hist,
+                             const int32_t* context_lens, int32_t rows, int32_t k, int32_t key_dtype,
+                             int32_t* indices, void* stream) {
+  return topk_call(logits, logits_stride, false, hist, context_lens, rows, k, key_dtype, indices, nullptr, 0,
+                   stream, true);
 }
 
 idx_status topk_rows_f16(const uint16_t* logits, int64_t logits_stride, const int32_t* hist,

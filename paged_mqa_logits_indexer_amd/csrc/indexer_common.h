@@ -247,6 +247,9 @@ struct TopkArgs {
 };
 size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k);
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev = {});
+// topk_rows with the library's fixed per-device scratch (no workspace).
+size_t topk_noalloc_scratch_bytes();
+hipError_t launch_topk_rows_noalloc(const TopkArgs& a, hipStream_t stream, LaunchEvents ev = {});
 
 hipError_t launch_score_histogram(const float* scores, int64_t stride, const int32_t* lens,
                                   int32_t rows, int32_t* hist, hipStream_t stream);

@@ -51,6 +51,8 @@
 // n_gt < k <= n_gt + n_eq, the top-k is those n_gt columns plus the best
 // k - n_gt of the candidates.  Any other count means the histogram was not the
 // histogram of these scores, and the row is selected from scratch.
+#include <mutex>
+
 #include "bin_key_range.h"
 #include "indexer_common.h"
 
@@ -1242,6 +1244,55 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents 
     launch_chunked<IDX_KEY_FP32, false>(a, ws, hist, hist_stride, own, chunks, stream, start, ev.stop);
   else launch_chunked<IDX_KEY_FP16, false>(a, ws, hist, hist_stride, own, chunks, stream, start, ev.stop);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// topk_rows_noalloc: the chunked path's per-row records for up to
+// IDX_NOALLOC_MAX_ROWS rows live in this fixed device array instead of a
+// caller's workspace.  Each GPU holds its own copy from the time the library
+// is loaded until the process ends; host code reaches it only through the
+// device address hipGetSymbolAddress returns for the current device (the
+// array's name is a host-side stand-in, not a device address).  Nothing in
+// it has to start at zero: the finish pass checks the counters against the
+// stored per-workgroup counts and leaves counters and built histograms zero.
+constexpr size_t kNoallocBytes = kRowScratchBytes * IDX_NOALLOC_MAX_ROWS;  // 18,939,904
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (on its first call) with that device current.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+size_t topk_noalloc_scratch_bytes() { return kNoallocBytes; }
+
+hipError_t launch_topk_rows_noalloc(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
+  TopkArgs b = a;
+  if (a.logits_stride > kRowSpanMax) {  // only the chunked path uses scratch
+    if (a.rows > IDX_NOALLOC_MAX_ROWS) return hipErrorInvalidValue;  // checked by the ABI first
+    hipError_t e = scratch_address(&b.workspace);
+    if (e != hipSuccess) return e;
+  }
+  return launch_topk_rows(b, stream, ev);
 }
 
 hipError_t launch_score_histogram(const float* scores, int64_t stride, const int32_t* lens,

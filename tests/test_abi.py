@@ -12,7 +12,7 @@ import paged_mqa_logits_indexer_amd as pmqa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_mqa_indexer.h")
 
-IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_ELAUNCH, IDX_EWORKSPACE = range(6)
+IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EALIGN, IDX_ELAUNCH, IDX_EWORKSPACE, IDX_ESCRATCH = range(7)
 
 
 def declared_functions():
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert pmqa.indexer_status_str(code).startswith("IDX_")
     assert "unknown" in pmqa.indexer_status_str(99)
 
@@ -166,6 +166,32 @@ def topk_call(lib, **kw):
 ])
 def test_topk_rows_rejects(lib, kw, status):
     assert topk_call(lib, **kw) == status
+
+
+def noalloc_call(lib, **kw):
+    args = dict(logits=A, stride=256, hist=None, lens=A, rows=8, k=2048, key=0, idx=A, stream=None)
+    args.update(kw)
+    return lib.topk_rows_noalloc(args["logits"], args["stride"], args["hist"], args["lens"],
+                                 args["rows"], args["k"], args["key"], args["idx"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), IDX_EINVAL),
+    (dict(lens=None), IDX_EINVAL),
+    (dict(idx=None), IDX_EINVAL),
+    (dict(rows=0), IDX_EINVAL),
+    (dict(k=8193), IDX_EINVAL),
+    (dict(key=2), IDX_EUNSUPPORTED),
+    (dict(stride=(1 << 23) + 4), IDX_EUNSUPPORTED),
+    (dict(logits=A + 4), IDX_EALIGN),
+    (dict(hist=A + 4), IDX_EALIGN),
+    # the fixed scratch holds 256 rows of the chunked path (stride > 16384)
+    (dict(rows=257, stride=16388), IDX_ESCRATCH),
+    (dict(rows=65535, stride=1 << 20), IDX_ESCRATCH),
+])
+def test_topk_rows_noalloc_rejects(lib, kw, status):
+    assert noalloc_call(lib, **kw) == status
+    assert "IDX_ESCRATCH" in pmqa.indexer_status_str(IDX_ESCRATCH)
 
 
 @pytest.mark.parametrize("kw,status", [
