@@ -263,6 +263,38 @@ def head_sum_at(q, kv_pages, k_scales, weights, block_table, next_n, row, cols):
     return weights[row].astype(np.float64) @ np.maximum(qd @ keys.T, 0.0)
 
 
+def logits_terms_at(q, kv_pages, k_scales, weights, block_table, next_n, rows, cols,
+                    rel=1e-5):
+    """For rows of one request at the key positions ``cols``: the expected
+    logits and the three acceptance terms, from one gather of the keys.
+
+    Returns (want, bound, head_sum, head_bound), each float [len(rows), n]:
+    row by row the values of indexer_logits_at, logits_error_bound_at (with
+    and without the scale) and head_sum_at -- the same expressions, so the
+    same numbers (the dot products are exact in float64; the head sums are
+    the same vector-matrix products as there).
+    """
+    b = rows[0] // next_n
+    if any(r // next_n != b for r in rows):
+        raise ValueError("rows of one request only")
+    keys, sc = _request_keys_at(kv_pages, k_scales, block_table[b], cols)
+    abs_keys_t = np.abs(keys).T
+    out = [np.empty((len(rows), len(cols)), dtype) for dtype in
+           (np.float32, np.float64, np.float64, np.float64)]
+    for i, r in enumerate(rows):
+        qd = decode_e4m3fn(q[r])
+        dots = qd @ keys.T
+        w = weights[r].astype(np.float64)
+        head_sum = w @ np.maximum(dots, 0.0)
+        head = np.abs(w) @ (np.abs(qd) @ abs_keys_t)
+        with np.errstate(invalid="ignore", over="ignore"):
+            out[0][i] = (sc * head_sum).astype(np.float32)
+            out[1][i] = rel * np.abs(sc) * head
+        out[2][i] = head_sum
+        out[3][i] = rel * head
+    return tuple(out)
+
+
 def check_logits(got, want, bound, head_sum=None, head_bound=None):
     """Element-wise acceptance of GPU logits against the oracle.
 

@@ -57,7 +57,7 @@ namespace {
 #define PMQA_LOGITS_PERSIST_PPW 64  // <= PMQA_LOGITS_MAX_PPW
 #endif
 #ifndef PMQA_LOGITS_PERSIST_WGS_PER_CU
-#define PMQA_LOGITS_PERSIST_WGS_PER_CU 2
+#define PMQA_LOGITS_PERSIST_WGS_PER_CU 0  // 0: one per CU when the K pages go through LDS, else two
 #endif
 #ifndef PMQA_LOGITS_WAVES_MANY_ROWS
 #define PMQA_LOGITS_WAVES_MANY_ROWS 8
@@ -67,8 +67,11 @@ namespace {
 // 8 per CU rather than two of 4, so that every wave's start-up loads are
 // issued before any of them streams K (a second workgroup's loads would queue
 // behind the first one's pages in the CU's memory pipeline).
+#ifndef PMQA_LOGITS_WAVES_ONE_ROW
+#define PMQA_LOGITS_WAVES_ONE_ROW 4
+#endif
 template <int NN>
-constexpr int kWavesOf = NN >= 3 ? PMQA_LOGITS_WAVES_MANY_ROWS : 4;
+constexpr int kWavesOf = NN >= 3 ? PMQA_LOGITS_WAVES_MANY_ROWS : (NN == 1 ? PMQA_LOGITS_WAVES_ONE_ROW : 4);
 constexpr int kPrefetch = PMQA_LOGITS_PREFETCH;  // pages in flight per wave
 // MXFP4 pages are half the bytes: with one row per request a wave keeps two
 // of them in flight (measured 18.6 -> 16.8 us at long decode; with more rows
@@ -145,6 +148,142 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, u
                                            0x00020000);
 }
 
+// FP8 pages of one-row requests go HBM -> LDS with buffer loads that write
+// LDS directly (no VGPRs), each instruction a contiguous kilobyte -- 8 whole
+// keys, full 128-byte lines -- with the 16-byte pieces permuted inside it, so
+// that ds_read_b128 then fetches the MFMA operand layout (16 keys x 16 bytes
+// per lane group) without LDS bank conflicts.  Read straight into registers
+// in operand layout, every load instruction touches 16 half lines instead
+// (measured on a paged-gather probe over the long-decode pool: 1.2-1.3 us
+// slower at 138 MB).  Each wave keeps a ring of kRing page slots.
+#ifndef PMQA_LOGITS_DMA
+#define PMQA_LOGITS_DMA 1
+#endif
+#ifndef PMQA_LOGITS_DMA_RING
+#define PMQA_LOGITS_DMA_RING 2
+#endif
+template <int NN, int KF>
+constexpr bool kDmaOf = PMQA_LOGITS_DMA && NN == 1 && KF == kKFp8;
+constexpr int kRing = PMQA_LOGITS_DMA_RING;
+static_assert(kRing >= 2 && kRing <= 3, "ring depth: the waits below cover 2 or 3 slots");
+// With the page ring, each wave stores its page's scores as soon as they are
+// computed (the waits on the page loads count loads only, so stores in
+// between cost them nothing) instead of staging the share's scores in LDS
+// for stores after its last page.
+#ifndef PMQA_LOGITS_DIRECT_STORE
+#define PMQA_LOGITS_DIRECT_STORE 0
+#endif
+#ifndef PMQA_LOGITS_NT_STORE
+#define PMQA_LOGITS_NT_STORE 0
+#endif
+template <int NN, int KF>
+constexpr bool kDirectOf = kDmaOf<NN, KF> && PMQA_LOGITS_DIRECT_STORE;
+constexpr int kSlotBytes = kPageBytes + kPage * 4;  // K codes, then the 64 scales
+constexpr int kDmaInstrs = kPageBytes / 1024 + 1;   // per page: 8 K kilobytes + the scales
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS offset, inside a page slot, of 16-byte piece j (0..7) of key 8 i + kk:
+// pieces of a key stay in its 128 bytes, exchanged by an XOR that differs
+// between even and odd kilobytes, so the 16 keys an operand read touches
+// (8 of an even and 8 of an odd kilobyte, one piece each) fall on 16
+// different 16-byte bank groups.
+__device__ __forceinline__ int dma_piece(int i, int kk, int j) {
+  return i * 1024 + kk * 128 + ((j ^ ((kk >> 1) | ((i & 1) << 2))) * 16);
+}
+
+// Per-lane source offsets of the page loads: instruction i, lane l takes
+// piece (l & 7) ^ f of key 8 i + (l >> 3), the piece dma_piece() puts in LDS
+// slot l of kilobyte i.
+struct DmaOffsets {
+  uint32_t k[kPageBytes / 1024];
+  uint32_t scale;
+  __device__ explicit DmaOffsets(int lane) {
+    const int kk = lane >> 3;
+#pragma unroll
+    for (int i = 0; i < kPageBytes / 1024; ++i)
+      k[i] = static_cast<uint32_t>(i * 1024 + kk * 128 + (((lane & 7) ^ ((kk >> 1) | ((i & 1) << 2))) * 16));
+    scale = static_cast<uint32_t>(lane * 4);
+  }
+};
+
+// Issue one page into an LDS slot: eight kilobyte loads (keys 8i..8i+7, whole
+// lines) and the 64 scales, each writing LDS at m0 + 16 (or 4) x lane.
+// Written out in assembly so that the compiler, which cannot tell the ring's
+// slots apart, does not drain every load in flight before each LDS access of
+// the page loop; the caller waits for them itself (vmcnt, in issue order).
+// A load that writes LDS must not directly follow the write of m0 that
+// addresses it (one wait state on this GPU family): hence the s_nop after each.
+__device__ __forceinline__ void dma_page(const uint8_t* __restrict__ kv_pages, const float* __restrict__ k_scales,
+                                         int page, const DmaOffsets& off, uint32_t slot) {
+  const uint8_t* kp = kv_pages + static_cast<int64_t>(page) * kPageBytes;
+  const float* sp = k_scales + static_cast<int64_t>(page) * kPage;
+  __asm__ volatile(
+      "s_mov_b32 m0, %[l0]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v0], %[kb]\n"
+      "s_mov_b32 m0, %[l1]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v1], %[kb]\n"
+      "s_mov_b32 m0, %[l2]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v2], %[kb]\n"
+      "s_mov_b32 m0, %[l3]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v3], %[kb]\n"
+      "s_mov_b32 m0, %[l4]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v4], %[kb]\n"
+      "s_mov_b32 m0, %[l5]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v5], %[kb]\n"
+      "s_mov_b32 m0, %[l6]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v6], %[kb]\n"
+      "s_mov_b32 m0, %[l7]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v7], %[kb]\n"
+      "s_mov_b32 m0, %[l8]\n"
+      "s_nop 0\n"
+      "global_load_lds_dword %[vs], %[sb]\n"
+      :
+      : [kb] "s"(kp), [sb] "s"(sp), [l0] "s"(slot), [l1] "s"(slot + 1024), [l2] "s"(slot + 2048),
+        [l3] "s"(slot + 3072), [l4] "s"(slot + 4096), [l5] "s"(slot + 5120), [l6] "s"(slot + 6144),
+        [l7] "s"(slot + 7168), [l8] "s"(slot + kPageBytes), [v0] "v"(off.k[0]), [v1] "v"(off.k[1]),
+        [v2] "v"(off.k[2]), [v3] "v"(off.k[3]), [v4] "v"(off.k[4]), [v5] "v"(off.k[5]), [v6] "v"(off.k[6]),
+        [v7] "v"(off.k[7]), [vs] "v"(off.scale)
+      : "memory", "m0");
+}
+
+// The MFMA operands of a page slot: lane (n, g) reads pieces g and 4 + g of
+// key 16 kb + n, and the scale of key `lane`.  The reads are written out with
+// their own wait: the compiler would otherwise drain every page in flight
+// before them (it cannot tell the ring's slots apart), and a load written in
+// assembly must complete inside its own statement.
+__device__ __forceinline__ void read_page(uint32_t base, int lane, PageRegs<kKFp8>& r) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint32_t a0 = base + dma_piece(n >> 3, n & 7, g);      // half 0, key block 0
+  const uint32_t a1 = base + dma_piece(n >> 3, n & 7, g + 4);  // half 1, key block 0
+  const uint32_t as = base + kPageBytes + lane * 4;
+  float sc;
+  __asm__ volatile(
+      "ds_read_b128 %0, %9\n"
+      "ds_read_b128 %1, %10\n"
+      "ds_read_b128 %2, %9 offset:2048\n"
+      "ds_read_b128 %3, %10 offset:2048\n"
+      "ds_read_b128 %4, %9 offset:4096\n"
+      "ds_read_b128 %5, %10 offset:4096\n"
+      "ds_read_b128 %6, %9 offset:6144\n"
+      "ds_read_b128 %7, %10 offset:6144\n"
+      "ds_read_b32 %8, %11\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.v[2]), "=&v"(r.v[3]), "=&v"(r.v[4]), "=&v"(r.v[5]),
+        "=&v"(r.v[6]), "=&v"(r.v[7]), "=&v"(sc)
+      : "v"(a0), "v"(a1), "v"(as)
+      : "memory");
+  r.scale = sc;
+}
+
 // One page of K in MFMA operand layout plus the scale of key `lane`.  Buffer
 // loads take the page's base from scalar registers and a loop-invariant
 // per-lane offset, so no address register is rewritten from one page to the
@@ -213,10 +352,11 @@ struct RequestRegs {
 // global store issued between this page and the next one's prefetch would
 // have to complete before that page counts as arrived: the vector-memory
 // counter covers loads and stores in issue order.
-template <int NN, bool HIST, bool F16, int KF>
+template <int NN, bool HIST, bool F16, int KF, bool DIRECT = false>
 __device__ __forceinline__ void compute_page(const PageRegs<KF>& pr, int lp, int lpi, int ppw,
                                              int lane, const RequestRegs<NN>& rq,
-                                             StageT<F16>* s_out, int* s_hist) {
+                                             StageT<F16>* s_out, int* s_hist,
+                                             StageT<F16>* __restrict__ out_row = nullptr) {
   const int key = lp * kPage + lane;
 #pragma unroll
   for (int j = 0; j < NN; ++j) {
@@ -255,8 +395,20 @@ __device__ __forceinline__ void compute_page(const PageRegs<KF>& pr, int lp, int
     const float logit = as_stored(head_sum);
     uint32_t hb = 0u;
     if constexpr (HIST || F16) hb = f16_bits_rn(logit);
-    if constexpr (F16) s_out[(j * ppw + lpi) * kPage + lane] = static_cast<uint16_t>(hb);
-    else s_out[(j * ppw + lpi) * kPage + lane] = logit;
+    if constexpr (DIRECT) {
+      // one row (DIRECT is the one-row path): store the live score right away
+      StageT<F16> v;
+      if constexpr (F16) v = static_cast<uint16_t>(hb);
+      else v = logit;
+      if (key < rq.len[0]) {
+        if constexpr (PMQA_LOGITS_NT_STORE) __builtin_nontemporal_store(v, out_row + key);
+        else out_row[key] = v;
+      }
+    } else if constexpr (F16) {
+      s_out[(j * ppw + lpi) * kPage + lane] = static_cast<uint16_t>(hb);
+    } else {
+      s_out[(j * ppw + lpi) * kPage + lane] = logit;
+    }
     if constexpr (HIST && NN >= 2) {
       // Several rows: every lane adds, without a branch, so the binning
       // interleaves with the next row's MFMAs (spec verify 20.8 -> 19.1 us);
@@ -275,15 +427,17 @@ __device__ __forceinline__ void compute_page(const PageRegs<KF>& pr, int lp, int
 
 // Resident waves per SIMD the register budget is held to: 4 for one row per
 // request (128 VGPRs), 3 for two rows, 2 for three or four.
+// (One row with the LDS page ring: its LDS holds one workgroup per CU.)
 template <int NN>
-constexpr int kWavesPerSimd = NN == 1 ? (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 3 : 2))
+constexpr int kWavesPerSimd = NN == 1 ? (PMQA_LOGITS_DMA ? 1 : (kPrefetch == 1 ? 4 : (kPrefetch == 2 ? 3 : 2)))
                                       : (NN == 2 && kPrefetch == 1 ? 3 : 2);
 
 // One share of the grid: pages [p0_64, p0_64 + pages_per_wg) of request b
 // (the workgroup returns at once if that is past the request's last page).
 template <int NN, bool HIST, bool F16, int KF>
 __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_wg, int b, int64_t p0_64,
-                                             int* s_hist, StageT<F16>* s_out, i32x4* s_q, float* s_w) {
+                                             int* s_hist, StageT<F16>* s_out, i32x4* s_q, float* s_w,
+                                             char* s_ring) {
   constexpr int kWaves = kWavesOf<NN>;
   constexpr int kThreads = kThreadsOf<NN>;
   const int tid = threadIdx.x;
@@ -423,10 +577,48 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
       rq.q[0][mb][1] = q_slice[mb * 2 + 1];
       rq.w[0][mb] = w_direct[mb];
     }
-    prefetch();
+    if constexpr (!kDmaOf<NN, KF>) prefetch();
   }
 
-  if (n_mine > 0) {
+  if constexpr (kDmaOf<NN, KF>) {
+    // Ring of kRing LDS slots per wave: while page `it` is read and computed,
+    // pages it+1 .. it+kRing-1 are in flight (past the last page the last one
+    // is issued again, which keeps the count of loads behind each page
+    // fixed).  The compiler does not order LDS reads after these loads, so
+    // the waits are explicit: before a slot is refilled, every LDS access
+    // issued so far has completed (its last reads are a page old); before a
+    // page is read, at most the (kRing - 1) * kDmaInstrs loads issued after
+    // it are outstanding -- the loop issues no other vector memory operation,
+    // and loads complete in issue order.
+    // The compiler does not see the page loads (assembly), so it would place
+    // its waits for Q and the weights at their first use inside the loop,
+    // where they would drain the loads in flight on every page; consuming
+    // them here makes it wait once, before the first page is issued.
+    __asm__ volatile("" ::"v"(rq.q[0][0][0]), "v"(rq.q[0][0][1]), "v"(rq.q[0][1][0]), "v"(rq.q[0][1][1]),
+                     "v"(rq.w[0][0]), "v"(rq.w[0][1]));
+    if (n_mine > 0) {
+      const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(s_ring))) +
+                            static_cast<uint32_t>(wave * (kRing * kSlotBytes));
+      const DmaOffsets off(lane);
+#pragma unroll
+      for (int s = 0; s < kRing - 1; ++s)
+        dma_page(a.kv_pages, a.k_scales, page_id(s < n_mine ? s : n_mine - 1), off, ring + s * kSlotBytes);
+      for (int it = 0; it < n_mine; ++it) {
+        const int nx = it + kRing - 1 < n_mine ? it + kRing - 1 : n_mine - 1;
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        dma_page(a.kv_pages, a.k_scales, page_id(nx), off, ring + ((it + kRing - 1) % kRing) * kSlotBytes);
+        if constexpr (kRing == 2) __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else __asm__ volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        PageRegs<KF> pr;
+        read_page(ring + (it % kRing) * kSlotBytes, lane, pr);
+        compute_page<NN, HIST, F16, KF, kDirectOf<NN, KF>>(
+            pr, p0 + lpi0 + it * kWaves, lpi0 + it * kWaves, pages_per_wg, lane, rq, s_out, s_hist,
+            static_cast<StageT<F16>*>(a.logits) + static_cast<int64_t>(row0) * a.logits_stride);
+      }
+      // the re-issued last pages land before the slots can be refilled
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  } else if (n_mine > 0) {
     for (int it0 = 0; it0 < n_mine; it0 += kRg) {
 #pragma unroll
       for (int s = 0; s < kRg; ++s) {
@@ -445,7 +637,7 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
   // p0 * 64 and the stride are multiples of 16 bytes: 4 floats, 8 halves).
   constexpr int kPerVec = 16 / static_cast<int>(sizeof(StageT<F16>));
 #pragma unroll
-  for (int j = 0; j < NN; ++j) {
+  for (int j = 0; j < (kDirectOf<NN, KF> ? 0 : NN); ++j) {
     const int64_t k0 = static_cast<int64_t>(p0) * kPage;
     // Live scores of this share (none for a workgroup past the request's end).
     const int n = max(0, static_cast<int>(min(static_cast<int64_t>(p1) * kPage, static_cast<int64_t>(rq.len[j])) - k0));
@@ -491,10 +683,12 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   __shared__ __align__(16) i32x4 s_q[NN >= 2 ? NN * 4 * kWave : 1];
   __shared__ __align__(16) float s_w[NN >= 2 ? NN * kHeads : 1];
   __shared__ int s_pref[PERSIST ? kPersistMaxB + 1 : 1];  // shares of requests < b (persistent grid)
+  // K page slots of each wave (one-row requests, FP8 K)
+  __shared__ __align__(16) char s_ring[kDmaOf<NN, KF> ? kWavesOf<NN> * kRing * kSlotBytes : 16];
 
   if constexpr (!PERSIST) {
     logits_share<NN, HIST, F16, KF>(a, pages_per_wg, blockIdx.y, static_cast<int64_t>(blockIdx.x) * pages_per_wg,
-                                    s_hist, s_out, s_q, s_w);
+                                    s_hist, s_out, s_q, s_w, s_ring);
     return;
   }
   constexpr int kThreads = kThreadsOf<NN>;
@@ -537,7 +731,7 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
       else hi = mid;
     }
     logits_share<NN, HIST, F16, KF>(a, pages_per_wg, lo, static_cast<int64_t>(item - s_pref[lo]) * pages_per_wg,
-                                    s_hist, s_out, s_q, s_w);
+                                    s_hist, s_out, s_q, s_w, s_ring);
     __syncthreads();  // LDS of this share is read to the end before the next one writes it
   }
 }
@@ -953,7 +1147,9 @@ hipError_t launch_indexer_logits(const LogitsArgs& a, hipStream_t stream, Launch
   if (a.next_n == 1 && !a.k_mxfp4 && a.B >= 32 && a.B <= kPersistMaxB) {
     ppw = PMQA_LOGITS_PERSIST_PPW;  // equal shares dealt round robin (at most kMaxPagesPerWg)
     const int64_t upper = (a.max_pages + ppw - 1) / ppw * a.B;
-    const int64_t wgs = static_cast<int64_t>(PMQA_LOGITS_PERSIST_WGS_PER_CU) * info->cus;
+    // the LDS page ring leaves room for one workgroup per CU
+    const int64_t per_cu = PMQA_LOGITS_PERSIST_WGS_PER_CU ? PMQA_LOGITS_PERSIST_WGS_PER_CU : (PMQA_LOGITS_DMA ? 1 : 2);
+    const int64_t wgs = per_cu * info->cus;
     grid = dim3(static_cast<unsigned>(upper < wgs ? upper : wgs), 1);
     persistent = 1;
   }

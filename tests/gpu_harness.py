@@ -152,6 +152,41 @@ def check_logits(x, got, sample=None, seed=0, rows=None):
     return worst
 
 
+def check_logits_full(x, got, chunk=32768):
+    """Every live logit of every row within the tolerance of the oracle (the
+    keys of a request gathered once per chunk for all of its rows); returns
+    (max |err|/bound over finite expected values, logits checked)."""
+    worst, checked = 0.0, 0
+    next_n = x.next_n
+    for b in range(x.B):
+        rows = list(range(b * next_n, (b + 1) * next_n))
+        n_max = int(max(int(x.context_lens[r]) for r in rows))
+        for c0 in range(0, n_max, chunk):
+            cols = np.arange(c0, min(n_max, c0 + chunk))
+            want, bound, hs, hb = O.logits_terms_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                                    x.block_table, next_n, rows, cols)
+            for i, r in enumerate(rows):
+                n = min(int(x.context_lens[r]) - c0, cols.size)
+                if n <= 0:
+                    continue
+                g = got[r, c0:c0 + n]
+                w_, bd = want[i, :n], bound[i, :n]
+                check = O.check_logits_f16 if g.dtype == np.float16 else O.check_logits
+                ok = check(g, w_, bd, hs[i, :n], hb[i, :n])
+                if not ok.all():
+                    bad = np.nonzero(~ok)[0][:5]
+                    raise AssertionError(
+                        f"row {r}: {int((~ok).sum())} logits outside tolerance, e.g. cols "
+                        f"{(bad + c0).tolist()} got {g[bad].tolist()} want {w_[bad].tolist()} "
+                        f"bound {bd[bad].tolist()}")
+                fin = np.isfinite(w_) & (bd > 0)
+                if fin.any():
+                    worst = max(worst, float(np.max(np.abs(g[fin].astype(np.float64) - w_[fin])
+                                                    / bd[fin])))
+                checked += n
+    return worst, checked
+
+
 def check_padding(x, got, fill):
     for r in range(x.rows):
         n = int(x.context_lens[r])

@@ -641,6 +641,36 @@ def pin_check_logits_classes(O):
     return fails
 
 
+def pin_logits_terms_match(O):
+    """logits_terms_at (one gather for all four terms) gives, row for row,
+    exactly what indexer_logits_at, logits_error_bound_at (both modes) and
+    head_sum_at give -- on FP8 keys with infinite scales and on MXFP4 keys."""
+    import gen
+    fails = []
+    xs = [_acceptance_inputs(),
+          gen.make_indexer_inputs("terms_mx", 2, 3, [200, 77], 43, kfmt="mxfp4")]
+    for x in xs:
+        for b in range(x.B):
+            rows = list(range(b * x.next_n, (b + 1) * x.next_n))
+            cols = np.arange(int(x.context_lens[rows].max()))
+            want, bound, hs, hb = O.logits_terms_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                                    x.block_table, x.next_n, rows, cols)
+            for i, r in enumerate(rows):
+                ref = (O.indexer_logits_at(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                                           x.next_n, r, cols),
+                       O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                               x.block_table, x.next_n, r, cols),
+                       O.head_sum_at(x.q, x.kv_pages, x.k_scales, x.weights, x.block_table,
+                                     x.next_n, r, cols),
+                       O.logits_error_bound_at(x.q, x.kv_pages, x.k_scales, x.weights,
+                                               x.block_table, x.next_n, r, cols, unscaled=True))
+                for name, got, want_ in zip(("logits", "bound", "head_sum", "head_bound"),
+                                            (want[i], bound[i], hs[i], hb[i]), ref):
+                    if not np.array_equal(got, want_, equal_nan=True):
+                        fails.append(f"{x.name} row {r}: {name} differs from the separate helper")
+    return fails
+
+
 def _f32_between(lo, hi):
     """Every float32 in [lo, hi] (float64 bounds), by bit pattern."""
     a = np.float32(lo)
@@ -995,7 +1025,7 @@ ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_logits_f16_check, pin_bins_golden, pin_b
             pin_keys, pin_bins_coarsen_keys, pin_histogram, pin_topk,
             pin_topk_invariants, pin_logits_exact, pin_logits_library,
             pin_logits_paging, pin_error_bound, pin_head_sum_exact,
-            pin_error_bound_exact, pin_check_logits_classes, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
+            pin_error_bound_exact, pin_check_logits_classes, pin_logits_terms_match, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
             pin_mxfp4_matches_fp8_path, pin_mxfp4_exact, pin_block_amax8,
             pin_sort_candidate_blocks, pin_sparse_logits, pin_prefill_decode_case,
             pin_prefill_exact)
