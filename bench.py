@@ -87,6 +87,62 @@ def algorithmic_bytes(x) -> dict:
     return {"k": k, "total": k + scales + logits + table + qw + hist}
 
 
+def gpu_clock_mhz():
+    """The current shader clock (MHz) of every card sysfs lists, from the
+    active pp_dpm_sclk level; {} when the driver does not expose it."""
+    import glob
+    out = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        out[path.split("/")[4]] = int(line.split(":")[1].strip().rstrip("*").strip()
+                                                      .lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            pass
+    return out
+
+
+def page_list(x):
+    """The physical pages one logits call reads: each request's block-table
+    row up to its last live page (int32, request after request)."""
+    import numpy as np
+    pages = (x.request_keys().astype(np.int64) + 63) // 64
+    return np.concatenate([x.block_table[b, :int(pages[b])] for b in range(x.B)]).astype(np.int32)
+
+
+def sampled_cpu_baseline(x, budget_rows_keys=3_000_000):
+    """The oracle on a bounded sample of one workload -- whole requests in
+    order until about budget (row, key) pairs -- scaled to the whole step by
+    the (row, key) pairs: logits, histogram, top-2048 FP32 of those rows."""
+    import numpy as np
+    import oracle as O
+    lens = x.context_lens.astype(np.int64)
+    nn = max(x.next_n, 1)
+    reqs, pairs = 0, 0
+    while reqs < x.B and (reqs == 0 or pairs + int(lens[reqs * nn:(reqs + 1) * nn].sum()) <= budget_rows_keys):
+        pairs += int(lens[reqs * nn:(reqs + 1) * nn].sum())
+        reqs += 1
+    rows = reqs * nn
+    sub_q, sub_w, sub_bt, sub_l = x.q[:rows], x.weights[:rows], x.block_table[:reqs], x.context_lens[:rows]
+    t0 = time.perf_counter()
+    lg = O.indexer_logits(sub_q, x.kv_pages, x.k_scales, sub_w, sub_bt, sub_l, x.next_n, x.logits_stride)
+    O.coarse_histogram(lg, sub_l)
+    O.topk_rows(lg, sub_l, 2048, O.KEY_FP32)
+    dt = time.perf_counter() - t0
+    total = int(lens.sum())
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    return {"value": round(dt * total / pairs * 1e6, 1), "unit": "us/step", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reqs} of {x.B} requests ({pairs} of {total} row-key pairs), {dt:.2f} s, "
+                      f"scaled by the pairs"}
+
+
 def pct(a, q):
     import numpy as np
     return float(np.percentile(np.asarray(a), q))
@@ -175,6 +231,8 @@ def main() -> int:
                     help="steps of the ragged prefill (extend) logits on prefill/extend")
     ap.add_argument("--hist-steps", type=int, default=50,
                     help="steps of the logits kernel with and without the histogram (interleaved)")
+    ap.add_argument("--sweep-steps", type=int, default=40,
+                    help="steps per decode workload in the all-workload sweep (0: skip it)")
     ap.add_argument("--scores-steps", type=int, default=30,
                     help="steps of top-2048 over the very-long synthetic score rows (no histogram)")
     ap.add_argument("--candidate-blocks", type=int, default=512,
@@ -272,7 +330,7 @@ def main() -> int:
             out = [a.elapsed_time(b) * 1e3 for a, b in evs]
         return out
 
-    def run(n_steps, key, record, split=False, x=x, t=t, logits=logits, hist=hist):
+    def run(n_steps, key, record, split=False, x=x, t=t, logits=logits, hist=hist, idx=idx, ws=ws):
         """Steps of logits + top-k.  Without `split` only the step's start
         (logits kernel begins) and end (last top-k kernel ends) are recorded,
         so no event sits between the two calls; with it each call is timed
@@ -300,6 +358,7 @@ def main() -> int:
                     wt.append(ws0.elapsed_time(ws1) * 1e3)
         return lt, tt, st, wt
 
+    clock_before = gpu_clock_mhz()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     run(args.warmup, pmqa.KEY_FP32, False)
     torch.cuda.synchronize()
@@ -491,18 +550,77 @@ def main() -> int:
                   "score_read_gbps": round(sc.numel() * 4 / (float(np.mean(us)) * 1e-6) / 1e9, 1)}
         del sc, sc_lens, sc_idx, sc_ws
 
-    # practical read ceiling over the same number of bytes as K
+    def probes(xw, tw, reps):
+        """Read ceilings for one workload's K stream: a contiguous read of the
+        same bytes (K codes + scales), and the paged gather of exactly the
+        pages the logits call reads; times in us."""
+        kb = algorithmic_bytes(xw)
+        src = torch.ones((kb["k"] + kb["k"] // 32) // 4, dtype=torch.int32, device=dev)
+        plist = torch.from_numpy(page_list(xw)).to(dev)
+        rd, ga = [], []
+        for i in range(reps + 3):
+            e0, e1, e2, e3 = new_events(4)
+            evict()
+            pmqa.hbm_read_probe(src, sink, events=(e0, e1))
+            evict()
+            pmqa.hbm_gather_probe(tw["kv_pages"], tw["k_scales"], plist, sink, events=(e2, e3))
+            torch.cuda.synchronize()
+            if i >= 3:
+                rd.append(e0.elapsed_time(e1) * 1e3)
+                ga.append(e2.elapsed_time(e3) * 1e3)
+        del src, plist
+        return rd, ga
+
+    # every decode workload: logits (histogram on) + top-2048, the roofline of
+    # its logits kernel, the read ceilings of its K stream and the oracle on a
+    # bounded sample of it
+    sweep_out = None
+    if args.sweep_steps > 0:
+        sweep_out = {}
+        for name in gen.CONFIG_NAMES:
+            print(f"[bench] sweep {name}: {args.sweep_steps} steps", file=sys.stderr, flush=True)
+            xw = x if name == x.name else gen.config_inputs(name)
+            tw = t if name == x.name else upload(xw)
+            lw = torch.full((xw.rows, xw.logits_stride), float("inf"), dtype=torch.float32, device=dev)
+            hw = torch.zeros((xw.rows, 1024), dtype=torch.int32, device=dev)
+            iw = torch.empty((xw.rows, K), dtype=torch.int32, device=dev)
+            key = pmqa.KEY_FP16 if name == "varlen_decode" else pmqa.KEY_FP32
+            kw = dict(x=xw, t=tw, logits=lw, hist=hw, idx=iw, ws=None)
+            run(3, key, False, **kw)
+            _, _, sw, _ = run(args.sweep_steps, key, True, **kw)
+            lw_us, tw_us, _, _ = run(args.sweep_steps, key, True, split=True, **kw)
+            rd, ga = probes(xw, tw, max(10, args.sweep_steps // 2))
+            abw = algorithmic_bytes(xw)
+            lm = float(np.mean(lw_us))
+            ach = abw["total"] / (lm * 1e-6) / 1e9
+            sweep_out[name] = {
+                "B": xw.B, "next_n": xw.next_n, "key": "fp16" if key == pmqa.KEY_FP16 else "fp32",
+                "step_us": {"mean": round(float(np.mean(sw)), 3), "p10": round(pct(sw, 10), 3),
+                            "p50": round(pct(sw, 50), 3), "p90": round(pct(sw, 90), 3)},
+                "indexer_logits_us": {"mean": round(lm, 3), "p10": round(pct(lw_us, 10), 3),
+                                      "p50": round(pct(lw_us, 50), 3), "p90": round(pct(lw_us, 90), 3)},
+                "topk_rows_us": {"mean": round(float(np.mean(tw_us)), 3), "p10": round(pct(tw_us, 10), 3),
+                                 "p50": round(pct(tw_us, 50), 3), "p90": round(pct(tw_us, 90), 3)},
+                "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(ach / HBM_PEAK_GBPS, 4), "bytes_per_launch": abw["total"],
+                             "k_bytes": abw["k"],
+                             "k_frac": round(abw["k"] / (lm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+                "read_probe_us_p50": round(pct(rd, 50), 3),
+                "gather_probe_us_p50": round(pct(ga, 50), 3),
+                "logits_vs_gather_probe": round(pct(ga, 50) / pct(lw_us, 50), 4),
+                "cpu_baseline": (None if args.no_cpu_baseline else sampled_cpu_baseline(xw)),
+            }
+            if name != x.name:
+                del tw
+            del lw, hw, iw
+            torch.cuda.empty_cache()
+
+    # practical read ceilings for the headline workload's K stream
     ab = algorithmic_bytes(x)
-    probe_src = torch.empty(ab["k"] // 4, dtype=torch.int32, device=dev)
-    probe_src.fill_(1)
-    pts = []
-    for i in range(30):
-        e0, e1 = new_events(2)
-        evict()
-        pmqa.hbm_read_probe(probe_src, sink, events=(e0, e1))
-        torch.cuda.synchronize()
-        pts.append(e0.elapsed_time(e1) * 1e3)
-    probe_us = float(np.median(pts[5:]))
+    rd_pts, ga_pts = probes(x, t, 30)
+    probe_us = pct(rd_pts, 50)
+    gather_us = pct(ga_pts, 50)
+    clock_after = gpu_clock_mhz()
 
     if args.copy_calibration:
         # int32 -> float32: an elementwise copy kernel (a same-dtype copy may
@@ -575,9 +693,19 @@ def main() -> int:
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),
             "k_frac_of_peak": round(ab["k"] / (mean_logits * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "read_probe_us": round(probe_us, 3),
-            "read_probe_gbps": round(ab["k"] / (probe_us * 1e-6) / 1e9, 1),
+            # contiguous read of the K codes + scales (the best streaming shape)
+            "read_probe_us_p50": round(probe_us, 3),
+            "read_probe_us_p10_p90": [round(pct(rd_pts, 10), 3), round(pct(rd_pts, 90), 3)],
+            "read_probe_gbps": round(ab["k"] * 33 / 32 / (probe_us * 1e-6) / 1e9, 1),
+            # the same pages read through the block table, whole lines, no arithmetic
+            "gather_probe_us_p50": round(gather_us, 3),
+            "gather_probe_us_p10_p90": [round(pct(ga_pts, 10), 3), round(pct(ga_pts, 90), 3)],
+            "logits_median_vs_gather_probe": round(gather_us / pct(lt, 50), 4),
+            "logits_median_vs_read_probe": round(probe_us / pct(lt, 50), 4),
         },
+        "gpu_clock_mhz": {"before": clock_before, "after": clock_after},
+        # every decode workload, each with its roofline and oracle baseline
+        "workloads": sweep_out,
         # MFMA work of the same launch: 2*32*128 flop per (row, live key)
         "mfma": {"flop_per_launch": mfma_flop,
                  "tflops": round(mfma_flop / (mean_logits * 1e-6) / 1e12, 1),

@@ -428,6 +428,19 @@ const char* indexer_status_str(int32_t status);
  */
 idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * hbm_gather_probe -- measurement aid, not part of the method: reads the
+ * FP8 K pages listed in page_list (n_pages ids into kv_pages [num_pages][64]
+ * [128] and k_scales [num_pages][64]; ids are clamped into [0, num_pages))
+ * the way a paged K stream must be read -- page ids first, then whole-line
+ * 16-byte loads of each page and its scales -- with no arithmetic, and writes
+ * one checksum word to *sink.  Over the pages a logits call reads (each
+ * request's block-table row up to its last live page), its duration is the
+ * practical ceiling for that call's K stream.
+ */
+idx_status hbm_gather_probe(const uint8_t* kv_pages, const float* k_scales, const int32_t* page_list,
+                            int32_t n_pages, int32_t num_pages, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,7 @@ Entry points (same names as the C ABI):
   indexer_status_str(status)
   indexer_time_next_call(start, stop)
   hbm_read_probe(src, sink, events=None)
+  hbm_gather_probe(kv_pages, k_scales, page_list, sink, events=None)
 With ``events=(start, stop)`` (torch.cuda.Event with timing enabled, either
 may be None) the call is preceded by indexer_time_next_call, so its own
 kernel dispatches record the events: start when its first kernel begins,
@@ -50,7 +51,7 @@ __all__ = [
     "indexer_sparse_logits_mxfp4", "indexer_prefill_logits", "indexer_prefill_logits_mxfp4",
     "sparse_to_logical",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "topk_rows_noalloc", "score_histogram",
-    "indexer_status_str", "indexer_time_next_call", "hbm_read_probe",
+    "indexer_status_str", "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe",
 ]
 
 KEY_FP32 = 0
@@ -67,7 +68,7 @@ EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp
                     "indexer_prefill_logits", "indexer_prefill_logits_mxfp4", "sparse_to_logical",
                     "topk_workspace_bytes", "topk_rows", "topk_rows_noalloc",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
-                    "indexer_time_next_call", "hbm_read_probe")
+                    "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe")
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpaged_mqa_indexer.so"
@@ -110,6 +111,8 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_status_str.restype = ctypes.c_char_p
     lib.hbm_read_probe.argtypes = [vp, sz, vp, vp]
     lib.hbm_read_probe.restype = ctypes.c_int
+    lib.hbm_gather_probe.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+    lib.hbm_gather_probe.restype = ctypes.c_int
     lib.indexer_logits_f16.argtypes = lib.indexer_logits.argtypes
     lib.indexer_logits_f16.restype = ctypes.c_int
     lib.indexer_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp]
@@ -526,3 +529,24 @@ def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, events=None) -> None:
         _arm(events, src.device)
         st = lib.hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream_ptr(src.device))
     _check("hbm_read_probe", st)
+
+
+def hbm_gather_probe(kv_pages: torch.Tensor, k_scales: torch.Tensor, page_list: torch.Tensor,
+                     sink: torch.Tensor, events=None) -> None:
+    """Read the FP8 K pages (and their scales) listed in ``page_list`` once,
+    the way the paged K stream is read; checksum to ``sink``."""
+    dev = kv_pages.device
+    _need(kv_pages, "kv_pages", torch.uint8, dev, 3)
+    _need(k_scales, "k_scales", torch.float32, dev, 2)
+    _need(page_list, "page_list", torch.int32, dev, 1)
+    _need(sink, "sink", torch.int32, dev)
+    if not (kv_pages.is_contiguous() and k_scales.is_contiguous() and page_list.is_contiguous()):
+        raise ValueError("kv_pages, k_scales and page_list must be contiguous")
+    if tuple(kv_pages.shape[1:]) != (PAGE_TOKENS, HEAD_DIM):
+        raise ValueError("kv_pages must be [num_pages, 64, 128]")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        st = lib.hbm_gather_probe(_ptr(kv_pages), _ptr(k_scales), _ptr(page_list), int(page_list.numel()),
+                                  int(kv_pages.shape[0]), _ptr(sink), _stream_ptr(dev))
+    _check("hbm_gather_probe", st)

@@ -313,6 +313,16 @@ idx_status sparse_to_logical(const int32_t* indices, int32_t k, const int32_t* t
                                                  static_cast<hipStream_t>(stream), ev));
 }
 
+idx_status hbm_gather_probe(const uint8_t* kv_pages, const float* k_scales, const int32_t* page_list,
+                            int32_t n_pages, int32_t num_pages, uint32_t* sink, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!kv_pages || !k_scales || !page_list || !sink || n_pages <= 0 || num_pages <= 0) return IDX_EINVAL;
+  if (!aligned(kv_pages, 16) || !aligned(k_scales, 4) || !aligned(page_list, 4) || !aligned(sink, 4))
+    return IDX_EALIGN;
+  return from_hip(pmqa::launch_hbm_gather_probe(kv_pages, k_scales, page_list, n_pages, num_pages, sink,
+                                                static_cast<hipStream_t>(stream), ev));
+}
+
 idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   const pmqa::LaunchEvents ev = take_events();
   if (!src || !sink || bytes == 0) return IDX_EINVAL;

@@ -1,16 +1,21 @@
-// Streaming-read probe: the practical HBM read ceiling for 16-byte vector
-// loads, measured beside the logits kernel.  Not part of the method.
+// Read probes: the practical HBM read ceilings the logits kernel is measured
+// against.  Measurement aids, not part of the method.
 #include "indexer_common.h"
 
 namespace pmqa {
 namespace {
 
+// Streaming read of a contiguous buffer.  Each workgroup reads one contiguous
+// 32 KiB chunk, 8 16-byte loads per thread in flight (a wave's load
+// instruction covers 1 KiB of consecutive bytes).  Of the shapes swept on
+// this GPU (16-128 KiB chunks, 256-1024 threads, one to four persistent
+// workgroups per CU, loads straight to LDS, cache-policy bits), this one and
+// four persistent workgroups per CU were fastest at 64-512 MB (138 MB:
+// 23.0-23.4 us median, cold caches).
 constexpr int kProbeThreads = 256;
-constexpr int kProbeVecs = 16;  // 16-byte loads per thread, all in flight together
-constexpr int64_t kProbeChunk = kProbeThreads * kProbeVecs;  // 64 KiB per workgroup
+constexpr int kProbeVecs = 8;
+constexpr int64_t kProbeChunk = kProbeThreads * kProbeVecs;  // 16-byte vectors: 32 KiB per workgroup
 
-// Each workgroup reads one contiguous 64 KiB chunk; a wave's load instruction
-// covers 1 KiB of consecutive bytes.
 __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32x4* __restrict__ src,
                                                                         int64_t n_vec, uint32_t* sink) {
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kProbeChunk + threadIdx.x;
@@ -28,6 +33,67 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32
   if (__lane_id() == 0 && acc == 0x9E3779B9u) atomicXor(sink, acc);  // keeps the loads live
 }
 
+// Paged gather: the pages listed in `table` (8 KiB of FP8 keys each, plus
+// the page's 64 fp32 scales), read the way a paged K stream must be read --
+// page ids first, then whole-line 16-byte loads of each page -- with no
+// arithmetic.  Workgroups of 8 waves take 64 consecutive table entries; wave
+// w reads entries w, w + 8, ... with the next page in flight while the
+// current one is folded into a checksum.  The fastest of the static shapes
+// swept on a long-decode pool (4 or 8 waves, 8-64 pages per workgroup,
+// strided or contiguous shares, operand-layout or whole-line loads).
+constexpr int kGatherWaves = 8;
+constexpr int kGatherPagesPerWg = 64;
+
+struct GatherPage {
+  i32x4 v[kPageBytes / 1024];
+  int sc;
+};
+
+__device__ __forceinline__ void gather_load(const uint8_t* pool, const float* scales, int page, int lane,
+                                            GatherPage& p) {
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(pool + static_cast<int64_t>(page) * kPageBytes), 0, kPageBytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < kPageBytes / 1024; ++i)
+    p.v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, i * 1024 + lane * 16, 0, 0));
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scales + static_cast<int64_t>(page) * kPage), 0, kPage * 4, 0x00020000);
+  p.sc = __builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t gather_fold(const GatherPage& p) {
+  uint32_t a = static_cast<uint32_t>(p.sc);
+#pragma unroll
+  for (int i = 0; i < kPageBytes / 1024; ++i) a ^= static_cast<uint32_t>(p.v[i][0] ^ p.v[i][1] ^ p.v[i][2] ^ p.v[i][3]);
+  return a;
+}
+
+__global__ __launch_bounds__(kGatherWaves * kWave) void hbm_gather_probe_kernel(
+    const uint8_t* __restrict__ pool, const float* __restrict__ scales, const int32_t* __restrict__ table,
+    int32_t n_pages, int32_t pool_pages, uint32_t* sink) {
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int first = static_cast<int>(blockIdx.x) * kGatherPagesPerWg + wave;
+  const int last = min(static_cast<int>(blockIdx.x) * kGatherPagesPerWg + kGatherPagesPerWg, n_pages);
+  const int count = last > first ? (last - first + kGatherWaves - 1) / kGatherWaves : 0;
+  if (count == 0) return;
+  // lane i holds the wave's i-th page id (at most 64 / 8 = 8 of them)
+  const int ids = table[min(first + lane * kGatherWaves, n_pages - 1)];
+  auto id = [&](int it) { return min(max(__builtin_amdgcn_readlane(ids, it), 0), pool_pages - 1); };
+  GatherPage a, b;
+  uint32_t acc = 0u;
+  gather_load(pool, scales, id(0), lane, a);
+  for (int it = 0;;) {
+    gather_load(pool, scales, id(it + 1 < count ? it + 1 : it), lane, b);
+    acc ^= gather_fold(a);
+    if (++it >= count) break;
+    gather_load(pool, scales, id(it + 1 < count ? it + 1 : it), lane, a);
+    acc ^= gather_fold(b);
+    if (++it >= count) break;
+  }
+  if (acc == 0x9E3779B9u) atomicXor(sink, acc);  // keeps the loads live
+}
+
 }  // namespace
 
 hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream,
@@ -37,6 +103,16 @@ hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, 
   if (grid < 1 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   launch_kernel(hbm_read_probe_kernel, dim3(static_cast<unsigned>(grid)), dim3(kProbeThreads), stream,
                 ev.start, ev.stop, static_cast<const i32x4*>(src), n_vec, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_hbm_gather_probe(const uint8_t* pool, const float* scales, const int32_t* table,
+                                   int32_t n_pages, int32_t pool_pages, uint32_t* sink, hipStream_t stream,
+                                   LaunchEvents ev) {
+  const int64_t grid = (static_cast<int64_t>(n_pages) + kGatherPagesPerWg - 1) / kGatherPagesPerWg;
+  if (grid < 1 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  launch_kernel(hbm_gather_probe_kernel, dim3(static_cast<unsigned>(grid)), dim3(kGatherWaves * kWave), stream,
+                ev.start, ev.stop, pool, scales, table, n_pages, pool_pages, sink);
   return hipGetLastError();
 }
 

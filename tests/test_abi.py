@@ -293,3 +293,18 @@ def test_prefill_rejects_before_launch(lib, mx, kw, status):
 
 def test_prefill_needs_scales_for_fp8(lib):
     assert prefill_call(lib, sc=None) == IDX_EINVAL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pool=None), IDX_EINVAL),
+    (dict(table=None), IDX_EINVAL),
+    (dict(n=0), IDX_EINVAL),
+    (dict(num=0), IDX_EINVAL),
+    (dict(pool=A + 8), IDX_EALIGN),
+    (dict(scales=A + 2), IDX_EALIGN),
+])
+def test_gather_probe_rejects(lib, kw, status):
+    args = dict(pool=A, scales=A, table=A, n=64, num=64, sink=A)
+    args.update(kw)
+    assert lib.hbm_gather_probe(args["pool"], args["scales"], args["table"], args["n"], args["num"],
+                                args["sink"], None) == status

@@ -114,3 +114,26 @@ def test_committed_traffic_record_is_close_to_the_algorithmic_bytes():
     assert len(tr["kernel_src_sha"]) == 16
     total = bench.algorithmic_bytes(_decode_shape([131072] * 8))["total"]
     assert total <= tr["bytes_per_launch"] <= 1.05 * total
+
+
+def test_page_list_is_each_requests_live_pages_in_order():
+    import gen
+    x = gen.make_indexer_inputs("pl", 3, 2, [64, 130, 1], 5)
+    got = bench.page_list(x)
+    # request b's rows see base + j keys (next_n = 2): 65, 131 and 2 keys ->
+    # 2, 3 and 1 pages of its block-table row
+    want = np.concatenate([x.block_table[0, :2], x.block_table[1, :3], x.block_table[2, :1]])
+    assert got.dtype == np.int32 and np.array_equal(got, want)
+
+
+def test_sampled_cpu_baseline_scales_by_row_key_pairs():
+    import gen
+    x = gen.make_indexer_inputs("cb", 4, 1, [3000, 1000, 1000, 1000], 6)
+    out = bench.sampled_cpu_baseline(x, budget_rows_keys=4000)
+    assert out["kind"] == "oracle" and out["unit"] == "us/step" and out["cores"] >= 1
+    assert "2 of 4 requests (4000 of 6000 row-key pairs)" in out["sample"]
+    assert out["value"] > 0
+
+
+def test_gpu_clock_reader_returns_a_mapping():
+    assert isinstance(bench.gpu_clock_mhz(), dict)

@@ -500,3 +500,19 @@ def test_topk_rows_up_to_16384_in_one_workgroup(gpu, key, k):
         announce(f"topk_rows stride 16384 k={k} key={key} hist={'given' if hist is not None else 'NULL'}")
         idx = topk(s_, hist, ln, k, key)
         check_topk(idx.cpu().numpy(), buf, lens, k, key)
+
+
+def test_read_probes_run_on_small_buffers(gpu):
+    """The measurement aids launch on small inputs (partial chunks, a page
+    list shorter than a workgroup's share, out-of-range ids clamped) and
+    leave the sink alone for data whose checksum is not the marker."""
+    announce("hbm_read_probe / hbm_gather_probe small buffers")
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    src = torch.zeros(100_000 // 4 * 4, dtype=torch.int32, device=DEV)
+    gpu.hbm_read_probe(src, sink)
+    pool = torch.zeros((10, 64, 128), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((10, 64), dtype=torch.float32, device=DEV)
+    plist = torch.tensor([3, 9, 0, 12, -1, 5, 5], dtype=torch.int32, device=DEV)
+    gpu.hbm_gather_probe(pool, scales, plist, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
