@@ -75,7 +75,7 @@ typedef enum { IDX_KEY_FP32 = 0, IDX_KEY_FP16 = 1 } idx_key_dtype;
  * whose strides are limited to 2^23 (8x the longest context on the pages). */
 #define IDX_TOPK_MAX_STRIDE (1 << 23)
 /* topk_rows_noalloc: rows its fixed scratch holds (chunked path only). */
-#define IDX_NOALLOC_MAX_ROWS 256
+#define IDX_NOALLOC_MAX_ROWS 128
 
 /*
  * indexer_logits -- paged MQA logits with an optional fused coarse histogram.
@@ -126,9 +126,10 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
 
 /*
  * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
- * `rows` rows (host-only query, no device work): one 73,984-byte record per
- * row -- two 8-byte counter pairs (padded to 256 bytes), a 4 KiB histogram,
- * 64 KiB of candidates and 4 KiB of per-workgroup counts -- whatever the
+ * `rows` rows (host-only query, no device work): one 140,544-byte record per
+ * row -- two 8-byte counter pairs (padded to 256 bytes), a 1 KiB histogram of
+ * the threshold bin's sub-bins, a 4 KiB histogram, 128 KiB of candidates and
+ * 4 KiB of per-workgroup counts -- whatever the
  * stride and k, so a row's record sits at the same place for every call.
  * Rows of at most 16384 scores (logits_stride <= 16384) leave the workspace
  * untouched.  Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
@@ -149,10 +150,10 @@ size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
  *
  * With hist != NULL (the producer's histogram of exactly these scores), the
  * threshold bin is read from it: columns in higher bins are emitted directly,
- * columns of the threshold bin become candidates (at most 8192 per row) that
+ * columns of the threshold bin become candidates (at most 16384 per row) that
  * a radix select on the remaining key bits ranks.  The real counts found in
  * the scores are checked against the threshold; a stale histogram, or a
- * threshold bin with more than 8192 scores, makes that row fall back to an
+ * threshold bin with more than 16384 scores, makes that row fall back to an
  * exact whole-row radix select -- the result is exact in every case.  With
  * hist == NULL the histogram is first built from the scores.
  *
@@ -184,7 +185,7 @@ idx_status topk_rows(const float* logits, int64_t logits_stride,
  * allocate device memory (code under HIP graph capture, serving loops and
  * harnesses that forbid hipMalloc).  The chunked path's per-row records
  * (rows of more than 16384 scores) live in a fixed array of the library,
- * IDX_NOALLOC_MAX_ROWS records = 18,939,904 bytes per GPU, held from the
+ * IDX_NOALLOC_MAX_ROWS records = 17,989,632 bytes per GPU, held from the
  * time the library is loaded until the process ends; its device address is
  * looked up once per GPU, on the first call there.  The call allocates and
  * frees nothing.  Every call on a GPU shares that GPU's array: calls that

@@ -492,7 +492,7 @@ def topk_rows_f16(logits, hist, context_lens, k, indices, workspace=None, events
 
 def topk_rows_noalloc(logits, hist, context_lens, k, key_dtype, indices, events=None):
     """topk_rows with the library's fixed per-GPU scratch instead of a workspace
-    (at most 256 rows when rows hold more than 16384 scores); allocates
+    (at most 128 rows when rows hold more than 16384 scores); allocates
     nothing.  Calls that overlap on one GPU race on that scratch."""
     _topk_call("topk_rows_noalloc", torch.float32, logits, hist, context_lens, k, key_dtype, indices,
                None, events)

@@ -31,7 +31,7 @@
 //                  (above b*, in b*) reserves the chunk's places: columns
 //                  above b* go straight to the output (places below k), the
 //                  (key, column) candidates of b* to the row's candidate
-//                  buffer (places below 8192)
+//                  buffer (places below 16384)
 //   topk_finish    one 512-thread workgroup per row reads the counter pair
 //                  (with the row's bins and the first candidates) and checks
 //                  it against b*: if it confirms b*, the candidates are
@@ -68,7 +68,14 @@ constexpr int kRowSpan = kRefineThreads * kPerThread;  // 8192: rows topk_row ta
 constexpr int kAllBins = kBins;             // threshold meaning "every live score"
 static_assert(kBins == 4 * kThreads, "collect: four bins per thread");
 static_assert(kBins == 2 * kRefineThreads, "row and finish: two bins per thread");
-static_assert(kRowSpan <= kCandCap, "a whole row's candidates fit the LDS buffer");
+// Candidates of the threshold bin the selector refines in LDS: twice the
+// pages' capacity of 8192 (which stays the largest k), so that a threshold
+// bin of up to 16384 scores -- one row of a verify batch whose scores mostly
+// saturate holds about 16,000 -- is still refined from the collected
+// candidates instead of by passes over the whole row; LDS holds 128 KiB of
+// them beside the select's own arrays.
+constexpr int kCandBuf = 2 * kCandCap;
+static_assert(kRowSpan <= kCandBuf, "a whole row's candidates fit the LDS buffer");
 constexpr int kRowSpanMax = 2 * kRowSpan;  // 16384: rows topk_row takes in two parts per thread
 
 // Scratch of the chunked path, one fixed-size record per row, so a row's
@@ -78,20 +85,33 @@ constexpr int kRowSpanMax = 2 * kRowSpan;  // 16384: rows topk_row takes in two 
 //             the candidate buffer, odd ones from the back, which halves the
 //             atomics on each counter; the lists meet in the middle only when
 //             the counts contradict b*.  The finish pass leaves them zero.
+//   sub       256 sub-bins of the threshold bin (its FP16-key range cut into
+//             256 equal parts), added to by the collect workgroups from the
+//             candidates they place; the finish pass cuts the threshold bin
+//             once more with it and refines only the candidates of one
+//             sub-bin (it checks the cut against the candidates' real counts
+//             and, should they disagree, refines the whole bin), then leaves
+//             it zero
 //   hist      1024 bins, built here when the caller has no histogram (left
 //             zero by the finish pass as well)
-//   cand      8192 (key, column) candidates of b*
+//   cand      16384 (key, column) candidates of b*
 //   slots     the two counts of each collect workgroup, stored (not added),
 //             so their sums are this call's true counts whatever the
 //             counters held before it: a counter pair that did not start at
 //             zero (a workspace never used before, or overwritten since) is
 //             detected exactly, and its row is selected from scratch.
 constexpr int kMaxCollectWgs = 1024;                 // per row: rows of up to 2^23 scores
+constexpr int kSubBins = 256;
+// Threshold bins of more than this many scores are cut once more by their
+// sub-bins before the select; smaller ones are selected whole (two selects
+// over a few hundred candidates cost more than one).
+constexpr int kCutMin = 2048;
 constexpr size_t kRecCount = 0;
-constexpr size_t kRecHist = 256;
+constexpr size_t kRecSub = 256;
+constexpr size_t kRecHist = kRecSub + sizeof(int) * kSubBins;
 constexpr size_t kRecCand = kRecHist + sizeof(int) * kBins;
-constexpr size_t kRecSlots = kRecCand + sizeof(uint2) * kCandCap;
-constexpr size_t kRowScratchBytes = kRecSlots + sizeof(int) * kMaxCollectWgs;  // 73,984
+constexpr size_t kRecSlots = kRecCand + sizeof(uint2) * kCandBuf;
+constexpr size_t kRowScratchBytes = kRecSlots + sizeof(int) * kMaxCollectWgs;  // 140,544
 static_assert(kRowScratchBytes % 256 == 0, "records keep 256-byte alignment");
 constexpr int64_t kRecHistStride = static_cast<int64_t>(kRowScratchBytes / sizeof(int));  // ints per record
 constexpr int64_t kMaxChunkedStride = int64_t{2} * kMaxCollectWgs * kThreads * kPerThread;  // 2^23
@@ -106,6 +126,9 @@ struct Workspace {
   }
   __device__ uint2* cand(int row) const {
     return reinterpret_cast<uint2*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecCand);
+  }
+  __device__ int* sub(int row) const {
+    return reinterpret_cast<int*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecSub);
   }
   __device__ int* slots(int row) const {
     return reinterpret_cast<int*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecSlots);
@@ -231,7 +254,7 @@ struct Threshold {
 };
 
 template <int NT, int B>
-__device__ Threshold threshold_bin(const int (&c)[B], int k, int* s_red) {
+__device__ __forceinline__ Threshold threshold_bin(const int (&c)[B], int k, int* s_red) {
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < B; ++i) sum += c[i];
@@ -271,7 +294,7 @@ __device__ Threshold threshold_bin(const int (&c)[B], int k, int* s_red) {
 // with one compare.
 struct Classifier {
   uint32_t lo, eq_span, hi, gt_span;
-  __device__ explicit Classifier(int bstar) {
+  __device__ __forceinline__ explicit Classifier(int bstar) {
     const KeyRange r = bin_key_range(bstar);
     lo = r.lo;
     hi = r.hi;
@@ -281,6 +304,34 @@ struct Classifier {
   __device__ bool above(uint32_t key16) const { return key16 - hi < gt_span; }
   __device__ bool in_bin(uint32_t key16) const { return key16 - lo < eq_span; }
 };
+
+// Sub-bin of a key of the threshold bin: its FP16 key's place in the bin's
+// key range [lo, hi), cut into 256 equal parts (non-decreasing in the key, so
+// every key of a higher sub-bin is larger).  Collect and finish compute it
+// with this same arithmetic.
+struct SubDigit {
+  uint32_t lo, mult;
+  __device__ __forceinline__ explicit SubDigit(int bstar) {
+    const KeyRange r = bin_key_range(bstar);
+    lo = r.lo;
+    const uint32_t span = r.hi > r.lo ? r.hi - r.lo : 1u;  // <= 8457: the product below fits 32 bits
+    mult = (static_cast<uint32_t>(kSubBins) << 16) / span;
+  }
+  __device__ __forceinline__ uint32_t of(uint32_t key16) const {
+    return min(((key16 - lo) * mult) >> 16, static_cast<uint32_t>(kSubBins - 1));
+  }
+};
+
+// The FP16 key of a stored selection key (FP32 keys hold the score itself).
+template <int KEY>
+__device__ __forceinline__ uint32_t key16_of(uint32_t key) {
+  if constexpr (KEY == IDX_KEY_FP32) {
+    const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+    return key_f16(f16_bits_rn(__uint_as_float(u)));
+  } else {
+    return key;
+  }
+}
 
 // The 16 consecutive scores of a thread, from kPerThread / kPerVec 16-byte
 // loads.  Loads past the row's last live vector are clamped to it (in
@@ -395,6 +446,7 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
                                                                 const int32_t* __restrict__ lens, int k,
                                                                 int32_t* __restrict__ indices, Workspace ws) {
   __shared__ int s_red[kWaves + 5];
+  __shared__ int s_sub[kSubBins];
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
   const int len = clamp_len(lens, row, stride);
@@ -419,7 +471,11 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
     sc[m].load(x, s0[m], len);
   }
   const int hc[4] = {h01.x, h01.y, h23.x, h23.y};
-  const int bstar = threshold_bin<kThreads, 4>(hc, k, s_red).bin;
+  static_assert(kThreads == kSubBins, "one sub-bin per thread");
+  s_sub[tid] = 0;  // published by the barriers of the scans below
+  const Threshold th = threshold_bin<kThreads, 4>(hc, k, s_red);
+  const int bstar = th.bin;
+  const bool with_sub = th.count > kCutMin;  // uniform
 
   const Classifier cl(bstar);
   uint32_t gmask[M], emask[M];
@@ -451,6 +507,7 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
   const bool back = (blockIdx.x & 1) != 0;
   int32_t* out = indices + static_cast<int64_t>(row) * k;
   uint2* cand = ws.cand(row);
+  const SubDigit sd(bstar);  // (no candidates when bstar is the all-bins threshold)
 #pragma unroll
   for (int m = 0; m < M; ++m) {
 #pragma unroll
@@ -460,23 +517,29 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
         ++og;
       }
       if ((emask[m] >> i) & 1u) {
-        if (oe < static_cast<uint32_t>(kCandCap))
-          cand[back ? kCandCap - 1 - static_cast<int>(oe) : static_cast<int>(oe)] =
+        if (oe < static_cast<uint32_t>(kCandBuf))
+          cand[back ? kCandBuf - 1 - static_cast<int>(oe) : static_cast<int>(oe)] =
               uint2{sc[m].template key<KEY>(i), static_cast<uint32_t>(s0[m] + i)};
         ++oe;
+        if (with_sub) atomicAdd(&s_sub[sd.of(key_f16(sc[m].half_bits(i)))], 1);
       }
     }
   }
+  if (!with_sub || (tot >> 16) == 0) return;  // uniform
+  lds_barrier();
+  const int v = s_sub[tid];
+  if (v) atomicAdd(ws.sub(row) + tid, v);
 }
 
 // ---------------------------------------------------------------------------
 // Shared memory of the row and finish passes.
 struct RefineShared {
-  uint2 cand[kCandCap];   // 64 KiB
+  uint2 cand[kCandBuf];   // 128 KiB
   int digit_hist[256];
   int red[2 * (kRefineThreads / kWave) + 4];
-  uint32_t small[kWave];  // the few keys left after a radix pass
+  uint32_t small[kWave];  // the few keys left after a radix pass, or the columns of few ties
   int small_n;
+  int tie_n;
   int out_pos;
   uint32_t red_or, red_and;
   int bcast[4];
@@ -501,7 +564,8 @@ __device__ __forceinline__ void block_or_and(uint32_t o, uint32_t a, RefineShare
 // taken from the largest digit down (or, ascending, from the smallest up)
 // first reaches `need`; *before = the count strictly before d, *in_bin = the
 // count of d.
-__device__ int pick_digit(RefineShared& sh, int need, int* before, int* in_bin, bool descending = true) {
+__device__ __forceinline__ int pick_digit(RefineShared& sh, int need, int* before, int* in_bin,
+                                          bool descending = true) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     int c[4], sum = 0;
@@ -537,7 +601,7 @@ __device__ __forceinline__ int top_bit(uint32_t x) { return 31 - __clz(x); }
 // The need-th largest of the m <= 64 candidate keys that match (prefix,
 // fixed): the candidates are collected in LDS and wave 0 ranks each against
 // all the others.  *above = how many of them exceed the result.
-__device__ uint32_t rank_small(RefineShared& sh, int n, uint32_t prefix, uint32_t fixed, int need,
+__device__ __forceinline__ uint32_t rank_small(RefineShared& sh, int n, uint32_t prefix, uint32_t fixed, int need,
                                int* above) {
   for (int i = threadIdx.x; i < n; i += kRefineThreads) {
     const uint32_t key = sh.cand[i].x;
@@ -573,7 +637,7 @@ __device__ uint32_t rank_small(RefineShared& sh, int n, uint32_t prefix, uint32_
 // Radix select over the n LDS candidates: the key T of the need-th largest
 // key; *above = how many keys exceed T.  Bits every key shares are skipped,
 // and once a digit holds at most 64 keys they are ranked directly.
-__device__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above) {
+__device__ __forceinline__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above) {
   uint32_t o = 0u, a = 0xFFFFFFFFu;
   for (int i = threadIdx.x; i < n; i += kRefineThreads) {
     o |= sh.cand[i].x;
@@ -619,7 +683,7 @@ __device__ uint32_t select_key_lds(RefineShared& sh, int n, int need, int* above
 // Among the LDS candidates with key == T, the need-th smallest column C:
 // taking the ties with column <= C takes exactly `need` of them (columns are
 // distinct).  For candidate lists not in column order.
-__device__ uint32_t select_col_lds(RefineShared& sh, int n, uint32_t T, int need) {
+__device__ __forceinline__ uint32_t select_col_lds(RefineShared& sh, int n, uint32_t T, int need) {
   uint32_t o = 0u, a = 0xFFFFFFFFu;
   for (int i = threadIdx.x; i < n; i += kRefineThreads) {
     const uint2 c = sh.cand[i];
@@ -677,7 +741,10 @@ __device__ __forceinline__ void emit(RefineShared& sh, int32_t* out, int k, bool
 template <bool F16>
 struct SegmentReader {
   static constexpr int kPerVec = F16 ? 8 : 4;
-  static constexpr int kBatch = 4;  // vectors in flight per thread
+#ifndef PMQA_TOPK_SEG_BATCH
+#define PMQA_TOPK_SEG_BATCH 4
+#endif
+  static constexpr int kBatch = PMQA_TOPK_SEG_BATCH;  // vectors in flight per thread
   const char* x;
   int begin, end;  // this thread's columns
   __device__ SegmentReader(const void* row, int len) : x(static_cast<const char*>(row)) {
@@ -690,7 +757,7 @@ struct SegmentReader {
   // inside the row (the stride is a multiple of kPerVec); vectors of a batch
   // past the segment read its first vector again and are not visited.
   template <int KEY, typename F>
-  __device__ void for_each(F&& f) const {
+  __device__ __forceinline__ void for_each(F&& f) const {
     for (int s0 = begin; s0 < end; s0 += kBatch * kPerVec) {
       i32x4 v[kBatch];
 #pragma unroll
@@ -732,7 +799,7 @@ struct SegmentReader {
 // unit-regime verify row of 32K scores alone: 45.7 -> 39.2 us; aggregating
 // the first lane's digit with ballots, the design before, gave 73 -> 64 us
 // over plain adds).  FP16 keys add to digit_hist directly (measured faster).
-static_assert(sizeof(uint2) * kCandCap >= sizeof(int) * 256 * kWave, "lane bins fit the candidate buffer");
+static_assert(sizeof(uint2) * kCandBuf >= sizeof(int) * 256 * kWave, "lane bins fit the candidate buffer");
 
 template <bool LANE_BINS>
 __device__ __forceinline__ void digit_clear(RefineShared& sh) {
@@ -772,12 +839,12 @@ __device__ __forceinline__ void digit_publish(RefineShared& sh) {
   }
 }
 
-__device__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt, int n_eq,
-                                  int first_free, bool column_order);
+__device__ __forceinline__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt,
+                                                  int n_eq, int first_free, bool column_order);
 
 template <int KEY, bool F16>
-__device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, int len, int k,
-                                 int32_t* __restrict__ out) {
+__device__ __forceinline__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, int len, int k,
+                                                 int32_t* __restrict__ out) {
   constexpr int kKey = F16 ? IDX_KEY_FP16 : KEY;
   constexpr int kKeyBits = kKey == IDX_KEY_FP32 ? 32 : 16;
   const SegmentReader<F16> rd(x, len);
@@ -816,7 +883,7 @@ __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, i
     need -= before;
     prefix |= static_cast<uint32_t>(d) << shift;
     fixed |= 0xFFu << shift;
-    if (shift > 0 && in_bin <= kCandCap) {
+    if (shift > 0 && in_bin <= kCandBuf) {
       // The keys that share the prefix fit the LDS buffer: one pass emits the
       // keys above the prefix and gathers these candidates, and the row is
       // finished in LDS as for a confirmed threshold bin.
@@ -860,7 +927,7 @@ __device__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, i
 // k.
 __device__ __forceinline__ bool counts_confirm(int bstar, int n_gt, int n_eq, int k) {
   if (bstar == kAllBins) return n_gt <= k && n_eq == 0;
-  return n_gt < k && n_gt + n_eq >= k && n_eq <= kCandCap;
+  return n_gt < k && n_gt + n_eq >= k && n_eq <= kCandBuf;
 }
 
 // The n_eq candidates of b* are in sh.cand and the output row holds the n_gt
@@ -870,10 +937,13 @@ __device__ __forceinline__ bool counts_confirm(int bstar, int n_gt, int n_eq, in
 // the lowest columns: the first ones in list order when the list is in
 // column order (thread t ranks a run of consecutive candidates), else those
 // up to the column a radix select on the columns finds.
-__device__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt, int n_eq,
-                                  int first_free, bool column_order) {
+__device__ __forceinline__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt,
+                                                  int n_eq, int first_free, bool column_order) {
   const int need = k - n_gt;
-  if (threadIdx.x == 0) sh.out_pos = first_free;
+  if (threadIdx.x == 0) {
+    sh.out_pos = first_free;
+    sh.tie_n = 0;
+  }
   lds_barrier();
   int above = 0;
   const uint32_t T = select_key_lds(sh, n_eq, need, &above);
@@ -901,10 +971,41 @@ __device__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, i
     }
     return;
   }
+  // Count the ties at T; the columns of the first 64 are gathered as well
+  // (select_key_lds is done with sh.small), so that few ties -- the usual
+  // case -- are cut by ranking their columns directly.
   int tc = 0;
-  for (int i = threadIdx.x; i < n_eq; i += kRefineThreads) tc += sh.cand[i].x == T ? 1 : 0;
-  const int ties = block_sum<kRefineThreads>(tc, sh.red);
-  const uint32_t col_cut = ties > ties_needed ? select_col_lds(sh, n_eq, T, ties_needed) : 0xFFFFFFFFu;
+  for (int i0 = 0; i0 < n_eq; i0 += kRefineThreads) {
+    const int i = i0 + static_cast<int>(threadIdx.x);
+    const uint2 cd = i < n_eq ? sh.cand[i] : uint2{0u, 0u};
+    const bool tie = i < n_eq && cd.x == T;
+    tc += tie ? 1 : 0;
+    const uint64_t m = __ballot(tie);
+    if (m) {  // uniform in the wave
+      int pos = 0;
+      if (__lane_id() == 0) pos = atomicAdd(&sh.tie_n, __popcll(m));
+      pos = __builtin_amdgcn_readfirstlane(pos) + lanes_below(m);
+      if (tie && pos < kWave) sh.small[pos] = cd.y;
+    }
+  }
+  const int ties = block_sum<kRefineThreads>(tc, sh.red);  // its barriers publish sh.small
+  uint32_t col_cut = 0xFFFFFFFFu;
+  if (ties > ties_needed) {
+    if (ties <= kWave) {
+      // The ties_needed-th smallest of the (distinct) tie columns.
+      if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const uint32_t cj = lane < ties ? sh.small[lane] : 0xFFFFFFFFu;
+        int below = 0;
+        for (int i = 0; i < ties; ++i) below += sh.small[i] < cj ? 1 : 0;
+        if (lane < ties && below == ties_needed - 1) sh.bcast[0] = static_cast<int>(cj);
+      }
+      lds_barrier();
+      col_cut = static_cast<uint32_t>(sh.bcast[0]);
+    } else {
+      col_cut = select_col_lds(sh, n_eq, T, ties_needed);
+    }
+  }
   for (int i0 = 0; i0 < n_eq; i0 += kRefineThreads) {
     const int i = i0 + threadIdx.x;
     bool take = false;
@@ -1029,6 +1130,37 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
 // candidates from each end are requested together (the candidate buffer has a
 // fixed address; entries past the counts are unused).
 constexpr int kEarlyCand = 2;  // candidates per thread and end loaded with the counts
+
+// The candidates past the early ones, front list then back list as one list
+// of ef + eb: f(i, candidate) for i in [kEarlyCand * threads, ef) and
+// [ef + kEarlyCand * threads, ef + eb).  Eight loads per thread are requested
+// before any is used (a loop that waits for each load in turn costs a round
+// trip per 512 candidates: about 20 us for a bin of 16,000).
+template <typename F>
+__device__ __forceinline__ void copy_rest(const uint2* __restrict__ cand, int ef, int eb, F&& f) {
+  constexpr int kBatch = 8;
+  const int tid = threadIdx.x;
+  const int n_rest_f = max(ef - kEarlyCand * kRefineThreads, 0);
+  const int n_rest = n_rest_f + max(eb - kEarlyCand * kRefineThreads, 0);
+  for (int j0 = 0; j0 < n_rest; j0 += kBatch * kRefineThreads) {
+    uint2 c[kBatch];
+    int at[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u * kRefineThreads + tid;
+      // j < n_rest_f: front entry i; else back entry; past the end: index 0
+      // is read again (in bounds) and not used
+      const int fi = kEarlyCand * kRefineThreads + j;
+      const int bi = kEarlyCand * kRefineThreads + (j - n_rest_f);
+      const bool front = j < n_rest_f;
+      at[u] = j < n_rest ? (front ? fi : ef + bi) : -1;
+      c[u] = cand[j < n_rest ? (front ? fi : kCandBuf - 1 - bi) : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (at[u] >= 0) f(at[u], c[u]);
+  }
+}
 constexpr int kSlotsPerThread = kMaxCollectWgs / kRefineThreads;
 static_assert(kSlotsPerThread * kRefineThreads == kMaxCollectWgs && kRefineThreads % 2 == 0,
               "a thread's slots are all front or all back");
@@ -1076,11 +1208,12 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
   int slot[kSlotsPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) slot[j] = ws.slots(row)[j * kRefineThreads + tid];
+  const int sub = ws.sub(row)[tid < kSubBins ? tid : 0];
   uint2 early_f[kEarlyCand], early_b[kEarlyCand];
 #pragma unroll
   for (int j = 0; j < kEarlyCand; ++j) {
     early_f[j] = cand[j * kRefineThreads + tid];
-    early_b[j] = cand[kCandCap - 1 - (j * kRefineThreads + tid)];
+    early_b[j] = cand[kCandBuf - 1 - (j * kRefineThreads + tid)];
   }
   const int hv[2] = {h.x, h.y};
   const int bstar = threshold_bin<kRefineThreads, 2>(hv, k, sh.red).bin;
@@ -1101,6 +1234,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
     count[0] = 0ull;
     count[1] = 0ull;
   }
+  if (tid < kSubBins) ws.sub(row)[tid] = 0;
   // The counters must hold exactly this call's counts: a pair that did not
   // start at zero shifted every place its workgroups took, so the row is
   // selected from scratch rather than from places this call did not fill.
@@ -1124,10 +1258,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
       if (i < ef) out[gf + i] = static_cast<int32_t>(early_f[j].y);
       if (i < eb) out[gf + ef + i] = static_cast<int32_t>(early_b[j].y);
     }
-    for (int i = kEarlyCand * kRefineThreads + tid; i < ef; i += kRefineThreads)
-      out[gf + i] = static_cast<int32_t>(cand[i].y);
-    for (int i = kEarlyCand * kRefineThreads + tid; i < eb; i += kRefineThreads)
-      out[gf + ef + i] = static_cast<int32_t>(cand[kCandCap - 1 - i].y);
+    copy_rest(cand, ef, eb, [&](int i, uint2 c) { out[gf + i] = static_cast<int32_t>(c.y); });
     for (int i = gf + n_eq + tid; i < k - gb; i += kRefineThreads) out[i] = -1;
     return;
   }
@@ -1137,9 +1268,72 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
     if (i < ef) sh.cand[i] = early_f[j];
     if (i < eb) sh.cand[ef + i] = early_b[j];
   }
-  for (int i = kEarlyCand * kRefineThreads + tid; i < ef; i += kRefineThreads) sh.cand[i] = cand[i];
-  for (int i = kEarlyCand * kRefineThreads + tid; i < eb; i += kRefineThreads) sh.cand[ef + i] = cand[kCandCap - 1 - i];
-  lds_barrier();
+  copy_rest(cand, ef, eb, [&](int i, uint2 c) { sh.cand[i] = c; });
+  // Second cut: the sub-bin s* of the threshold bin where the running count
+  // (largest sub-bins first) reaches need; the candidates of higher sub-bins
+  // are taken, those of s* refined.
+  if (n_eq > kCutMin) {  // uniform
+    if (tid == 0) sh.bcast[0] = -1;
+    if (tid < kSubBins) sh.digit_hist[tid] = sub;
+    lds_barrier();
+    const int need = k - n_gt;
+    int sub_above = 0, sub_in = 0;
+    const int sstar = pick_digit(sh, need, &sub_above, &sub_in);
+    if (sstar >= 0 && sub_in < n_eq) {
+      // Thread t takes candidates t, t + 512, ... (at most 32 of 16384; a
+      // wave's reads are conflict-free), counts those above s* and in it, and
+      // after one block scan writes the former to the output and the latter to
+      // the front of the LDS list (every read precedes the scan's barriers).
+      // Groups of 8 are read together, and only groups that hold candidates
+      // (a uniform test); reads past n_eq stay inside the LDS list and are
+      // masked off.
+      const SubDigit sd(bstar);
+      constexpr int kGroup = 8;
+      constexpr int kMaxPer = kCandBuf / kRefineThreads;
+      static_assert(kMaxPer % kGroup == 0 && kMaxPer <= 32, "masks hold one bit per candidate");
+      const uint32_t sstar_u = static_cast<uint32_t>(sstar);
+      uint2 c[kMaxPer];
+      uint32_t m_above = 0u, m_in = 0u;
+#pragma unroll
+      for (int g = 0; g < kMaxPer / kGroup; ++g) {
+        if (g * kGroup * kRefineThreads < n_eq) {
+#pragma unroll
+          for (int u = 0; u < kGroup; ++u) c[g * kGroup + u] = sh.cand[(g * kGroup + u) * kRefineThreads + tid];
+#pragma unroll
+          for (int u = 0; u < kGroup; ++u) {
+            const int j = g * kGroup + u;
+            const bool live = j * kRefineThreads + tid < n_eq;
+            const uint32_t d = sd.of(key16_of<F16 ? IDX_KEY_FP16 : KEY>(c[j].x));
+            m_above |= (live && d > sstar_u ? 1u : 0u) << j;
+            m_in |= (live && d == sstar_u ? 1u : 0u) << j;
+          }
+        }
+      }
+      int2 tot2;
+      const int2 off = block_excl_scan2<kRefineThreads>(__popc(m_above), __popc(m_in), sh.red, &tot2);
+      // The cut holds when the counts found confirm it: fewer than need above
+      // s*, at least need with it.  (The sub-histogram is accumulated by
+      // atomics on the workspace; a workspace that did not start zeroed shows
+      // here and the whole bin is refined.)
+      if (tot2.x == sub_above && tot2.x < need && tot2.x + tot2.y >= need) {
+        int pa = gf + off.x, pt = off.y;
+#pragma unroll
+        for (int g = 0; g < kMaxPer / kGroup; ++g) {
+          if (g * kGroup * kRefineThreads < n_eq) {
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+              const int j = g * kGroup + u;
+              if ((m_above >> j) & 1u) out[pa++] = static_cast<int32_t>(c[j].y);
+              if ((m_in >> j) & 1u) sh.cand[pt++] = c[j];
+            }
+          }
+        }
+        lds_barrier();
+        finish_candidates(sh, out, k, n_gt + tot2.x, tot2.y, gf + tot2.x, false);
+        return;
+      }
+    }
+  }
   finish_candidates(sh, out, k, n_gt, n_eq, gf, false);
 }
 
@@ -1255,7 +1449,7 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents 
 // array's name is a host-side stand-in, not a device address).  Nothing in
 // it has to start at zero: the finish pass checks the counters against the
 // stored per-workgroup counts and leaves counters and built histograms zero.
-constexpr size_t kNoallocBytes = kRowScratchBytes * IDX_NOALLOC_MAX_ROWS;  // 18,939,904
+constexpr size_t kNoallocBytes = kRowScratchBytes * IDX_NOALLOC_MAX_ROWS;  // 17,989,632
 static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
 
 namespace {

@@ -50,9 +50,9 @@ def test_status_strings(lib):
 
 def per_row_bytes(stride, k):
     """The documented layout: one record per row -- two counter pairs padded
-    to 256 bytes, a histogram, 8192 candidates and 1024 per-workgroup counts
-    (whatever the stride and k)."""
-    return 256 + 4096 + 8 * 8192 + 4 * 1024
+    to 256 bytes, a 256-bin sub-histogram, a histogram, 16384 candidates and
+    1024 per-workgroup counts (whatever the stride and k)."""
+    return 256 + 1024 + 4096 + 8 * 16384 + 4 * 1024
 
 
 def test_workspace_query(lib):
@@ -185,8 +185,8 @@ def noalloc_call(lib, **kw):
     (dict(stride=(1 << 23) + 4), IDX_EUNSUPPORTED),
     (dict(logits=A + 4), IDX_EALIGN),
     (dict(hist=A + 4), IDX_EALIGN),
-    # the fixed scratch holds 256 rows of the chunked path (stride > 16384)
-    (dict(rows=257, stride=16388), IDX_ESCRATCH),
+    # the fixed scratch holds 128 rows of the chunked path (stride > 16384)
+    (dict(rows=129, stride=16388), IDX_ESCRATCH),
     (dict(rows=65535, stride=1 << 20), IDX_ESCRATCH),
 ])
 def test_topk_rows_noalloc_rejects(lib, kw, status):

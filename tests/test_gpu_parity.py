@@ -478,6 +478,62 @@ def test_topk_fallback_overflow_shapes(gpu, key):
         check_topk(idx.cpu().numpy(), buf, lens, k, key)
 
 
+def _sub_cut_rows(k, rng):
+    """Rows of 40,000 scores whose threshold bin holds 2049 .. 16384 scores,
+    so that the selector cuts the bin by its 256 sub-bins: spread over the
+    saturating bin (many FP16 values per sub-bin), a fine bin with float32
+    values between its FP16 ones, 8000 ties at one value beside spread
+    values, only the bin's extreme keys (+inf, 65504, 223: the top and
+    bottom sub-bins), one value only (no cut), and exactly 16384 in the
+    bin."""
+    n = 40000
+
+    def row(parts):
+        r = np.concatenate(parts + [rng.standard_normal(n - sum(len(p) for p in parts))]).astype(np.float32)
+        rng.shuffle(r)
+        return r
+
+    above = np.full(k // 2, 200.0, np.float32)  # in a bin above the fine one
+    return [
+        row([rng.uniform(223.0, 60000.0, 12000)]),
+        row([above, (np.float32(5.0) + rng.uniform(0, 0.25, 9000)).astype(np.float32)]),
+        row([np.full(8000, 300.0), rng.uniform(223.0, 60000.0, 1000)]),
+        row([np.full(100, np.inf), np.full(2400, 65504.0), np.full(2500, 223.0)]),
+        row([above, np.full(6000, 7.0)]),
+        row([rng.uniform(223.0, 60000.0, 16384)]),
+    ]
+
+
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+@pytest.mark.parametrize("k", [100, 2048, 8192])
+def test_topk_threshold_bin_cut_by_sub_bins(gpu, key, k):
+    """Threshold bins of more than 2048 scores are cut once more by the
+    sub-bins the collect pass counts: exact with the producer's histogram and
+    without one, and with a workspace whose sub-bin counts hold garbage (the
+    cut is checked against the candidates' real counts, so only its speed
+    may suffer), then again on the same workspace."""
+    rng = np.random.default_rng(4242 + k)
+    rows = _sub_cut_rows(k, rng)
+    buf, lens = _scores_dev(rows)
+    s_, ln = torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV)
+    h = torch.zeros((len(rows), 1024), dtype=torch.int32, device=DEV)
+    gpu.score_histogram(s_, ln, h)
+    for hist in (h, None):
+        announce(f"topk_rows sub-bin cut k={k} key={key} hist={'given' if hist is not None else 'NULL'}")
+        idx = topk(s_, hist, ln, k, key)
+        check_topk(idx.cpu().numpy(), buf, lens, k, key)
+    rec = gpu.topk_workspace_bytes(1, buf.shape[1], k)
+    ws = torch.zeros(len(rows) * rec, dtype=torch.uint8, device=DEV)
+    w32 = ws.view(torch.int32).view(len(rows), rec // 4)
+    # the documented record: counters in bytes 0..255, sub-bin counts in 256..1279
+    w32[:, 64:320] = torch.from_numpy(rng.integers(0, 3000, (len(rows), 256), dtype=np.int32)).to(DEV)
+    for call in range(2):
+        announce(f"topk_rows sub-bin cut, garbage sub-bin counts k={k} key={key} call={call}")
+        idx = topk(s_, h, ln, k, key, workspace=ws)
+        check_topk(idx.cpu().numpy(), buf, lens, k, key)
+    assert int(w32[:, 64:320].abs().sum().item()) == 0  # left zero for the next call
+
+
 @pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
 @pytest.mark.parametrize("k", [1, 2048, 8192])
 def test_topk_rows_up_to_16384_in_one_workgroup(gpu, key, k):

@@ -83,8 +83,8 @@ def test_noalloc_matches_workspace_entry_point(gpu, shapes):
 
 def test_noalloc_refuses_rows_beyond_its_scratch(gpu):
     lib = pmqa.load_library()
-    s = torch.zeros((257, 16388), dtype=torch.float32, device=DEV)
-    ln = torch.full((257,), 16388, dtype=torch.int32, device=DEV)
-    idx = torch.empty((257, 8), dtype=torch.int32, device=DEV)
-    st = lib.topk_rows_noalloc(_vp(s), s.stride(0), None, _vp(ln), 257, 8, 0, _vp(idx), _stream())
+    s = torch.zeros((129, 16388), dtype=torch.float32, device=DEV)
+    ln = torch.full((129,), 16388, dtype=torch.int32, device=DEV)
+    idx = torch.empty((129, 8), dtype=torch.int32, device=DEV)
+    st = lib.topk_rows_noalloc(_vp(s), s.stride(0), None, _vp(ln), 129, 8, 0, _vp(idx), _stream())
     assert st == 6, pmqa.indexer_status_str(st)  # IDX_ESCRATCH, nothing launched
