@@ -49,15 +49,66 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA, MI355X
 FLUSH_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.json")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_long_decode_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
-# The counted kernel: one row per request, histogram on, float32 logits, FP8 K,
-# the (chunks, B) grid
-# (the long-decode launch; other instantiations in the same run are ignored).
-LOGITS_KERNEL = "indexer_logits_kernel<1, true, false, 0, false>"
+# The logits kernel each workload launches, whose counters and trace are
+# read: indexer_logits_kernel<rows per request, histogram, FP16 output, K
+# format (0 FP8, 1 MXFP4), persistent grid> (varlen_decode: 64 one-row
+# requests take the persistent grid), and the ragged prefill kernel
+# indexer_prefill_logits_kernel<K format>.
+COUNTED_KERNEL = {
+    "tiny_decode": "indexer_logits_kernel<1, true, false, 0, false>",
+    "long_decode": "indexer_logits_kernel<1, true, false, 0, false>",
+    "spec_verify/fine": "indexer_logits_kernel<4, true, false, 0, false>",
+    "spec_verify/unit": "indexer_logits_kernel<4, true, false, 0, false>",
+    "spec_verify/mixed": "indexer_logits_kernel<4, true, false, 0, false>",
+    "varlen_decode": "indexer_logits_kernel<1, true, false, 0, true>",
+    "very_long": "indexer_logits_kernel<1, true, false, 0, false>",
+    "long_decode/mxfp4": "indexer_logits_kernel<1, true, false, 1, false>",
+    "spec_verify/mxfp4": "indexer_logits_kernel<4, true, false, 1, false>",
+    "prefill/extend": "indexer_prefill_logits_kernel<0>",
+    "prefill/extend_mxfp4": "indexer_prefill_logits_kernel<1>",
+}
+LOGITS_KERNEL = COUNTED_KERNEL["long_decode"]
+# bench.py arguments of the profiled runs: one workload's step and nothing
+# else (the prefill workloads run in the prefill leg, after two long-decode
+# steps).
+LEGS_OFF = ("--fp16-steps 0 --mxfp4-steps 0 --candidate-steps 0 --prefill-steps 0 --hist-steps 0 "
+            "--sweep-steps 0 --scores-steps 0 --no-cpu-baseline")
+
+
+def slug(workload: str) -> str:
+    return workload.replace("/", "_")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"logits_{slug(workload)}_traffic.json")
+
+
+TRAFFIC_FILE = traffic_file("long_decode")
+
+
+def profile_args(workload: str, steps: int = 5) -> str:
+    """The bench.py arguments of a profiled run of one workload."""
+    if workload.startswith("prefill/"):
+        legs = LEGS_OFF.replace("--prefill-steps 0", f"--prefill-steps {steps}")
+        return f"--workload long_decode --steps 2 --warmup 1 --spin-up-ms 1000 {legs}"
+    return f"--workload {workload} --steps {steps} --warmup 2 --spin-up-ms 1000 {LEGS_OFF}"
 KERNEL_SOURCES = ("paged_mqa_logits_indexer_amd/csrc/logits_kernel.hip",
                   "paged_mqa_logits_indexer_amd/csrc/indexer_common.h")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the workload's committed counter record,
+    or None when there is none or the kernel sources changed since."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_src_sha") != kernel_source_digest() or tr.get("workload") != workload:
+        return None
+    return tr.get("bytes_per_launch")
 
 
 def kernel_source_digest() -> str:
@@ -83,7 +134,8 @@ def algorithmic_bytes(x) -> dict:
     logits = int(lens.sum()) * 4             # fp32 logits written
     table = int(pages.sum()) * 4             # block-table entries
     qw = x.rows * (32 * 128 + 32 * 4 + 4)    # Q, weights, lengths
-    hist = x.rows * 1024 * 4 * 2             # histogram read-modify-write
+    # histogram read-modify-write (the prefill kernel has none)
+    hist = 0 if getattr(x, "cu_q", None) is not None else x.rows * 1024 * 4 * 2
     return {"k": k, "total": k + scales + logits + table + qw + hist}
 
 
@@ -192,16 +244,21 @@ def read_counters(directory: str, counter: str):
 
 
 def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
-    """HBM bytes per logits launch from the FETCH_SIZE and WRITE_SIZE runs
-    (KiB per dispatch), each scaled by the same counter on the calibration
-    copies: the device-to-device copies after the last logits dispatch."""
+    """HBM bytes per launch of the workload's logits kernel from the
+    FETCH_SIZE and WRITE_SIZE runs (KiB per dispatch), each scaled by the
+    same counter on the calibration copies: the device-to-device copies
+    after the kernel's last dispatch."""
     import numpy as np
-    out = {"workload": workload, "kernel_src_sha": kernel_source_digest(),
+    kernel = COUNTED_KERNEL[workload]
+    out = {"workload": workload, "kernel": kernel, "kernel_src_sha": kernel_source_digest(),
            "copy_bytes": COPY_BYTES}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read_counters(d, counter)
-        last_logits = max(i for i, (_, name, _) in enumerate(rows) if LOGITS_KERNEL in name)
-        logits = [v for _, name, v in rows if LOGITS_KERNEL in name]
+        hits = [i for i, (_, name, _) in enumerate(rows) if kernel in name]
+        if not hits:
+            raise SystemExit(f"{counter}: no dispatch of {kernel} under {d}")
+        last_logits = max(hits)
+        logits = [v for _, name, v in rows if kernel in name]
         copies = [v for _, name, v in rows[last_logits + 1:] if "copy" in name.lower()]
         if not copies:
             raise SystemExit(f"{counter}: no calibration copy after the last logits dispatch")
@@ -213,6 +270,136 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
     out["bytes_per_launch"] = int(round(out["FETCH_SIZE"]["bytes_per_launch"]
                                         + out["WRITE_SIZE"]["bytes_per_launch"]))
     return out
+
+
+def short_kernel_name(n: str) -> str:
+    """A trace's kernel name without namespaces and parameter lists."""
+    import re
+    n = n.replace("pmqa::(anonymous namespace)::", "").replace("void ", "")
+    if n.startswith("at::native") or "rocclr" in n:
+        return "torch/runtime kernel (set-up, histogram reset, calibration copy)"
+    m = re.match(r"([A-Za-z_0-9]+(<[^>]*>)?)", n)
+    return m.group(1) if m else n[:60]
+
+
+def profiled_command(tool: str, workload: str, steps: int) -> str:
+    return (f"rocprofv3 {tool} -d <out> -o run --output-format csv -- \\\n"
+            f"    python3 bench.py {profile_args(workload, steps)}")
+
+
+def write_traffic_md(tr: dict, alg_bytes: int, out_dir: str = PROFILES) -> str:
+    w = tr["workload"]
+    path = os.path.join(out_dir, f"logits_{slug(w)}_traffic.md")
+    lines = [f"# HBM traffic of {tr['kernel']}: {w}", "",
+             "Two counter runs (one counter each) and the conversion, from the repository root "
+             "with `TMPDIR=/tmp`:", "", "```"]
+    for c, d in (("FETCH_SIZE", "<fetch>"), ("WRITE_SIZE", "<write>")):
+        lines.append(profiled_command(f"--pmc {c}", w, 5).replace("<out>", d) + " --copy-calibration")
+    lines += [f"python3 bench.py --workload {w} --traffic-from <fetch> <write>", "```", "",
+              "Every dispatch follows a 1 GiB read sweep, so K comes from HBM.  The calibration "
+              "copy is an int32 -> float32 elementwise copy of 256 MiB (reads and writes "
+              "268,435,456 bytes), counted after the kernel's last dispatch.", "",
+              "| counter | KiB / dispatch | dispatches | copy KiB / dispatch | factor | bytes / launch |",
+              "|---|---|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = tr[c]
+        lines.append(f"| {c} | {r['logits_kib_per_dispatch']:.1f} | {r['dispatches']} | "
+                     f"{r['copy_kib_per_dispatch']:.1f} | {r['factor']:.4f} | {r['bytes_per_launch']:,.0f} |")
+    lines += ["", f"Traffic per launch: {tr['bytes_per_launch']:,} bytes against {alg_bytes:,} "
+              f"algorithmic bytes: ratio {tr['bytes_per_launch'] / alg_bytes:.4f}.  Kernel source digest "
+              f"`{tr['kernel_src_sha']}` (bench.py reports the traffic only while the kernel sources "
+              "still have this digest)."]
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def write_stats_md(csv_path: str, workload: str, steps: int, out_dir: str = PROFILES) -> str:
+    """A rocprofv3 --stats kernel table as markdown, with its command."""
+    import csv
+    with open(csv_path) as fh:
+        rows = list(csv.DictReader(fh))
+    path = os.path.join(out_dir, f"{slug(workload)}_kernel_trace.md")
+    lines = [f"# Kernel trace: {workload}", "", "From the repository root with `TMPDIR=/tmp`:", "", "```",
+             profiled_command("--kernel-trace --stats", workload, steps),
+             f"python3 bench.py --workload {workload} --profile-steps {steps} --stats-md <out>/run_kernel_stats.csv",
+             "```", "",
+             f"Calls include warm-up, the timed steps, the per-call timing and the read-ceiling "
+             f"probes of `bench.py`; `hbm_read_probe_kernel` also covers the 1 GiB cache sweeps before "
+             f"every step.  The workload's logits kernel is `{COUNTED_KERNEL[workload]}`.", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    agg = {}  # kernels that share a short name are merged (calls-weighted average)
+    for r in rows:
+        n = short_kernel_name(r["Name"])
+        c, a, lo, hi = int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])
+        if n in agg:
+            c0, a0, lo0, hi0 = agg[n]
+            agg[n] = (c0 + c, (a0 * c0 + a * c) / (c0 + c), min(lo0, lo), max(hi0, hi))
+        else:
+            agg[n] = (c, a, lo, hi)
+    for n, (c, a, lo, hi) in sorted(agg.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        lines.append(f"| {n} | {c} | {a / 1e3:.2f} | {lo / 1e3:.2f} | {hi / 1e3:.2f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def counters_of(directory: str, kernel: str) -> dict:
+    """Median per dispatch of every counter of one kernel in a --pmc run, and
+    the median dispatch duration (profiler timestamps, us)."""
+    import csv
+    import glob
+    import numpy as np
+    per = {}
+    dur = {}
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                key = (r["Dispatch_Id"], r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                if r.get("Start_Timestamp"):
+                    dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    if not per:
+        raise SystemExit(f"no dispatch of {kernel} under {directory}")
+    names = sorted({c for _, c in per})
+    out = {c: float(np.median([v for (d, cc), v in per.items() if cc == c])) for c in names}
+    out["dispatches"] = len(dur) or len({d for d, _ in per})
+    out["duration_us"] = float(np.median(list(dur.values()))) if dur else None
+    return out
+
+
+MFMA_COUNTERS = "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_BUSY_CYCLES SQ_WAVES GRBM_GUI_ACTIVE"
+
+
+def write_counters_md(directory: str, workload: str, out_dir: str = PROFILES) -> str:
+    """MFMA use of the workload's kernel from one --pmc run (MFMA_COUNTERS)."""
+    kernel = COUNTED_KERNEL[workload]
+    c = counters_of(directory, kernel)
+    path = os.path.join(out_dir, f"logits_{slug(workload)}_mfma.md")
+    lines = [f"# MFMA use of {kernel}: {workload}", "", "One counter run, from the repository root with "
+             "`TMPDIR=/tmp`:", "", "```", profiled_command(f"--pmc {MFMA_COUNTERS}", workload, 5),
+             f"python3 bench.py --workload {workload} --counters-md <out>", "```", "",
+             f"Medians over the kernel's {c['dispatches']} dispatches:", "", "| counter | per dispatch |",
+             "|---|---|"]
+    for k, v in c.items():
+        if k.startswith(("SQ_", "GRBM_")):
+            lines.append(f"| {k} | {v:,.0f} |")
+    if c.get("duration_us"):
+        lines.append(f"| dispatch duration (profiler timestamps) | {c['duration_us']:.2f} us |")
+    busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    if busy is not None and c.get("duration_us"):
+        cyc = c["duration_us"] * 1e-6 * 2.4e9
+        frac = busy / 1024 / cyc
+        lines += ["", f"MFMA busy per SIMD: {busy:,.0f} / 1,024 SIMDs = {busy / 1024:,.0f} cycles of "
+                  f"{cyc:,.0f} ({c['duration_us']:.2f} us at 2.4 GHz): {100 * frac:.1f} %."]
+        if c.get("SQ_INSTS_MFMA"):
+            lines.append(f"Busy cycles per MFMA: {busy / c['SQ_INSTS_MFMA']:.1f}; VALU instructions per "
+                         f"MFMA: {c.get('SQ_INSTS_VALU', 0) / c['SQ_INSTS_MFMA']:.2f}.")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
 
 
 def main() -> int:
@@ -244,14 +431,33 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timing, run plain 256 MiB device copies (counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc runs into the traffic record (no GPU)")
+                    help="turn two rocprofv3 --pmc runs of --workload into its traffic record (no GPU)")
+    ap.add_argument("--stats-md", metavar="KERNEL_STATS_CSV",
+                    help="write the kernel-trace summary of --workload under profiles/ (no GPU)")
+    ap.add_argument("--counters-md", metavar="PMC_DIR",
+                    help="write the MFMA counter summary of --workload under profiles/ (no GPU)")
+    ap.add_argument("--profile-args", action="store_true",
+                    help="print the bench.py arguments of a profiled run of --workload")
+    ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--spin-up-ms", type=float, default=0.0,
+                    help="read sweeps for this long before the warmup, so that a short run is timed "
+                         "at the clocks a sustained load reaches")
     args = ap.parse_args()
 
-    if args.traffic_from:
-        tr = traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
-        with open(TRAFFIC_FILE, "w") as f:
-            json.dump(tr, f, indent=1)
-        print(json.dumps(tr))
+    if args.profile_args:
+        print(profile_args(args.workload, args.profile_steps))
+        return 0
+    if args.traffic_from or args.stats_md or args.counters_md:
+        import gen
+        if args.traffic_from:
+            tr = traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
+            with open(traffic_file(args.workload), "w") as f:
+                json.dump(tr, f, indent=1)
+            print(write_traffic_md(tr, algorithmic_bytes(gen.config_inputs(args.workload))["total"]))
+        if args.stats_md:
+            print(write_stats_md(args.stats_md, args.workload, args.profile_steps))
+        if args.counters_md:
+            print(write_counters_md(args.counters_md, args.workload))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -358,6 +564,13 @@ def main() -> int:
                     wt.append(ws0.elapsed_time(ws1) * 1e3)
         return lt, tt, st, wt
 
+    if args.spin_up_ms > 0:
+        print(f"[bench] spin-up {args.spin_up_ms:.0f} ms", file=sys.stderr, flush=True)
+        t_end = time.perf_counter() + args.spin_up_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                pmqa.hbm_read_probe(flush, sink)
+            torch.cuda.synchronize()
     clock_before = gpu_clock_mhz()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     run(args.warmup, pmqa.KEY_FP32, False)
@@ -553,21 +766,25 @@ def main() -> int:
     def probes(xw, tw, reps):
         """Read ceilings for one workload's K stream: a contiguous read of the
         same bytes (K codes + scales), and the paged gather of exactly the
-        pages the logits call reads; times in us."""
+        pages the logits call reads (FP8 pages only); times in us."""
         kb = algorithmic_bytes(xw)
-        src = torch.ones((kb["k"] + kb["k"] // 32) // 4, dtype=torch.int32, device=dev)
+        # MXFP4 tokens carry their scales; FP8 keys add one 4-byte scale per 128 bytes
+        src = torch.ones((kb["k"] if xw.mxfp4 else kb["k"] + kb["k"] // 32) // 4, dtype=torch.int32,
+                         device=dev)
         plist = torch.from_numpy(page_list(xw)).to(dev)
         rd, ga = [], []
         for i in range(reps + 3):
             e0, e1, e2, e3 = new_events(4)
             evict()
             pmqa.hbm_read_probe(src, sink, events=(e0, e1))
-            evict()
-            pmqa.hbm_gather_probe(tw["kv_pages"], tw["k_scales"], plist, sink, events=(e2, e3))
+            if not xw.mxfp4:
+                evict()
+                pmqa.hbm_gather_probe(tw["kv_pages"], tw["k_scales"], plist, sink, events=(e2, e3))
             torch.cuda.synchronize()
             if i >= 3:
                 rd.append(e0.elapsed_time(e1) * 1e3)
-                ga.append(e2.elapsed_time(e3) * 1e3)
+                if not xw.mxfp4:
+                    ga.append(e2.elapsed_time(e3) * 1e3)
         del src, plist
         return rd, ga
 
@@ -603,6 +820,7 @@ def main() -> int:
                                  "p50": round(pct(tw_us, 50), 3), "p90": round(pct(tw_us, 90), 3)},
                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                              "frac": round(ach / HBM_PEAK_GBPS, 4), "bytes_per_launch": abw["total"],
+                             "traffic": measured_traffic(name), "kernel": COUNTED_KERNEL[name],
                              "k_bytes": abw["k"],
                              "k_frac": round(abw["k"] / (lm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
                 "read_probe_us_p50": round(pct(rd, 50), 3),
@@ -619,7 +837,7 @@ def main() -> int:
     ab = algorithmic_bytes(x)
     rd_pts, ga_pts = probes(x, t, 30)
     probe_us = pct(rd_pts, 50)
-    gather_us = pct(ga_pts, 50)
+    gather_us = pct(ga_pts, 50) if ga_pts else None
     clock_after = gpu_clock_mhz()
 
     if args.copy_calibration:
@@ -637,12 +855,7 @@ def main() -> int:
     mean_logits = float(np.mean(lt))
     mfma_flop = int(x.context_lens.astype(np.int64).sum()) * 2 * 32 * 128
     achieved = ab["total"] / (mean_logits * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_src_sha") == kernel_source_digest() and tr.get("workload") == x.name:
-            traffic = tr.get("bytes_per_launch")
+    traffic = measured_traffic(x.name)
     value = float(np.mean(step_us))
     out = {
         "metric": "indexer logits+hist+top-2048 us/step and HBM GB/s (% peak), B=8 L=128K",
@@ -698,9 +911,9 @@ def main() -> int:
             "read_probe_us_p10_p90": [round(pct(rd_pts, 10), 3), round(pct(rd_pts, 90), 3)],
             "read_probe_gbps": round(ab["k"] * 33 / 32 / (probe_us * 1e-6) / 1e9, 1),
             # the same pages read through the block table, whole lines, no arithmetic
-            "gather_probe_us_p50": round(gather_us, 3),
-            "gather_probe_us_p10_p90": [round(pct(ga_pts, 10), 3), round(pct(ga_pts, 90), 3)],
-            "logits_median_vs_gather_probe": round(gather_us / pct(lt, 50), 4),
+            "gather_probe_us_p50": round(gather_us, 3) if ga_pts else None,
+            "gather_probe_us_p10_p90": [round(pct(ga_pts, 10), 3), round(pct(ga_pts, 90), 3)] if ga_pts else None,
+            "logits_median_vs_gather_probe": round(gather_us / pct(lt, 50), 4) if ga_pts else None,
             "logits_median_vs_read_probe": round(probe_us / pct(lt, 50), 4),
         },
         "gpu_clock_mhz": {"before": clock_before, "after": clock_after},
@@ -712,7 +925,7 @@ def main() -> int:
                  "frac_of_fp8_peak": round(mfma_flop / (mean_logits * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "indexer_logits_kernel<1, true, false, 0, false>",
+                     "traffic": traffic, "kernel": COUNTED_KERNEL[x.name],
                      "bytes_per_launch": ab["total"]},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }

@@ -137,3 +137,61 @@ def test_sampled_cpu_baseline_scales_by_row_key_pairs():
 
 def test_gpu_clock_reader_returns_a_mapping():
     assert isinstance(bench.gpu_clock_mhz(), dict)
+
+
+def test_every_workload_names_its_counted_kernel_and_profile_args():
+    import gen
+    for w in gen.CONFIG_NAMES + gen.MXFP4_CONFIG_NAMES + gen.PREFILL_CONFIG_NAMES:
+        assert w in bench.COUNTED_KERNEL
+        args = bench.profile_args(w, 5)
+        assert "--no-cpu-baseline" in args and "--sweep-steps 0" in args
+        if w.startswith("prefill/"):
+            assert "--prefill-steps 5" in args
+        else:
+            assert f"--workload {w} " in args and "--prefill-steps 0" in args
+    assert bench.traffic_file("spec_verify/unit").endswith("logits_spec_verify_unit_traffic.json")
+
+
+def test_traffic_record_of_another_workload_reads_its_kernel(tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    pf = "void pmqa::(anonymous namespace)::indexer_prefill_logits_kernel<0>(pmqa::PrefillArgs)"
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [
+        (LOGITS, 50.0), (pf, 400.0), (pf, 600.0), (COPY, copy_kib / 2)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [(LOGITS, 9.0), (pf, 100.0), (COPY, copy_kib)])
+    tr = bench.traffic_from(str(tmp_path / "f"), str(tmp_path / "w"), "prefill/extend")
+    assert tr["kernel"] == bench.COUNTED_KERNEL["prefill/extend"]
+    assert tr["FETCH_SIZE"]["dispatches"] == 2
+    assert tr["bytes_per_launch"] == round(500.0 * 1024 * 2 + 100.0 * 1024)
+    md = bench.write_traffic_md(tr, 1_000_000, out_dir=str(tmp_path))
+    text = open(md).read()
+    assert "--traffic-from" in text and "prefill/extend" in text and "--prefill-steps 5" in text
+
+
+def test_stats_and_counter_summaries(tmp_path):
+    st = tmp_path / "run_kernel_stats.csv"
+    with open(st, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        w.writerow({"Name": "void pmqa::(anonymous namespace)::topk_finish_kernel<0, false>(int)",
+                    "Calls": 7, "AverageNs": 8000.0, "MinNs": 7000, "MaxNs": 9000})
+    md = open(bench.write_stats_md(str(st), "varlen_decode", 5, out_dir=str(tmp_path))).read()
+    assert "| topk_finish_kernel<0, false> | 7 | 8.00 | 7.00 | 9.00 |" in md
+    assert "--kernel-trace --stats" in md and "--workload varlen_decode" in md
+    d = tmp_path / "pmc"
+    os.makedirs(d)
+    k = "void pmqa::(anonymous namespace)::" + bench.COUNTED_KERNEL["spec_verify/fine"] + "(pmqa::LogitsArgs, int)"
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                                          "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for disp, busy in ((1, 3200.0), (2, 3200.0), (3, 6400.0)):
+            for name, v in (("SQ_INSTS_MFMA", 100.0), ("SQ_VALU_MFMA_BUSY_CYCLES", busy)):
+                # two rows per counter and dispatch (e.g. per XCD) are summed
+                for _ in range(2):
+                    w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Counter_Name": name,
+                                "Counter_Value": v / 2, "Start_Timestamp": 1000, "End_Timestamp": 21000})
+    c = bench.counters_of(str(d), bench.COUNTED_KERNEL["spec_verify/fine"])
+    assert c["SQ_INSTS_MFMA"] == 100.0 and c["SQ_VALU_MFMA_BUSY_CYCLES"] == 3200.0
+    assert c["dispatches"] == 3 and c["duration_us"] == 20.0
+    md = open(bench.write_counters_md(str(d), "spec_verify/fine", out_dir=str(tmp_path))).read()
+    assert "Busy cycles per MFMA: 32.0" in md
