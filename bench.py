@@ -631,7 +631,7 @@ def main() -> int:
         width = -(-(-(-x.logits_stride // 8)) // 4) * 4
         am = torch.empty((x.rows, width), dtype=torch.float32, device=dev)
         ah = torch.zeros((x.rows, 1024), dtype=torch.int32, device=dev)
-        blens = (t["context_lens"] + 7) // 8
+        blens = torch.empty(x.rows, dtype=torch.int32, device=dev)
         bsel = torch.empty((x.rows, kbk), dtype=torch.int32, device=dev)
         table = torch.empty_like(bsel)
         slots = torch.empty_like(bsel)
@@ -651,7 +651,7 @@ def main() -> int:
                 ev = new_events(12)
                 evict()
                 ah.zero_()
-                pmqa.block_amax8(logits, t["context_lens"], am, ah, events=(ev[0], ev[1]))
+                pmqa.block_amax8(logits, t["context_lens"], am, ah, block_lens=blens, events=(ev[0], ev[1]))
                 pmqa.topk_rows(am, ah, blens, kbk, pmqa.KEY_FP32, bsel, ws_b, events=(ev[2], ev[3]))
                 pmqa.sort_candidate_blocks(bsel, t["context_lens"], x.logits_stride, t["block_table"],
                                            x.next_n, table, slots, slens, events=(ev[4], ev[5]))

@@ -265,18 +265,20 @@ idx_status indexer_logits_mxfp4(const uint8_t* q, const uint8_t* kv_pages,
  * 8j .. 8j+7 of row r (NaN ignored; NaN if all are NaN) for j < ceil(len_r/8),
  * except the newest block, written as +inf so it is always selected; nothing
  * is written at or past ceil(len_r / 8).  The block top-k is topk_rows over
- * these rows with lengths ceil(len_r / 8).  With hist != NULL the maxima are
- * also added to the row's 1024-bin coarse histogram ([P1] contract: zero at
+ * these rows with lengths ceil(len_r / 8), which the call writes to
+ * block_lens when it is not NULL.  With hist != NULL the maxima are also
+ * added to the row's 1024-bin coarse histogram ([P1] contract: zero at
  * entry, accumulating), so that top-k needs no first pass.
  *
  * scores       (device) float [rows][stride], 16-B aligned, stride % 4 == 0
  * context_lens (device) int32 [rows]; clamped to [0, stride]
  * out          (device) float [rows][out_stride], out_stride >= ceil(stride/8)
  * hist         (device) int32 [rows][1024], 8-B aligned, or NULL
+ * block_lens   (device) int32 [rows] (overwritten), 4-B aligned, or NULL
  */
 idx_status block_amax8(const float* scores, int64_t stride, const int32_t* context_lens,
                        int32_t rows, float* out, int64_t out_stride, int32_t* hist,
-                       void* stream);
+                       int32_t* block_lens, void* stream);
 
 /*
  * sort_candidate_blocks -- [P2] sort_candidate_blocks: the selected block ids

@@ -117,7 +117,7 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_logits_f16.restype = ctypes.c_int
     lib.indexer_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp]
     lib.indexer_logits_mxfp4.restype = ctypes.c_int
-    lib.block_amax8.argtypes = [vp, i64, vp, i32, vp, i64, vp, vp]
+    lib.block_amax8.argtypes = [vp, i64, vp, i32, vp, i64, vp, vp, vp]
     lib.block_amax8.restype = ctypes.c_int
     lib.sort_candidate_blocks.argtypes = [vp, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp, vp]
     lib.sort_candidate_blocks.restype = ctypes.c_int
@@ -284,9 +284,11 @@ def _rows2(t, name, dtype, dev, rows=None):
         raise ValueError(f"{name} must be contiguous [{rows if rows is not None else 'rows'}, n]")
 
 
-def block_amax8(scores, context_lens, out, hist=None, events=None):
+def block_amax8(scores, context_lens, out, hist=None, block_lens=None, events=None):
     """Block maxima of 8 scores per row (newest block +inf) into out [rows, >= ceil(stride/8)];
-    with ``hist`` [rows, 1024] int32 their coarse histogram is accumulated too."""
+    with ``hist`` [rows, 1024] int32 their coarse histogram is accumulated too, and
+    ``block_lens`` [rows] int32 receives each row's block count ceil(len / 8) (the
+    lengths the block top-k takes)."""
     dev = scores.device
     _need(scores, "scores", torch.float32, dev, 2)
     rows = scores.shape[0]
@@ -299,8 +301,12 @@ def block_amax8(scores, context_lens, out, hist=None, events=None):
         _arm(events, dev)
         if hist is not None:
             _rows2(hist, "hist", torch.int32, dev, rows)
+        if block_lens is not None:
+            _need(block_lens, "block_lens", torch.int32, dev, 1)
+            if tuple(block_lens.shape) != (rows,) or not block_lens.is_contiguous():
+                raise ValueError("block_lens must be a contiguous int32 [rows]")
         st = lib.block_amax8(_ptr(scores), int(scores.stride(0)), _ptr(context_lens), int(rows), _ptr(out),
-                             int(out.stride(0)), _ptr(hist), _stream_ptr(dev))
+                             int(out.stride(0)), _ptr(hist), _ptr(block_lens), _stream_ptr(dev))
     _check("block_amax8", st)
 
 

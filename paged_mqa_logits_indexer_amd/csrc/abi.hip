@@ -178,15 +178,15 @@ idx_status score_histogram(const float* scores, int64_t stride, const int32_t* c
 }
 
 idx_status block_amax8(const float* scores, int64_t stride, const int32_t* context_lens, int32_t rows,
-                       float* out, int64_t out_stride, int32_t* hist, void* stream) {
+                       float* out, int64_t out_stride, int32_t* hist, int32_t* block_lens, void* stream) {
   const pmqa::LaunchEvents ev = take_events();
   if (!scores || !context_lens || !out) return IDX_EINVAL;
   if (rows <= 0 || stride <= 0 || out_stride < (stride + 7) / 8) return IDX_EINVAL;
   if (rows > IDX_MAX_ROWS || stride > (int64_t{1} << 31) - 4) return IDX_EUNSUPPORTED;
   if (!aligned(scores, 16) || (stride % 4) != 0 || !aligned(context_lens, 4) || !aligned(out, 4) ||
-      (hist && !aligned(hist, 8)))
+      (hist && !aligned(hist, 8)) || (block_lens && !aligned(block_lens, 4)))
     return IDX_EALIGN;
-  return from_hip(pmqa::launch_block_amax8(scores, stride, context_lens, rows, out, out_stride, hist,
+  return from_hip(pmqa::launch_block_amax8(scores, stride, context_lens, rows, out, out_stride, hist, block_lens,
                                            static_cast<hipStream_t>(stream), ev));
 }
 

@@ -28,18 +28,22 @@ constexpr int kWordsPerThread = kBitmapWords / kSortThreads;
 // block before the newest lies wholly below len, so its two 16-byte loads
 // read live scores only.  HIST: the maxima also go into the row's coarse
 // histogram (per-workgroup LDS slots added with 64-bit atomics, as in the
-// logits kernel), so the block top-k can skip its own first pass.
+// logits kernel), so the block top-k can skip its own first pass.  The first
+// thread of each row writes the row's block count to block_lens (if given):
+// the lengths the block top-k takes.
 template <bool HIST>
 __global__ __launch_bounds__(256) void block_amax8_kernel(const float* __restrict__ scores, int64_t stride,
                                                           const int32_t* __restrict__ lens,
                                                           float* __restrict__ out, int64_t out_stride,
-                                                          int32_t* __restrict__ hist) {
+                                                          int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ block_lens) {
   __shared__ int s_hist[HIST ? kBins : 1];
   const int row = blockIdx.y;
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t l = lens[row];
   const int64_t len = l < 0 ? 0 : (l > stride ? stride : l);
-  const int64_t nb = (len + kBlk - 1) / kBlk;
+  const int64_t nb = (len + kBlk - 1) / kBlk;  // < 2^28: stride < 2^31
+  if (block_lens && j == 0) block_lens[row] = static_cast<int32_t>(nb);
   if (static_cast<int64_t>(blockIdx.x) * 256 >= nb) return;  // uniform: no block of this row here
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < kBins; i += 256) s_hist[i] = 0;
@@ -172,17 +176,18 @@ __global__ void sparse_to_logical_kernel(const int32_t* __restrict__ idx, int k,
 }  // namespace
 
 hipError_t launch_block_amax8(const float* scores, int64_t stride, const int32_t* lens, int32_t rows, float* out,
-                              int64_t out_stride, int32_t* hist, hipStream_t stream, LaunchEvents ev) {
+                              int64_t out_stride, int32_t* hist, int32_t* block_lens, hipStream_t stream,
+                              LaunchEvents ev) {
   const int64_t nbmax = (stride + kBlk - 1) / kBlk;
   const int64_t gx = (nbmax + 255) / 256;
   if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(rows));
   if (hist)
     launch_kernel(block_amax8_kernel<true>, grid, dim3(256), stream, ev.start, ev.stop, scores, stride, lens, out,
-                  out_stride, hist);
+                  out_stride, hist, block_lens);
   else
     launch_kernel(block_amax8_kernel<false>, grid, dim3(256), stream, ev.start, ev.stop, scores, stride, lens, out,
-                  out_stride, hist);
+                  out_stride, hist, block_lens);
   return hipGetLastError();
 }
 

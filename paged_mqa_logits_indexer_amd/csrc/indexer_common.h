@@ -225,7 +225,8 @@ struct PrefillArgs {
 };
 hipError_t launch_indexer_prefill_logits(const PrefillArgs& a, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_block_amax8(const float* scores, int64_t stride, const int32_t* lens, int32_t rows, float* out,
-                              int64_t out_stride, int32_t* hist, hipStream_t stream, LaunchEvents ev = {});
+                              int64_t out_stride, int32_t* hist, int32_t* block_lens, hipStream_t stream,
+                              LaunchEvents ev = {});
 hipError_t launch_sort_candidate_blocks(const int32_t* blocks, int32_t kb, const int32_t* lens, int32_t rows,
                                         int64_t max_len, const int32_t* block_table, int32_t max_pages,
                                         int32_t next_n, int32_t* table, int32_t* slots, int32_t* sparse_lens,

@@ -33,14 +33,16 @@ def test_block_amax8(gpu):
     out = torch.full((rows, width + 3), SENT, dtype=torch.float32, device=DEV)
     out2 = torch.full((rows, width + 3), SENT, dtype=torch.float32, device=DEV)
     h = torch.zeros((rows, 1024), dtype=torch.int32, device=DEV)
+    bl = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
     announce("block_amax8")
     gpu.block_amax8(s, ln, out)
-    gpu.block_amax8(s, ln, out2, h)
+    gpu.block_amax8(s, ln, out2, h, block_lens=bl)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.array_equal(got, out2.cpu().numpy(), equal_nan=True), "the histogram changes the maxima"
     want = C.block_amax8(sc, lens)
     blk_lens = -(-lens.astype(np.int64) // 8)
+    assert np.array_equal(bl.cpu().numpy(), blk_lens), "block counts (lengths of the block rows)"
     assert np.array_equal(h.cpu().numpy(), O.coarse_histogram(got[:, :width], blk_lens)), \
         "histogram of the block maxima differs"
     for r in range(rows):
@@ -140,8 +142,10 @@ def test_candidate_chain(gpu, name, kb_blocks):
     am = torch.full((x.rows, width), SENT, dtype=torch.float32, device=DEV)
     ah = torch.zeros((x.rows, 1024), dtype=torch.int32, device=DEV)
     announce(f"{name}: block_amax8")
-    gpu.block_amax8(lg, d.lens, am, ah)
-    blens = torch.from_numpy(-(-lens.astype(np.int64) // 8).astype(np.int32)).to(DEV)
+    blens = torch.full((x.rows,), -5, dtype=torch.int32, device=DEV)
+    gpu.block_amax8(lg, d.lens, am, ah, block_lens=blens)
+    torch.cuda.synchronize()
+    assert np.array_equal(blens.cpu().numpy(), -(-lens.astype(np.int64) // 8))
     announce(f"{name}: block top-{kb_blocks}")
     bsel = topk(am, ah, blens, kb_blocks, O.KEY_FP32)
     am_h = am.cpu().numpy()
