@@ -51,6 +51,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA, MI355X
 FLUSH_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
+CALIBRATION_COPIES = 3  # copies run after the timing with --copy-calibration
 # The logits kernel each workload launches, whose counters and trace are
 # read: indexer_logits_kernel<rows per request, histogram, FP16 output, K
 # format (0 FP8, 1 MXFP4), persistent grid> (varlen_decode: 64 one-row
@@ -74,7 +75,7 @@ LOGITS_KERNEL = COUNTED_KERNEL["long_decode"]
 # else (the prefill workloads run in the prefill leg, after two long-decode
 # steps).
 LEGS_OFF = ("--fp16-steps 0 --mxfp4-steps 0 --candidate-steps 0 --prefill-steps 0 --hist-steps 0 "
-            "--sweep-steps 0 --scores-steps 0 --no-cpu-baseline")
+            "--sweep-steps 0 --scores-steps 0 --coissue-iters 0 --no-cpu-baseline")
 
 
 def slug(workload: str) -> str:
@@ -259,7 +260,9 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
             raise SystemExit(f"{counter}: no dispatch of {kernel} under {d}")
         last_logits = max(hits)
         logits = [v for _, name, v in rows if kernel in name]
-        copies = [v for _, name, v in rows[last_logits + 1:] if "copy" in name.lower()]
+        # the calibration copies are the run's last three copy kernels (other
+        # copies, such as uploads of later inputs, may follow the kernel too)
+        copies = [v for _, name, v in rows[last_logits + 1:] if "copy" in name.lower()][-CALIBRATION_COPIES:]
         if not copies:
             raise SystemExit(f"{counter}: no calibration copy after the last logits dispatch")
         copy_kib = float(np.mean(copies))
@@ -420,6 +423,8 @@ def main() -> int:
                     help="steps of the logits kernel with and without the histogram (interleaved)")
     ap.add_argument("--sweep-steps", type=int, default=40,
                     help="steps per decode workload in the all-workload sweep (0: skip it)")
+    ap.add_argument("--coissue-iters", type=int, default=4096,
+                    help="rounds per wave of the MFMA / VALU co-issue probe (0: skip it)")
     ap.add_argument("--scores-steps", type=int, default=30,
                     help="steps of top-2048 over the very-long synthetic score rows (no histogram)")
     ap.add_argument("--candidate-blocks", type=int, default=512,
@@ -738,6 +743,33 @@ def main() -> int:
                 "logits_write_gbps": round(pairs * 4 / (pu * 1e-6) / 1e9, 1)}
             del tp, cu, lgp
 
+    # how far a SIMD's matrix and vector pipes overlap: fp8 MFMAs only, fp32
+    # FMAs only (eight per MFMA, the logits epilogue's ratio), and both
+    co_out = None
+    if args.coissue_iters > 0:
+        print(f"[bench] MFMA / VALU co-issue probe: {args.coissue_iters} rounds", file=sys.stderr, flush=True)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        co_out = {"rounds_per_wave": args.coissue_iters, "mfma_per_round": 4, "fma_per_round": 32}
+        for wps in (1, 2):
+            buf = torch.empty(cus * wps * 256, dtype=torch.float32, device=dev)
+            us = {}
+            for mode, name in ((0, "mfma_only_us"), (1, "valu_only_us"), (2, "both_us")):
+                pmqa.mfma_valu_probe(mode, wps, args.coissue_iters, buf)
+                evs = []
+                for i in range(5):
+                    e0, e1 = new_events(2)
+                    pmqa.mfma_valu_probe(mode, wps, args.coissue_iters, buf, events=(e0, e1))
+                    evs.append((e0, e1))
+                torch.cuda.synchronize()
+                us[name] = round(float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs])), 2)
+            m, v, b = us["mfma_only_us"], us["valu_only_us"], us["both_us"]
+            rounds = args.coissue_iters * wps  # per SIMD
+            us.update({"both_over_sum": round(b / (m + v), 3), "both_over_max": round(b / max(m, v), 3),
+                       "cycles_per_mfma_at_2400mhz": round(m * 2400.0 / (4 * rounds), 1),
+                       "cycles_per_fma_at_2400mhz": round(v * 2400.0 / (32 * rounds), 2)})
+            co_out[f"waves_per_simd_{wps}"] = us
+            del buf
+
     # top-2048 over synthetic fp32 score rows [4, 1048576] (0.99 N(0, var 4) +
     # 0.01 N(40, var 10)), FP16 keys, no histogram: the selector's own first
     # pass, then threshold bin, collect and refine
@@ -846,7 +878,7 @@ def main() -> int:
         # 4 B written per element.
         src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
         dst = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        for i in range(3):
+        for i in range(CALIBRATION_COPIES):
             evict()
             dst.copy_(src)
         torch.cuda.synchronize()
@@ -902,6 +934,8 @@ def main() -> int:
         "prefill": pf_out,
         # top-2048 over synthetic score rows [4, 1048576], FP16 keys, hist=NULL
         "topk_scores_1m": sc_out,
+        # MFMA / VALU co-issue probe (the prefill epilogue's bound)
+        "mfma_valu_coissue": co_out,
         "hbm": {
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),

@@ -444,6 +444,20 @@ idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* s
 idx_status hbm_gather_probe(const uint8_t* kv_pages, const float* k_scales, const int32_t* page_list,
                             int32_t n_pages, int32_t num_pages, uint32_t* sink, void* stream);
 
+/*
+ * mfma_valu_probe -- measurement aid, not part of the method: how far a
+ * SIMD's matrix and vector pipes overlap.  Launches waves_per_simd (1..8)
+ * 256-thread workgroups per CU (one wave per SIMD each); every wave runs
+ * `iters` (1..2^20) rounds of four independent fp8 16x16x128 MFMAs (mode 0),
+ * 32 independent fp32 FMAs (mode 1) or both, interleaved and independent
+ * (mode 2) -- eight FMAs per MFMA, the logits epilogue's ratio -- and stores
+ * one float per thread to out (device, 4-B aligned, out_len >= CUs *
+ * waves_per_simd * 256 floats).  IDX_EINVAL for a mode, count or out_len out
+ * of range, before anything is launched.
+ */
+idx_status mfma_valu_probe(int32_t mode, int32_t waves_per_simd, int32_t iters, float* out, int64_t out_len,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

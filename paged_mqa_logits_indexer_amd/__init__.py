@@ -31,6 +31,7 @@ Entry points (same names as the C ABI):
   indexer_time_next_call(start, stop)
   hbm_read_probe(src, sink, events=None)
   hbm_gather_probe(kv_pages, k_scales, page_list, sink, events=None)
+  mfma_valu_probe(mode, waves_per_simd, iters, out, events=None)
 With ``events=(start, stop)`` (torch.cuda.Event with timing enabled, either
 may be None) the call is preceded by indexer_time_next_call, so its own
 kernel dispatches record the events: start when its first kernel begins,
@@ -52,6 +53,7 @@ __all__ = [
     "sparse_to_logical",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "topk_rows_noalloc", "score_histogram",
     "indexer_status_str", "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe",
+    "mfma_valu_probe",
 ]
 
 KEY_FP32 = 0
@@ -68,7 +70,7 @@ EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp
                     "indexer_prefill_logits", "indexer_prefill_logits_mxfp4", "sparse_to_logical",
                     "topk_workspace_bytes", "topk_rows", "topk_rows_noalloc",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
-                    "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe")
+                    "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe", "mfma_valu_probe")
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpaged_mqa_indexer.so"
@@ -113,6 +115,8 @@ def load_library() -> ctypes.CDLL:
     lib.hbm_read_probe.restype = ctypes.c_int
     lib.hbm_gather_probe.argtypes = [vp, vp, vp, i32, i32, vp, vp]
     lib.hbm_gather_probe.restype = ctypes.c_int
+    lib.mfma_valu_probe.argtypes = [i32, i32, i32, vp, i64, vp]
+    lib.mfma_valu_probe.restype = ctypes.c_int
     lib.indexer_logits_f16.argtypes = lib.indexer_logits.argtypes
     lib.indexer_logits_f16.restype = ctypes.c_int
     lib.indexer_logits_mxfp4.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp]
@@ -556,3 +560,19 @@ def hbm_gather_probe(kv_pages: torch.Tensor, k_scales: torch.Tensor, page_list: 
         st = lib.hbm_gather_probe(_ptr(kv_pages), _ptr(k_scales), _ptr(page_list), int(page_list.numel()),
                                   int(kv_pages.shape[0]), _ptr(sink), _stream_ptr(dev))
     _check("hbm_gather_probe", st)
+
+
+def mfma_valu_probe(mode: int, waves_per_simd: int, iters: int, out: torch.Tensor, events=None) -> None:
+    """MFMA / VALU co-issue probe: mode 0 fp8 MFMAs only, 1 fp32 FMAs only,
+    2 both (independent, eight FMAs per MFMA); ``out`` float32 with at least
+    CUs * waves_per_simd * 256 elements."""
+    dev = out.device
+    _need(out, "out", torch.float32, dev)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        st = lib.mfma_valu_probe(int(mode), int(waves_per_simd), int(iters), _ptr(out), int(out.numel()),
+                                 _stream_ptr(dev))
+    _check("mfma_valu_probe", st)

@@ -323,6 +323,23 @@ idx_status hbm_gather_probe(const uint8_t* kv_pages, const float* k_scales, cons
                                                 static_cast<hipStream_t>(stream), ev));
 }
 
+idx_status mfma_valu_probe(int32_t mode, int32_t waves_per_simd, int32_t iters, float* out, int64_t out_len,
+                           void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!out || mode < 0 || mode > 2 || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 ||
+      iters > (1 << 20))
+    return IDX_EINVAL;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return IDX_ELAUNCH;
+  const int64_t workgroups = static_cast<int64_t>(cus) * waves_per_simd;  // 4 waves each: one per SIMD
+  if (out_len < workgroups * 256) return IDX_EINVAL;
+  if (!aligned(out, 4)) return IDX_EALIGN;
+  return from_hip(pmqa::launch_mfma_valu_probe(mode, static_cast<int>(workgroups), iters, out,
+                                               static_cast<hipStream_t>(stream), ev));
+}
+
 idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   const pmqa::LaunchEvents ev = take_events();
   if (!src || !sink || bytes == 0) return IDX_EINVAL;

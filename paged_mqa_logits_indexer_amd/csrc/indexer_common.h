@@ -260,4 +260,6 @@ hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
 hipError_t launch_hbm_gather_probe(const uint8_t* pool, const float* scales, const int32_t* table,
                                    int32_t n_pages, int32_t pool_pages, uint32_t* sink, hipStream_t stream,
                                    LaunchEvents ev = {});
+hipError_t launch_mfma_valu_probe(int mode, int workgroups, int iters, float* out, hipStream_t stream,
+                                  LaunchEvents ev = {});
 }  // namespace pmqa

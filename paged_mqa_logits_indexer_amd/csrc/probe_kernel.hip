@@ -94,7 +94,57 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void hbm_gather_probe_kernel(
   if (acc == 0x9E3779B9u) atomicXor(sink, acc);  // keeps the loads live
 }
 
+// MFMA / VALU co-issue: every wave runs `iters` rounds of four independent
+// fp8 16x16x128 MFMAs (the logits kernels' instruction) and/or 32
+// independent fp32 FMAs (eight per MFMA: the logits epilogue's two VALU
+// operations on each of an MFMA's four outputs per lane), with no dependence
+// between the two streams.  Timing the three modes shows how far the matrix
+// and vector pipes of a SIMD overlap; the result per thread is stored so
+// that nothing is dropped.
+constexpr int kCoissueFmas = 32;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void mfma_valu_probe_kernel(float* __restrict__ out, int iters, float c) {
+  // e4m3 bytes 0x38 / 0x39 (1.0, 1.125) and 0x30 (0.5): finite products
+  const int lo = 0x38383838 + static_cast<int>(threadIdx.x & 1u);
+  const i32x8 a = {lo, lo, lo, lo, lo, lo, lo, lo};
+  const i32x8 b = {0x30303030, 0x30303030, 0x30303030, 0x30303030,
+                   0x30303030, 0x30303030, 0x30303030, 0x30303030};
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
+  float v[kCoissueFmas];
+#pragma unroll
+  for (int i = 0; i < kCoissueFmas; ++i) v[i] = static_cast<float>(threadIdx.x) * 1e-3f + static_cast<float>(i);
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MODE != 1) {
+      acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc0, 0, 0, 0, 127, 0, 127);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc1, 0, 0, 0, 127, 0, 127);
+      acc2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc2, 0, 0, 0, 127, 0, 127);
+      acc3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc3, 0, 0, 0, 127, 0, 127);
+    }
+    if constexpr (MODE != 0) {
+#pragma unroll
+      for (int i = 0; i < kCoissueFmas; ++i) v[i] = fmaf(v[i], c, 0.5f);
+    }
+  }
+  float s = acc0[0] + acc1[1] + acc2[2] + acc3[3];
+#pragma unroll
+  for (int i = 0; i < kCoissueFmas; ++i) s += v[i];
+  out[static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_valu_probe(int mode, int workgroups, int iters, float* out, hipStream_t stream,
+                                  LaunchEvents ev) {
+  const dim3 grid(static_cast<unsigned>(workgroups)), block(256);
+  if (mode == 0)
+    launch_kernel(mfma_valu_probe_kernel<0>, grid, block, stream, ev.start, ev.stop, out, iters, 0.999f);
+  else if (mode == 1)
+    launch_kernel(mfma_valu_probe_kernel<1>, grid, block, stream, ev.start, ev.stop, out, iters, 0.999f);
+  else
+    launch_kernel(mfma_valu_probe_kernel<2>, grid, block, stream, ev.start, ev.stop, out, iters, 0.999f);
+  return hipGetLastError();
+}
 
 hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream,
                                  LaunchEvents ev) {

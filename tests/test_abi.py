@@ -308,3 +308,14 @@ def test_gather_probe_rejects(lib, kw, status):
     args.update(kw)
     assert lib.hbm_gather_probe(args["pool"], args["scales"], args["table"], args["n"], args["num"],
                                 args["sink"], None) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(out=None), dict(mode=-1), dict(mode=3), dict(waves=0), dict(waves=9), dict(iters=0),
+    dict(iters=(1 << 20) + 1),
+])
+def test_coissue_probe_rejects_before_any_device_query(lib, kw):
+    args = dict(mode=2, waves=1, iters=16, out=A, out_len=1 << 20)
+    args.update(kw)
+    assert lib.mfma_valu_probe(args["mode"], args["waves"], args["iters"], args["out"], args["out_len"],
+                               None) == IDX_EINVAL

@@ -155,8 +155,9 @@ def test_every_workload_names_its_counted_kernel_and_profile_args():
 def test_traffic_record_of_another_workload_reads_its_kernel(tmp_path):
     copy_kib = bench.COPY_BYTES / 1024
     pf = "void pmqa::(anonymous namespace)::indexer_prefill_logits_kernel<0>(pmqa::PrefillArgs)"
+    # an upload copy after the kernel's last dispatch is not a calibration copy
     _write_counters(tmp_path / "f", "FETCH_SIZE", [
-        (LOGITS, 50.0), (pf, 400.0), (pf, 600.0), (COPY, copy_kib / 2)])
+        (LOGITS, 50.0), (pf, 400.0), (pf, 600.0), (COPY, 3.0)] + [(COPY, copy_kib / 2)] * 3)
     _write_counters(tmp_path / "w", "WRITE_SIZE", [(LOGITS, 9.0), (pf, 100.0), (COPY, copy_kib)])
     tr = bench.traffic_from(str(tmp_path / "f"), str(tmp_path / "w"), "prefill/extend")
     assert tr["kernel"] == bench.COUNTED_KERNEL["prefill/extend"]

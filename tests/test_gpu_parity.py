@@ -572,3 +572,21 @@ def test_read_probes_run_on_small_buffers(gpu):
     gpu.hbm_gather_probe(pool, scales, plist, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
+
+
+def test_coissue_probe_runs_every_mode(gpu):
+    """The MFMA / VALU co-issue probe: every mode and wave count launches and
+    writes one finite value per thread; a too-short output is refused."""
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    for wps in (1, 2):
+        out = torch.full((cus * wps * 256 + 5,), float("nan"), dtype=torch.float32, device=DEV)
+        for mode in (0, 1, 2):
+            announce(f"mfma_valu_probe mode={mode} waves/SIMD={wps}")
+            out.fill_(float("nan"))
+            gpu.mfma_valu_probe(mode, wps, 64, out)
+            torch.cuda.synchronize()
+            got = out[:cus * wps * 256]
+            assert bool(torch.isfinite(got).all()), (mode, wps)
+            assert bool(torch.isnan(out[cus * wps * 256:]).all()), "written past the grid"
+    with pytest.raises(pmqa.IndexerError):
+        gpu.mfma_valu_probe(2, 1, 16, torch.zeros(cus * 256 - 1, dtype=torch.float32, device=DEV))
