@@ -127,10 +127,11 @@ idx_status indexer_logits(const uint8_t* q, const uint8_t* kv_pages,
 /*
  * topk_workspace_bytes -- size of the scratch buffer topk_rows needs for
  * `rows` rows (host-only query, no device work): one 140,544-byte record per
- * row -- two 8-byte counter pairs (padded to 256 bytes), a 1 KiB histogram of
- * the threshold bin's sub-bins, a 4 KiB histogram, 128 KiB of candidates and
- * 4 KiB of per-workgroup counts -- whatever the
- * stride and k, so a row's record sits at the same place for every call.
+ * row -- two 8-byte counter pairs and the threshold bin (padded to 256
+ * bytes), a 1 KiB histogram of the threshold bin's sub-bins, a 4 KiB
+ * histogram, 128 KiB of candidates and 4 KiB of per-workgroup counts --
+ * whatever the stride and k, so a row's record sits at the same place for
+ * every call.
  * Rows of at most 16384 scores (logits_stride <= 16384) leave the workspace
  * untouched.  Returns 0 for rows <= 0, logits_stride <= 0 or k <= 0.
  */

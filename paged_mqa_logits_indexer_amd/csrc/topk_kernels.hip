@@ -85,6 +85,9 @@ constexpr int kRowSpanMax = 2 * kRowSpan;  // 16384: rows topk_row takes in two 
 //             the candidate buffer, odd ones from the back, which halves the
 //             atomics on each counter; the lists meet in the middle only when
 //             the counts contradict b*.  The finish pass leaves them zero.
+//             Then b* as the collect pass found it (the finish pass takes it
+//             from here instead of scanning the histogram again); the
+//             counters and b* are padded to 256 bytes.
 //   sub       256 sub-bins of the threshold bin (its FP16-key range cut into
 //             256 equal parts), added to by the collect workgroups from the
 //             candidates they place; the finish pass cuts the threshold bin
@@ -120,6 +123,10 @@ struct Workspace {
   char* base;
   __device__ unsigned long long* count(int row) const {
     return reinterpret_cast<unsigned long long*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecCount);
+  }
+  // b* of the row's last collect pass (after the two counter pairs)
+  __device__ int* bstar(int row) const {
+    return reinterpret_cast<int*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecCount + 16);
   }
   __host__ __device__ int* hist(int row) const {
     return reinterpret_cast<int*>(base + static_cast<size_t>(row) * kRowScratchBytes + kRecHist);
@@ -476,6 +483,9 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
   const Threshold th = threshold_bin<kThreads, 4>(hc, k, s_red);
   const int bstar = th.bin;
   const bool with_sub = th.count > kCutMin;  // uniform
+  // Every workgroup of the row finds the same b*; the first (which runs
+  // whenever the row has a live score) hands it to the finish pass.
+  if (blockIdx.x == 0 && tid == 0) *ws.bstar(row) = bstar;
 
   const Classifier cl(bstar);
   uint32_t gmask[M], emask[M];
@@ -1204,7 +1214,11 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
   const int n_wg = static_cast<int>((static_cast<int64_t>(len) + collect_span - 1) / collect_span);
 
   const unsigned long long front = count[0], back = count[1];
-  const int2 h = *reinterpret_cast<const int2*>(hist + row * hist_stride + 2 * tid);
+  // b* as the collect pass found it (the same for all of its workgroups).  A
+  // row with no live score ran no collect workgroup and may read a stale
+  // value: its counts (zero) then send it to the padding-only output, either
+  // directly (b* = all bins) or through the whole-row select.
+  const int bstar = *ws.bstar(row);
   int slot[kSlotsPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) slot[j] = ws.slots(row)[j * kRefineThreads + tid];
@@ -1215,8 +1229,6 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
     early_f[j] = cand[j * kRefineThreads + tid];
     early_b[j] = cand[kCandBuf - 1 - (j * kRefineThreads + tid)];
   }
-  const int hv[2] = {h.x, h.y};
-  const int bstar = threshold_bin<kRefineThreads, 2>(hv, k, sh.red).bin;
   // This call's true counts: the sums of the slots of the workgroups that
   // ran, even ones (front pair) and odd ones (back pair) apart.
   i32x4 mine{0, 0, 0, 0};

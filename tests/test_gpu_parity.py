@@ -356,6 +356,34 @@ def test_topk_garbage_workspace_with_stale_histogram(gpu, key):
 
 
 @pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+def test_topk_empty_rows_with_a_stale_threshold_slot(gpu, key):
+    """The finish pass takes b* from the record the collect pass wrote; a row
+    with no live score runs no collect workgroup, so it reads whatever the
+    slot holds (all bins, bin 0, a middle bin, a negative value, 0xA5 bytes):
+    it must still come out as padding only, next to normal rows."""
+    rng = np.random.default_rng(515)
+    stride = 40000
+    rows = [np.zeros(0, np.float32), rng.standard_normal(30000).astype(np.float32),
+            np.zeros(0, np.float32), np.array([2.5], np.float32), np.zeros(0, np.float32)]
+    buf, lens = _scores_dev(rows)
+    buf = np.concatenate([buf, np.full((buf.shape[0], stride - buf.shape[1]), np.inf, np.float32)], axis=1)
+    s_, ln = torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV)
+    h = torch.zeros((len(rows), 1024), dtype=torch.int32, device=DEV)
+    gpu.score_histogram(s_, ln, h)
+    rec = gpu.topk_workspace_bytes(1, stride, 1)
+    for slot in (1024, 0, 600, -5, None):
+        ws = torch.full((len(rows) * rec,), 0xA5, dtype=torch.uint8, device=DEV)
+        w32 = ws.view(torch.int32).view(len(rows), rec // 4)
+        w32[:, 0:4] = 0  # clean counter pairs
+        if slot is not None:
+            w32[:, 4] = slot  # the b* slot after the two pairs
+        for k in (1, 2048):
+            announce(f"topk_rows empty rows, b* slot {slot}, k={k} key={key}")
+            idx = topk(s_, h, ln, k, key, workspace=ws)
+            check_topk(idx.cpu().numpy(), buf, lens, k, key)
+
+
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
 def test_topk_without_histogram_reuses_its_workspace(gpu, key):
     """hist=NULL on rows longer than 8192: the selector builds its histograms
     in the workspace, and every call leaves them zero for the next.  A
