@@ -678,6 +678,51 @@ def main() -> int:
         chain(3, False)
         per, pub, sel = chain(args.candidate_steps, True)
         keys_listed = int(slens.sum().item())
+        ref_pos = pos.clone()
+
+        # The same two halves captured as HIP graphs and replayed, as a
+        # serving loop would run them: no host dispatch between the calls.
+        # Stream events around each replay; every replay's positions must
+        # equal the eager chain's.
+        def publish_calls():
+            ah.zero_()
+            pmqa.block_amax8(logits, t["context_lens"], am, ah, block_lens=blens)
+            pmqa.topk_rows(am, ah, blens, kbk, pmqa.KEY_FP32, bsel, ws_b)
+            pmqa.sort_candidate_blocks(bsel, t["context_lens"], x.logits_stride, t["block_table"],
+                                       x.next_n, table, slots, slens)
+
+        def select_calls():
+            pmqa.indexer_sparse_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"], table,
+                                       slots, t["context_lens"], sparse)
+            pmqa.topk_rows(sparse, None, slens, K, pmqa.KEY_FP32, ssel, ws_s)
+            pmqa.sparse_to_logical(ssel, table, pos)
+
+        graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graphs[0], stream=cap):
+                publish_calls()
+            with torch.cuda.graph(graphs[1], stream=cap):
+                select_calls()
+        torch.cuda.synchronize()
+        g_pub, g_sel, g_ok = [], [], True
+        for i in range(args.candidate_steps + 3):
+            e0, e1, e2, e3 = new_events(4)
+            evict()
+            pos.fill_(-7)
+            e0.record(stream)
+            graphs[0].replay()
+            e1.record(stream)
+            e2.record(stream)
+            graphs[1].replay()
+            e3.record(stream)
+            torch.cuda.synchronize()
+            g_ok = g_ok and bool(torch.equal(torch.sort(pos, dim=1).values, torch.sort(ref_pos, dim=1).values))
+            if i >= 3:
+                g_pub.append(e0.elapsed_time(e1) * 1e3)
+                g_sel.append(e2.elapsed_time(e3) * 1e3)
+        del graphs
         sp_bytes = keys_listed * (128 + 4 + 4) + x.rows * kbk * 8 + x.rows * (32 * 128 + 32 * 4 + 4)
         sp_us = float(np.mean(per["indexer_sparse_logits"]))
         cand_out = {"blocks_per_row": kbk, "k": K,
@@ -686,7 +731,12 @@ def main() -> int:
                     "per_call_us_mean": {nm: round(float(np.mean(per[nm])), 3) for nm in names},
                     "sparse_logits_bytes": sp_bytes,
                     "sparse_logits_gbps": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
-                    "note": "publish/select spans include the dispatch gaps between their calls"}
+                    "publish_graph_us_mean": round(float(np.mean(g_pub)), 3),
+                    "select_graph_us_mean": round(float(np.mean(g_sel)), 3),
+                    "graph_replays_match_eager": g_ok,
+                    "note": "publish/select: eager calls, the spans include the host dispatch gaps "
+                            "between them; *_graph: the same calls captured in a HIP graph and "
+                            "replayed, timed by stream events around the replay"}
         del am, ah, bsel, table, slots, slens, sparse, ssel, pos, ws_b, ws_s
 
     # cost of the fused histogram: the logits kernel with and without it,

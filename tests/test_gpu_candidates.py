@@ -186,3 +186,64 @@ def test_candidate_chain(gpu, name, kb_blocks):
     assert np.array_equal(pos.cpu().numpy(), want_pos)
     del d, lg, am, sl
     torch.cuda.empty_cache()
+
+
+def test_candidate_chain_replays_in_a_hip_graph(gpu):
+    """The consumer chain (block maxima with histogram and block counts,
+    block top-k, sort, sparse logits, top-k in the sparse row, map back)
+    captured in one HIP graph: every replay, with eager work and an eager
+    run of the chain on the same workspaces between replays, gives the
+    eager chain's logical positions."""
+    x = gen.make_indexer_inputs("cand_graph", 4, 1, [20000, 9000, 40000, 3000], 77)
+    d = DevInputs(x)
+    kb, k = 512, 2048
+    lg = d.new_logits(float("inf"))
+    d.logits(lg, None)
+    rows = x.rows
+    width = -(-(-(-x.logits_stride // 8)) // 4) * 4
+    am = torch.empty((rows, width), dtype=torch.float32, device=DEV)
+    ah = torch.zeros((rows, 1024), dtype=torch.int32, device=DEV)
+    blens = torch.empty(rows, dtype=torch.int32, device=DEV)
+    bsel = torch.empty((rows, kb), dtype=torch.int32, device=DEV)
+    table, slots = torch.empty_like(bsel), torch.empty_like(bsel)
+    slens = torch.empty(rows, dtype=torch.int32, device=DEV)
+    sparse = torch.empty((rows, kb * 8), dtype=torch.float32, device=DEV)
+    ssel = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    pos = torch.empty_like(ssel)
+    ws_b = torch.full((gpu.topk_workspace_bytes(rows, width, kb),), 0xA5, dtype=torch.uint8, device=DEV)
+    ws_s = torch.full((gpu.topk_workspace_bytes(rows, kb * 8, k),), 0xA5, dtype=torch.uint8, device=DEV)
+
+    def chain():
+        ah.zero_()
+        gpu.block_amax8(lg, d.lens, am, ah, block_lens=blens)
+        gpu.topk_rows(am, ah, blens, kb, O.KEY_FP32, bsel, ws_b)
+        gpu.sort_candidate_blocks(bsel, d.lens, x.logits_stride, d.bt, x.next_n, table, slots, slens)
+        gpu.indexer_sparse_logits(d.q, d.kv, d.sc, d.w, table, slots, d.lens, sparse)
+        gpu.topk_rows(sparse, None, slens, k, O.KEY_FP32, ssel, ws_s)
+        gpu.sparse_to_logical(ssel, table, pos)
+
+    announce("candidate chain: eager reference")
+    chain()
+    torch.cuda.synchronize()
+    ref = np.sort(pos.cpu().numpy(), axis=1)
+    # the final positions are the oracle's top-k of the dense logits over the listed blocks
+    assert np.all(ref[:, -1] < x.logits_stride)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            chain()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        announce(f"candidate chain graph replay {rep}")
+        pos.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(pos.cpu().numpy(), axis=1), ref), f"replay {rep}"
+        _ = (lg * 2).sum().item()  # unrelated eager work between replays
+        pos.fill_(-7)
+        chain()  # the same buffers and workspaces, eager
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(pos.cpu().numpy(), axis=1), ref), f"eager after replay {rep}"
