@@ -103,13 +103,20 @@ def sparse_row_lens(table, lens):
 
 
 def sparse_to_logical(table, cols):
-    """Logical key position of sparse column c of each row: 8 * table[c // 8] + c % 8."""
+    """Logical key position of sparse column c of each row: 8 * table[c // 8] + c % 8.
+
+    Outside that definition (a reading): -1 stays -1, and a column past the
+    row's table (c >= 8 * kb) or on a padding entry (INT32_MAX) has no key
+    and gives -1 as well.
+    """
     table = np.asarray(table, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
+    kb = table.shape[1]
     out = np.full(cols.shape, -1, dtype=np.int64)
-    ok = cols >= 0
+    ok = (cols >= 0) & (cols < BLOCK * kb)
     r = np.nonzero(ok)
-    out[ok] = BLOCK * table[r[0], cols[ok] // BLOCK] + cols[ok] % BLOCK
+    blocks = table[r[0], cols[ok] // BLOCK]
+    out[ok] = np.where(blocks == INT32_MAX, -1, BLOCK * blocks + cols[ok] % BLOCK)
     return out
 
 

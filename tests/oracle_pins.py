@@ -970,6 +970,20 @@ def pin_sparse_logits(O, seed=65):
     return fails
 
 
+def pin_sparse_to_logical_edges(O):
+    """sparse_to_logical written out by hand on a two-block table whose second
+    entry is padding: columns of the first block map to 8 * 3 + c, columns of
+    the padding entry and past the table (c >= 16) and -1 give -1."""
+    big = 2 ** 31 - 1
+    table = np.array([[3, big], [0, 7]], dtype=np.int32)
+    cols = np.array([[0, 7, 8, 15, 16, -1, 23, 5],
+                     [8, 15, 0, 16, 9, -1, 2, 14]], dtype=np.int32)
+    want = [[24, 31, -1, -1, -1, -1, -1, 29],
+            [56, 63, 0, -1, 57, -1, 2, 62]]
+    got = O.candidates.sparse_to_logical(table, cols)
+    return [] if got.tolist() == want else [f"got {got.tolist()} want {want}"]
+
+
 def pin_prefill_decode_case(O):
     """A ragged batch whose requests all have next_n rows is a decode call:
     the prefill oracle equals the decode oracle bit for bit (fill included)."""
@@ -1027,5 +1041,6 @@ ALL_PINS = (pin_e4m3, pin_fp16_rne, pin_logits_f16_check, pin_bins_golden, pin_b
             pin_logits_paging, pin_error_bound, pin_head_sum_exact,
             pin_error_bound_exact, pin_check_logits_classes, pin_logits_terms_match, pin_e2m1, pin_e8m0, pin_mxfp4_layout,
             pin_mxfp4_matches_fp8_path, pin_mxfp4_exact, pin_block_amax8,
-            pin_sort_candidate_blocks, pin_sparse_logits, pin_prefill_decode_case,
+            pin_sort_candidate_blocks, pin_sparse_logits, pin_sparse_to_logical_edges,
+            pin_prefill_decode_case,
             pin_prefill_exact)

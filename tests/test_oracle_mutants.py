@@ -273,6 +273,38 @@ def m_amax8_newest_not_inf(O):
     O.candidates.block_amax8 = amax
 
 
+def m_s2l_padding_mapped(O):
+    # table padding (INT32_MAX) treated as a block id
+    B = O.candidates.BLOCK
+
+    def s2l(table, cols):
+        table = np.asarray(table, np.int64)
+        cols = np.asarray(cols, np.int64)
+        out = np.full(cols.shape, -1, np.int64)
+        ok = (cols >= 0) & (cols < B * table.shape[1])
+        r = np.nonzero(ok)
+        out[ok] = B * table[r[0], cols[ok] // B] + cols[ok] % B
+        return out
+    O.candidates.sparse_to_logical = s2l
+
+
+def m_s2l_past_table_clamped(O):
+    # columns past the table read the last entry instead of giving -1
+    B = O.candidates.BLOCK
+    big = O.candidates.INT32_MAX
+
+    def s2l(table, cols):
+        table = np.asarray(table, np.int64)
+        cols = np.asarray(cols, np.int64)
+        out = np.full(cols.shape, -1, np.int64)
+        ok = cols >= 0
+        r = np.nonzero(ok)
+        blocks = table[r[0], np.minimum(cols[ok] // B, table.shape[1] - 1)]
+        out[ok] = np.where(blocks == big, -1, B * blocks + cols[ok] % B)
+        return out
+    O.candidates.sparse_to_logical = s2l
+
+
 def m_sort_no_identity(O):
     orig = O.candidates.sort_candidate_blocks
     O.candidates.sort_candidate_blocks = lambda b, n, bt, nn: orig(
@@ -433,6 +465,8 @@ MUTANTS = [
     (m_mxfp4_scale_ignored, [P.pin_mxfp4_layout, P.pin_mxfp4_matches_fp8_path]),
     (m_e8m0_bias_128, [P.pin_e8m0, P.pin_mxfp4_exact]),
     (m_amax8_block_count, [P.pin_block_amax8]),
+    (m_s2l_padding_mapped, [P.pin_sparse_to_logical_edges]),
+    (m_s2l_past_table_clamped, [P.pin_sparse_to_logical_edges]),
     (m_amax8_newest_not_inf, [P.pin_block_amax8]),
     (m_sort_no_identity, [P.pin_sort_candidate_blocks]),
     (m_sort_slot_transform, [P.pin_sort_candidate_blocks]),
