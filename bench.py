@@ -644,16 +644,20 @@ def main() -> int:
         sparse = torch.empty((x.rows, kbk * 8), dtype=torch.float32, device=dev)
         ssel = torch.empty((x.rows, K), dtype=torch.int32, device=dev)
         pos = torch.empty_like(ssel)
+        pos2 = torch.empty_like(ssel)
         ws_b = torch.zeros(pmqa.topk_workspace_bytes(x.rows, width, kbk), dtype=torch.uint8, device=dev)
         ws_s = torch.zeros(pmqa.topk_workspace_bytes(x.rows, kbk * 8, K), dtype=torch.uint8, device=dev)
+        # select = sparse logits + sparse_topk (the top-k inside the sparse
+        # row and the map to logical keys in one launch); the unfused pair
+        # (topk_rows + sparse_to_logical) is timed after it for comparison
         names = ("block_amax8", "block_topk", "sort_candidate_blocks", "indexer_sparse_logits",
-                 "sparse_topk", "sparse_to_logical")
+                 "sparse_topk", "sparse_topk_unfused", "sparse_to_logical")
 
         def chain(n_steps, record):
             per = {nm: [] for nm in names}
             pub, sel = [], []
             for i in range(n_steps):
-                ev = new_events(12)
+                ev = new_events(14)
                 evict()
                 ah.zero_()
                 pmqa.block_amax8(logits, t["context_lens"], am, ah, block_lens=blens, events=(ev[0], ev[1]))
@@ -662,8 +666,9 @@ def main() -> int:
                                            x.next_n, table, slots, slens, events=(ev[4], ev[5]))
                 pmqa.indexer_sparse_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"], table,
                                            slots, t["context_lens"], sparse, events=(ev[6], ev[7]))
-                pmqa.topk_rows(sparse, None, slens, K, pmqa.KEY_FP32, ssel, ws_s, events=(ev[8], ev[9]))
-                pmqa.sparse_to_logical(ssel, table, pos, events=(ev[10], ev[11]))
+                pmqa.sparse_topk(sparse, None, slens, K, pmqa.KEY_FP32, table, pos, events=(ev[8], ev[9]))
+                pmqa.topk_rows(sparse, None, slens, K, pmqa.KEY_FP32, ssel, ws_s, events=(ev[10], ev[11]))
+                pmqa.sparse_to_logical(ssel, table, pos2, events=(ev[12], ev[13]))
                 if record:
                     per["_ev"] = per.get("_ev", []) + [ev]
             torch.cuda.synchronize()
@@ -672,57 +677,15 @@ def main() -> int:
                     for j, nm in enumerate(names):
                         per[nm].append(ev[2 * j].elapsed_time(ev[2 * j + 1]) * 1e3)
                     pub.append(ev[0].elapsed_time(ev[5]) * 1e3)
-                    sel.append(ev[6].elapsed_time(ev[11]) * 1e3)
+                    sel.append(ev[6].elapsed_time(ev[9]) * 1e3)
             return per, pub, sel
 
         chain(3, False)
         per, pub, sel = chain(args.candidate_steps, True)
         keys_listed = int(slens.sum().item())
-        ref_pos = pos.clone()
+        fused_matches_unfused = bool(torch.equal(torch.sort(pos, dim=1).values, torch.sort(pos2, dim=1).values))
 
-        # The same two halves captured as HIP graphs and replayed, as a
-        # serving loop would run them: no host dispatch between the calls.
-        # Stream events around each replay; every replay's positions must
-        # equal the eager chain's.
-        def publish_calls():
-            ah.zero_()
-            pmqa.block_amax8(logits, t["context_lens"], am, ah, block_lens=blens)
-            pmqa.topk_rows(am, ah, blens, kbk, pmqa.KEY_FP32, bsel, ws_b)
-            pmqa.sort_candidate_blocks(bsel, t["context_lens"], x.logits_stride, t["block_table"],
-                                       x.next_n, table, slots, slens)
 
-        def select_calls():
-            pmqa.indexer_sparse_logits(t["q"], t["kv_pages"], t["k_scales"], t["weights"], table,
-                                       slots, t["context_lens"], sparse)
-            pmqa.topk_rows(sparse, None, slens, K, pmqa.KEY_FP32, ssel, ws_s)
-            pmqa.sparse_to_logical(ssel, table, pos)
-
-        graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graphs[0], stream=cap):
-                publish_calls()
-            with torch.cuda.graph(graphs[1], stream=cap):
-                select_calls()
-        torch.cuda.synchronize()
-        g_pub, g_sel, g_ok = [], [], True
-        for i in range(args.candidate_steps + 3):
-            e0, e1, e2, e3 = new_events(4)
-            evict()
-            pos.fill_(-7)
-            e0.record(stream)
-            graphs[0].replay()
-            e1.record(stream)
-            e2.record(stream)
-            graphs[1].replay()
-            e3.record(stream)
-            torch.cuda.synchronize()
-            g_ok = g_ok and bool(torch.equal(torch.sort(pos, dim=1).values, torch.sort(ref_pos, dim=1).values))
-            if i >= 3:
-                g_pub.append(e0.elapsed_time(e1) * 1e3)
-                g_sel.append(e2.elapsed_time(e3) * 1e3)
-        del graphs
         sp_bytes = keys_listed * (128 + 4 + 4) + x.rows * kbk * 8 + x.rows * (32 * 128 + 32 * 4 + 4)
         sp_us = float(np.mean(per["indexer_sparse_logits"]))
         cand_out = {"blocks_per_row": kbk, "k": K,
@@ -731,13 +694,10 @@ def main() -> int:
                     "per_call_us_mean": {nm: round(float(np.mean(per[nm])), 3) for nm in names},
                     "sparse_logits_bytes": sp_bytes,
                     "sparse_logits_gbps": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
-                    "publish_graph_us_mean": round(float(np.mean(g_pub)), 3),
-                    "select_graph_us_mean": round(float(np.mean(g_sel)), 3),
-                    "graph_replays_match_eager": g_ok,
-                    "note": "publish/select: eager calls, the spans include the host dispatch gaps "
-                            "between them; *_graph: the same calls captured in a HIP graph and "
-                            "replayed, timed by stream events around the replay"}
-        del am, ah, bsel, table, slots, slens, sparse, ssel, pos, ws_b, ws_s
+                    "fused_matches_unfused": fused_matches_unfused,
+                    "note": "select = indexer_sparse_logits + sparse_topk; the publish and select "
+                            "spans include the gaps between their calls"}
+        del am, ah, bsel, table, slots, slens, sparse, ssel, pos, pos2, ws_b, ws_s
 
     # cost of the fused histogram: the logits kernel with and without it,
     # interleaved (the pages' producer-cost measure: histogram extra)

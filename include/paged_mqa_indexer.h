@@ -393,6 +393,26 @@ idx_status sparse_to_logical(const int32_t* indices, int32_t k, const int32_t* t
                              int32_t kb, int32_t rows, int32_t* out, void* stream);
 
 /*
+ * sparse_topk -- [P2] the top-k inside the sparse rows and the map back to
+ * logical keys in one call: topk_rows over the sparse logits (rows of at most
+ * 16384 scores, lengths sparse_lens, float32, FP32 or FP16 keys, hist
+ * optional as for topk_rows), each selected column c written as
+ * 8 * table[r][c / 8] + c % 8 -- what sparse_to_logical does to topk_rows'
+ * output, without its launch -- and -1 for padding, for columns past the
+ * table and for table padding (INT32_MAX).  No workspace: rows this short
+ * are selected by one workgroup each.
+ *
+ * scores       (device) float [rows][stride], 16-B aligned, stride % 4 == 0,
+ *              stride <= 16384 (else IDX_EUNSUPPORTED)
+ * sparse_lens  (device) int32 [rows]
+ * table        (device) int32 [rows][kb], kb <= 131072 blocks
+ * out          (device) int32 [rows][k], overwritten
+ */
+idx_status sparse_topk(const float* scores, int64_t stride, const int32_t* hist, const int32_t* sparse_lens,
+                       int32_t rows, int32_t k, int32_t key_dtype, const int32_t* table, int32_t kb,
+                       int32_t* out, void* stream);
+
+/*
  * topk_rows_f16 -- topk_rows over binary16 scores ([P3] "Summary": selection
  * on FP16 logits).  The key is the FP16 value itself (scores that are the
  * same half tie, and the lower column wins), the same order as topk_rows

@@ -27,6 +27,7 @@ Entry points (same names as the C ABI):
   indexer_sparse_logits(q, kv_pages, k_scales, weights, table, slots,
                         context_lens, logits)
   sparse_to_logical(indices, table, out)
+  sparse_topk(scores, hist, sparse_lens, k, key_dtype, table, out)
   indexer_status_str(status)
   indexer_time_next_call(start, stop)
   hbm_read_probe(src, sink, events=None)
@@ -50,7 +51,7 @@ __all__ = [
     "EXPORTED_SYMBOLS", "load_library", "library_path", "indexer_logits", "indexer_logits_f16",
     "indexer_logits_mxfp4", "block_amax8", "sort_candidate_blocks", "indexer_sparse_logits",
     "indexer_sparse_logits_mxfp4", "indexer_prefill_logits", "indexer_prefill_logits_mxfp4",
-    "sparse_to_logical",
+    "sparse_to_logical", "sparse_topk",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "topk_rows_noalloc", "score_histogram",
     "indexer_status_str", "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe",
     "mfma_valu_probe",
@@ -67,7 +68,7 @@ MXFP4_TOKEN_BYTES = 68
 
 EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp4", "block_amax8",
                     "sort_candidate_blocks", "indexer_sparse_logits", "indexer_sparse_logits_mxfp4",
-                    "indexer_prefill_logits", "indexer_prefill_logits_mxfp4", "sparse_to_logical",
+                    "indexer_prefill_logits", "indexer_prefill_logits_mxfp4", "sparse_to_logical", "sparse_topk",
                     "topk_workspace_bytes", "topk_rows", "topk_rows_noalloc",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
                     "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe", "mfma_valu_probe")
@@ -134,6 +135,8 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_prefill_logits_mxfp4.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, i64, vp]
     lib.indexer_prefill_logits_mxfp4.restype = ctypes.c_int
     lib.sparse_to_logical.argtypes = [vp, i32, vp, i32, i32, vp, vp]
+    lib.sparse_topk.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, i32, vp, vp]
+    lib.sparse_topk.restype = ctypes.c_int
     lib.sparse_to_logical.restype = ctypes.c_int
     lib.topk_rows_f16.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.topk_rows_f16.restype = ctypes.c_int
@@ -424,6 +427,29 @@ def sparse_to_logical(indices, table, out, events=None):
         st = lib.sparse_to_logical(_ptr(indices), int(k), _ptr(table), int(table.shape[1]), int(rows),
                                    _ptr(out), _stream_ptr(dev))
     _check("sparse_to_logical", st)
+
+
+def sparse_topk(scores, hist, sparse_lens, k, key_dtype, table, out, events=None):
+    """Top-k inside the sparse rows (float32 [rows, stride <= 16384]) written
+    as logical key positions through ``table`` [rows, kb]: topk_rows followed
+    by sparse_to_logical in one launch."""
+    dev = scores.device
+    _need(scores, "scores", torch.float32, dev, 2)
+    rows = scores.shape[0]
+    _need(sparse_lens, "sparse_lens", torch.int32, dev, 1)
+    _rows2(table, "table", torch.int32, dev, rows)
+    _rows2(out, "out", torch.int32, dev, rows)
+    if scores.stride(1) != 1 or tuple(sparse_lens.shape) != (rows,) or out.shape[1] != k:
+        raise ValueError("scores must have unit column stride; sparse_lens [rows]; out [rows, k]")
+    if hist is not None:
+        _rows2(hist, "hist", torch.int32, dev, rows)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _arm(events, dev)
+        st = lib.sparse_topk(_ptr(scores), int(scores.stride(0)), _ptr(hist), _ptr(sparse_lens), int(rows),
+                             int(k), int(key_dtype), _ptr(table), int(table.shape[1]), _ptr(out),
+                             _stream_ptr(dev))
+    _check("sparse_topk", st)
 
 
 def topk_workspace_bytes(rows: int, logits_stride: int, k: int) -> int:

@@ -313,6 +313,31 @@ idx_status sparse_to_logical(const int32_t* indices, int32_t k, const int32_t* t
                                                  static_cast<hipStream_t>(stream), ev));
 }
 
+idx_status sparse_topk(const float* scores, int64_t stride, const int32_t* hist, const int32_t* sparse_lens,
+                       int32_t rows, int32_t k, int32_t key_dtype, const int32_t* table, int32_t kb,
+                       int32_t* out, void* stream) {
+  const pmqa::LaunchEvents ev = take_events();
+  if (!scores || !sparse_lens || !table || !out) return IDX_EINVAL;
+  if (rows <= 0 || stride <= 0 || kb <= 0 || k < 1 || k > IDX_CANDIDATE_CAPACITY) return IDX_EINVAL;
+  if (key_dtype != IDX_KEY_FP32 && key_dtype != IDX_KEY_FP16) return IDX_EUNSUPPORTED;
+  if (rows > IDX_MAX_ROWS || stride > 16384 || kb > pmqa::kMaxCandidateBlocks) return IDX_EUNSUPPORTED;
+  if (!aligned(scores, 16) || (stride % 4) != 0 || !aligned(sparse_lens, 4) || !aligned(table, 4) ||
+      !aligned(out, 4) || (hist && !aligned(hist, 8)))
+    return IDX_EALIGN;
+  pmqa::TopkArgs a;
+  a.logits = scores;
+  a.hist = hist;
+  a.context_lens = sparse_lens;
+  a.indices = out;
+  a.workspace = nullptr;
+  a.logits_stride = stride;
+  a.rows = rows;
+  a.k = k;
+  a.key_dtype = key_dtype;
+  a.logits_f16 = 0;
+  return from_hip(pmqa::launch_sparse_topk(a, table, kb, static_cast<hipStream_t>(stream), ev));
+}
+
 idx_status hbm_gather_probe(const uint8_t* kv_pages, const float* k_scales, const int32_t* page_list,
                             int32_t n_pages, int32_t num_pages, uint32_t* sink, void* stream) {
   const pmqa::LaunchEvents ev = take_events();

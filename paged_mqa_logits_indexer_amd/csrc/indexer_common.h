@@ -248,6 +248,10 @@ struct TopkArgs {
 };
 size_t topk_workspace_size(int32_t rows, int64_t logits_stride, int32_t k);
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev = {});
+// topk_rows over sparse rows (stride <= 16384, float32) writing logical keys
+// through the rows' block tables [rows][kb].
+hipError_t launch_sparse_topk(const TopkArgs& a, const int32_t* table, int kb, hipStream_t stream,
+                              LaunchEvents ev = {});
 // topk_rows with the library's fixed per-device scratch (no workspace).
 size_t topk_noalloc_scratch_bytes();
 hipError_t launch_topk_rows_noalloc(const TopkArgs& a, hipStream_t stream, LaunchEvents ev = {});

@@ -66,6 +66,7 @@ constexpr int kChunk = kThreads * kPerThread;  // 4096 scores per collect workgr
 constexpr int kRefineThreads = 512;         // row and finish workgroups
 constexpr int kRowSpan = kRefineThreads * kPerThread;  // 8192: rows topk_row takes whole
 constexpr int kAllBins = kBins;             // threshold meaning "every live score"
+constexpr int kSparseBlock = 8;             // keys per block of the two-level candidate indexer
 static_assert(kBins == 4 * kThreads, "collect: four bins per thread");
 static_assert(kBins == 2 * kRefineThreads, "row and finish: two bins per thread");
 // Candidates of the threshold bin the selector refines in LDS: twice the
@@ -1035,12 +1036,17 @@ __device__ __forceinline__ void finish_candidates(RefineShared& sh, int32_t* __r
 // per-thread counts (part 0's places before part 1's) keep both lists in
 // column order.  OWN_HIST: no histogram was given; the workgroup bins its row
 // in LDS first.
-template <int KEY, bool F16, bool OWN_HIST, int M>
+// MAP (the sparse rows of the two-level candidate indexer): once the row's
+// selection is written, each column c becomes the logical key
+// 8 * table[row][c / 8] + c % 8 (-1 for padding, for columns past the table
+// and for table padding), in place.
+template <int KEY, bool F16, bool OWN_HIST, int M, bool MAP = false>
 __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __restrict__ logits,
                                                                   int64_t stride,
                                                                   const int32_t* __restrict__ hist,
                                                                   const int32_t* __restrict__ lens, int k,
-                                                                  int32_t* __restrict__ indices) {
+                                                                  int32_t* __restrict__ indices,
+                                                                  const int32_t* __restrict__ table, int kb) {
   __shared__ RefineShared sh;
   __shared__ int s_hist[OWN_HIST ? kBins : 1];
   const int row = blockIdx.x;
@@ -1109,29 +1115,45 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
   }
   if (!counts_confirm(bstar, n_gt, n_eq, k)) {
     whole_row_select<KEY, F16>(sh, x, len, k, out);
-    return;
-  }
-  // When every candidate is taken (none exist below the all-bins threshold)
-  // their columns go straight to the output.
-  const bool direct = bstar == kAllBins || k - n_gt == n_eq;
+  } else {
+    // When every candidate is taken (none exist below the all-bins
+    // threshold) their columns go straight to the output.
+    const bool direct = bstar == kAllBins || k - n_gt == n_eq;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
+    for (int m = 0; m < M; ++m) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      if ((gmask[m] >> i) & 1u) out[og[m]++] = s0[m] + i;  // og < n_gt <= k
-      if ((emask[m] >> i) & 1u) {
-        if (direct) out[n_gt + oe[m]] = s0[m] + i;
-        else sh.cand[oe[m]] = uint2{sc[m].template key<KEY>(i), static_cast<uint32_t>(s0[m] + i)};
-        ++oe[m];
+      for (int i = 0; i < kPerThread; ++i) {
+        if ((gmask[m] >> i) & 1u) out[og[m]++] = s0[m] + i;  // og < n_gt <= k
+        if ((emask[m] >> i) & 1u) {
+          if (direct) out[n_gt + oe[m]] = s0[m] + i;
+          else sh.cand[oe[m]] = uint2{sc[m].template key<KEY>(i), static_cast<uint32_t>(s0[m] + i)};
+          ++oe[m];
+        }
       }
     }
+    if (direct) {
+      for (int i = n_gt + n_eq + tid; i < k; i += kRefineThreads) out[i] = -1;
+    } else {
+      lds_barrier();
+      finish_candidates(sh, out, k, n_gt, n_eq, n_gt, true);
+    }
   }
-  if (direct) {
-    for (int i = n_gt + n_eq + tid; i < k; i += kRefineThreads) out[i] = -1;
-    return;
+  if constexpr (MAP) {
+    // Every entry of the row is written by now (the barrier waits for the
+    // workgroup's stores); they are read back from L2 (agent-scope loads
+    // skip this CU's vector cache) and mapped in place.
+    __syncthreads();
+    const int32_t* trow = table + static_cast<int64_t>(row) * kb;
+    for (int i = tid; i < k; i += kRefineThreads) {
+      const int c = __hip_atomic_load(out + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int v = -1;
+      if (c >= 0 && c < kb * kSparseBlock) {
+        const int b = trow[c / kSparseBlock];
+        v = b == INT32_MAX ? -1 : b * kSparseBlock + (c % kSparseBlock);
+      }
+      out[i] = v;
+    }
   }
-  lds_barrier();
-  finish_candidates(sh, out, k, n_gt, n_eq, n_gt, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -1361,18 +1383,40 @@ void launch_rows_whole(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {
   if (a.logits_stride > kRowSpan) {  // rows of up to 2 * kRowSpan: two parts per thread
     if (a.hist)
       launch_kernel(topk_row_kernel<KEY, F16, false, 2>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start,
-                    ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+                    ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, nullptr, 0);
     else
       launch_kernel(topk_row_kernel<KEY, F16, true, 2>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start,
-                    ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+                    ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, nullptr, 0);
     return;
   }
   if (a.hist)
     launch_kernel(topk_row_kernel<KEY, F16, false, 1>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
-                  a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+                  a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, nullptr, 0);
   else
     launch_kernel(topk_row_kernel<KEY, F16, true, 1>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start, ev.stop,
-                  a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices);
+                  a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, nullptr, 0);
+}
+
+// Top-k inside the sparse rows (at most 16384 scores each) with the columns
+// mapped to logical keys through the rows' block tables.
+template <int KEY>
+void launch_sparse_topk_rows(const TopkArgs& a, const int32_t* table, int kb, hipStream_t stream,
+                             LaunchEvents ev) {
+  if (a.logits_stride > kRowSpan) {
+    if (a.hist)
+      launch_kernel(topk_row_kernel<KEY, false, false, 2, true>, dim3(a.rows), dim3(kRefineThreads), stream,
+                    ev.start, ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, table, kb);
+    else
+      launch_kernel(topk_row_kernel<KEY, false, true, 2, true>, dim3(a.rows), dim3(kRefineThreads), stream,
+                    ev.start, ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, table, kb);
+    return;
+  }
+  if (a.hist)
+    launch_kernel(topk_row_kernel<KEY, false, false, 1, true>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start,
+                  ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, table, kb);
+  else
+    launch_kernel(topk_row_kernel<KEY, false, true, 1, true>, dim3(a.rows), dim3(kRefineThreads), stream, ev.start,
+                  ev.stop, a.logits, a.logits_stride, a.hist, a.context_lens, a.k, a.indices, table, kb);
 }
 
 // Chunks per collect workgroup: two for rows of more than 64 chunks, which
@@ -1403,6 +1447,14 @@ void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist,
   launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, a.logits,
                 a.logits_stride, hist, hist_stride, own_hist ? 1 : 0, a.context_lens, a.k, a.indices, ws,
                 m * kChunk);
+}
+
+hipError_t launch_sparse_topk(const TopkArgs& a, const int32_t* table, int kb, hipStream_t stream,
+                              LaunchEvents ev) {
+  if (a.logits_stride > kRowSpanMax || a.logits_f16) return hipErrorInvalidValue;  // checked by the ABI first
+  if (a.key_dtype == IDX_KEY_FP32) launch_sparse_topk_rows<IDX_KEY_FP32>(a, table, kb, stream, ev);
+  else launch_sparse_topk_rows<IDX_KEY_FP16>(a, table, kb, stream, ev);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t stream, LaunchEvents ev) {

@@ -319,3 +319,24 @@ def test_coissue_probe_rejects_before_any_device_query(lib, kw):
     args.update(kw)
     assert lib.mfma_valu_probe(args["mode"], args["waves"], args["iters"], args["out"], args["out_len"],
                                None) == IDX_EINVAL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(scores=None), IDX_EINVAL),
+    (dict(table=None), IDX_EINVAL),
+    (dict(out=None), IDX_EINVAL),
+    (dict(k=0), IDX_EINVAL),
+    (dict(k=8193), IDX_EINVAL),
+    (dict(kb=0), IDX_EINVAL),
+    (dict(key=7), IDX_EUNSUPPORTED),
+    (dict(stride=16388), IDX_EUNSUPPORTED),
+    (dict(kb=(1 << 17) + 1), IDX_EUNSUPPORTED),
+    (dict(scores=A + 8), IDX_EALIGN),
+    (dict(stride=4098), IDX_EALIGN),
+    (dict(hist=A + 4), IDX_EALIGN),
+])
+def test_sparse_topk_rejects(lib, kw, status):
+    args = dict(scores=A, stride=4096, hist=None, lens=A, rows=4, k=2048, key=0, table=A, kb=512, out=A)
+    args.update(kw)
+    assert lib.sparse_topk(args["scores"], args["stride"], args["hist"], args["lens"], args["rows"], args["k"],
+                           args["key"], args["table"], args["kb"], args["out"], None) == status

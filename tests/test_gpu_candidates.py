@@ -184,6 +184,11 @@ def test_candidate_chain(gpu, name, kb_blocks):
     torch.cuda.synchronize()
     want_pos = C.sparse_to_logical(tab, sel.cpu().numpy())
     assert np.array_equal(pos.cpu().numpy(), want_pos)
+    announce(f"{name}: sparse_topk (top-k and map in one launch)")
+    fused = torch.full_like(sel, -9)
+    gpu.sparse_topk(sl, None, slens, 2048, O.KEY_FP32, table, fused)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.sort(fused.cpu().numpy(), axis=1), np.sort(want_pos, axis=1))
     del d, lg, am, sl
     torch.cuda.empty_cache()
 
@@ -247,3 +252,35 @@ def test_candidate_chain_replays_in_a_hip_graph(gpu):
         chain()  # the same buffers and workspaces, eager
         torch.cuda.synchronize()
         assert np.array_equal(np.sort(pos.cpu().numpy(), axis=1), ref), f"eager after replay {rep}"
+
+
+
+@pytest.mark.parametrize("key", [O.KEY_FP32, O.KEY_FP16])
+@pytest.mark.parametrize("k", [1, 100, 2048, 8192])
+def test_sparse_topk_edges(gpu, key, k):
+    """sparse_topk against the oracle's top-k mapped through the table
+    (sparse_to_logical's definition): rows of one and two 8192-column parts,
+    lengths 0, 1 and below k, live columns past the table (kb * 8 < len),
+    table padding (INT32_MAX), ties, with the histogram given and without."""
+    rng = np.random.default_rng(3030 + k)
+    for stride in (4096, 12000):
+        rows = 6
+        kb = stride // 8 - 3  # the last 24 columns lie past every table
+        sc = (np.round(rng.standard_normal((rows, stride)) * 3)).astype(np.float32)
+        lens = np.array([stride, 0, 1, min(stride, k // 2 + 5), stride - 7, stride // 3], np.int32)
+        table = np.sort(rng.choice(1 << 16, size=(rows, kb), replace=True), axis=1).astype(np.int32)
+        table[4, kb // 2:] = np.iinfo(np.int32).max  # padded second half
+        s_ = torch.from_numpy(sc).to(DEV)
+        ln = torch.from_numpy(lens).to(DEV)
+        tb = torch.from_numpy(table).to(DEV)
+        h = torch.zeros((rows, 1024), dtype=torch.int32, device=DEV)
+        gpu.score_histogram(s_, ln, h)
+        want = C.sparse_to_logical(table, O.topk_rows(sc, lens, k, key))
+        for hist in (h, None):
+            announce(f"sparse_topk stride={stride} k={k} key={key} hist={'given' if hist is not None else 'NULL'}")
+            out = torch.full((rows, k), -9, dtype=torch.int32, device=DEV)
+            gpu.sparse_topk(s_, hist, ln, k, key, tb, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            for r in range(rows):
+                assert np.array_equal(np.sort(got[r]), np.sort(want[r])), f"stride {stride} row {r}"
