@@ -1,6 +1,7 @@
 // C ABI of the paged MQA indexer: host-side argument checks, then launches.
 // Every check runs before anything is enqueued; see paged_mqa_indexer.h.
 #include "indexer_common.h"
+#include "launches.h"
 
 namespace {
 

@@ -13,6 +13,7 @@
 #include <climits>
 
 #include "indexer_common.h"
+#include "launches.h"
 
 namespace pmqa {
 namespace {

@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "indexer_common.h"
+#include "launches.h"
 
 namespace pmqa {
 namespace {

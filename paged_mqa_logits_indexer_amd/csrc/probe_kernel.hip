@@ -1,6 +1,7 @@
 // Read probes: the practical HBM read ceilings the logits kernel is measured
 // against.  Measurement aids, not part of the method.
 #include "indexer_common.h"
+#include "launches.h"
 
 namespace pmqa {
 namespace {

@@ -55,6 +55,7 @@
 
 #include "bin_key_range.h"
 #include "indexer_common.h"
+#include "launches.h"
 
 namespace pmqa {
 namespace {
