@@ -1297,6 +1297,72 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
     for (int i = gf + n_eq + tid; i < k - gb; i += kRefineThreads) out[i] = -1;
     return;
   }
+  if (n_eq > kCutMin) {  // uniform
+    // A large bin: cut once more by its sub-bins.  Candidate i of the list
+    // (front entries [0, ef), then back entries) is taken by thread i % 512,
+    // all of a thread's (at most 32) requested at once: one round trip for up
+    // to 16384 candidates; indices past n_eq reread the last one, in bounds,
+    // and are masked off.  They stay in registers: only the candidates that go
+    // on are written to LDS.
+    constexpr int kMaxPer = kCandBuf / kRefineThreads;
+    static_assert(kMaxPer <= 32, "masks hold one bit per candidate");
+    uint2 c[kMaxPer];
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int i = min(j * kRefineThreads + tid, n_eq - 1);
+      c[j] = make_uint2(0u, 0u);
+      if (j * kRefineThreads < n_eq) c[j] = cand[i < ef ? i : kCandBuf - 1 - (i - ef)];  // uniform
+    }
+    // The sub-bin s* where the running count (largest sub-bins first)
+    // reaches need; the candidates of higher sub-bins are taken, those of s*
+    // refined.
+    if (tid == 0) sh.bcast[0] = -1;
+    if (tid < kSubBins) sh.digit_hist[tid] = sub;
+    lds_barrier();
+    const int need = k - n_gt;
+    int sub_above = 0, sub_in = 0;
+    const int sstar = pick_digit(sh, need, &sub_above, &sub_in);
+    uint32_t m_live = 0u, m_above = 0u, m_in = 0u;
+    const SubDigit sd(bstar);
+    const uint32_t sstar_u = static_cast<uint32_t>(sstar);
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const bool live = j * kRefineThreads + tid < n_eq;
+      const uint32_t d = sd.of(key16_of<F16 ? IDX_KEY_FP16 : KEY>(c[j].x));
+      m_live |= (live ? 1u : 0u) << j;
+      m_above |= (live && d > sstar_u ? 1u : 0u) << j;
+      m_in |= (live && d == sstar_u ? 1u : 0u) << j;
+    }
+    int2 tot2;
+    const int2 off = block_excl_scan2<kRefineThreads>(__popc(m_above), __popc(m_in), sh.red, &tot2);
+    // The cut holds when the counts found confirm it: fewer than need above
+    // s*, at least need with it (the sub-histogram is accumulated by atomics
+    // on the workspace; a workspace that did not start zeroed shows here).
+    // Otherwise, or when no sub-bin was found, the whole bin is refined.
+    if (sstar >= 0 && tot2.x == sub_above && tot2.x < need && tot2.x + tot2.y >= need) {
+      // A wave writes its entries at consecutive places from its first
+      // lane's offset (the sum over the waves before it), candidate j of
+      // every lane together, so that each store is contiguous.
+      int pa = gf + __builtin_amdgcn_readfirstlane(off.x), pt = __builtin_amdgcn_readfirstlane(off.y);
+#pragma unroll
+      for (int j = 0; j < kMaxPer; ++j) {
+        const bool a = (m_above >> j) & 1u, t = (m_in >> j) & 1u;
+        const uint64_t ba = __ballot(a), bt = __ballot(t);
+        if (a) out[pa + lanes_below(ba)] = static_cast<int32_t>(c[j].y);
+        if (t) sh.cand[pt + lanes_below(bt)] = c[j];
+        pa += __popcll(ba);
+        pt += __popcll(bt);
+      }
+      lds_barrier();
+      finish_candidates(sh, out, k, n_gt + tot2.x, tot2.y, gf + tot2.x, false);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j)
+      if ((m_live >> j) & 1u) sh.cand[j * kRefineThreads + tid] = c[j];
+    finish_candidates(sh, out, k, n_gt, n_eq, gf, false);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kEarlyCand; ++j) {
     const int i = j * kRefineThreads + tid;
@@ -1304,71 +1370,6 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void*
     if (i < eb) sh.cand[ef + i] = early_b[j];
   }
   copy_rest(cand, ef, eb, [&](int i, uint2 c) { sh.cand[i] = c; });
-  // Second cut: the sub-bin s* of the threshold bin where the running count
-  // (largest sub-bins first) reaches need; the candidates of higher sub-bins
-  // are taken, those of s* refined.
-  if (n_eq > kCutMin) {  // uniform
-    if (tid == 0) sh.bcast[0] = -1;
-    if (tid < kSubBins) sh.digit_hist[tid] = sub;
-    lds_barrier();
-    const int need = k - n_gt;
-    int sub_above = 0, sub_in = 0;
-    const int sstar = pick_digit(sh, need, &sub_above, &sub_in);
-    if (sstar >= 0 && sub_in < n_eq) {
-      // Thread t takes candidates t, t + 512, ... (at most 32 of 16384; a
-      // wave's reads are conflict-free), counts those above s* and in it, and
-      // after one block scan writes the former to the output and the latter to
-      // the front of the LDS list (every read precedes the scan's barriers).
-      // Groups of 8 are read together, and only groups that hold candidates
-      // (a uniform test); reads past n_eq stay inside the LDS list and are
-      // masked off.
-      const SubDigit sd(bstar);
-      constexpr int kGroup = 8;
-      constexpr int kMaxPer = kCandBuf / kRefineThreads;
-      static_assert(kMaxPer % kGroup == 0 && kMaxPer <= 32, "masks hold one bit per candidate");
-      const uint32_t sstar_u = static_cast<uint32_t>(sstar);
-      uint2 c[kMaxPer];
-      uint32_t m_above = 0u, m_in = 0u;
-#pragma unroll
-      for (int g = 0; g < kMaxPer / kGroup; ++g) {
-        if (g * kGroup * kRefineThreads < n_eq) {
-#pragma unroll
-          for (int u = 0; u < kGroup; ++u) c[g * kGroup + u] = sh.cand[(g * kGroup + u) * kRefineThreads + tid];
-#pragma unroll
-          for (int u = 0; u < kGroup; ++u) {
-            const int j = g * kGroup + u;
-            const bool live = j * kRefineThreads + tid < n_eq;
-            const uint32_t d = sd.of(key16_of<F16 ? IDX_KEY_FP16 : KEY>(c[j].x));
-            m_above |= (live && d > sstar_u ? 1u : 0u) << j;
-            m_in |= (live && d == sstar_u ? 1u : 0u) << j;
-          }
-        }
-      }
-      int2 tot2;
-      const int2 off = block_excl_scan2<kRefineThreads>(__popc(m_above), __popc(m_in), sh.red, &tot2);
-      // The cut holds when the counts found confirm it: fewer than need above
-      // s*, at least need with it.  (The sub-histogram is accumulated by
-      // atomics on the workspace; a workspace that did not start zeroed shows
-      // here and the whole bin is refined.)
-      if (tot2.x == sub_above && tot2.x < need && tot2.x + tot2.y >= need) {
-        int pa = gf + off.x, pt = off.y;
-#pragma unroll
-        for (int g = 0; g < kMaxPer / kGroup; ++g) {
-          if (g * kGroup * kRefineThreads < n_eq) {
-#pragma unroll
-            for (int u = 0; u < kGroup; ++u) {
-              const int j = g * kGroup + u;
-              if ((m_above >> j) & 1u) out[pa++] = static_cast<int32_t>(c[j].y);
-              if ((m_in >> j) & 1u) sh.cand[pt++] = c[j];
-            }
-          }
-        }
-        lds_barrier();
-        finish_candidates(sh, out, k, n_gt + tot2.x, tot2.y, gf + tot2.x, false);
-        return;
-      }
-    }
-  }
   finish_candidates(sh, out, k, n_gt, n_eq, gf, false);
 }
 
