@@ -29,6 +29,9 @@ COMPILE_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results straight into VGPRs (no accumulator-register reads).
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # Leading kernel arguments arrive in scalar registers (no load of the
+    # argument block before the first dependent load).
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

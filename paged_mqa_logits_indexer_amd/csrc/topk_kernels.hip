@@ -1217,13 +1217,16 @@ __device__ __forceinline__ i32x4 block_sum4(i32x4 v, int* s_red4) {
 }
 
 template <int KEY, bool F16>
-__global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(const void* __restrict__ logits,
-                                                                     int64_t stride,
-                                                                     const int32_t* __restrict__ hist,
-                                                                     int64_t hist_stride, int own_hist,
-                                                                     const int32_t* __restrict__ lens, int k,
+// The arguments the first loads need come first (the leading ones are placed
+// in scalar registers before the kernel starts).
+__global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __restrict__ ws_base,
+                                                                     const int32_t* __restrict__ lens,
+                                                                     int collect_span, int k, int64_t stride,
                                                                      int32_t* __restrict__ indices,
-                                                                     Workspace ws, int collect_span) {
+                                                                     const void* __restrict__ logits,
+                                                                     const int32_t* __restrict__ hist,
+                                                                     int64_t hist_stride, int own_hist) {
+  const Workspace ws{ws_base};
   __shared__ RefineShared sh;
   __shared__ int s_red4[4 * (kRefineThreads / kWave)];
   const int row = blockIdx.x;
@@ -1446,9 +1449,9 @@ void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist,
   const int m = chunks_per_collect(chunks);
   if (m == 2) launch_collect<KEY, F16, 2>(a, ws, hist, hist_stride, chunks, stream, start);
   else launch_collect<KEY, F16, 1>(a, ws, hist, hist_stride, chunks, stream, start);
-  launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, a.logits,
-                a.logits_stride, hist, hist_stride, own_hist ? 1 : 0, a.context_lens, a.k, a.indices, ws,
-                m * kChunk);
+  launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, ws.base,
+                a.context_lens, m * kChunk, a.k, a.logits_stride, a.indices, a.logits, hist, hist_stride,
+                own_hist ? 1 : 0);
 }
 
 hipError_t launch_sparse_topk(const TopkArgs& a, const int32_t* table, int kb, hipStream_t stream,
