@@ -64,6 +64,8 @@ constexpr int kThreads = 256;               // histogram and collect workgroups
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPerThread = 16;              // consecutive scores per thread
 constexpr int kChunk = kThreads * kPerThread;  // 4096 scores per collect workgroup
+constexpr int kChunkShift = 12;
+static_assert(kChunk == 1 << kChunkShift, "chunks are 2^kChunkShift scores");
 constexpr int kRefineThreads = 512;         // row and finish workgroups
 constexpr int kRowSpan = kRefineThreads * kPerThread;  // 8192: rows topk_row takes whole
 constexpr int kAllBins = kBins;             // threshold meaning "every live score"
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
 template <int KEY, bool F16, int M>
 __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __restrict__ logits,
                                                                 int64_t stride,
-                                                                const int32_t* __restrict__ hist,
+                                                                const int32_t* hist,  // (see below)
                                                                 int64_t hist_stride,
                                                                 const int32_t* __restrict__ lens, int k,
                                                                 int32_t* __restrict__ indices, Workspace ws) {
@@ -458,14 +460,20 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
   __shared__ int s_sub[kSubBins];
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
+  // The histogram is requested before the row's length arrives (a
+  // workgroup past the row's end reads 4 KiB for nothing), so that the
+  // threshold scan overlaps the round trip of the scores, which wait for
+  // the length.  The compiler barrier keeps the loads here: through a
+  // __restrict__ pointer they would count as invariant and be sunk past the
+  // exit test.
+  const int* h = hist + row * hist_stride + tid * 4;
+  const int2 h01 = *reinterpret_cast<const int2*>(h);  // 8-B aligned
+  const int2 h23 = *reinterpret_cast<const int2*>(h + 2);
+  __asm__ volatile("" ::: "memory");
   const int len = clamp_len(lens, row, stride);
   const int64_t first = static_cast<int64_t>(blockIdx.x) * M * kChunk;  // first column of the workgroup
   if (first >= len) return;
 
-  // The histogram and the chunks' scores are requested together.
-  const int* h = hist + row * hist_stride + tid * 4;
-  const int2 h01 = *reinterpret_cast<const int2*>(h);  // 8-B aligned
-  const int2 h23 = *reinterpret_cast<const int2*>(h + 2);
   const char* x = static_cast<const char*>(score_row<F16>(logits, row, stride));
   int s0[M], live[M];  // live[m]: columns of chunk m below this length count
   ThreadScores<F16> sc[M];
@@ -1221,7 +1229,7 @@ template <int KEY, bool F16>
 // in scalar registers before the kernel starts).
 __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __restrict__ ws_base,
                                                                      const int32_t* __restrict__ lens,
-                                                                     int collect_span, int k, int64_t stride,
+                                                                     int collect_shift, int k, int64_t stride,
                                                                      int32_t* __restrict__ indices,
                                                                      const void* __restrict__ logits,
                                                                      const int32_t* __restrict__ hist,
@@ -1231,14 +1239,11 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __res
   __shared__ int s_red4[4 * (kRefineThreads / kWave)];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int len = clamp_len(lens, row, stride);
-  const void* x = score_row<F16>(logits, row, stride);
-  int32_t* out = indices + static_cast<int64_t>(row) * k;
   const uint2* cand = ws.cand(row);
   unsigned long long* count = ws.count(row);
-  // Collect workgroups that took part: those whose first column is below len.
-  const int n_wg = static_cast<int>((static_cast<int64_t>(len) + collect_span - 1) / collect_span);
-
+  // What the collect pass left is requested first (none of it depends on the
+  // row's length); the compiler barrier after these loads keeps them ahead
+  // of the length's round trip.
   const unsigned long long front = count[0], back = count[1];
   // b* as the collect pass found it (the same for all of its workgroups).  A
   // row with no live score ran no collect workgroup and may read a stale
@@ -1255,6 +1260,13 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __res
     early_f[j] = cand[j * kRefineThreads + tid];
     early_b[j] = cand[kCandBuf - 1 - (j * kRefineThreads + tid)];
   }
+  __asm__ volatile("" ::: "memory");
+  const int len = clamp_len(lens, row, stride);
+  const void* x = score_row<F16>(logits, row, stride);
+  int32_t* out = indices + static_cast<int64_t>(row) * k;
+  // Collect workgroups that took part: those whose first column is below len
+  // (each took 2^collect_shift columns).
+  const int n_wg = static_cast<int>((static_cast<uint32_t>(len) + (1u << collect_shift) - 1u) >> collect_shift);
   // This call's true counts: the sums of the slots of the workgroups that
   // ran, even ones (front pair) and odd ones (back pair) apart.
   i32x4 mine{0, 0, 0, 0};
@@ -1450,7 +1462,8 @@ void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist,
   if (m == 2) launch_collect<KEY, F16, 2>(a, ws, hist, hist_stride, chunks, stream, start);
   else launch_collect<KEY, F16, 1>(a, ws, hist, hist_stride, chunks, stream, start);
   launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, ws.base,
-                a.context_lens, m * kChunk, a.k, a.logits_stride, a.indices, a.logits, hist, hist_stride,
+                a.context_lens, m == 2 ? kChunkShift + 1 : kChunkShift, a.k, a.logits_stride, a.indices, a.logits,
+                hist, hist_stride,
                 own_hist ? 1 : 0);
 }
 
