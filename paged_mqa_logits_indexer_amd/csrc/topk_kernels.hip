@@ -1166,11 +1166,140 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
 }
 
 // ---------------------------------------------------------------------------
+// A threshold bin whose candidates all came with the early loads (at most
+// 1024 from each end) is finished from registers: thread t holds front
+// entries t and t + 512 and back entries t and t + 512.  The radix passes
+// count into histograms of their own (zeroed once, up front), and after each
+// pass's barrier every wave reads the counts and finds the digit itself, so
+// a pass costs one barrier; the LDS candidate list is not used.
+constexpr int kEarlyCand = 2;  // candidates per thread and end loaded with the counts
+constexpr int kRegCand = 2 * kEarlyCand;
+constexpr int kRegPasses = 4;  // 8-bit digits of a 32-bit value
+
+// Radix select over the values v[i] (bit i of `valid`) of every thread of
+// the block, `total` of them: the need-th largest value, *above = how many
+// exceed it, *at = how many equal it.  hists: kRegPasses zeroed 256-bin
+// histograms; o and a: the OR and AND of every valid value (block-wide).
+// Block-uniform control flow: every wave finds the same digits.
+__device__ __forceinline__ uint32_t select_regs(const uint32_t (&v)[kRegCand], uint32_t valid, uint32_t o,
+                                                uint32_t a, int total, int need, int (*hists)[256], int* above,
+                                                int* at) {
+  const int lane = __lane_id();
+  const uint32_t diff = o ^ a;
+  uint32_t prefix = a & ~diff, fixed = ~diff;
+  int gt = 0, eq = total;  // (every value the same when diff is 0)
+  int shift = max(top_bit(diff | 1u) - 7, 0);
+  for (int p = 0; diff != 0u && p < kRegPasses; ++p) {
+    int* h = hists[p];
+#pragma unroll
+    for (int i = 0; i < kRegCand; ++i)
+      if (((valid >> i) & 1u) && ((v[i] ^ prefix) & fixed) == 0u) atomicAdd(&h[(v[i] >> shift) & 0xFFu], 1);
+    lds_barrier();
+    // Lane l reads digits 255 - 4l down to 252 - 4l; every wave finds the same digit.
+    const int4 q = reinterpret_cast<const int4*>(h)[kWave - 1 - lane];
+    const int c[4] = {q.w, q.z, q.y, q.x};
+    const int sum = c[0] + c[1] + c[2] + c[3];
+    int run = wave_inclusive_scan(sum) - sum;
+    int hit = -1, hit_before = 0, hit_in = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (run < need && run + c[i] >= need) {
+        hit = 255 - 4 * lane - i;
+        hit_before = run;
+        hit_in = c[i];
+      }
+      run += c[i];
+    }
+    const int src = first_lane(__ballot(hit >= 0));
+    const int d = __builtin_amdgcn_readlane(hit, src) & 0xFF;
+    const int before = __builtin_amdgcn_readlane(hit_before, src);
+    eq = __builtin_amdgcn_readlane(hit_in, src);
+    need -= before;
+    gt += before;
+    prefix |= static_cast<uint32_t>(d) << shift;
+    fixed |= 0xFFu << shift;
+    if (shift == 0) break;
+    shift = max(shift - 8, 0);
+  }
+  *above = gt;
+  *at = eq;
+  return prefix;
+}
+
+// The block-wide OR and AND of the values v[i] with bit i of `valid`, through
+// slots [0, 16) of s_red (one barrier).
+__device__ __forceinline__ void or_and_regs(const uint32_t (&v)[kRegCand], uint32_t valid, int* s_red, uint32_t* o,
+                                            uint32_t* a) {
+  uint32_t x = 0u, y = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < kRegCand; ++i) {
+    if ((valid >> i) & 1u) {
+      x |= v[i];
+      y &= v[i];
+    }
+  }
+  x = wave_or(x);
+  y = wave_and(y);
+  const int wave = threadIdx.x / kWave;
+  if (__lane_id() == 0) {
+    s_red[wave] = static_cast<int>(x);
+    s_red[8 + wave] = static_cast<int>(y);
+  }
+  lds_barrier();
+  x = 0u;
+  y = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kRefineThreads / kWave; ++w) {
+    x |= static_cast<uint32_t>(s_red[w]);
+    y &= static_cast<uint32_t>(s_red[8 + w]);
+  }
+  *o = x;
+  *a = y;
+}
+
+__device__ __forceinline__ void finish_regs(RefineShared& sh, int32_t* __restrict__ out, int k, int need,
+                                            int n_eq, int first_free, const uint2 (&c)[kRegCand],
+                                            uint32_t valid) {
+  static_assert(kRefineThreads / kWave <= 8 && 2 * kRegPasses * 256 * 4 <= sizeof(sh.cand), "layout");
+  // Eight zeroed histograms (keys, then columns) in the unused candidate list.
+  int (*hists)[256] = reinterpret_cast<int (*)[256]>(&sh.cand[0]);
+  reinterpret_cast<int4*>(&hists[0][0])[threadIdx.x] = make_int4(0, 0, 0, 0);
+  if (threadIdx.x == 0) sh.out_pos = first_free;
+  uint32_t key[kRegCand], ncol[kRegCand];
+#pragma unroll
+  for (int i = 0; i < kRegCand; ++i) {
+    key[i] = c[i].x;
+    ncol[i] = ~c[i].y;
+  }
+  uint32_t o, a;
+  or_and_regs(key, valid, sh.red, &o, &a);  // its barrier also publishes the zeroed histograms
+  int above = 0, ties = 0;
+  const uint32_t T = select_regs(key, valid, o, a, n_eq, need, hists, &above, &ties);
+  const int ties_needed = need - above;
+  // Of more ties than needed, those up to the ties_needed-th smallest column
+  // (columns are distinct): the ties_needed-th largest complemented column.
+  uint32_t col_cut = 0xFFFFFFFFu;
+  if (ties > ties_needed) {  // uniform
+    uint32_t tie = 0u;
+#pragma unroll
+    for (int i = 0; i < kRegCand; ++i) tie |= (((valid >> i) & 1u) && key[i] == T ? 1u : 0u) << i;
+    lds_barrier();  // every read of the first OR/AND slots is done
+    or_and_regs(ncol, tie, sh.red, &o, &a);
+    int unused0 = 0, unused1 = 0;
+    col_cut = ~select_regs(ncol, tie, o, a, ties, ties_needed, hists + kRegPasses, &unused0, &unused1);
+  }
+#pragma unroll
+  for (int i = 0; i < kRegCand; ++i) {
+    const bool take = ((valid >> i) & 1u) && (key[i] > T || (key[i] == T && c[i].y <= col_cut));
+    emit(sh, out, k, take, static_cast<int>(c[i].y));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One workgroup per row after topk_collect: the two counter pairs, the
 // collect workgroups' stored counts, the thread's two bins and the first 1024
 // candidates from each end are requested together (the candidate buffer has a
 // fixed address; entries past the counts are unused).
-constexpr int kEarlyCand = 2;  // candidates per thread and end loaded with the counts
 
 // The candidates past the early ones, front list then back list as one list
 // of ef + eb: f(i, candidate) for i in [kEarlyCand * threads, ef) and
@@ -1310,6 +1439,20 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __res
     }
     copy_rest(cand, ef, eb, [&](int i, uint2 c) { out[gf + i] = static_cast<int32_t>(c.y); });
     for (int i = gf + n_eq + tid; i < k - gb; i += kRefineThreads) out[i] = -1;
+    return;
+  }
+  if (ef <= kEarlyCand * kRefineThreads && eb <= kEarlyCand * kRefineThreads) {  // uniform
+    uint2 c[kRegCand];
+    uint32_t valid = 0u;
+#pragma unroll
+    for (int j = 0; j < kEarlyCand; ++j) {
+      const int i = j * kRefineThreads + tid;
+      c[j] = early_f[j];
+      c[kEarlyCand + j] = early_b[j];
+      valid |= (i < ef ? 1u : 0u) << j;
+      valid |= (i < eb ? 1u : 0u) << (kEarlyCand + j);
+    }
+    finish_regs(sh, out, k, k - n_gt, n_eq, gf, c, valid);
     return;
   }
   if (n_eq > kCutMin) {  // uniform
