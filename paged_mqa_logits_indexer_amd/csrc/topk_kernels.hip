@@ -450,12 +450,16 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const void* __restr
 // serves the atomics on one counter one after another, so long rows give each
 // workgroup two chunks.
 template <int KEY, bool F16, int M>
+// (Arguments in the order of first use: the leading 56 bytes arrive in scalar
+// registers.)
 __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __restrict__ logits,
                                                                 int64_t stride,
                                                                 const int32_t* hist,  // (see below)
-                                                                int64_t hist_stride,
-                                                                const int32_t* __restrict__ lens, int k,
-                                                                int32_t* __restrict__ indices, Workspace ws) {
+                                                                const int32_t* __restrict__ lens,
+                                                                char* __restrict__ ws_base,
+                                                                int32_t* __restrict__ indices, int k,
+                                                                int hist_stride) {
+  const Workspace ws{ws_base};
   __shared__ int s_red[kWaves + 5];
   __shared__ int s_sub[kSubBins];
   const int row = blockIdx.y;
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const void* __re
   // the length.  The compiler barrier keeps the loads here: through a
   // __restrict__ pointer they would count as invariant and be sunk past the
   // exit test.
-  const int* h = hist + row * hist_stride + tid * 4;
+  const int* h = hist + static_cast<int64_t>(row) * hist_stride + tid * 4;
   const int2 h01 = *reinterpret_cast<const int2*>(h);  // 8-B aligned
   const int2 h23 = *reinterpret_cast<const int2*>(h + 2);
   __asm__ volatile("" ::: "memory");
@@ -1358,11 +1362,9 @@ template <int KEY, bool F16>
 // in scalar registers before the kernel starts).
 __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __restrict__ ws_base,
                                                                      const int32_t* __restrict__ lens,
-                                                                     int collect_shift, int k, int64_t stride,
-                                                                     int32_t* __restrict__ indices,
-                                                                     const void* __restrict__ logits,
-                                                                     const int32_t* __restrict__ hist,
-                                                                     int64_t hist_stride, int own_hist) {
+                                                                     int64_t stride, int32_t* __restrict__ indices,
+                                                                     int collect_shift, int k, int own_hist,
+                                                                     const void* __restrict__ logits) {
   const Workspace ws{ws_base};
   __shared__ RefineShared sh;
   __shared__ int s_red4[4 * (kRefineThreads / kWave)];
@@ -1595,7 +1597,7 @@ void launch_collect(const TopkArgs& a, const Workspace& ws, const int32_t* hist,
                     hipStream_t stream, hipEvent_t start) {
   const dim3 grid(static_cast<unsigned>((chunks + M - 1) / M), static_cast<unsigned>(a.rows));
   launch_kernel(topk_collect_kernel<KEY, F16, M>, grid, dim3(kThreads), stream, start, nullptr, a.logits,
-                a.logits_stride, hist, hist_stride, a.context_lens, a.k, a.indices, ws);
+                a.logits_stride, hist, a.context_lens, ws.base, a.indices, a.k, static_cast<int>(hist_stride));
 }
 
 template <int KEY, bool F16>
@@ -1605,9 +1607,8 @@ void launch_chunked(const TopkArgs& a, const Workspace& ws, const int32_t* hist,
   if (m == 2) launch_collect<KEY, F16, 2>(a, ws, hist, hist_stride, chunks, stream, start);
   else launch_collect<KEY, F16, 1>(a, ws, hist, hist_stride, chunks, stream, start);
   launch_kernel(topk_finish_kernel<KEY, F16>, dim3(a.rows), dim3(kRefineThreads), stream, nullptr, stop, ws.base,
-                a.context_lens, m == 2 ? kChunkShift + 1 : kChunkShift, a.k, a.logits_stride, a.indices, a.logits,
-                hist, hist_stride,
-                own_hist ? 1 : 0);
+                a.context_lens, a.logits_stride, a.indices, m == 2 ? kChunkShift + 1 : kChunkShift, a.k,
+                own_hist ? 1 : 0, a.logits);
 }
 
 hipError_t launch_sparse_topk(const TopkArgs& a, const int32_t* table, int kb, hipStream_t stream,
