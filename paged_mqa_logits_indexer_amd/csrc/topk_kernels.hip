@@ -1183,7 +1183,9 @@ constexpr int kRegPasses = 4;  // 8-bit digits of a 32-bit value
 // Radix select over the values v[i] (bit i of `valid`) of every thread of
 // the block, `total` of them: the need-th largest value, *above = how many
 // exceed it, *at = how many equal it.  hists: kRegPasses zeroed 256-bin
-// histograms; o and a: the OR and AND of every valid value (block-wide).
+// histograms; o and a: bits that some valid value may have set, and bits
+// that every valid value has set (the block-wide OR and AND, or looser
+// bounds, which cost passes only).
 // Block-uniform control flow: every wave finds the same digits.
 __device__ __forceinline__ uint32_t select_regs(const uint32_t (&v)[kRegCand], uint32_t valid, uint32_t o,
                                                 uint32_t a, int total, int need, int (*hists)[256], int* above,
@@ -1261,8 +1263,8 @@ __device__ __forceinline__ void or_and_regs(const uint32_t (&v)[kRegCand], uint3
   *a = y;
 }
 
-__device__ __forceinline__ void finish_regs(RefineShared& sh, int32_t* __restrict__ out, int k, int need,
-                                            int n_eq, int first_free, const uint2 (&c)[kRegCand],
+__device__ __forceinline__ void finish_regs(RefineShared& sh, int32_t* __restrict__ out, int k, int len,
+                                            int need, int n_eq, int first_free, const uint2 (&c)[kRegCand],
                                             uint32_t valid) {
   static_assert(kRefineThreads / kWave <= 8 && 2 * kRegPasses * 256 * 4 <= sizeof(sh.cand), "layout");
   // Eight zeroed histograms (keys, then columns) in the unused candidate list.
@@ -1287,10 +1289,13 @@ __device__ __forceinline__ void finish_regs(RefineShared& sh, int32_t* __restric
     uint32_t tie = 0u;
 #pragma unroll
     for (int i = 0; i < kRegCand; ++i) tie |= (((valid >> i) & 1u) && key[i] == T ? 1u : 0u) << i;
-    lds_barrier();  // every read of the first OR/AND slots is done
-    or_and_regs(ncol, tie, sh.red, &o, &a);
+    // The columns lie in [0, len): their complements differ at most in the
+    // low bits that len - 1 spans, which bounds the passes without a
+    // block-wide OR/AND of the tie columns.
+    const uint32_t span = len > 1 ? (0xFFFFFFFFu >> __clz(static_cast<uint32_t>(len - 1))) : 1u;
     int unused0 = 0, unused1 = 0;
-    col_cut = ~select_regs(ncol, tie, o, a, ties, ties_needed, hists + kRegPasses, &unused0, &unused1);
+    col_cut = ~select_regs(ncol, tie, 0xFFFFFFFFu, ~span, ties, ties_needed, hists + kRegPasses, &unused0,
+                           &unused1);
   }
 #pragma unroll
   for (int i = 0; i < kRegCand; ++i) {
@@ -1454,7 +1459,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __res
       valid |= (i < ef ? 1u : 0u) << j;
       valid |= (i < eb ? 1u : 0u) << (kEarlyCand + j);
     }
-    finish_regs(sh, out, k, k - n_gt, n_eq, gf, c, valid);
+    finish_regs(sh, out, k, len, k - n_gt, n_eq, gf, c, valid);
     return;
   }
   if (n_eq > kCutMin) {  // uniform
