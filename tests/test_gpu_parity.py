@@ -275,6 +275,47 @@ def test_topk_ties_go_to_lower_columns(gpu, path):
             check_topk(idx.cpu().numpy(), buf, lens, k, key)
 
 
+def _register_bin_row(rng, n, n_above, inside, ties, below):
+    """A row whose threshold bin [20, 21) holds `inside` distinct values above
+    20.5, `ties` copies of 20.5 (one of them in the last column) and `below`
+    distinct values under it, with n_above distinct values in [25, 200) and
+    the rest far below the bin: a bin of a few hundred candidates."""
+    above = rng.uniform(25.0, 200.0, n_above).astype(np.float32)
+    hi = rng.uniform(20.5, 21.0, inside * 2).astype(np.float32)
+    hi = np.unique(hi[hi > np.float32(20.5)])[:inside]
+    lo = np.unique(rng.uniform(20.0, 20.5, below * 2).astype(np.float32))[:below]
+    rest = np.clip(rng.standard_normal(n - n_above - len(hi) - ties - len(lo)) * 2.0, -15, 15)
+    row = np.concatenate([above, hi, np.full(ties - 1, 20.5, np.float32), lo,
+                          rest.astype(np.float32)])
+    rng.shuffle(row)
+    return np.concatenate([row, np.array([20.5], np.float32)])
+
+
+@pytest.mark.parametrize("path", ["as_is", "wide"])
+def test_topk_threshold_bin_selected_from_registers(gpu, path):
+    # threshold bins of a few hundred candidates (all of them in the finish
+    # pass's early loads): ties at the final key cut by column with more than
+    # 64 ties, a bin whose keys are all equal, and few ties; rows of lengths
+    # that are not powers of two (the column bound comes from the length)
+    rng = np.random.default_rng(2024)
+    cases = [  # (row, k)
+        (_register_bin_row(rng, 40000, 1900, 100, 300, 100), 2048),
+        (_register_bin_row(rng, 39999, 1900, 0, 500, 0), 2048),
+        (_register_bin_row(rng, 25001, 1900, 100, 40, 300), 2020),
+        (_register_bin_row(rng, 65537, 1900, 60, 200, 60), 2000),
+    ]
+    for ci, (row, k) in enumerate(cases):
+        buf, lens = _scores_dev([row])
+        s, ln = on_path(torch.from_numpy(buf).to(DEV), torch.from_numpy(lens).to(DEV), path)
+        buf, lens = s.cpu().numpy(), ln.cpu().numpy()
+        h = torch.zeros((1, 1024), dtype=torch.int32, device=DEV)
+        gpu.score_histogram(s, ln, h)
+        for key in (O.KEY_FP32, O.KEY_FP16):
+            announce(f"topk_rows register-path bin case={ci} key={key} k={k} path={path}")
+            idx = topk(s, h, ln, k, key)
+            check_topk(idx.cpu().numpy(), buf, lens, k, key)
+
+
 def test_topk_row_of_more_than_512_chunks(gpu):
     # the last workgroup adds up and gathers the chunk slots 512 at a time
     n = 512 * 8192 + 5000
