@@ -595,8 +595,21 @@ def main() -> int:
         run16(3, False)
         st_h = run16(args.fp16_steps, True)
         lt_h = run16(args.fp16_steps, True, split=True)
+        # The three step kinds once more, interleaved (order rotated every
+        # step), so that clock and thermal drift between the legs above does
+        # not decide their comparison.
+        print(f"[bench] interleaved FP32 / FP16-key / FP16-logits steps {args.fp16_steps}",
+              file=sys.stderr, flush=True)
+        inter = {0: [], 1: [], 2: []}
+        for i in range(args.fp16_steps):
+            for v in ((0, 1, 2), (1, 2, 0), (2, 0, 1))[i % 3]:
+                if v == 2:
+                    inter[2] += run16(1, True)
+                else:
+                    inter[v] += run(1, pmqa.KEY_FP32 if v == 0 else pmqa.KEY_FP16, True)[2]
     else:
         st16, tt16, lt_h, st_h = [], [], [], []
+        inter = None
 
     # the same shape with MXFP4 K pages (half the K bytes)
     mx_out = None
@@ -933,6 +946,11 @@ def main() -> int:
         # FP16 logits output: indexer_logits_f16 (halves) + topk_rows_f16 (FP16 keys)
         "fp16_logits": ({"step_us_mean": round(float(np.mean(st_h)), 3),
                          "indexer_logits_f16_mean": round(float(np.mean(lt_h)), 3)} if st_h else None),
+        # The same three steps interleaved step by step (means and medians).
+        "interleaved_steps": ({name: {"mean": round(float(np.mean(inter[v])), 3),
+                                      "median": round(float(np.median(inter[v])), 3)}
+                               for v, name in ((0, "fp32"), (1, "fp16_keys"), (2, "fp16_logits"))}
+                              if inter else None),
         # the same shape with MXFP4 K: indexer_logits_mxfp4 + topk_rows (FP32 keys);
         # frac = algorithmic bytes / time against the HBM peak
         "mxfp4_k": mx_out,
