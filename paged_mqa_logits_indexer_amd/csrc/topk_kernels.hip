@@ -1044,6 +1044,144 @@ __device__ __forceinline__ void finish_candidates(RefineShared& sh, int32_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// A threshold bin whose candidates all came with the early loads (at most
+// 1024 from each end) is finished from registers: thread t holds front
+// entries t and t + 512 and back entries t and t + 512.  The radix passes
+// count into histograms of their own (zeroed once, up front), and after each
+// pass's barrier every wave reads the counts and finds the digit itself, so
+// a pass costs one barrier; the LDS candidate list is not used.
+constexpr int kEarlyCand = 2;  // candidates per thread and end loaded with the counts
+constexpr int kRegCand = 2 * kEarlyCand;
+constexpr int kRegPasses = 4;  // 8-bit digits of a 32-bit value
+
+// Radix select over the values v[i] (bit i of `valid`) of every thread of
+// the block, `total` of them: the need-th largest value, *above = how many
+// exceed it, *at = how many equal it.  hists: kRegPasses zeroed 256-bin
+// histograms; o and a: bits that some valid value may have set, and bits
+// that every valid value has set (the block-wide OR and AND, or looser
+// bounds, which cost passes only).
+// Block-uniform control flow: every wave finds the same digits.
+__device__ __forceinline__ uint32_t select_regs(const uint32_t (&v)[kRegCand], uint32_t valid, uint32_t o,
+                                                uint32_t a, int total, int need, int (*hists)[256], int* above,
+                                                int* at) {
+  const int lane = __lane_id();
+  const uint32_t diff = o ^ a;
+  uint32_t prefix = a & ~diff, fixed = ~diff;
+  int gt = 0, eq = total;  // (every value the same when diff is 0)
+  int shift = max(top_bit(diff | 1u) - 7, 0);
+  for (int p = 0; diff != 0u && p < kRegPasses; ++p) {
+    int* h = hists[p];
+#pragma unroll
+    for (int i = 0; i < kRegCand; ++i)
+      if (((valid >> i) & 1u) && ((v[i] ^ prefix) & fixed) == 0u) atomicAdd(&h[(v[i] >> shift) & 0xFFu], 1);
+    lds_barrier();
+    // Lane l reads digits 255 - 4l down to 252 - 4l; every wave finds the same digit.
+    const int4 q = reinterpret_cast<const int4*>(h)[kWave - 1 - lane];
+    const int c[4] = {q.w, q.z, q.y, q.x};
+    const int sum = c[0] + c[1] + c[2] + c[3];
+    int run = wave_inclusive_scan(sum) - sum;
+    int hit = -1, hit_before = 0, hit_in = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (run < need && run + c[i] >= need) {
+        hit = 255 - 4 * lane - i;
+        hit_before = run;
+        hit_in = c[i];
+      }
+      run += c[i];
+    }
+    const int src = first_lane(__ballot(hit >= 0));
+    const int d = __builtin_amdgcn_readlane(hit, src) & 0xFF;
+    const int before = __builtin_amdgcn_readlane(hit_before, src);
+    eq = __builtin_amdgcn_readlane(hit_in, src);
+    need -= before;
+    gt += before;
+    prefix |= static_cast<uint32_t>(d) << shift;
+    fixed |= 0xFFu << shift;
+    if (shift == 0) break;
+    shift = max(shift - 8, 0);
+  }
+  *above = gt;
+  *at = eq;
+  return prefix;
+}
+
+// The block-wide OR and AND of the values v[i] with bit i of `valid`, through
+// slots [0, 16) of s_red (one barrier).
+__device__ __forceinline__ void or_and_regs(const uint32_t (&v)[kRegCand], uint32_t valid, int* s_red, uint32_t* o,
+                                            uint32_t* a) {
+  uint32_t x = 0u, y = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < kRegCand; ++i) {
+    if ((valid >> i) & 1u) {
+      x |= v[i];
+      y &= v[i];
+    }
+  }
+  x = wave_or(x);
+  y = wave_and(y);
+  const int wave = threadIdx.x / kWave;
+  if (__lane_id() == 0) {
+    s_red[wave] = static_cast<int>(x);
+    s_red[8 + wave] = static_cast<int>(y);
+  }
+  lds_barrier();
+  x = 0u;
+  y = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kRefineThreads / kWave; ++w) {
+    x |= static_cast<uint32_t>(s_red[w]);
+    y &= static_cast<uint32_t>(s_red[8 + w]);
+  }
+  *o = x;
+  *a = y;
+}
+
+__device__ __forceinline__ void finish_regs(RefineShared& sh, int32_t* __restrict__ out, int k, int len,
+                                            int need, int n_eq, int first_free, const uint2 (&c)[kRegCand],
+                                            uint32_t valid) {
+  // Eight zeroed histograms (keys, then columns) at the end of the LDS
+  // candidate list: the candidates, when they were gathered there first (the
+  // row pass), occupy at most its first 2048 entries.
+  constexpr int kHistEntries = 2 * kRegPasses * 256 * 4 / static_cast<int>(sizeof(uint2));
+  static_assert(kRefineThreads / kWave <= 8 && kHistEntries + kRegCand * kRefineThreads <= kCandBuf, "layout");
+  int (*hists)[256] = reinterpret_cast<int (*)[256]>(&sh.cand[kCandBuf - kHistEntries]);
+  reinterpret_cast<int4*>(&hists[0][0])[threadIdx.x] = make_int4(0, 0, 0, 0);
+  if (threadIdx.x == 0) sh.out_pos = first_free;
+  uint32_t key[kRegCand], ncol[kRegCand];
+#pragma unroll
+  for (int i = 0; i < kRegCand; ++i) {
+    key[i] = c[i].x;
+    ncol[i] = ~c[i].y;
+  }
+  uint32_t o, a;
+  or_and_regs(key, valid, sh.red, &o, &a);  // its barrier also publishes the zeroed histograms
+  int above = 0, ties = 0;
+  const uint32_t T = select_regs(key, valid, o, a, n_eq, need, hists, &above, &ties);
+  const int ties_needed = need - above;
+  // Of more ties than needed, those up to the ties_needed-th smallest column
+  // (columns are distinct): the ties_needed-th largest complemented column.
+  uint32_t col_cut = 0xFFFFFFFFu;
+  if (ties > ties_needed) {  // uniform
+    uint32_t tie = 0u;
+#pragma unroll
+    for (int i = 0; i < kRegCand; ++i) tie |= (((valid >> i) & 1u) && key[i] == T ? 1u : 0u) << i;
+    // The columns lie in [0, len): their complements differ at most in the
+    // low bits that len - 1 spans, which bounds the passes without a
+    // block-wide OR/AND of the tie columns.
+    const uint32_t span = len > 1 ? (0xFFFFFFFFu >> __clz(static_cast<uint32_t>(len - 1))) : 1u;
+    int unused0 = 0, unused1 = 0;
+    col_cut = ~select_regs(ncol, tie, 0xFFFFFFFFu, ~span, ties, ties_needed, hists + kRegPasses, &unused0,
+                           &unused1);
+  }
+#pragma unroll
+  for (int i = 0; i < kRegCand; ++i) {
+    const bool take = ((valid >> i) & 1u) && (key[i] > T || (key[i] == T && c[i].y <= col_cut));
+    emit(sh, out, k, take, static_cast<int>(c[i].y));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Rows of at most M * 8192 scores: one workgroup per row, thread t takes
 // columns 8192m + 16t .. 8192m + 16t+15 of each part m, so block scans of the
 // per-thread counts (part 0's places before part 1's) keep both lists in
@@ -1148,7 +1286,21 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
       for (int i = n_gt + n_eq + tid; i < k; i += kRefineThreads) out[i] = -1;
     } else {
       lds_barrier();
-      finish_candidates(sh, out, k, n_gt, n_eq, n_gt, true);
+      if (n_eq <= kRegCand * kRefineThreads) {  // uniform
+        // Few candidates: thread t takes list entries t, t + 512, ... into
+        // registers and the select runs there (see finish_regs).
+        uint2 c[kRegCand];
+        uint32_t valid = 0u;
+#pragma unroll
+        for (int j = 0; j < kRegCand; ++j) {
+          const int i = j * kRefineThreads + tid;
+          c[j] = i < n_eq ? sh.cand[i] : make_uint2(0u, 0u);
+          valid |= (i < n_eq ? 1u : 0u) << j;
+        }
+        finish_regs(sh, out, k, len, k - n_gt, n_eq, n_gt, c, valid);
+      } else {
+        finish_candidates(sh, out, k, n_gt, n_eq, n_gt, true);
+      }
     }
   }
   if constexpr (MAP) {
@@ -1169,140 +1321,6 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
   }
 }
 
-// ---------------------------------------------------------------------------
-// A threshold bin whose candidates all came with the early loads (at most
-// 1024 from each end) is finished from registers: thread t holds front
-// entries t and t + 512 and back entries t and t + 512.  The radix passes
-// count into histograms of their own (zeroed once, up front), and after each
-// pass's barrier every wave reads the counts and finds the digit itself, so
-// a pass costs one barrier; the LDS candidate list is not used.
-constexpr int kEarlyCand = 2;  // candidates per thread and end loaded with the counts
-constexpr int kRegCand = 2 * kEarlyCand;
-constexpr int kRegPasses = 4;  // 8-bit digits of a 32-bit value
-
-// Radix select over the values v[i] (bit i of `valid`) of every thread of
-// the block, `total` of them: the need-th largest value, *above = how many
-// exceed it, *at = how many equal it.  hists: kRegPasses zeroed 256-bin
-// histograms; o and a: bits that some valid value may have set, and bits
-// that every valid value has set (the block-wide OR and AND, or looser
-// bounds, which cost passes only).
-// Block-uniform control flow: every wave finds the same digits.
-__device__ __forceinline__ uint32_t select_regs(const uint32_t (&v)[kRegCand], uint32_t valid, uint32_t o,
-                                                uint32_t a, int total, int need, int (*hists)[256], int* above,
-                                                int* at) {
-  const int lane = __lane_id();
-  const uint32_t diff = o ^ a;
-  uint32_t prefix = a & ~diff, fixed = ~diff;
-  int gt = 0, eq = total;  // (every value the same when diff is 0)
-  int shift = max(top_bit(diff | 1u) - 7, 0);
-  for (int p = 0; diff != 0u && p < kRegPasses; ++p) {
-    int* h = hists[p];
-#pragma unroll
-    for (int i = 0; i < kRegCand; ++i)
-      if (((valid >> i) & 1u) && ((v[i] ^ prefix) & fixed) == 0u) atomicAdd(&h[(v[i] >> shift) & 0xFFu], 1);
-    lds_barrier();
-    // Lane l reads digits 255 - 4l down to 252 - 4l; every wave finds the same digit.
-    const int4 q = reinterpret_cast<const int4*>(h)[kWave - 1 - lane];
-    const int c[4] = {q.w, q.z, q.y, q.x};
-    const int sum = c[0] + c[1] + c[2] + c[3];
-    int run = wave_inclusive_scan(sum) - sum;
-    int hit = -1, hit_before = 0, hit_in = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (run < need && run + c[i] >= need) {
-        hit = 255 - 4 * lane - i;
-        hit_before = run;
-        hit_in = c[i];
-      }
-      run += c[i];
-    }
-    const int src = first_lane(__ballot(hit >= 0));
-    const int d = __builtin_amdgcn_readlane(hit, src) & 0xFF;
-    const int before = __builtin_amdgcn_readlane(hit_before, src);
-    eq = __builtin_amdgcn_readlane(hit_in, src);
-    need -= before;
-    gt += before;
-    prefix |= static_cast<uint32_t>(d) << shift;
-    fixed |= 0xFFu << shift;
-    if (shift == 0) break;
-    shift = max(shift - 8, 0);
-  }
-  *above = gt;
-  *at = eq;
-  return prefix;
-}
-
-// The block-wide OR and AND of the values v[i] with bit i of `valid`, through
-// slots [0, 16) of s_red (one barrier).
-__device__ __forceinline__ void or_and_regs(const uint32_t (&v)[kRegCand], uint32_t valid, int* s_red, uint32_t* o,
-                                            uint32_t* a) {
-  uint32_t x = 0u, y = 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = 0; i < kRegCand; ++i) {
-    if ((valid >> i) & 1u) {
-      x |= v[i];
-      y &= v[i];
-    }
-  }
-  x = wave_or(x);
-  y = wave_and(y);
-  const int wave = threadIdx.x / kWave;
-  if (__lane_id() == 0) {
-    s_red[wave] = static_cast<int>(x);
-    s_red[8 + wave] = static_cast<int>(y);
-  }
-  lds_barrier();
-  x = 0u;
-  y = 0xFFFFFFFFu;
-#pragma unroll
-  for (int w = 0; w < kRefineThreads / kWave; ++w) {
-    x |= static_cast<uint32_t>(s_red[w]);
-    y &= static_cast<uint32_t>(s_red[8 + w]);
-  }
-  *o = x;
-  *a = y;
-}
-
-__device__ __forceinline__ void finish_regs(RefineShared& sh, int32_t* __restrict__ out, int k, int len,
-                                            int need, int n_eq, int first_free, const uint2 (&c)[kRegCand],
-                                            uint32_t valid) {
-  static_assert(kRefineThreads / kWave <= 8 && 2 * kRegPasses * 256 * 4 <= sizeof(sh.cand), "layout");
-  // Eight zeroed histograms (keys, then columns) in the unused candidate list.
-  int (*hists)[256] = reinterpret_cast<int (*)[256]>(&sh.cand[0]);
-  reinterpret_cast<int4*>(&hists[0][0])[threadIdx.x] = make_int4(0, 0, 0, 0);
-  if (threadIdx.x == 0) sh.out_pos = first_free;
-  uint32_t key[kRegCand], ncol[kRegCand];
-#pragma unroll
-  for (int i = 0; i < kRegCand; ++i) {
-    key[i] = c[i].x;
-    ncol[i] = ~c[i].y;
-  }
-  uint32_t o, a;
-  or_and_regs(key, valid, sh.red, &o, &a);  // its barrier also publishes the zeroed histograms
-  int above = 0, ties = 0;
-  const uint32_t T = select_regs(key, valid, o, a, n_eq, need, hists, &above, &ties);
-  const int ties_needed = need - above;
-  // Of more ties than needed, those up to the ties_needed-th smallest column
-  // (columns are distinct): the ties_needed-th largest complemented column.
-  uint32_t col_cut = 0xFFFFFFFFu;
-  if (ties > ties_needed) {  // uniform
-    uint32_t tie = 0u;
-#pragma unroll
-    for (int i = 0; i < kRegCand; ++i) tie |= (((valid >> i) & 1u) && key[i] == T ? 1u : 0u) << i;
-    // The columns lie in [0, len): their complements differ at most in the
-    // low bits that len - 1 spans, which bounds the passes without a
-    // block-wide OR/AND of the tie columns.
-    const uint32_t span = len > 1 ? (0xFFFFFFFFu >> __clz(static_cast<uint32_t>(len - 1))) : 1u;
-    int unused0 = 0, unused1 = 0;
-    col_cut = ~select_regs(ncol, tie, 0xFFFFFFFFu, ~span, ties, ties_needed, hists + kRegPasses, &unused0,
-                           &unused1);
-  }
-#pragma unroll
-  for (int i = 0; i < kRegCand; ++i) {
-    const bool take = ((valid >> i) & 1u) && (key[i] > T || (key[i] == T && c[i].y <= col_cut));
-    emit(sh, out, k, take, static_cast<int>(c[i].y));
-  }
-}
 
 // ---------------------------------------------------------------------------
 // One workgroup per row after topk_collect: the two counter pairs, the
