@@ -19,7 +19,9 @@
 //                  bin b* from the histogram (or from one it builds in LDS
 //                  when there is none), the columns above b* straight to the
 //                  output, the candidates of b* to LDS, where a radix select
-//                  on the remaining key bits finishes the row.
+//                  on the remaining key bits finishes the row (from
+//                  registers, up to four candidates per thread, when the bin
+//                  holds at most 2048).
 //   longer rows:
 //   [hist == NULL] topk_hist: build the row histograms in the workspace
 //                  (the first pass the producer's fused histogram normally
@@ -33,11 +35,14 @@
 //                  (key, column) candidates of b* to the row's candidate
 //                  buffer (places below 16384)
 //   topk_finish    one 512-thread workgroup per row reads the counter pair
-//                  (with the row's bins and the first candidates) and checks
-//                  it against b*: if it confirms b*, the candidates are
-//                  ranked in LDS as above; otherwise an exact radix select
-//                  over the whole row rewrites the output.  It then clears
-//                  the counter pair for the next call.
+//                  (with b*, the slots and the first 1024 candidates from
+//                  each end) and checks it against b*: if it confirms b*,
+//                  the candidates are ranked -- from registers when those
+//                  early loads hold them all, after a cut by sub-bins when
+//                  the bin holds more than 2048, else in LDS as above;
+//                  otherwise an exact radix select over the whole row
+//                  rewrites the output.  It then clears the counter pair,
+//                  sub-bins and built bins for the next call.
 //
 // Scores are classified against the FP16-key range of b* (bin_key_range),
 // not by computing each score's bin.  Places taken by atomics put neither
