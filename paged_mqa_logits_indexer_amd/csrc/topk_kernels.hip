@@ -1542,7 +1542,19 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __res
         pt += __popcll(bt);
       }
       lds_barrier();
-      finish_candidates(sh, out, k, n_gt + tot2.x, tot2.y, gf + tot2.x, false);
+      if (tot2.y <= kRegCand * kRefineThreads) {  // uniform: the kept sub-bin, from registers
+        uint2 r[kRegCand];
+        uint32_t valid = 0u;
+#pragma unroll
+        for (int j = 0; j < kRegCand; ++j) {
+          const int i = j * kRefineThreads + tid;
+          r[j] = i < tot2.y ? sh.cand[i] : make_uint2(0u, 0u);
+          valid |= (i < tot2.y ? 1u : 0u) << j;
+        }
+        finish_regs(sh, out, k, len, need - tot2.x, tot2.y, gf + tot2.x, r, valid);
+      } else {
+        finish_candidates(sh, out, k, n_gt + tot2.x, tot2.y, gf + tot2.x, false);
+      }
       return;
     }
 #pragma unroll
