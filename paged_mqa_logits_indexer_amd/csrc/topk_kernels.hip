@@ -870,6 +870,8 @@ __device__ __forceinline__ void digit_publish(RefineShared& sh) {
 
 __device__ __forceinline__ void finish_candidates(RefineShared& sh, int32_t* __restrict__ out, int k, int n_gt,
                                                   int n_eq, int first_free, bool column_order);
+__device__ __forceinline__ void finish_list(RefineShared& sh, int32_t* __restrict__ out, int k, int len,
+                                            int n_gt, int n_eq, int first_free);
 
 template <int KEY, bool F16>
 __device__ __forceinline__ void whole_row_select(RefineShared& sh, const void* __restrict__ x, int len, int k,
@@ -932,7 +934,7 @@ __device__ __forceinline__ void whole_row_select(RefineShared& sh, const void* _
       });
       lds_barrier();
       const int n_above = k - need;
-      finish_candidates(sh, out, k, n_above, in_bin, n_above, false);
+      finish_list(sh, out, k, len, n_above, in_bin, n_above);
       return;
     }
   }
@@ -1184,6 +1186,26 @@ __device__ __forceinline__ void finish_regs(RefineShared& sh, int32_t* __restric
     const bool take = ((valid >> i) & 1u) && (key[i] > T || (key[i] == T && c[i].y <= col_cut));
     emit(sh, out, k, take, static_cast<int>(c[i].y));
   }
+}
+
+// The n_eq candidates just written to the LDS list (by any thread): selected
+// from registers when they fit four per thread, else by the LDS select.
+__device__ __forceinline__ void finish_list(RefineShared& sh, int32_t* __restrict__ out, int k, int len,
+                                            int n_gt, int n_eq, int first_free) {
+  if (n_eq <= kRegCand * kRefineThreads) {  // uniform
+    lds_barrier();
+    uint2 r[kRegCand];
+    uint32_t valid = 0u;
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) {
+      const int i = j * kRefineThreads + static_cast<int>(threadIdx.x);
+      r[j] = i < n_eq ? sh.cand[i] : make_uint2(0u, 0u);
+      valid |= (i < n_eq ? 1u : 0u) << j;
+    }
+    finish_regs(sh, out, k, len, k - n_gt, n_eq, first_free, r, valid);
+    return;
+  }
+  finish_candidates(sh, out, k, n_gt, n_eq, first_free, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1570,7 +1592,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_finish_kernel(char* __res
     if (i < eb) sh.cand[ef + i] = early_b[j];
   }
   copy_rest(cand, ef, eb, [&](int i, uint2 c) { sh.cand[i] = c; });
-  finish_candidates(sh, out, k, n_gt, n_eq, gf, false);
+  finish_list(sh, out, k, len, n_gt, n_eq, gf);
 }
 
 }  // namespace

@@ -298,11 +298,19 @@ def test_topk_threshold_bin_selected_from_registers(gpu, path):
     # 64 ties, a bin whose keys are all equal, and few ties; rows of lengths
     # that are not powers of two (the column bound comes from the length)
     rng = np.random.default_rng(2024)
+    # 1500 candidates all in even 4096-column chunks: more than 1024 come from
+    # the front list, so they reach the finish pass through LDS first
+    row = np.clip(rng.standard_normal(40000) * 2.0, -15, 15).astype(np.float32)
+    even = np.concatenate([np.arange(c * 4096, min(c * 4096 + 4096, 40000)) for c in range(0, 10, 2)])
+    cols = rng.choice(even, 1900 + 1500, replace=False)
+    row[cols[:1900]] = rng.uniform(25.0, 200.0, 1900).astype(np.float32)
+    row[cols[1900:]] = np.round(rng.uniform(20.0, 21.0, 1500) * 64) / np.float32(64)  # ties
     cases = [  # (row, k)
         (_register_bin_row(rng, 40000, 1900, 100, 300, 100), 2048),
         (_register_bin_row(rng, 39999, 1900, 0, 500, 0), 2048),
         (_register_bin_row(rng, 25001, 1900, 100, 40, 300), 2020),
         (_register_bin_row(rng, 65537, 1900, 60, 200, 60), 2000),
+        (row, 2048),
     ]
     for ci, (row, k) in enumerate(cases):
         buf, lens = _scores_dev([row])
