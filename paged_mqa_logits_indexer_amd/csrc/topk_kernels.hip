@@ -1313,9 +1313,12 @@ __global__ __launch_bounds__(kRefineThreads) void topk_row_kernel(const void* __
       for (int i = n_gt + n_eq + tid; i < k; i += kRefineThreads) out[i] = -1;
     } else {
       lds_barrier();
-      if (n_eq <= kRegCand * kRefineThreads) {  // uniform
+      if (M == 1 && n_eq <= kRefineThreads) {  // uniform
         // Few candidates: thread t takes list entries t, t + 512, ... into
-        // registers and the select runs there (see finish_regs).
+        // registers and the select runs there (see finish_regs).  Measured
+        // faster only for one-part rows with at most one candidate per
+        // thread (tiny decode); rows of two parts (the candidate chain's
+        // block top-k) and larger bins (its sparse rows) keep the LDS select.
         uint2 c[kRegCand];
         uint32_t valid = 0u;
 #pragma unroll
