@@ -215,6 +215,13 @@ struct DmaOffsets {
 // the page loop; the caller waits for them itself (vmcnt, in issue order).
 // A load that writes LDS must not directly follow the write of m0 that
 // addresses it (one wait state on this GPU family): hence the s_nop after each.
+// The loads carry the non-temporal cache policy (`nt`): every line of the K
+// stream is read once, by one instruction, and streaming it through the
+// caches as such measured faster (long decode 27.4 -> 25.6 us, very long
+// 102.2 -> 97.1 us, varlen 129.8 -> 125.4 us; the sc0/sc1 bits add nothing).
+// The operand-layout register loads of the other launches touch each line
+// with two instructions, and there `nt` measured slower (spec verify 19.1 ->
+// 21.4 us, also when only the line's second access carries it).
 __device__ __forceinline__ void dma_page(const uint8_t* __restrict__ kv_pages, const float* __restrict__ k_scales,
                                          int page, const DmaOffsets& off, uint32_t slot) {
   const uint8_t* kp = kv_pages + static_cast<int64_t>(page) * kPageBytes;
@@ -222,31 +229,31 @@ __device__ __forceinline__ void dma_page(const uint8_t* __restrict__ kv_pages, c
   __asm__ volatile(
       "s_mov_b32 m0, %[l0]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v0], %[kb]\n"
+      "global_load_lds_dwordx4 %[v0], %[kb] nt\n"
       "s_mov_b32 m0, %[l1]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v1], %[kb]\n"
+      "global_load_lds_dwordx4 %[v1], %[kb] nt\n"
       "s_mov_b32 m0, %[l2]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v2], %[kb]\n"
+      "global_load_lds_dwordx4 %[v2], %[kb] nt\n"
       "s_mov_b32 m0, %[l3]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v3], %[kb]\n"
+      "global_load_lds_dwordx4 %[v3], %[kb] nt\n"
       "s_mov_b32 m0, %[l4]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v4], %[kb]\n"
+      "global_load_lds_dwordx4 %[v4], %[kb] nt\n"
       "s_mov_b32 m0, %[l5]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v5], %[kb]\n"
+      "global_load_lds_dwordx4 %[v5], %[kb] nt\n"
       "s_mov_b32 m0, %[l6]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v6], %[kb]\n"
+      "global_load_lds_dwordx4 %[v6], %[kb] nt\n"
       "s_mov_b32 m0, %[l7]\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %[v7], %[kb]\n"
+      "global_load_lds_dwordx4 %[v7], %[kb] nt\n"
       "s_mov_b32 m0, %[l8]\n"
       "s_nop 0\n"
-      "global_load_lds_dword %[vs], %[sb]\n"
+      "global_load_lds_dword %[vs], %[sb] nt\n"
       :
       : [kb] "s"(kp), [sb] "s"(sp), [l0] "s"(slot), [l1] "s"(slot + 1024), [l2] "s"(slot + 2048),
         [l3] "s"(slot + 3072), [l4] "s"(slot + 4096), [l5] "s"(slot + 5120), [l6] "s"(slot + 6144),
@@ -583,14 +590,14 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
 
   if constexpr (kDmaOf<NN, KF>) {
     // Ring of kRing LDS slots per wave: while page `it` is read and computed,
-    // pages it+1 .. it+kRing-1 are in flight (past the last page the last one
-    // is issued again, which keeps the count of loads behind each page
-    // fixed).  The compiler does not order LDS reads after these loads, so
-    // the waits are explicit: before a slot is refilled, every LDS access
-    // issued so far has completed (its last reads are a page old); before a
-    // page is read, at most the (kRing - 1) * kDmaInstrs loads issued after
-    // it are outstanding -- the loop issues no other vector memory operation,
-    // and loads complete in issue order.
+    // pages it+1 .. it+kRing-1 are in flight (those that exist: the last
+    // pages are not issued again, which with non-temporal loads would read
+    // them from HBM a second time).  The compiler does not order LDS reads
+    // after these loads, so the waits are explicit: before a slot is
+    // refilled, every LDS access issued so far has completed (its last reads
+    // are a page old); before a page is read, at most the kDmaInstrs loads of
+    // each page issued after it are outstanding -- the loop issues no other
+    // vector memory operation, and loads complete in issue order.
     // The compiler does not see the page loads (assembly), so it would place
     // its waits for Q and the weights at their first use inside the loop,
     // where they would drain the loads in flight on every page; consuming
@@ -603,21 +610,25 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
       const DmaOffsets off(lane);
 #pragma unroll
       for (int s = 0; s < kRing - 1; ++s)
-        dma_page(a.kv_pages, a.k_scales, page_id(s < n_mine ? s : n_mine - 1), off, ring + s * kSlotBytes);
+        if (s < n_mine) dma_page(a.kv_pages, a.k_scales, page_id(s), off, ring + s * kSlotBytes);
       for (int it = 0; it < n_mine; ++it) {
-        const int nx = it + kRing - 1 < n_mine ? it + kRing - 1 : n_mine - 1;
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        dma_page(a.kv_pages, a.k_scales, page_id(nx), off, ring + ((it + kRing - 1) % kRing) * kSlotBytes);
-        if constexpr (kRing == 2) __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else __asm__ volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        if (it + kRing - 1 < n_mine) {  // wave-uniform
+          __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          dma_page(a.kv_pages, a.k_scales, page_id(it + kRing - 1), off,
+                   ring + ((it + kRing - 1) % kRing) * kSlotBytes);
+        }
+        const int ahead = min(kRing - 1, n_mine - 1 - it);  // pages in flight issued after page `it`
+        static_assert(kDmaInstrs == 9, "the waits below count 9 loads per page");
+        if (kRing == 3 && ahead == 2) __asm__ volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else if (ahead >= 1) __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         PageRegs<KF> pr;
         read_page(ring + (it % kRing) * kSlotBytes, lane, pr);
         compute_page<NN, HIST, F16, KF, kDirectOf<NN, KF>>(
             pr, p0 + lpi0 + it * kWaves, lpi0 + it * kWaves, pages_per_wg, lane, rq, s_out, s_hist,
             static_cast<StageT<F16>*>(a.logits) + static_cast<int64_t>(row0) * a.logits_stride);
       }
-      // the re-issued last pages land before the slots can be refilled
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // (every page issued has landed: the last iteration waited for all)
     }
   } else if (n_mine > 0) {
     for (int it0 = 0; it0 < n_mine; it0 += kRg) {

@@ -6,13 +6,19 @@
 namespace pmqa {
 namespace {
 
+// Both probes read with the non-temporal cache policy (`nt`), as the logits
+// kernel streams its whole-line K loads: each line is read once, and `nt`
+// made both probes ~6 % faster at the long-decode size (read 23.1 -> 21.7 us,
+// gather 24.3 -> 23.0 us), so the ceilings stay comparable with the kernel.
+constexpr int kNtAux = 2;  // buffer-load cache-policy bits: nt
+
 // Streaming read of a contiguous buffer.  Each workgroup reads one contiguous
 // 32 KiB chunk, 8 16-byte loads per thread in flight (a wave's load
 // instruction covers 1 KiB of consecutive bytes).  Of the shapes swept on
 // this GPU (16-128 KiB chunks, 256-1024 threads, one to four persistent
-// workgroups per CU, loads straight to LDS, cache-policy bits), this one and
-// four persistent workgroups per CU were fastest at 64-512 MB (138 MB:
-// 23.0-23.4 us median, cold caches).
+// workgroups per CU, loads straight to LDS), this one and four persistent
+// workgroups per CU were fastest at 64-512 MB (138 MB: 23.0-23.4 us median,
+// cold caches, before the loads were made non-temporal).
 constexpr int kProbeThreads = 256;
 constexpr int kProbeVecs = 8;
 constexpr int64_t kProbeChunk = kProbeThreads * kProbeVecs;  // 16-byte vectors: 32 KiB per workgroup
@@ -24,7 +30,7 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32
 #pragma unroll
   for (int i = 0; i < kProbeVecs; ++i) {
     const int64_t j = base + static_cast<int64_t>(i) * kProbeThreads;
-    v[i] = j < n_vec ? src[j] : i32x4{0, 0, 0, 0};
+    v[i] = j < n_vec ? __builtin_nontemporal_load(src + j) : i32x4{0, 0, 0, 0};
   }
   uint32_t acc = 0u;
 #pragma unroll
@@ -56,10 +62,10 @@ __device__ __forceinline__ void gather_load(const uint8_t* pool, const float* sc
       const_cast<uint8_t*>(pool + static_cast<int64_t>(page) * kPageBytes), 0, kPageBytes, 0x00020000);
 #pragma unroll
   for (int i = 0; i < kPageBytes / 1024; ++i)
-    p.v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, i * 1024 + lane * 16, 0, 0));
+    p.v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, i * 1024 + lane * 16, 0, kNtAux));
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(scales + static_cast<int64_t>(page) * kPage), 0, kPage * 4, 0x00020000);
-  p.sc = __builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, 0, 0);
+  p.sc = __builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, 0, kNtAux);
 }
 
 __device__ __forceinline__ uint32_t gather_fold(const GatherPage& p) {
