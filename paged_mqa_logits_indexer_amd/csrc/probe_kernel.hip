@@ -6,19 +6,14 @@
 namespace pmqa {
 namespace {
 
-// Both probes read with the non-temporal cache policy (`nt`), as the logits
-// kernel streams its whole-line K loads: each line is read once, and `nt`
-// made both probes ~6 % faster at the long-decode size (read 23.1 -> 21.7 us,
-// gather 24.3 -> 23.0 us), so the ceilings stay comparable with the kernel.
-constexpr int kNtAux = 2;  // buffer-load cache-policy bits: nt
-
-// Streaming read of a contiguous buffer.  Each workgroup reads one contiguous
-// 32 KiB chunk, 8 16-byte loads per thread in flight (a wave's load
-// instruction covers 1 KiB of consecutive bytes).  Of the shapes swept on
-// this GPU (16-128 KiB chunks, 256-1024 threads, one to four persistent
-// workgroups per CU, loads straight to LDS), this one and four persistent
-// workgroups per CU were fastest at 64-512 MB (138 MB: 23.0-23.4 us median,
-// cold caches, before the loads were made non-temporal).
+// Streaming read of a contiguous buffer.  The same kernel is the cache sweep
+// that evicts K between timed calls, so its loads are ordinary (allocating)
+// ones.  Each workgroup reads one contiguous 32 KiB chunk, 8 16-byte loads
+// per thread in flight (a wave's load instruction covers 1 KiB of
+// consecutive bytes).  Of the shapes swept on this GPU (16-128 KiB chunks,
+// 256-1024 threads, one to four persistent workgroups per CU, loads straight
+// to LDS), this one and four persistent workgroups per CU were fastest at
+// 64-512 MB (138 MB: 23.0-23.4 us median, cold caches).
 constexpr int kProbeThreads = 256;
 constexpr int kProbeVecs = 8;
 constexpr int64_t kProbeChunk = kProbeThreads * kProbeVecs;  // 16-byte vectors: 32 KiB per workgroup
@@ -30,7 +25,7 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32
 #pragma unroll
   for (int i = 0; i < kProbeVecs; ++i) {
     const int64_t j = base + static_cast<int64_t>(i) * kProbeThreads;
-    v[i] = j < n_vec ? __builtin_nontemporal_load(src + j) : i32x4{0, 0, 0, 0};
+    v[i] = j < n_vec ? src[j] : i32x4{0, 0, 0, 0};
   }
   uint32_t acc = 0u;
 #pragma unroll
@@ -39,6 +34,10 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32
   for (int off = kWave / 2; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, kWave);
   if (__lane_id() == 0 && acc == 0x9E3779B9u) atomicXor(sink, acc);  // keeps the loads live
 }
+
+// The gather probe reads with the non-temporal cache policy (`nt`), as the
+// logits kernel's whole-line page loads do.
+constexpr int kNtAux = 2;  // buffer-load cache-policy bits: nt
 
 // Paged gather: the pages listed in `table` (8 KiB of FP8 keys each, plus
 // the page's 64 fp32 scales), read the way a paged K stream must be read --
