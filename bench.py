@@ -831,7 +831,7 @@ def main() -> int:
         for i in range(reps + 3):
             e0, e1, e2, e3 = new_events(4)
             evict()
-            pmqa.hbm_read_probe(src, sink, events=(e0, e1))
+            pmqa.hbm_read_probe_nt(src, sink, events=(e0, e1))
             if not xw.mxfp4:
                 evict()
                 pmqa.hbm_gather_probe(tw["kv_pages"], tw["k_scales"], plist, sink, events=(e2, e3))
@@ -968,7 +968,7 @@ def main() -> int:
             "k_bytes": ab["k"],
             "k_gbps": round(ab["k"] / (mean_logits * 1e-6) / 1e9, 1),
             "k_frac_of_peak": round(ab["k"] / (mean_logits * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            # contiguous read of the K codes + scales (the best streaming shape)
+            # contiguous read of the K codes + scales: non-temporal loads, the best streaming shape
             "read_probe_us_p50": round(probe_us, 3),
             "read_probe_us_p10_p90": [round(pct(rd_pts, 10), 3), round(pct(rd_pts, 90), 3)],
             "read_probe_gbps": round(ab["k"] * 33 / 32 / (probe_us * 1e-6) / 1e9, 1),

@@ -445,12 +445,21 @@ const char* indexer_status_str(int32_t status);
 
 /*
  * hbm_read_probe -- measurement aid, not part of the method: streams `bytes`
- * bytes (a multiple of 16) from `src` (device, 16-B aligned) with the same
- * 16-B vector loads the logits kernel uses and writes one checksum word to
- * *sink (device).  Its duration gives the practical HBM read ceiling that the
- * logits kernel is compared with.
+ * bytes (a multiple of 16) from `src` (device, 16-B aligned) with ordinary
+ * 16-B vector loads (they allocate in the caches, so a large buffer read this
+ * way is a cache sweep) and writes one checksum word to *sink (device).
+ * Errors: IDX_EINVAL for a null pointer or bytes == 0, IDX_EALIGN for a
+ * misaligned src/sink or bytes not a multiple of 16.
  */
 idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * hbm_read_probe_nt -- as hbm_read_probe with non-temporal loads, the cache
+ * policy of the logits kernel's page loads: its duration is the practical
+ * contiguous HBM read ceiling that kernel is compared with.  Same arguments
+ * and errors.
+ */
+idx_status hbm_read_probe_nt(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /*
  * hbm_gather_probe -- measurement aid, not part of the method: reads the

@@ -31,6 +31,7 @@ Entry points (same names as the C ABI):
   indexer_status_str(status)
   indexer_time_next_call(start, stop)
   hbm_read_probe(src, sink, events=None)
+  hbm_read_probe_nt(src, sink, events=None)
   hbm_gather_probe(kv_pages, k_scales, page_list, sink, events=None)
   mfma_valu_probe(mode, waves_per_simd, iters, out, events=None)
 With ``events=(start, stop)`` (torch.cuda.Event with timing enabled, either
@@ -53,8 +54,8 @@ __all__ = [
     "indexer_sparse_logits_mxfp4", "indexer_prefill_logits", "indexer_prefill_logits_mxfp4",
     "sparse_to_logical", "sparse_topk",
     "topk_workspace_bytes", "topk_rows", "topk_rows_f16", "topk_rows_noalloc", "score_histogram",
-    "indexer_status_str", "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe",
-    "mfma_valu_probe",
+    "indexer_status_str", "indexer_time_next_call", "hbm_read_probe", "hbm_read_probe_nt",
+    "hbm_gather_probe", "mfma_valu_probe",
 ]
 
 KEY_FP32 = 0
@@ -71,7 +72,8 @@ EXPORTED_SYMBOLS = ("indexer_logits", "indexer_logits_f16", "indexer_logits_mxfp
                     "indexer_prefill_logits", "indexer_prefill_logits_mxfp4", "sparse_to_logical", "sparse_topk",
                     "topk_workspace_bytes", "topk_rows", "topk_rows_noalloc",
                     "topk_rows_f16", "score_histogram", "indexer_status_str",
-                    "indexer_time_next_call", "hbm_read_probe", "hbm_gather_probe", "mfma_valu_probe")
+                    "indexer_time_next_call", "hbm_read_probe", "hbm_read_probe_nt", "hbm_gather_probe",
+                    "mfma_valu_probe")
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpaged_mqa_indexer.so"
@@ -114,6 +116,8 @@ def load_library() -> ctypes.CDLL:
     lib.indexer_status_str.restype = ctypes.c_char_p
     lib.hbm_read_probe.argtypes = [vp, sz, vp, vp]
     lib.hbm_read_probe.restype = ctypes.c_int
+    lib.hbm_read_probe_nt.argtypes = [vp, sz, vp, vp]
+    lib.hbm_read_probe_nt.restype = ctypes.c_int
     lib.hbm_gather_probe.argtypes = [vp, vp, vp, i32, i32, vp, vp]
     lib.hbm_gather_probe.restype = ctypes.c_int
     lib.mfma_valu_probe.argtypes = [i32, i32, i32, vp, i64, vp]
@@ -554,8 +558,7 @@ def score_histogram(scores, context_lens, hist):
     _check("score_histogram", st)
 
 
-def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, events=None) -> None:
-    """Stream all bytes of ``src`` (contiguous GPU tensor) once; checksum to sink."""
+def _read_probe(name: str, src: torch.Tensor, sink: torch.Tensor, events) -> None:
     if src.device.type != "cuda" or not src.is_contiguous():
         raise ValueError("src must be a contiguous GPU tensor")
     _need(sink, "sink", torch.int32, src.device)
@@ -563,8 +566,19 @@ def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, events=None) -> None:
     nbytes = src.numel() * src.element_size()
     with torch.cuda.device(src.device):
         _arm(events, src.device)
-        st = lib.hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream_ptr(src.device))
-    _check("hbm_read_probe", st)
+        st = getattr(lib, name)(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream_ptr(src.device))
+    _check(name, st)
+
+
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, events=None) -> None:
+    """Stream all bytes of ``src`` (contiguous GPU tensor) once with ordinary
+    loads (a cache sweep for large buffers); checksum to sink."""
+    _read_probe("hbm_read_probe", src, sink, events)
+
+
+def hbm_read_probe_nt(src: torch.Tensor, sink: torch.Tensor, events=None) -> None:
+    """hbm_read_probe with non-temporal loads: the contiguous read ceiling."""
+    _read_probe("hbm_read_probe_nt", src, sink, events)
 
 
 def hbm_gather_probe(kv_pages: torch.Tensor, k_scales: torch.Tensor, page_list: torch.Tensor,

@@ -366,11 +366,19 @@ idx_status mfma_valu_probe(int32_t mode, int32_t waves_per_simd, int32_t iters, 
                                                static_cast<hipStream_t>(stream), ev));
 }
 
-idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+static idx_status read_probe(const void* src, size_t bytes, uint32_t* sink, bool nt, void* stream) {
   const pmqa::LaunchEvents ev = take_events();
   if (!src || !sink || bytes == 0) return IDX_EINVAL;
   if (!aligned(src, 16) || (bytes % 16) != 0 || !aligned(sink, 4)) return IDX_EALIGN;
-  return from_hip(pmqa::launch_hbm_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream), ev));
+  return from_hip(pmqa::launch_hbm_read_probe(src, bytes, sink, nt, static_cast<hipStream_t>(stream), ev));
+}
+
+idx_status hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  return read_probe(src, bytes, sink, false, stream);
+}
+
+idx_status hbm_read_probe_nt(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  return read_probe(src, bytes, sink, true, stream);
 }
 
 }  // extern "C"

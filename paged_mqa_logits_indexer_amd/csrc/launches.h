@@ -44,7 +44,7 @@ hipError_t launch_topk_rows_noalloc(const TopkArgs& a, hipStream_t stream, Launc
 hipError_t launch_score_histogram(const float* scores, int64_t stride, const int32_t* lens,
                                   int32_t rows, int32_t* hist, hipStream_t stream);
 
-hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, bool nt,
                                  hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_hbm_gather_probe(const uint8_t* pool, const float* scales, const int32_t* table,
                                    int32_t n_pages, int32_t pool_pages, uint32_t* sink, hipStream_t stream,

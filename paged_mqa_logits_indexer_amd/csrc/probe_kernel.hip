@@ -6,9 +6,10 @@
 namespace pmqa {
 namespace {
 
-// Streaming read of a contiguous buffer.  The same kernel is the cache sweep
-// that evicts K between timed calls, so its loads are ordinary (allocating)
-// ones.  Each workgroup reads one contiguous 32 KiB chunk, 8 16-byte loads
+// Streaming read of a contiguous buffer, with ordinary (allocating) loads --
+// the cache sweep that evicts K between timed calls -- or (NT) non-temporal
+// ones, as the logits kernel's page loads into LDS: the read ceiling.  Each
+// workgroup reads one contiguous 32 KiB chunk, 8 16-byte loads
 // per thread in flight (a wave's load instruction covers 1 KiB of
 // consecutive bytes).  Of the shapes swept on this GPU (16-128 KiB chunks,
 // 256-1024 threads, one to four persistent workgroups per CU, loads straight
@@ -18,6 +19,7 @@ constexpr int kProbeThreads = 256;
 constexpr int kProbeVecs = 8;
 constexpr int64_t kProbeChunk = kProbeThreads * kProbeVecs;  // 16-byte vectors: 32 KiB per workgroup
 
+template <bool NT>
 __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32x4* __restrict__ src,
                                                                         int64_t n_vec, uint32_t* sink) {
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kProbeChunk + threadIdx.x;
@@ -25,7 +27,8 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const i32
 #pragma unroll
   for (int i = 0; i < kProbeVecs; ++i) {
     const int64_t j = base + static_cast<int64_t>(i) * kProbeThreads;
-    v[i] = j < n_vec ? src[j] : i32x4{0, 0, 0, 0};
+    if constexpr (NT) v[i] = j < n_vec ? __builtin_nontemporal_load(src + j) : i32x4{0, 0, 0, 0};
+    else v[i] = j < n_vec ? src[j] : i32x4{0, 0, 0, 0};
   }
   uint32_t acc = 0u;
 #pragma unroll
@@ -152,13 +155,13 @@ hipError_t launch_mfma_valu_probe(int mode, int workgroups, int iters, float* ou
   return hipGetLastError();
 }
 
-hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream,
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, bool nt, hipStream_t stream,
                                  LaunchEvents ev) {
   const int64_t n_vec = static_cast<int64_t>(bytes / 16);
   const int64_t grid = (n_vec + kProbeChunk - 1) / kProbeChunk;
   if (grid < 1 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  launch_kernel(hbm_read_probe_kernel, dim3(static_cast<unsigned>(grid)), dim3(kProbeThreads), stream,
-                ev.start, ev.stop, static_cast<const i32x4*>(src), n_vec, sink);
+  launch_kernel(nt ? hbm_read_probe_kernel<true> : hbm_read_probe_kernel<false>, dim3(static_cast<unsigned>(grid)),
+                dim3(kProbeThreads), stream, ev.start, ev.stop, static_cast<const i32x4*>(src), n_vec, sink);
   return hipGetLastError();
 }
 

@@ -204,6 +204,7 @@ def test_probe_rejects(lib, kw, status):
     args = dict(src=A, nbytes=1 << 20, sink=A)
     args.update(kw)
     assert lib.hbm_read_probe(args["src"], args["nbytes"], args["sink"], None) == status
+    assert lib.hbm_read_probe_nt(args["src"], args["nbytes"], args["sink"], None) == status
 
 
 @pytest.mark.parametrize("kw,status", [

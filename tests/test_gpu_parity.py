@@ -639,10 +639,11 @@ def test_read_probes_run_on_small_buffers(gpu):
     """The measurement aids launch on small inputs (partial chunks, a page
     list shorter than a workgroup's share, out-of-range ids clamped) and
     leave the sink alone for data whose checksum is not the marker."""
-    announce("hbm_read_probe / hbm_gather_probe small buffers")
+    announce("hbm_read_probe / hbm_read_probe_nt / hbm_gather_probe small buffers")
     sink = torch.zeros(1, dtype=torch.int32, device=DEV)
     src = torch.zeros(100_000 // 4 * 4, dtype=torch.int32, device=DEV)
     gpu.hbm_read_probe(src, sink)
+    gpu.hbm_read_probe_nt(src, sink)
     pool = torch.zeros((10, 64, 128), dtype=torch.uint8, device=DEV)
     scales = torch.zeros((10, 64), dtype=torch.float32, device=DEV)
     plist = torch.tensor([3, 9, 0, 12, -1, 5, 5], dtype=torch.int32, device=DEV)
