@@ -82,15 +82,17 @@ constexpr int kPrefetchOf = (KF == 1 && NN == 1) ? 2 : kPrefetch;
 #ifndef PMQA_LOGITS_MAX_PPW
 #define PMQA_LOGITS_MAX_PPW 64
 #endif
-// Pages per share at most: 128 with one row per request (its staging is then
-// 32 KiB; a long row's bins receive the flush atomics of half as many
-// workgroups: very_long 104.1 -> 103.3 us, histogram extra 2.1 -> 0.3 us),
-// 64 with several (their staging is NN times larger).
+// Pages per share at most: 256 with one row per request, 64 with several
+// (their staging is NN times larger).  With one row, longer shares mean
+// fewer workgroups per long row: each bin receives fewer flush atomics
+// (128 pages against 64: very_long 104.1 -> 103.3 us, histogram extra 2.1 ->
+// 0.3 us), and at 256 a 4 x 1M-key call fits in one round of workgroups, one
+// per CU, instead of two (very_long 96.0 -> 91.0 us).
 constexpr int kMaxPagesPerWg = PMQA_LOGITS_MAX_PPW;
-constexpr int kMaxPagesPerWgOneRow = 2 * kMaxPagesPerWg;
+constexpr int kMaxPagesPerWgOneRow = 4 * kMaxPagesPerWg;
 static_assert(kMaxPagesPerWgOneRow <= 4 * kWave, "page ids of a share must fit one fetch");
 // LDS staging of a share's scores: next_n * pages_per_wg * 64 floats
-// (32 KiB for one row, 16 KiB per row with several).
+// (64 KiB for one row, 16 KiB per row with several).
 template <int NN>
 constexpr int kStageFloats = NN * (NN == 1 ? kMaxPagesPerWgOneRow : kMaxPagesPerWg) * kPage;
 // Staged score type: float32 logits, or the bits of their FP16 rounding.
