@@ -165,8 +165,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, u
 #ifndef PMQA_LOGITS_DMA_RING
 #define PMQA_LOGITS_DMA_RING 2
 #endif
+// One row per request, either K format (MXFP4: 16.3 -> 15.7 us at long
+// decode against the register path, with an evicting cache sweep).
 template <int NN, int KF>
-constexpr bool kDmaOf = PMQA_LOGITS_DMA && NN == 1 && KF == kKFp8;
+constexpr bool kDmaOf = PMQA_LOGITS_DMA && NN == 1;
 constexpr int kRing = PMQA_LOGITS_DMA_RING;
 static_assert(kRing >= 2 && kRing <= 3, "ring depth: the waits below cover 2 or 3 slots");
 // With the page ring, each wave stores its page's scores as soon as they are
@@ -181,8 +183,13 @@ static_assert(kRing >= 2 && kRing <= 3, "ring depth: the waits below cover 2 or 
 #endif
 template <int NN, int KF>
 constexpr bool kDirectOf = kDmaOf<NN, KF> && PMQA_LOGITS_DIRECT_STORE;
-constexpr int kSlotBytes = kPageBytes + kPage * 4;  // K codes, then the 64 scales
-constexpr int kDmaInstrs = kPageBytes / 1024 + 1;   // per page: 8 K kilobytes + the scales
+// Page slot: FP8 codes then the 64 scales; or the MXFP4 page verbatim.
+template <int KF>
+constexpr int kSlotBytesOf = KF == kKFp8 ? kPageBytes + kPage * 4 : kMxPageBytes;
+// Loads per page: 8 FP8 kilobytes + the scales; 4 MXFP4 kilobytes + 256 bytes.
+template <int KF>
+constexpr int kDmaInstrsOf = KF == kKFp8 ? kPageBytes / 1024 + 1 : kMxPageBytes / 1024 + 1;
+static_assert(kMxPageBytes == 4 * 1024 + kPage * 4, "an MXFP4 page is four kilobytes and 64 words");
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -292,6 +299,92 @@ __device__ __forceinline__ void read_page(uint32_t base, int lane, PageRegs<kKFp
       : "v"(a0), "v"(a1), "v"(as)
       : "memory");
   r.scale = sc;
+}
+
+// MXFP4 pages go to LDS verbatim, in whole lines: instruction i (0..3) copies
+// kilobyte i of the page (lane l: bytes 16 l .. 16 l + 15) and the fifth its
+// last 256 bytes (lane l: one word), all non-temporal like the FP8 pages.
+// Tokens are 68 bytes, so an operand piece -- bytes [16 g, 16 g + 16) of
+// token 16 kb + n -- is only 4-byte aligned in LDS and is read as four words;
+// consecutive tokens lie 17 words apart (17 is odd), so the 64 lanes of a
+// read hit every bank twice, without conflicts.
+struct DmaOffsetsMx {
+  uint32_t k[4];
+  uint32_t tail;
+  __device__ explicit DmaOffsetsMx(int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = static_cast<uint32_t>(i * 1024 + lane * 16);
+    tail = static_cast<uint32_t>(4 * 1024 + lane * 4);
+  }
+};
+
+__device__ __forceinline__ void dma_page(const uint8_t* __restrict__ kv_pages, const float* __restrict__ /*k_scales*/,
+                                         int page, const DmaOffsetsMx& off, uint32_t slot) {
+  const uint8_t* kp = kv_pages + static_cast<int64_t>(page) * kMxPageBytes;
+  __asm__ volatile(
+      "s_mov_b32 m0, %[l0]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v0], %[kb] nt\n"
+      "s_mov_b32 m0, %[l1]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v1], %[kb] nt\n"
+      "s_mov_b32 m0, %[l2]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v2], %[kb] nt\n"
+      "s_mov_b32 m0, %[l3]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[v3], %[kb] nt\n"
+      "s_mov_b32 m0, %[l4]\n"
+      "s_nop 0\n"
+      "global_load_lds_dword %[vt], %[kb] nt\n"
+      :
+      : [kb] "s"(kp), [l0] "s"(slot), [l1] "s"(slot + 1024), [l2] "s"(slot + 2048), [l3] "s"(slot + 3072),
+        [l4] "s"(slot + 4096), [v0] "v"(off.k[0]), [v1] "v"(off.k[1]), [v2] "v"(off.k[2]), [v3] "v"(off.k[3]),
+        [vt] "v"(off.tail)
+      : "memory", "m0");
+}
+
+// The MFMA operands of an MXFP4 page slot: lane (n, g) reads bytes
+// [16 g, 16 g + 16) of token 16 kb + n and the token's scale word, per key
+// block kb; written out with its own wait, as read_page for FP8 pages.
+__device__ __forceinline__ void read_page(uint32_t base, int lane, PageRegs<kKMxfp4>& r) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint32_t a = base + static_cast<uint32_t>(n * kMxTokenBytes + g * 16);
+  const uint32_t as = base + static_cast<uint32_t>(n * kMxTokenBytes + 64);
+  static_assert(16 * kMxTokenBytes == 1088, "key blocks 1088 bytes apart (offsets below)");
+  int w[16], sc[4];
+  __asm__ volatile(
+      "ds_read_b32 %0, %20\n"
+      "ds_read_b32 %1, %20 offset:4\n"
+      "ds_read_b32 %2, %20 offset:8\n"
+      "ds_read_b32 %3, %20 offset:12\n"
+      "ds_read_b32 %4, %20 offset:1088\n"
+      "ds_read_b32 %5, %20 offset:1092\n"
+      "ds_read_b32 %6, %20 offset:1096\n"
+      "ds_read_b32 %7, %20 offset:1100\n"
+      "ds_read_b32 %8, %20 offset:2176\n"
+      "ds_read_b32 %9, %20 offset:2180\n"
+      "ds_read_b32 %10, %20 offset:2184\n"
+      "ds_read_b32 %11, %20 offset:2188\n"
+      "ds_read_b32 %12, %20 offset:3264\n"
+      "ds_read_b32 %13, %20 offset:3268\n"
+      "ds_read_b32 %14, %20 offset:3272\n"
+      "ds_read_b32 %15, %20 offset:3276\n"
+      "ds_read_b32 %16, %21\n"
+      "ds_read_b32 %17, %21 offset:1088\n"
+      "ds_read_b32 %18, %21 offset:2176\n"
+      "ds_read_b32 %19, %21 offset:3264\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7]),
+        "=&v"(w[8]), "=&v"(w[9]), "=&v"(w[10]), "=&v"(w[11]), "=&v"(w[12]), "=&v"(w[13]), "=&v"(w[14]),
+        "=&v"(w[15]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3])
+      : "v"(a), "v"(as)
+      : "memory");
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    r.v[kb] = i32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]};
+    r.sc[kb] = sc[kb];
+  }
 }
 
 // One page of K in MFMA operand layout plus the scale of key `lane`.  Buffer
@@ -597,7 +690,7 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
     // them from HBM a second time).  The compiler does not order LDS reads
     // after these loads, so the waits are explicit: before a slot is
     // refilled, every LDS access issued so far has completed (its last reads
-    // are a page old); before a page is read, at most the kDmaInstrs loads of
+    // are a page old); before a page is read, at most the kDmaInstrsOf loads of
     // each page issued after it are outstanding -- the loop issues no other
     // vector memory operation, and loads complete in issue order.
     // The compiler does not see the page loads (assembly), so it would place
@@ -608,8 +701,9 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
                      "v"(rq.w[0][0]), "v"(rq.w[0][1]));
     if (n_mine > 0) {
       const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(s_ring))) +
-                            static_cast<uint32_t>(wave * (kRing * kSlotBytes));
-      const DmaOffsets off(lane);
+                            static_cast<uint32_t>(wave * (kRing * kSlotBytesOf<KF>));
+      constexpr int kSlotBytes = kSlotBytesOf<KF>;
+      const typename std::conditional<KF == kKFp8, DmaOffsets, DmaOffsetsMx>::type off(lane);
 #pragma unroll
       for (int s = 0; s < kRing - 1; ++s)
         if (s < n_mine) dma_page(a.kv_pages, a.k_scales, page_id(s), off, ring + s * kSlotBytes);
@@ -620,10 +714,17 @@ __device__ __forceinline__ void logits_share(const LogitsArgs& a, int pages_per_
                    ring + ((it + kRing - 1) % kRing) * kSlotBytes);
         }
         const int ahead = min(kRing - 1, n_mine - 1 - it);  // pages in flight issued after page `it`
-        static_assert(kDmaInstrs == 9, "the waits below count 9 loads per page");
-        if (kRing == 3 && ahead == 2) __asm__ volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else if (ahead >= 1) __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (KF == kKFp8) {
+          static_assert(kDmaInstrsOf<KF> == 9, "the waits below count 9 loads per page");
+          if (kRing == 3 && ahead == 2) __asm__ volatile("s_waitcnt vmcnt(18)" ::: "memory");
+          else if (ahead >= 1) __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");
+          else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
+          static_assert(kDmaInstrsOf<KF> == 5, "the waits below count 5 loads per page");
+          if (kRing == 3 && ahead == 2) __asm__ volatile("s_waitcnt vmcnt(10)" ::: "memory");
+          else if (ahead >= 1) __asm__ volatile("s_waitcnt vmcnt(5)" ::: "memory");
+          else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         PageRegs<KF> pr;
         read_page(ring + (it % kRing) * kSlotBytes, lane, pr);
         compute_page<NN, HIST, F16, KF, kDirectOf<NN, KF>>(
@@ -698,7 +799,7 @@ void indexer_logits_kernel(LogitsArgs a, int pages_per_wg) {
   __shared__ __align__(16) float s_w[NN >= 2 ? NN * kHeads : 1];
   __shared__ int s_pref[PERSIST ? kPersistMaxB + 1 : 1];  // shares of requests < b (persistent grid)
   // K page slots of each wave (one-row requests, FP8 K)
-  __shared__ __align__(16) char s_ring[kDmaOf<NN, KF> ? kWavesOf<NN> * kRing * kSlotBytes : 16];
+  __shared__ __align__(16) char s_ring[kDmaOf<NN, KF> ? kWavesOf<NN> * kRing * kSlotBytesOf<KF> : 16];
 
   if constexpr (!PERSIST) {
     logits_share<NN, HIST, F16, KF>(a, pages_per_wg, blockIdx.y, static_cast<int64_t>(blockIdx.x) * pages_per_wg,
